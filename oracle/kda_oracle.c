@@ -1,0 +1,163 @@
+/*
+ * kda_oracle.c -- plain fp64 token-by-token recurrence of the KDA scan.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the correctness oracle that the HIP
+ * path is checked against. Only the tests, the smoke check and the CPU
+ * baseline of the benchmark may load it; the product path never does. It
+ * shares no code, header or table with the HIP library.
+ *
+ * What it computes (Chimera, arXiv 2607.28611):
+ *   - the state update printed in the explainer page, section "One stream,
+ *     three mechanisms, no positions":
+ *         S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     with alpha_t in (0,1)^{d_k} a per-key-channel forget gate and beta_t a
+ *     scalar write/erase strength (paper Sec. 3, KDA paragraph, Eq. 14);
+ *   - S_t in R^{d_k x d_v} is the state after processing position t, and the
+ *     state is reset to S_0 = 0 at every packed-sample boundary (same paragraph);
+ *   - every head uses the same causal scan order (same paragraph);
+ *   - readout o_t = S_t^T q_t from the post-update state. The display
+ *     equation that states the readout did not survive extraction; this is
+ *     the plain reading of the definitions (S_t is the state "after
+ *     processing" position t, q_t in R^{d_q} with d_q = d_k, no scale). The
+ *     pages themselves print no readout, so its form is a reading; the
+ *     exact-recall pin fixes that it uses the post-update state.
+ *
+ * The update is evaluated in its expanded form, token by token:
+ *     S~ = Diag(alpha) S            decay each key row
+ *     p  = S~^T k                   what the decayed state returns for k
+ *     u  = beta (v - p)             innovation
+ *     S  = S~ + k u^T               (I - beta k k^T) S~ + beta k v^T
+ *     o  = S^T q
+ * All arithmetic is fp64 with libm exp; inputs arrive as fp64 (exact upcasts
+ * of the stored fp32/bf16 values). There is no chunking, blocking or reordering.
+ *
+ * Layout: q, k, log_alpha [T][H][dk]; v, out [T][H][dv]; beta [T][H];
+ * cu_seqlens int32 [N+1]; final_state [N][H][dk][dv] (rows = key channels).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+    const double *q, *k, *v, *log_alpha, *beta;
+    const int32_t *cu_seqlens;
+    int32_t n_seqs, H, dk, dv;
+    const uint8_t *head_mask;   /* NULL = all heads */
+    double *out, *final_state;
+    /* work queue over (sequence, head) units */
+    pthread_mutex_t lock;
+    int64_t next_unit;
+    int failed;
+} oracle_job;
+
+/* One (sequence, head) unit: the recurrence over the tokens of that sample. */
+static int scan_unit(oracle_job *job, int32_t n, int32_t h)
+{
+    const int32_t H = job->H, dk = job->dk, dv = job->dv;
+    const int64_t t0 = job->cu_seqlens[n], t1 = job->cu_seqlens[n + 1];
+    double *S = calloc((size_t)dk * dv, sizeof(double));   /* reset: S_0 = 0 */
+    double *p = malloc(sizeof(double) * dv);
+    double *u = malloc(sizeof(double) * dv);
+    if (!S || !p || !u) { free(S); free(p); free(u); return -1; }
+
+    for (int64_t t = t0; t < t1; ++t) {
+        const double *kt = job->k + (t * H + h) * dk;
+        const double *qt = job->q + (t * H + h) * dk;
+        const double *lat = job->log_alpha + (t * H + h) * dk;
+        const double *vt = job->v + (t * H + h) * dv;
+        const double bt = job->beta[t * H + h];
+
+        /* decay: S~ = Diag(alpha_t) S_{t-1}, alpha = exp(log alpha) per key channel */
+        for (int32_t c = 0; c < dk; ++c) {
+            const double a = exp(lat[c]);
+            double *row = S + (size_t)c * dv;
+            for (int32_t j = 0; j < dv; ++j) row[j] *= a;
+        }
+        /* p = S~^T k_t */
+        for (int32_t j = 0; j < dv; ++j) p[j] = 0.0;
+        for (int32_t c = 0; c < dk; ++c) {
+            const double kc = kt[c];
+            const double *row = S + (size_t)c * dv;
+            for (int32_t j = 0; j < dv; ++j) p[j] += row[j] * kc;
+        }
+        /* u = beta_t (v_t - p) */
+        for (int32_t j = 0; j < dv; ++j) u[j] = bt * (vt[j] - p[j]);
+        /* S_t = S~ + k_t u^T */
+        for (int32_t c = 0; c < dk; ++c) {
+            const double kc = kt[c];
+            double *row = S + (size_t)c * dv;
+            for (int32_t j = 0; j < dv; ++j) row[j] += kc * u[j];
+        }
+        /* o_t = S_t^T q_t */
+        double *ot = job->out + (t * H + h) * dv;
+        for (int32_t j = 0; j < dv; ++j) ot[j] = 0.0;
+        for (int32_t c = 0; c < dk; ++c) {
+            const double qc = qt[c];
+            const double *row = S + (size_t)c * dv;
+            for (int32_t j = 0; j < dv; ++j) ot[j] += row[j] * qc;
+        }
+    }
+    if (job->final_state)
+        memcpy(job->final_state + ((size_t)n * H + h) * dk * dv, S, sizeof(double) * dk * dv);
+    free(S); free(p); free(u);
+    return 0;
+}
+
+static void *worker(void *arg)
+{
+    oracle_job *job = (oracle_job *)arg;
+    const int64_t units = (int64_t)job->n_seqs * job->H;
+    for (;;) {
+        pthread_mutex_lock(&job->lock);
+        const int64_t i = job->next_unit++;
+        pthread_mutex_unlock(&job->lock);
+        if (i >= units) break;
+        const int32_t n = (int32_t)(i / job->H), h = (int32_t)(i % job->H);
+        if (job->head_mask && !job->head_mask[h]) continue;
+        if (scan_unit(job, n, h) != 0) {
+            pthread_mutex_lock(&job->lock);
+            job->failed = 1;
+            pthread_mutex_unlock(&job->lock);
+        }
+    }
+    return NULL;
+}
+
+/*
+ * Run the recurrence for every (sequence, head) unit, or for the heads whose
+ * head_mask entry is nonzero. out rows of skipped heads are left untouched.
+ * threads <= 0 means one thread. Returns 0 on success, -1 on bad arguments or
+ * allocation failure.
+ */
+int kda_oracle_forward(const double *q, const double *k, const double *v,
+                       const double *log_alpha, const double *beta,
+                       const int32_t *cu_seqlens, int32_t n_seqs, int32_t H,
+                       int32_t dk, int32_t dv, const uint8_t *head_mask,
+                       double *out, double *final_state, int32_t threads)
+{
+    if (!cu_seqlens || n_seqs < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+    if (cu_seqlens[0] != 0) return -1;
+    for (int32_t n = 0; n < n_seqs; ++n)
+        if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
+    if (cu_seqlens[n_seqs] > 0 && (!q || !k || !v || !log_alpha || !beta || !out)) return -1;
+
+    oracle_job job;
+    memset(&job, 0, sizeof job);
+    job.q = q; job.k = k; job.v = v; job.log_alpha = log_alpha; job.beta = beta;
+    job.cu_seqlens = cu_seqlens; job.n_seqs = n_seqs; job.H = H; job.dk = dk; job.dv = dv;
+    job.head_mask = head_mask; job.out = out; job.final_state = final_state;
+    pthread_mutex_init(&job.lock, NULL);
+
+    if (threads < 1) threads = 1;
+    if (threads > 256) threads = 256;
+    pthread_t tid[256];
+    int started = 0;
+    for (int i = 1; i < threads; ++i)
+        if (pthread_create(&tid[started], NULL, worker, &job) == 0) ++started;
+    worker(&job);
+    for (int i = 0; i < started; ++i) pthread_join(tid[i], NULL);
+    pthread_mutex_destroy(&job.lock);
+    return job.failed ? -1 : 0;
+}
