@@ -20,6 +20,7 @@ then one cast to the storage dtype by round-to-nearest-even.
 from __future__ import annotations
 
 import dataclasses
+import os
 from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -33,24 +34,26 @@ TENSOR_ID = {"q": 1, "k": 2, "v": 3, "log_alpha": 4, "beta": 5}
 def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp64 values to bf16 (nearest, ties to even); return uint16 bits.
 
-    Goes through fp32 with round-to-odd, which makes the second rounding exact
-    (two spare bits suffice), then rounds the fp32 pattern to bf16.
+    The fp32 cast is exact enough everywhere except where it lands exactly on a
+    bf16 halfway point; there the fp64 value decides the direction (a plain
+    second rounding would round an inexact tie to even instead).
     """
     x = np.ascontiguousarray(x, dtype=np.float64)
     f = x.astype(np.float32)
-    # round-to-odd: truncate toward zero, set the sticky bit when inexact
-    over = np.abs(f.astype(np.float64)) > np.abs(x)
-    f = np.where(over, np.nextafter(f, np.float32(0)), f)
-    bits = f.view(np.uint32).copy()
-    inexact = f.astype(np.float64) != x
-    finite = np.isfinite(x)
-    bits = np.where(inexact & finite, bits | np.uint32(1), bits)
-    # fp32 -> bf16, nearest-even on the low 16 bits
+    bits = f.view(np.uint32)
     lsb = (bits >> np.uint32(16)) & np.uint32(1)
-    rounded = (bits + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    out = ((bits + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+    ties = np.flatnonzero((bits & np.uint32(0xFFFF)) == np.uint32(0x8000))
+    if ties.size:
+        xf, ff = x.reshape(-1)[ties], f.reshape(-1)[ties].astype(np.float64)
+        hi = (bits.reshape(-1)[ties] >> np.uint32(16)).astype(np.uint16)
+        o = out.reshape(-1)
+        o[ties] = np.where(np.abs(xf) > np.abs(ff), hi + np.uint16(1),
+                           np.where(np.abs(xf) < np.abs(ff), hi, o[ties]))
     nan = np.isnan(x)
-    rounded = np.where(nan, np.uint32(0x7FC0), rounded)
-    return rounded.astype(np.uint16)
+    if nan.any():
+        out[nan] = np.uint16(0x7FC0)
+    return out
 
 
 def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
@@ -179,9 +182,19 @@ def generate(spec: KdaSpec, heads: Optional[Sequence[int]] = None) -> Dict[str, 
         "log_alpha": np.zeros((T, H, spec.dk), store),
         "beta": np.zeros((T, H), store),
     }
-    for h in (range(H) if heads is None else heads):
-        for name in out:
-            out[name][:, h] = _cast(draw_head(spec, name, h), spec.dtype)
+    jobs = [(name, h) for h in (range(H) if heads is None else heads) for name in out]
+
+    def fill(job):
+        name, h = job
+        out[name][:, h] = _cast(draw_head(spec, name, h), spec.dtype)
+
+    if len(jobs) > 1 and spec.total_tokens * spec.dk > 1 << 16:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(fill, jobs))
+    else:
+        for job in jobs:
+            fill(job)
     out["cu_seqlens"] = spec.cu_seqlens()
     return out
 

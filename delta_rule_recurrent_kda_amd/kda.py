@@ -1,0 +1,123 @@
+"""Python binding of libkda (ctypes). Argument marshalling only.
+
+Every step of the scan runs in the HIP kernels of libkda.so; there is no
+fallback. If the library is missing the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+
+KDA_F32 = 0
+KDA_BF16 = 1
+STATUS = {0: "KDA_OK", 1: "KDA_E_NULL", 2: "KDA_E_DTYPE", 3: "KDA_E_SHAPE", 4: "KDA_E_ALIGN",
+          5: "KDA_E_UNSUPPORTED", 6: "KDA_E_SEQLENS", 7: "KDA_E_HIP"}
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+def library() -> ctypes.CDLL:
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "or python -m delta_rule_recurrent_kda_amd.build")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp = ctypes.c_void_p
+        lib.kda_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
+                                    vp]
+        lib.kda_forward.restype = ctypes.c_int
+        lib.kda_status_str.argtypes = [ctypes.c_int]
+        lib.kda_status_str.restype = ctypes.c_char_p
+        lib.kda_last_error.argtypes = []
+        lib.kda_last_error.restype = ctypes.c_char_p
+        lib.kda_version.argtypes = []
+        lib.kda_version.restype = ctypes.c_int32
+        _lib = lib
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def kda_forward_raw(q, k, v, log_alpha, beta, cu_seqlens, out, final_state, total_tokens: int,
+                    num_seqs: int, num_heads: int, d_k: int, d_v: int, dtype: int,
+                    stream: Optional[int]) -> int:
+    """Direct C call with integer device addresses; returns the status code."""
+    return library().kda_forward(q, k, v, log_alpha, beta, cu_seqlens, out, final_state,
+                                 int(total_tokens), int(num_seqs), int(num_heads), int(d_k),
+                                 int(d_v), int(dtype), stream)
+
+
+def kda_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
+                beta: torch.Tensor, cu_seqlens: torch.Tensor, out: torch.Tensor,
+                final_state: Optional[torch.Tensor] = None,
+                stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Enqueue the KDA forward scan on ``stream`` (default: torch's current stream).
+
+    q, k, log_alpha: [T, H, d_k]; v, out: [T, H, d_v]; beta: [T, H] (one dtype,
+    float32 or bfloat16); cu_seqlens: int32 [N+1]; final_state: float32
+    [N, H, d_k, d_v] or None. All on the same GPU, contiguous.
+    """
+    tensors = {"q": q, "k": k, "v": v, "log_alpha": log_alpha, "beta": beta,
+               "cu_seqlens": cu_seqlens, "out": out}
+    if final_state is not None:
+        tensors["final_state"] = final_state
+    for name, t in tensors.items():
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dtype == torch.bfloat16:
+        dt = KDA_BF16
+    elif q.dtype == torch.float32:
+        dt = KDA_F32
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for name in ("k", "v", "log_alpha", "beta", "out"):
+        if tensors[name].dtype != q.dtype:
+            raise ValueError(f"{name} dtype {tensors[name].dtype} != q dtype {q.dtype}")
+    if cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if final_state is not None and final_state.dtype != torch.float32:
+        raise ValueError("final_state must be float32")
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape != (T, H, dv) or \
+            out.shape != (T, H, dv) or beta.shape != (T, H) or cu_seqlens.dim() != 1:
+        raise ValueError("inconsistent shapes")
+    N = cu_seqlens.numel() - 1
+    if final_state is not None and final_state.shape != (N, H, dk, dv):
+        raise ValueError("final_state must be [N, H, d_k, d_v]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = kda_forward_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(cu_seqlens),
+                         _ptr(out), _ptr(final_state), T, N, H, dk, dv, dt, stream.cuda_stream)
+    if st != 0:
+        raise KdaError(st, library().kda_last_error().decode())
+
+
+def forward(q, k, v, log_alpha, beta, cu_seqlens, with_state: bool = True,
+            stream: Optional[torch.cuda.Stream] = None):
+    """Allocate outputs and run the scan. Returns (out, final_state or None)."""
+    T, H, _ = q.shape
+    N = cu_seqlens.numel() - 1
+    out = torch.empty((T, H, v.shape[2]), dtype=q.dtype, device=q.device)
+    fs = torch.empty((N, H, q.shape[2], v.shape[2]), dtype=torch.float32, device=q.device) \
+        if with_state else None
+    kda_forward(q, k, v, log_alpha, beta, cu_seqlens, out, fs, stream)
+    return out, fs

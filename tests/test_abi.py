@@ -1,0 +1,89 @@
+"""C ABI: the library loads, exports what include/kda.h declares, and rejects
+bad arguments before touching the device (CPU only: no launches here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from delta_rule_recurrent_kda_amd import build as kbuild
+    from delta_rule_recurrent_kda_amd import kda
+    if kbuild.is_stale():
+        kbuild.build()
+    return kda.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert {"kda_forward", "kda_status_str", "kda_last_error", "kda_version"} <= set(declared_functions())
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from delta_rule_recurrent_kda_amd import kda
+    nm = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True, text=True,
+                        check=True).stdout
+    exported = set(re.findall(r"\bT (kda_\w+)$", nm, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "kda.h"\nint main(void){ return (int)kda_version() < 0; }\n')
+    subprocess.run(["gcc", "-std=c11", "-fsyntax-only", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", str(src)], check=True)
+
+
+def test_status_strings(lib):
+    assert lib.kda_status_str(0) == b"KDA_OK"
+    assert lib.kda_status_str(5) == b"KDA_E_UNSUPPORTED"
+    assert lib.kda_version() >= 100
+
+
+def _call(kw):
+    from delta_rule_recurrent_kda_amd import kda
+    a = dict(q=0x1000, k=0x2000, v=0x3000, log_alpha=0x4000, beta=0x5000, cu_seqlens=0x6000,
+             out=0x7000, final_state=0x8000, total_tokens=128, num_seqs=1, num_heads=2, d_k=128,
+             d_v=128, dtype=kda.KDA_BF16, stream=None)
+    a.update(kw)
+    st = kda.kda_forward_raw(**a)
+    return st, kda.library().kda_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), 2),
+    (dict(total_tokens=-1), 3),
+    (dict(num_heads=0), 3),
+    (dict(num_seqs=-2), 3),
+    (dict(d_k=96), 5),
+    (dict(d_v=256), 5),
+    (dict(cu_seqlens=None), 1),
+    (dict(q=None), 1),
+    (dict(out=None), 1),
+    (dict(v=0x3008), 4),
+    (dict(final_state=0x8004), 4),
+    (dict(out=0x1000), 3),
+    (dict(total_tokens=1 << 26, num_heads=64), 5),
+])
+def test_bad_arguments_are_rejected_without_launch(lib, kw, code):
+    st, msg = _call(kw)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def test_empty_batch_is_a_no_op(lib):
+    st, _ = _call(dict(num_seqs=0, total_tokens=0))
+    assert st == 0

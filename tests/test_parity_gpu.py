@@ -1,0 +1,125 @@
+"""HIP path vs the fp64 oracle on seeded inputs (GPU; calls go through the C ABI)."""
+import numpy as np
+import pytest
+
+from delta_rule_recurrent_kda_amd import inputs
+
+import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from delta_rule_recurrent_kda_amd import kda
+    kda.library()
+
+
+def _check(spec, heads=None, label=None):
+    label = label or spec.name
+    gu.log(f"case {label}: seqs={len(spec.seq_lens)} T={spec.total_tokens} H={spec.heads} "
+           f"dk={spec.dk} dv={spec.dv} {spec.dtype}")
+    a = inputs.generate(spec)
+    d = gu.device_inputs(spec, a)
+    out, fs = gu.run_hip(spec, d)
+    o_ref, f_ref = gu.oracle_ref(spec, a, heads=heads)
+    return gu.compare(spec, out, fs, o_ref, f_ref, heads=heads, label=label)
+
+
+EDGE = [
+    ("L1", [1], 2, 128, 128, "bf16"),
+    ("L17", [17], 2, 128, 128, "bf16"),
+    ("L64", [64], 2, 128, 128, "bf16"),
+    ("L65", [65], 2, 128, 128, "bf16"),
+    ("L129_ragged_many", [129, 3, 64, 200, 1, 63], 3, 128, 128, "bf16"),
+    ("zero_len", [0, 50, 0, 0, 77, 0], 2, 128, 128, "bf16"),
+    ("tiny_pack100", list(np.random.default_rng(5).integers(1, 21, 100)), 2, 128, 128, "bf16"),
+    ("d64_bf16", [300, 45], 3, 64, 64, "bf16"),
+    ("dk64_dv128", [150, 99], 2, 64, 128, "bf16"),
+    ("dk128_dv64", [150, 99], 2, 128, 64, "bf16"),
+    ("f32_d128", [33, 100, 1, 257], 2, 128, 128, "f32"),
+    ("f32_d64_ragged", [31, 32, 33, 95], 2, 64, 64, "f32"),
+    ("f32_dk64_dv128", [70, 10], 1, 64, 128, "f32"),
+]
+
+
+@pytest.mark.parametrize("name,lens,H,dk,dv,dt", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_cases(name, lens, H, dk, dv, dt):
+    spec = inputs.KdaSpec(name, tuple(int(x) for x in lens), H, dk, dv, dt, (0.001, 0.1), 4242)
+    _check(spec, label=name)
+
+
+def test_strong_decay_within_precondition():
+    spec = inputs.KdaSpec("strong", (300, 129), 2, 128, 128, "bf16", (0.3, 1.2), 77)
+    _check(spec, label="strong decay")
+
+
+def test_beta_zero_gives_exact_zeros():
+    import torch
+    from delta_rule_recurrent_kda_amd import kda
+    spec = inputs.custom([100, 37], heads=2, d=128, seed=3)
+    a = inputs.generate(spec)
+    a["beta"][:] = 0
+    d = gu.device_inputs(spec, a)
+    o, fs = kda.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"])
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(o.float()).item() == 0
+    assert torch.count_nonzero(fs).item() == 0
+
+
+def test_nan_stays_in_its_sample_and_head():
+    import torch
+    from delta_rule_recurrent_kda_amd import kda
+    spec = inputs.custom([80, 80, 80], heads=2, d=128, seed=4)
+    a = inputs.generate(spec)
+    a["v"][90, 1, 5] = 0x7FC0                     # NaN in sample 1, head 1
+    d = gu.device_inputs(spec, a)
+    o, fs = kda.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"])
+    torch.cuda.synchronize()
+    bad = torch.isnan(o.float()).any(dim=2).cpu().numpy()
+    assert not bad[:80].any() and not bad[160:].any() and not bad[:, 0].any()
+    assert bad[90:160, 1].all()
+    fsn = torch.isnan(fs).cpu().numpy()
+    assert fsn[1, 1].any() and not fsn[[0, 2]].any() and not fsn[1, 0].any()
+
+
+def test_bitwise_deterministic():
+    import torch
+    spec = inputs.custom([700, 300], heads=4, d=128, seed=6)
+    a = inputs.generate(spec)
+    d = gu.device_inputs(spec, a)
+    from delta_rule_recurrent_kda_amd import kda
+    o1, f1 = kda.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"])
+    o2, f2 = kda.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(f1, f2)
+
+
+def test_side_stream_and_null_final_state():
+    import torch
+    from delta_rule_recurrent_kda_amd import kda
+    spec = inputs.custom([130, 70], heads=2, d=128, seed=8)
+    a = inputs.generate(spec)
+    d = gu.device_inputs(spec, a)
+    ref, _ = kda.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"])
+    s = torch.cuda.Stream()
+    out = torch.empty_like(ref)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        kda.kda_forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"], out, None,
+                        stream=s)
+    s.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+def test_named_config_full(cfg):
+    _check(inputs.config(cfg))
+
+
+def test_config4_sampled_heads():
+    # full 189,272-token launch; the oracle recomputes three heads in full
+    _check(inputs.config(4), heads=[0, 7, 15])
