@@ -1,0 +1,181 @@
+"""Benchmark of the KDA forward scan on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload packed8|image4|clip5s|clip30s|tiny]
+
+A step is one kda_forward call over the whole packed batch (every stage of the
+scan runs inside it). Inputs are generated once, copied to HBM, and the timed
+region holds exactly K back-to-back steps between two device synchronisations.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+MFMA_F32_PEAK_TFLOPS = 157.3
+KERNEL_SOURCES = ["delta_rule_recurrent_kda_amd/csrc/kda_fwd.hip",
+                  "delta_rule_recurrent_kda_amd/csrc/kda_internal.h"]
+WORKLOADS = {"tiny": 0, "packed8": 1, "image4": 2, "clip5s": 3, "clip30s": 4}
+CHUNK = 64
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(spec) -> int:
+    """Bytes the scan must move: read q, k, v, log a, beta once, write out and final state."""
+    es = 4 if spec.dtype == "f32" else 2
+    T, H = spec.total_tokens, spec.heads
+    return T * H * (3 * spec.dk + spec.dv) * es + T * H * es + T * H * spec.dv * es + \
+        len(spec.seq_lens) * H * spec.dk * spec.dv * 4
+
+
+def chunk_flops(spec) -> int:
+    """Dense chunk contractions per launch: 10*C*d + 6*d^2 per head-token (d = d_k = d_v)."""
+    d = spec.dk
+    return spec.head_tokens * (10 * CHUNK * d + 6 * d * d)
+
+
+def traffic_for(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel is unchanged."""
+    path = os.path.join(ROOT, "profiles", f"traffic_kda_fwd_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_sha") != kernel_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(spec, a):
+    """The fp64 oracle on the host cores over the whole workload (all samples, all heads)."""
+    import oracle
+    from delta_rule_recurrent_kda_amd import inputs
+    cores = min(16, os.cpu_count() or 1)
+    f = {x: inputs.to_f64(a[x], spec.dtype) for x in ("q", "k", "v", "log_alpha", "beta")}
+    oracle.build()
+    t0 = time.perf_counter()
+    oracle.forward(f["q"], f["k"], f["v"], f["log_alpha"], f["beta"], a["cu_seqlens"], threads=cores)
+    dt = time.perf_counter() - t0
+    return {"value": spec.head_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"whole workload: {len(spec.seq_lens)} samples x {spec.heads} heads, "
+                      f"{spec.head_tokens} head-tokens, fp64 token recurrence, {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="packed8", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="after timing, run 3 plain device copies of this many MiB (for scaling "
+                         "HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the scan shards by (sample, head) with no exchange, see the design notes.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from delta_rule_recurrent_kda_amd import inputs, kda
+
+    spec = inputs.config(WORKLOADS[args.workload])
+    a = inputs.generate(spec)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t = {}
+    for name in ("q", "k", "v", "log_alpha", "beta"):
+        arr = a[name]
+        t[name] = (torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16) if spec.dtype == "bf16"
+                   else torch.from_numpy(arr)).to(dev)
+    cu = torch.from_numpy(a["cu_seqlens"]).to(dev)
+    out = torch.empty((spec.total_tokens, spec.heads, spec.dv), dtype=t["q"].dtype, device=dev)
+    fs = torch.empty((len(spec.seq_lens), spec.heads, spec.dk, spec.dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        kda.kda_forward(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], cu, out, fs, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-launch HIP events on the launch stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for s, e in evs:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    kern_ms = [s.elapsed_time(e) for s, e in evs]
+    avg_ms = float(np.mean(kern_ms))
+    ms_per_step = wall * 1e3 / args.steps
+
+    bytes_ = algorithmic_bytes(spec)
+    flops = chunk_flops(spec)
+    achieved = bytes_ / (avg_ms * 1e-3) / 1e9
+    tflops = flops / (avg_ms * 1e-3) / 1e12
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if spec.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    traffic = traffic_for(args.workload)
+
+    rec = {
+        "metric": "KDA fwd tokens/s (B·L·H) at dk=dv=128; % MFMA peak and % HBM BW, 1 MI355X",
+        "value": spec.head_tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic",
+        "config": {"workload": spec.name, "samples": len(spec.seq_lens), "tokens": spec.total_tokens,
+                   "heads": spec.heads, "d_k": spec.dk, "d_v": spec.dv, "chunk": CHUNK,
+                   "head_tokens": spec.head_tokens},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "kda_fwd_kernel", "kernel_ms_avg": avg_ms,
+                     "kernel_ms_min": float(np.min(kern_ms)), "algorithmic_bytes": bytes_,
+                     "kernel_sha": kernel_sha()},
+        "mfma": {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s", "frac": tflops / mfma_peak,
+                 "flops_per_launch": flops},
+    }
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_calib_bytes"] = n
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(spec, a)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

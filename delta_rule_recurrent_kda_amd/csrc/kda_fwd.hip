@@ -9,23 +9,30 @@
 // Chunkwise form used here (derived from that recurrence; the pages give no
 // kernel). For a chunk of n <= C tokens with state S on entry, G = inclusive
 // row-cumsum of log a (per key channel), gamma = exp(G[n-1]):
-//     Qh = Q*exp(G)   Kh = K*exp(G)   Kc = K*exp(-G)   Kb = K*exp(G[n-1]-G)
-//     A  = StrictLower(diag(b) Kh Kc^T),   T = (I + A)^{-1}        (UT transform)
-//     X  = V - Kh S,   Vn = T diag(b) X   (rows are the delta-rule innovations)
+//     Qh = Q*exp(G)   Kh = K*exp(G)   Kc = K*exp(-G)   Kb = gamma*Kc
+//     A  = StrictLower(diag(b) Kh Kc^T)                               (UT transform)
+//     X  = V - Kh S,   (I + A) Vn = diag(b) X   (rows of Vn are the delta-rule innovations)
 //     O  = Qh S + LowerIncl(Qh Kc^T) Vn,   S <- diag(gamma) S + Kb^T Vn
+// (I + A) Vn = diag(b) X is solved by blocks of 16 rows: the 16x16 diagonal blocks
+// of (I + A) are inverted by substitution in fp32, the off-diagonal blocks enter
+// as products with the already solved rows.
 // The diagonal of Qh Kc^T equals q_t . k_t exactly and is taken in fp32 from the
-// stored inputs rather than from the rounded decayed operands.
+// stored inputs. With bf16 data Qh Kc^T is formed from hi/lo bf16 pairs
+// (hi*hi + lo*hi + hi*lo): rows whose output is a near-cancelling sum of a few
+// such products (the first tokens of a sample) would otherwise carry the full
+// bf16 operand error relative to a small result.
 //
 // Mapping: one workgroup of 4 wave64s per (sample, head, 64-column value tile).
 // Every wave owns 16 value columns of the state for the whole scan (S is fp32 in
-// VGPRs, 128x16 per wave), so the only cross-wave traffic is the v-independent
-// per-chunk operands staged in LDS. Value columns never mix in the recurrence,
-// which is what makes this split exact.
+// registers, DK x 16 per wave), so the only cross-wave traffic is the
+// v-independent per-chunk operands staged in LDS. Value columns never mix in the
+// recurrence, which is what makes this split exact.
 //
 // MFMA fragments: all contractions use 16x16 output tiles (v_mfma_f32_16x16x32_bf16
-// for bf16 data, v_mfma_f32_16x16x4_f32 for fp32 data). A k-block of 32 is held by
-// lane (r = lane%16, g = lane/16) as 8 elements: k = 16*t + 4*g + i (t in {0,1},
-// i in 0..3). An MFMA accumulator holds rows 4*g + i, column r, so two stacked
+// and _16x16x16_bf16 for bf16 data, v_mfma_f32_16x16x4_f32 for fp32 data). A
+// k-block of 32 is held by lane (r = lane%16, g = lane/16) as 8 elements:
+// k = 16*t + 4*g + i (t in {0,1}, i in 0..3); a k-block of 16 is the t = 0 half.
+// An accumulator tile holds rows 4*g + i, column r, so one or two stacked
 // accumulator tiles are directly a B operand (k along their rows) and the A
 // operand of their transpose; both operands of every product use the same k map.
 #include <hip/hip_runtime.h>
@@ -33,143 +40,191 @@
 
 #include "kda_internal.h"
 
+// Optional per-phase cycle accounting hooks (empty in normal builds).
+#ifndef KDA_PHASE_DECL
+#define KDA_PHASE_DECL
+#define KDA_PHASE_MARK(i) ((void)0)
+#define KDA_PHASE_FLUSH
+#endif
+
 namespace kda {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;   // 4 wave64
 constexpr int kBV = 64;         // value columns per workgroup (16 per wave)
+constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
 __device__ __forceinline__ uint16_t f2bf(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return uint32_t(f2bf(a)) | (uint32_t(f2bf(b)) << 16);
+}
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
-// element-type traits: storage type E, MFMA fragment and product
+// element-type traits: storage type E, MFMA fragments and products
 // ---------------------------------------------------------------------------
 template <typename E> struct Elt;
 
 template <> struct Elt<uint16_t> {            // bf16 data
-    struct Frag { uint4 u; };
-    static constexpr int kPad = 4;            // row padding (elements) of LDS operand tiles
+    struct Frag { uint4 u; };                 // k-block of 32
+    struct Frag16 { uint2 u; };               // k-block of 16
+    static constexpr int kVec = 8;            // elements per 16-byte vector
+    using Vec = uint4;
     __device__ static float to_f(uint16_t x) { return bf2f(x); }
     __device__ static uint16_t from_f(float x) { return f2bf(x); }
-    // 8 elements of a row at k = 16t + 4g + i
     __device__ static Frag load(const uint16_t* row, int g) {
         const uint2 lo = *reinterpret_cast<const uint2*>(row + 4 * g);
         const uint2 hi = *reinterpret_cast<const uint2*>(row + 16 + 4 * g);
         return Frag{make_uint4(lo.x, lo.y, hi.x, hi.y)};
     }
-    // same k map, elements taken down a column (B operand from a row-major matrix)
-    __device__ static Frag load_col(const float* m, int ld, int k0, int col, int g, bool upper_half) {
-        float v[8];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                v[4 * t + i] = (t == 0 || upper_half) ? m[(k0 + 16 * t + 4 * g + i) * ld + col] : 0.f;
-        return pack(v);
+    __device__ static Frag16 load16(const uint16_t* row, int g) {
+        return Frag16{*reinterpret_cast<const uint2*>(row + 4 * g)};
     }
-    __device__ static Frag load_f32row(const float* row, int g, bool upper_half) {
-        float v[8];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[4 * t + i] = (t == 0 || upper_half) ? row[16 * t + 4 * g + i] : 0.f;
-        return pack(v);
-    }
-    __device__ static Frag pack(const float* v) {
-        uint32_t w[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            w[j] = uint32_t(f2bf(v[2 * j])) | (uint32_t(f2bf(v[2 * j + 1])) << 16);
-        return Frag{make_uint4(w[0], w[1], w[2], w[3])};
-    }
-    // two accumulator tiles (rows 0..15 and 16..31 of a k-block), optional row scale
     __device__ static Frag from_acc(const f32x4& a0, const f32x4& a1) {
-        float v[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        return pack(v);
+        return Frag{make_uint4(pack2(a0[0], a0[1]), pack2(a0[2], a0[3]), pack2(a1[0], a1[1]),
+                               pack2(a1[2], a1[3]))};
+    }
+    __device__ static Frag16 from_acc16(const f32x4& a0) {
+        return Frag16{make_uint2(pack2(a0[0], a0[1]), pack2(a0[2], a0[3]))};
     }
     __device__ static f32x4 mma(const Frag& a, const Frag& b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.u),
                                                        __builtin_bit_cast(bf16x8, b.u), c, 0, 0, 0);
     }
+    __device__ static f32x4 mma16(const Frag16& a, const Frag16& b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a.u),
+                                                         __builtin_bit_cast(s16x4, b.u), c, 0, 0, 0);
+    }
+    __device__ static void unpack(const Vec& v, float (&f)[8]) {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f[2 * j] = __uint_as_float(w[j] << 16);
+            f[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+        }
+    }
+    // 8 values to a row of LDS whose rows are 8-byte aligned
+    __device__ static void store_vec(uint16_t* dst, const float (&f)[8]) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(f[0], f[1]), pack2(f[2], f[3]));
+        *reinterpret_cast<uint2*>(dst + 4) = make_uint2(pack2(f[4], f[5]), pack2(f[6], f[7]));
+    }
+    // n consecutive values (n = 2 or 4)
+    template <int N> __device__ static void store_run(uint16_t* dst, const float* f) {
+        if constexpr (N == 4) *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(f[0], f[1]), pack2(f[2], f[3]));
+        else *reinterpret_cast<uint32_t*>(dst) = pack2(f[0], f[1]);
+    }
+    __device__ static void store4(uint16_t* dst, const f32x4& a) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(a[0], a[1]), pack2(a[2], a[3]));
+    }
 };
 
 template <> struct Elt<float> {               // fp32 data
     struct Frag { float4 lo, hi; };
-    static constexpr int kPad = 4;
+    struct Frag16 { float4 lo; };
+    static constexpr int kVec = 4;
+    using Vec = float4;
     __device__ static float to_f(float x) { return x; }
     __device__ static float from_f(float x) { return x; }
     __device__ static Frag load(const float* row, int g) {
         return Frag{*reinterpret_cast<const float4*>(row + 4 * g),
                     *reinterpret_cast<const float4*>(row + 16 + 4 * g)};
     }
-    __device__ static Frag load_col(const float* m, int ld, int k0, int col, int g, bool upper_half) {
-        const float* p = m + (k0 + 4 * g) * ld + col;
-        Frag f{make_float4(p[0], p[ld], p[2 * ld], p[3 * ld]), make_float4(0.f, 0.f, 0.f, 0.f)};
-        if (upper_half) f.hi = make_float4(p[16 * ld], p[17 * ld], p[18 * ld], p[19 * ld]);
-        return f;
-    }
-    // rows of the fp32 scratch have an odd stride: scalar reads only
-    __device__ static Frag load_f32row(const float* row, int g, bool upper_half) {
-        const float* p = row + 4 * g;
-        Frag f{make_float4(p[0], p[1], p[2], p[3]), make_float4(0.f, 0.f, 0.f, 0.f)};
-        if (upper_half) f.hi = make_float4(p[16], p[17], p[18], p[19]);
-        return f;
+    __device__ static Frag16 load16(const float* row, int g) {
+        return Frag16{*reinterpret_cast<const float4*>(row + 4 * g)};
     }
     __device__ static Frag from_acc(const f32x4& a0, const f32x4& a1) {
         return Frag{make_float4(a0[0], a0[1], a0[2], a0[3]), make_float4(a1[0], a1[1], a1[2], a1[3])};
     }
-    __device__ static f32x4 mma(const Frag& a, const Frag& b, f32x4 c) {
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.x, b.lo.x, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.y, b.lo.y, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.z, b.lo.z, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.w, b.lo.w, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.x, b.hi.x, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.y, b.hi.y, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.z, b.hi.z, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.w, b.hi.w, c, 0, 0, 0);
+    __device__ static Frag16 from_acc16(const f32x4& a0) {
+        return Frag16{make_float4(a0[0], a0[1], a0[2], a0[3])};
+    }
+    __device__ static f32x4 mma4(const float4& a, const float4& b, f32x4 c) {
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, c, 0, 0, 0);
         return c;
+    }
+    __device__ static f32x4 mma(const Frag& a, const Frag& b, f32x4 c) {
+        return mma4(a.hi, b.hi, mma4(a.lo, b.lo, c));
+    }
+    __device__ static f32x4 mma16(const Frag16& a, const Frag16& b, f32x4 c) { return mma4(a.lo, b.lo, c); }
+    __device__ static void unpack(const Vec& v, float (&f)[4]) { f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w; }
+    __device__ static void store_vec(float* dst, const float (&f)[4]) {
+        *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
+    }
+    template <int N> __device__ static void store_run(float* dst, const float* f) {
+        if constexpr (N == 4) *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
+        else *reinterpret_cast<float2*>(dst) = make_float2(f[0], f[1]);
+    }
+    __device__ static void store4(float* dst, const f32x4& a) {
+        *reinterpret_cast<float4*>(dst) = make_float4(a[0], a[1], a[2], a[3]);
     }
 };
 
-// Raw per-lane chunk loads: CPL consecutive key channels of one row.
-template <typename E, int CPL> struct Raw;
-template <> struct Raw<uint16_t, 1> { using T = uint16_t;
-    __device__ static float get(T x, int) { return bf2f(x); } };
-template <> struct Raw<uint16_t, 2> { using T = uint32_t;
-    __device__ static float get(T x, int c) { return bf2f(uint16_t(c ? (x >> 16) : (x & 0xFFFFu))); } };
-template <> struct Raw<float, 1> { using T = float;
-    __device__ static float get(T x, int) { return x; } };
-template <> struct Raw<float, 2> { using T = float2;
-    __device__ static float get(T x, int c) { return c ? x.y : x.x; } };
-
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+// Sum N per-lane values over 2*MASK consecutive lanes (a power of two dividing 64).
+// On return every lane holds the total of value index reduce_index<N, 2*MASK>(lane).
+template <int N, int MASK>
+__device__ __forceinline__ float reduce_scatter(const float* v, int lane)
+{
+    if constexpr (N == 1) {
+        float x = v[0];
+#pragma unroll
+        for (int m = MASK; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+        return x;
+    } else {
+        const bool up = (lane & MASK) != 0;
+        float w[N / 2];
+#pragma unroll
+        for (int j = 0; j < N / 2; ++j) {
+            const float send = up ? v[j] : v[j + N / 2];
+            const float keep = up ? v[j + N / 2] : v[j];
+            w[j] = keep + __shfl_xor(send, MASK);
+        }
+        return reduce_scatter<N / 2, MASK / 2>(w, lane);
+    }
+}
+template <int N, int W>
+__device__ __forceinline__ int reduce_index(int lane)
+{
+    int idx = 0;
+#pragma unroll
+    for (int n = N / 2, m = W / 2; n >= 1; n /= 2, m /= 2)
+        if (lane & m) idx += n;
+    return idx;
+}
 
 // ---------------------------------------------------------------------------
 // shared-memory layout
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int C> struct Smem {
-    static constexpr int LDK = DK + Elt<E>::kPad;     // row stride of [C][DK] tiles
-    static constexpr int LDC = C + Elt<E>::kPad;      // row stride of [*][C] tiles
-    static constexpr int LDV = kBV + 16 / sizeof(E);  // row stride of V / O staging (16B rows)
-    static constexpr int LDA = C + 1;                 // fp32 [C][C] scratch
-    E qh[C * LDK];        // Qh
-    E kh[C * LDK];        // -Kh
-    E kc[C * LDK];        // Kc
-    E kbt[DK * LDC];      // Kb^T (key channel major)
-    E p[C * LDC];         // LowerIncl(Qh Kc^T), row-major [i][j]
-    E tb[C * LDC];        // T in the operand type
-    E vs[C * LDV];        // V tile
-    E os[C * LDV];        // O tile staging
-    float a[C * LDA];     // A (strictly lower)
-    float t32[C * LDA];   // T in fp32 while it is being built
-    float gam[DK];
+    static constexpr bool kSplit = sizeof(E) == 2;
+    static constexpr int LDK = DK + 4;                         // row stride of [C][DK] tiles
+    static constexpr int LDC = C + 4;                          // row stride of [*][C] tiles
+    static constexpr int LDV = kBV + 16 / sizeof(E);           // V / O staging (16-byte rows)
+    static constexpr int LDT = 16 + 4;                         // 16x16 blocks
+    static constexpr int NRG = kThreads / (DK / Elt<E>::kVec); // row groups of the elementwise phase
+    alignas(16) E qh[C * LDK];            // Qh (hi part for bf16)
+    alignas(16) E kh[C * LDK];            // -Kh
+    alignas(16) E kc[C * LDK];            // Kc (hi part for bf16)
+    alignas(16) E qlo[kSplit ? C * LDK : 4];
+    alignas(16) E kclo[kSplit ? C * LDK : 4];
+    alignas(16) E kbt[DK * LDC];          // Kb^T (key channel major)
+    alignas(16) E p[C * LDC];             // LowerIncl(Qh Kc^T), row-major [i][j]
+    alignas(16) E ab[C * LDC];            // -A below the diagonal blocks, row-major
+    alignas(16) E tbb[C * LDT];           // inverses of the diagonal 16x16 blocks of I + A
+    alignas(16) E vo[C * LDV];            // V tile, then the O tile of the same chunk
+    alignas(16) float a16[C * LDT];       // diagonal 16x16 blocks of A (fp32)
+    alignas(16) float wtot[4 * DK];       // per-wave sums of log a
+    alignas(16) float gam[DK];
     float beta[C];
     float diag[C];
-    float tot[4 * DK];
 };
 
 // ---------------------------------------------------------------------------
@@ -184,25 +239,30 @@ __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
 {
     using EL = Elt<E>;
     using Frag = typename EL::Frag;
-    constexpr int CPL = DK / 64;          // key channels per lane in the elementwise phase
-    constexpr int RPW = C / 4;            // chunk rows per wave in the elementwise phase
-    constexpr int NRT = C / 16;           // 16-row tiles per chunk
-    constexpr int NKC = C / 32;           // 32-wide k-blocks over chunk rows
-    constexpr int NKD = DK / 32;          // 32-wide k-blocks over key channels
-    constexpr int NCT = DK / 16;          // 16-row tiles over key channels
-    constexpr int VPR = kBV * sizeof(E) / 16;                 // 16-byte pieces per V row
-    constexpr int VLD = C * VPR / kThreads;                   // V pieces per thread
-    static_assert(VLD >= 1 && (C * VPR) % kThreads == 0, "V tile split");
-    using RT = Raw<E, CPL>;
-    using RawT = typename RT::T;
+    using Vec = typename EL::Vec;
     using S_ = Smem<E, DK, C>;
-    constexpr int LDK = S_::LDK, LDC = S_::LDC, LDV = S_::LDV, LDA = S_::LDA;
+    constexpr int VE = EL::kVec;            // elements per 16-byte vector
+    constexpr int NV = DK / VE;             // vectors per key row
+    constexpr int NRG = S_::NRG;            // row groups (threads sharing a vector column)
+    constexpr int RPT = C / NRG;            // consecutive chunk rows per thread
+    constexpr int NRT = C / 16;             // 16-row tiles per chunk
+    constexpr int NKC = C / 32;             // 32-wide k-blocks over chunk rows
+    constexpr int NKD = DK / 32;            // 32-wide k-blocks over key channels
+    constexpr int NCT = DK / 16;            // 16-row tiles over key channels
+    constexpr int VPR = kBV * sizeof(E) / 16;       // 16-byte pieces per V row
+    constexpr int VLD = C * VPR / kThreads;         // V pieces per thread
+    constexpr int NPAIR = NRT * (NRT + 1) / 2;      // lower 16x16 tiles of a CxC matrix
+    constexpr int LDK = S_::LDK, LDC = S_::LDC, LDV = S_::LDV, LDT = S_::LDT;
+    static_assert(RPT == 2 || RPT == 4, "elementwise row split");
+    static_assert(VLD >= 1 && (C * VPR) % kThreads == 0, "V tile split");
+    static_assert(64 % NV == 0, "a row group must sit inside one wave");
 
     extern __shared__ __align__(16) unsigned char smem_raw[];
     S_& sm = *reinterpret_cast<S_*>(smem_raw);
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, g = lane >> 4;
+    const int vcol = tid % NV, rg = tid / NV;       // elementwise phase: vector column, row group
 
     // XCD-aware block order: the value tiles of one (sample, head) are 8 blocks
     // apart so that they land on the same XCD and share its L2 for q, k, log a.
@@ -216,10 +276,10 @@ __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
     const int64_t len = int64_t(cu[n + 1]) - seq0;
     const int nchunks = int((len + C - 1) / C);
     const int col0 = vt * kBV;
+    const int64_t rstride = int64_t(H) * DK;       // elements between consecutive tokens
 
-    // blocks above the diagonal of T and P are never written: clear once
-    for (int i = tid; i < C * LDA; i += kThreads) sm.t32[i] = 0.f;
-    for (int i = tid; i < C * LDC; i += kThreads) { sm.tb[i] = E(0); sm.p[i] = E(0); }
+    // the blocks of P and -A above the diagonal are never written: clear once
+    for (int i = tid; i < C * LDC; i += kThreads) { sm.p[i] = E(0); sm.ab[i] = E(0); }
 
     // state: wave owns value columns [16*wave, 16*wave+16) of the tile; NCT tiles of 16 key rows
     f32x4 S[NCT];
@@ -227,22 +287,21 @@ __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
     for (int i = 0; i < NCT; ++i) S[i] = zero4();
 
     // ---- raw loads of one chunk into registers --------------------------------
-    RawT rq[RPW], rk[RPW], rg[RPW];
+    Vec rq[RPT], rk[RPT], rla[RPT];
     uint4 rv[VLD];
     E rb = E(0);
     auto load_chunk = [&](int c) {
         const int64_t t0 = seq0 + int64_t(c) * C;
         const int nrow = int(min<int64_t>(C, len - int64_t(c) * C));
+        const int64_t base = (t0 + rg * RPT) * rstride + int64_t(h) * DK + vcol * VE;
 #pragma unroll
-        for (int j = 0; j < RPW; ++j) {
-            const int row = wave * RPW + j;
-            if (row < nrow) {
-                const int64_t off = ((t0 + row) * H + h) * DK + lane * CPL;
-                rq[j] = *reinterpret_cast<const RawT*>(q + off);
-                rk[j] = *reinterpret_cast<const RawT*>(k + off);
-                rg[j] = *reinterpret_cast<const RawT*>(la + off);
+        for (int i = 0; i < RPT; ++i) {
+            if (rg * RPT + i < nrow) {
+                rq[i] = *reinterpret_cast<const Vec*>(q + base + i * rstride);
+                rk[i] = *reinterpret_cast<const Vec*>(k + base + i * rstride);
+                rla[i] = *reinterpret_cast<const Vec*>(la + base + i * rstride);
             } else {
-                rq[j] = RawT{}; rk[j] = RawT{}; rg[j] = RawT{};
+                rq[i] = Vec{}; rk[i] = Vec{}; rla[i] = Vec{};
             }
         }
 #pragma unroll
@@ -259,288 +318,311 @@ __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
     };
 
     if (nchunks > 0) load_chunk(0);
+    KDA_PHASE_DECL
 
     for (int c = 0; c < nchunks; ++c) {
         const int64_t t0 = seq0 + int64_t(c) * C;
         const int nrow = int(min<int64_t>(C, len - int64_t(c) * C));
 
-        // ---- phase 0a: local cumsum of log a over this wave's rows -------------
-        float G[RPW][CPL];
-        float diagp[RPW];
+        // ---- phase A: sums of log a over row groups and their prefix inside the wave;
+        //      exact diagonal q.k ----------------------------------------------------
+        float excl[VE];                           // log a summed over earlier rows of this wave
+        {
+            float tl[VE], inc[VE];
 #pragma unroll
-        for (int ch = 0; ch < CPL; ++ch) {
-            float run = 0.f;
+            for (int e = 0; e < VE; ++e) tl[e] = 0.f;
 #pragma unroll
-            for (int j = 0; j < RPW; ++j) { run += RT::get(rg[j], ch); G[j][ch] = run; }
-            sm.tot[wave * DK + lane * CPL + ch] = run;
+            for (int i = 0; i < RPT; ++i) {
+                float gv[VE];
+                EL::unpack(rla[i], gv);
+#pragma unroll
+                for (int e = 0; e < VE; ++e) tl[e] += gv[e];
+            }
+#pragma unroll
+            for (int e = 0; e < VE; ++e) inc[e] = tl[e];
+#pragma unroll
+            for (int sft = NV; sft < 64; sft *= 2) {          // row groups of a wave are NV lanes apart
+#pragma unroll
+                for (int e = 0; e < VE; ++e) {
+                    const float o = __shfl_up(inc[e], sft);
+                    if (lane >= sft) inc[e] += o;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < VE; ++e) excl[e] = inc[e] - tl[e];
+            if (lane >= 64 - NV) {
+#pragma unroll
+                for (int e = 0; e < VE; e += 4)
+                    *reinterpret_cast<float4*>(&sm.wtot[wave * DK + vcol * VE + e]) =
+                        make_float4(inc[e], inc[e + 1], inc[e + 2], inc[e + 3]);
+            }
+            float dp[RPT];
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                float qv[VE], kv[VE];
+                EL::unpack(rq[i], qv);
+                EL::unpack(rk[i], kv);
+                float sum = 0.f;
+#pragma unroll
+                for (int e = 0; e < VE; ++e) sum += qv[e] * kv[e];
+                dp[i] = sum;
+            }
+            const float tot = reduce_scatter<RPT, NV / 2>(dp, lane);
+            if ((lane & (NV / RPT - 1)) == 0) sm.diag[rg * RPT + reduce_index<RPT, NV>(lane)] = tot;
         }
-#pragma unroll
-        for (int j = 0; j < RPW; ++j) {
-            float s = 0.f;
-#pragma unroll
-            for (int ch = 0; ch < CPL; ++ch) s += RT::get(rq[j], ch) * RT::get(rk[j], ch);
-            diagp[j] = s;
-        }
+        if (tid < C) sm.beta[tid] = EL::to_f(rb);
+        KDA_PHASE_MARK(0); __syncthreads(); KDA_PHASE_MARK(1);  // B1
+
+        // ---- phase B: decay factors and decayed operands -------------------------
+        // (the V tile goes in only now: the previous chunk's O store read this buffer)
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
             const int piece = tid + i * kThreads;
-            *reinterpret_cast<uint4*>(&sm.vs[(piece / VPR) * LDV + (piece % VPR) * (16 / sizeof(E))]) = rv[i];
+            *reinterpret_cast<uint4*>(&sm.vo[(piece / VPR) * LDV + (piece % VPR) * (16 / sizeof(E))]) = rv[i];
         }
-        if (tid < C) sm.beta[tid] = EL::to_f(rb);
-
-        // exact diagonal q_t . k_t: reduce-scatter the RPW row partials over the wave
         {
-            float vals[RPW];
+            float run[VE], gam[VE];
 #pragma unroll
-            for (int j = 0; j < RPW; ++j) vals[j] = diagp[j];
-            int cnt = RPW;
-            int mask = 32;
+            for (int e = 0; e < VE; ++e) { run[e] = excl[e]; gam[e] = 0.f; }
 #pragma unroll
-            for (int step = 0; step < 6; ++step) {
-                if (cnt > 1) {
-                    const bool upper = (lane & mask) != 0;
-                    const int half = cnt / 2;
+            for (int w = 0; w < 4; ++w) {
 #pragma unroll
-                    for (int j = 0; j < RPW / 2; ++j) {
-                        if (j < half) {
-                            const float send = upper ? vals[j] : vals[j + half];
-                            const float keep = upper ? vals[j + half] : vals[j];
-                            vals[j] = keep + __shfl_xor(send, mask);
+                for (int e = 0; e < VE; e += 4) {
+                    const float4 t4 = *reinterpret_cast<const float4*>(&sm.wtot[w * DK + vcol * VE + e]);
+                    const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        gam[e + u] += tv[u];
+                        if (w < wave) run[e + u] += tv[u];
+                    }
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < VE; ++e) gam[e] = fast_exp2(gam[e] * kLog2e);
+            if (rg == 0) {
+#pragma unroll
+                for (int e = 0; e < VE; e += 4)
+                    *reinterpret_cast<float4*>(&sm.gam[vcol * VE + e]) =
+                        make_float4(gam[e], gam[e + 1], gam[e + 2], gam[e + 3]);
+            }
+#pragma unroll
+            for (int i = 0; i < RPT; i += 2) {
+                float kb[VE][2];
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii) {
+                    const int row = rg * RPT + i + ii;
+                    float gv[VE], qv[VE], kv[VE];
+                    EL::unpack(rla[i + ii], gv);
+                    EL::unpack(rq[i + ii], qv);
+                    EL::unpack(rk[i + ii], kv);
+                    float fq[VE], fkh[VE], fkc[VE];
+#pragma unroll
+                    for (int e = 0; e < VE; ++e) {
+                        run[e] += gv[e];
+                        const float G2 = run[e] * kLog2e;
+                        const float ex = fast_exp2(G2), ei = fast_exp2(-G2);
+                        fq[e] = qv[e] * ex;
+                        fkh[e] = -(kv[e] * ex);
+                        fkc[e] = kv[e] * ei;
+                        kb[e][ii] = fkc[e] * gam[e];
+                    }
+                    EL::store_vec(&sm.qh[row * LDK + vcol * VE], fq);
+                    EL::store_vec(&sm.kh[row * LDK + vcol * VE], fkh);
+                    EL::store_vec(&sm.kc[row * LDK + vcol * VE], fkc);
+                    if constexpr (S_::kSplit) {
+                        float lq[VE], lk[VE];
+#pragma unroll
+                        for (int e = 0; e < VE; ++e) {
+                            lq[e] = fq[e] - bf2f(f2bf(fq[e]));
+                            lk[e] = fkc[e] - bf2f(f2bf(fkc[e]));
+                        }
+                        EL::store_vec(&sm.qlo[row * LDK + vcol * VE], lq);
+                        EL::store_vec(&sm.kclo[row * LDK + vcol * VE], lk);
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < VE; ++e)
+                    EL::template store_run<2>(&sm.kbt[(vcol * VE + e) * LDC + rg * RPT + i], kb[e]);
+            }
+        }
+        KDA_PHASE_MARK(2); __syncthreads(); KDA_PHASE_MARK(3);  // B2
+
+        // ---- phase C: P and A tiles, inverse of this wave's diagonal block of I + A,
+        //      and the S-dependent products that need neither -------------------------
+        const int vc = 16 * wave + r;                               // column within the value tile
+        f32x4 X[NRT], O[NRT];
+        {
+            // wave w computes the diagonal tile (w, w) and tiles below the diagonal;
+            // tiles are computed transposed (Kc rows as the A operand) so that each
+            // lane writes four consecutive columns of a row-major result
+            int its[3], jts[3];
+            bool ok[3];
+#pragma unroll
+            for (int u = 0; u < 3; ++u) { its[u] = jts[u] = 0; ok[u] = false; }
+            if constexpr (NRT == 4) {
+                its[0] = jts[0] = wave; ok[0] = true;
+                const int t1i[4] = {1, 2, 2, 3}, t1j[4] = {0, 0, 1, 0};
+                its[1] = t1i[wave]; jts[1] = t1j[wave]; ok[1] = true;
+                its[2] = 3; jts[2] = 2 - wave; ok[2] = wave < 2;       // (3,2) and (3,1)
+            } else {
+                const int ti[4] = {0, 1, 1, 0}, tj[4] = {0, 1, 0, 0};
+                its[0] = ti[wave]; jts[0] = tj[wave]; ok[0] = wave < 3;
+            }
+            f32x4 accP[3], accA[3];
+#pragma unroll
+            for (int u = 0; u < 3; ++u) { accP[u] = zero4(); accA[u] = zero4(); }
+#pragma unroll
+            for (int kb = 0; kb < NKD; ++kb) {
+#pragma unroll
+                for (int u = 0; u < 3; ++u) {
+                    if (ok[u]) {
+                        const int it = its[u], jt = jts[u];
+                        const Frag fa = EL::load(&sm.kc[(16 * jt + r) * LDK + 32 * kb], g);
+                        const Frag fq = EL::load(&sm.qh[(16 * it + r) * LDK + 32 * kb], g);
+                        accP[u] = EL::mma(fa, fq, accP[u]);
+                        accA[u] = EL::mma(fa, EL::load(&sm.kh[(16 * it + r) * LDK + 32 * kb], g), accA[u]);
+                        if constexpr (S_::kSplit) {
+                            accP[u] = EL::mma(EL::load(&sm.kclo[(16 * jt + r) * LDK + 32 * kb], g), fq, accP[u]);
+                            accP[u] = EL::mma(fa, EL::load(&sm.qlo[(16 * it + r) * LDK + 32 * kb], g), accP[u]);
                         }
                     }
-                    cnt = half;
-                } else {
-                    vals[0] += __shfl_xor(vals[0], mask);
                 }
-                mask >>= 1;
             }
-            // lane holds the total for row index built from its upper lane bits
-            int rowi = 0, m2 = 32, c2 = RPW;
+            // accumulator element i of tile (it, jt) is entry [16it + r][16jt + 4g + i]
 #pragma unroll
-            for (int step = 0; step < 6; ++step) {
-                if (c2 > 1) { c2 >>= 1; if (lane & m2) rowi += c2; }
-                m2 >>= 1;
+            for (int u = 0; u < 3; ++u) {
+                if (ok[u]) {
+                    const int it = its[u], jt = jts[u];
+                    const int irow = 16 * it + r;
+                    const float bi = sm.beta[irow];
+                    f32x4 pv, av;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int jcol = 16 * jt + 4 * g + i;
+                        pv[i] = (jcol < irow) ? accP[u][i] : (jcol == irow ? sm.diag[irow] : 0.f);
+                        av[i] = bi * accA[u][i];            // kh holds -Kh: this is -A
+                    }
+                    EL::store4(&sm.p[irow * LDC + 16 * jt + 4 * g], pv);
+                    if (jt < it) {
+                        EL::store4(&sm.ab[irow * LDC + 16 * jt + 4 * g], av);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) av[i] = (4 * g + i < r) ? -av[i] : 0.f;
+                        *reinterpret_cast<float4*>(&sm.a16[irow * LDT + 4 * g]) =
+                            make_float4(av[0], av[1], av[2], av[3]);
+                    }
+                }
             }
-            constexpr int low_bits = 64 / RPW;       // lanes sharing one row total
-            if ((lane & (low_bits - 1)) == 0) sm.diag[wave * RPW + rowi] = vals[0];
-        }
-        __syncthreads();                                             // B1
 
-        // ---- phase 0b: decay factors, decayed operands --------------------------
-        {
-            float off[CPL], glast[CPL];
-#pragma unroll
-            for (int ch = 0; ch < CPL; ++ch) {
-                float o = 0.f, a = 0.f;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const float t = sm.tot[w * DK + lane * CPL + ch];
-                    a += t;
-                    if (w < wave) o += t;
-                }
-                off[ch] = o; glast[ch] = a;
-            }
-            if (wave == 0) {
-#pragma unroll
-                for (int ch = 0; ch < CPL; ++ch) sm.gam[lane * CPL + ch] = __expf(glast[ch]);
-            }
-#pragma unroll
-            for (int j = 0; j < RPW; ++j) {
-                const int row = wave * RPW + j;
-#pragma unroll
-                for (int ch = 0; ch < CPL; ++ch) {
-                    const int col = lane * CPL + ch;
-                    const float Gj = G[j][ch] + off[ch];
-                    const float e = __expf(Gj), ei = __expf(-Gj), eb = __expf(glast[ch] - Gj);
-                    const float qv = RT::get(rq[j], ch), kv = RT::get(rk[j], ch);
-                    sm.qh[row * LDK + col] = EL::from_f(qv * e);
-                    sm.kh[row * LDK + col] = EL::from_f(-(kv * e));
-                    sm.kc[row * LDK + col] = EL::from_f(kv * ei);
-                    sm.kbt[col * LDC + row] = EL::from_f(kv * eb);
-                }
-            }
-        }
-        // prefetch the next chunk while this one is processed
-        if (c + 1 < nchunks) load_chunk(c + 1);
-        __syncthreads();                                             // B2
-
-        // ---- phase 1: A = StrictLower(diag(b) Kh Kc^T), P = LowerIncl(Qh Kc^T) ----
-        // computed transposed (Kc rows as the A operand) so that every lane writes
-        // four consecutive columns of a row-major result.
-        {
-            constexpr int NPAIR = NRT * (NRT + 1) / 2;
-            for (int pi = wave; pi < NPAIR; pi += 4) {
-                int it = 0, rem = pi;
-                while (rem > it) { rem -= it + 1; ++it; }
-                const int jt = rem;                                    // jt <= it
-                f32x4 accP = zero4(), accA = zero4();
-#pragma unroll
-                for (int kb = 0; kb < NKD; ++kb) {
-                    const Frag fa = EL::load(&sm.kc[(16 * jt + r) * LDK + 32 * kb], g);
-                    const Frag fq = EL::load(&sm.qh[(16 * it + r) * LDK + 32 * kb], g);
-                    const Frag fk = EL::load(&sm.kh[(16 * it + r) * LDK + 32 * kb], g);
-                    accP = EL::mma(fa, fq, accP);
-                    accA = EL::mma(fa, fk, accA);
-                }
-                // accumulator element (row 16jt+4g+i, col 16it+r) is entry [i_=16it+r][j_=16jt+4g+i]
-                const int irow = 16 * it + r;
-                const float bi = sm.beta[irow];
-                float pv[4], av[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int jcol = 16 * jt + 4 * g + i;
-                    pv[i] = (jcol < irow) ? accP[i] : (jcol == irow ? sm.diag[irow] : 0.f);
-                    av[i] = (jcol < irow) ? -bi * accA[i] : 0.f;       // kh holds -Kh
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sm.p[irow * LDC + 16 * jt + 4 * g + i] = EL::from_f(pv[i]);
-                    sm.a[irow * LDA + 16 * jt + 4 * g + i] = av[i];
-                }
-            }
-        }
-        __syncthreads();                                             // B3
-
-        // ---- phase 2a: diagonal 16x16 blocks of T = (I + A)^{-1} ----------------
-        if (wave < NRT && lane < 16) {
-            const int bb = 16 * wave, j = lane;
-            float t[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float s = (i == j) ? 1.f : 0.f;
-#pragma unroll
-                for (int m = 0; m < i; ++m) s -= sm.a[(bb + i) * LDA + bb + m] * t[m];
-                t[i] = s;
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                sm.t32[(bb + i) * LDA + bb + j] = t[i];
-                sm.tb[(bb + i) * LDC + bb + j] = EL::from_f(t[i]);
-            }
-        }
-        __syncthreads();                                             // B4
-
-        // ---- phase 2b: T[b1][b0] = -T[b1][b1] (A[b1][b0] T[b0][b0]) in each 32-row block
-        if (wave < NRT / 2) {
-            const int b0 = 32 * wave, b1 = b0 + 16;
-            // Y = A[b1][b0] T[b0][b0] (k over 16 -> upper half of the k-block is zero)
-            const Frag fa = EL::load_f32row(&sm.a[(b1 + r) * LDA + b0], g, false);
-            const Frag fb = EL::load_col(sm.t32, LDA, b0, b0 + r, g, false);   // T[b0+k][b0+r]
-            f32x4 y = EL::mma(fa, fb, zero4());
-            // T[b1][b0] = -T[b1][b1] Y: A operand T[b1][b1] (k over 16), B operand Y (accumulator rows)
-            const Frag ft = EL::load_f32row(&sm.t32[(b1 + r) * LDA + b1], g, false);
-            const Frag fy = EL::from_acc(y, zero4());
-            f32x4 tz = EL::mma(ft, fy, zero4());
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float tv = -tz[i];
-                sm.t32[(b1 + 4 * g + i) * LDA + b0 + r] = tv;
-                sm.tb[(b1 + 4 * g + i) * LDC + b0 + r] = EL::from_f(tv);
-            }
-        }
-        __syncthreads();                                             // B5
-
-        // ---- phase 2c (C = 64): T[32:64][0:32] = -T2 (A[32:64][0:32] T1) ---------
-        if constexpr (NRT == 4) {
-            if (wave < 2) {
-                const int cj = 16 * wave;                               // column tile of the result
-                f32x4 z[2];
-#pragma unroll
-                for (int zi = 0; zi < 2; ++zi) {
-                    const Frag fa = EL::load_f32row(&sm.a[(32 + 16 * zi + r) * LDA + 0], g, true);
-                    const Frag fb = EL::load_col(sm.t32, LDA, 0, cj + r, g, true);
-                    z[zi] = EL::mma(fa, fb, zero4());
-                }
-                const Frag fz = EL::from_acc(z[0], z[1]);
-#pragma unroll
-                for (int ti = 0; ti < 2; ++ti) {
-                    const Frag ft = EL::load_f32row(&sm.t32[(32 + 16 * ti + r) * LDA + 32], g, true);
-                    const f32x4 tz = EL::mma(ft, fz, zero4());
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        sm.tb[(32 + 16 * ti + 4 * g + i) * LDC + cj + r] = EL::from_f(-tz[i]);
-                }
-            }
-            __syncthreads();                                         // B6
-        }
-
-        // ---- phase 3: the state pass for this wave's 16 value columns -----------
-        {
-            const int vc = 16 * wave + r;                               // column within the tile
+            // X = V - Kh S and O = Qh S
             Frag sf[NKD];
 #pragma unroll
             for (int kb = 0; kb < NKD; ++kb) sf[kb] = EL::from_acc(S[2 * kb], S[2 * kb + 1]);
-
-            // X = V - Kh S, scaled by beta per row
-            f32x4 X[NRT];
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) {
-                f32x4 acc;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = EL::to_f(sm.vs[(16 * rt + 4 * g + i) * LDV + vc]);
-#pragma unroll
-                for (int kb = 0; kb < NKD; ++kb)
-                    acc = EL::mma(EL::load(&sm.kh[(16 * rt + r) * LDK + 32 * kb], g), sf[kb], acc);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] *= sm.beta[16 * rt + 4 * g + i];
-                X[rt] = acc;
+                for (int i = 0; i < 4; ++i) X[rt][i] = EL::to_f(sm.vo[(16 * rt + 4 * g + i) * LDV + vc]);
+                O[rt] = zero4();
             }
-            Frag xf[NKC];
 #pragma unroll
-            for (int kb = 0; kb < NKC; ++kb) xf[kb] = EL::from_acc(X[2 * kb], X[2 * kb + 1]);
+            for (int kb = 0; kb < NKD; ++kb) {
+#pragma unroll
+                for (int rt = 0; rt < NRT; ++rt) {
+                    X[rt] = EL::mma(EL::load(&sm.kh[(16 * rt + r) * LDK + 32 * kb], g), sf[kb], X[rt]);
+                    O[rt] = EL::mma(EL::load(&sm.qh[(16 * rt + r) * LDK + 32 * kb], g), sf[kb], O[rt]);
+                }
+            }
 
-            // Vn = T (beta X)
+            // (I + A_ww)^{-1} for this wave's diagonal block by substitution: lane j%16
+            // builds column j; every lane computes so the work can interleave with the
+            // products above, lanes 0..15 store
+            if (NRT == 4 || wave < NRT) {
+                const float* ablk = &sm.a16[wave * 16 * LDT];
+                const int j = lane & 15;
+                float t[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float s0 = (i == j) ? 1.f : 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+                    for (int m = 0; m < i; m += 4) {
+                        s0 -= ablk[i * LDT + m] * t[m];
+                        if (m + 1 < i) s1 -= ablk[i * LDT + m + 1] * t[m + 1];
+                        if (m + 2 < i) s2 -= ablk[i * LDT + m + 2] * t[m + 2];
+                        if (m + 3 < i) s3 -= ablk[i * LDT + m + 3] * t[m + 3];
+                    }
+                    t[i] = (s0 + s1) + (s2 + s3);
+                }
+                if (lane < 16) {
+                    E* dst = &sm.tbb[wave * 16 * LDT + j];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) dst[i * LDT] = EL::from_f(t[i]);
+                }
+            }
+        }
+        KDA_PHASE_MARK(4); __syncthreads(); KDA_PHASE_MARK(5);  // B3
+
+        // ---- phase E: innovations, output, state update ----------------------------
+        // prefetch the next chunk while this one finishes
+        if (c + 1 < nchunks) load_chunk(c + 1);
+        {
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) X[rt][i] *= sm.beta[16 * rt + 4 * g + i];
+            // (I + A) Vn = diag(b) X by blocks of 16 rows
             f32x4 Vn[NRT];
 #pragma unroll
-            for (int rt = 0; rt < NRT; ++rt) {
-                f32x4 acc = zero4();
+            for (int bb = 0; bb < NRT; ++bb) {
+                f32x4 acc = X[bb];
 #pragma unroll
-                for (int kb = 0; kb <= rt / 2; ++kb)
-                    acc = EL::mma(EL::load(&sm.tb[(16 * rt + r) * LDC + 32 * kb], g), xf[kb], acc);
-                Vn[rt] = acc;
+                for (int kb = 0; kb < bb / 2; ++kb)
+                    acc = EL::mma(EL::load(&sm.ab[(16 * bb + r) * LDC + 32 * kb], g),
+                                  EL::from_acc(Vn[2 * kb], Vn[2 * kb + 1]), acc);
+                if (bb & 1)
+                    acc = EL::mma16(EL::load16(&sm.ab[(16 * bb + r) * LDC + 16 * (bb - 1)], g),
+                                    EL::from_acc16(Vn[bb - 1]), acc);
+                Vn[bb] = EL::mma16(EL::load16(&sm.tbb[(16 * bb + r) * LDT], g), EL::from_acc16(acc), zero4());
             }
             Frag vf[NKC];
 #pragma unroll
             for (int kb = 0; kb < NKC; ++kb) vf[kb] = EL::from_acc(Vn[2 * kb], Vn[2 * kb + 1]);
 
-            // O = Qh S + P Vn
+            // O += P Vn, to the staging tile
 #pragma unroll
-            for (int rt = 0; rt < NRT; ++rt) {
-                f32x4 acc = zero4();
+            for (int kb = 0; kb < NKC; ++kb)
 #pragma unroll
-                for (int kb = 0; kb < NKD; ++kb)
-                    acc = EL::mma(EL::load(&sm.qh[(16 * rt + r) * LDK + 32 * kb], g), sf[kb], acc);
+                for (int rt = 2 * kb; rt < NRT; ++rt)
+                    O[rt] = EL::mma(EL::load(&sm.p[(16 * rt + r) * LDC + 32 * kb], g), vf[kb], O[rt]);
 #pragma unroll
-                for (int kb = 0; kb <= rt / 2; ++kb)
-                    acc = EL::mma(EL::load(&sm.p[(16 * rt + r) * LDC + 32 * kb], g), vf[kb], acc);
+            for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sm.os[(16 * rt + 4 * g + i) * LDV + vc] = EL::from_f(acc[i]);
-            }
+                for (int i = 0; i < 4; ++i) sm.vo[(16 * rt + 4 * g + i) * LDV + vc] = EL::from_f(O[rt][i]);
 
             // S <- diag(gamma) S + Kb^T Vn
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                f32x4 acc = S[ct];
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] *= sm.gam[16 * ct + 4 * g + i];
+                for (int i = 0; i < 4; ++i) S[ct][i] *= sm.gam[16 * ct + 4 * g + i];
 #pragma unroll
-                for (int kb = 0; kb < NKC; ++kb)
-                    acc = EL::mma(EL::load(&sm.kbt[(16 * ct + r) * LDC + 32 * kb], g), vf[kb], acc);
-                S[ct] = acc;
-            }
+            for (int kb = 0; kb < NKC; ++kb)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+                    S[ct] = EL::mma(EL::load(&sm.kbt[(16 * ct + r) * LDC + 32 * kb], g), vf[kb], S[ct]);
         }
-        __syncthreads();                                             // B7
+        KDA_PHASE_MARK(6); __syncthreads(); KDA_PHASE_MARK(7);  // B4
 
-        // ---- phase 4: coalesced store of the output tile ------------------------
+        // ---- phase F: coalesced store of the output tile ---------------------------
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
             const int piece = tid + i * kThreads;
             const int row = piece / VPR, part = piece % VPR;
             if (row < nrow)
                 *reinterpret_cast<uint4*>(out + ((t0 + row) * H + h) * DV + col0 + part * (16 / sizeof(E))) =
-                    *reinterpret_cast<const uint4*>(&sm.os[row * LDV + part * (16 / sizeof(E))]);
+                    *reinterpret_cast<const uint4*>(&sm.vo[row * LDV + part * (16 / sizeof(E))]);
         }
     }
+    KDA_PHASE_MARK(15);
+    KDA_PHASE_FLUSH
 
     // ---- final state: rows = key channels, this wave's 16 columns -----------------
     if (final_state) {

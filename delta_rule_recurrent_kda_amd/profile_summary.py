@@ -1,0 +1,98 @@
+"""Summaries of rocprofv3 result databases (kernel trace and PMC counter runs).
+
+python -m delta_rule_recurrent_kda_amd.profile_summary trace DB [--kernel NAME]
+python -m delta_rule_recurrent_kda_amd.profile_summary traffic FETCH_DB WRITE_DB --calib-bytes N
+    [--kernel NAME] [--out JSON] [--workload W] [--kernel-sha SHA]
+
+`trace` prints per-kernel call counts and durations. `traffic` scales the
+FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) of the scan kernel by the
+ratio the same counters read for a plain device copy of known size, giving
+HBM bytes per launch.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import sqlite3
+import statistics
+import sys
+
+
+def _con(path):
+    return sqlite3.connect(path)
+
+
+def kernel_stats(db: str):
+    con = _con(db)
+    rows = con.execute("select name, total_calls, total_duration, average, percentage from top_kernels").fetchall()
+    out = []
+    for name, calls, total, avg, pct in rows:
+        durs = [r[0] for r in con.execute("select duration from kernels where name = ?", (name,))]
+        out.append({"name": name, "calls": calls, "total_us": total / 1e3 if total > 1e6 else total,
+                    "avg_ns": None if not durs else statistics.mean(durs),
+                    "min_ns": None if not durs else min(durs),
+                    "max_ns": None if not durs else max(durs), "pct": pct})
+    return out
+
+
+def counters(db: str, counter: str):
+    con = _con(db)
+    return con.execute("select dispatch_id, kernel_name, grid_size, value, duration from counters_collection "
+                       "where counter_name = ? order by dispatch_id", (counter,)).fetchall()
+
+
+def _is_copy(name: str) -> bool:
+    return "copyBuffer" in name or "copy_kernel" in name
+
+
+def traffic(fetch_db: str, write_db: str, calib_bytes: int, kernel: str = "kda_fwd_kernel"):
+    f = counters(fetch_db, "FETCH_SIZE")
+    w = counters(write_db, "WRITE_SIZE")
+    kf = [v for _, n, _, v, _ in f if kernel in n]
+    kw = [v for _, n, _, v, _ in w if kernel in n]
+    # the calibration copies are the largest copy dispatches
+    cf = sorted([v for _, n, g, v, _ in f if _is_copy(n)])[-3:]
+    cw = sorted([v for _, n, g, v, _ in w if _is_copy(n)])[-3:]
+    if not kf or not kw or not cf or not cw:
+        raise SystemExit("missing kernel or calibration dispatches in the counter databases")
+    calib_kib = calib_bytes / 1024.0
+    f_scale = calib_kib / statistics.mean(cf)          # true bytes read per counted KiB
+    w_scale = calib_kib / statistics.mean(cw)
+    fetch = statistics.mean(kf) * 1024 * f_scale
+    write = statistics.mean(kw) * 1024 * w_scale
+    return {"fetch_kib_per_dispatch": statistics.mean(kf), "write_kib_per_dispatch": statistics.mean(kw),
+            "copy_fetch_kib": statistics.mean(cf), "copy_write_kib": statistics.mean(cw),
+            "copy_bytes": calib_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
+            "fetch_bytes": fetch, "write_bytes": write, "bytes_per_launch": fetch + write,
+            "dispatches": len(kf)}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("db")
+    c = sub.add_parser("traffic")
+    c.add_argument("fetch_db")
+    c.add_argument("write_db")
+    c.add_argument("--calib-bytes", type=int, required=True)
+    c.add_argument("--kernel", default="kda_fwd_kernel")
+    c.add_argument("--out")
+    c.add_argument("--workload", default="")
+    c.add_argument("--kernel-sha", default="")
+    a = ap.parse_args(argv)
+    if a.cmd == "trace":
+        for k in kernel_stats(a.db):
+            print(f"{k['calls']:6d} calls  avg {k['avg_ns'] / 1e3:10.2f} us  min {k['min_ns'] / 1e3:10.2f} us  "
+                  f"max {k['max_ns'] / 1e3:10.2f} us  {k['pct']:6.2f}%  {k['name'][:110]}")
+    else:
+        rec = traffic(a.fetch_db, a.write_db, a.calib_bytes, a.kernel)
+        rec.update({"workload": a.workload, "kernel_sha": a.kernel_sha})
+        txt = json.dumps(rec, indent=1)
+        print(txt)
+        if a.out:
+            open(a.out, "w").write(txt + "\n")
+
+
+if __name__ == "__main__":
+    sys.exit(main())
