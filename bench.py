@@ -25,6 +25,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
 MFMA_F32_PEAK_TFLOPS = 157.3
 KERNEL_SOURCES = ["delta_rule_recurrent_kda_amd/csrc/kda_fwd.hip",
+                  "delta_rule_recurrent_kda_amd/csrc/kda_fwd_pipe.hip",
+                  "delta_rule_recurrent_kda_amd/csrc/kda_device.h",
                   "delta_rule_recurrent_kda_amd/csrc/kda_internal.h"]
 WORKLOADS = {"tiny": 0, "packed8": 1, "image4": 2, "clip5s": 3, "clip30s": 4}
 CHUNK = 64

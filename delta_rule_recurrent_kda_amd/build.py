@@ -9,8 +9,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = [os.path.join(CSRC, "kda_fwd.hip"), os.path.join(CSRC, "kda_api.cpp")]
-HEADERS = [os.path.join(CSRC, "kda_internal.h"), os.path.join(ROOT, "include", "kda.h")]
+SOURCES = [os.path.join(CSRC, "kda_fwd.hip"), os.path.join(CSRC, "kda_fwd_pipe.hip"),
+           os.path.join(CSRC, "kda_api.cpp")]
+HEADERS = [os.path.join(CSRC, "kda_internal.h"), os.path.join(CSRC, "kda_device.h"),
+           os.path.join(ROOT, "include", "kda.h")]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",

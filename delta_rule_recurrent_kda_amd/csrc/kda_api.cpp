@@ -35,6 +35,14 @@ bool validate_env()
     return e && e[0] == '1';
 }
 
+// KDA_SCAN_VARIANT=sequential selects the one-chunk-at-a-time kernel for bf16 data
+// (the pipelined kernel is the default); fp32 data always uses the sequential one.
+bool sequential_env()
+{
+    const char* e = std::getenv("KDA_SCAN_VARIANT");
+    return e && std::strcmp(e, "sequential") == 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -104,7 +112,8 @@ kda_status kda_forward(const void* q, const void* k, const void* v, const void* 
 
     kda::LaunchArgs a{q, k, v, log_alpha, beta, cu_seqlens, out, final_state, total_tokens,
                       num_seqs, num_heads, d_k, d_v, dtype == KDA_BF16 ? 1 : 0, stream};
-    const hipError_t e = kda::launch_forward(a);
+    const hipError_t e = (a.dtype_bf16 && !sequential_env()) ? kda::launch_forward_pipe(a)
+                                                              : kda::launch_forward_seq(a);
     if (e != hipSuccess) return fail(KDA_E_HIP, "launch failed: %s", hipGetErrorString(e));
     return KDA_OK;
 }

@@ -38,6 +38,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kda_device.h"
 #include "kda_internal.h"
 
 // Optional per-phase cycle accounting hooks (empty in normal builds).
@@ -50,155 +51,10 @@
 namespace kda {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+using namespace dev;
 
 constexpr int kThreads = 256;   // 4 wave64
 constexpr int kBV = 64;         // value columns per workgroup (16 per wave)
-constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
-__device__ __forceinline__ uint16_t f2bf(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-    return uint32_t(f2bf(a)) | (uint32_t(f2bf(b)) << 16);
-}
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// ---------------------------------------------------------------------------
-// element-type traits: storage type E, MFMA fragments and products
-// ---------------------------------------------------------------------------
-template <typename E> struct Elt;
-
-template <> struct Elt<uint16_t> {            // bf16 data
-    struct Frag { uint4 u; };                 // k-block of 32
-    struct Frag16 { uint2 u; };               // k-block of 16
-    static constexpr int kVec = 8;            // elements per 16-byte vector
-    using Vec = uint4;
-    __device__ static float to_f(uint16_t x) { return bf2f(x); }
-    __device__ static uint16_t from_f(float x) { return f2bf(x); }
-    __device__ static Frag load(const uint16_t* row, int g) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(row + 4 * g);
-        const uint2 hi = *reinterpret_cast<const uint2*>(row + 16 + 4 * g);
-        return Frag{make_uint4(lo.x, lo.y, hi.x, hi.y)};
-    }
-    __device__ static Frag16 load16(const uint16_t* row, int g) {
-        return Frag16{*reinterpret_cast<const uint2*>(row + 4 * g)};
-    }
-    __device__ static Frag from_acc(const f32x4& a0, const f32x4& a1) {
-        return Frag{make_uint4(pack2(a0[0], a0[1]), pack2(a0[2], a0[3]), pack2(a1[0], a1[1]),
-                               pack2(a1[2], a1[3]))};
-    }
-    __device__ static Frag16 from_acc16(const f32x4& a0) {
-        return Frag16{make_uint2(pack2(a0[0], a0[1]), pack2(a0[2], a0[3]))};
-    }
-    __device__ static f32x4 mma(const Frag& a, const Frag& b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.u),
-                                                       __builtin_bit_cast(bf16x8, b.u), c, 0, 0, 0);
-    }
-    __device__ static f32x4 mma16(const Frag16& a, const Frag16& b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a.u),
-                                                         __builtin_bit_cast(s16x4, b.u), c, 0, 0, 0);
-    }
-    __device__ static void unpack(const Vec& v, float (&f)[8]) {
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            f[2 * j] = __uint_as_float(w[j] << 16);
-            f[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-        }
-    }
-    // 8 values to a row of LDS whose rows are 8-byte aligned
-    __device__ static void store_vec(uint16_t* dst, const float (&f)[8]) {
-        *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(f[0], f[1]), pack2(f[2], f[3]));
-        *reinterpret_cast<uint2*>(dst + 4) = make_uint2(pack2(f[4], f[5]), pack2(f[6], f[7]));
-    }
-    // n consecutive values (n = 2 or 4)
-    template <int N> __device__ static void store_run(uint16_t* dst, const float* f) {
-        if constexpr (N == 4) *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(f[0], f[1]), pack2(f[2], f[3]));
-        else *reinterpret_cast<uint32_t*>(dst) = pack2(f[0], f[1]);
-    }
-    __device__ static void store4(uint16_t* dst, const f32x4& a) {
-        *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(a[0], a[1]), pack2(a[2], a[3]));
-    }
-};
-
-template <> struct Elt<float> {               // fp32 data
-    struct Frag { float4 lo, hi; };
-    struct Frag16 { float4 lo; };
-    static constexpr int kVec = 4;
-    using Vec = float4;
-    __device__ static float to_f(float x) { return x; }
-    __device__ static float from_f(float x) { return x; }
-    __device__ static Frag load(const float* row, int g) {
-        return Frag{*reinterpret_cast<const float4*>(row + 4 * g),
-                    *reinterpret_cast<const float4*>(row + 16 + 4 * g)};
-    }
-    __device__ static Frag16 load16(const float* row, int g) {
-        return Frag16{*reinterpret_cast<const float4*>(row + 4 * g)};
-    }
-    __device__ static Frag from_acc(const f32x4& a0, const f32x4& a1) {
-        return Frag{make_float4(a0[0], a0[1], a0[2], a0[3]), make_float4(a1[0], a1[1], a1[2], a1[3])};
-    }
-    __device__ static Frag16 from_acc16(const f32x4& a0) {
-        return Frag16{make_float4(a0[0], a0[1], a0[2], a0[3])};
-    }
-    __device__ static f32x4 mma4(const float4& a, const float4& b, f32x4 c) {
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, c, 0, 0, 0);
-        return c;
-    }
-    __device__ static f32x4 mma(const Frag& a, const Frag& b, f32x4 c) {
-        return mma4(a.hi, b.hi, mma4(a.lo, b.lo, c));
-    }
-    __device__ static f32x4 mma16(const Frag16& a, const Frag16& b, f32x4 c) { return mma4(a.lo, b.lo, c); }
-    __device__ static void unpack(const Vec& v, float (&f)[4]) { f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w; }
-    __device__ static void store_vec(float* dst, const float (&f)[4]) {
-        *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
-    }
-    template <int N> __device__ static void store_run(float* dst, const float* f) {
-        if constexpr (N == 4) *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
-        else *reinterpret_cast<float2*>(dst) = make_float2(f[0], f[1]);
-    }
-    __device__ static void store4(float* dst, const f32x4& a) {
-        *reinterpret_cast<float4*>(dst) = make_float4(a[0], a[1], a[2], a[3]);
-    }
-};
-
-// Sum N per-lane values over 2*MASK consecutive lanes (a power of two dividing 64).
-// On return every lane holds the total of value index reduce_index<N, 2*MASK>(lane).
-template <int N, int MASK>
-__device__ __forceinline__ float reduce_scatter(const float* v, int lane)
-{
-    if constexpr (N == 1) {
-        float x = v[0];
-#pragma unroll
-        for (int m = MASK; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-        return x;
-    } else {
-        const bool up = (lane & MASK) != 0;
-        float w[N / 2];
-#pragma unroll
-        for (int j = 0; j < N / 2; ++j) {
-            const float send = up ? v[j] : v[j + N / 2];
-            const float keep = up ? v[j + N / 2] : v[j];
-            w[j] = keep + __shfl_xor(send, MASK);
-        }
-        return reduce_scatter<N / 2, MASK / 2>(w, lane);
-    }
-}
-template <int N, int W>
-__device__ __forceinline__ int reduce_index(int lane)
-{
-    int idx = 0;
-#pragma unroll
-    for (int n = N / 2, m = W / 2; n >= 1; n /= 2, m /= 2)
-        if (lane & m) idx += n;
-    return idx;
-}
 
 // ---------------------------------------------------------------------------
 // shared-memory layout
@@ -290,39 +146,44 @@ __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
     Vec rq[RPT], rk[RPT], rla[RPT];
     uint4 rv[VLD];
     E rb = E(0);
+    // loads are issued unconditionally from a clamped, valid address and masked
+    // where they are consumed (a conditional load makes the compiler wait for the
+    // data right away)
     auto load_chunk = [&](int c) {
+        c = min(c, nchunks - 1);
         const int64_t t0 = seq0 + int64_t(c) * C;
-        const int nrow = int(min<int64_t>(C, len - int64_t(c) * C));
-        const int64_t base = (t0 + rg * RPT) * rstride + int64_t(h) * DK + vcol * VE;
+        const int last = int(min<int64_t>(C, len - int64_t(c) * C)) - 1;
+        const int64_t base = int64_t(h) * DK + vcol * VE;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-            if (rg * RPT + i < nrow) {
-                rq[i] = *reinterpret_cast<const Vec*>(q + base + i * rstride);
-                rk[i] = *reinterpret_cast<const Vec*>(k + base + i * rstride);
-                rla[i] = *reinterpret_cast<const Vec*>(la + base + i * rstride);
-            } else {
-                rq[i] = Vec{}; rk[i] = Vec{}; rla[i] = Vec{};
-            }
+            const int64_t off = (t0 + min(rg * RPT + i, last)) * rstride + base;
+            rq[i] = *reinterpret_cast<const Vec*>(q + off);
+            rk[i] = *reinterpret_cast<const Vec*>(k + off);
+            rla[i] = *reinterpret_cast<const Vec*>(la + off);
         }
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
             const int piece = tid + i * kThreads;
-            const int row = piece / VPR, part = piece % VPR;
-            if (row < nrow)
-                rv[i] = *reinterpret_cast<const uint4*>(v + ((t0 + row) * H + h) * DV + col0 +
-                                                        part * (16 / sizeof(E)));
-            else
-                rv[i] = make_uint4(0, 0, 0, 0);
+            const int row = min(piece / VPR, last), part = piece % VPR;
+            rv[i] = *reinterpret_cast<const uint4*>(v + ((t0 + row) * H + h) * DV + col0 + part * (16 / sizeof(E)));
         }
-        if (tid < C) rb = (tid < nrow) ? beta[(t0 + tid) * H + h] : E(0);
+        rb = beta[(t0 + min(tid % C, last)) * H + h];
     };
-
     if (nchunks > 0) load_chunk(0);
     KDA_PHASE_DECL
 
     for (int c = 0; c < nchunks; ++c) {
         const int64_t t0 = seq0 + int64_t(c) * C;
         const int nrow = int(min<int64_t>(C, len - int64_t(c) * C));
+
+        // rows past the sample's end were loaded from a valid row: zero them
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            if (rg * RPT + i >= nrow) { rq[i] = Vec{}; rk[i] = Vec{}; rla[i] = Vec{}; }
+#pragma unroll
+        for (int i = 0; i < VLD; ++i)
+            if ((tid + i * kThreads) / VPR >= nrow) rv[i] = make_uint4(0, 0, 0, 0);
+        if (tid >= nrow) rb = E(0);
 
         // ---- phase A: sums of log a over row groups and their prefix inside the wave;
         //      exact diagonal q.k ----------------------------------------------------
@@ -371,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
             if ((lane & (NV / RPT - 1)) == 0) sm.diag[rg * RPT + reduce_index<RPT, NV>(lane)] = tot;
         }
         if (tid < C) sm.beta[tid] = EL::to_f(rb);
-        KDA_PHASE_MARK(0); __syncthreads(); KDA_PHASE_MARK(1);  // B1
+        KDA_PHASE_MARK(0); lds_barrier(); KDA_PHASE_MARK(1);  // B1
 
         // ---- phase B: decay factors and decayed operands -------------------------
         // (the V tile goes in only now: the previous chunk's O store read this buffer)
@@ -445,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
                     EL::template store_run<2>(&sm.kbt[(vcol * VE + e) * LDC + rg * RPT + i], kb[e]);
             }
         }
-        KDA_PHASE_MARK(2); __syncthreads(); KDA_PHASE_MARK(3);  // B2
+        KDA_PHASE_MARK(2); lds_barrier(); KDA_PHASE_MARK(3);  // B2
 
         // ---- phase C: P and A tiles, inverse of this wave's diagonal block of I + A,
         //      and the S-dependent products that need neither -------------------------
@@ -559,11 +420,11 @@ __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
                 }
             }
         }
-        KDA_PHASE_MARK(4); __syncthreads(); KDA_PHASE_MARK(5);  // B3
+        KDA_PHASE_MARK(4); lds_barrier(); KDA_PHASE_MARK(5);  // B3
 
         // ---- phase E: innovations, output, state update ----------------------------
         // prefetch the next chunk while this one finishes
-        if (c + 1 < nchunks) load_chunk(c + 1);
+        load_chunk(c + 1);
         {
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt)
@@ -609,7 +470,7 @@ __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
                 for (int ct = 0; ct < NCT; ++ct)
                     S[ct] = EL::mma(EL::load(&sm.kbt[(16 * ct + r) * LDC + 32 * kb], g), vf[kb], S[ct]);
         }
-        KDA_PHASE_MARK(6); __syncthreads(); KDA_PHASE_MARK(7);  // B4
+        KDA_PHASE_MARK(6); lds_barrier(); KDA_PHASE_MARK(7);  // B4
 
         // ---- phase F: coalesced store of the output tile ---------------------------
 #pragma unroll
@@ -661,7 +522,7 @@ size_t smem_bytes(int dtype_bf16, int d_k)
     return d_k == 128 ? sizeof(Smem<float, 128, 32>) : sizeof(Smem<float, 64, 32>);
 }
 
-hipError_t launch_forward(const LaunchArgs& a)
+hipError_t launch_forward_seq(const LaunchArgs& a)
 {
     if (a.dtype_bf16) {
         if (a.d_k == 128) return launch_t<uint16_t, 128, 64>(a);

@@ -24,10 +24,16 @@ struct LaunchArgs {
     hipStream_t stream;
 };
 
-// Enqueue the scan. Arguments are already validated.
-hipError_t launch_forward(const LaunchArgs& a);
+// Scan variants (arguments already validated).
+// Sequential: 4 waves per (sample, head, 64-column tile), 64-token chunks for bf16
+// and 32-token chunks for fp32, one chunk at a time.
+hipError_t launch_forward_seq(const LaunchArgs& a);
+// Pipelined (bf16 only): 8 waves, 32-token chunks, the decayed operands of the
+// next chunk computed while the current chunk's products run.
+hipError_t launch_forward_pipe(const LaunchArgs& a);
 
-// LDS bytes one workgroup of the scan kernel uses.
+// LDS bytes one workgroup uses.
 size_t smem_bytes(int dtype_bf16, int d_k);
+size_t smem_bytes_pipe(int d_k);
 
 }  // namespace kda

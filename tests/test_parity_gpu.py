@@ -123,3 +123,14 @@ def test_named_config_full(cfg):
 def test_config4_sampled_heads():
     # full 189,272-token launch; the oracle recomputes three heads in full
     _check(inputs.config(4), heads=[0, 7, 15])
+
+
+@pytest.mark.parametrize("case", ["packed8", "ragged_d64"])
+def test_sequential_variant(monkeypatch, case):
+    # the one-chunk-at-a-time bf16 kernel stays selectable; it must meet the same bar
+    monkeypatch.setenv("KDA_SCAN_VARIANT", "sequential")
+    if case == "packed8":
+        _check(inputs.config(1), label="packed8 sequential")
+    else:
+        spec = inputs.KdaSpec("ragged_d64_seq", (129, 3, 64, 200, 1), 3, 64, 64, "bf16", (0.001, 0.1), 4343)
+        _check(spec, label="ragged d64 sequential")
