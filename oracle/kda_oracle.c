@@ -33,6 +33,12 @@
  *
  * Layout: q, k, log_alpha [T][H][dk]; v, out [T][H][dv]; beta [T][H];
  * cu_seqlens int32 [N+1]; final_state [N][H][dk][dv] (rows = key channels).
+ *
+ * kda_oracle_forward_from additionally takes initial_state [N][H][dk][dv]: the
+ * state a sample starts from in place of 0, for continuing a scan from a retained
+ * state (the per-head state is all a sample carries forward: explainer page "What
+ * O(N) buys in memory and latency"; paper Sec. 5 efficiency study, Fig. 18,
+ * roll-out-cache setting). Everything else is the same recurrence.
  */
 #include <math.h>
 #include <pthread.h>
@@ -43,6 +49,7 @@
 typedef struct {
     const double *q, *k, *v, *log_alpha, *beta;
     const int32_t *cu_seqlens;
+    const double *initial_state;   /* NULL = S_0 = 0 */
     int32_t n_seqs, H, dk, dv;
     const uint8_t *head_mask;   /* NULL = all heads */
     double *out, *final_state;
@@ -61,6 +68,8 @@ static int scan_unit(oracle_job *job, int32_t n, int32_t h)
     double *p = malloc(sizeof(double) * dv);
     double *u = malloc(sizeof(double) * dv);
     if (!S || !p || !u) { free(S); free(p); free(u); return -1; }
+    if (job->initial_state)
+        memcpy(S, job->initial_state + ((size_t)n * H + h) * dk * dv, sizeof(double) * dk * dv);
 
     for (int64_t t = t0; t < t1; ++t) {
         const double *kt = job->k + (t * H + h) * dk;
@@ -128,14 +137,15 @@ static void *worker(void *arg)
 /*
  * Run the recurrence for every (sequence, head) unit, or for the heads whose
  * head_mask entry is nonzero. out rows of skipped heads are left untouched.
- * threads <= 0 means one thread. Returns 0 on success, -1 on bad arguments or
- * allocation failure.
+ * initial_state NULL means every sample starts from 0. threads <= 0 means one
+ * thread. Returns 0 on success, -1 on bad arguments or allocation failure.
  */
-int kda_oracle_forward(const double *q, const double *k, const double *v,
-                       const double *log_alpha, const double *beta,
-                       const int32_t *cu_seqlens, int32_t n_seqs, int32_t H,
-                       int32_t dk, int32_t dv, const uint8_t *head_mask,
-                       double *out, double *final_state, int32_t threads)
+int kda_oracle_forward_from(const double *q, const double *k, const double *v,
+                            const double *log_alpha, const double *beta,
+                            const int32_t *cu_seqlens, const double *initial_state,
+                            int32_t n_seqs, int32_t H, int32_t dk, int32_t dv,
+                            const uint8_t *head_mask, double *out, double *final_state,
+                            int32_t threads)
 {
     if (!cu_seqlens || n_seqs < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
     if (cu_seqlens[0] != 0) return -1;
@@ -148,6 +158,7 @@ int kda_oracle_forward(const double *q, const double *k, const double *v,
     job.q = q; job.k = k; job.v = v; job.log_alpha = log_alpha; job.beta = beta;
     job.cu_seqlens = cu_seqlens; job.n_seqs = n_seqs; job.H = H; job.dk = dk; job.dv = dv;
     job.head_mask = head_mask; job.out = out; job.final_state = final_state;
+    job.initial_state = initial_state;
     pthread_mutex_init(&job.lock, NULL);
 
     if (threads < 1) threads = 1;
@@ -160,4 +171,15 @@ int kda_oracle_forward(const double *q, const double *k, const double *v,
     for (int i = 0; i < started; ++i) pthread_join(tid[i], NULL);
     pthread_mutex_destroy(&job.lock);
     return job.failed ? -1 : 0;
+}
+
+/* The scan from zero states. */
+int kda_oracle_forward(const double *q, const double *k, const double *v,
+                       const double *log_alpha, const double *beta,
+                       const int32_t *cu_seqlens, int32_t n_seqs, int32_t H,
+                       int32_t dk, int32_t dv, const uint8_t *head_mask,
+                       double *out, double *final_state, int32_t threads)
+{
+    return kda_oracle_forward_from(q, k, v, log_alpha, beta, cu_seqlens, NULL, n_seqs, H, dk, dv,
+                                   head_mask, out, final_state, threads);
 }

@@ -14,8 +14,9 @@ def transition(k, alpha, beta):
     return (np.eye(dk) - beta * np.outer(k, k)) @ np.diag(alpha)
 
 
-def scan_matrices(q, k, v, log_alpha, beta, cu_seqlens):
-    """Dense-matrix recurrence. Shapes as the oracle: [T, H, d]."""
+def scan_matrices(q, k, v, log_alpha, beta, cu_seqlens, initial_state=None):
+    """Dense-matrix recurrence. Shapes as the oracle: [T, H, d]; initial_state
+    [N, H, dk, dv] or None (zero states)."""
     T, H, dk = k.shape
     dv = v.shape[2]
     N = len(cu_seqlens) - 1
@@ -23,7 +24,7 @@ def scan_matrices(q, k, v, log_alpha, beta, cu_seqlens):
     fs = np.zeros((N, H, dk, dv))
     for n in range(N):
         for h in range(H):
-            S = np.zeros((dk, dv))
+            S = np.zeros((dk, dv)) if initial_state is None else np.array(initial_state[n, h], float)
             for t in range(cu_seqlens[n], cu_seqlens[n + 1]):
                 M = transition(k[t, h], np.exp(log_alpha[t, h]), beta[t, h])
                 S = M @ S + beta[t, h] * np.outer(k[t, h], v[t, h])
@@ -43,3 +44,13 @@ def final_state_unrolled(k, v, log_alpha, beta, t0, t1, h):
             P = Ms[t - t0] @ P
         S += P @ (beta[s, h] * np.outer(k[s, h], v[s, h]))
     return S
+
+
+def transition_product(k, log_alpha, beta, t0, t1, h):
+    """M_{t1-1} ... M_{t0}: the linear part of the map from the state before t0 to
+    the state after t1 - 1."""
+    dk = k.shape[2]
+    P = np.eye(dk)
+    for t in range(t0, t1):
+        P = transition(k[t, h], np.exp(log_alpha[t, h]), beta[t, h]) @ P
+    return P

@@ -257,7 +257,47 @@ def pin_nan_confined(fwd, seed=11):
     assert np.isnan(fs[1, 1]).any() and not np.isnan(fs[[0, 2]]).any() and not np.isnan(fs[1, 0]).any()
 
 
+# -- P14: a retained state continues the scan (initial_state) -------------------
+# The per-head state is all a sample carries forward (explainer page, "What O(N)
+# buys in memory and latency"); starting from S_0 the state after the sample is the
+# affine map S_L = Phi S_0 + S_L(0) with Phi the product of the transition matrices.
+def pin_initial_state(fwd, seed=12):
+    rng = np.random.default_rng(seed)
+    lens, H, dk, dv = (9, 0, 14), 2, 5, 4
+    q, k, v, la, b, cu = _rand_case(rng, lens, H, dk, dv)
+    N = len(lens)
+    s0 = rng.standard_normal((N, H, dk, dv))
+    out, fs = fwd(q, k, v, la, b, cu, initial_state=s0)
+    ob, fb = brute.scan_matrices(q, k, v, la, b, cu, initial_state=s0)
+    assert _rel(out, ob) < 1e-12, _rel(out, ob)
+    assert _rel(fs, fb) < 1e-12, _rel(fs, fb)
+    # affine in S_0: S_L(S_0) - S_L(0) = Phi S_0; an empty sample returns S_0 itself
+    _, f0 = fwd(q, k, v, la, b, cu)
+    for n in range(N):
+        for h in range(H):
+            phi = brute.transition_product(k, la, b, cu[n], cu[n + 1], h)
+            assert np.allclose(fs[n, h] - f0[n, h], phi @ s0[n, h], rtol=1e-11, atol=1e-12)
+    assert np.array_equal(fs[1], s0[1])
+    # zero initial state is the plain scan, bit for bit
+    o2, f2 = fwd(q, k, v, la, b, cu, initial_state=np.zeros_like(s0))
+    o1, f1 = fwd(q, k, v, la, b, cu)
+    assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
+
+
+# -- P15: splitting a sample and carrying the state gives the one-pass result ---
+def pin_split_composition(fwd, seed=13):
+    rng = np.random.default_rng(seed)
+    L, H, dk, dv = 37, 2, 6, 3
+    q, k, v, la, b, cu = _rand_case(rng, (L,), H, dk, dv)
+    out, fs = fwd(q, k, v, la, b, cu)
+    for a in (1, 16, 36):
+        oa, fa = fwd(q[:a], k[:a], v[:a], la[:a], b[:a], np.array([0, a], np.int32))
+        ob, fb = fwd(q[a:], k[a:], v[a:], la[a:], b[a:], np.array([0, L - a], np.int32),
+                     initial_state=fa)
+        assert np.array_equal(np.concatenate([oa, ob]), out) and np.array_equal(fb, fs)
+
+
 ALL_PINS = [pin_worked_example, pin_brute_force, pin_beta_zero, pin_exact_recall, pin_half_life,
             pin_reset_and_packing, pin_write_readback, pin_column_separability, pin_linearity,
             pin_channel_equivariance, pin_scalar_closed_form, pin_lms_step, pin_contraction,
-            pin_nan_confined]
+            pin_nan_confined, pin_initial_state, pin_split_composition]

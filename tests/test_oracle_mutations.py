@@ -17,6 +17,7 @@ MUTANTS = {
     "beta_on_write_only": ("u[j] = bt * (vt[j] - p[j]);", "u[j] = bt * vt[j] - p[j];"),
     "no_reset": ("const int64_t t0 = job->cu_seqlens[n], t1", "const int64_t t0 = 0, t1"),
     "readout_key_not_query": ("const double qc = qt[c];", "const double qc = kt[c];"),
+    "initial_state_ignored": ("    if (job->initial_state)\n", "    if (0)\n"),
     "decay_after_retrieve": (
         "        /* u = beta_t (v_t - p) */\n",
         "        for (int32_t c = 0; c < dk; ++c) for (int32_t j = 0; j < dv; ++j) p[j] += 0.0 * c;\n"
