@@ -5,7 +5,10 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "../../include/kda.h"
@@ -35,13 +38,77 @@ bool validate_env()
     return e && e[0] == '1';
 }
 
-// KDA_SCAN_VARIANT=sequential selects the one-chunk-at-a-time kernel for bf16 data
-// (the pipelined kernel is the default); fp32 data always uses the sequential one.
-bool sequential_env()
+// KDA_SCAN_VARIANT selects the bf16 scan: "wy" (default; a prep kernel over all
+// chunks and a chain kernel, with a workspace), "pipe" (one software-pipelined
+// kernel) or "sequential" (one chunk at a time). fp32 data always uses the
+// sequential kernel.
+enum class Variant { Wy, Pipe, Sequential };
+Variant variant_env()
 {
     const char* e = std::getenv("KDA_SCAN_VARIANT");
-    return e && std::strcmp(e, "sequential") == 0;
+    if (e && std::strcmp(e, "sequential") == 0) return Variant::Sequential;
+    if (e && std::strcmp(e, "pipe") == 0) return Variant::Pipe;
+    return Variant::Wy;
 }
+
+// ---- per-kernel event timing (diagnostics) ----
+struct Timing : kda::TimingHook {
+    std::mutex mu;
+    bool on = false;
+    std::vector<hipEvent_t> free_events;
+    struct Rec { std::string name; hipEvent_t start, stop; };
+    std::vector<Rec> recs;
+    std::string cur;
+    hipEvent_t cur_start = nullptr;
+
+    hipEvent_t get() {
+        if (!free_events.empty()) {
+            hipEvent_t e = free_events.back();
+            free_events.pop_back();
+            return e;
+        }
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        return e;
+    }
+    void begin(const char* kernel, hipStream_t stream) override {
+        cur = kernel;
+        cur_start = get();
+        if (cur_start) hipEventRecord(cur_start, stream);
+    }
+    void end(hipStream_t stream) override {
+        hipEvent_t stop = get();
+        if (!cur_start || !stop) return;
+        hipEventRecord(stop, stream);
+        recs.push_back({cur, cur_start, stop});
+        cur_start = nullptr;
+    }
+};
+Timing g_timing;
+
+// The device's default stream-ordered pool keeps freed workspace for reuse instead of
+// returning it to the driver at every synchronisation.
+bool prepare_pool(int dev)
+{
+    static std::mutex mu;
+    static std::vector<bool> done;
+    std::lock_guard<std::mutex> lk(mu);
+    if (dev < 0) return false;
+    if (size_t(dev) >= done.size()) done.resize(size_t(dev) + 1, false);
+    if (done[size_t(dev)]) return true;
+    hipMemPool_t pool = nullptr;
+    if (hipDeviceGetDefaultMemPool(&pool, dev) != hipSuccess) return false;
+    uint64_t thr = UINT64_MAX;
+    if (hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr) != hipSuccess) return false;
+    done[size_t(dev)] = true;
+    return true;
+}
+
+kda_status check_args(const void* q, const void* k, const void* v, const void* log_alpha,
+                      const void* beta, const int32_t* cu_seqlens, void* out, float* final_state,
+                      const float* initial_state, int64_t total_tokens, int32_t num_seqs,
+                      int32_t num_heads, int32_t d_k, int32_t d_v, kda_dtype dtype, hipStream_t stream);
+kda_status run(const kda::LaunchArgs& a);
 
 }  // namespace
 
@@ -72,6 +139,84 @@ kda_status kda_forward(const void* q, const void* k, const void* v, const void* 
                        int32_t d_v, kda_dtype dtype, hipStream_t stream)
 {
     g_last_error.clear();
+    const kda_status st = check_args(q, k, v, log_alpha, beta, cu_seqlens, out, final_state, nullptr,
+                                     total_tokens, num_seqs, num_heads, d_k, d_v, dtype, stream);
+    if (st != KDA_OK || num_seqs == 0) return st;
+    return run(kda::LaunchArgs{q, k, v, log_alpha, beta, cu_seqlens, out, final_state, nullptr,
+                               total_tokens, num_seqs, num_heads, d_k, d_v, dtype == KDA_BF16 ? 1 : 0,
+                               stream});
+}
+
+kda_status kda_forward_from_state(const void* q, const void* k, const void* v, const void* log_alpha,
+                                  const void* beta, const int32_t* cu_seqlens,
+                                  const float* initial_state, void* out, float* final_state,
+                                  int64_t total_tokens, int32_t num_seqs, int32_t num_heads,
+                                  int32_t d_k, int32_t d_v, kda_dtype dtype, hipStream_t stream)
+{
+    g_last_error.clear();
+    const kda_status st = check_args(q, k, v, log_alpha, beta, cu_seqlens, out, final_state,
+                                     initial_state, total_tokens, num_seqs, num_heads, d_k, d_v, dtype, stream);
+    if (st != KDA_OK || num_seqs == 0) return st;
+    return run(kda::LaunchArgs{q, k, v, log_alpha, beta, cu_seqlens, out, final_state, initial_state,
+                               total_tokens, num_seqs, num_heads, d_k, d_v, dtype == KDA_BF16 ? 1 : 0,
+                               stream});
+}
+
+kda_status kda_timing_enable(int32_t on)
+{
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    g_timing.on = on != 0;
+    return KDA_OK;
+}
+
+kda_status kda_timing_read(const char* kernel, int32_t* launches, double* total_ms)
+{
+    g_last_error.clear();
+    if (!kernel || !launches || !total_ms) return fail(KDA_E_NULL, "kda_timing_read: NULL argument");
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    int32_t n = 0;
+    double ms = 0.0;
+    std::vector<Timing::Rec> keep;
+    for (auto& rec : g_timing.recs) {
+        if (rec.name != kernel) {
+            keep.push_back(rec);
+            continue;
+        }
+        hipError_t e = hipEventSynchronize(rec.stop);
+        float t = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&t, rec.start, rec.stop);
+        if (e != hipSuccess) {
+            g_timing.recs.clear();
+            return fail(KDA_E_HIP, "kda_timing_read: %s", hipGetErrorString(e));
+        }
+        ++n;
+        ms += t;
+        g_timing.free_events.push_back(rec.start);
+        g_timing.free_events.push_back(rec.stop);
+    }
+    g_timing.recs.swap(keep);
+    *launches = n;
+    *total_ms = ms;
+    return KDA_OK;
+}
+
+size_t kda_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads, int32_t d_k,
+                           int32_t d_v, kda_dtype dtype)
+{
+    if (dtype != KDA_BF16 || total_tokens < 0 || num_seqs <= 0 || num_heads < 1) return 0;
+    if ((d_k != 64 && d_k != 128) || (d_v != 64 && d_v != 128)) return 0;
+    return kda::wy_workspace_bytes(total_tokens, num_seqs, num_heads, d_k, d_v);
+}
+
+}  // extern "C"
+
+namespace {
+
+kda_status check_args(const void* q, const void* k, const void* v, const void* log_alpha,
+                      const void* beta, const int32_t* cu_seqlens, void* out, float* final_state,
+                      const float* initial_state, int64_t total_tokens, int32_t num_seqs,
+                      int32_t num_heads, int32_t d_k, int32_t d_v, kda_dtype dtype, hipStream_t stream)
+{
     if (dtype != KDA_F32 && dtype != KDA_BF16)
         return fail(KDA_E_DTYPE, "dtype %d is neither KDA_F32 nor KDA_BF16", int(dtype));
     if (total_tokens < 0 || num_seqs < 0 || num_heads < 1)
@@ -86,22 +231,26 @@ kda_status kda_forward(const void* q, const void* k, const void* v, const void* 
     if (!cu_seqlens) return fail(KDA_E_NULL, "cu_seqlens is NULL");
     if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !out))
         return fail(KDA_E_NULL, "a tensor pointer is NULL");
-    const void* ptrs[] = {q, k, v, log_alpha, beta, cu_seqlens, out, final_state};
-    const char* names[] = {"q", "k", "v", "log_alpha", "beta", "cu_seqlens", "out", "final_state"};
-    for (int i = 0; i < 8; ++i)
+    const void* ptrs[] = {q, k, v, log_alpha, beta, cu_seqlens, out, final_state, initial_state};
+    const char* names[] = {"q", "k", "v", "log_alpha", "beta", "cu_seqlens", "out", "final_state",
+                           "initial_state"};
+    for (int i = 0; i < 9; ++i)
         if (ptrs[i] && !aligned16(ptrs[i]))
             return fail(KDA_E_ALIGN, "%s is not 16-byte aligned", names[i]);
     if (out && (out == q || out == k || out == v || out == log_alpha || out == beta))
         return fail(KDA_E_SHAPE, "out aliases an input");
+    if (initial_state && final_state && static_cast<const void*>(initial_state) == final_state)
+        return fail(KDA_E_SHAPE, "final_state aliases initial_state");
     if (num_seqs == 0) return KDA_OK;
+    if (initial_state && (dtype != KDA_BF16 || variant_env() != Variant::Wy))
+        return fail(KDA_E_UNSUPPORTED, "initial_state is supported for bf16 data on the default scan");
 
     if (validate_env()) {
         std::vector<int32_t> h(size_t(num_seqs) + 1);
         hipError_t e = hipMemcpyAsync(h.data(), cu_seqlens, h.size() * sizeof(int32_t),
                                       hipMemcpyDeviceToHost, stream);
         if (e == hipSuccess) e = hipStreamSynchronize(stream);
-        if (e != hipSuccess)
-            return fail(KDA_E_HIP, "reading cu_seqlens: %s", hipGetErrorString(e));
+        if (e != hipSuccess) return fail(KDA_E_HIP, "reading cu_seqlens: %s", hipGetErrorString(e));
         if (h[0] != 0) return fail(KDA_E_SEQLENS, "cu_seqlens[0] = %d, expected 0", h[0]);
         for (int32_t n = 0; n < num_seqs; ++n)
             if (h[n + 1] < h[n]) return fail(KDA_E_SEQLENS, "cu_seqlens decreases at %d", n);
@@ -109,13 +258,36 @@ kda_status kda_forward(const void* q, const void* k, const void* v, const void* 
             return fail(KDA_E_SEQLENS, "cu_seqlens[N] = %d, expected total_tokens = %lld",
                         h[num_seqs], (long long)total_tokens);
     }
+    return KDA_OK;
+}
 
-    kda::LaunchArgs a{q, k, v, log_alpha, beta, cu_seqlens, out, final_state, total_tokens,
-                      num_seqs, num_heads, d_k, d_v, dtype == KDA_BF16 ? 1 : 0, stream};
-    const hipError_t e = (a.dtype_bf16 && !sequential_env()) ? kda::launch_forward_pipe(a)
-                                                              : kda::launch_forward_seq(a);
+kda_status run(const kda::LaunchArgs& a)
+{
+    std::unique_lock<std::mutex> lk(g_timing.mu);
+    kda::TimingHook* th = g_timing.on ? &g_timing : nullptr;
+    if (!th) lk.unlock();
+    const Variant var = a.dtype_bf16 ? variant_env() : Variant::Sequential;
+    hipError_t e = hipSuccess;
+    if (var == Variant::Wy) {
+        int dev = -1;
+        e = hipGetDevice(&dev);
+        if (e != hipSuccess || !prepare_pool(dev))
+            return fail(KDA_E_HIP, "setting up the workspace pool: %s", hipGetErrorString(e));
+        const size_t bytes = kda::wy_workspace_bytes(a.total_tokens, a.num_seqs, a.num_heads, a.d_k, a.d_v);
+        void* ws = nullptr;
+        e = hipMallocAsync(&ws, bytes, a.stream);
+        if (e != hipSuccess)
+            return fail(KDA_E_HIP, "workspace of %zu bytes: %s", bytes, hipGetErrorString(e));
+        e = kda::launch_forward_wy(a, ws, th);
+        const hipError_t ef = hipFreeAsync(ws, a.stream);
+        if (e == hipSuccess) e = ef;
+    } else {
+        if (th) th->begin("scan", a.stream);
+        e = var == Variant::Pipe ? kda::launch_forward_pipe(a) : kda::launch_forward_seq(a);
+        if (th) th->end(a.stream);
+    }
     if (e != hipSuccess) return fail(KDA_E_HIP, "launch failed: %s", hipGetErrorString(e));
     return KDA_OK;
 }
 
-}  // extern "C"
+}  // namespace

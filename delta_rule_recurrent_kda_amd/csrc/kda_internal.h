@@ -15,6 +15,7 @@ struct LaunchArgs {
     const int32_t* cu_seqlens;
     void* out;
     float* final_state;
+    const float* init_state;        // [num_seqs][num_heads][d_k][d_v] fp32 or NULL (zero state)
     int64_t total_tokens;
     int32_t num_seqs;
     int32_t num_heads;
@@ -31,6 +32,20 @@ hipError_t launch_forward_seq(const LaunchArgs& a);
 // Pipelined (bf16 only): 8 waves, 32-token chunks, the decayed operands of the
 // next chunk computed while the current chunk's products run.
 hipError_t launch_forward_pipe(const LaunchArgs& a);
+
+// Records a pair of HIP events on the launch stream around each kernel launch
+// (diagnostic per-kernel timing; NULL when off).
+struct TimingHook {
+    virtual void begin(const char* kernel, hipStream_t stream) = 0;
+    virtual void end(hipStream_t stream) = 0;
+    virtual ~TimingHook() = default;
+};
+
+// Two-kernel path (bf16 only): a prep kernel over all (64-token chunk, head) pairs
+// writes the chunk operands to `workspace`, a chain kernel carries the state.
+// `workspace` must hold wy_workspace_bytes(...) bytes, 256-byte aligned.
+hipError_t launch_forward_wy(const LaunchArgs& a, void* workspace, TimingHook* th);
+size_t wy_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads, int d_k, int d_v);
 
 // LDS bytes one workgroup uses.
 size_t smem_bytes(int dtype_bf16, int d_k);

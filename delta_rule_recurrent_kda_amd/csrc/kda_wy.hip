@@ -1,0 +1,641 @@
+// kda_wy.hip -- two-kernel chunkwise KDA forward scan for bf16 data (gfx950).
+//
+// Recurrence (Chimera, arXiv 2607.28611: update printed in the explainer page,
+// "One stream, three mechanisms, no positions"; state reset at every packed
+// sample, paper Sec. 3 KDA paragraph), per (sample, head):
+//     S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t v_t^T,   o_t = S_t^T q_t.
+// Chunkwise form over chunks of C = 64 tokens (G = inclusive cumsum of log a over
+// the chunk's rows, per key channel; gamma = exp(G of the last row)):
+//     Qh = Q e^G, Kh = K e^G, Kc = K e^-G, Kb = K e^(G_last - G)
+//     A = StrictLower(diag(b) Kh Kc^T),  (I + A) [W | U] = diag(b) [Kh | V]
+//     Vn = U - W S,  O = Qh S + LowerIncl(Qh Kc^T) Vn,  S <- diag(gamma) S + Kb^T Vn
+// Every term except the last three lines is independent of S, so it is computed
+// for all (chunk, head) pairs at once by the prep kernel, which writes the chunk's
+// operands to a workspace in the exact MFMA fragment order the chain kernel reads.
+// The chain kernel carries S through the chunks of one sample: three groups of
+// products per chunk and no solve on the serial path.
+//
+// Fragment conventions are those of kda_device.h. With the 16x16x16 product, an
+// accumulator tile (rows 4g+s, column r) is the B operand of the same matrix and
+// the A operand of its transpose; a product with the identity as B operand
+// transposes a tile exactly (bf16 values times one, fp32 accumulation).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+using namespace dev;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 16 bytes as a native vector:
+                                                               // copies stay in registers
+constexpr int kWC = 64;            // chunk rows
+constexpr int kWThreads = 256;     // 4 wave64
+constexpr uint16_t kOne = 0x3F80;  // bf16 1.0
+
+// Workspace record of one (chunk, head), in bf16 units.
+template <int DK, int DV> struct WyLayout {
+    static constexpr int NKB = DK / 32;    // k-blocks over key channels
+    static constexpr int NCT = DK / 16;    // 16-wide key channel tiles
+    static constexpr int NVT = DV / 16;    // 16-wide value column tiles
+    static constexpr int W = 0;                        // -W: [rt 4][kb NKB][lane 64][8], token rows
+    static constexpr int Q = W + 4 * NKB * 512;        // Qh: [rt 4][kb NKB][64][8], token rows
+    static constexpr int K = Q + 4 * NKB * 512;        // Kb^T: [ct NCT][kb 2][64][8], key channel rows
+    static constexpr int P = K + NCT * 2 * 512;        // P: [rt 4][kb 2][64][8], token rows
+    static constexpr int G = P + 8 * 512;              // gamma: DK fp32
+    static constexpr int SHARED = G + 2 * DK;          // operands every value tile reads
+    static constexpr int U = SHARED;                   // U: [vt NVT][rt 4][64][4], accumulator layout
+    static constexpr int UTILE = 4 * 1024;             // U of one 64-column value tile
+    static constexpr int TOTAL = U + NVT * 1024;
+    static_assert((SHARED * 2) % 16 == 0 && (TOTAL * 2) % 16 == 0, "16-byte sections");
+};
+
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+    return make_uint2(pack2(a, b), pack2(c, d));
+}
+__device__ __forceinline__ uint2 pack4(const f32x4& x) { return pack4(x[0], x[1], x[2], x[3]); }
+__device__ __forceinline__ void unpack4(const uint2& u, float (&f)[4]) {
+    f[0] = __uint_as_float(u.x << 16);
+    f[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    f[2] = __uint_as_float(u.y << 16);
+    f[3] = __uint_as_float(u.y & 0xFFFF0000u);
+}
+
+// ---------------------------------------------------------------------------
+// plan: chunk_off[n] = number of chunks of the samples before n (one workgroup)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void kda_wy_plan_kernel(const int32_t* __restrict__ cu,
+                                                           int32_t* __restrict__ chunk_off,
+                                                           int num_seqs, int64_t total_tokens)
+{
+    __shared__ int32_t part[1024];
+    const int tid = threadIdx.x;
+    int32_t carry = 0;
+    for (int base = 0; base < num_seqs; base += 1024) {
+        const int n = base + tid;
+        int32_t cnt = 0;
+        if (n < num_seqs) {
+            const int64_t s0 = min<int64_t>(max<int64_t>(cu[n], 0), total_tokens);
+            const int64_t s1 = min<int64_t>(max<int64_t>(cu[n + 1], s0), total_tokens);
+            cnt = int32_t((s1 - s0 + kWC - 1) / kWC);
+        }
+        part[tid] = cnt;
+        __syncthreads();
+        for (int d = 1; d < 1024; d <<= 1) {          // inclusive scan
+            const int32_t add = tid >= d ? part[tid - d] : 0;
+            __syncthreads();
+            part[tid] += add;
+            __syncthreads();
+        }
+        if (n < num_seqs) chunk_off[n + 1] = carry + part[tid];
+        carry += part[1023];
+        __syncthreads();
+    }
+    if (tid == 0) chunk_off[0] = 0;
+}
+
+// clamped sample bounds, so that malformed offsets never address outside the tokens
+__device__ __forceinline__ void sample_bounds(const int32_t* cu, int n, int64_t T, int64_t& s0, int64_t& s1) {
+    s0 = min<int64_t>(max<int64_t>(cu[n], 0), T);
+    s1 = min<int64_t>(max<int64_t>(cu[n + 1], s0), T);
+}
+
+// ---------------------------------------------------------------------------
+// prep: the S-independent operands of one (chunk, head)
+// ---------------------------------------------------------------------------
+template <int DK> struct PrepSmem {
+    static constexpr int LDK = DK + 8;       // token rows, 16-byte aligned
+    alignas(16) uint16_t qk[kWC * LDK];      // raw q; each wave then writes Kc hi over its own rows
+    alignas(16) uint16_t kcl[kWC * LDK];     // Kc, lo part
+    alignas(16) uint16_t kr[kWC * LDK];      // raw k; each wave then writes Kh over its own rows
+    alignas(16) uint16_t lr[kWC * LDK];      // raw log a
+    alignas(16) uint16_t aoff[6 * 256];      // -A blocks (i, j), j < i: 16x16x16 A fragments [blk][lane][4]
+    alignas(16) float at[4 * 16 * 20];       // strictly lower diagonal blocks of A, rows; then (I + A_ii)^-1
+    alignas(16) float beta[kWC];
+    alignas(16) float gam[DK];               // exp(G) of the chunk's last row
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kWThreads) void kda_wy_prep_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ la, const uint16_t* __restrict__ beta, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ chunk_off, uint16_t* __restrict__ ws, int num_seqs, int H,
+    int64_t total_tokens, int max_chunks)
+{
+    using EL = Elt<uint16_t>;
+    using Frag = EL::Frag;
+    using Frag16 = EL::Frag16;
+    using Lay = WyLayout<DK, DV>;
+    using Sm = PrepSmem<DK>;
+    constexpr int NKB = Lay::NKB, NCT = Lay::NCT, NVT = Lay::NVT;
+    constexpr int CW = NCT / 4, VW = NVT / 4;   // key channel / value tiles per wave
+    constexpr int LDK = Sm::LDK;
+    static_assert(CW >= 1 && VW >= 1, "d_k and d_v must be multiples of 64");
+
+    __shared__ Sm sm;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, g = lane >> 4;
+
+    const int c = blockIdx.x, h = blockIdx.y;
+    const int ntot = min(chunk_off[num_seqs], max_chunks);
+    if (c >= ntot) return;
+    int lo = 0, hi = num_seqs;                  // chunk_off[lo] <= c < chunk_off[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (chunk_off[mid] <= c) lo = mid; else hi = mid;
+    }
+    int64_t s0, s1;
+    sample_bounds(cu, lo, total_tokens, s0, s1);
+    const int64_t t0 = s0 + int64_t(c - chunk_off[lo]) * kWC;
+    const int nrow = int(min<int64_t>(kWC, s1 - t0));   // >= 1
+    uint16_t* rec = ws + (int64_t(c) * H + h) * Lay::TOTAL;
+    auto grow = [&](int row) { return (t0 + min(row, nrow - 1)) * H + h; };   // clamped token row
+
+    // ===== stage: raw q, k, log a rows of the chunk to LDS (zero past the sample's
+    //       end), this wave's value columns and the gates to registers; every load is
+    //       issued before the first wait =====
+    constexpr int PPR = DK / 8;                 // 16-byte pieces per row
+    constexpr int NPC = kWC * PPR / kWThreads;  // pieces per thread and array
+    static_assert(kWC * PPR % kWThreads == 0, "staging split");
+    u32x4 rq[NPC], rk[NPC], rl[NPC];
+#pragma unroll
+    for (int j = 0; j < NPC; ++j) {
+        const int p = tid + j * kWThreads, row = p / PPR, col = (p % PPR) * 8;
+        const int64_t off = grow(row) * DK + col;
+        rq[j] = *reinterpret_cast<const u32x4*>(q + off);
+        rk[j] = *reinterpret_cast<const u32x4*>(k + off);
+        rl[j] = *reinterpret_cast<const u32x4*>(la + off);
+    }
+    uint2 vraw[VW][4];
+#pragma unroll
+    for (int u = 0; u < VW; ++u)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+            vraw[u][rt] = *reinterpret_cast<const uint2*>(v + grow(16 * rt + r) * DV + 16 * (VW * wave + u) + 4 * g);
+    const uint16_t braw = beta[grow(tid & 63)];
+#pragma unroll
+    for (int j = 0; j < NPC; ++j) {
+        const int p = tid + j * kWThreads, row = p / PPR, col = (p % PPR) * 8;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const bool ok = row < nrow;
+        *reinterpret_cast<u32x4*>(&sm.qk[row * LDK + col]) = ok ? rq[j] : z;
+        *reinterpret_cast<u32x4*>(&sm.kr[row * LDK + col]) = ok ? rk[j] : z;
+        *reinterpret_cast<u32x4*>(&sm.lr[row * LDK + col]) = ok ? rl[j] : z;
+    }
+    if (tid < kWC) sm.beta[tid] = tid < nrow ? bf2f(braw) : 0.f;
+#pragma unroll
+    for (int u = 0; u < VW; ++u)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+            if (16 * rt + r >= nrow) vraw[u][rt] = make_uint2(0, 0);
+    lds_barrier();
+
+    // 4 consecutive elements of an LDS row
+    auto lds4 = [&](const uint16_t* arr, int row, int col) -> uint2 {
+        return *reinterpret_cast<const uint2*>(&arr[row * LDK + col]);
+    };
+    // constant fragments: identity, all-ones, inclusive lower triangle (k <= row)
+    Frag16 ident, ones, tri;
+    {
+        uint32_t e[4], t[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            e[s] = (4 * g + s == r) ? kOne : 0u;
+            t[s] = (4 * g + s <= r) ? kOne : 0u;
+        }
+        ident.u = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+        tri.u = make_uint2(t[0] | (t[1] << 16), t[2] | (t[3] << 16));
+        ones.u = make_uint2(kOne | (uint32_t(kOne) << 16), kOne | (uint32_t(kOne) << 16));
+    }
+
+    // ===== phase 1: token tile i = wave, all key channels (token-row layout) =====
+    const int i = wave;
+    uint2 khv[NCT], qhh[NCT], qhl[NCT];         // Kh, Qh hi, Qh lo of token tile i
+    float dp = 0.f;                             // q.k of token 16i + r (partial over this lane's channels)
+    {
+        // G of token tile i: G^T(ct, i) = sum_{rp <= i} Lam^T(ct, rp) L^T(rp, i)
+        f32x4 gt[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) gt[ct] = zero4();
+        for (int rp = 0; rp <= i; ++rp) {
+            const Frag16 lb = (rp < i) ? ones : tri;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                // transposed tile: Lam[16rp + 4g + s][16ct + r], the A operand of Lam^T
+                const Frag16 lamT = EL::from_acc16(EL::mma16(Frag16{lds4(sm.lr, 16 * rp + r, 16 * ct + 4 * g)}, ident, zero4()));
+                gt[ct] = EL::mma16(lamT, lb, gt[ct]);
+            }
+        }
+        // lane (r, g), tile ct: G[16i + r][16ct + 4g + s]; q, k in the same layout
+        uint2 qv[NCT], kv[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            qv[ct] = lds4(sm.qk, 16 * i + r, 16 * ct + 4 * g);
+            kv[ct] = lds4(sm.kr, 16 * i + r, 16 * ct + 4 * g);
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            float qf[4], kf[4], fq[4], fkh[4], fkc[4], lq[4], lk[4];
+            unpack4(qv[ct], qf);
+            unpack4(kv[ct], kf);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const float G2 = gt[ct][s] * kLog2e;
+                const float ex = fast_exp2(G2), ei = fast_exp2(-G2);
+                dp += qf[s] * kf[s];
+                fq[s] = qf[s] * ex;
+                fkh[s] = kf[s] * ex;
+                fkc[s] = kf[s] * ei;
+                lq[s] = fq[s] - bf2f(f2bf(fq[s]));
+                lk[s] = fkc[s] - bf2f(f2bf(fkc[s]));
+            }
+            qhh[ct] = pack4(fq[0], fq[1], fq[2], fq[3]);
+            qhl[ct] = pack4(lq[0], lq[1], lq[2], lq[3]);
+            khv[ct] = pack4(fkh[0], fkh[1], fkh[2], fkh[3]);
+            // Kc hi over the raw q and Kh over the raw k of this wave's own rows (no
+            // other wave reads them)
+            *reinterpret_cast<uint2*>(&sm.qk[(16 * i + r) * LDK + 16 * ct + 4 * g]) = pack4(fkc[0], fkc[1], fkc[2], fkc[3]);
+            *reinterpret_cast<uint2*>(&sm.kcl[(16 * i + r) * LDK + 16 * ct + 4 * g]) = pack4(lk[0], lk[1], lk[2], lk[3]);
+            *reinterpret_cast<uint2*>(&sm.kr[(16 * i + r) * LDK + 16 * ct + 4 * g]) = khv[ct];
+            // gamma = exp(G of row 63); rows past the sample's end add nothing to G
+            if (i == 3 && r == 15)
+                *reinterpret_cast<float4*>(&sm.gam[16 * ct + 4 * g]) =
+                    make_float4(fast_exp2(gt[ct][0] * kLog2e), fast_exp2(gt[ct][1] * kLog2e),
+                                fast_exp2(gt[ct][2] * kLog2e), fast_exp2(gt[ct][3] * kLog2e));
+        }
+        dp += __shfl_xor(dp, 16);
+        dp += __shfl_xor(dp, 32);
+        // Qh fragments of the chain kernel: (rt = i, kb) = [tile 2kb | tile 2kb + 1]
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+            *reinterpret_cast<uint4*>(rec + Lay::Q + ((i * NKB + kb) * 64 + lane) * 8) =
+                make_uint4(qhh[2 * kb].x, qhh[2 * kb].y, qhh[2 * kb + 1].x, qhh[2 * kb + 1].y);
+    }
+    const float bt = sm.beta[16 * i + r];
+    lds_barrier();
+
+    // ===== phase 2: A and P tiles of token rows i (columns j <= i) =====
+    for (int j = 0; j <= i; ++j) {
+        f32x4 aa = zero4(), pp = zero4();
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            const Frag kh = EL::load(&sm.qk[(16 * j + r) * LDK + 32 * kb], g);
+            const Frag kl = EL::load(&sm.kcl[(16 * j + r) * LDK + 32 * kb], g);
+            const Frag khat{make_uint4(khv[2 * kb].x, khv[2 * kb].y, khv[2 * kb + 1].x, khv[2 * kb + 1].y)};
+            const Frag qh{make_uint4(qhh[2 * kb].x, qhh[2 * kb].y, qhh[2 * kb + 1].x, qhh[2 * kb + 1].y)};
+            const Frag ql{make_uint4(qhl[2 * kb].x, qhl[2 * kb].y, qhl[2 * kb + 1].x, qhl[2 * kb + 1].y)};
+            aa = EL::mma(kh, khat, aa);      // (Kh Kc^T)[16i + r][16j + 4g + s]
+            pp = EL::mma(kh, qh, pp);        // (Qh Kc^T)[16i + r][16j + 4g + s], hi/lo
+            pp = EL::mma(kl, qh, pp);
+            pp = EL::mma(kh, ql, pp);
+        }
+        if (j < i) {
+            *reinterpret_cast<uint2*>(&sm.aoff[((i * (i - 1)) / 2 + j) * 256 + lane * 4]) =
+                pack4(-bt * aa[0], -bt * aa[1], -bt * aa[2], -bt * aa[3]);
+        } else {
+            float4 x;
+            x.x = (4 * g + 0 < r) ? bt * aa[0] : 0.f;
+            x.y = (4 * g + 1 < r) ? bt * aa[1] : 0.f;
+            x.z = (4 * g + 2 < r) ? bt * aa[2] : 0.f;
+            x.w = (4 * g + 3 < r) ? bt * aa[3] : 0.f;
+            *reinterpret_cast<float4*>(&sm.at[(i * 16 + r) * 20 + 4 * g]) = x;
+        }
+        float pv[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int col = 4 * g + s;
+            pv[s] = (j < i || col < r) ? pp[s] : (col == r ? dp : 0.f);
+        }
+        *reinterpret_cast<uint2*>(rec + Lay::P + ((i * 2 + j / 2) * 64 + lane) * 8 + (j & 1) * 4) =
+            pack4(pv[0], pv[1], pv[2], pv[3]);
+    }
+    if ((i & 1) == 0)   // the upper half of the last fragment of rows i lies above the diagonal
+        *reinterpret_cast<uint2*>(rec + Lay::P + ((i * 2 + i / 2) * 64 + lane) * 8 + 4) = make_uint2(0, 0);
+    lds_barrier();
+
+    // ===== phase 3: inverse of diagonal block `wave`; key channel and value slabs =====
+    {
+        // column r of (I + A_ww)^-1 by forward substitution (fp32), written over A_ww;
+        // the block's rows are read into registers before the dependent chain starts
+        float* a = &sm.at[wave * 16 * 20];
+        float4 arow[16][4];
+#pragma unroll
+        for (int m = 1; m < 16; ++m)
+#pragma unroll
+            for (int q4 = 0; q4 < (m + 3) / 4; ++q4) arow[m][q4] = *reinterpret_cast<const float4*>(&a[m * 20 + 4 * q4]);
+        float t[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            float acc = (m == r) ? 1.f : 0.f;
+#pragma unroll
+            for (int jj = 0; jj < m; ++jj) acc -= arow[m][jj / 4][jj % 4] * t[jj];
+            t[m] = acc;
+        }
+        if (g == 0) {
+#pragma unroll
+            for (int m = 0; m < 16; ++m) a[m * 20 + r] = t[m];
+        }
+    }
+    // right-hand sides diag(b) Kh (key channel tiles) and diag(b) V (value tiles),
+    // channel-row layout: lane (r, g) of tile (rt, x) holds row 16rt + 4g + s, column
+    // 16x + r. Token-row tiles are transposed exactly by the identity product.
+    f32x4 yw[CW][4], yu[VW][4];
+    float4 b4[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) b4[rt] = *reinterpret_cast<const float4*>(&sm.beta[16 * rt + 4 * g]);
+    float* gam_out = reinterpret_cast<float*>(rec + Lay::G);
+#pragma unroll
+    for (int u = 0; u < CW; ++u) {
+        const int ct = CW * wave + u;
+        const float gam = sm.gam[16 * ct + r];
+        if (g == 0) gam_out[16 * ct + r] = gam;
+        uint2 kbp[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const f32x4 kh = EL::mma16(Frag16{lds4(sm.kr, 16 * rt + r, 16 * ct + 4 * g)}, ident, zero4());
+            f32x4 kc = EL::mma16(Frag16{lds4(sm.qk, 16 * rt + r, 16 * ct + 4 * g)}, ident, zero4());
+            kc = EL::mma16(Frag16{lds4(sm.kcl, 16 * rt + r, 16 * ct + 4 * g)}, ident, kc);
+            // Kb = K exp(G_last - G) = gamma Kc
+            kbp[rt] = pack4(gam * kc[0], gam * kc[1], gam * kc[2], gam * kc[3]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) yw[u][rt][s] = b4[rt][s] * kh[s];
+        }
+        // Kb^T fragments (ct, kb): token tiles 2kb (t = 0) and 2kb + 1 (t = 1)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            *reinterpret_cast<uint4*>(rec + Lay::K + ((ct * 2 + kb) * 64 + lane) * 8) =
+                make_uint4(kbp[2 * kb].x, kbp[2 * kb].y, kbp[2 * kb + 1].x, kbp[2 * kb + 1].y);
+    }
+#pragma unroll
+    for (int u = 0; u < VW; ++u) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const f32x4 vv = EL::mma16(Frag16{vraw[u][rt]}, ident, zero4());   // V[16rt + 4g + s][16vt + r]
+#pragma unroll
+            for (int s = 0; s < 4; ++s) yu[u][rt][s] = b4[rt][s] * vv[s];
+        }
+    }
+    lds_barrier();
+
+    // ===== phase 4: (I + A) X = Y by 16-row blocks, for this wave's tiles =====
+    Frag16 tf[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        const float4 x = *reinterpret_cast<const float4*>(&sm.at[(ii * 16 + r) * 20 + 4 * g]);
+        tf[ii].u = pack4(x.x, x.y, x.z, x.w);
+    }
+    auto solve = [&](f32x4 (&y)[4]) {
+        y[0] = EL::mma16(tf[0], EL::from_acc16(y[0]), zero4());
+#pragma unroll
+        for (int ii = 1; ii < 4; ++ii) {
+            f32x4 acc = y[ii];
+#pragma unroll
+            for (int jj = 0; jj < ii; ++jj)
+                acc = EL::mma16(Frag16{*reinterpret_cast<const uint2*>(&sm.aoff[((ii * (ii - 1)) / 2 + jj) * 256 + lane * 4])},
+                                EL::from_acc16(y[jj]), acc);
+            y[ii] = EL::mma16(tf[ii], EL::from_acc16(acc), zero4());
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < VW; ++u) {
+        solve(yu[u]);
+        const int vt = VW * wave + u;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+            *reinterpret_cast<uint2*>(rec + Lay::U + ((vt * 4 + rt) * 64 + lane) * 4) = pack4(yu[u][rt]);
+    }
+#pragma unroll
+    for (int u = 0; u < CW; ++u) {
+        solve(yw[u]);
+        const int ct = CW * wave + u;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            // -W tile (rt, ct) in token rows: transpose with the identity product
+            const f32x4 nw = -yw[u][rt];
+            const f32x4 wt = EL::mma16(EL::from_acc16(nw), ident, zero4());   // W[16rt + r][16ct + 4g + s]
+            *reinterpret_cast<uint2*>(rec + Lay::W + ((rt * NKB + ct / 2) * 64 + lane) * 8 + (ct & 1) * 4) = pack4(wt);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// chain: the state pass of one (sample, head, 64-column value tile)
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+__global__ __launch_bounds__(kWThreads) void kda_wy_chain_kernel(
+    const uint16_t* ws, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
+    const float* __restrict__ init_state, uint16_t* __restrict__ out, float* __restrict__ final_state,
+    int num_seqs, int H, int64_t total_tokens, int max_chunks)
+{
+    using EL = Elt<uint16_t>;
+    using Frag = EL::Frag;
+    using Lay = WyLayout<DK, DV>;
+    constexpr int NKB = Lay::NKB, NCT = Lay::NCT;
+    constexpr int NVT64 = DV / 64;
+    constexpr int SH16 = Lay::SHARED * 2 / 16;     // 16-byte pieces of the shared operands
+    constexpr int U16 = Lay::UTILE * 2 / 16;       // 16-byte pieces of this tile's U
+    constexpr int NP = SH16 + U16;
+    constexpr int PER = (NP + kWThreads - 1) / kWThreads;
+
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    u32x4* lds = reinterpret_cast<u32x4*>(smem_raw);
+    const uint16_t* sl = reinterpret_cast<const uint16_t*>(smem_raw);
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, g = lane >> 4;
+
+    // the value tiles of one (sample, head) are 8 blocks apart: same XCD, shared L2
+    const int b = blockIdx.x;
+    const int vt = (b >> 3) % NVT64;
+    const int unit = (b / (8 * NVT64)) * 8 + (b & 7);
+    if (unit >= num_seqs * H) return;
+    const int n = unit / H, h = unit % H;
+    const int c0 = min(chunk_off[n], max_chunks), c1 = min(chunk_off[n + 1], max_chunks);
+    int64_t s0, s1;
+    sample_bounds(cu, n, total_tokens, s0, s1);
+    const int vc = 4 * vt + wave;               // this wave's 16 value columns
+    const int col = 16 * vc;
+
+    f32x4 S[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        if (init_state) {
+            const float* st = init_state + ((int64_t(n) * H + h) * DK + 16 * ct + 4 * g) * DV + col + r;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) S[ct][s] = st[s * DV];
+        } else {
+            S[ct] = zero4();
+        }
+    }
+
+    // operands of one chunk: the shared part and this value tile's U, 16 bytes per
+    // piece; piece p of thread tid is tid + 256 p (clamped, so every load is valid)
+    u32x4 pf[PER];
+    auto fetch = [&](int cc) __attribute__((always_inline)) {
+        const u32x4* rec = reinterpret_cast<const u32x4*>(ws + (int64_t(cc) * H + h) * Lay::TOTAL);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int idx = min(tid + j * kWThreads, NP - 1);
+            pf[j] = rec[idx + (idx >= SH16 ? vt * U16 : 0)];
+        }
+    };
+    auto commit = [&]() __attribute__((always_inline)) {   // pieces past NP land in padding
+#pragma unroll
+        for (int j = 0; j < PER; ++j) lds[tid + j * kWThreads] = pf[j];
+    };
+    // The operands of chunk c are loaded while chunk c - 1 is computed and written
+    // to LDS at the top of iteration c; the workspace pointer is deliberately not
+    // __restrict__, so the loads are not moved down to their use.
+    if (c0 < c1) fetch(c0);
+    for (int c = c0; c < c1; ++c) {
+        commit();
+        lds_barrier();
+        fetch(min(c + 1, c1 - 1));              // next chunk's operands (unconditional, clamped)
+
+        Frag sf[NKB];                           // S as the B operand over key channels
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) sf[kb] = EL::from_acc(S[2 * kb], S[2 * kb + 1]);
+        // Vn = U - W S: tile rt holds Vn[16rt + 4g + s][col + r]
+        f32x4 X[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            float u4[4];
+            unpack4(*reinterpret_cast<const uint2*>(sl + Lay::SHARED + ((wave * 4 + rt) * 64 + lane) * 4), u4);
+            X[rt] = f32x4{u4[0], u4[1], u4[2], u4[3]};
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+                X[rt] = EL::mma(Frag{*reinterpret_cast<const uint4*>(sl + Lay::W + ((rt * NKB + kb) * 64 + lane) * 8)},
+                                sf[kb], X[rt]);
+        // O^T = S^T Qh^T + Vn^T P^T: tile rt holds O[16rt + r][col + 4g + s]
+        f32x4 O[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) O[rt] = zero4();
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+                O[rt] = EL::mma(sf[kb], Frag{*reinterpret_cast<const uint4*>(sl + Lay::Q + ((rt * NKB + kb) * 64 + lane) * 8)},
+                                O[rt]);
+        const Frag vf[2] = {EL::from_acc(X[0], X[1]), EL::from_acc(X[2], X[3])};
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int kb = 0; kb <= rt / 2; ++kb)
+                O[rt] = EL::mma(vf[kb], Frag{*reinterpret_cast<const uint4*>(sl + Lay::P + ((rt * 2 + kb) * 64 + lane) * 8)},
+                                O[rt]);
+        // S <- diag(gamma) S + Kb^T Vn
+        const float* gam = reinterpret_cast<const float*>(sl + Lay::G);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const float4 g4 = *reinterpret_cast<const float4*>(gam + 16 * ct + 4 * g);
+            S[ct][0] *= g4.x; S[ct][1] *= g4.y; S[ct][2] *= g4.z; S[ct][3] *= g4.w;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                S[ct] = EL::mma(Frag{*reinterpret_cast<const uint4*>(sl + Lay::K + ((ct * 2 + kb) * 64 + lane) * 8)},
+                                vf[kb], S[ct]);
+        }
+        // output rows of this chunk
+        const int64_t t0 = s0 + int64_t(c - c0) * kWC;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const int64_t t = t0 + 16 * rt + r;
+            if (t < s1) *reinterpret_cast<uint2*>(out + (t * H + h) * DV + col + 4 * g) = pack4(O[rt]);
+        }
+        lds_barrier();                          // every wave is done with this chunk's operands
+    }
+
+    if (final_state) {
+        float* fs = final_state + ((int64_t(n) * H + h) * DK) * DV + col + r;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) fs[int64_t(16 * ct + 4 * g + s) * DV] = S[ct][s];
+    }
+}
+
+// LDS of the chain kernel: one chunk's operands, padded to whole 16-byte pieces per thread
+template <int DK, int DV>
+constexpr size_t chain_smem() {
+    constexpr int np = (WyLayout<DK, DV>::SHARED + WyLayout<DK, DV>::UTILE) * 2 / 16;
+    return size_t((np + kWThreads - 1) / kWThreads) * kWThreads * 16;
+}
+
+template <int DK, int DV>
+hipError_t launch_dims(const LaunchArgs& a, uint16_t* ws, int32_t* chunk_off, int max_chunks, TimingHook* th)
+{
+    const int units = a.num_seqs * a.num_heads;
+    dim3 pgrid(max_chunks, a.num_heads);
+    if (th) th->begin("prep", a.stream);
+    hipLaunchKernelGGL((kda_wy_prep_kernel<DK, DV>), pgrid, dim3(kWThreads), 0, a.stream,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.log_alpha),
+                       static_cast<const uint16_t*>(a.beta), a.cu_seqlens, chunk_off, ws, a.num_seqs,
+                       a.num_heads, a.total_tokens, max_chunks);
+    if (th) th->end(a.stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    constexpr size_t smem = chain_smem<DK, DV>();
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_wy_chain_kernel<DK, DV>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+    if (e != hipSuccess) return e;
+    const int nvt = a.d_v / 64;
+    const int blocks = ((units + 7) / 8) * 8 * nvt;
+    if (th) th->begin("chain", a.stream);
+    hipLaunchKernelGGL((kda_wy_chain_kernel<DK, DV>), dim3(blocks), dim3(kWThreads), smem, a.stream,
+                       ws, a.cu_seqlens, chunk_off, a.init_state, static_cast<uint16_t*>(a.out),
+                       a.final_state, a.num_seqs, a.num_heads, a.total_tokens, max_chunks);
+    if (th) th->end(a.stream);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t wy_record_bytes(int d_k, int d_v)
+{
+    if (d_k == 128 && d_v == 128) return size_t(WyLayout<128, 128>::TOTAL) * 2;
+    if (d_k == 128 && d_v == 64) return size_t(WyLayout<128, 64>::TOTAL) * 2;
+    if (d_k == 64 && d_v == 128) return size_t(WyLayout<64, 128>::TOTAL) * 2;
+    return size_t(WyLayout<64, 64>::TOTAL) * 2;
+}
+
+int64_t wy_max_chunks(int64_t total_tokens, int32_t num_seqs)
+{
+    return (total_tokens + kWC - 1) / kWC + num_seqs;
+}
+
+size_t wy_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads, int d_k, int d_v)
+{
+    const size_t off = (size_t(num_seqs) + 1) * sizeof(int32_t);
+    const size_t off_al = (off + 255) & ~size_t(255);
+    return off_al + size_t(wy_max_chunks(total_tokens, num_seqs)) * size_t(num_heads) * wy_record_bytes(d_k, d_v);
+}
+
+hipError_t launch_forward_wy(const LaunchArgs& a, void* workspace, TimingHook* th)
+{
+    const int64_t mc = wy_max_chunks(a.total_tokens, a.num_seqs);
+    if (mc > 0x7FFFFFFF / 2) return hipErrorInvalidValue;
+    const int max_chunks = int(mc);
+    int32_t* chunk_off = static_cast<int32_t*>(workspace);
+    const size_t off = (size_t(a.num_seqs) + 1) * sizeof(int32_t);
+    uint16_t* ws = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + ((off + 255) & ~size_t(255)));
+
+    if (th) th->begin("plan", a.stream);
+    hipLaunchKernelGGL(kda_wy_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, chunk_off,
+                       a.num_seqs, a.total_tokens);
+    if (th) th->end(a.stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    if (a.d_k == 128 && a.d_v == 128) return launch_dims<128, 128>(a, ws, chunk_off, max_chunks, th);
+    if (a.d_k == 128 && a.d_v == 64) return launch_dims<128, 64>(a, ws, chunk_off, max_chunks, th);
+    if (a.d_k == 64 && a.d_v == 128) return launch_dims<64, 128>(a, ws, chunk_off, max_chunks, th);
+    return launch_dims<64, 64>(a, ws, chunk_off, max_chunks, th);
+}
+
+}  // namespace kda

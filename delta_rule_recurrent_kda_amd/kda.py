@@ -46,6 +46,18 @@ def library() -> ctypes.CDLL:
         lib.kda_last_error.restype = ctypes.c_char_p
         lib.kda_version.argtypes = []
         lib.kda_version.restype = ctypes.c_int32
+        lib.kda_forward_from_state.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int64,
+                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.c_int, vp]
+        lib.kda_forward_from_state.restype = ctypes.c_int
+        lib.kda_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int]
+        lib.kda_workspace_bytes.restype = ctypes.c_size_t
+        lib.kda_timing_enable.argtypes = [ctypes.c_int32]
+        lib.kda_timing_enable.restype = ctypes.c_int
+        lib.kda_timing_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int32),
+                                        ctypes.POINTER(ctypes.c_double)]
+        lib.kda_timing_read.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -63,20 +75,42 @@ def kda_forward_raw(q, k, v, log_alpha, beta, cu_seqlens, out, final_state, tota
                                  int(d_v), int(dtype), stream)
 
 
-def kda_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
-                beta: torch.Tensor, cu_seqlens: torch.Tensor, out: torch.Tensor,
-                final_state: Optional[torch.Tensor] = None,
-                stream: Optional[torch.cuda.Stream] = None) -> None:
-    """Enqueue the KDA forward scan on ``stream`` (default: torch's current stream).
+def kda_forward_from_state_raw(q, k, v, log_alpha, beta, cu_seqlens, initial_state, out,
+                               final_state, total_tokens: int, num_seqs: int, num_heads: int,
+                               d_k: int, d_v: int, dtype: int, stream: Optional[int]) -> int:
+    """Direct C call of kda_forward_from_state; returns the status code."""
+    return library().kda_forward_from_state(q, k, v, log_alpha, beta, cu_seqlens, initial_state,
+                                            out, final_state, int(total_tokens), int(num_seqs),
+                                            int(num_heads), int(d_k), int(d_v), int(dtype), stream)
 
-    q, k, log_alpha: [T, H, d_k]; v, out: [T, H, d_v]; beta: [T, H] (one dtype,
-    float32 or bfloat16); cu_seqlens: int32 [N+1]; final_state: float32
-    [N, H, d_k, d_v] or None. All on the same GPU, contiguous.
-    """
+
+def workspace_bytes(total_tokens: int, num_seqs: int, num_heads: int, d_k: int, d_v: int,
+                    dtype: int) -> int:
+    return int(library().kda_workspace_bytes(int(total_tokens), int(num_seqs), int(num_heads),
+                                             int(d_k), int(d_v), int(dtype)))
+
+
+def timing_enable(on: bool) -> None:
+    library().kda_timing_enable(1 if on else 0)
+
+
+def timing_read(kernel: str):
+    """(launches, total milliseconds) of the named kernel since the last read."""
+    n = ctypes.c_int32(0)
+    ms = ctypes.c_double(0.0)
+    st = library().kda_timing_read(kernel.encode(), ctypes.byref(n), ctypes.byref(ms))
+    if st != 0:
+        raise KdaError(st, library().kda_last_error().decode())
+    return int(n.value), float(ms.value)
+
+
+def _check(q, k, v, log_alpha, beta, cu_seqlens, out, final_state, initial_state):
     tensors = {"q": q, "k": k, "v": v, "log_alpha": log_alpha, "beta": beta,
                "cu_seqlens": cu_seqlens, "out": out}
     if final_state is not None:
         tensors["final_state"] = final_state
+    if initial_state is not None:
+        tensors["initial_state"] = initial_state
     for name, t in tensors.items():
         if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
@@ -93,31 +127,56 @@ def kda_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: to
             raise ValueError(f"{name} dtype {tensors[name].dtype} != q dtype {q.dtype}")
     if cu_seqlens.dtype != torch.int32:
         raise ValueError("cu_seqlens must be int32")
-    if final_state is not None and final_state.dtype != torch.float32:
-        raise ValueError("final_state must be float32")
+    for name in ("final_state", "initial_state"):
+        if name in tensors and tensors[name].dtype != torch.float32:
+            raise ValueError(f"{name} must be float32")
     T, H, dk = q.shape
     dv = v.shape[2]
     if k.shape != q.shape or log_alpha.shape != q.shape or v.shape != (T, H, dv) or \
             out.shape != (T, H, dv) or beta.shape != (T, H) or cu_seqlens.dim() != 1:
         raise ValueError("inconsistent shapes")
     N = cu_seqlens.numel() - 1
-    if final_state is not None and final_state.shape != (N, H, dk, dv):
-        raise ValueError("final_state must be [N, H, d_k, d_v]")
+    for name in ("final_state", "initial_state"):
+        if name in tensors and tensors[name].shape != (N, H, dk, dv):
+            raise ValueError(f"{name} must be [N, H, d_k, d_v]")
+    return T, N, H, dk, dv, dt
+
+
+def kda_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
+                beta: torch.Tensor, cu_seqlens: torch.Tensor, out: torch.Tensor,
+                final_state: Optional[torch.Tensor] = None,
+                stream: Optional[torch.cuda.Stream] = None,
+                initial_state: Optional[torch.Tensor] = None) -> None:
+    """Enqueue the KDA forward scan on ``stream`` (default: torch's current stream).
+
+    q, k, log_alpha: [T, H, d_k]; v, out: [T, H, d_v]; beta: [T, H] (one dtype,
+    float32 or bfloat16); cu_seqlens: int32 [N+1]; final_state and initial_state:
+    float32 [N, H, d_k, d_v] or None. All on the same GPU, contiguous. With an
+    initial_state the call goes to kda_forward_from_state.
+    """
+    T, N, H, dk, dv, dt = _check(q, k, v, log_alpha, beta, cu_seqlens, out, final_state,
+                                 initial_state)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    st = kda_forward_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(cu_seqlens),
-                         _ptr(out), _ptr(final_state), T, N, H, dk, dv, dt, stream.cuda_stream)
+    if initial_state is None:
+        st = kda_forward_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                             _ptr(cu_seqlens), _ptr(out), _ptr(final_state), T, N, H, dk, dv, dt,
+                             stream.cuda_stream)
+    else:
+        st = kda_forward_from_state_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                        _ptr(cu_seqlens), _ptr(initial_state), _ptr(out),
+                                        _ptr(final_state), T, N, H, dk, dv, dt, stream.cuda_stream)
     if st != 0:
         raise KdaError(st, library().kda_last_error().decode())
 
 
 def forward(q, k, v, log_alpha, beta, cu_seqlens, with_state: bool = True,
-            stream: Optional[torch.cuda.Stream] = None):
+            stream: Optional[torch.cuda.Stream] = None, initial_state=None):
     """Allocate outputs and run the scan. Returns (out, final_state or None)."""
     T, H, _ = q.shape
     N = cu_seqlens.numel() - 1
     out = torch.empty((T, H, v.shape[2]), dtype=q.dtype, device=q.device)
     fs = torch.empty((N, H, q.shape[2], v.shape[2]), dtype=torch.float32, device=q.device) \
         if with_state else None
-    kda_forward(q, k, v, log_alpha, beta, cu_seqlens, out, fs, stream)
+    kda_forward(q, k, v, log_alpha, beta, cu_seqlens, out, fs, stream, initial_state)
     return out, fs

@@ -26,6 +26,7 @@
 #ifndef KDA_H
 #define KDA_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -69,15 +70,21 @@ typedef enum {
  *
  * Numerics: inputs are used as stored; internally fp32 state and accumulation. For
  * bf16 inputs the chunk contractions run on bf16 MFMA; out is rounded to nearest-even.
- * Precondition: within any 64-token chunk (32 for fp32 with d_k = 128) the summed
+ * Precondition: within any 64-token chunk (the longest chunk of any scan) the summed
  * log_alpha of each key channel is above -80; stronger decay overflows the factored
  * per-chunk decay and gives non-finite results. NaN/Inf inputs propagate only within
  * their own (sample, head).
  *
  * Execution: enqueued on `stream` (NULL = the null stream) and returns without
  * synchronising; buffers must stay valid until the stream reaches the work. The
- * library keeps no pointer after returning and allocates no device memory on this
- * path. Results are bitwise deterministic for identical inputs on the same device.
+ * library keeps no pointer after returning. For bf16 data the default scan takes a
+ * workspace of kda_workspace_bytes(...) bytes (about 1.2 KB per token and head)
+ * from the device's default stream-ordered memory pool (hipMallocAsync on `stream`,
+ * released with hipFreeAsync on `stream` after the kernels; the pool keeps the
+ * memory for the next call). The environment variable KDA_SCAN_VARIANT=pipe or
+ * =sequential selects a single-kernel bf16 scan that needs no workspace; fp32 data
+ * always uses the sequential one. Results are bitwise deterministic for identical
+ * inputs on the same device and variant.
  * cu_seqlens is read on the device; its content is checked on the host only when the
  * environment variable KDA_VALIDATE=1 (one synchronous device-to-host copy).
  *
@@ -89,6 +96,52 @@ kda_status kda_forward(const void *q, const void *k, const void *v, const void *
                        float *final_state, int64_t total_tokens, int32_t num_seqs,
                        int32_t num_heads, int32_t d_k, int32_t d_v, kda_dtype dtype,
                        hipStream_t stream);
+
+/*
+ * kda_forward_from_state -- kda_forward with a given state at the start of each sample.
+ *
+ * The recurrent state is the only thing a sample carries forward (fixed size per
+ * head, independent of the number of tokens: explainer page "What O(N) buys in
+ * memory and latency"; paper Sec. 5 hybrid-attention efficiency study, Fig. 18,
+ * "roll-out cache" setting). This entry point continues a scan from a retained
+ * state: S_0 = initial_state[n][h] instead of 0, every other step as kda_forward.
+ * Running tokens [0, a) and then [a, L) of one sample, the second call starting from
+ * the first call's final_state, gives the result of one call over [0, L) up to
+ * floating-point rounding.
+ *
+ *   initial_state : [num_seqs][num_heads][d_k][d_v] fp32 DEVICE pointer, rows = key
+ *                   channels, 16-byte aligned; read only; may not alias final_state.
+ *                   NULL means zero states (then identical to kda_forward).
+ * All other arguments, errors and execution as kda_forward. Supported for bf16 data
+ * on the default scan; KDA_E_UNSUPPORTED otherwise (non-NULL initial_state).
+ */
+kda_status kda_forward_from_state(const void *q, const void *k, const void *v,
+                                  const void *log_alpha, const void *beta,
+                                  const int32_t *cu_seqlens, const float *initial_state,
+                                  void *out, float *final_state, int64_t total_tokens,
+                                  int32_t num_seqs, int32_t num_heads, int32_t d_k, int32_t d_v,
+                                  kda_dtype dtype, hipStream_t stream);
+
+/*
+ * kda_workspace_bytes -- bytes of device workspace the default bf16 scan takes for
+ * these sizes (0 when it takes none: fp32 data, no samples, unsupported sizes).
+ * Layout: per (64-token chunk, head) record of the chunk's decayed operands and
+ * WY factors, plus a chunk table. Pure function of the sizes; no device access.
+ */
+size_t kda_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads,
+                           int32_t d_k, int32_t d_v, kda_dtype dtype);
+
+/*
+ * Diagnostics: per-kernel timing with HIP events. While enabled (on != 0), each
+ * kda_forward* call records a pair of events on its stream around every kernel it
+ * launches, named "plan", "prep" and "chain" (default bf16 scan) or "scan"
+ * (single-kernel scans). kda_timing_read waits for the recorded events of `kernel`,
+ * returns their count and summed duration in milliseconds, and drops them.
+ * Process-wide state guarded by a mutex; returns KDA_E_NULL on NULL arguments and
+ * KDA_E_HIP if an event cannot be read (all records are then dropped).
+ */
+kda_status kda_timing_enable(int32_t on);
+kda_status kda_timing_read(const char *kernel, int32_t *launches, double *total_ms);
 
 /* Static string naming a status code. */
 const char *kda_status_str(kda_status status);

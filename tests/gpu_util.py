@@ -33,23 +33,23 @@ def device_inputs(spec, a, device="cuda:0"):
     return out
 
 
-def run_hip(spec, d, stream=None):
+def run_hip(spec, d, stream=None, initial_state=None):
     """Call the library through the C ABI; returns fp64 numpy (out, final_state)."""
     import torch
     from delta_rule_recurrent_kda_amd import kda
     o, fs = kda.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"],
-                        stream=stream)
+                        stream=stream, initial_state=initial_state)
     torch.cuda.synchronize()
     return o.float().cpu().double().numpy(), fs.cpu().double().numpy()
 
 
-def oracle_ref(spec, a, heads=None, threads=None):
+def oracle_ref(spec, a, heads=None, threads=None, initial_state=None):
     import oracle
     f = {x: inputs.to_f64(a[x], spec.dtype) for x in ("q", "k", "v", "log_alpha", "beta")}
     if threads is None:
         threads = min(16, os.cpu_count() or 1)
     return oracle.forward(f["q"], f["k"], f["v"], f["log_alpha"], f["beta"], a["cu_seqlens"],
-                          heads=heads, threads=threads)
+                          heads=heads, threads=threads, initial_state=initial_state)
 
 
 def compare(spec, out, fs, o_ref, f_ref, heads=None, label=""):

@@ -27,7 +27,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert {"kda_forward", "kda_status_str", "kda_last_error", "kda_version"} <= set(declared_functions())
+    assert {"kda_forward", "kda_forward_from_state", "kda_workspace_bytes", "kda_timing_enable",
+            "kda_timing_read", "kda_status_str", "kda_last_error", "kda_version"} <= set(declared_functions())
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -87,3 +88,50 @@ def test_bad_arguments_are_rejected_without_launch(lib, kw, code):
 def test_empty_batch_is_a_no_op(lib):
     st, _ = _call(dict(num_seqs=0, total_tokens=0))
     assert st == 0
+
+
+def _call_from_state(kw):
+    from delta_rule_recurrent_kda_amd import kda
+    a = dict(q=0x1000, k=0x2000, v=0x3000, log_alpha=0x4000, beta=0x5000, cu_seqlens=0x6000,
+             initial_state=0x9000, out=0x7000, final_state=0x8000, total_tokens=128, num_seqs=1,
+             num_heads=2, d_k=128, d_v=128, dtype=kda.KDA_BF16, stream=None)
+    a.update(kw)
+    st = kda.kda_forward_from_state_raw(**a)
+    return st, kda.library().kda_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(initial_state=0x9004), 4),                 # misaligned
+    (dict(final_state=0x9000), 3),                   # final_state aliases initial_state
+    (dict(dtype=0), 5),                              # fp32 scan takes no initial state
+    (dict(d_k=96), 5),
+    (dict(q=None), 1),
+])
+def test_from_state_bad_arguments_are_rejected_without_launch(lib, kw, code):
+    st, msg = _call_from_state(kw)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def test_from_state_on_single_kernel_variant_is_unsupported(lib, monkeypatch):
+    monkeypatch.setenv("KDA_SCAN_VARIANT", "pipe")
+    st, msg = _call_from_state({})
+    assert st == 5 and "initial_state" in msg
+
+
+def test_workspace_bytes(lib):
+    from delta_rule_recurrent_kda_amd import kda
+    rec = {(128, 128): 74240, (128, 64): 74240 - 8192}
+    # record: -W, Qh (4*d_k/32 fragments of 1 KB each), Kb^T (d_k/16 * 2 KB), P (8 KB),
+    # gamma (4 d_k bytes), U (d_v/16 * 2 KB); plus the chunk table rounded up to 256 bytes
+    def record(dk, dv):
+        return 2 * (4 * dk // 32 * 512) * 2 + (dk // 16) * 2 * 1024 + 8192 + 4 * dk + (dv // 16) * 2048
+    assert record(128, 128) == rec[(128, 128)] and record(128, 64) == rec[(128, 64)]
+    for T, N, H, dk, dv in [(17108, 8, 16, 128, 128), (1, 1, 1, 64, 64), (189272, 1, 16, 128, 64),
+                            (640, 300, 3, 64, 128)]:
+        chunks = (T + 63) // 64 + N
+        table = ((N + 1) * 4 + 255) // 256 * 256
+        assert kda.workspace_bytes(T, N, H, dk, dv, kda.KDA_BF16) == table + chunks * H * record(dk, dv)
+    assert kda.workspace_bytes(1000, 2, 2, 128, 128, kda.KDA_F32) == 0
+    assert kda.workspace_bytes(1000, 0, 2, 128, 128, kda.KDA_BF16) == 0
+    assert kda.workspace_bytes(1000, 2, 2, 96, 128, kda.KDA_BF16) == 0

@@ -125,12 +125,70 @@ def test_config4_sampled_heads():
     _check(inputs.config(4), heads=[0, 7, 15])
 
 
+@pytest.mark.parametrize("variant", ["sequential", "pipe"])
 @pytest.mark.parametrize("case", ["packed8", "ragged_d64"])
-def test_sequential_variant(monkeypatch, case):
-    # the one-chunk-at-a-time bf16 kernel stays selectable; it must meet the same bar
-    monkeypatch.setenv("KDA_SCAN_VARIANT", "sequential")
+def test_single_kernel_variants(monkeypatch, variant, case):
+    # the single-kernel bf16 scans stay selectable; they must meet the same bar
+    monkeypatch.setenv("KDA_SCAN_VARIANT", variant)
     if case == "packed8":
-        _check(inputs.config(1), label="packed8 sequential")
+        _check(inputs.config(1), label=f"packed8 {variant}")
     else:
         spec = inputs.KdaSpec("ragged_d64_seq", (129, 3, 64, 200, 1), 3, 64, 64, "bf16", (0.001, 0.1), 4343)
-        _check(spec, label="ragged d64 sequential")
+        _check(spec, label=f"ragged d64 {variant}")
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64)])
+def test_initial_state_vs_oracle(dk, dv):
+    import torch
+    spec = inputs.KdaSpec(f"init_{dk}_{dv}", (129, 0, 64, 200, 1, 63), 3, dk, dv, "bf16", (0.001, 0.1), 5151)
+    gu.log(f"case initial_state dk={dk} dv={dv}")
+    a = inputs.generate(spec)
+    d = gu.device_inputs(spec, a)
+    s0 = np.random.default_rng(17).standard_normal((len(spec.seq_lens), spec.heads, dk, dv)) * 0.5
+    s0 = s0.astype(np.float32)
+    out, fs = gu.run_hip(spec, d, initial_state=torch.from_numpy(s0).to("cuda:0"))
+    o_ref, f_ref = gu.oracle_ref(spec, a, initial_state=s0.astype(np.float64))
+    gu.compare(spec, out, fs, o_ref, f_ref, label=f"initial state {dk}x{dv}")
+    assert np.array_equal(fs[1], s0[1].astype(np.float64))      # empty sample returns its state
+
+
+def test_split_scan_matches_one_pass():
+    # tokens [0, a) then [a, L) from the carried state == one pass over [0, L)
+    import torch
+    from delta_rule_recurrent_kda_amd import kda
+    spec = inputs.custom([1000], heads=4, d=128, seed=21)
+    a_ = inputs.generate(spec)
+    d = gu.device_inputs(spec, a_)
+    o_ref, f_ref = gu.oracle_ref(spec, a_)
+    for cut in (100, 640):
+        gu.log(f"case split at {cut}")
+        part = {x: d[x][:cut].contiguous() for x in ("q", "k", "v", "log_alpha", "beta")}
+        rest = {x: d[x][cut:].contiguous() for x in ("q", "k", "v", "log_alpha", "beta")}
+        o1, f1 = kda.forward(part["q"], part["k"], part["v"], part["log_alpha"], part["beta"],
+                             torch.tensor([0, cut], dtype=torch.int32, device="cuda:0"))
+        o2, f2 = kda.forward(rest["q"], rest["k"], rest["v"], rest["log_alpha"], rest["beta"],
+                             torch.tensor([0, 1000 - cut], dtype=torch.int32, device="cuda:0"),
+                             initial_state=f1)
+        torch.cuda.synchronize()
+        out = torch.cat([o1, o2]).float().cpu().double().numpy()
+        gu.compare(spec, out, f2.cpu().double().numpy(), o_ref, f_ref, label=f"split at {cut}")
+
+
+def test_kernel_timing_records_each_kernel():
+    import torch
+    from delta_rule_recurrent_kda_amd import kda
+    spec = inputs.custom([300, 40], heads=2, d=128, seed=9)
+    d = gu.device_inputs(spec, inputs.generate(spec))
+    for name in ("plan", "prep", "chain", "scan"):
+        kda.timing_read(name)
+    kda.timing_enable(True)
+    try:
+        for _ in range(3):
+            kda.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"])
+        torch.cuda.synchronize()
+        for name in ("plan", "prep", "chain"):
+            n, ms = kda.timing_read(name)
+            assert n == 3 and ms > 0, (name, n, ms)
+        assert kda.timing_read("scan") == (0, 0.0)
+    finally:
+        kda.timing_enable(False)
