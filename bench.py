@@ -3,9 +3,12 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload packed8|image4|clip5s|clip30s|tiny]
 
 A step is one kda_forward call over the whole packed batch (every stage of the
-scan runs inside it). Inputs are generated once, copied to HBM, and the timed
-region holds exactly K back-to-back steps between two device synchronisations.
-Prints one JSON line.
+scan runs inside it: chunk table, chunk prep, state chain). Inputs are generated
+once, copied to HBM, and the timed region holds exactly K back-to-back steps
+between two device synchronisations. Inside the timed region the library records
+HIP events on the launch stream around each of its kernels; the roofline entry is
+for the kernel with the largest average duration, priced with that kernel's own
+algorithmic bytes. Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -24,12 +27,13 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
 MFMA_F32_PEAK_TFLOPS = 157.3
-KERNEL_SOURCES = ["delta_rule_recurrent_kda_amd/csrc/kda_fwd.hip",
-                  "delta_rule_recurrent_kda_amd/csrc/kda_fwd_pipe.hip",
+KERNEL_SOURCES = ["delta_rule_recurrent_kda_amd/csrc/kda_wy.hip",
                   "delta_rule_recurrent_kda_amd/csrc/kda_device.h",
                   "delta_rule_recurrent_kda_amd/csrc/kda_internal.h"]
 WORKLOADS = {"tiny": 0, "packed8": 1, "image4": 2, "clip5s": 3, "clip30s": 4}
 CHUNK = 64
+KERNEL_SYMBOL = {"prep": "kda_wy_prep_kernel", "chain": "kda_wy_chain_kernel", "plan": "kda_wy_plan_kernel",
+                 "scan": "kda_fwd"}
 
 
 def kernel_sha() -> str:
@@ -47,15 +51,46 @@ def algorithmic_bytes(spec) -> int:
         len(spec.seq_lens) * H * spec.dk * spec.dv * 4
 
 
+def record_bytes(spec):
+    """Per (64-token chunk, head) workspace record: (written by the prep, read by the chain).
+
+    -W, Qh: 4 * d_k/32 fragments of 1 KB each; Kb^T: d_k/16 * 2 KB; P: 6 KB of used
+    fragments; gamma: 4 d_k; U: d_v/16 * 2 KB. The chain reads the shared part once per
+    (chunk, head) and U once in total over its value tiles.
+    """
+    dk, dv = spec.dk, spec.dv
+    w = q = 4 * (dk // 32) * 1024
+    kb = (dk // 16) * 2048
+    return w + q + kb + 6 * 1024 + 4 * dk + (dv // 16) * 2048
+
+
+def chunk_heads(spec) -> int:
+    return sum((n + CHUNK - 1) // CHUNK for n in spec.seq_lens) * spec.heads
+
+
+def kernel_bytes(spec, kernel: str) -> int:
+    """Algorithmic bytes of one launch of each kernel of the default bf16 scan."""
+    es = 2
+    T, H, N = spec.total_tokens, spec.heads, len(spec.seq_lens)
+    rec = chunk_heads(spec) * record_bytes(spec)
+    if kernel == "prep":        # read q, k, v, log a, beta; write the records
+        return T * H * (3 * spec.dk + spec.dv + 1) * es + rec
+    if kernel == "chain":       # read the records; write out and final state
+        return rec + T * H * spec.dv * es + N * H * spec.dk * spec.dv * 4
+    if kernel == "plan":
+        return 4 * (2 * N + 1)
+    return algorithmic_bytes(spec)
+
+
 def chunk_flops(spec) -> int:
     """Dense chunk contractions per launch: 10*C*d + 6*d^2 per head-token (d = d_k = d_v)."""
     d = spec.dk
     return spec.head_tokens * (10 * CHUNK * d + 6 * d * d)
 
 
-def traffic_for(workload: str):
+def traffic_for(workload: str, kernel: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel is unchanged."""
-    path = os.path.join(ROOT, "profiles", f"traffic_kda_fwd_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -118,28 +153,39 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    for name in KERNEL_SYMBOL:
+        kda.timing_read(name)
 
-    # per-launch HIP events on the launch stream
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # timed region: K back-to-back steps; the library records HIP events on `stream`
+    # around each of its kernels
+    kda.timing_enable(True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    for s, e in evs:
-        s.record(stream)
+    for _ in range(args.steps):
         step()
-        e.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    kern_ms = [s.elapsed_time(e) for s, e in evs]
-    avg_ms = float(np.mean(kern_ms))
+    kda.timing_enable(False)
     ms_per_step = wall * 1e3 / args.steps
+    kernels = {}
+    for name in KERNEL_SYMBOL:
+        n, ms = kda.timing_read(name)
+        if n:
+            kernels[name] = {"launches": n, "ms_avg": ms / n}
+    dom = max(kernels, key=lambda k: kernels[k]["ms_avg"])
+    dom_ms = kernels[dom]["ms_avg"]
+    dom_bytes = kernel_bytes(spec, dom)
+    for name, rec_ in kernels.items():
+        b = kernel_bytes(spec, name)
+        rec_.update({"algorithmic_bytes": b, "achieved_GBs": b / (rec_["ms_avg"] * 1e-3) / 1e9})
 
     bytes_ = algorithmic_bytes(spec)
     flops = chunk_flops(spec)
-    achieved = bytes_ / (avg_ms * 1e-3) / 1e9
-    tflops = flops / (avg_ms * 1e-3) / 1e12
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    path_gbs = bytes_ / (ms_per_step * 1e-3) / 1e9
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if spec.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
-    traffic = traffic_for(args.workload)
+    traffic = traffic_for(args.workload, KERNEL_SYMBOL[dom])
 
     rec = {
         "metric": "KDA fwd tokens/s (B·L·H) at dk=dv=128; % MFMA peak and % HBM BW, 1 MI355X",
@@ -159,9 +205,10 @@ def main():
                    "head_tokens": spec.head_tokens},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "kda_fwd_kernel", "kernel_ms_avg": avg_ms,
-                     "kernel_ms_min": float(np.min(kern_ms)), "algorithmic_bytes": bytes_,
+                     "kernel": KERNEL_SYMBOL[dom], "kernel_ms_avg": dom_ms, "algorithmic_bytes": dom_bytes,
                      "kernel_sha": kernel_sha()},
+        "kernels": kernels,
+        "path": {"algorithmic_bytes": bytes_, "achieved_GBs": path_gbs, "frac_hbm": path_gbs / HBM_PEAK_GBS},
         "mfma": {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s", "frac": tflops / mfma_peak,
                  "flops_per_launch": flops},
     }

@@ -71,15 +71,24 @@ struct Timing : kda::TimingHook {
         if (hipEventCreate(&e) != hipSuccess) return nullptr;
         return e;
     }
+    // a launch whose events cannot be recorded is left out of the records
     void begin(const char* kernel, hipStream_t stream) override {
         cur = kernel;
         cur_start = get();
-        if (cur_start) hipEventRecord(cur_start, stream);
+        if (cur_start && hipEventRecord(cur_start, stream) != hipSuccess) {
+            free_events.push_back(cur_start);
+            cur_start = nullptr;
+        }
     }
     void end(hipStream_t stream) override {
+        if (!cur_start) return;
         hipEvent_t stop = get();
-        if (!cur_start || !stop) return;
-        hipEventRecord(stop, stream);
+        if (!stop || hipEventRecord(stop, stream) != hipSuccess) {
+            free_events.push_back(cur_start);
+            if (stop) free_events.push_back(stop);
+            cur_start = nullptr;
+            return;
+        }
         recs.push_back({cur, cur_start, stop});
         cur_start = nullptr;
     }

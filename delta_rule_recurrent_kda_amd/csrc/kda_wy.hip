@@ -25,6 +25,12 @@
 #include "kda_device.h"
 #include "kda_internal.h"
 
+#ifndef KDA_PHASE_DECL
+#define KDA_PHASE_DECL
+#define KDA_PHASE_MARK(i) ((void)0)
+#define KDA_PHASE_FLUSH
+#endif
+
 namespace kda {
 namespace {
 using namespace dev;
@@ -112,13 +118,14 @@ template <int DK> struct PrepSmem {
     alignas(16) uint16_t kr[kWC * LDK];      // raw k; each wave then writes Kh over its own rows
     alignas(16) uint16_t lr[kWC * LDK];      // raw log a
     alignas(16) uint16_t aoff[6 * 256];      // -A blocks (i, j), j < i: 16x16x16 A fragments [blk][lane][4]
-    alignas(16) float at[4 * 16 * 20];       // strictly lower diagonal blocks of A, rows; then (I + A_ii)^-1
+    alignas(16) float at[4 * 16 * 20];       // strictly lower diagonal blocks of A, rows; then
+                                             // (I + A_ii)^-1 as 16x16x16 A fragments
     alignas(16) float beta[kWC];
     alignas(16) float gam[DK];               // exp(G) of the chunk's last row
 };
 
 template <int DK, int DV>
-__global__ __launch_bounds__(kWThreads) void kda_wy_prep_kernel(
+__global__ __launch_bounds__(kWThreads, 2) void kda_wy_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ la, const uint16_t* __restrict__ beta, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ chunk_off, uint16_t* __restrict__ ws, int num_seqs, int H,
@@ -317,26 +324,39 @@ __global__ __launch_bounds__(kWThreads) void kda_wy_prep_kernel(
 
     // ===== phase 3: inverse of diagonal block `wave`; key channel and value slabs =====
     {
-        // column r of (I + A_ww)^-1 by forward substitution (fp32), written over A_ww;
-        // the block's rows are read into registers before the dependent chain starts
+        // A_ww is strictly lower triangular, so (A_ww)^16 = 0 and
+        // (I + A)^-1 = sum_{k<16} (-A)^k = (I - A)(I + A^2)(I + A^4)(I + A^8), exactly.
+        // Products run on fp32 MFMA straight from accumulator-layout registers: with
+        // k = 4g + s in step s, element s of the accumulator tile of X^T is the A operand
+        // of X and element s of the tile of Y is the B operand of Y.
         float* a = &sm.at[wave * 16 * 20];
-        float4 arow[16][4];
+        f32x4 ac, at, id;                       // A, A^T, I in accumulator layout
+        {
+            const float4 x = *reinterpret_cast<const float4*>(&a[r * 20 + 4 * g]);   // A[r][4g + s]
+            at = f32x4{x.x, x.y, x.z, x.w};
 #pragma unroll
-        for (int m = 1; m < 16; ++m)
-#pragma unroll
-            for (int q4 = 0; q4 < (m + 3) / 4; ++q4) arow[m][q4] = *reinterpret_cast<const float4*>(&a[m * 20 + 4 * q4]);
-        float t[16];
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            float acc = (m == r) ? 1.f : 0.f;
-#pragma unroll
-            for (int jj = 0; jj < m; ++jj) acc -= arow[m][jj / 4][jj % 4] * t[jj];
-            t[m] = acc;
+            for (int s = 0; s < 4; ++s) {
+                ac[s] = a[(4 * g + s) * 20 + r];
+                id[s] = (4 * g + s == r) ? 1.f : 0.f;
+            }
         }
-        if (g == 0) {
+        auto mm = [](const f32x4& xt, const f32x4& y) {   // X Y from tiles of X^T and Y
+            f32x4 c = zero4();
 #pragma unroll
-            for (int m = 0; m < 16; ++m) a[m * 20 + r] = t[m];
-        }
+            for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(xt[s], y[s], c, 0, 0, 0);
+            return c;
+        };
+        const f32x4 b1 = mm(at, ac), b1t = mm(ac, at);          // A^2, (A^2)^T
+        const f32x4 b2 = mm(b1t, b1), b2t = mm(b1, b1t);        // A^4, (A^4)^T
+        const f32x4 b3 = mm(b2t, b2);                           // A^8
+        // X1 = (I - A)(I + A^2) = I - A + A^2 - A A^2, as X1^T
+        const f32x4 x1t = id - at + b1t - mm(b1, at);
+        // X2^T = ((X1 (I + A^4)))^T = X1^T + (A^4)^T X1^T
+        const f32x4 x2t = x1t + mm(b2, x1t);
+        // T^T = X2^T + (A^8)^T X2^T; lane (r, g) holds T[r][4g + s], the A operand of T
+        const f32x4 tt = x2t + mm(b3, x2t);
+        // T_ww over this wave's own block (no other wave reads it), as a 16x16x16 A fragment
+        *reinterpret_cast<uint2*>(&a[lane * 2]) = pack4(tt);
     }
     // right-hand sides diag(b) Kh (key channel tiles) and diag(b) V (value tiles),
     // channel-row layout: lane (r, g) of tile (rt, x) holds row 16rt + 4g + s, column
@@ -382,10 +402,7 @@ __global__ __launch_bounds__(kWThreads) void kda_wy_prep_kernel(
     // ===== phase 4: (I + A) X = Y by 16-row blocks, for this wave's tiles =====
     Frag16 tf[4];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-        const float4 x = *reinterpret_cast<const float4*>(&sm.at[(ii * 16 + r) * 20 + 4 * g]);
-        tf[ii].u = pack4(x.x, x.y, x.z, x.w);
-    }
+    for (int ii = 0; ii < 4; ++ii) tf[ii].u = *reinterpret_cast<const uint2*>(&sm.at[ii * 16 * 20 + lane * 2]);
     auto solve = [&](f32x4 (&y)[4]) {
         y[0] = EL::mma16(tf[0], EL::from_acc16(y[0]), zero4());
 #pragma unroll
@@ -423,8 +440,18 @@ __global__ __launch_bounds__(kWThreads) void kda_wy_prep_kernel(
 // ---------------------------------------------------------------------------
 // chain: the state pass of one (sample, head, 64-column value tile)
 // ---------------------------------------------------------------------------
+// Waves 0-3 carry the state (16 value columns each, fp32 in registers; the code
+// also allows two waves of 32 columns, which measured slower) and read a chunk's
+// operands only from LDS; waves 4-7 load the operands. Two LDS buffers and two
+// register sets in the loading waves keep every chunk's loads two iterations ahead of
+// its products: in iteration i the loaders commit chunk i + 1 (loaded during
+// iteration i - 2) to the buffer freed by chunk i - 1, then load chunk i + 3 into the
+// registers they just emptied.
+constexpr int kStateWaves = 4;
+constexpr int kCThreads = (kStateWaves + 4) * 64;
+
 template <int DK, int DV>
-__global__ __launch_bounds__(kWThreads) void kda_wy_chain_kernel(
+__global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
     const uint16_t* ws, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
     const float* __restrict__ init_state, uint16_t* __restrict__ out, float* __restrict__ final_state,
     int num_seqs, int H, int64_t total_tokens, int max_chunks)
@@ -434,17 +461,21 @@ __global__ __launch_bounds__(kWThreads) void kda_wy_chain_kernel(
     using Lay = WyLayout<DK, DV>;
     constexpr int NKB = Lay::NKB, NCT = Lay::NCT;
     constexpr int NVT64 = DV / 64;
+    constexpr int CPW = 4 / kStateWaves;           // 16-column tiles per state wave
     constexpr int SH16 = Lay::SHARED * 2 / 16;     // 16-byte pieces of the shared operands
     constexpr int U16 = Lay::UTILE * 2 / 16;       // 16-byte pieces of this tile's U
     constexpr int NP = SH16 + U16;
-    constexpr int PER = (NP + kWThreads - 1) / kWThreads;
+    constexpr int LT = 256;                        // loading threads
+    constexpr int PER = (NP + LT - 1) / LT;        // pieces per loading thread
+    constexpr int BUF = PER * LT;                  // pieces per LDS buffer (padded)
 
     extern __shared__ __align__(16) unsigned char smem_raw[];
     u32x4* lds = reinterpret_cast<u32x4*>(smem_raw);
-    const uint16_t* sl = reinterpret_cast<const uint16_t*>(smem_raw);
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, g = lane >> 4;
+    const bool loader = wave >= kStateWaves;
+    const int ltid = tid - kStateWaves * 64;
 
     // the value tiles of one (sample, head) are 8 blocks apart: same XCD, shared L2
     const int b = blockIdx.x;
@@ -453,116 +484,200 @@ __global__ __launch_bounds__(kWThreads) void kda_wy_chain_kernel(
     if (unit >= num_seqs * H) return;
     const int n = unit / H, h = unit % H;
     const int c0 = min(chunk_off[n], max_chunks), c1 = min(chunk_off[n + 1], max_chunks);
+    const int nch = c1 - c0;
     int64_t s0, s1;
     sample_bounds(cu, n, total_tokens, s0, s1);
-    const int vc = 4 * vt + wave;               // this wave's 16 value columns
-    const int col = 16 * vc;
 
-    f32x4 S[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        if (init_state) {
-            const float* st = init_state + ((int64_t(n) * H + h) * DK + 16 * ct + 4 * g) * DV + col + r;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) S[ct][s] = st[s * DV];
-        } else {
-            S[ct] = zero4();
-        }
-    }
-
-    // operands of one chunk: the shared part and this value tile's U, 16 bytes per
-    // piece; piece p of thread tid is tid + 256 p (clamped, so every load is valid)
-    u32x4 pf[PER];
-    auto fetch = [&](int cc) __attribute__((always_inline)) {
+    // loading threads: piece j of chunk cc (clamped, so every load is valid)
+    u32x4 ra[PER], rb[PER];
+    auto fetch = [&](u32x4 (&dst)[PER], int i) __attribute__((always_inline)) {
+        const int cc = c0 + min(i, nch - 1);
         const u32x4* rec = reinterpret_cast<const u32x4*>(ws + (int64_t(cc) * H + h) * Lay::TOTAL);
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-            const int idx = min(tid + j * kWThreads, NP - 1);
-            pf[j] = rec[idx + (idx >= SH16 ? vt * U16 : 0)];
+            const int idx = min(ltid + j * LT, NP - 1);
+            dst[j] = rec[idx + (idx >= SH16 ? vt * U16 : 0)];
         }
     };
-    auto commit = [&]() __attribute__((always_inline)) {   // pieces past NP land in padding
+    // the compiler barrier keeps the next loads after the commit, so the two register
+    // sets are issued in the same order on every path into the loop
+    auto commit = [&](const u32x4 (&src)[PER], int bi) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < PER; ++j) lds[tid + j * kWThreads] = pf[j];
+        for (int j = 0; j < PER; ++j) lds[bi * BUF + ltid + j * LT] = src[j];   // pieces past NP land in padding
+        asm volatile("" ::: "memory");
     };
-    // The operands of chunk c are loaded while chunk c - 1 is computed and written
-    // to LDS at the top of iteration c; the workspace pointer is deliberately not
-    // __restrict__, so the loads are not moved down to their use.
-    if (c0 < c1) fetch(c0);
-    for (int c = c0; c < c1; ++c) {
-        commit();
-        lds_barrier();
-        fetch(min(c + 1, c1 - 1));              // next chunk's operands (unconditional, clamped)
 
-        Frag sf[NKB];                           // S as the B operand over key channels
+    // one chunk of products from LDS buffer bi, for this wave's CPW column tiles
+    auto products = [&](f32x4 (&S)[CPW][NCT], int i, int bi) __attribute__((always_inline)) {
+        const uint16_t* sl = reinterpret_cast<const uint16_t*>(lds + bi * BUF);
+        Frag sf[CPW][NKB];                      // S as the B operand over key channels
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) sf[kb] = EL::from_acc(S[2 * kb], S[2 * kb + 1]);
-        // Vn = U - W S: tile rt holds Vn[16rt + 4g + s][col + r]
-        f32x4 X[4];
+        for (int j = 0; j < CPW; ++j)
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            float u4[4];
-            unpack4(*reinterpret_cast<const uint2*>(sl + Lay::SHARED + ((wave * 4 + rt) * 64 + lane) * 4), u4);
-            X[rt] = f32x4{u4[0], u4[1], u4[2], u4[3]};
+            for (int kb = 0; kb < NKB; ++kb) sf[j][kb] = EL::from_acc(S[j][2 * kb], S[j][2 * kb + 1]);
+        // Vn = U - W S: tile (j, rt) holds Vn[16rt + 4g + s][16 vc_j + r]
+        f32x4 X[CPW][4];
+#pragma unroll
+        for (int j = 0; j < CPW; ++j)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                float u4[4];
+                unpack4(*reinterpret_cast<const uint2*>(sl + Lay::SHARED + (((CPW * wave + j) * 4 + rt) * 64 + lane) * 4), u4);
+                X[j][rt] = f32x4{u4[0], u4[1], u4[2], u4[3]};
+            }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const Frag wf{*reinterpret_cast<const uint4*>(sl + Lay::W + ((rt * NKB + kb) * 64 + lane) * 8)};
+#pragma unroll
+                for (int j = 0; j < CPW; ++j) X[j][rt] = EL::mma(wf, sf[j][kb], X[j][rt]);
+            }
+        // O^T = S^T Qh^T + Vn^T P^T: tile (j, rt) holds O[16rt + r][16 vc_j + 4g + s]
+        f32x4 O[CPW][4];
+#pragma unroll
+        for (int j = 0; j < CPW; ++j)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) O[j][rt] = zero4();
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const Frag qf{*reinterpret_cast<const uint4*>(sl + Lay::Q + ((rt * NKB + kb) * 64 + lane) * 8)};
+#pragma unroll
+                for (int j = 0; j < CPW; ++j) O[j][rt] = EL::mma(sf[j][kb], qf, O[j][rt]);
+            }
+        Frag vf[CPW][2];
+#pragma unroll
+        for (int j = 0; j < CPW; ++j) {
+            vf[j][0] = EL::from_acc(X[j][0], X[j][1]);
+            vf[j][1] = EL::from_acc(X[j][2], X[j][3]);
         }
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-                X[rt] = EL::mma(Frag{*reinterpret_cast<const uint4*>(sl + Lay::W + ((rt * NKB + kb) * 64 + lane) * 8)},
-                                sf[kb], X[rt]);
-        // O^T = S^T Qh^T + Vn^T P^T: tile rt holds O[16rt + r][col + 4g + s]
-        f32x4 O[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) O[rt] = zero4();
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-                O[rt] = EL::mma(sf[kb], Frag{*reinterpret_cast<const uint4*>(sl + Lay::Q + ((rt * NKB + kb) * 64 + lane) * 8)},
-                                O[rt]);
-        const Frag vf[2] = {EL::from_acc(X[0], X[1]), EL::from_acc(X[2], X[3])};
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-            for (int kb = 0; kb <= rt / 2; ++kb)
-                O[rt] = EL::mma(vf[kb], Frag{*reinterpret_cast<const uint4*>(sl + Lay::P + ((rt * 2 + kb) * 64 + lane) * 8)},
-                                O[rt]);
+            for (int kb = 0; kb <= rt / 2; ++kb) {
+                const Frag pf{*reinterpret_cast<const uint4*>(sl + Lay::P + ((rt * 2 + kb) * 64 + lane) * 8)};
+#pragma unroll
+                for (int j = 0; j < CPW; ++j) O[j][rt] = EL::mma(vf[j][kb], pf, O[j][rt]);
+            }
         // S <- diag(gamma) S + Kb^T Vn
         const float* gam = reinterpret_cast<const float*>(sl + Lay::G);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             const float4 g4 = *reinterpret_cast<const float4*>(gam + 16 * ct + 4 * g);
-            S[ct][0] *= g4.x; S[ct][1] *= g4.y; S[ct][2] *= g4.z; S[ct][3] *= g4.w;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                S[ct] = EL::mma(Frag{*reinterpret_cast<const uint4*>(sl + Lay::K + ((ct * 2 + kb) * 64 + lane) * 8)},
-                                vf[kb], S[ct]);
+            for (int j = 0; j < CPW; ++j) {
+                S[j][ct][0] *= g4.x; S[j][ct][1] *= g4.y; S[j][ct][2] *= g4.z; S[j][ct][3] *= g4.w;
+            }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const Frag kf{*reinterpret_cast<const uint4*>(sl + Lay::K + ((ct * 2 + kb) * 64 + lane) * 8)};
+#pragma unroll
+                for (int j = 0; j < CPW; ++j) S[j][ct] = EL::mma(kf, vf[j][kb], S[j][ct]);
+            }
         }
         // output rows of this chunk
-        const int64_t t0 = s0 + int64_t(c - c0) * kWC;
+        const int64_t t0 = s0 + int64_t(i) * kWC;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             const int64_t t = t0 + 16 * rt + r;
-            if (t < s1) *reinterpret_cast<uint2*>(out + (t * H + h) * DV + col + 4 * g) = pack4(O[rt]);
+            if (t < s1) {
+#pragma unroll
+                for (int j = 0; j < CPW; ++j)
+                    *reinterpret_cast<uint2*>(out + (t * H + h) * DV + 16 * (4 * vt + CPW * wave + j) + 4 * g) = pack4(O[j][rt]);
+            }
         }
-        lds_barrier();                          // every wave is done with this chunk's operands
+    };
+
+    // The two roles run separate loops with the same barrier sequence (one barrier
+    // after the prologue and one per chunk), so their registers never overlap.
+    KDA_PHASE_DECL
+    if (loader) {
+        // prologue: chunk 0 in buffer 0, chunks 1 and 2 in flight in ra and rb
+        if (nch > 0) {
+            fetch(ra, 0);
+            commit(ra, 0);
+            fetch(ra, 1);
+            asm volatile("" ::: "memory");      // all of ra is issued before any of rb
+            fetch(rb, 2);
+        }
+        lds_barrier();
+        // pairs of iterations; the loop always closes after the odd one, so the two
+        // register sets stay in the same issue order on every path
+        int i = 0;
+        KDA_PHASE_MARK(5);
+        for (; i + 1 < nch; i += 2) {
+            commit(ra, 1);                      // chunk i + 1 to buffer 1 (freed by chunk i - 1)
+            KDA_PHASE_MARK(2);
+            fetch(ra, i + 3);
+            KDA_PHASE_MARK(3);
+            lds_barrier();
+            KDA_PHASE_MARK(4);
+            commit(rb, 0);                      // chunk i + 2 to buffer 0 (freed by chunk i)
+            KDA_PHASE_MARK(2);
+            fetch(rb, i + 4);
+            KDA_PHASE_MARK(3);
+            lds_barrier();
+            KDA_PHASE_MARK(4);
+        }
+        if (i < nch) lds_barrier();             // last, even iteration: nothing left to load
+        KDA_PHASE_FLUSH
+        return;
     }
 
+    f32x4 S[CPW][NCT];
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) S[j][ct] = zero4();
+    if (init_state) {
+#pragma unroll
+        for (int j = 0; j < CPW; ++j)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const float* st = init_state + ((int64_t(n) * H + h) * DK + 16 * ct + 4 * g) * DV +
+                                  16 * (4 * vt + CPW * wave + j) + r;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) S[j][ct][s] = st[s * DV];
+            }
+    }
+    lds_barrier();
+    KDA_PHASE_MARK(5);
+    int i = 0;
+    for (; i + 1 < nch; i += 2) {
+        products(S, i, 0);
+        KDA_PHASE_MARK(0);
+        lds_barrier();
+        KDA_PHASE_MARK(1);
+        products(S, i + 1, 1);
+        KDA_PHASE_MARK(0);
+        lds_barrier();
+        KDA_PHASE_MARK(1);
+    }
+    if (i < nch) {
+        products(S, i, 0);
+        lds_barrier();
+    }
+    KDA_PHASE_FLUSH
     if (final_state) {
-        float* fs = final_state + ((int64_t(n) * H + h) * DK) * DV + col + r;
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
+        for (int j = 0; j < CPW; ++j) {
+            float* fs = final_state + ((int64_t(n) * H + h) * DK) * DV + 16 * (4 * vt + CPW * wave + j) + r;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) fs[int64_t(16 * ct + 4 * g + s) * DV] = S[ct][s];
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) fs[int64_t(16 * ct + 4 * g + s) * DV] = S[j][ct][s];
+        }
     }
 }
 
-// LDS of the chain kernel: one chunk's operands, padded to whole 16-byte pieces per thread
+// LDS of the chain kernel: two buffers of one chunk's operands, each padded to whole
+// 16-byte pieces per loading thread
 template <int DK, int DV>
 constexpr size_t chain_smem() {
     constexpr int np = (WyLayout<DK, DV>::SHARED + WyLayout<DK, DV>::UTILE) * 2 / 16;
-    return size_t((np + kWThreads - 1) / kWThreads) * kWThreads * 16;
+    return 2 * size_t((np + 255) / 256) * 256 * 16;
 }
 
 template <int DK, int DV>
@@ -587,7 +702,7 @@ hipError_t launch_dims(const LaunchArgs& a, uint16_t* ws, int32_t* chunk_off, in
     const int nvt = a.d_v / 64;
     const int blocks = ((units + 7) / 8) * 8 * nvt;
     if (th) th->begin("chain", a.stream);
-    hipLaunchKernelGGL((kda_wy_chain_kernel<DK, DV>), dim3(blocks), dim3(kWThreads), smem, a.stream,
+    hipLaunchKernelGGL((kda_wy_chain_kernel<DK, DV>), dim3(blocks), dim3(kCThreads), smem, a.stream,
                        ws, a.cu_seqlens, chunk_off, a.init_state, static_cast<uint16_t*>(a.out),
                        a.final_state, a.num_seqs, a.num_heads, a.total_tokens, max_chunks);
     if (th) th->end(a.stream);
