@@ -3,11 +3,17 @@
 python -m delta_rule_recurrent_kda_amd.profile_summary trace DB [--kernel NAME]
 python -m delta_rule_recurrent_kda_amd.profile_summary traffic FETCH_DB WRITE_DB --calib-bytes N
     [--kernel NAME] [--out JSON] [--workload W] [--kernel-sha SHA]
+python -m delta_rule_recurrent_kda_amd.profile_summary mfma DB --trace TRACE_DB [--kernel NAME]
 
 `trace` prints per-kernel call counts and durations. `traffic` scales the
-FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) of the scan kernel by the
+FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) of one kernel by the
 ratio the same counters read for a plain device copy of known size, giving
-HBM bytes per launch.
+HBM bytes per launch. `mfma` reads SQ_VALU_MFMA_BUSY_CYCLES,
+SQ_INSTS_VALU_MFMA_MOPS_BF16 / _F32 and GRBM_GUI_ACTIVE per dispatch of one
+kernel: matrix-core busy fraction (busy cycles over active cycles times the
+1024 SIMDs; the stored GRBM_GUI_ACTIVE is the sum over the 8 XCDs, so one XCD's
+active cycles are a eighth of it) and MFMA flops (512 per counted op), priced
+against the kernel's mean duration from a kernel-trace database.
 """
 from __future__ import annotations
 
@@ -67,6 +73,29 @@ def traffic(fetch_db: str, write_db: str, calib_bytes: int, kernel: str = "kda_f
             "dispatches": len(kf)}
 
 
+SIMD_NUM = 1024     # 256 CUs x 4 SIMDs
+XCD_NUM = 8
+
+
+def mfma(db: str, trace_db: str, kernel: str):
+    def per_dispatch(name):
+        vals = [v for _, n, _, v, _ in counters(db, name) if kernel in n]
+        return statistics.mean(vals) if vals else None
+    busy = per_dispatch("SQ_VALU_MFMA_BUSY_CYCLES")
+    gui = per_dispatch("GRBM_GUI_ACTIVE")
+    bf16 = per_dispatch("SQ_INSTS_VALU_MFMA_MOPS_BF16") or 0.0
+    f32 = per_dispatch("SQ_INSTS_VALU_MFMA_MOPS_F32") or 0.0
+    durs = [k for k in kernel_stats(trace_db) if kernel in k["name"]]
+    avg_ns = durs[0]["avg_ns"] if durs else None
+    rec = {"kernel": kernel, "mfma_busy_cycles": busy, "gui_active_cycles": gui,
+           "mfma_busy_frac": (busy / (gui / XCD_NUM * SIMD_NUM)) if busy and gui else None,
+           "bf16_flops": bf16 * 512, "f32_flops": f32 * 512, "avg_ns": avg_ns}
+    if avg_ns:
+        rec["bf16_tflops"] = bf16 * 512 / (avg_ns * 1e-9) / 1e12
+        rec["f32_tflops"] = f32 * 512 / (avg_ns * 1e-9) / 1e12
+    return rec
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -80,7 +109,14 @@ def main(argv=None):
     c.add_argument("--out")
     c.add_argument("--workload", default="")
     c.add_argument("--kernel-sha", default="")
+    m = sub.add_parser("mfma")
+    m.add_argument("db")
+    m.add_argument("--trace", required=True)
+    m.add_argument("--kernel", default="kda_wy_chain_kernel")
     a = ap.parse_args(argv)
+    if a.cmd == "mfma":
+        print(json.dumps(mfma(a.db, a.trace, a.kernel), indent=1))
+        return 0
     if a.cmd == "trace":
         for k in kernel_stats(a.db):
             print(f"{k['calls']:6d} calls  avg {k['avg_ns'] / 1e3:10.2f} us  min {k['min_ns'] / 1e3:10.2f} us  "
