@@ -46,6 +46,8 @@ struct TimingHook {
 // `workspace` must hold wy_workspace_bytes(...) bytes, 256-byte aligned.
 hipError_t launch_forward_wy(const LaunchArgs& a, void* workspace, TimingHook* th);
 size_t wy_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads, int d_k, int d_v);
+// Bytes of one (64-token chunk, head) record of the workspace.
+size_t wy_record_bytes(int d_k, int d_v);
 
 // LDS bytes one workgroup uses.
 size_t smem_bytes(int dtype_bf16, int d_k);

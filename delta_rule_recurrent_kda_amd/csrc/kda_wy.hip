@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -70,36 +72,50 @@ __device__ __forceinline__ void unpack4(const uint2& u, float (&f)[4]) {
 }
 
 // ---------------------------------------------------------------------------
-// plan: chunk_off[n] = number of chunks of the samples before n (one workgroup)
+// plan (one workgroup): chunk_off[n] = number of chunks of the samples before n;
+// seg_off[n] = number of segments before n, where a sample of c chunks has
+// ceil(c / lseg) segments of lseg chunks (at least one; one when lseg = 0)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void kda_wy_plan_kernel(const int32_t* __restrict__ cu,
                                                            int32_t* __restrict__ chunk_off,
-                                                           int num_seqs, int64_t total_tokens)
+                                                           int32_t* __restrict__ seg_off, int num_seqs,
+                                                           int64_t total_tokens, int lseg)
 {
-    __shared__ int32_t part[1024];
+    __shared__ int32_t part[1024], segp[1024];
     const int tid = threadIdx.x;
-    int32_t carry = 0;
+    int32_t carry = 0, scarry = 0;
     for (int base = 0; base < num_seqs; base += 1024) {
         const int n = base + tid;
-        int32_t cnt = 0;
+        int32_t cnt = 0, nseg = 0;
         if (n < num_seqs) {
             const int64_t s0 = min<int64_t>(max<int64_t>(cu[n], 0), total_tokens);
             const int64_t s1 = min<int64_t>(max<int64_t>(cu[n + 1], s0), total_tokens);
             cnt = int32_t((s1 - s0 + kWC - 1) / kWC);
+            nseg = lseg > 0 ? max(1, (cnt + lseg - 1) / lseg) : 1;
         }
         part[tid] = cnt;
+        segp[tid] = nseg;
         __syncthreads();
-        for (int d = 1; d < 1024; d <<= 1) {          // inclusive scan
+        for (int d = 1; d < 1024; d <<= 1) {          // inclusive scans
             const int32_t add = tid >= d ? part[tid - d] : 0;
+            const int32_t sadd = tid >= d ? segp[tid - d] : 0;
             __syncthreads();
             part[tid] += add;
+            segp[tid] += sadd;
             __syncthreads();
         }
-        if (n < num_seqs) chunk_off[n + 1] = carry + part[tid];
+        if (n < num_seqs) {
+            chunk_off[n + 1] = carry + part[tid];
+            seg_off[n + 1] = scarry + segp[tid];
+        }
         carry += part[1023];
+        scarry += segp[1023];
         __syncthreads();
     }
-    if (tid == 0) chunk_off[0] = 0;
+    if (tid == 0) {
+        chunk_off[0] = 0;
+        seg_off[0] = 0;
+    }
 }
 
 // clamped sample bounds, so that malformed offsets never address outside the tokens
@@ -450,11 +466,19 @@ __global__ __launch_bounds__(kWThreads, 2) void kda_wy_prep_kernel(
 constexpr int kStateWaves = 4;
 constexpr int kCThreads = (kStateWaves + 4) * 64;
 
-template <int DK, int DV>
+// MODE 0: one workgroup walks a whole sample.
+// MODE 1 (sequence split, first pass): per segment that is not the last of its
+// sample, the state reached from zero (S_loc, value tiles) and the segment's
+// transition Phi (d_k columns: identity start, U taken as zero), written to sloc / phi.
+// MODE 2 (second pass): per segment, the state on entry from the prefix
+// S_in(k) = Phi(k-1) S_in(k-1) + S_loc(k-1) starting at the sample's initial state,
+// then the segment's chunks with outputs; the last segment writes final_state.
+template <int DK, int DV, int MODE>
 __global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
     const uint16_t* ws, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
     const float* __restrict__ init_state, uint16_t* __restrict__ out, float* __restrict__ final_state,
-    int num_seqs, int H, int64_t total_tokens, int max_chunks)
+    int num_seqs, int H, int64_t total_tokens, int max_chunks, const int32_t* __restrict__ seg_off,
+    int lseg, int max_segs, float* __restrict__ sloc, float* __restrict__ phi)
 {
     using EL = Elt<uint16_t>;
     using Frag = EL::Frag;
@@ -477,17 +501,42 @@ __global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
     const bool loader = wave >= kStateWaves;
     const int ltid = tid - kStateWaves * 64;
 
-    // the value tiles of one (sample, head) are 8 blocks apart: same XCD, shared L2
+    // the column tiles of one unit are 8 blocks apart: same XCD, shared L2
+    constexpr int NT = MODE == 1 ? NVT64 + DK / 64 : NVT64;      // column tiles per unit
     const int b = blockIdx.x;
-    const int vt = (b >> 3) % NVT64;
-    const int unit = (b / (8 * NVT64)) * 8 + (b & 7);
-    if (unit >= num_seqs * H) return;
-    const int n = unit / H, h = unit % H;
-    const int c0 = min(chunk_off[n], max_chunks), c1 = min(chunk_off[n + 1], max_chunks);
+    const int tile = (b >> 3) % NT;
+    const int unit = (b / (8 * NT)) * 8 + (b & 7);
+    const bool trans = MODE == 1 && tile >= NVT64;               // a tile of Phi
+    const int vt = trans ? 0 : tile;                             // value tile of U to load
+    int n, h, seg = 0, nseg = 1, sid = 0;
+    if constexpr (MODE == 0) {
+        if (unit >= num_seqs * H) return;
+        n = unit / H;
+        h = unit % H;
+    } else {
+        const int ns = min(seg_off[num_seqs], max_segs);        // the workspace holds max_segs segments
+        if (unit >= ns * H) return;
+        sid = unit / H;
+        h = unit % H;
+        int lo = 0, hi = num_seqs;              // seg_off[lo] <= sid < seg_off[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (seg_off[mid] <= sid) lo = mid; else hi = mid;
+        }
+        n = lo;
+        seg = sid - seg_off[n];
+        nseg = seg_off[n + 1] - seg_off[n];
+        if (MODE == 1 && seg == nseg - 1) return;                // the last segment needs no transition
+    }
+    int c0 = min(chunk_off[n], max_chunks), c1 = min(chunk_off[n + 1], max_chunks);
+    if constexpr (MODE != 0) {
+        c0 = min(c0 + seg * lseg, c1);
+        c1 = min(c0 + lseg, c1);
+    }
     const int nch = c1 - c0;
     int64_t s0, s1;
     sample_bounds(cu, n, total_tokens, s0, s1);
-
+    if constexpr (MODE != 0) s0 += int64_t(seg) * lseg * kWC;    // first token of the segment
     // loading threads: piece j of chunk cc (clamped, so every load is valid)
     u32x4 ra[PER], rb[PER];
     auto fetch = [&](u32x4 (&dst)[PER], int i) __attribute__((always_inline)) {
@@ -523,7 +572,7 @@ __global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
             for (int rt = 0; rt < 4; ++rt) {
                 float u4[4];
                 unpack4(*reinterpret_cast<const uint2*>(sl + Lay::SHARED + (((CPW * wave + j) * 4 + rt) * 64 + lane) * 4), u4);
-                X[j][rt] = f32x4{u4[0], u4[1], u4[2], u4[3]};
+                X[j][rt] = trans ? zero4() : f32x4{u4[0], u4[1], u4[2], u4[3]};
             }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -578,14 +627,16 @@ __global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
             }
         }
         // output rows of this chunk
-        const int64_t t0 = s0 + int64_t(i) * kWC;
+        if constexpr (MODE != 1) {
+            const int64_t t0 = s0 + int64_t(i) * kWC;
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            const int64_t t = t0 + 16 * rt + r;
-            if (t < s1) {
+            for (int rt = 0; rt < 4; ++rt) {
+                const int64_t t = t0 + 16 * rt + r;
+                if (t < s1) {
 #pragma unroll
-                for (int j = 0; j < CPW; ++j)
-                    *reinterpret_cast<uint2*>(out + (t * H + h) * DV + 16 * (4 * vt + CPW * wave + j) + 4 * g) = pack4(O[j][rt]);
+                    for (int j = 0; j < CPW; ++j)
+                        *reinterpret_cast<uint2*>(out + (t * H + h) * DV + 16 * (4 * vt + CPW * wave + j) + 4 * g) = pack4(O[j][rt]);
+                }
             }
         }
     };
@@ -626,12 +677,21 @@ __global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
         return;
     }
 
+    // column c of this wave's tile j: 16 * (4 * tile + CPW * wave + j) + r
     f32x4 S[CPW][NCT];
 #pragma unroll
     for (int j = 0; j < CPW; ++j)
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) S[j][ct] = zero4();
-    if (init_state) {
+    if (trans) {                                // Phi starts at the identity
+#pragma unroll
+        for (int j = 0; j < CPW; ++j)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    S[j][ct][s] = (16 * ct + 4 * g + s == 16 * (4 * (tile - NVT64) + CPW * wave + j) + r) ? 1.f : 0.f;
+    } else if (init_state && MODE != 1) {
 #pragma unroll
         for (int j = 0; j < CPW; ++j)
 #pragma unroll
@@ -641,6 +701,55 @@ __global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
 #pragma unroll
                 for (int s = 0; s < 4; ++s) S[j][ct][s] = st[s * DV];
             }
+    }
+    if constexpr (MODE == 2) {
+        // S_in(seg) = Phi(k) S_in(k) + S_loc(k) for k < seg, with hi/lo bf16 operands
+        for (int kseg = 0; kseg < seg; ++kseg) {
+            const int64_t ks = int64_t(seg_off[n] + kseg) * H + h;
+            const float* ph = phi + ks * DK * DK;
+            const float* sl0 = sloc + ks * DK * DV;
+#pragma unroll
+            for (int j = 0; j < CPW; ++j) {
+                const int colj = 16 * (4 * vt + CPW * wave + j) + r;
+                Frag shi[NKB], slo[NKB];
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    f32x4 l0, l1;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        l0[s] = S[j][2 * kb][s] - bf2f(f2bf(S[j][2 * kb][s]));
+                        l1[s] = S[j][2 * kb + 1][s] - bf2f(f2bf(S[j][2 * kb + 1][s]));
+                    }
+                    shi[kb] = EL::from_acc(S[j][2 * kb], S[j][2 * kb + 1]);
+                    slo[kb] = EL::from_acc(l0, l1);
+                }
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    f32x4 acc;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) acc[s] = sl0[int64_t(16 * ct + 4 * g + s) * DV + colj];
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb) {
+                        // Phi rows 16ct + r, k = 32kb + 16t + 4g + i, as hi and lo A operands
+                        const float* pr = ph + int64_t(16 * ct + r) * DK + 32 * kb + 4 * g;
+                        const float4 p0 = *reinterpret_cast<const float4*>(pr);
+                        const float4 p1 = *reinterpret_cast<const float4*>(pr + 16);
+                        const f32x4 a0{p0.x, p0.y, p0.z, p0.w}, a1{p1.x, p1.y, p1.z, p1.w};
+                        f32x4 b0, b1;
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) {
+                            b0[s] = a0[s] - bf2f(f2bf(a0[s]));
+                            b1[s] = a1[s] - bf2f(f2bf(a1[s]));
+                        }
+                        const Frag ahi = EL::from_acc(a0, a1), alo = EL::from_acc(b0, b1);
+                        acc = EL::mma(ahi, shi[kb], acc);
+                        acc = EL::mma(ahi, slo[kb], acc);
+                        acc = EL::mma(alo, shi[kb], acc);
+                    }
+                    S[j][ct] = acc;     // safe: later ct read only shi / slo, taken before the loop
+                }
+            }
+        }
     }
     lds_barrier();
     KDA_PHASE_MARK(5);
@@ -660,7 +769,21 @@ __global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
         lds_barrier();
     }
     KDA_PHASE_FLUSH
-    if (final_state) {
+    if constexpr (MODE == 1) {
+        // segment result: S_loc (value tiles) or Phi (transition tiles)
+        const int64_t ks = int64_t(sid) * H + h;
+        float* dst = trans ? phi + ks * DK * DK : sloc + ks * DK * DV;
+        const int ld = trans ? DK : DV;
+        const int tc = trans ? tile - NVT64 : vt;
+#pragma unroll
+        for (int j = 0; j < CPW; ++j) {
+            float* fs = dst + 16 * (4 * tc + CPW * wave + j) + r;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) fs[int64_t(16 * ct + 4 * g + s) * ld] = S[j][ct][s];
+        }
+    } else if (final_state && seg == nseg - 1) {
 #pragma unroll
         for (int j = 0; j < CPW; ++j) {
             float* fs = final_state + ((int64_t(n) * H + h) * DK) * DV + 16 * (4 * vt + CPW * wave + j) + r;
@@ -680,33 +803,83 @@ constexpr size_t chain_smem() {
     return 2 * size_t((np + 255) / 256) * 256 * 16;
 }
 
-template <int DK, int DV>
-hipError_t launch_dims(const LaunchArgs& a, uint16_t* ws, int32_t* chunk_off, int max_chunks, TimingHook* th)
+struct WyPlan {
+    int max_chunks;
+    int lseg;          // chunks per segment of the sequence split; 0 = no split
+    int max_segs;
+    size_t table_bytes, rec_bytes, sloc_bytes, phi_bytes;
+};
+
+template <int DK, int DV, int MODE>
+hipError_t launch_chain(const LaunchArgs& a, const uint16_t* ws, const int32_t* chunk_off, const int32_t* seg_off,
+                        const WyPlan& p, float* sloc, float* phi)
 {
-    const int units = a.num_seqs * a.num_heads;
-    dim3 pgrid(max_chunks, a.num_heads);
+    constexpr size_t smem = chain_smem<DK, DV>();
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_wy_chain_kernel<DK, DV, MODE>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+    if (e != hipSuccess) return e;
+    const int nt = MODE == 1 ? (DV + DK) / 64 : DV / 64;
+    const int units = (MODE == 0 ? a.num_seqs : p.max_segs) * a.num_heads;
+    const int blocks = ((units + 7) / 8) * 8 * nt;
+    hipLaunchKernelGGL((kda_wy_chain_kernel<DK, DV, MODE>), dim3(blocks), dim3(kCThreads), smem, a.stream,
+                       ws, a.cu_seqlens, chunk_off, a.init_state, static_cast<uint16_t*>(a.out), a.final_state,
+                       a.num_seqs, a.num_heads, a.total_tokens, p.max_chunks, seg_off, p.lseg, p.max_segs,
+                       sloc, phi);
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch_dims(const LaunchArgs& a, uint16_t* ws, const int32_t* chunk_off, const int32_t* seg_off,
+                       const WyPlan& p, float* sloc, float* phi, TimingHook* th)
+{
+    dim3 pgrid(p.max_chunks, a.num_heads);
     if (th) th->begin("prep", a.stream);
     hipLaunchKernelGGL((kda_wy_prep_kernel<DK, DV>), pgrid, dim3(kWThreads), 0, a.stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.log_alpha),
                        static_cast<const uint16_t*>(a.beta), a.cu_seqlens, chunk_off, ws, a.num_seqs,
-                       a.num_heads, a.total_tokens, max_chunks);
+                       a.num_heads, a.total_tokens, p.max_chunks);
     if (th) th->end(a.stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-
-    constexpr size_t smem = chain_smem<DK, DV>();
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_wy_chain_kernel<DK, DV>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
-    if (e != hipSuccess) return e;
-    const int nvt = a.d_v / 64;
-    const int blocks = ((units + 7) / 8) * 8 * nvt;
-    if (th) th->begin("chain", a.stream);
-    hipLaunchKernelGGL((kda_wy_chain_kernel<DK, DV>), dim3(blocks), dim3(kCThreads), smem, a.stream,
-                       ws, a.cu_seqlens, chunk_off, a.init_state, static_cast<uint16_t*>(a.out),
-                       a.final_state, a.num_seqs, a.num_heads, a.total_tokens, max_chunks);
+    if (p.lseg == 0) {
+        if (th) th->begin("chain", a.stream);
+        e = launch_chain<DK, DV, 0>(a, ws, chunk_off, seg_off, p, sloc, phi);
+        if (th) th->end(a.stream);
+        return e;
+    }
+    if (th) th->begin("segments", a.stream);
+    e = launch_chain<DK, DV, 1>(a, ws, chunk_off, seg_off, p, sloc, phi);
     if (th) th->end(a.stream);
-    return hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (th) th->begin("chain", a.stream);
+    e = launch_chain<DK, DV, 2>(a, ws, chunk_off, seg_off, p, sloc, phi);
+    if (th) th->end(a.stream);
+    return e;
+}
+
+// Sequence split: when the samples give at most 64 chain workgroups (a quarter of the
+// CUs or less), each sample is cut into segments of lseg chunks so that about 256
+// workgroups run the second pass.
+WyPlan make_plan(int64_t total_tokens, int32_t num_seqs, int32_t num_heads, int d_k, int d_v)
+{
+    WyPlan p{};
+    const int64_t chunks_bound = (total_tokens + kWC - 1) / kWC;
+    p.max_chunks = int(chunks_bound + num_seqs);
+    const int64_t chain_units = int64_t(num_seqs) * num_heads * (d_v / 64);
+    p.lseg = 0;
+    if (chain_units <= 64) {
+        const int64_t segs = std::max<int64_t>(1, 256 / (int64_t(num_heads) * (d_v / 64)));
+        const int64_t lseg = std::max<int64_t>(32, (chunks_bound + segs - 1) / segs);
+        if (lseg < chunks_bound) p.lseg = int(lseg);
+    }
+    p.max_segs = p.lseg ? int((chunks_bound + num_seqs + p.lseg - 1) / p.lseg + num_seqs) : num_seqs;
+    const size_t tab = 2 * (size_t(num_seqs) + 1) * sizeof(int32_t);
+    p.table_bytes = (tab + 255) & ~size_t(255);
+    p.rec_bytes = size_t(p.max_chunks) * size_t(num_heads) * wy_record_bytes(d_k, d_v);
+    p.sloc_bytes = p.lseg ? size_t(p.max_segs) * num_heads * d_k * d_v * sizeof(float) : 0;
+    p.phi_bytes = p.lseg ? size_t(p.max_segs) * num_heads * d_k * d_k * sizeof(float) : 0;
+    return p;
 }
 
 }  // namespace
@@ -719,38 +892,34 @@ size_t wy_record_bytes(int d_k, int d_v)
     return size_t(WyLayout<64, 64>::TOTAL) * 2;
 }
 
-int64_t wy_max_chunks(int64_t total_tokens, int32_t num_seqs)
-{
-    return (total_tokens + kWC - 1) / kWC + num_seqs;
-}
-
 size_t wy_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads, int d_k, int d_v)
 {
-    const size_t off = (size_t(num_seqs) + 1) * sizeof(int32_t);
-    const size_t off_al = (off + 255) & ~size_t(255);
-    return off_al + size_t(wy_max_chunks(total_tokens, num_seqs)) * size_t(num_heads) * wy_record_bytes(d_k, d_v);
+    const WyPlan p = make_plan(total_tokens, num_seqs, num_heads, d_k, d_v);
+    return p.table_bytes + p.rec_bytes + p.sloc_bytes + p.phi_bytes;
 }
 
 hipError_t launch_forward_wy(const LaunchArgs& a, void* workspace, TimingHook* th)
 {
-    const int64_t mc = wy_max_chunks(a.total_tokens, a.num_seqs);
-    if (mc > 0x7FFFFFFF / 2) return hipErrorInvalidValue;
-    const int max_chunks = int(mc);
-    int32_t* chunk_off = static_cast<int32_t*>(workspace);
-    const size_t off = (size_t(a.num_seqs) + 1) * sizeof(int32_t);
-    uint16_t* ws = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + ((off + 255) & ~size_t(255)));
+    const WyPlan p = make_plan(a.total_tokens, a.num_seqs, a.num_heads, a.d_k, a.d_v);
+    if (int64_t(p.max_chunks) * a.num_heads > 0x7FFFFFFF / 8) return hipErrorInvalidValue;
+    char* base = static_cast<char*>(workspace);
+    int32_t* chunk_off = reinterpret_cast<int32_t*>(base);
+    int32_t* seg_off = chunk_off + (a.num_seqs + 1);
+    uint16_t* ws = reinterpret_cast<uint16_t*>(base + p.table_bytes);
+    float* sloc = p.lseg ? reinterpret_cast<float*>(base + p.table_bytes + p.rec_bytes) : nullptr;
+    float* phi = p.lseg ? reinterpret_cast<float*>(base + p.table_bytes + p.rec_bytes + p.sloc_bytes) : nullptr;
 
     if (th) th->begin("plan", a.stream);
-    hipLaunchKernelGGL(kda_wy_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, chunk_off,
-                       a.num_seqs, a.total_tokens);
+    hipLaunchKernelGGL(kda_wy_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, chunk_off, seg_off,
+                       a.num_seqs, a.total_tokens, p.lseg);
     if (th) th->end(a.stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    if (a.d_k == 128 && a.d_v == 128) return launch_dims<128, 128>(a, ws, chunk_off, max_chunks, th);
-    if (a.d_k == 128 && a.d_v == 64) return launch_dims<128, 64>(a, ws, chunk_off, max_chunks, th);
-    if (a.d_k == 64 && a.d_v == 128) return launch_dims<64, 128>(a, ws, chunk_off, max_chunks, th);
-    return launch_dims<64, 64>(a, ws, chunk_off, max_chunks, th);
+    if (a.d_k == 128 && a.d_v == 128) return launch_dims<128, 128>(a, ws, chunk_off, seg_off, p, sloc, phi, th);
+    if (a.d_k == 128 && a.d_v == 64) return launch_dims<128, 64>(a, ws, chunk_off, seg_off, p, sloc, phi, th);
+    if (a.d_k == 64 && a.d_v == 128) return launch_dims<64, 128>(a, ws, chunk_off, seg_off, p, sloc, phi, th);
+    return launch_dims<64, 64>(a, ws, chunk_off, seg_off, p, sloc, phi, th);
 }
 
 }  // namespace kda

@@ -127,11 +127,22 @@ def test_workspace_bytes(lib):
     def record(dk, dv):
         return 2 * (4 * dk // 32 * 512) * 2 + (dk // 16) * 2 * 1024 + 8192 + 4 * dk + (dv // 16) * 2048
     assert record(128, 128) == rec[(128, 128)] and record(128, 64) == rec[(128, 64)]
+    # chunk and segment offset tables (rounded up to 256 bytes), one record per
+    # (64-token chunk, head) for the upper bound ceil(T / 64) + N of chunks, and, when the
+    # chain would get at most 64 workgroups, per-segment local states and transitions (fp32)
     for T, N, H, dk, dv in [(17108, 8, 16, 128, 128), (1, 1, 1, 64, 64), (189272, 1, 16, 128, 64),
-                            (640, 300, 3, 64, 128)]:
-        chunks = (T + 63) // 64 + N
-        table = ((N + 1) * 4 + 255) // 256 * 256
-        assert kda.workspace_bytes(T, N, H, dk, dv, kda.KDA_BF16) == table + chunks * H * record(dk, dv)
+                            (640, 300, 3, 64, 128), (189272, 1, 16, 128, 128), (5000, 1, 2, 128, 128)]:
+        bound = (T + 63) // 64
+        chunks = bound + N
+        table = (2 * (N + 1) * 4 + 255) // 256 * 256
+        expect = table + chunks * H * record(dk, dv)
+        if N * H * (dv // 64) <= 64:
+            segs = max(1, 256 // (H * (dv // 64)))
+            lseg = max(32, (bound + segs - 1) // segs)
+            if lseg < bound:
+                max_segs = (bound + N + lseg - 1) // lseg + N
+                expect += max_segs * H * dk * (dv + dk) * 4
+        assert kda.workspace_bytes(T, N, H, dk, dv, kda.KDA_BF16) == expect, (T, N, H, dk, dv)
     assert kda.workspace_bytes(1000, 2, 2, 128, 128, kda.KDA_F32) == 0
     assert kda.workspace_bytes(1000, 0, 2, 128, 128, kda.KDA_BF16) == 0
     assert kda.workspace_bytes(1000, 2, 2, 96, 128, kda.KDA_BF16) == 0

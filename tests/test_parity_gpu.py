@@ -174,6 +174,45 @@ def test_split_scan_matches_one_pass():
         gu.compare(spec, out, f2.cpu().double().numpy(), o_ref, f_ref, label=f"split at {cut}")
 
 
+# The sequence split cuts a sample into segments when the chain would otherwise use at
+# most 64 workgroups: one pass gives each segment's transition and local state, a
+# second pass scans every segment from its true initial state.
+SPLIT = [
+    ("one_long", [5000], 2, 128, 128),            # 3 segments of 32 chunks
+    ("ragged_pack", [3000, 0, 2100, 70], 1, 128, 128),
+    ("d64", [4100, 900], 2, 64, 64),
+    ("dk128_dv64", [2600], 3, 128, 64),
+]
+
+
+@pytest.mark.parametrize("name,lens,H,dk,dv", SPLIT, ids=[c[0] for c in SPLIT])
+def test_sequence_split(name, lens, H, dk, dv):
+    from delta_rule_recurrent_kda_amd import kda
+    timing = {}
+    for k in ("segments", "chain"):
+        kda.timing_read(k)
+    kda.timing_enable(True)
+    try:
+        spec = inputs.KdaSpec(f"split_{name}", tuple(lens), H, dk, dv, "bf16", (0.0005, 0.05), 6161)
+        _check(spec, label=f"split {name}")
+    finally:
+        kda.timing_enable(False)
+        for k in ("segments", "chain"):
+            timing[k] = kda.timing_read(k)[0]
+    assert timing["segments"] == 1 and timing["chain"] == 1, timing   # the split path ran
+
+
+def test_sequence_split_from_state():
+    import torch
+    spec = inputs.KdaSpec("split_init", (4500, 700), 2, 128, 128, "bf16", (0.0005, 0.05), 7171)
+    a = inputs.generate(spec)
+    d = gu.device_inputs(spec, a)
+    s0 = (np.random.default_rng(19).standard_normal((2, 2, 128, 128)) * 0.5).astype(np.float32)
+    out, fs = gu.run_hip(spec, d, initial_state=torch.from_numpy(s0).to("cuda:0"))
+    o_ref, f_ref = gu.oracle_ref(spec, a, initial_state=s0.astype(np.float64))
+    gu.compare(spec, out, fs, o_ref, f_ref, label="split from state")
+
+
 def test_kernel_timing_records_each_kernel():
     import torch
     from delta_rule_recurrent_kda_amd import kda
