@@ -458,13 +458,11 @@ __global__ __launch_bounds__(kWThreads, 2) void kda_wy_prep_kernel(
 // ---------------------------------------------------------------------------
 // Waves 0-3 carry the state (16 value columns each, fp32 in registers; the code
 // also allows two waves of 32 columns, which measured slower) and read a chunk's
-// operands only from LDS; waves 4-7 load the operands. Two LDS buffers and two
-// register sets in the loading waves keep every chunk's loads two iterations ahead of
-// its products: in iteration i the loaders commit chunk i + 1 (loaded during
-// iteration i - 2) to the buffer freed by chunk i - 1, then load chunk i + 3 into the
-// registers they just emptied.
+// operands only from LDS; waves 4-7 move the next chunk's operands from the
+// workspace into the other of two LDS buffers with global-to-LDS transfers.
 constexpr int kStateWaves = 4;
-constexpr int kCThreads = (kStateWaves + 4) * 64;
+constexpr int kLoadWaves = 4;
+constexpr int kCThreads = (kStateWaves + kLoadWaves) * 64;
 
 // MODE 0: one workgroup walks a whole sample.
 // MODE 1 (sequence split, first pass): per segment that is not the last of its
@@ -489,7 +487,7 @@ __global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
     constexpr int SH16 = Lay::SHARED * 2 / 16;     // 16-byte pieces of the shared operands
     constexpr int U16 = Lay::UTILE * 2 / 16;       // 16-byte pieces of this tile's U
     constexpr int NP = SH16 + U16;
-    constexpr int LT = 256;                        // loading threads
+    constexpr int LT = kLoadWaves * 64;            // loading threads
     constexpr int PER = (NP + LT - 1) / LT;        // pieces per loading thread
     constexpr int BUF = PER * LT;                  // pieces per LDS buffer (padded)
 
@@ -537,23 +535,29 @@ __global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
     int64_t s0, s1;
     sample_bounds(cu, n, total_tokens, s0, s1);
     if constexpr (MODE != 0) s0 += int64_t(seg) * lseg * kWC;    // first token of the segment
-    // loading threads: piece j of chunk cc (clamped, so every load is valid)
-    u32x4 ra[PER], rb[PER];
-    auto fetch = [&](u32x4 (&dst)[PER], int i) __attribute__((always_inline)) {
+    // loading waves: piece j of a chunk goes straight from the workspace to LDS
+    // (global_load_lds_dwordx4: each lane's 16 bytes land at the wave's LDS base + 16 *
+    // lane); pieces past NP re-read the last piece into the buffer's padding
+    const int lw = wave - kStateWaves;         // loading wave index
+    int src[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int idx = min(ltid + j * LT, NP - 1);
+        src[j] = idx + (idx >= SH16 ? vt * U16 : 0);
+    }
+    auto dma = [&](int i, int bi) __attribute__((always_inline)) {
         const int cc = c0 + min(i, nch - 1);
         const u32x4* rec = reinterpret_cast<const u32x4*>(ws + (int64_t(cc) * H + h) * Lay::TOTAL);
 #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const int idx = min(ltid + j * LT, NP - 1);
-            dst[j] = rec[idx + (idx >= SH16 ? vt * U16 : 0)];
-        }
+        for (int j = 0; j < PER; ++j)
+            __builtin_amdgcn_global_load_lds(
+                (__attribute__((address_space(1))) void*)(rec + src[j]),
+                (__attribute__((address_space(3))) void*)(lds + bi * BUF + lw * 64 + j * LT), 16, 0, 0);
     };
-    // the compiler barrier keeps the next loads after the commit, so the two register
-    // sets are issued in the same order on every path into the loop
-    auto commit = [&](const u32x4 (&src)[PER], int bi) __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < PER; ++j) lds[bi * BUF + ltid + j * LT] = src[j];   // pieces past NP land in padding
-        asm volatile("" ::: "memory");
+    // wait for this wave's transfers to land in LDS, then hand the buffer over
+    auto dma_barrier = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
     };
 
     // one chunk of products from LDS buffer bi, for this wave's CPW column tiles
@@ -642,37 +646,19 @@ __global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
     };
 
     // The two roles run separate loops with the same barrier sequence (one barrier
-    // after the prologue and one per chunk), so their registers never overlap.
+    // after the prologue and one per chunk). In iteration i the state waves read
+    // buffer i & 1 while the loading waves fill buffer (i + 1) & 1, freed by chunk i - 1.
     KDA_PHASE_DECL
     if (loader) {
-        // prologue: chunk 0 in buffer 0, chunks 1 and 2 in flight in ra and rb
-        if (nch > 0) {
-            fetch(ra, 0);
-            commit(ra, 0);
-            fetch(ra, 1);
-            asm volatile("" ::: "memory");      // all of ra is issued before any of rb
-            fetch(rb, 2);
-        }
-        lds_barrier();
-        // pairs of iterations; the loop always closes after the odd one, so the two
-        // register sets stay in the same issue order on every path
-        int i = 0;
+        if (nch > 0) dma(0, 0);
+        dma_barrier();
         KDA_PHASE_MARK(5);
-        for (; i + 1 < nch; i += 2) {
-            commit(ra, 1);                      // chunk i + 1 to buffer 1 (freed by chunk i - 1)
-            KDA_PHASE_MARK(2);
-            fetch(ra, i + 3);
+        for (int i = 0; i < nch; ++i) {
+            if (i + 1 < nch) dma(i + 1, (i + 1) & 1);
             KDA_PHASE_MARK(3);
-            lds_barrier();
-            KDA_PHASE_MARK(4);
-            commit(rb, 0);                      // chunk i + 2 to buffer 0 (freed by chunk i)
-            KDA_PHASE_MARK(2);
-            fetch(rb, i + 4);
-            KDA_PHASE_MARK(3);
-            lds_barrier();
+            dma_barrier();
             KDA_PHASE_MARK(4);
         }
-        if (i < nch) lds_barrier();             // last, even iteration: nothing left to load
         KDA_PHASE_FLUSH
         return;
     }
@@ -753,20 +739,11 @@ __global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
     }
     lds_barrier();
     KDA_PHASE_MARK(5);
-    int i = 0;
-    for (; i + 1 < nch; i += 2) {
-        products(S, i, 0);
+    for (int i = 0; i < nch; ++i) {
+        products(S, i, i & 1);
         KDA_PHASE_MARK(0);
         lds_barrier();
         KDA_PHASE_MARK(1);
-        products(S, i + 1, 1);
-        KDA_PHASE_MARK(0);
-        lds_barrier();
-        KDA_PHASE_MARK(1);
-    }
-    if (i < nch) {
-        products(S, i, 0);
-        lds_barrier();
     }
     KDA_PHASE_FLUSH
     if constexpr (MODE == 1) {
@@ -800,7 +777,8 @@ __global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
 template <int DK, int DV>
 constexpr size_t chain_smem() {
     constexpr int np = (WyLayout<DK, DV>::SHARED + WyLayout<DK, DV>::UTILE) * 2 / 16;
-    return 2 * size_t((np + 255) / 256) * 256 * 16;
+    constexpr int lt = kLoadWaves * 64;
+    return 2 * size_t((np + lt - 1) / lt) * lt * 16;
 }
 
 struct WyPlan {
