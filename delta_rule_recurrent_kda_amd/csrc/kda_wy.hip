@@ -124,6 +124,23 @@ __device__ __forceinline__ void sample_bounds(const int32_t* cu, int n, int64_t 
     s1 = min<int64_t>(max<int64_t>(cu[n + 1], s0), T);
 }
 
+// For a pack of at most 64 samples each wave forms the chunk table itself: lane l
+// holds the number of chunks of samples 0..l (inclusive), and no plan kernel runs.
+__device__ __forceinline__ int wave_chunk_scan(const int32_t* cu, int num_seqs, int64_t T, int lane) {
+    int v = 0;
+    if (lane < num_seqs) {
+        int64_t s0, s1;
+        sample_bounds(cu, lane, T, s0, s1);
+        v = int((s1 - s0 + kWC - 1) / kWC);
+    }
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(v, d);
+        if (lane >= d) v += t;
+    }
+    return v;
+}
+
 // ---------------------------------------------------------------------------
 // prep: the S-independent operands of one (chunk, head)
 // ---------------------------------------------------------------------------
@@ -162,16 +179,26 @@ __global__ __launch_bounds__(kWThreads, 2) void kda_wy_prep_kernel(
     const int r = lane & 15, g = lane >> 4;
 
     const int c = blockIdx.x, h = blockIdx.y;
-    const int ntot = min(chunk_off[num_seqs], max_chunks);
-    if (c >= ntot) return;
-    int lo = 0, hi = num_seqs;                  // chunk_off[lo] <= c < chunk_off[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (chunk_off[mid] <= c) lo = mid; else hi = mid;
+    int lo, cbase;                              // sample owning chunk c, its first chunk
+    if (!chunk_off) {
+        const int incl = wave_chunk_scan(cu, num_seqs, total_tokens, lane);
+        if (c >= min(__shfl(incl, 63), max_chunks)) return;
+        lo = __popcll(__ballot(incl <= c));     // samples that end at or before chunk c
+        cbase = lo > 0 ? __shfl(incl, lo - 1) : 0;
+    } else {
+        const int ntot = min(chunk_off[num_seqs], max_chunks);
+        if (c >= ntot) return;
+        lo = 0;
+        int hi = num_seqs;                      // chunk_off[lo] <= c < chunk_off[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (chunk_off[mid] <= c) lo = mid; else hi = mid;
+        }
+        cbase = chunk_off[lo];
     }
     int64_t s0, s1;
     sample_bounds(cu, lo, total_tokens, s0, s1);
-    const int64_t t0 = s0 + int64_t(c - chunk_off[lo]) * kWC;
+    const int64_t t0 = s0 + int64_t(c - cbase) * kWC;
     const int nrow = int(min<int64_t>(kWC, s1 - t0));   // >= 1
     uint16_t* rec = ws + (int64_t(c) * H + h) * Lay::TOTAL;
     auto grow = [&](int row) { return (t0 + min(row, nrow - 1)) * H + h; };   // clamped token row
@@ -526,7 +553,15 @@ __global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
         nseg = seg_off[n + 1] - seg_off[n];
         if (MODE == 1 && seg == nseg - 1) return;                // the last segment needs no transition
     }
-    int c0 = min(chunk_off[n], max_chunks), c1 = min(chunk_off[n + 1], max_chunks);
+    int c0, c1;
+    if (!chunk_off) {                           // small pack: the wave forms the chunk table
+        const int incl = wave_chunk_scan(cu, num_seqs, total_tokens, lane);
+        c0 = min(n > 0 ? __shfl(incl, n - 1) : 0, max_chunks);
+        c1 = min(__shfl(incl, n), max_chunks);
+    } else {
+        c0 = min(chunk_off[n], max_chunks);
+        c1 = min(chunk_off[n + 1], max_chunks);
+    }
     if constexpr (MODE != 0) {
         c0 = min(c0 + seg * lseg, c1);
         c1 = min(c0 + lseg, c1);
@@ -545,14 +580,24 @@ __global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
         const int idx = min(ltid + j * LT, NP - 1);
         src[j] = idx + (idx >= SH16 ? vt * U16 : 0);
     }
+    // 64-piece blocks a pass never reads are skipped: the first pass of the sequence
+    // split writes no output (no Qh, no P), and its transition tiles take U as zero
+    auto needed = [&](int b0) {
+        if constexpr (MODE != 1) return true;
+        const bool in_q = b0 >= Lay::Q / 8 && b0 + 64 <= Lay::K / 8;
+        const bool in_p = b0 >= Lay::P / 8 && b0 + 64 <= Lay::G / 8;
+        const bool in_u = b0 >= SH16;
+        return !(in_q || in_p || (trans && in_u));
+    };
     auto dma = [&](int i, int bi) __attribute__((always_inline)) {
         const int cc = c0 + min(i, nch - 1);
         const u32x4* rec = reinterpret_cast<const u32x4*>(ws + (int64_t(cc) * H + h) * Lay::TOTAL);
 #pragma unroll
         for (int j = 0; j < PER; ++j)
-            __builtin_amdgcn_global_load_lds(
-                (__attribute__((address_space(1))) void*)(rec + src[j]),
-                (__attribute__((address_space(3))) void*)(lds + bi * BUF + lw * 64 + j * LT), 16, 0, 0);
+            if (needed(lw * 64 + j * LT))
+                __builtin_amdgcn_global_load_lds(
+                    (__attribute__((address_space(1))) void*)(rec + src[j]),
+                    (__attribute__((address_space(3))) void*)(lds + bi * BUF + lw * 64 + j * LT), 16, 0, 0);
     };
     // wait for this wave's transfers to land in LDS, then hand the buffer over
     auto dma_barrier = [&]() __attribute__((always_inline)) {
@@ -887,12 +932,16 @@ hipError_t launch_forward_wy(const LaunchArgs& a, void* workspace, TimingHook* t
     float* sloc = p.lseg ? reinterpret_cast<float*>(base + p.table_bytes + p.rec_bytes) : nullptr;
     float* phi = p.lseg ? reinterpret_cast<float*>(base + p.table_bytes + p.rec_bytes + p.sloc_bytes) : nullptr;
 
-    if (th) th->begin("plan", a.stream);
-    hipLaunchKernelGGL(kda_wy_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, chunk_off, seg_off,
-                       a.num_seqs, a.total_tokens, p.lseg);
-    if (th) th->end(a.stream);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (p.lseg == 0 && a.num_seqs <= 64) {
+        chunk_off = nullptr;                    // the kernels form the chunk table per wave
+    } else {
+        if (th) th->begin("plan", a.stream);
+        hipLaunchKernelGGL(kda_wy_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, chunk_off, seg_off,
+                           a.num_seqs, a.total_tokens, p.lseg);
+        if (th) th->end(a.stream);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
 
     if (a.d_k == 128 && a.d_v == 128) return launch_dims<128, 128>(a, ws, chunk_off, seg_off, p, sloc, phi, th);
     if (a.d_k == 128 && a.d_v == 64) return launch_dims<128, 64>(a, ws, chunk_off, seg_off, p, sloc, phi, th);

@@ -225,9 +225,11 @@ def test_kernel_timing_records_each_kernel():
         for _ in range(3):
             kda.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"])
         torch.cuda.synchronize()
-        for name in ("plan", "prep", "chain"):
+        for name in ("prep", "chain"):
             n, ms = kda.timing_read(name)
             assert n == 3 and ms > 0, (name, n, ms)
+        # a pack of at most 64 samples forms its chunk table inside the kernels
+        assert kda.timing_read("plan") == (0, 0.0)
         assert kda.timing_read("scan") == (0, 0.0)
     finally:
         kda.timing_enable(False)
