@@ -33,7 +33,7 @@ KERNEL_SOURCES = ["delta_rule_recurrent_kda_amd/csrc/kda_wy.hip",
 WORKLOADS = {"tiny": 0, "packed8": 1, "image4": 2, "clip5s": 3, "clip30s": 4}
 CHUNK = 64
 KERNEL_SYMBOL = {"prep": "kda_wy_prep_kernel", "chain": "kda_wy_chain_kernel", "plan": "kda_wy_plan_kernel",
-                 "scan": "kda_fwd"}
+                 "segments": "kda_wy_chain_kernel", "scan": "kda_fwd"}
 
 
 def kernel_sha() -> str:
@@ -68,15 +68,39 @@ def chunk_heads(spec) -> int:
     return sum((n + CHUNK - 1) // CHUNK for n in spec.seq_lens) * spec.heads
 
 
+def split_plan(spec):
+    """Sequence split of the library (same rule): chunks per segment (0 = none) and, over
+    all samples, the chunks that lie in segments other than a sample's last one."""
+    chunks = [(n + CHUNK - 1) // CHUNK for n in spec.seq_lens]
+    bound = (spec.total_tokens + CHUNK - 1) // CHUNK
+    lseg = 0
+    if len(chunks) * spec.heads * (spec.dv // 64) <= 64:
+        segs = max(1, 256 // (spec.heads * (spec.dv // 64)))
+        cand = max(32, (bound + segs - 1) // segs)
+        lseg = cand if cand < bound else 0
+    if not lseg:
+        return 0, 0, 0
+    nsegs = [max(1, (c + lseg - 1) // lseg) for c in chunks]
+    inner_segs = sum(s - 1 for s in nsegs)
+    inner_chunks = sum(min(c, (s - 1) * lseg) for c, s in zip(chunks, nsegs))
+    return lseg, inner_segs, inner_chunks
+
+
 def kernel_bytes(spec, kernel: str) -> int:
     """Algorithmic bytes of one launch of each kernel of the default bf16 scan."""
     es = 2
     T, H, N = spec.total_tokens, spec.heads, len(spec.seq_lens)
+    dk, dv = spec.dk, spec.dv
     rec = chunk_heads(spec) * record_bytes(spec)
+    _, inner_segs, inner_chunks = split_plan(spec)
+    carry = inner_segs * H * (dk * dv + dk * dk) * 4       # S_loc and Phi of each inner segment
     if kernel == "prep":        # read q, k, v, log a, beta; write the records
-        return T * H * (3 * spec.dk + spec.dv + 1) * es + rec
-    if kernel == "chain":       # read the records; write out and final state
-        return rec + T * H * spec.dv * es + N * H * spec.dk * spec.dv * 4
+        return T * H * (3 * dk + dv + 1) * es + rec
+    if kernel == "chain":       # read the records (and the segment carries); write out and final state
+        return rec + T * H * dv * es + N * H * dk * dv * 4 + carry
+    if kernel == "segments":    # read the records of inner segments without Qh and P; write the carries
+        used = record_bytes(spec) - 4 * (dk // 32) * 1024 - 6 * 1024
+        return inner_chunks * H * used + carry
     if kernel == "plan":
         return 4 * (2 * N + 1)
     return algorithmic_bytes(spec)

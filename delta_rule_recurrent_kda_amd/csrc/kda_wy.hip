@@ -200,7 +200,7 @@ __global__ __launch_bounds__(kWThreads, 2) void kda_wy_prep_kernel(
     sample_bounds(cu, lo, total_tokens, s0, s1);
     const int64_t t0 = s0 + int64_t(c - cbase) * kWC;
     const int nrow = int(min<int64_t>(kWC, s1 - t0));   // >= 1
-    uint16_t* rec = ws + (int64_t(c) * H + h) * Lay::TOTAL;
+    uint16_t* rec = ws + (int64_t(h) * max_chunks + c) * Lay::TOTAL;
     auto grow = [&](int row) { return (t0 + min(row, nrow - 1)) * H + h; };   // clamped token row
 
     // ===== stage: raw q, k, log a rows of the chunk to LDS (zero past the sample's
@@ -591,7 +591,7 @@ __global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
     };
     auto dma = [&](int i, int bi) __attribute__((always_inline)) {
         const int cc = c0 + min(i, nch - 1);
-        const u32x4* rec = reinterpret_cast<const u32x4*>(ws + (int64_t(cc) * H + h) * Lay::TOTAL);
+        const u32x4* rec = reinterpret_cast<const u32x4*>(ws + (int64_t(h) * max_chunks + cc) * Lay::TOTAL);
 #pragma unroll
         for (int j = 0; j < PER; ++j)
             if (needed(lw * 64 + j * LT))
