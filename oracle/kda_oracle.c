@@ -39,6 +39,14 @@
  * state (the per-head state is all a sample carries forward: explainer page "What
  * O(N) buys in memory and latency"; paper Sec. 5 efficiency study, Fig. 18,
  * roll-out-cache setting). Everything else is the same recurrence.
+ *
+ * kda_oracle_forward_ex also takes qk_l2norm: when nonzero, q_t and k_t of every
+ * (token, head) are first divided by their Euclidean length (a zero vector stays
+ * zero) and the recurrence then runs on the unit vectors. The paper's training
+ * setup names chunked KDA kernels with fused normalization; its form is not
+ * printed, and this is the per-token L2 normalisation of queries and keys that the
+ * unit-key statements of the explainer page (erase-then-write of one direction)
+ * take for granted.
  */
 #include <math.h>
 #include <pthread.h>
@@ -50,6 +58,7 @@ typedef struct {
     const double *q, *k, *v, *log_alpha, *beta;
     const int32_t *cu_seqlens;
     const double *initial_state;   /* NULL = S_0 = 0 */
+    int32_t qk_l2norm;             /* nonzero: unit-length q_t, k_t */
     int32_t n_seqs, H, dk, dv;
     const uint8_t *head_mask;   /* NULL = all heads */
     double *out, *final_state;
@@ -67,13 +76,25 @@ static int scan_unit(oracle_job *job, int32_t n, int32_t h)
     double *S = calloc((size_t)dk * dv, sizeof(double));   /* reset: S_0 = 0 */
     double *p = malloc(sizeof(double) * dv);
     double *u = malloc(sizeof(double) * dv);
-    if (!S || !p || !u) { free(S); free(p); free(u); return -1; }
+    double *qn = malloc(sizeof(double) * dk);
+    double *kn = malloc(sizeof(double) * dk);
+    if (!S || !p || !u || !qn || !kn) { free(S); free(p); free(u); free(qn); free(kn); return -1; }
     if (job->initial_state)
         memcpy(S, job->initial_state + ((size_t)n * H + h) * dk * dv, sizeof(double) * dk * dv);
 
     for (int64_t t = t0; t < t1; ++t) {
         const double *kt = job->k + (t * H + h) * dk;
         const double *qt = job->q + (t * H + h) * dk;
+        if (job->qk_l2norm) {
+            /* q_t / |q_t|, k_t / |k_t| (a zero vector stays zero) */
+            double sq = 0.0, sk = 0.0;
+            for (int32_t c = 0; c < dk; ++c) { sq += qt[c] * qt[c]; sk += kt[c] * kt[c]; }
+            sq = sq > 0.0 ? 1.0 / sqrt(sq) : 0.0;
+            sk = sk > 0.0 ? 1.0 / sqrt(sk) : 0.0;
+            for (int32_t c = 0; c < dk; ++c) { qn[c] = qt[c] * sq; kn[c] = kt[c] * sk; }
+            qt = qn;
+            kt = kn;
+        }
         const double *lat = job->log_alpha + (t * H + h) * dk;
         const double *vt = job->v + (t * H + h) * dv;
         const double bt = job->beta[t * H + h];
@@ -110,7 +131,7 @@ static int scan_unit(oracle_job *job, int32_t n, int32_t h)
     }
     if (job->final_state)
         memcpy(job->final_state + ((size_t)n * H + h) * dk * dv, S, sizeof(double) * dk * dv);
-    free(S); free(p); free(u);
+    free(S); free(p); free(u); free(qn); free(kn);
     return 0;
 }
 
@@ -140,12 +161,12 @@ static void *worker(void *arg)
  * initial_state NULL means every sample starts from 0. threads <= 0 means one
  * thread. Returns 0 on success, -1 on bad arguments or allocation failure.
  */
-int kda_oracle_forward_from(const double *q, const double *k, const double *v,
-                            const double *log_alpha, const double *beta,
-                            const int32_t *cu_seqlens, const double *initial_state,
-                            int32_t n_seqs, int32_t H, int32_t dk, int32_t dv,
-                            const uint8_t *head_mask, double *out, double *final_state,
-                            int32_t threads)
+int kda_oracle_forward_ex(const double *q, const double *k, const double *v,
+                          const double *log_alpha, const double *beta,
+                          const int32_t *cu_seqlens, const double *initial_state, int32_t qk_l2norm,
+                          int32_t n_seqs, int32_t H, int32_t dk, int32_t dv,
+                          const uint8_t *head_mask, double *out, double *final_state,
+                          int32_t threads)
 {
     if (!cu_seqlens || n_seqs < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
     if (cu_seqlens[0] != 0) return -1;
@@ -159,6 +180,7 @@ int kda_oracle_forward_from(const double *q, const double *k, const double *v,
     job.cu_seqlens = cu_seqlens; job.n_seqs = n_seqs; job.H = H; job.dk = dk; job.dv = dv;
     job.head_mask = head_mask; job.out = out; job.final_state = final_state;
     job.initial_state = initial_state;
+    job.qk_l2norm = qk_l2norm;
     pthread_mutex_init(&job.lock, NULL);
 
     if (threads < 1) threads = 1;
@@ -171,6 +193,18 @@ int kda_oracle_forward_from(const double *q, const double *k, const double *v,
     for (int i = 0; i < started; ++i) pthread_join(tid[i], NULL);
     pthread_mutex_destroy(&job.lock);
     return job.failed ? -1 : 0;
+}
+
+/* The scan from given initial states, q and k used as stored. */
+int kda_oracle_forward_from(const double *q, const double *k, const double *v,
+                            const double *log_alpha, const double *beta,
+                            const int32_t *cu_seqlens, const double *initial_state,
+                            int32_t n_seqs, int32_t H, int32_t dk, int32_t dv,
+                            const uint8_t *head_mask, double *out, double *final_state,
+                            int32_t threads)
+{
+    return kda_oracle_forward_ex(q, k, v, log_alpha, beta, cu_seqlens, initial_state, 0, n_seqs, H,
+                                 dk, dv, head_mask, out, final_state, threads);
 }
 
 /* The scan from zero states. */

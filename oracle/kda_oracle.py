@@ -45,6 +45,11 @@ def _load(path: str):
                                             ctypes.c_int32, ctypes.POINTER(ctypes.c_uint8), dp, dp,
                                             ctypes.c_int32]
     lib.kda_oracle_forward_from.restype = ctypes.c_int
+    lib.kda_oracle_forward_ex.argtypes = [dp, dp, dp, dp, dp, ctypes.POINTER(ctypes.c_int32), dp,
+                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.POINTER(ctypes.c_uint8), dp, dp, ctypes.c_int32]
+    lib.kda_oracle_forward_ex.restype = ctypes.c_int
     return lib
 
 
@@ -63,11 +68,13 @@ def _ptr(a: Optional[np.ndarray], ctype):
 
 
 def forward(q, k, v, log_alpha, beta, cu_seqlens, heads: Optional[Sequence[int]] = None,
-            threads: Optional[int] = None, _library=None, initial_state=None):
+            threads: Optional[int] = None, _library=None, initial_state=None,
+            qk_l2norm: bool = False):
     """Token-by-token fp64 recurrence.
 
     q, k, log_alpha: [T, H, dk]; v: [T, H, dv]; beta: [T, H]; cu_seqlens: [N+1];
-    initial_state: [N, H, dk, dv] or None (zero states). Returns (out [T, H, dv],
+    initial_state: [N, H, dk, dv] or None (zero states); qk_l2norm: divide q_t and k_t
+    by their Euclidean length before the recurrence (zero vectors stay zero). Returns (out [T, H, dv],
     final_state [N, H, dk, dv]) in fp64. With ``heads`` only those head slices are
     computed (other rows of ``out`` are NaN and the other final states zero, or the
     initial state where one is given).
@@ -97,10 +104,10 @@ def forward(q, k, v, log_alpha, beta, cu_seqlens, heads: Optional[Sequence[int]]
         assert s0.shape == (N, H, dk, dv)
         fs[:] = s0
     lib = _lib() if _library is None else _library
-    rc = lib.kda_oracle_forward_from(_ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
-                                     _ptr(v, ctypes.c_double), _ptr(la, ctypes.c_double),
-                                     _ptr(b, ctypes.c_double), _ptr(cu, ctypes.c_int32),
-                                     _ptr(s0, ctypes.c_double), N, H, dk, dv,
+    rc = lib.kda_oracle_forward_ex(_ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
+                                   _ptr(v, ctypes.c_double), _ptr(la, ctypes.c_double),
+                                   _ptr(b, ctypes.c_double), _ptr(cu, ctypes.c_int32),
+                                   _ptr(s0, ctypes.c_double), int(bool(qk_l2norm)), N, H, dk, dv,
                                      _ptr(mask, ctypes.c_uint8), _ptr(out, ctypes.c_double),
                                      _ptr(fs, ctypes.c_double), int(threads))
     if rc != 0:

@@ -297,7 +297,83 @@ def pin_split_composition(fwd, seed=13):
         assert np.array_equal(np.concatenate([oa, ob]), out) and np.array_equal(fb, fs)
 
 
+# -- NEXT-3: per-token L2 normalisation of q and k before the recurrence ----------
+# (the paper's training setup names kernels with fused normalisation; the form
+# taken is q_t / |q_t|, k_t / |k_t| per (token, head), zero vectors kept zero)
+def pin_l2norm_scale_invariance(fwd, seed=14):
+    """Normalised inputs do not depend on the length of q_t or k_t: scaling each
+    (token, head) vector by its own positive factor leaves out and state unchanged."""
+    rng = np.random.default_rng(seed)
+    q, k, v, la, b, cu = _rand_case(rng, [7, 12, 5], H=2, dk=6, dv=5, unit_keys=False)
+    T, H = q.shape[:2]
+    cq = rng.uniform(0.2, 5.0, (T, H, 1))
+    ck = rng.uniform(0.2, 5.0, (T, H, 1))
+    o1, f1 = fwd(q, k, v, la, b, cu, qk_l2norm=True)
+    o2, f2 = fwd(q * cq, k * ck, v, la, b, cu, qk_l2norm=True)
+    assert _rel(o2, o1) < 1e-12 and _rel(f2, f1) < 1e-12, (_rel(o2, o1), _rel(f2, f1))
+    # and the option is not a no-op on keys of non-unit length
+    o3, _ = fwd(q, k, v, la, b, cu)
+    assert _rel(o3, o1) > 1e-3
+
+
+def pin_l2norm_recall(fwd, seed=15):
+    """alpha = beta = 1 with keys along orthonormal directions but of random lengths:
+    after normalisation a query along a stored direction returns the latest value
+    written there, whatever the lengths of the key and the query."""
+    rng = np.random.default_rng(seed)
+    d = 8
+    Qm, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    T = d + 3
+    order = list(range(d)) + [2, 5, 2]
+    k = np.stack([Qm[:, s] * rng.uniform(0.3, 3.0) for s in order])[:, None, :]
+    v = rng.standard_normal((T, 1, d))
+    src = [0, 0, 1, 3, 2, 4, 5, 1, 0, 5, 2]
+    q = np.stack([Qm[:, s] * rng.uniform(0.3, 3.0) for s in src])[:, None, :]
+    la = np.zeros((T, 1, d)); b = np.ones((T, 1))
+    out, _ = fwd(q, k, v, la, b, np.array([0, T], np.int32), qk_l2norm=True)
+    for t in range(T):
+        last = max(u for u in range(t + 1) if order[u] == src[t])
+        assert np.allclose(out[t, 0], v[last, 0], rtol=0, atol=1e-12), (t, src[t], last)
+
+
+def pin_l2norm_zero_vectors(fwd, seed=16):
+    """A zero query reads 0; a zero key writes and erases nothing, which is the
+    same step as beta_t = 0 (S_t = Diag(alpha_t) S_{t-1})."""
+    rng = np.random.default_rng(seed)
+    q, k, v, la, b, cu = _rand_case(rng, [9, 6], H=2, dk=4, dv=3, unit_keys=False)
+    zq = [(1, 0), (4, 1), (10, 0)]
+    zk = [(2, 1), (5, 0), (12, 1)]
+    q0 = q.copy(); k0 = k.copy(); b0 = b.copy()
+    for t, h in zq:
+        q0[t, h] = 0.0
+    for t, h in zk:
+        k0[t, h] = 0.0
+        b0[t, h] = 0.0
+    out, fs = fwd(q0, k0, v, la, b, cu, qk_l2norm=True)
+    ref, rfs = fwd(q0, np.where(k0 == 0.0, k, k0), v, la, b0, cu, qk_l2norm=True)
+    for t, h in zq:
+        assert np.all(out[t, h] == 0.0)
+    assert _rel(out, ref) < 1e-13 and _rel(fs, rfs) < 1e-13
+
+
+def pin_l2norm_scalar(fwd, seed=17):
+    """d_k = 1: normalisation keeps only signs, s_t = alpha_t (1 - beta_t) s_{t-1} +
+    beta_t sgn(k_t) v_t and o_t = sgn(q_t) s_t, solved by cumulative products."""
+    rng = np.random.default_rng(seed)
+    T = 30
+    k = rng.uniform(-3, 3, (T, 1, 1)); v = rng.standard_normal((T, 1, 1))
+    q = rng.uniform(-3, 3, (T, 1, 1)); la = -rng.uniform(0, 0.5, (T, 1, 1))
+    b = rng.uniform(0, 1, (T, 1))
+    out, fs = fwd(q, k, v, la, b, np.array([0, T], np.int32), qk_l2norm=True)
+    a = np.exp(la[:, 0, 0]) * (1 - b[:, 0])
+    c = b[:, 0] * np.sign(k[:, 0, 0]) * v[:, 0, 0]
+    s = np.array([sum(np.prod(a[r + 1:t + 1]) * c[r] for r in range(t + 1)) for t in range(T)])
+    assert np.allclose(out[:, 0, 0], s * np.sign(q[:, 0, 0]), rtol=1e-11, atol=1e-13)
+    assert np.isclose(fs[0, 0, 0, 0], s[-1], rtol=1e-11, atol=1e-13)
+
+
 ALL_PINS = [pin_worked_example, pin_brute_force, pin_beta_zero, pin_exact_recall, pin_half_life,
             pin_reset_and_packing, pin_write_readback, pin_column_separability, pin_linearity,
             pin_channel_equivariance, pin_scalar_closed_form, pin_lms_step, pin_contraction,
-            pin_nan_confined, pin_initial_state, pin_split_composition]
+            pin_nan_confined, pin_initial_state, pin_split_composition,
+            pin_l2norm_scale_invariance, pin_l2norm_recall, pin_l2norm_zero_vectors, pin_l2norm_scalar]

@@ -18,6 +18,10 @@ MUTANTS = {
     "no_reset": ("const int64_t t0 = job->cu_seqlens[n], t1", "const int64_t t0 = 0, t1"),
     "readout_key_not_query": ("const double qc = qt[c];", "const double qc = kt[c];"),
     "initial_state_ignored": ("    if (job->initial_state)\n", "    if (0)\n"),
+    "qk_norm_ignored": ("if (job->qk_l2norm) {", "if (0) {"),
+    "qk_norm_query_only": ("            qt = qn;\n            kt = kn;\n", "            qt = qn;\n"),
+    "qk_norm_squared_length": ("sk = sk > 0.0 ? 1.0 / sqrt(sk) : 0.0;", "sk = sk > 0.0 ? 1.0 / sk : 0.0;"),
+    "qk_norm_key_by_query_length": ("kn[c] = kt[c] * sk;", "kn[c] = kt[c] * sq;"),
     "decay_after_retrieve": (
         "        /* u = beta_t (v_t - p) */\n",
         "        for (int32_t c = 0; c < dk; ++c) for (int32_t j = 0; j < dv; ++j) p[j] += 0.0 * c;\n"
