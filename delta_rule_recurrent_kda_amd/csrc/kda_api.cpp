@@ -116,7 +116,8 @@ bool prepare_pool(int dev)
 kda_status check_args(const void* q, const void* k, const void* v, const void* log_alpha,
                       const void* beta, const int32_t* cu_seqlens, void* out, float* final_state,
                       const float* initial_state, int64_t total_tokens, int32_t num_seqs,
-                      int32_t num_heads, int32_t d_k, int32_t d_v, kda_dtype dtype, hipStream_t stream);
+                      int32_t num_heads, int32_t d_k, int32_t d_v, kda_dtype dtype, uint32_t options,
+                      hipStream_t stream);
 kda_status run(const kda::LaunchArgs& a);
 
 }  // namespace
@@ -149,11 +150,11 @@ kda_status kda_forward(const void* q, const void* k, const void* v, const void* 
 {
     g_last_error.clear();
     const kda_status st = check_args(q, k, v, log_alpha, beta, cu_seqlens, out, final_state, nullptr,
-                                     total_tokens, num_seqs, num_heads, d_k, d_v, dtype, stream);
+                                     total_tokens, num_seqs, num_heads, d_k, d_v, dtype, 0u, stream);
     if (st != KDA_OK || num_seqs == 0) return st;
     return run(kda::LaunchArgs{q, k, v, log_alpha, beta, cu_seqlens, out, final_state, nullptr,
                                total_tokens, num_seqs, num_heads, d_k, d_v, dtype == KDA_BF16 ? 1 : 0,
-                               stream});
+                               stream, 0});
 }
 
 kda_status kda_forward_from_state(const void* q, const void* k, const void* v, const void* log_alpha,
@@ -163,12 +164,24 @@ kda_status kda_forward_from_state(const void* q, const void* k, const void* v, c
                                   int32_t d_k, int32_t d_v, kda_dtype dtype, hipStream_t stream)
 {
     g_last_error.clear();
+    return kda_forward_ex(q, k, v, log_alpha, beta, cu_seqlens, initial_state, out, final_state,
+                          total_tokens, num_seqs, num_heads, d_k, d_v, dtype, 0u, stream);
+}
+
+kda_status kda_forward_ex(const void* q, const void* k, const void* v, const void* log_alpha,
+                          const void* beta, const int32_t* cu_seqlens, const float* initial_state,
+                          void* out, float* final_state, int64_t total_tokens, int32_t num_seqs,
+                          int32_t num_heads, int32_t d_k, int32_t d_v, kda_dtype dtype, uint32_t options,
+                          hipStream_t stream)
+{
+    g_last_error.clear();
     const kda_status st = check_args(q, k, v, log_alpha, beta, cu_seqlens, out, final_state,
-                                     initial_state, total_tokens, num_seqs, num_heads, d_k, d_v, dtype, stream);
+                                     initial_state, total_tokens, num_seqs, num_heads, d_k, d_v, dtype,
+                                     options, stream);
     if (st != KDA_OK || num_seqs == 0) return st;
     return run(kda::LaunchArgs{q, k, v, log_alpha, beta, cu_seqlens, out, final_state, initial_state,
                                total_tokens, num_seqs, num_heads, d_k, d_v, dtype == KDA_BF16 ? 1 : 0,
-                               stream});
+                               stream, (options & KDA_OPT_QK_L2NORM) ? 1 : 0});
 }
 
 kda_status kda_timing_enable(int32_t on)
@@ -224,8 +237,11 @@ namespace {
 kda_status check_args(const void* q, const void* k, const void* v, const void* log_alpha,
                       const void* beta, const int32_t* cu_seqlens, void* out, float* final_state,
                       const float* initial_state, int64_t total_tokens, int32_t num_seqs,
-                      int32_t num_heads, int32_t d_k, int32_t d_v, kda_dtype dtype, hipStream_t stream)
+                      int32_t num_heads, int32_t d_k, int32_t d_v, kda_dtype dtype, uint32_t options,
+                      hipStream_t stream)
 {
+    if (options & ~uint32_t(KDA_OPT_QK_L2NORM))
+        return fail(KDA_E_UNSUPPORTED, "unknown option bits 0x%x", unsigned(options & ~uint32_t(KDA_OPT_QK_L2NORM)));
     if (dtype != KDA_F32 && dtype != KDA_BF16)
         return fail(KDA_E_DTYPE, "dtype %d is neither KDA_F32 nor KDA_BF16", int(dtype));
     if (total_tokens < 0 || num_seqs < 0 || num_heads < 1)
@@ -253,6 +269,8 @@ kda_status check_args(const void* q, const void* k, const void* v, const void* l
     if (num_seqs == 0) return KDA_OK;
     if (initial_state && (dtype != KDA_BF16 || variant_env() != Variant::Wy))
         return fail(KDA_E_UNSUPPORTED, "initial_state is supported for bf16 data on the default scan");
+    if ((options & KDA_OPT_QK_L2NORM) && dtype == KDA_BF16 && variant_env() == Variant::Pipe)
+        return fail(KDA_E_UNSUPPORTED, "KDA_OPT_QK_L2NORM is not supported by the pipelined scan");
 
     if (validate_env()) {
         std::vector<int32_t> h(size_t(num_seqs) + 1);

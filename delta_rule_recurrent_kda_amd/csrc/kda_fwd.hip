@@ -81,12 +81,16 @@ template <typename E, int DK, int C> struct Smem {
     alignas(16) float gam[DK];
     float beta[C];
     float diag[C];
+    float qs[C], ks[C];                   // 1/|q_t|, 1/|k_t| when normalising on load
 };
 
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
-template <typename E, int DK, int C>
+// NORM: q_t and k_t are divided by their Euclidean length on load (a zero vector
+// stays zero), the normalisation fused into the scan kernels that the paper's
+// training setup describes.
+template <typename E, int DK, int C, bool NORM>
 __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ la, const E* __restrict__ beta, const int32_t* __restrict__ cu,
@@ -217,19 +221,37 @@ __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
                     *reinterpret_cast<float4*>(&sm.wtot[wave * DK + vcol * VE + e]) =
                         make_float4(inc[e], inc[e + 1], inc[e + 2], inc[e + 3]);
             }
-            float dp[RPT];
+            float dp[RPT], qq[RPT], kk[RPT];
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
                 float qv[VE], kv[VE];
                 EL::unpack(rq[i], qv);
                 EL::unpack(rk[i], kv);
-                float sum = 0.f;
+                float sum = 0.f, sq = 0.f, sk = 0.f;
 #pragma unroll
-                for (int e = 0; e < VE; ++e) sum += qv[e] * kv[e];
+                for (int e = 0; e < VE; ++e) {
+                    sum += qv[e] * kv[e];
+                    sq += qv[e] * qv[e];
+                    sk += kv[e] * kv[e];
+                }
                 dp[i] = sum;
+                qq[i] = sq;
+                kk[i] = sk;
             }
-            const float tot = reduce_scatter<RPT, NV / 2>(dp, lane);
-            if ((lane & (NV / RPT - 1)) == 0) sm.diag[rg * RPT + reduce_index<RPT, NV>(lane)] = tot;
+            float tot = reduce_scatter<RPT, NV / 2>(dp, lane);
+            const int drow = rg * RPT + reduce_index<RPT, NV>(lane);
+            if constexpr (NORM) {
+                const float tq = reduce_scatter<RPT, NV / 2>(qq, lane);
+                const float tk = reduce_scatter<RPT, NV / 2>(kk, lane);
+                const float qs = tq > 0.f ? 1.f / sqrtf(tq) : 0.f;
+                const float ks = tk > 0.f ? 1.f / sqrtf(tk) : 0.f;
+                tot *= qs * ks;
+                if ((lane & (NV / RPT - 1)) == 0) {
+                    sm.qs[drow] = qs;
+                    sm.ks[drow] = ks;
+                }
+            }
+            if ((lane & (NV / RPT - 1)) == 0) sm.diag[drow] = tot;
         }
         if (tid < C) sm.beta[tid] = EL::to_f(rb);
         KDA_PHASE_MARK(0); lds_barrier(); KDA_PHASE_MARK(1);  // B1
@@ -276,6 +298,14 @@ __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
                     EL::unpack(rla[i + ii], gv);
                     EL::unpack(rq[i + ii], qv);
                     EL::unpack(rk[i + ii], kv);
+                    if constexpr (NORM) {
+                        const float qs = sm.qs[row], ks = sm.ks[row];
+#pragma unroll
+                        for (int e = 0; e < VE; ++e) {
+                            qv[e] *= qs;
+                            kv[e] *= ks;
+                        }
+                    }
                     float fq[VE], fkh[VE], fkc[VE];
 #pragma unroll
                     for (int e = 0; e < VE; ++e) {
@@ -503,7 +533,7 @@ hipError_t launch_t(const LaunchArgs& a)
     const int groups = (units + 7) / 8;
     const dim3 grid(groups * 8 * nvt), block(kThreads);
     const size_t shmem = sizeof(Smem<E, DK, C>);
-    auto kern = kda_fwd_kernel<E, DK, C>;
+    auto kern = a.qk_l2norm ? kda_fwd_kernel<E, DK, C, true> : kda_fwd_kernel<E, DK, C, false>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem));
     if (e != hipSuccess) return e;

@@ -23,6 +23,7 @@ struct LaunchArgs {
     int32_t d_v;
     int32_t dtype_bf16;
     hipStream_t stream;
+    int32_t qk_l2norm;              // nonzero: q_t, k_t divided by their length on load
 };
 
 // Scan variants (arguments already validated).

@@ -157,7 +157,10 @@ template <int DK> struct PrepSmem {
     alignas(16) float gam[DK];               // exp(G) of the chunk's last row
 };
 
-template <int DK, int DV>
+// NORM: q_t and k_t are divided by their Euclidean length on load (per token and
+// head; a zero vector stays zero), the normalisation fused into the scan kernels
+// that the paper's training setup describes.
+template <int DK, int DV, bool NORM>
 __global__ __launch_bounds__(kWThreads, 2) void kda_wy_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ la, const uint16_t* __restrict__ beta, const int32_t* __restrict__ cu,
@@ -285,11 +288,40 @@ __global__ __launch_bounds__(kWThreads, 2) void kda_wy_prep_kernel(
             qv[ct] = lds4(sm.qk, 16 * i + r, 16 * ct + 4 * g);
             kv[ct] = lds4(sm.kr, 16 * i + r, 16 * ct + 4 * g);
         }
+        // the four lanes r, r + 16, r + 32, r + 48 hold all channels of row 16i + r
+        float qs = 1.f, ks = 1.f;
+        if constexpr (NORM) {
+            float qq = 0.f, kk = 0.f;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                float qf[4], kf[4];
+                unpack4(qv[ct], qf);
+                unpack4(kv[ct], kf);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    qq += qf[s] * qf[s];
+                    kk += kf[s] * kf[s];
+                }
+            }
+            qq += __shfl_xor(qq, 16);
+            qq += __shfl_xor(qq, 32);
+            kk += __shfl_xor(kk, 16);
+            kk += __shfl_xor(kk, 32);
+            qs = qq > 0.f ? 1.f / sqrtf(qq) : 0.f;
+            ks = kk > 0.f ? 1.f / sqrtf(kk) : 0.f;
+        }
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             float qf[4], kf[4], fq[4], fkh[4], fkc[4], lq[4], lk[4];
             unpack4(qv[ct], qf);
             unpack4(kv[ct], kf);
+            if constexpr (NORM) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    qf[s] *= qs;
+                    kf[s] *= ks;
+                }
+            }
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const float G2 = gt[ct][s] * kLog2e;
@@ -857,7 +889,8 @@ hipError_t launch_dims(const LaunchArgs& a, uint16_t* ws, const int32_t* chunk_o
 {
     dim3 pgrid(p.max_chunks, a.num_heads);
     if (th) th->begin("prep", a.stream);
-    hipLaunchKernelGGL((kda_wy_prep_kernel<DK, DV>), pgrid, dim3(kWThreads), 0, a.stream,
+    auto prep = a.qk_l2norm ? kda_wy_prep_kernel<DK, DV, true> : kda_wy_prep_kernel<DK, DV, false>;
+    hipLaunchKernelGGL(prep, pgrid, dim3(kWThreads), 0, a.stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.log_alpha),
                        static_cast<const uint16_t*>(a.beta), a.cu_seqlens, chunk_off, ws, a.num_seqs,

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
 KDA_F32 = 0
 KDA_BF16 = 1
+KDA_OPT_QK_L2NORM = 1   # kda_forward_ex option: unit-length q_t, k_t
 STATUS = {0: "KDA_OK", 1: "KDA_E_NULL", 2: "KDA_E_DTYPE", 3: "KDA_E_SHAPE", 4: "KDA_E_ALIGN",
           5: "KDA_E_UNSUPPORTED", 6: "KDA_E_SEQLENS", 7: "KDA_E_HIP"}
 
@@ -50,6 +51,10 @@ def library() -> ctypes.CDLL:
                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.c_int32, ctypes.c_int, vp]
         lib.kda_forward_from_state.restype = ctypes.c_int
+        lib.kda_forward_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int64,
+                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_int, ctypes.c_uint32, vp]
+        lib.kda_forward_ex.restype = ctypes.c_int
         lib.kda_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int]
         lib.kda_workspace_bytes.restype = ctypes.c_size_t
@@ -82,6 +87,15 @@ def kda_forward_from_state_raw(q, k, v, log_alpha, beta, cu_seqlens, initial_sta
     return library().kda_forward_from_state(q, k, v, log_alpha, beta, cu_seqlens, initial_state,
                                             out, final_state, int(total_tokens), int(num_seqs),
                                             int(num_heads), int(d_k), int(d_v), int(dtype), stream)
+
+
+def kda_forward_ex_raw(q, k, v, log_alpha, beta, cu_seqlens, initial_state, out, final_state,
+                       total_tokens: int, num_seqs: int, num_heads: int, d_k: int, d_v: int,
+                       dtype: int, options: int, stream: Optional[int]) -> int:
+    """Direct C call of kda_forward_ex; returns the status code."""
+    return library().kda_forward_ex(q, k, v, log_alpha, beta, cu_seqlens, initial_state, out,
+                                    final_state, int(total_tokens), int(num_seqs), int(num_heads),
+                                    int(d_k), int(d_v), int(dtype), int(options), stream)
 
 
 def workspace_bytes(total_tokens: int, num_seqs: int, num_heads: int, d_k: int, d_v: int,
@@ -146,19 +160,24 @@ def kda_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: to
                 beta: torch.Tensor, cu_seqlens: torch.Tensor, out: torch.Tensor,
                 final_state: Optional[torch.Tensor] = None,
                 stream: Optional[torch.cuda.Stream] = None,
-                initial_state: Optional[torch.Tensor] = None) -> None:
+                initial_state: Optional[torch.Tensor] = None, qk_l2norm: bool = False) -> None:
     """Enqueue the KDA forward scan on ``stream`` (default: torch's current stream).
 
     q, k, log_alpha: [T, H, d_k]; v, out: [T, H, d_v]; beta: [T, H] (one dtype,
     float32 or bfloat16); cu_seqlens: int32 [N+1]; final_state and initial_state:
     float32 [N, H, d_k, d_v] or None. All on the same GPU, contiguous. With an
-    initial_state the call goes to kda_forward_from_state.
+    initial_state the call goes to kda_forward_from_state; with qk_l2norm (q_t and
+    k_t normalised to unit length inside the scan) to kda_forward_ex.
     """
     T, N, H, dk, dv, dt = _check(q, k, v, log_alpha, beta, cu_seqlens, out, final_state,
                                  initial_state)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    if initial_state is None:
+    if qk_l2norm:
+        st = kda_forward_ex_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                _ptr(cu_seqlens), _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                T, N, H, dk, dv, dt, KDA_OPT_QK_L2NORM, stream.cuda_stream)
+    elif initial_state is None:
         st = kda_forward_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                              _ptr(cu_seqlens), _ptr(out), _ptr(final_state), T, N, H, dk, dv, dt,
                              stream.cuda_stream)
@@ -171,12 +190,12 @@ def kda_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: to
 
 
 def forward(q, k, v, log_alpha, beta, cu_seqlens, with_state: bool = True,
-            stream: Optional[torch.cuda.Stream] = None, initial_state=None):
+            stream: Optional[torch.cuda.Stream] = None, initial_state=None, qk_l2norm: bool = False):
     """Allocate outputs and run the scan. Returns (out, final_state or None)."""
     T, H, _ = q.shape
     N = cu_seqlens.numel() - 1
     out = torch.empty((T, H, v.shape[2]), dtype=q.dtype, device=q.device)
     fs = torch.empty((N, H, q.shape[2], v.shape[2]), dtype=torch.float32, device=q.device) \
         if with_state else None
-    kda_forward(q, k, v, log_alpha, beta, cu_seqlens, out, fs, stream, initial_state)
+    kda_forward(q, k, v, log_alpha, beta, cu_seqlens, out, fs, stream, initial_state, qk_l2norm)
     return out, fs

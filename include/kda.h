@@ -17,7 +17,7 @@
  *
  *   with alpha_t = exp(log_alpha_t) in (0,1]^{d_k} a forget gate per key
  *   channel, beta_t a scalar write/erase strength, S_t in R^{d_k x d_v}. No query
- *   scale and no normalisation is applied inside the operation.
+ *   scale is applied, and no normalisation unless kda_forward_ex asks for it.
  *
  * The library evaluates this recurrence in a chunkwise form on bf16/fp32 MFMA
  * with fp32 accumulation and an fp32 state; results agree with the token
@@ -122,6 +122,33 @@ kda_status kda_forward_from_state(const void *q, const void *k, const void *v,
                                   int32_t num_seqs, int32_t num_heads, int32_t d_k, int32_t d_v,
                                   kda_dtype dtype, hipStream_t stream);
 
+/* Option bits of kda_forward_ex. */
+#define KDA_OPT_QK_L2NORM 1u   /* normalise q_t and k_t to unit length on load */
+
+/*
+ * kda_forward_ex -- kda_forward with an optional initial state and option bits.
+ *
+ * KDA_OPT_QK_L2NORM: before the recurrence, q_t and k_t of every (token, head) are
+ * divided by their Euclidean length (over the d_k channels; a zero vector stays
+ * zero), in fp32 from the stored values, and the scan runs on the unit vectors. The
+ * paper's training setup names chunked KDA kernels with the normalisation fused in
+ * (paper, training setup paragraph on the custom kernels over the packed tokens); it
+ * does not print the form, and this one, x / |x| per token and head, is the reading
+ * taken. It spares the caller a separate pass over q and k in HBM. The stored q and
+ * k are not modified.
+ *
+ *   initial_state : as kda_forward_from_state (NULL = zero states).
+ *   options       : bitwise OR of KDA_OPT_* values; unknown bits give KDA_E_UNSUPPORTED.
+ * All other arguments, errors and execution as kda_forward. KDA_OPT_QK_L2NORM is
+ * supported for fp32 and bf16 data on the default scans (KDA_E_UNSUPPORTED with
+ * KDA_SCAN_VARIANT=pipe); initial_state as for kda_forward_from_state.
+ */
+kda_status kda_forward_ex(const void *q, const void *k, const void *v, const void *log_alpha,
+                          const void *beta, const int32_t *cu_seqlens, const float *initial_state,
+                          void *out, float *final_state, int64_t total_tokens, int32_t num_seqs,
+                          int32_t num_heads, int32_t d_k, int32_t d_v, kda_dtype dtype,
+                          uint32_t options, hipStream_t stream);
+
 /*
  * kda_workspace_bytes -- bytes of device workspace the default bf16 scan takes for
  * these sizes (0 when it takes none: fp32 data, no samples, unsupported sizes).
@@ -134,8 +161,10 @@ size_t kda_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_h
 /*
  * Diagnostics: per-kernel timing with HIP events. While enabled (on != 0), each
  * kda_forward* call records a pair of events on its stream around every kernel it
- * launches, named "plan", "prep" and "chain" (default bf16 scan) or "scan"
- * (single-kernel scans). kda_timing_read waits for the recorded events of `kernel`,
+ * launches, named "plan", "prep", "segments" and "chain" (default bf16 scan;
+ * "segments" is the first pass of the within-GPU sequence split, "plan" the chunk
+ * table, launched only for packs of more than 64 samples or with the split) or
+ * "scan" (single-kernel scans). kda_timing_read waits for the recorded events of `kernel`,
  * returns their count and summed duration in milliseconds, and drops them.
  * Process-wide state guarded by a mutex; returns KDA_E_NULL on NULL arguments and
  * KDA_E_HIP if an event cannot be read (all records are then dropped).

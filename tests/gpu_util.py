@@ -33,23 +33,39 @@ def device_inputs(spec, a, device="cuda:0"):
     return out
 
 
-def run_hip(spec, d, stream=None, initial_state=None):
+def run_hip(spec, d, stream=None, initial_state=None, qk_l2norm=False):
     """Call the library through the C ABI; returns fp64 numpy (out, final_state)."""
     import torch
     from delta_rule_recurrent_kda_amd import kda
     o, fs = kda.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"],
-                        stream=stream, initial_state=initial_state)
+                        stream=stream, initial_state=initial_state, qk_l2norm=qk_l2norm)
     torch.cuda.synchronize()
     return o.float().cpu().double().numpy(), fs.cpu().double().numpy()
 
 
-def oracle_ref(spec, a, heads=None, threads=None, initial_state=None):
+def oracle_ref(spec, a, heads=None, threads=None, initial_state=None, qk_l2norm=False):
     import oracle
     f = {x: inputs.to_f64(a[x], spec.dtype) for x in ("q", "k", "v", "log_alpha", "beta")}
     if threads is None:
         threads = min(16, os.cpu_count() or 1)
     return oracle.forward(f["q"], f["k"], f["v"], f["log_alpha"], f["beta"], a["cu_seqlens"],
-                          heads=heads, threads=threads, initial_state=initial_state)
+                          heads=heads, threads=threads, initial_state=initial_state,
+                          qk_l2norm=qk_l2norm)
+
+
+def unnormalised(spec, a, seed):
+    """The same draws with every (token, head) q and k vector scaled by its own factor
+    in [0.05, 20], and a few of them set to zero, re-stored in the spec's dtype."""
+    rng = np.random.default_rng(seed)
+    T, H = spec.total_tokens, spec.heads
+    b = dict(a)
+    for i, x in enumerate(("q", "k")):
+        f = inputs.to_f64(a[x], spec.dtype) * rng.uniform(0.05, 20.0, (T, H, 1))
+        for t in (1 + i, T // 2 + i, T - 1 - i):
+            if 0 <= t < T:
+                f[t, t % H] = 0.0
+        b[x] = inputs.f64_to_bf16_bits(f) if spec.dtype == "bf16" else f.astype(np.float32)
+    return b
 
 
 def compare(spec, out, fs, o_ref, f_ref, heads=None, label=""):

@@ -27,7 +27,7 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert {"kda_forward", "kda_forward_from_state", "kda_workspace_bytes", "kda_timing_enable",
+    assert {"kda_forward", "kda_forward_from_state", "kda_forward_ex", "kda_workspace_bytes", "kda_timing_enable",
             "kda_timing_read", "kda_status_str", "kda_last_error", "kda_version"} <= set(declared_functions())
 
 
@@ -117,6 +117,42 @@ def test_from_state_on_single_kernel_variant_is_unsupported(lib, monkeypatch):
     monkeypatch.setenv("KDA_SCAN_VARIANT", "pipe")
     st, msg = _call_from_state({})
     assert st == 5 and "initial_state" in msg
+
+
+def _call_ex(kw):
+    from delta_rule_recurrent_kda_amd import kda
+    a = dict(q=0x1000, k=0x2000, v=0x3000, log_alpha=0x4000, beta=0x5000, cu_seqlens=0x6000,
+             initial_state=None, out=0x7000, final_state=0x8000, total_tokens=128, num_seqs=1,
+             num_heads=2, d_k=128, d_v=128, dtype=kda.KDA_BF16, options=kda.KDA_OPT_QK_L2NORM,
+             stream=None)
+    a.update(kw)
+    st = kda.kda_forward_ex_raw(**a)
+    return st, kda.library().kda_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(options=2), 5),                            # unknown option bit
+    (dict(options=0x80000001), 5),
+    (dict(initial_state=0x9000, dtype=0), 5),        # fp32 scan takes no initial state
+    (dict(d_v=96), 5),
+    (dict(k=None), 1),
+    (dict(out=0x2000), 3),
+])
+def test_forward_ex_bad_arguments_are_rejected_without_launch(lib, kw, code):
+    st, msg = _call_ex(kw)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def test_forward_ex_empty_batch_is_a_no_op(lib):
+    st, _ = _call_ex(dict(num_seqs=0, total_tokens=0))
+    assert st == 0
+
+
+def test_qk_norm_on_single_kernel_variant_is_unsupported(lib, monkeypatch):
+    monkeypatch.setenv("KDA_SCAN_VARIANT", "pipe")
+    st, msg = _call_ex({})
+    assert st == 5 and "QK_L2NORM" in msg
 
 
 def test_workspace_bytes(lib):

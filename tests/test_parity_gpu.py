@@ -152,6 +152,44 @@ def test_initial_state_vs_oracle(dk, dv):
     assert np.array_equal(fs[1], s0[1].astype(np.float64))      # empty sample returns its state
 
 
+# Normalisation of q_t and k_t inside the scan (kda_forward_ex, KDA_OPT_QK_L2NORM) on
+# vectors of arbitrary length, zero vectors included, against the oracle's option.
+NORM = [
+    ("bf16_d128", (129, 0, 64, 200, 1, 63), 3, 128, 128, "bf16", None),
+    ("bf16_d64_128", (129, 0, 64, 200, 1, 63), 3, 64, 128, "bf16", None),
+    ("bf16_seq_kernel", (129, 3, 64, 200, 1), 3, 128, 64, "bf16", "sequential"),
+    ("f32_d64", (100, 37, 0, 250), 2, 64, 64, "f32", None),
+    ("f32_d128", (70, 130), 2, 128, 128, "f32", None),
+    ("bf16_split", (5000,), 2, 128, 128, "bf16", None),
+]
+
+
+@pytest.mark.parametrize("case", NORM, ids=[c[0] for c in NORM])
+def test_qk_l2norm_vs_oracle(monkeypatch, case):
+    name, lens, H, dk, dv, dt, variant = case
+    if variant:
+        monkeypatch.setenv("KDA_SCAN_VARIANT", variant)
+    spec = inputs.KdaSpec(f"norm_{name}", lens, H, dk, dv, dt, (0.001, 0.1), 6161)
+    gu.log(f"case qk_l2norm {name}")
+    a = gu.unnormalised(spec, inputs.generate(spec), 61)
+    d = gu.device_inputs(spec, a)
+    out, fs = gu.run_hip(spec, d, qk_l2norm=True)
+    o_ref, f_ref = gu.oracle_ref(spec, a, qk_l2norm=True)
+    gu.compare(spec, out, fs, o_ref, f_ref, label=f"qk_l2norm {name}")
+
+
+def test_qk_l2norm_with_initial_state():
+    import torch
+    spec = inputs.KdaSpec("norm_init", (129, 0, 64, 200), 2, 128, 128, "bf16", (0.001, 0.1), 6262)
+    gu.log("case qk_l2norm with initial state")
+    a = gu.unnormalised(spec, inputs.generate(spec), 62)
+    d = gu.device_inputs(spec, a)
+    s0 = (np.random.default_rng(18).standard_normal((4, 2, 128, 128)) * 0.5).astype(np.float32)
+    out, fs = gu.run_hip(spec, d, initial_state=torch.from_numpy(s0).to("cuda:0"), qk_l2norm=True)
+    o_ref, f_ref = gu.oracle_ref(spec, a, initial_state=s0.astype(np.float64), qk_l2norm=True)
+    gu.compare(spec, out, fs, o_ref, f_ref, label="qk_l2norm initial state")
+
+
 def test_split_scan_matches_one_pass():
     # tokens [0, a) then [a, L) from the carried state == one pass over [0, L)
     import torch
