@@ -50,6 +50,11 @@ def _load(path: str):
                                           ctypes.c_int32, ctypes.c_int32,
                                           ctypes.POINTER(ctypes.c_uint8), dp, dp, ctypes.c_int32]
     lib.kda_oracle_forward_ex.restype = ctypes.c_int
+    lib.kda_oracle_backward.argtypes = [dp, dp, dp, dp, dp, ctypes.POINTER(ctypes.c_int32), dp,
+                                        ctypes.c_int32, dp, dp, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_int32, dp, dp, dp, dp, dp, dp,
+                                        ctypes.c_int32]
+    lib.kda_oracle_backward.restype = ctypes.c_int
     return lib
 
 
@@ -115,6 +120,45 @@ def forward(q, k, v, log_alpha, beta, cu_seqlens, heads: Optional[Sequence[int]]
     return out, fs
 
 
+def backward(q, k, v, log_alpha, beta, cu_seqlens, d_out, d_final_state=None, initial_state=None,
+             qk_l2norm: bool = False, threads: Optional[int] = None, _library=None):
+    """Reverse-mode fp64 gradients of L = sum(d_out * out) + sum(d_final_state * final_state).
+
+    Shapes as forward(); d_out like out, d_final_state like final_state (None = 0).
+    Returns (dq, dk, dv, dlog_alpha, dbeta, d_initial_state) in fp64; d_initial_state is
+    the gradient with respect to the initial states (zero states when none are given).
+    """
+    q = np.ascontiguousarray(q, np.float64)
+    k = np.ascontiguousarray(k, np.float64)
+    v = np.ascontiguousarray(v, np.float64)
+    la = np.ascontiguousarray(log_alpha, np.float64)
+    b = np.ascontiguousarray(beta, np.float64)
+    cu = np.ascontiguousarray(cu_seqlens, np.int32)
+    do = np.ascontiguousarray(d_out, np.float64)
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    N = len(cu) - 1
+    assert q.shape == k.shape == la.shape and v.shape == do.shape == (T, H, dv) and b.shape == (T, H)
+    assert N >= 0 and cu[0] == 0 and cu[-1] == T
+    dfs = None if d_final_state is None else np.ascontiguousarray(d_final_state, np.float64)
+    s0 = None if initial_state is None else np.ascontiguousarray(initial_state, np.float64)
+    for x in (dfs, s0):
+        assert x is None or x.shape == (N, H, dk, dv)
+    g = [np.zeros_like(q), np.zeros_like(k), np.zeros_like(v), np.zeros_like(la), np.zeros_like(b)]
+    ds0 = np.zeros((N, H, dk, dv))
+    if threads is None:
+        threads = min(os.cpu_count() or 1, 64)
+    lib = _lib() if _library is None else _library
+    P = ctypes.c_double
+    rc = lib.kda_oracle_backward(_ptr(q, P), _ptr(k, P), _ptr(v, P), _ptr(la, P), _ptr(b, P),
+                                 _ptr(cu, ctypes.c_int32), _ptr(s0, P), int(bool(qk_l2norm)),
+                                 _ptr(do, P), _ptr(dfs, P), N, H, dk, dv, *[_ptr(x, P) for x in g],
+                                 _ptr(ds0, P), int(threads))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_backward failed (bad arguments or out of memory)")
+    return (*g, ds0)
+
+
 def forward_from(path: str):
     """A forward() bound to another build of the same C source (mutation tests)."""
     lib = _load(path)
@@ -122,3 +166,12 @@ def forward_from(path: str):
     def fwd(*args, **kw):
         return forward(*args, _library=lib, **kw)
     return fwd
+
+
+def backward_from(path: str):
+    """A backward() bound to another build of the same C source (mutation tests)."""
+    lib = _load(path)
+
+    def bwd(*args, **kw):
+        return backward(*args, _library=lib, **kw)
+    return bwd
