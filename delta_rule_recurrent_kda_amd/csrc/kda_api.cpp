@@ -184,6 +184,67 @@ kda_status kda_forward_ex(const void* q, const void* k, const void* v, const voi
                                stream, (options & KDA_OPT_QK_L2NORM) ? 1 : 0});
 }
 
+kda_status kda_backward(const void* q, const void* k, const void* v, const void* log_alpha,
+                        const void* beta, const int32_t* cu_seqlens, const float* initial_state,
+                        const void* d_out, const float* d_final_state, void* dq, void* dk, void* dv,
+                        void* dlog_alpha, void* dbeta, float* d_initial_state, int64_t total_tokens,
+                        int32_t num_seqs, int32_t num_heads, int32_t d_k, int32_t d_v, kda_dtype dtype,
+                        uint32_t options, hipStream_t stream)
+{
+    g_last_error.clear();
+    if (options & ~uint32_t(KDA_OPT_QK_L2NORM))
+        return fail(KDA_E_UNSUPPORTED, "unknown option bits 0x%x", unsigned(options & ~uint32_t(KDA_OPT_QK_L2NORM)));
+    // the forward-argument checks on the inputs (no output there: pass q as a stand-in
+    // that aliases nothing of its own)
+    kda_status st = check_args(q, k, v, log_alpha, beta, cu_seqlens, dq, nullptr, nullptr, total_tokens,
+                               num_seqs, num_heads, d_k, d_v, dtype, 0u, stream);
+    if (st != KDA_OK) return st;
+    if (total_tokens > 0 && (!d_out || !dq || !dk || !dv || !dlog_alpha || !dbeta))
+        return fail(KDA_E_NULL, "d_out or a gradient pointer is NULL");
+    const void* ptrs[] = {d_out, dk, dv, dlog_alpha, dbeta, initial_state, d_final_state, d_initial_state};
+    const char* names[] = {"d_out", "dk", "dv", "dlog_alpha", "dbeta", "initial_state", "d_final_state",
+                           "d_initial_state"};
+    for (int i = 0; i < 8; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i])) return fail(KDA_E_ALIGN, "%s is not 16-byte aligned", names[i]);
+    const void* ins[] = {q, k, v, log_alpha, beta, d_out, initial_state, d_final_state};
+    const void* outs[] = {dq, dk, dv, dlog_alpha, dbeta, d_initial_state};
+    for (const void* o : outs)
+        for (const void* i : ins)
+            if (o && o == i) return fail(KDA_E_SHAPE, "a gradient output aliases an input");
+    for (int i = 0; i < 6; ++i)
+        for (int j = i + 1; j < 6; ++j)
+            if (outs[i] && outs[i] == outs[j]) return fail(KDA_E_SHAPE, "two gradient outputs alias");
+    if (num_seqs == 0) return KDA_OK;
+
+    std::unique_lock<std::mutex> lk(g_timing.mu);
+    kda::TimingHook* th = g_timing.on ? &g_timing : nullptr;
+    if (!th) lk.unlock();
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || !prepare_pool(dev))
+        return fail(KDA_E_HIP, "setting up the workspace pool: %s", hipGetErrorString(e));
+    const size_t bytes = kda::bwd_workspace_bytes(total_tokens, num_seqs, num_heads, d_k, d_v);
+    void* ws = nullptr;
+    e = hipMallocAsync(&ws, bytes, stream);
+    if (e != hipSuccess) return fail(KDA_E_HIP, "workspace of %zu bytes: %s", bytes, hipGetErrorString(e));
+    const kda::BwdArgs a{q, k, v, log_alpha, beta, cu_seqlens, initial_state, d_out, d_final_state, dq, dk, dv,
+                         dlog_alpha, dbeta, d_initial_state, total_tokens, num_seqs, num_heads, d_k, d_v,
+                         dtype == KDA_BF16 ? 1 : 0, (options & KDA_OPT_QK_L2NORM) ? 1 : 0, stream};
+    e = kda::launch_backward(a, ws, th);
+    const hipError_t ef = hipFreeAsync(ws, stream);
+    if (e == hipSuccess) e = ef;
+    if (e != hipSuccess) return fail(KDA_E_HIP, "launch failed: %s", hipGetErrorString(e));
+    return KDA_OK;
+}
+
+size_t kda_backward_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads, int32_t d_k,
+                                    int32_t d_v)
+{
+    if (total_tokens < 0 || num_seqs <= 0 || num_heads < 1) return 0;
+    if ((d_k != 64 && d_k != 128) || (d_v != 64 && d_v != 128)) return 0;
+    return kda::bwd_workspace_bytes(total_tokens, num_seqs, num_heads, d_k, d_v);
+}
+
 kda_status kda_timing_enable(int32_t on)
 {
     std::lock_guard<std::mutex> lk(g_timing.mu);

@@ -1,0 +1,1007 @@
+// kda_bwd.hip -- gradients of the KDA scan (q, k, v, log alpha, beta and the initial
+// state) for fp32 and bf16 data, fp32 arithmetic on fp32 MFMA (gfx950).
+//
+// The paper trains its model through these kernels (training setup paragraph on the
+// custom kernels over the packed tokens). The recurrence, per (sample, head)
+// (explainer page, "One stream, three mechanisms, no positions"; reset at each packed
+// sample, paper Sec. 3 KDA paragraph):
+//     S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t v_t^T,   o_t = S_t^T q_t.
+// Chunkwise over C = 32 tokens (G = inclusive cumsum of log a over the chunk's rows
+// per key channel, gamma = exp(G of the last row)):
+//     Qh = Q e^G, Kh = K e^G, Kc = K e^-G, M = Kh Kc^T, A = StrictLower(diag(b) M),
+//     T = (I + A)^-1, P = LowerIncl(Qh Kc^T),
+//     X = V - Kh S,  Vn = T diag(b) X,  O = Qh S + P Vn,  S' = diag(gamma)(S + Kc^T Vn)
+// (Vn = U - W S with the WY factors U = T diag(b) V, W = T diag(b) Kh multiplied out.)
+// For a loss with gradients dO and dS' (the state leaving the chunk):
+//     dVn = P^T dO + Kc diag(gamma) dS',   dX = diag(b) T^T dVn
+//     dS  = diag(gamma) dS' + Qh^T dO - Kh^T dX              (state entering the chunk)
+//     dP  = LowerIncl(dO Vn^T),  dT = dVn X^T diag(b),  dA = StrictLower(-T^T dT T^T)
+//     dM  = diag(b) dA,  dV = dX,  db = rowsum((T^T dVn) X) + rowsum(dA M)
+//     dQh = dO S^T + dP Kc,  dKh = -dX S^T + dM Kc,
+//     dKc = dP^T Qh + (Vn dS'^T) diag(gamma) + dM^T Kh
+//     dgamma = colsum((Vn dS'^T) Kc) + rowsum(dS' S)
+// and through the decays: dQ = dQh e^G, dK = dKh e^G + dKc e^-G,
+//     dG = dQh Qh + dKh Kh - dKc Kc (+ dgamma gamma on the last row), dlog a = the
+//     reverse cumsum of dG over the chunk's rows.
+//
+// Kernels: a chunk table; a prep over all (chunk, head) pairs writing Kh, Kc, Qh, T, P,
+// gamma, b; a chain carrying S forwards that saves the state entering every chunk; a
+// chain carrying dS backwards that saves the gradient of the state leaving every chunk;
+// and a gradient kernel over all (chunk, head) pairs that rebuilds the chunk's
+// operands and applies the formulas above.
+//
+// MFMA: v_mfma_f32_16x16x4f32; lane (r = lane%16, g = lane/16) supplies A(r, k) and
+// B(k, r) for the four k of a step, and holds D(4g + v, r), v = 0..3. Supplying
+// k = 16t + 4g + s in step s makes an accumulator tile (rows 4g + v) a B operand as it
+// stands; every operand read from LDS takes any k order.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+using namespace dev;
+
+constexpr int kBC = 32;            // chunk rows
+constexpr int kBT = 256;           // threads per workgroup: 4 wave64
+constexpr int kLC = kBC + 4;       // row stride of [C][C] tiles in LDS
+
+__device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <typename E> __device__ __forceinline__ float ldf(const E* p);
+template <> __device__ __forceinline__ float ldf<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float ldf<uint16_t>(const uint16_t* p) { return bf2f(*p); }
+template <typename E> __device__ __forceinline__ void stf(E* p, float x);
+template <> __device__ __forceinline__ void stf<float>(float* p, float x) { *p = x; }
+template <> __device__ __forceinline__ void stf<uint16_t>(uint16_t* p, float x) { *p = f2bf(x); }
+
+// Record of one (chunk, head) written by the prep for the two chains (floats).
+template <int DK> struct BRec {
+    static constexpr int KH = 0;                    // Kh [C][DK]
+    static constexpr int KC = KH + kBC * DK;        // Kc [C][DK]
+    static constexpr int QH = KC + kBC * DK;        // Qh [C][DK]
+    static constexpr int T = QH + kBC * DK;         // T  [C][C]
+    static constexpr int P = T + kBC * kBC;         // P  [C][C]
+    static constexpr int GAM = P + kBC * kBC;       // gamma [DK]
+    static constexpr int BETA = GAM + DK;           // b [C] (0 past the sample's end)
+    static constexpr int TOTAL = BETA + kBC;
+    static_assert(TOTAL % 4 == 0, "16-byte records");
+};
+
+// ---------------------------------------------------------------------------
+// chunk table: chunk_off[n] = number of 32-token chunks of samples 0..n-1
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void kda_bwd_plan_kernel(const int32_t* __restrict__ cu,
+                                                            int32_t* __restrict__ chunk_off, int num_seqs,
+                                                            int64_t total_tokens)
+{
+    __shared__ int32_t part[1024];
+    const int tid = threadIdx.x;
+    int32_t carry = 0;
+    for (int base = 0; base < num_seqs; base += 1024) {
+        const int n = base + tid;
+        int32_t cnt = 0;
+        if (n < num_seqs) {
+            const int64_t s0 = min<int64_t>(max<int64_t>(cu[n], 0), total_tokens);
+            const int64_t s1 = min<int64_t>(max<int64_t>(cu[n + 1], s0), total_tokens);
+            cnt = int32_t((s1 - s0 + kBC - 1) / kBC);
+        }
+        part[tid] = cnt;
+        __syncthreads();
+        for (int d = 1; d < 1024; d <<= 1) {
+            const int32_t add = tid >= d ? part[tid - d] : 0;
+            __syncthreads();
+            part[tid] += add;
+            __syncthreads();
+        }
+        if (n < num_seqs) chunk_off[n + 1] = carry + part[tid];
+        carry += part[1023];
+        __syncthreads();
+    }
+    if (tid == 0) chunk_off[0] = 0;
+}
+
+__device__ __forceinline__ void bounds(const int32_t* cu, int n, int64_t T, int64_t& s0, int64_t& s1) {
+    s0 = min<int64_t>(max<int64_t>(cu[n], 0), T);
+    s1 = min<int64_t>(max<int64_t>(cu[n + 1], s0), T);
+}
+
+// sample owning global chunk c (chunk_off[n] <= c < chunk_off[n + 1]), or -1 past the end
+__device__ __forceinline__ int owner(const int32_t* chunk_off, int num_seqs, int c, int max_chunks) {
+    const int ntot = min(chunk_off[num_seqs], max_chunks);
+    if (c >= ntot) return -1;
+    int lo = 0, hi = num_seqs;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (chunk_off[mid] <= c) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+// ---------------------------------------------------------------------------
+// operands of one chunk in LDS: Qh, Kh, Kc (row stride LK), gamma, b, M, P, T
+// ---------------------------------------------------------------------------
+struct ChunkLds {
+    float *qh, *kh, *kc;    // [C][LK]
+    float *m, *t, *p;       // [C][kLC]
+    float *gam, *beta;      // [DK], [C]
+    float *qinv, *kinv;     // [C]: 1/|q_t|, 1/|k_t| (1 without normalisation)
+};
+
+template <typename E, int DK, bool NORM>
+__device__ void chunk_operands(const ChunkLds& L, const E* __restrict__ q, const E* __restrict__ k,
+                               const E* __restrict__ la, const E* __restrict__ beta, int64_t t0, int nrow,
+                               int H, int h)
+{
+    constexpr int LK = DK + 4;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, g = lane >> 4;
+    // raw q, k, log a rows to LDS (zeros past the sample's end); log a goes where Kc will be
+    for (int i = tid; i < kBC * DK; i += kBT) {
+        const int row = i / DK, c = i % DK;
+        float qv = 0.f, kv = 0.f, lv = 0.f;
+        if (row < nrow) {
+            const int64_t off = ((t0 + row) * H + h) * DK + c;
+            qv = ldf(q + off);
+            kv = ldf(k + off);
+            lv = ldf(la + off);
+        }
+        L.qh[row * LK + c] = qv;
+        L.kh[row * LK + c] = kv;
+        L.kc[row * LK + c] = lv;
+    }
+    if (tid < kBC) L.beta[tid] = tid < nrow ? ldf(beta + (t0 + tid) * H + h) : 0.f;
+    __syncthreads();
+    if constexpr (NORM) {
+        // 8 lanes per row, DK/8 channels each
+        const int row = tid >> 3, part = tid & 7;
+        float sq = 0.f, sk = 0.f;
+        for (int c = part; c < DK; c += 8) {
+            const float a = L.qh[row * LK + c], b = L.kh[row * LK + c];
+            sq += a * a;
+            sk += b * b;
+        }
+#pragma unroll
+        for (int m = 1; m < 8; m <<= 1) {
+            sq += __shfl_xor(sq, m);
+            sk += __shfl_xor(sk, m);
+        }
+        if (part == 0) {
+            L.qinv[row] = sq > 0.f ? 1.f / sqrtf(sq) : 0.f;
+            L.kinv[row] = sk > 0.f ? 1.f / sqrtf(sk) : 0.f;
+        }
+        __syncthreads();
+    } else {
+        if (tid < kBC) {
+            L.qinv[tid] = 1.f;
+            L.kinv[tid] = 1.f;
+        }
+    }
+    // cumulative log decay down each key channel, the decayed operands and gamma
+    if (tid < DK) {
+        const int c = tid;
+        float G = 0.f, ex = 1.f;
+        for (int row = 0; row < kBC; ++row) {
+            G += L.kc[row * LK + c];
+            ex = expf(G);
+            const float qv = L.qh[row * LK + c] * (NORM ? L.qinv[row] : 1.f);
+            const float kv = L.kh[row * LK + c] * (NORM ? L.kinv[row] : 1.f);
+            L.qh[row * LK + c] = qv * ex;
+            L.kh[row * LK + c] = kv * ex;
+            L.kc[row * LK + c] = kv * expf(-G);
+        }
+        L.gam[c] = ex;
+    }
+    __syncthreads();
+    // M = Kh Kc^T and P = LowerIncl(Qh Kc^T): wave w computes tile (w >> 1, w & 1) of each
+    {
+        const int ti = wave >> 1, tj = wave & 1;
+        f32x4 am = zero4(), ap = zero4();
+#pragma unroll 8
+        for (int k0 = 0; k0 < DK; k0 += 4) {
+            const float bk = L.kc[(16 * tj + r) * LK + k0 + g];
+            am = mma4(L.kh[(16 * ti + r) * LK + k0 + g], bk, am);
+            ap = mma4(L.qh[(16 * ti + r) * LK + k0 + g], bk, ap);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = 16 * ti + 4 * g + v, j = 16 * tj + r;
+            L.m[i * kLC + j] = am[v];
+            L.p[i * kLC + j] = i >= j ? ap[v] : 0.f;
+        }
+    }
+    __syncthreads();
+    // T = (I + A)^-1, A = StrictLower(diag(b) M): thread j forward-substitutes column j
+    // (T is unit lower triangular, so entries above the diagonal stay 0)
+    if (tid < kBC) {
+        const int j = tid;
+        float col[kBC];
+#pragma unroll
+        for (int i = 0; i < kBC; ++i) {
+            float acc = 0.f;
+#pragma unroll
+            for (int s = 0; s < i; ++s) acc += L.m[i * kLC + s] * col[s];
+            col[i] = (i == j ? 1.f : 0.f) - L.beta[i] * acc;
+        }
+#pragma unroll
+        for (int i = 0; i < kBC; ++i) L.t[i * kLC + j] = col[i];
+    }
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// prep: the records the chains read
+// ---------------------------------------------------------------------------
+template <int DK> struct PrepLds {
+    static constexpr int LK = DK + 4;
+    float qh[kBC * LK], kh[kBC * LK], kc[kBC * LK];
+    float m[kBC * kLC], t[kBC * kLC], p[kBC * kLC];
+    float gam[DK], beta[kBC], qinv[kBC], kinv[kBC];
+};
+
+template <typename E, int DK, bool NORM>
+__global__ __launch_bounds__(kBT) void kda_bwd_prep_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ la, const E* __restrict__ beta,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off, float* __restrict__ rec_ws,
+    int num_seqs, int H, int64_t total_tokens, int max_chunks)
+{
+    using R = BRec<DK>;
+    constexpr int LK = DK + 4;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    PrepLds<DK>& sm = *reinterpret_cast<PrepLds<DK>*>(smem_raw);
+    const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    const int n = owner(chunk_off, num_seqs, c, max_chunks);
+    if (n < 0) return;
+    int64_t s0, s1;
+    bounds(cu, n, total_tokens, s0, s1);
+    const int64_t t0 = s0 + int64_t(c - chunk_off[n]) * kBC;
+    const int nrow = int(min<int64_t>(kBC, s1 - t0));
+    const ChunkLds L{sm.qh, sm.kh, sm.kc, sm.m, sm.t, sm.p, sm.gam, sm.beta, sm.qinv, sm.kinv};
+    chunk_operands<E, DK, NORM>(L, q, k, la, beta, t0, nrow, H, h);
+    float* rec = rec_ws + (int64_t(h) * max_chunks + c) * R::TOTAL;
+    for (int i = tid; i < kBC * DK; i += kBT) {
+        const int row = i / DK, cc = i % DK;
+        rec[R::KH + i] = sm.kh[row * LK + cc];
+        rec[R::KC + i] = sm.kc[row * LK + cc];
+        rec[R::QH + i] = sm.qh[row * LK + cc];
+    }
+    for (int i = tid; i < kBC * kBC; i += kBT) {
+        rec[R::T + i] = sm.t[(i / kBC) * kLC + i % kBC];
+        rec[R::P + i] = sm.p[(i / kBC) * kLC + i % kBC];
+    }
+    if (tid < DK) rec[R::GAM + tid] = sm.gam[tid];
+    if (tid < kBC) rec[R::BETA + tid] = sm.beta[tid];
+}
+
+// ---------------------------------------------------------------------------
+// chains: one workgroup per (sample, head, 64-column value tile); wave w holds columns
+// 16w..16w+15 of the tile of S (or dS) as DK/16 accumulator tiles
+// ---------------------------------------------------------------------------
+template <int DK> struct ChainLds {
+    static constexpr int LK = DK + 4, LV = 64 + 4;
+    float qh[kBC * LK], kh[kBC * LK], kc[kBC * LK];
+    float t[kBC * kLC], p[kBC * kLC];
+    float vt[kBC * LV];                 // V (state chain) or dO (gradient chain) tile
+    float gam[DK], beta[kBC];
+};
+
+// unit of block b: the value tiles of one (sample, head) are 8 blocks apart (same XCD)
+__device__ __forceinline__ void chain_unit(int b, int nvt, int& unit, int& vt) {
+    vt = (b >> 3) % nvt;
+    unit = (b / (8 * nvt)) * 8 + (b & 7);
+}
+
+// stage the record of chunk cc and a [C][64] tile of `src` (V or dO, rows t0..) into LDS
+template <typename E, int DK, bool GRAD>
+__device__ __forceinline__ void chain_stage(ChainLds<DK>& sm, const float* __restrict__ rec, const E* __restrict__ src,
+                                            int64_t t0, int nrow, int H, int h, int DV, int col0)
+{
+    using R = BRec<DK>;
+    constexpr int LK = DK + 4, LV = 64 + 4;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < kBC * DK / 4; i += kBT) {
+        const int row = (4 * i) / DK, c = (4 * i) % DK;
+        const float4 a = *reinterpret_cast<const float4*>(rec + R::KH + 4 * i);
+        const float4 b = *reinterpret_cast<const float4*>(rec + R::KC + 4 * i);
+        *reinterpret_cast<float4*>(&sm.kh[row * LK + c]) = a;
+        *reinterpret_cast<float4*>(&sm.kc[row * LK + c]) = b;
+        if constexpr (GRAD) {
+            const float4 e = *reinterpret_cast<const float4*>(rec + R::QH + 4 * i);
+            *reinterpret_cast<float4*>(&sm.qh[row * LK + c]) = e;
+        }
+    }
+    for (int i = tid; i < kBC * kBC; i += kBT) {
+        sm.t[(i / kBC) * kLC + i % kBC] = rec[R::T + i];
+        if constexpr (GRAD) sm.p[(i / kBC) * kLC + i % kBC] = rec[R::P + i];
+    }
+    if (tid < DK) sm.gam[tid] = rec[R::GAM + tid];
+    if (tid < kBC) sm.beta[tid] = rec[R::BETA + tid];
+    for (int i = tid; i < kBC * 64; i += kBT) {
+        const int row = i / 64, c = i % 64;
+        sm.vt[row * LV + c] = row < nrow ? ldf(src + ((t0 + row) * H + h) * DV + col0 + c) : 0.f;
+    }
+}
+
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(kBT) void kda_bwd_state_kernel(
+    const E* __restrict__ v, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
+    const float* __restrict__ rec_ws, const float* __restrict__ init_state, float* __restrict__ s_in,
+    int num_seqs, int H, int64_t total_tokens, int max_chunks)
+{
+    using R = BRec<DK>;
+    constexpr int NCT = DK / 16, LK = DK + 4, LV = 64 + 4;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    ChainLds<DK>& sm = *reinterpret_cast<ChainLds<DK>*>(smem_raw);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+    int unit, vt;
+    chain_unit(blockIdx.x, DV / 64, unit, vt);
+    if (unit >= num_seqs * H) return;
+    const int n = unit / H, h = unit % H;
+    const int col = 64 * vt + 16 * wave + r;             // this lane's value column
+    const int c0 = min(chunk_off[n], max_chunks), c1 = min(chunk_off[n + 1], max_chunks);
+    int64_t s0, s1;
+    bounds(cu, n, total_tokens, s0, s1);
+
+    f32x4 S[NCT];
+#pragma unroll
+    for (int ti = 0; ti < NCT; ++ti) {
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4)
+            S[ti][v4] = init_state ? init_state[((int64_t(n) * H + h) * DK + 16 * ti + 4 * g + v4) * DV + col] : 0.f;
+    }
+    for (int cc = c0; cc < c1; ++cc) {
+        const int64_t t0 = s0 + int64_t(cc - c0) * kBC;
+        const int nrow = int(min<int64_t>(kBC, s1 - t0));
+        float* so = s_in + (int64_t(h) * max_chunks + cc) * DK * DV;
+#pragma unroll
+        for (int ti = 0; ti < NCT; ++ti)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) so[(16 * ti + 4 * g + v4) * DV + col] = S[ti][v4];
+        chain_stage<E, DK, false>(sm, rec_ws + (int64_t(h) * max_chunks + cc) * R::TOTAL, v, t0, nrow, H, h, DV, 64 * vt);
+        __syncthreads();
+        // X = V - Kh S, then Y = diag(b) X (rows 16xi + 4g + v)
+        f32x4 Y[2];
+#pragma unroll
+        for (int xi = 0; xi < 2; ++xi) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int ti = 0; ti < NCT; ++ti)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc = mma4(sm.kh[(16 * xi + r) * LK + 16 * ti + 4 * g + s], S[ti][s], acc);
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                const int row = 16 * xi + 4 * g + v4;
+                Y[xi][v4] = sm.beta[row] * (sm.vt[row * LV + 16 * wave + r] - acc[v4]);
+            }
+        }
+        // Vn = T Y
+        f32x4 Vn[2];
+#pragma unroll
+        for (int vi = 0; vi < 2; ++vi) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int xi = 0; xi < 2; ++xi)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc = mma4(sm.t[(16 * vi + r) * kLC + 16 * xi + 4 * g + s], Y[xi][s], acc);
+            Vn[vi] = acc;
+        }
+        // S <- diag(gamma) (S + Kc^T Vn)
+#pragma unroll
+        for (int ti = 0; ti < NCT; ++ti) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int vi = 0; vi < 2; ++vi)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc = mma4(sm.kc[(16 * vi + 4 * g + s) * LK + 16 * ti + r], Vn[vi][s], acc);
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) S[ti][v4] = sm.gam[16 * ti + 4 * g + v4] * (S[ti][v4] + acc[v4]);
+        }
+        __syncthreads();
+    }
+}
+
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(kBT) void kda_bwd_dstate_kernel(
+    const E* __restrict__ d_out, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
+    const float* __restrict__ rec_ws, const float* __restrict__ d_final, float* __restrict__ ds_out,
+    float* __restrict__ d_init, int num_seqs, int H, int64_t total_tokens, int max_chunks)
+{
+    using R = BRec<DK>;
+    constexpr int NCT = DK / 16, LK = DK + 4, LV = 64 + 4;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    ChainLds<DK>& sm = *reinterpret_cast<ChainLds<DK>*>(smem_raw);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+    int unit, vt;
+    chain_unit(blockIdx.x, DV / 64, unit, vt);
+    if (unit >= num_seqs * H) return;
+    const int n = unit / H, h = unit % H;
+    const int col = 64 * vt + 16 * wave + r;
+    const int c0 = min(chunk_off[n], max_chunks), c1 = min(chunk_off[n + 1], max_chunks);
+    int64_t s0, s1;
+    bounds(cu, n, total_tokens, s0, s1);
+
+    f32x4 dS[NCT];
+#pragma unroll
+    for (int ti = 0; ti < NCT; ++ti)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4)
+            dS[ti][v4] = d_final ? d_final[((int64_t(n) * H + h) * DK + 16 * ti + 4 * g + v4) * DV + col] : 0.f;
+    for (int cc = c1 - 1; cc >= c0; --cc) {
+        const int64_t t0 = s0 + int64_t(cc - c0) * kBC;
+        const int nrow = int(min<int64_t>(kBC, s1 - t0));
+        float* so = ds_out + (int64_t(h) * max_chunks + cc) * DK * DV;
+#pragma unroll
+        for (int ti = 0; ti < NCT; ++ti)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) so[(16 * ti + 4 * g + v4) * DV + col] = dS[ti][v4];
+        chain_stage<E, DK, true>(sm, rec_ws + (int64_t(h) * max_chunks + cc) * R::TOTAL, d_out, t0, nrow, H, h, DV, 64 * vt);
+        __syncthreads();
+        // dVn = P^T dO + Kc diag(gamma) dS
+        f32x4 dVn[2];
+#pragma unroll
+        for (int vi = 0; vi < 2; ++vi) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < kBC; k0 += 4)
+                acc = mma4(sm.p[(k0 + g) * kLC + 16 * vi + r], sm.vt[(k0 + g) * LV + 16 * wave + r], acc);
+#pragma unroll
+            for (int ti = 0; ti < NCT; ++ti)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int c = 16 * ti + 4 * g + s;
+                    acc = mma4(sm.kc[(16 * vi + r) * LK + c] * sm.gam[c], dS[ti][s], acc);
+                }
+            dVn[vi] = acc;
+        }
+        // dX = diag(b) T^T dVn
+        f32x4 dX[2];
+#pragma unroll
+        for (int zi = 0; zi < 2; ++zi) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int vi = 0; vi < 2; ++vi)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc = mma4(sm.t[(16 * vi + 4 * g + s) * kLC + 16 * zi + r], dVn[vi][s], acc);
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) dX[zi][v4] = sm.beta[16 * zi + 4 * g + v4] * acc[v4];
+        }
+        // dS <- diag(gamma) dS + Qh^T dO - Kh^T dX
+#pragma unroll
+        for (int ti = 0; ti < NCT; ++ti) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < kBC; k0 += 4)
+                acc = mma4(sm.qh[(k0 + g) * LK + 16 * ti + r], sm.vt[(k0 + g) * LV + 16 * wave + r], acc);
+#pragma unroll
+            for (int zi = 0; zi < 2; ++zi)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc = mma4(-sm.kh[(16 * zi + 4 * g + s) * LK + 16 * ti + r], dX[zi][s], acc);
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) dS[ti][v4] = sm.gam[16 * ti + 4 * g + v4] * dS[ti][v4] + acc[v4];
+        }
+        __syncthreads();
+    }
+    if (d_init) {
+#pragma unroll
+        for (int ti = 0; ti < NCT; ++ti)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4)
+                d_init[((int64_t(n) * H + h) * DK + 16 * ti + 4 * g + v4) * DV + col] = dS[ti][v4];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// gradients of one (chunk, head)
+// ---------------------------------------------------------------------------
+template <int DK, int DV> struct GradLds {
+    static constexpr int LK = DK + 4, LV = DV + 4;
+    float qh[kBC * LK], kh[kBC * LK], kc[kBC * LK];
+    // dead once the products are done; the last phase reuses them as one flat area
+    float x[kBC * LV], dout[kBC * LV], vn[kBC * LV], dvn[kBC * LV], sblk[kBC * LV];
+    float m[kBC * kLC], t[kBC * kLC], p[kBC * kLC], dp[kBC * kLC], dt[kBC * kLC];
+    float gam[DK], dgam[DK], beta[kBC], dbeta[kBC], qinv[kBC], kinv[kBC];
+    static_assert(5 * kBC * LV + 5 * kBC * kLC >= 3 * kBC * LK, "flat area holds three [C][DK] arrays");
+};
+
+// The [C][DK] gradients dQh, dKh, dKc live in registers. Wave w owns the 16x16 tiles
+// (ti, tj) with tj = ((w - 2 ti) & 3) + 4 j', j' < DK/64, at index m = ti DK/64 + j';
+// every block of 32 key channels then holds exactly one tile of each wave.
+template <typename E, int DK, int DV, bool NORM>
+__global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ la,
+    const E* __restrict__ beta, const E* __restrict__ d_out, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ chunk_off, const float* __restrict__ s_in, const float* __restrict__ ds_out,
+    E* __restrict__ dq, E* __restrict__ dk, E* __restrict__ dv, E* __restrict__ dla, E* __restrict__ dbeta,
+    int num_seqs, int H, int64_t total_tokens, int max_chunks)
+{
+    using S_ = GradLds<DK, DV>;
+    constexpr int LK = S_::LK, LV = S_::LV;
+    constexpr int NCT = DK / 16, NVT = DV / 16;
+    constexpr int XPW = NVT / 2;            // [C][DV] tiles per wave
+    constexpr int KPW = NCT / 2;            // [C][DK] tiles per wave
+    constexpr int J4 = DK / 64;             // j' range of the owned tiles
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    S_& sm = *reinterpret_cast<S_*>(smem_raw);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+
+    const int c = blockIdx.x, h = blockIdx.y;
+    const int n = owner(chunk_off, num_seqs, c, max_chunks);
+    if (n < 0) return;
+    int64_t s0, s1;
+    bounds(cu, n, total_tokens, s0, s1);
+    const int64_t t0 = s0 + int64_t(c - chunk_off[n]) * kBC;
+    const int nrow = int(min<int64_t>(kBC, s1 - t0));
+    const float* Sg = s_in + (int64_t(h) * max_chunks + c) * DK * DV;
+    const float* dSg = ds_out + (int64_t(h) * max_chunks + c) * DK * DV;
+
+    // ---- operands, V and dO ----
+    for (int i = tid; i < kBC * DV; i += kBT) {
+        const int row = i / DV, cc = i % DV;
+        const bool ok = row < nrow;
+        const int64_t off = ((t0 + row) * H + h) * DV + cc;
+        sm.x[row * LV + cc] = ok ? ldf(v + off) : 0.f;
+        sm.dout[row * LV + cc] = ok ? ldf(d_out + off) : 0.f;
+    }
+    if (tid < DK) sm.dgam[tid] = 0.f;
+    if (tid < kBC) sm.dbeta[tid] = 0.f;
+    const ChunkLds L{sm.qh, sm.kh, sm.kc, sm.m, sm.t, sm.p, sm.gam, sm.beta, sm.qinv, sm.kinv};
+    chunk_operands<E, DK, NORM>(L, q, k, la, beta, t0, nrow, H, h);   // ends with a barrier
+
+    // a [C][DV]-shaped result: tile index wave + 4 mm
+    auto xtile = [&](int mm, int& ti, int& tj) {
+        const int tt = wave + 4 * mm;
+        ti = tt / NVT;
+        tj = tt % NVT;
+    };
+    // 32 rows of a state matrix (rows 32 kb..) to sblk
+    auto load_block = [&](const float* src, int kb) {
+        for (int i = tid; i < kBC * DV / 4; i += kBT) {
+            const int row = (4 * i) / DV, cc = (4 * i) % DV;
+            *reinterpret_cast<float4*>(&sm.sblk[row * LV + cc]) =
+                *reinterpret_cast<const float4*>(src + (32 * kb + row) * DV + cc);
+        }
+    };
+
+    // ---- X = V - Kh S ----
+    {
+        f32x4 ax[XPW];
+#pragma unroll
+        for (int mm = 0; mm < XPW; ++mm) ax[mm] = zero4();
+        for (int kb = 0; kb < DK / 32; ++kb) {
+            load_block(Sg, kb);
+            __syncthreads();
+#pragma unroll
+            for (int mm = 0; mm < XPW; ++mm) {
+                int ti, tj;
+                xtile(mm, ti, tj);
+#pragma unroll
+                for (int k0 = 0; k0 < 32; k0 += 4)
+                    ax[mm] = mma4(sm.kh[(16 * ti + r) * LK + 32 * kb + k0 + g], sm.sblk[(k0 + g) * LV + 16 * tj + r], ax[mm]);
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int mm = 0; mm < XPW; ++mm) {
+            int ti, tj;
+            xtile(mm, ti, tj);
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) sm.x[(16 * ti + 4 * g + v4) * LV + 16 * tj + r] -= ax[mm][v4];
+        }
+    }
+    __syncthreads();
+    // ---- Vn = T diag(b) X ----
+#pragma unroll
+    for (int mm = 0; mm < XPW; ++mm) {
+        int ti, tj;
+        xtile(mm, ti, tj);
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < kBC; k0 += 4)
+            acc = mma4(sm.t[(16 * ti + r) * kLC + k0 + g], sm.beta[k0 + g] * sm.x[(k0 + g) * LV + 16 * tj + r], acc);
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) sm.vn[(16 * ti + 4 * g + v4) * LV + 16 * tj + r] = acc[v4];
+    }
+    __syncthreads();
+
+    f32x4 aQh[KPW], aKh[KPW], aKc[KPW];
+#pragma unroll
+    for (int mm = 0; mm < KPW; ++mm) {
+        aQh[mm] = zero4();
+        aKh[mm] = zero4();
+        aKc[mm] = zero4();
+    }
+    // this wave's tile in the 32-channel block kb: row tile ti, column tile tj
+    auto block_tile = [&](int kb, int& ti, int& tj) {
+        ti = (((wave & 3) >> 1) == (kb & 1)) ? 0 : 1;
+        tj = 4 * (kb >> 1) + ((wave - 2 * ti) & 3);
+    };
+
+    // ---- dVn = P^T dO + Kc diag(gamma) dS';  dKbar = Vn dS'^T -> dKc, dgamma ----
+    {
+        f32x4 adv[XPW];
+#pragma unroll
+        for (int mm = 0; mm < XPW; ++mm) {
+            int ti, tj;
+            xtile(mm, ti, tj);
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < kBC; k0 += 4)
+                acc = mma4(sm.p[(k0 + g) * kLC + 16 * ti + r], sm.dout[(k0 + g) * LV + 16 * tj + r], acc);
+            adv[mm] = acc;
+        }
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) {
+            load_block(dSg, kb);
+            __syncthreads();
+#pragma unroll
+            for (int mm = 0; mm < XPW; ++mm) {
+                int ti, tj;
+                xtile(mm, ti, tj);
+#pragma unroll
+                for (int k0 = 0; k0 < 32; k0 += 4) {
+                    const int cc = 32 * kb + k0 + g;
+                    adv[mm] = mma4(sm.kc[(16 * ti + r) * LK + cc] * sm.gam[cc], sm.sblk[(k0 + g) * LV + 16 * tj + r], adv[mm]);
+                }
+            }
+            int ti, tj;
+            block_tile(kb, ti, tj);
+            f32x4 acc = zero4();
+#pragma unroll 8
+            for (int j0 = 0; j0 < DV; j0 += 4)
+                acc = mma4(sm.vn[(16 * ti + r) * LV + j0 + g], sm.sblk[(16 * (tj - 2 * kb) + r) * LV + j0 + g], acc);
+            const int cc = 16 * tj + r;
+            const float gm = sm.gam[cc];
+            float part = 0.f;
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) part += acc[v4] * sm.kc[(16 * ti + 4 * g + v4) * LK + cc];
+            atomicAdd(&sm.dgam[cc], part);
+            if (ti == 0) {
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4) aKc[kb >> 1][v4] += acc[v4] * gm;
+            } else {
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4) aKc[J4 + (kb >> 1)][v4] += acc[v4] * gm;
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int mm = 0; mm < XPW; ++mm) {
+            int ti, tj;
+            xtile(mm, ti, tj);
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) sm.dvn[(16 * ti + 4 * g + v4) * LV + 16 * tj + r] = adv[mm][v4];
+        }
+    }
+    __syncthreads();
+
+    // ---- dP = LowerIncl(dO Vn^T);  Z = T^T dVn, dX = diag(b) Z, db += rowsum(Z X) ----
+    f32x4 adx[XPW];
+    {
+        const int ti = wave >> 1, tj = wave & 1;
+        f32x4 acc = zero4();
+#pragma unroll 8
+        for (int j0 = 0; j0 < DV; j0 += 4)
+            acc = mma4(sm.dout[(16 * ti + r) * LV + j0 + g], sm.vn[(16 * tj + r) * LV + j0 + g], acc);
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+            const int i = 16 * ti + 4 * g + v4, j = 16 * tj + r;
+            sm.dp[i * kLC + j] = i >= j ? acc[v4] : 0.f;
+        }
+    }
+#pragma unroll
+    for (int mm = 0; mm < XPW; ++mm) {
+        int ti, tj;
+        xtile(mm, ti, tj);
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < kBC; k0 += 4)
+            acc = mma4(sm.t[(k0 + g) * kLC + 16 * ti + r], sm.dvn[(k0 + g) * LV + 16 * tj + r], acc);
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+            const int row = 16 * ti + 4 * g + v4;
+            float part = acc[v4] * sm.x[row * LV + 16 * tj + r];
+#pragma unroll
+            for (int sh = 1; sh < 16; sh <<= 1) part += __shfl_xor(part, sh);
+            if (r == 0) atomicAdd(&sm.dbeta[row], part);
+            adx[mm][v4] = sm.beta[row] * acc[v4];
+        }
+    }
+    __syncthreads();
+    // ---- dX over Vn (dead); dT = dVn X^T diag(b) ----
+#pragma unroll
+    for (int mm = 0; mm < XPW; ++mm) {
+        int ti, tj;
+        xtile(mm, ti, tj);
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) sm.vn[(16 * ti + 4 * g + v4) * LV + 16 * tj + r] = adx[mm][v4];
+    }
+    {
+        const int ti = wave >> 1, tj = wave & 1;
+        f32x4 acc = zero4();
+#pragma unroll 8
+        for (int j0 = 0; j0 < DV; j0 += 4)
+            acc = mma4(sm.dvn[(16 * ti + r) * LV + j0 + g], sm.x[(16 * tj + r) * LV + j0 + g], acc);
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+            const int i = 16 * ti + 4 * g + v4, s = 16 * tj + r;
+            sm.dt[i * kLC + s] = acc[v4] * sm.beta[s];
+        }
+    }
+    __syncthreads();
+    // ---- R = dT T^T (over P, dead) ----
+    {
+        const int ti = wave >> 1, tj = wave & 1;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int u0 = 0; u0 < kBC; u0 += 4)
+            acc = mma4(sm.dt[(16 * ti + r) * kLC + u0 + g], sm.t[(16 * tj + r) * kLC + u0 + g], acc);
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) sm.p[(16 * ti + 4 * g + v4) * kLC + 16 * tj + r] = acc[v4];
+    }
+    __syncthreads();
+    // ---- dA = StrictLower(-T^T R), dM = diag(b) dA (over dT), db += rowsum(dA M) ----
+    {
+        const int ti = wave >> 1, tj = wave & 1;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int u0 = 0; u0 < kBC; u0 += 4)
+            acc = mma4(sm.t[(u0 + g) * kLC + 16 * ti + r], sm.p[(u0 + g) * kLC + 16 * tj + r], acc);
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+            const int i = 16 * ti + 4 * g + v4, s = 16 * tj + r;
+            const float da = i > s ? -acc[v4] : 0.f;
+            sm.dt[i * kLC + s] = sm.beta[i] * da;
+            float part = da * sm.m[i * kLC + s];
+#pragma unroll
+            for (int sh = 1; sh < 16; sh <<= 1) part += __shfl_xor(part, sh);
+            if (r == 0) atomicAdd(&sm.dbeta[i], part);
+        }
+    }
+    __syncthreads();
+
+    // ---- chunk-internal parts: dQh += dP Kc, dKh += dM Kc, dKc += dP^T Qh + dM^T Kh ----
+#pragma unroll
+    for (int mm = 0; mm < KPW; ++mm) {
+        const int ti = mm / J4, tj = ((wave - 2 * ti) & 3) + 4 * (mm % J4);
+#pragma unroll
+        for (int s0_ = 0; s0_ < kBC; s0_ += 4) {
+            const int s = s0_ + g;
+            const float kcv = sm.kc[s * LK + 16 * tj + r];
+            aQh[mm] = mma4(sm.dp[(16 * ti + r) * kLC + s], kcv, aQh[mm]);
+            aKh[mm] = mma4(sm.dt[(16 * ti + r) * kLC + s], kcv, aKh[mm]);
+            aKc[mm] = mma4(sm.dp[s * kLC + 16 * ti + r], sm.qh[s * LK + 16 * tj + r], aKc[mm]);
+            aKc[mm] = mma4(sm.dt[s * kLC + 16 * ti + r], sm.kh[s * LK + 16 * tj + r], aKc[mm]);
+        }
+    }
+    // ---- state parts: dQh += dO S^T, dKh -= dX S^T;  dgamma += rowsum(dS' S) ----
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) {
+        load_block(Sg, kb);
+        __syncthreads();
+        int ti, tj;
+        block_tile(kb, ti, tj);
+        f32x4 aq = zero4(), ak = zero4();
+#pragma unroll 8
+        for (int j0 = 0; j0 < DV; j0 += 4) {
+            const float sv = sm.sblk[(16 * (tj - 2 * kb) + r) * LV + j0 + g];
+            aq = mma4(sm.dout[(16 * ti + r) * LV + j0 + g], sv, aq);
+            ak = mma4(sm.vn[(16 * ti + r) * LV + j0 + g], sv, ak);
+        }
+        if (ti == 0) {
+            aQh[kb >> 1] += aq;
+            aKh[kb >> 1] -= ak;
+        } else {
+            aQh[J4 + (kb >> 1)] += aq;
+            aKh[J4 + (kb >> 1)] -= ak;
+        }
+        {
+            const int row = tid >> 3, part = tid & 7;         // 8 lanes per state row
+            float acc = 0.f;
+            for (int j = part * 4; j < DV; j += 32) {
+                const float4 a = *reinterpret_cast<const float4*>(dSg + (32 * kb + row) * DV + j);
+                const float4 b = *reinterpret_cast<const float4*>(&sm.sblk[row * LV + j]);
+                acc += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+            }
+#pragma unroll
+            for (int sh = 1; sh < 8; sh <<= 1) acc += __shfl_xor(acc, sh);
+            if (part == 0) atomicAdd(&sm.dgam[32 * kb + row], acc);
+        }
+        __syncthreads();
+    }
+    // ---- dv = dX, db ----
+    for (int i = tid; i < kBC * DV; i += kBT) {
+        const int row = i / DV, cc = i % DV;
+        if (row < nrow) stf(dv + ((t0 + row) * H + h) * DV + cc, sm.vn[row * LV + cc]);
+    }
+    if (tid < nrow) stf(dbeta + (t0 + tid) * H + h, sm.dbeta[tid]);
+    __syncthreads();
+
+    // ---- through the decays: G again (flat area 0), then dQ, dK, dG ----
+    float* F0 = sm.x;                       // G, then dQ
+    float* F1 = sm.x + kBC * LK;            // dK
+    float* F2 = sm.x + 2 * kBC * LK;        // dG, then dlog a
+    if (tid < DK) {
+        float G = 0.f;
+        for (int row = 0; row < kBC; ++row) {
+            if (row < nrow) G += ldf(la + ((t0 + row) * H + h) * DK + tid);
+            F0[row * LK + tid] = G;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int mm = 0; mm < KPW; ++mm) {
+        const int ti = mm / J4, tj = ((wave - 2 * ti) & 3) + 4 * (mm % J4);
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+            const int row = 16 * ti + 4 * g + v4, cc = 16 * tj + r, o = row * LK + cc;
+            const float G = F0[o], ex = expf(G), ei = expf(-G);
+            const float a = aQh[mm][v4], b = aKh[mm][v4], e = aKc[mm][v4];
+            F0[o] = a * ex;
+            F1[o] = b * ex + e * ei;
+            F2[o] = a * sm.qh[o] + b * sm.kh[o] - e * sm.kc[o];
+        }
+    }
+    __syncthreads();
+    // dlog a: reverse cumsum of dG over the valid rows, dgamma gamma entering at the last one
+    if (tid < DK) {
+        float acc = sm.dgam[tid] * sm.gam[tid];
+        for (int row = kBC - 1; row >= 0; --row) {
+            if (row < nrow) acc += F2[row * LK + tid];
+            F2[row * LK + tid] = row < nrow ? acc : 0.f;
+        }
+    }
+    if constexpr (NORM) {
+        // dx = (dx^ - x^ (x^ . dx^)) / |x| for x^ = x / |x|, x = q, k of the row
+        const int row = tid >> 3, part = tid & 7;
+        float dotq = 0.f, dotk = 0.f;
+        if (row < nrow) {
+            for (int cc = part; cc < DK; cc += 8) {
+                const int64_t off = ((t0 + row) * H + h) * DK + cc;
+                dotq += ldf(q + off) * sm.qinv[row] * F0[row * LK + cc];
+                dotk += ldf(k + off) * sm.kinv[row] * F1[row * LK + cc];
+            }
+        }
+#pragma unroll
+        for (int sh = 1; sh < 8; sh <<= 1) {
+            dotq += __shfl_xor(dotq, sh);
+            dotk += __shfl_xor(dotk, sh);
+        }
+        if (row < nrow) {
+            for (int cc = part; cc < DK; cc += 8) {
+                const int64_t off = ((t0 + row) * H + h) * DK + cc;
+                const float qn = ldf(q + off) * sm.qinv[row], kn = ldf(k + off) * sm.kinv[row];
+                F0[row * LK + cc] = (F0[row * LK + cc] - qn * dotq) * sm.qinv[row];
+                F1[row * LK + cc] = (F1[row * LK + cc] - kn * dotk) * sm.kinv[row];
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < kBC * DK; i += kBT) {
+        const int row = i / DK, cc = i % DK;
+        if (row < nrow) {
+            const int64_t off = ((t0 + row) * H + h) * DK + cc;
+            stf(dq + off, F0[row * LK + cc]);
+            stf(dk + off, F1[row * LK + cc]);
+            stf(dla + off, F2[row * LK + cc]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+struct BwdPlan {
+    int max_chunks;
+    size_t table_bytes, rec_bytes, state_bytes;
+};
+
+BwdPlan bwd_plan(int64_t total_tokens, int32_t num_seqs, int32_t num_heads, int d_k, int d_v)
+{
+    BwdPlan p{};
+    p.max_chunks = int((total_tokens + kBC - 1) / kBC + num_seqs);
+    p.table_bytes = ((size_t(num_seqs) + 1) * sizeof(int32_t) + 255) & ~size_t(255);
+    const size_t rec = d_k == 128 ? BRec<128>::TOTAL : BRec<64>::TOTAL;
+    p.rec_bytes = size_t(p.max_chunks) * num_heads * rec * sizeof(float);
+    p.state_bytes = size_t(p.max_chunks) * num_heads * d_k * d_v * sizeof(float);
+    return p;
+}
+
+template <typename K> hipError_t set_smem(K kern, size_t bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               int(bytes));
+}
+
+template <typename E, int DK, int DV, bool NORM>
+hipError_t launch_bwd_t(const BwdArgs& a, void* workspace, TimingHook* th)
+{
+    const BwdPlan p = bwd_plan(a.total_tokens, a.num_seqs, a.num_heads, DK, DV);
+    char* base = static_cast<char*>(workspace);
+    int32_t* chunk_off = reinterpret_cast<int32_t*>(base);
+    float* rec = reinterpret_cast<float*>(base + p.table_bytes);
+    float* s_in = reinterpret_cast<float*>(base + p.table_bytes + p.rec_bytes);
+    float* ds_out = reinterpret_cast<float*>(base + p.table_bytes + p.rec_bytes + p.state_bytes);
+    const E* q = static_cast<const E*>(a.q);
+    const E* k = static_cast<const E*>(a.k);
+    const E* v = static_cast<const E*>(a.v);
+    const E* la = static_cast<const E*>(a.log_alpha);
+    const E* beta = static_cast<const E*>(a.beta);
+    const E* dout = static_cast<const E*>(a.d_out);
+    const int H = a.num_heads;
+    hipError_t e;
+
+    if (th) th->begin("bwd_plan", a.stream);
+    hipLaunchKernelGGL(kda_bwd_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, chunk_off, a.num_seqs,
+                       a.total_tokens);
+    if (th) th->end(a.stream);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    const size_t prep_smem = sizeof(PrepLds<DK>);
+    auto prep = kda_bwd_prep_kernel<E, DK, NORM>;
+    if ((e = set_smem(prep, prep_smem)) != hipSuccess) return e;
+    if (th) th->begin("bwd_prep", a.stream);
+    hipLaunchKernelGGL(prep, dim3(p.max_chunks, H), dim3(kBT), prep_smem, a.stream, q, k, la, beta, a.cu_seqlens,
+                       chunk_off, rec, a.num_seqs, H, a.total_tokens, p.max_chunks);
+    if (th) th->end(a.stream);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    const int units = a.num_seqs * H;
+    const int cblocks = ((units + 7) / 8) * 8 * (DV / 64);
+    const size_t chain_smem = sizeof(ChainLds<DK>);
+    auto st = kda_bwd_state_kernel<E, DK, DV>;
+    auto dst = kda_bwd_dstate_kernel<E, DK, DV>;
+    if ((e = set_smem(st, chain_smem)) != hipSuccess) return e;
+    if ((e = set_smem(dst, chain_smem)) != hipSuccess) return e;
+    if (th) th->begin("bwd_state", a.stream);
+    hipLaunchKernelGGL(st, dim3(cblocks), dim3(kBT), chain_smem, a.stream, v, a.cu_seqlens, chunk_off, rec,
+                       a.init_state, s_in, a.num_seqs, H, a.total_tokens, p.max_chunks);
+    if (th) th->end(a.stream);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (th) th->begin("bwd_dstate", a.stream);
+    hipLaunchKernelGGL(dst, dim3(cblocks), dim3(kBT), chain_smem, a.stream, dout, a.cu_seqlens, chunk_off, rec,
+                       a.d_final_state, ds_out, a.d_init_state, a.num_seqs, H, a.total_tokens, p.max_chunks);
+    if (th) th->end(a.stream);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    const size_t grad_smem = sizeof(GradLds<DK, DV>);
+    auto grad = kda_bwd_grad_kernel<E, DK, DV, NORM>;
+    if ((e = set_smem(grad, grad_smem)) != hipSuccess) return e;
+    if (th) th->begin("bwd_grad", a.stream);
+    hipLaunchKernelGGL(grad, dim3(p.max_chunks, H), dim3(kBT), grad_smem, a.stream, q, k, v, la, beta, dout,
+                       a.cu_seqlens, chunk_off, s_in, ds_out, static_cast<E*>(a.dq), static_cast<E*>(a.dk),
+                       static_cast<E*>(a.dv), static_cast<E*>(a.dlog_alpha), static_cast<E*>(a.dbeta), a.num_seqs,
+                       H, a.total_tokens, p.max_chunks);
+    if (th) th->end(a.stream);
+    return hipGetLastError();
+}
+
+template <typename E, bool NORM>
+hipError_t launch_bwd_n(const BwdArgs& a, void* ws, TimingHook* th)
+{
+    if (a.d_k == 128 && a.d_v == 128) return launch_bwd_t<E, 128, 128, NORM>(a, ws, th);
+    if (a.d_k == 128 && a.d_v == 64) return launch_bwd_t<E, 128, 64, NORM>(a, ws, th);
+    if (a.d_k == 64 && a.d_v == 128) return launch_bwd_t<E, 64, 128, NORM>(a, ws, th);
+    return launch_bwd_t<E, 64, 64, NORM>(a, ws, th);
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads, int d_k, int d_v)
+{
+    const BwdPlan p = bwd_plan(total_tokens, num_seqs, num_heads, d_k, d_v);
+    return p.table_bytes + p.rec_bytes + 2 * p.state_bytes;
+}
+
+hipError_t launch_backward(const BwdArgs& a, void* workspace, TimingHook* th)
+{
+    const BwdPlan p = bwd_plan(a.total_tokens, a.num_seqs, a.num_heads, a.d_k, a.d_v);
+    if (int64_t(p.max_chunks) * a.num_heads > 0x7FFFFFFF / 64) return hipErrorInvalidValue;
+    if (a.dtype_bf16)
+        return a.qk_l2norm ? launch_bwd_n<uint16_t, true>(a, workspace, th) : launch_bwd_n<uint16_t, false>(a, workspace, th);
+    return a.qk_l2norm ? launch_bwd_n<float, true>(a, workspace, th) : launch_bwd_n<float, false>(a, workspace, th);
+}
+
+}  // namespace kda

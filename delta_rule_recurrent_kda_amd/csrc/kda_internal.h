@@ -50,6 +50,23 @@ size_t wy_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_he
 // Bytes of one (64-token chunk, head) record of the workspace.
 size_t wy_record_bytes(int d_k, int d_v);
 
+// Backward (gradients of the scan): chunk table, prep, forward state chain, reverse
+// state-gradient chain and a chunk-parallel gradient kernel; fp32 arithmetic.
+struct BwdArgs {
+    const void *q, *k, *v, *log_alpha, *beta;
+    const int32_t* cu_seqlens;
+    const float* init_state;        // [N][H][d_k][d_v] or NULL
+    const void* d_out;              // [T][H][d_v] dtype
+    const float* d_final_state;     // [N][H][d_k][d_v] or NULL
+    void *dq, *dk, *dv, *dlog_alpha, *dbeta;
+    float* d_init_state;            // [N][H][d_k][d_v] or NULL
+    int64_t total_tokens;
+    int32_t num_seqs, num_heads, d_k, d_v, dtype_bf16, qk_l2norm;
+    hipStream_t stream;
+};
+hipError_t launch_backward(const BwdArgs& a, void* workspace, TimingHook* th);
+size_t bwd_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads, int d_k, int d_v);
+
 // LDS bytes one workgroup uses.
 size_t smem_bytes(int dtype_bf16, int d_k);
 size_t smem_bytes_pipe(int d_k);

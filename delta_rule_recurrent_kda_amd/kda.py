@@ -55,6 +55,13 @@ def library() -> ctypes.CDLL:
                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_int, ctypes.c_uint32, vp]
         lib.kda_forward_ex.restype = ctypes.c_int
+        lib.kda_backward.argtypes = [vp] * 15 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                 ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
+                                                 ctypes.c_uint32, vp]
+        lib.kda_backward.restype = ctypes.c_int
+        lib.kda_backward_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                     ctypes.c_int32, ctypes.c_int32]
+        lib.kda_backward_workspace_bytes.restype = ctypes.c_size_t
         lib.kda_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int]
         lib.kda_workspace_bytes.restype = ctypes.c_size_t
@@ -199,3 +206,47 @@ def forward(q, k, v, log_alpha, beta, cu_seqlens, with_state: bool = True,
         if with_state else None
     kda_forward(q, k, v, log_alpha, beta, cu_seqlens, out, fs, stream, initial_state, qk_l2norm)
     return out, fs
+
+
+def kda_backward_raw(q, k, v, log_alpha, beta, cu_seqlens, initial_state, d_out, d_final_state, dq,
+                     dk, dv, dlog_alpha, dbeta, d_initial_state, total_tokens: int, num_seqs: int,
+                     num_heads: int, d_k: int, d_v: int, dtype: int, options: int,
+                     stream: Optional[int]) -> int:
+    """Direct C call of kda_backward; returns the status code."""
+    return library().kda_backward(q, k, v, log_alpha, beta, cu_seqlens, initial_state, d_out,
+                                  d_final_state, dq, dk, dv, dlog_alpha, dbeta, d_initial_state,
+                                  int(total_tokens), int(num_seqs), int(num_heads), int(d_k),
+                                  int(d_v), int(dtype), int(options), stream)
+
+
+def backward_workspace_bytes(total_tokens: int, num_seqs: int, num_heads: int, d_k: int,
+                             d_v: int) -> int:
+    return int(library().kda_backward_workspace_bytes(int(total_tokens), int(num_seqs),
+                                                      int(num_heads), int(d_k), int(d_v)))
+
+
+def backward(q, k, v, log_alpha, beta, cu_seqlens, d_out, d_final_state=None, initial_state=None,
+             qk_l2norm: bool = False, with_initial_grad: bool = True,
+             stream: Optional[torch.cuda.Stream] = None):
+    """Gradients of the scan: returns (dq, dk, dv, dlog_alpha, dbeta, d_initial_state or None).
+
+    Inputs as kda_forward; d_out like out; d_final_state float32 [N, H, d_k, d_v] or None.
+    Gradients come back in the data dtype, d_initial_state in float32.
+    """
+    out_like = torch.empty_like(v)
+    T, N, H, dk, dv, dt = _check(q, k, v, log_alpha, beta, cu_seqlens, out_like, d_final_state,
+                                 initial_state)
+    if d_out.shape != v.shape or d_out.dtype != q.dtype or not d_out.is_cuda or not d_out.is_contiguous():
+        raise ValueError("d_out must be a contiguous GPU tensor shaped and typed like out")
+    g = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(log_alpha),
+         torch.empty_like(beta)]
+    dinit = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device) if with_initial_grad else None
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = kda_backward_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(cu_seqlens),
+                          _ptr(initial_state), _ptr(d_out), _ptr(d_final_state), *[_ptr(x) for x in g],
+                          _ptr(dinit), T, N, H, dk, dv, dt, KDA_OPT_QK_L2NORM if qk_l2norm else 0,
+                          stream.cuda_stream)
+    if st != 0:
+        raise KdaError(st, library().kda_last_error().decode())
+    return (*g, dinit)

@@ -150,6 +150,46 @@ kda_status kda_forward_ex(const void *q, const void *k, const void *v, const voi
                           uint32_t options, hipStream_t stream);
 
 /*
+ * kda_backward -- gradients of the KDA scan.
+ *
+ * The paper trains its model through these kernels (paper, training setup paragraph
+ * on the custom kernels over the packed tokens). For a scalar loss L whose gradient
+ * with respect to out is d_out and with respect to final_state is d_final_state, this
+ * returns dL/dq, dL/dk, dL/dv, dL/dlog_alpha, dL/dbeta and dL/dinitial_state of the
+ * scan that kda_forward_ex computes from the same inputs, initial_state and options
+ * (the reverse-mode derivative of the recurrence above; with KDA_OPT_QK_L2NORM the
+ * gradients are those of the raw q and k, through the normalisation).
+ *
+ *   q, k, v, log_alpha, beta, cu_seqlens, initial_state, options : as kda_forward_ex
+ *                     (initial_state may be NULL = zero states; supported for both dtypes)
+ *   d_out           : [total_tokens][num_heads][d_v] dtype, read only
+ *   d_final_state   : [num_seqs][num_heads][d_k][d_v] fp32 or NULL (= zero)
+ *   dq, dk, dlog_alpha : [total_tokens][num_heads][d_k] dtype, written
+ *   dv              : [total_tokens][num_heads][d_v] dtype, written
+ *   dbeta           : [total_tokens][num_heads] dtype, written
+ *   d_initial_state : [num_seqs][num_heads][d_k][d_v] fp32 or NULL (not written); the
+ *                     gradient with respect to the initial states (equal to d_final_state
+ *                     for an empty sample)
+ * Outputs may not alias inputs or each other. Arithmetic is fp32 throughout (fp32
+ * MFMA), over 32-token chunks; results in the data dtype, rounded to nearest-even.
+ * Same size limits as kda_forward. Execution: enqueued on `stream`; takes a workspace of
+ * kda_backward_workspace_bytes(...) bytes (chunk operands and the per-chunk state and
+ * state gradient, about 5 KB per token and head at d = 128) from the device's default
+ * stream-ordered pool, returned on `stream` after the kernels. Errors as kda_forward.
+ */
+kda_status kda_backward(const void *q, const void *k, const void *v, const void *log_alpha,
+                        const void *beta, const int32_t *cu_seqlens, const float *initial_state,
+                        const void *d_out, const float *d_final_state, void *dq, void *dk, void *dv,
+                        void *dlog_alpha, void *dbeta, float *d_initial_state, int64_t total_tokens,
+                        int32_t num_seqs, int32_t num_heads, int32_t d_k, int32_t d_v, kda_dtype dtype,
+                        uint32_t options, hipStream_t stream);
+
+/* Bytes of device workspace kda_backward takes for these sizes (0 for no samples or
+ * unsupported sizes). Pure function of the sizes. */
+size_t kda_backward_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads,
+                                    int32_t d_k, int32_t d_v);
+
+/*
  * kda_workspace_bytes -- bytes of device workspace the default bf16 scan takes for
  * these sizes (0 when it takes none: fp32 data, no samples, unsupported sizes).
  * Layout: per (64-token chunk, head) record of the chunk's decayed operands and
@@ -164,7 +204,8 @@ size_t kda_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_h
  * launches, named "plan", "prep", "segments" and "chain" (default bf16 scan;
  * "segments" is the first pass of the within-GPU sequence split, "plan" the chunk
  * table, launched only for packs of more than 64 samples or with the split) or
- * "scan" (single-kernel scans). kda_timing_read waits for the recorded events of `kernel`,
+ * "scan" (single-kernel scans); kda_backward records "bwd_plan", "bwd_prep",
+ * "bwd_state", "bwd_dstate" and "bwd_grad". kda_timing_read waits for the recorded events of `kernel`,
  * returns their count and summed duration in milliseconds, and drops them.
  * Process-wide state guarded by a mutex; returns KDA_E_NULL on NULL arguments and
  * KDA_E_HIP if an event cannot be read (all records are then dropped).

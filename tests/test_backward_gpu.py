@@ -1,0 +1,119 @@
+"""GPU parity of kda_backward (through the C ABI) against the fp64 reverse-mode oracle.
+
+Tolerance, per gradient tensor and per (sample, head) block, relative Frobenius norm of
+the difference: fp32 data 1e-4 (the arithmetic is fp32 throughout); bf16 data 1e-2
+(inputs, d_out and the gradients are bf16; one rounding of a gradient to bf16 is up to
+2^-9 relative per element). The worst row error relative to its row norm is reported.
+"""
+import numpy as np
+import pytest
+
+import gpu_util as gu
+from delta_rule_recurrent_kda_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "d_initial_state")
+
+
+def _draw_grads(spec, seed):
+    rng = np.random.default_rng(seed)
+    T, H, N = spec.total_tokens, spec.heads, len(spec.seq_lens)
+    do = rng.standard_normal((T, H, spec.dv))
+    do = inputs.f64_to_bf16_bits(do) if spec.dtype == "bf16" else do.astype(np.float32)
+    dfs = (rng.standard_normal((N, H, spec.dk, spec.dv)) * 0.5).astype(np.float32)
+    s0 = (rng.standard_normal((N, H, spec.dk, spec.dv)) * 0.5).astype(np.float32)
+    return do, dfs, s0
+
+
+def _run(spec, a, do, dfs, s0, norm):
+    import torch
+    from delta_rule_recurrent_kda_amd import kda
+    d = gu.device_inputs(spec, a)
+    dev = "cuda:0"
+    dt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+    tdo = (torch.from_numpy(do.view(np.int16)).view(torch.bfloat16) if spec.dtype == "bf16"
+           else torch.from_numpy(do)).to(dev)
+    assert tdo.dtype == dt
+    g = kda.backward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"], tdo,
+                     d_final_state=None if dfs is None else torch.from_numpy(dfs).to(dev),
+                     initial_state=None if s0 is None else torch.from_numpy(s0).to(dev),
+                     qk_l2norm=norm)
+    torch.cuda.synchronize()
+    return [x.float().cpu().double().numpy() for x in g]
+
+
+def _oracle(spec, a, do, dfs, s0, norm):
+    import oracle
+    f = {x: inputs.to_f64(a[x], spec.dtype) for x in ("q", "k", "v", "log_alpha", "beta")}
+    return oracle.backward(f["q"], f["k"], f["v"], f["log_alpha"], f["beta"], a["cu_seqlens"],
+                           inputs.to_f64(do, spec.dtype), dfs, s0, qk_l2norm=norm,
+                           threads=16)
+
+
+def _compare(spec, got, ref, label):
+    tol = 1e-4 if spec.dtype == "f32" else 1e-2
+    cu = spec.cu_seqlens()
+    worst = {}
+    for name, x, y in zip(NAMES, got, ref):
+        w = 0.0
+        for n in range(len(cu) - 1):
+            for h in range(spec.heads):
+                if name == "d_initial_state":
+                    a, b = x[n, h], y[n, h]
+                else:
+                    a, b = x[cu[n]:cu[n + 1], h], y[cu[n]:cu[n + 1], h]
+                if b.size == 0:
+                    continue
+                nb = np.linalg.norm(b)
+                e = np.linalg.norm(a - b) / nb if nb > 0 else np.abs(a).max()
+                w = max(w, e)
+        worst[name] = w
+    gu.log(f"[{label}] worst per-block rel frob: " + ", ".join(f"{k} {v:.2e}" for k, v in worst.items()))
+    for name, w in worst.items():
+        assert w <= tol, (label, name, w, tol)
+
+
+CASES = [
+    ("bf16_d128", (129, 0, 64, 200, 1, 63), 3, 128, 128, "bf16", False, True),
+    ("bf16_d128_zero_state", (129, 0, 64, 200, 1, 63), 2, 128, 128, "bf16", False, False),
+    ("bf16_d64_128", (70, 33, 0, 100), 2, 64, 128, "bf16", False, True),
+    ("bf16_d128_64", (70, 33, 0, 100), 2, 128, 64, "bf16", False, True),
+    ("bf16_norm", (129, 0, 64, 200, 1, 63), 2, 128, 128, "bf16", True, True),
+    ("f32_d64", (100, 37, 0, 250), 2, 64, 64, "f32", False, True),
+    ("f32_d128_norm", (70, 130), 2, 128, 128, "f32", True, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_backward_vs_oracle(case):
+    name, lens, H, dk, dv, dt, norm, with_state = case
+    spec = inputs.KdaSpec(f"bwd_{name}", lens, H, dk, dv, dt, (0.001, 0.1), 7171)
+    gu.log(f"case backward {name}")
+    a = inputs.generate(spec)
+    if norm:
+        a = gu.unnormalised(spec, a, 71)
+    do, dfs, s0 = _draw_grads(spec, 72)
+    if not with_state:
+        dfs = s0 = None
+    got = _run(spec, a, do, dfs, s0, norm)
+    ref = _oracle(spec, a, do, dfs, s0, norm)
+    _compare(spec, got, ref, f"backward {name}")
+
+
+def test_backward_timing_records_each_kernel():
+    import torch
+    from delta_rule_recurrent_kda_amd import kda
+    spec = inputs.KdaSpec("bwd_timing", (300, 77), 2, 128, 128, "bf16", (0.001, 0.1), 7272)
+    gu.log("case backward timing")
+    a = inputs.generate(spec)
+    do, _, _ = _draw_grads(spec, 73)
+    kda.timing_enable(True)
+    try:
+        _run(spec, a, do, None, None, False)
+    finally:
+        kda.timing_enable(False)
+    for name in ("bwd_plan", "bwd_prep", "bwd_state", "bwd_dstate", "bwd_grad"):
+        n, ms = kda.timing_read(name)
+        assert n == 1 and ms > 0, (name, n, ms)
+    torch.cuda.synchronize()
