@@ -59,6 +59,54 @@ template <typename E> __device__ __forceinline__ void stf(E* p, float x);
 template <> __device__ __forceinline__ void stf<float>(float* p, float x) { *p = x; }
 template <> __device__ __forceinline__ void stf<uint16_t>(uint16_t* p, float x) { *p = f2bf(x); }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 16 raw bytes in registers
+
+// 16 bytes of data dtype E as fp32 to LDS (8 bf16 or 4 fp32 values), zeros when !ok
+template <typename E> __device__ __forceinline__ void put16(float* dst, const u32x4& raw, bool ok);
+template <> __device__ __forceinline__ void put16<float>(float* dst, const u32x4& raw, bool ok) {
+    const float4 f = ok ? make_float4(__uint_as_float(raw.x), __uint_as_float(raw.y), __uint_as_float(raw.z),
+                                      __uint_as_float(raw.w))
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(dst) = f;
+}
+template <> __device__ __forceinline__ void put16<uint16_t>(float* dst, const u32x4& raw, bool ok) {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+    if (ok) {
+        a = make_float4(__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xFFFF0000u),
+                        __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xFFFF0000u));
+        b = make_float4(__uint_as_float(raw.z << 16), __uint_as_float(raw.z & 0xFFFF0000u),
+                        __uint_as_float(raw.w << 16), __uint_as_float(raw.w & 0xFFFF0000u));
+    }
+    *reinterpret_cast<float4*>(dst) = a;
+    *reinterpret_cast<float4*>(dst + 4) = b;
+}
+
+// A [C][W] block of rows t0.. of a [T][H][W] tensor of dtype E, as 16-byte pieces held
+// by the workgroup's threads (rows past the chunk's end re-read its last row and are
+// zeroed when written to LDS). Loads only: put() writes them to a [C][ld] LDS array.
+template <typename E, int W> struct RowPieces {
+    static constexpr int EPP = 16 / sizeof(E);       // elements per piece
+    static constexpr int PPR = W / EPP;              // pieces per row
+    static constexpr int NP = (kBC * PPR + kBT - 1) / kBT;
+    u32x4 v[NP];
+    __device__ __forceinline__ void load(const E* __restrict__ src, int64_t t0, int nrow, int H, int h, int col0,
+                                         int rowlen) {
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int pc = min(int(threadIdx.x) + j * kBT, kBC * PPR - 1);
+            const int row = min(pc / PPR, nrow - 1);
+            v[j] = *reinterpret_cast<const u32x4*>(src + ((t0 + row) * H + h) * rowlen + col0 + (pc % PPR) * EPP);
+        }
+    }
+    __device__ __forceinline__ void put(float* dst, int ld, int nrow) const {
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int pc = int(threadIdx.x) + j * kBT;
+            if (pc < kBC * PPR) put16<E>(dst + (pc / PPR) * ld + (pc % PPR) * EPP, v[j], pc / PPR < nrow);
+        }
+    }
+};
+
 // Record of one (chunk, head) written by the prep for the two chains (floats).
 template <int DK> struct BRec {
     static constexpr int KH = 0;                    // Kh [C][DK]
@@ -140,21 +188,17 @@ __device__ void chunk_operands(const ChunkLds& L, const E* __restrict__ q, const
     constexpr int LK = DK + 4;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, g = lane >> 4;
-    // raw q, k, log a rows to LDS (zeros past the sample's end); log a goes where Kc will be
-    for (int i = tid; i < kBC * DK; i += kBT) {
-        const int row = i / DK, c = i % DK;
-        float qv = 0.f, kv = 0.f, lv = 0.f;
-        if (row < nrow) {
-            const int64_t off = ((t0 + row) * H + h) * DK + c;
-            qv = ldf(q + off);
-            kv = ldf(k + off);
-            lv = ldf(la + off);
-        }
-        L.qh[row * LK + c] = qv;
-        L.kh[row * LK + c] = kv;
-        L.kc[row * LK + c] = lv;
-    }
-    if (tid < kBC) L.beta[tid] = tid < nrow ? ldf(beta + (t0 + tid) * H + h) : 0.f;
+    // raw q, k, log a rows to LDS (zeros past the sample's end); log a goes where Kc
+    // will be. Every load is issued before the first LDS write.
+    RowPieces<E, DK> pq, pk, pl;
+    pq.load(q, t0, nrow, H, h, 0, DK);
+    pk.load(k, t0, nrow, H, h, 0, DK);
+    pl.load(la, t0, nrow, H, h, 0, DK);
+    const float bv = tid < nrow ? ldf(beta + (t0 + min(tid, nrow - 1)) * H + h) : 0.f;
+    pq.put(L.qh, LK, nrow);
+    pk.put(L.kh, LK, nrow);
+    pl.put(L.kc, LK, nrow);
+    if (tid < kBC) L.beta[tid] = bv;
     __syncthreads();
     if constexpr (NORM) {
         // 8 lanes per row, DK/8 channels each
@@ -295,36 +339,52 @@ __device__ __forceinline__ void chain_unit(int b, int nvt, int& unit, int& vt) {
     unit = (b / (8 * nvt)) * 8 + (b & 7);
 }
 
-// stage the record of chunk cc and a [C][64] tile of `src` (V or dO, rows t0..) into LDS
-template <typename E, int DK, bool GRAD>
-__device__ __forceinline__ void chain_stage(ChainLds<DK>& sm, const float* __restrict__ rec, const E* __restrict__ src,
-                                            int64_t t0, int nrow, int H, int h, int DV, int col0)
-{
+// The record of one chunk and a [C][64] tile of V or dO, held in registers: loaded one
+// chunk ahead, written to LDS once the previous chunk's products are done.
+template <typename E, int DK, bool GRAD> struct ChainFetch {
     using R = BRec<DK>;
-    constexpr int LK = DK + 4, LV = 64 + 4;
-    const int tid = threadIdx.x;
-    for (int i = tid; i < kBC * DK / 4; i += kBT) {
-        const int row = (4 * i) / DK, c = (4 * i) % DK;
-        const float4 a = *reinterpret_cast<const float4*>(rec + R::KH + 4 * i);
-        const float4 b = *reinterpret_cast<const float4*>(rec + R::KC + 4 * i);
-        *reinterpret_cast<float4*>(&sm.kh[row * LK + c]) = a;
-        *reinterpret_cast<float4*>(&sm.kc[row * LK + c]) = b;
-        if constexpr (GRAD) {
-            const float4 e = *reinterpret_cast<const float4*>(rec + R::QH + 4 * i);
-            *reinterpret_cast<float4*>(&sm.qh[row * LK + c]) = e;
+    static constexpr int NKP = kBC * DK / 4 / kBT;      // f32x4 per thread per [C][DK] array
+    static constexpr int NGB = (DK + kBC) / 4;          // f32x4 pieces of gamma and b
+    static_assert(kBC * kBC / 4 == kBT, "one f32x4 of T and of P per thread");
+    f32x4 kh[NKP], kc[NKP], qh[GRAD ? NKP : 1];
+    f32x4 t, p, gb;
+    RowPieces<E, 64> vt;
+    int nrow;
+    __device__ __forceinline__ void load(const float* __restrict__ rec, const E* __restrict__ src, int64_t t0,
+                                         int nrow_, int H, int h, int DV, int col0) {
+        const int tid = threadIdx.x;
+        nrow = nrow_;
+#pragma unroll
+        for (int j = 0; j < NKP; ++j) {
+            kh[j] = *reinterpret_cast<const f32x4*>(rec + R::KH + 4 * (tid + j * kBT));
+            kc[j] = *reinterpret_cast<const f32x4*>(rec + R::KC + 4 * (tid + j * kBT));
+            if constexpr (GRAD) qh[j] = *reinterpret_cast<const f32x4*>(rec + R::QH + 4 * (tid + j * kBT));
         }
+        t = *reinterpret_cast<const f32x4*>(rec + R::T + 4 * tid);
+        if constexpr (GRAD) p = *reinterpret_cast<const f32x4*>(rec + R::P + 4 * tid);
+        gb = *reinterpret_cast<const f32x4*>(rec + R::GAM + 4 * min(tid, NGB - 1));
+        vt.load(src, t0, nrow, H, h, col0, DV);
     }
-    for (int i = tid; i < kBC * kBC; i += kBT) {
-        sm.t[(i / kBC) * kLC + i % kBC] = rec[R::T + i];
-        if constexpr (GRAD) sm.p[(i / kBC) * kLC + i % kBC] = rec[R::P + i];
+    __device__ __forceinline__ void put(ChainLds<DK>& sm) const {
+        constexpr int LK = DK + 4, LV = 64 + 4;
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int j = 0; j < NKP; ++j) {
+            const int i = 4 * (tid + j * kBT), row = i / DK, c = i % DK;
+            *reinterpret_cast<f32x4*>(&sm.kh[row * LK + c]) = kh[j];
+            *reinterpret_cast<f32x4*>(&sm.kc[row * LK + c]) = kc[j];
+            if constexpr (GRAD) *reinterpret_cast<f32x4*>(&sm.qh[row * LK + c]) = qh[j];
+        }
+        const int i = 4 * tid, row = i / kBC, c = i % kBC;
+        *reinterpret_cast<f32x4*>(&sm.t[row * kLC + c]) = t;
+        if constexpr (GRAD) *reinterpret_cast<f32x4*>(&sm.p[row * kLC + c]) = p;
+        if (tid < NGB) {
+            if (4 * tid < DK) *reinterpret_cast<f32x4*>(&sm.gam[4 * tid]) = gb;
+            else *reinterpret_cast<f32x4*>(&sm.beta[4 * tid - DK]) = gb;
+        }
+        vt.put(sm.vt, LV, nrow);
     }
-    if (tid < DK) sm.gam[tid] = rec[R::GAM + tid];
-    if (tid < kBC) sm.beta[tid] = rec[R::BETA + tid];
-    for (int i = tid; i < kBC * 64; i += kBT) {
-        const int row = i / 64, c = i % 64;
-        sm.vt[row * LV + c] = row < nrow ? ldf(src + ((t0 + row) * H + h) * DV + col0 + c) : 0.f;
-    }
-}
+};
 
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(kBT) void kda_bwd_state_kernel(
@@ -353,16 +413,22 @@ __global__ __launch_bounds__(kBT) void kda_bwd_state_kernel(
         for (int v4 = 0; v4 < 4; ++v4)
             S[ti][v4] = init_state ? init_state[((int64_t(n) * H + h) * DK + 16 * ti + 4 * g + v4) * DV + col] : 0.f;
     }
-    for (int cc = c0; cc < c1; ++cc) {
+    ChainFetch<E, DK, false> f;
+    auto fetch = [&](int cc) __attribute__((always_inline)) {
         const int64_t t0 = s0 + int64_t(cc - c0) * kBC;
-        const int nrow = int(min<int64_t>(kBC, s1 - t0));
+        f.load(rec_ws + (int64_t(h) * max_chunks + cc) * R::TOTAL, v, t0, int(min<int64_t>(kBC, s1 - t0)), H, h,
+               DV, 64 * vt);
+    };
+    if (c0 < c1) fetch(c0);
+    for (int cc = c0; cc < c1; ++cc) {
+        f.put(sm);
+        __syncthreads();
         float* so = s_in + (int64_t(h) * max_chunks + cc) * DK * DV;
 #pragma unroll
         for (int ti = 0; ti < NCT; ++ti)
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) so[(16 * ti + 4 * g + v4) * DV + col] = S[ti][v4];
-        chain_stage<E, DK, false>(sm, rec_ws + (int64_t(h) * max_chunks + cc) * R::TOTAL, v, t0, nrow, H, h, DV, 64 * vt);
-        __syncthreads();
+        fetch(min(cc + 1, c1 - 1));                       // in flight during this chunk's products
         // X = V - Kh S, then Y = diag(b) X (rows 16xi + 4g + v)
         f32x4 Y[2];
 #pragma unroll
@@ -430,16 +496,22 @@ __global__ __launch_bounds__(kBT) void kda_bwd_dstate_kernel(
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4)
             dS[ti][v4] = d_final ? d_final[((int64_t(n) * H + h) * DK + 16 * ti + 4 * g + v4) * DV + col] : 0.f;
-    for (int cc = c1 - 1; cc >= c0; --cc) {
+    ChainFetch<E, DK, true> f;
+    auto fetch = [&](int cc) __attribute__((always_inline)) {
         const int64_t t0 = s0 + int64_t(cc - c0) * kBC;
-        const int nrow = int(min<int64_t>(kBC, s1 - t0));
+        f.load(rec_ws + (int64_t(h) * max_chunks + cc) * R::TOTAL, d_out, t0, int(min<int64_t>(kBC, s1 - t0)),
+               H, h, DV, 64 * vt);
+    };
+    if (c0 < c1) fetch(c1 - 1);
+    for (int cc = c1 - 1; cc >= c0; --cc) {
+        f.put(sm);
+        __syncthreads();
         float* so = ds_out + (int64_t(h) * max_chunks + cc) * DK * DV;
 #pragma unroll
         for (int ti = 0; ti < NCT; ++ti)
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) so[(16 * ti + 4 * g + v4) * DV + col] = dS[ti][v4];
-        chain_stage<E, DK, true>(sm, rec_ws + (int64_t(h) * max_chunks + cc) * R::TOTAL, d_out, t0, nrow, H, h, DV, 64 * vt);
-        __syncthreads();
+        fetch(max(cc - 1, c0));                           // in flight during this chunk's products
         // dVn = P^T dO + Kc diag(gamma) dS
         f32x4 dVn[2];
 #pragma unroll
@@ -507,6 +579,48 @@ template <int DK, int DV> struct GradLds {
     static_assert(5 * kBC * LV + 5 * kBC * kLC >= 3 * kBC * LK, "flat area holds three [C][DK] arrays");
 };
 
+// 32 rows (32 kb ..) of a [DK][DV] fp32 state matrix as float4 pieces in registers:
+// piece j of thread i is row (i + 256 j) / (DV/4), columns 4 ((i + 256 j) % (DV/4)) ..
+template <int DV> struct StateBlock {
+    static constexpr int PR = DV / 4;                // f32x4 per row
+    static constexpr int NP = kBC * PR / kBT;
+    f32x4 v[NP];
+    __device__ __forceinline__ void load(const float* __restrict__ src, int kb) {
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int pc = int(threadIdx.x) + j * kBT;
+            v[j] = *reinterpret_cast<const f32x4*>(src + (32 * kb + pc / PR) * DV + 4 * (pc % PR));
+        }
+    }
+    __device__ __forceinline__ void put(float* dst, int ld) const {
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int pc = int(threadIdx.x) + j * kBT;
+            *reinterpret_cast<f32x4*>(dst + (pc / PR) * ld + 4 * (pc % PR)) = v[j];
+        }
+    }
+};
+
+// rows < nrow of a [C][W] fp32 LDS array (row stride ld) to rows t0.. of a [T][H][W]
+// tensor of dtype E, 16 bytes per store
+template <typename E, int W>
+__device__ __forceinline__ void store_rows(E* __restrict__ dst, const float* src, int ld, int64_t t0, int nrow, int H,
+                                           int h) {
+    constexpr int EPP = 16 / sizeof(E), PPR = W / EPP;
+    for (int pc = threadIdx.x; pc < kBC * PPR; pc += kBT) {
+        const int row = pc / PPR, c = (pc % PPR) * EPP;
+        if (row >= nrow) continue;
+        E* d = dst + ((t0 + row) * H + h) * W + c;
+        const float* s = src + row * ld + c;
+        if constexpr (sizeof(E) == 4) {
+            *reinterpret_cast<float4*>(d) = *reinterpret_cast<const float4*>(s);
+        } else {
+            const float4 a = *reinterpret_cast<const float4*>(s), b = *reinterpret_cast<const float4*>(s + 4);
+            *reinterpret_cast<u32x4*>(d) = u32x4{pack2(a.x, a.y), pack2(a.z, a.w), pack2(b.x, b.y), pack2(b.z, b.w)};
+        }
+    }
+}
+
 // The [C][DK] gradients dQh, dKh, dKc live in registers. Wave w owns the 16x16 tiles
 // (ti, tj) with tj = ((w - 2 ti) & 3) + 4 j', j' < DK/64, at index m = ti DK/64 + j';
 // every block of 32 key channels then holds exactly one tile of each wave.
@@ -524,6 +638,7 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
     constexpr int XPW = NVT / 2;            // [C][DV] tiles per wave
     constexpr int KPW = NCT / 2;            // [C][DK] tiles per wave
     constexpr int J4 = DK / 64;             // j' range of the owned tiles
+    constexpr int NKB = DK / 32;            // 32-row blocks of a state matrix
     extern __shared__ __align__(16) unsigned char smem_raw[];
     S_& sm = *reinterpret_cast<S_*>(smem_raw);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
@@ -538,18 +653,18 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
     const float* Sg = s_in + (int64_t(h) * max_chunks + c) * DK * DV;
     const float* dSg = ds_out + (int64_t(h) * max_chunks + c) * DK * DV;
 
-    // ---- operands, V and dO ----
-    for (int i = tid; i < kBC * DV; i += kBT) {
-        const int row = i / DV, cc = i % DV;
-        const bool ok = row < nrow;
-        const int64_t off = ((t0 + row) * H + h) * DV + cc;
-        sm.x[row * LV + cc] = ok ? ldf(v + off) : 0.f;
-        sm.dout[row * LV + cc] = ok ? ldf(d_out + off) : 0.f;
-    }
+    // ---- operands, V and dO (every load issued before the first wait) ----
+    RowPieces<E, DV> pv, pd;
+    pv.load(v, t0, nrow, H, h, 0, DV);
+    pd.load(d_out, t0, nrow, H, h, 0, DV);
+    StateBlock<DV> sb;
+    sb.load(Sg, 0);
     if (tid < DK) sm.dgam[tid] = 0.f;
     if (tid < kBC) sm.dbeta[tid] = 0.f;
     const ChunkLds L{sm.qh, sm.kh, sm.kc, sm.m, sm.t, sm.p, sm.gam, sm.beta, sm.qinv, sm.kinv};
     chunk_operands<E, DK, NORM>(L, q, k, la, beta, t0, nrow, H, h);   // ends with a barrier
+    pv.put(sm.x, LV, nrow);
+    pd.put(sm.dout, LV, nrow);
 
     // a [C][DV]-shaped result: tile index wave + 4 mm
     auto xtile = [&](int mm, int& ti, int& tj) {
@@ -557,23 +672,23 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
         ti = tt / NVT;
         tj = tt % NVT;
     };
-    // 32 rows of a state matrix (rows 32 kb..) to sblk
-    auto load_block = [&](const float* src, int kb) {
-        for (int i = tid; i < kBC * DV / 4; i += kBT) {
-            const int row = (4 * i) / DV, cc = (4 * i) % DV;
-            *reinterpret_cast<float4*>(&sm.sblk[row * LV + cc]) =
-                *reinterpret_cast<const float4*>(src + (32 * kb + row) * DV + cc);
-        }
+    // this wave's owned [C][DK] tile in the 32-channel block kb
+    auto block_tile = [&](int kb, int& ti, int& tj) {
+        ti = (((wave & 3) >> 1) == (kb & 1)) ? 0 : 1;
+        tj = 4 * (kb >> 1) + ((wave - 2 * ti) & 3);
     };
 
-    // ---- X = V - Kh S ----
+    // ---- X = V - Kh S (S streamed in 32-row blocks, the next one loaded ahead) ----
     {
         f32x4 ax[XPW];
 #pragma unroll
         for (int mm = 0; mm < XPW; ++mm) ax[mm] = zero4();
-        for (int kb = 0; kb < DK / 32; ++kb) {
-            load_block(Sg, kb);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            sb.put(sm.sblk, LV);
             __syncthreads();
+            if (kb + 1 < NKB) sb.load(Sg, kb + 1);
+            else sb.load(dSg, 0);                        // first block of the next pass
 #pragma unroll
             for (int mm = 0; mm < XPW; ++mm) {
                 int ti, tj;
@@ -614,11 +729,6 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
         aKh[mm] = zero4();
         aKc[mm] = zero4();
     }
-    // this wave's tile in the 32-channel block kb: row tile ti, column tile tj
-    auto block_tile = [&](int kb, int& ti, int& tj) {
-        ti = (((wave & 3) >> 1) == (kb & 1)) ? 0 : 1;
-        tj = 4 * (kb >> 1) + ((wave - 2 * ti) & 3);
-    };
 
     // ---- dVn = P^T dO + Kc diag(gamma) dS';  dKbar = Vn dS'^T -> dKc, dgamma ----
     {
@@ -634,9 +744,11 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
             adv[mm] = acc;
         }
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) {
-            load_block(dSg, kb);
+        for (int kb = 0; kb < NKB; ++kb) {
+            sb.put(sm.sblk, LV);
             __syncthreads();
+            if (kb + 1 < NKB) sb.load(dSg, kb + 1);
+            else sb.load(Sg, 0);                         // first block of the last pass
 #pragma unroll
             for (int mm = 0; mm < XPW; ++mm) {
                 int ti, tj;
@@ -763,13 +875,21 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
     }
     __syncthreads();
 
+    // rows of log a (and of q, k) for the last phase, loaded now
+    RowPieces<E, DK> pl, pq, pk;
+    pl.load(la, t0, nrow, H, h, 0, DK);
+    if constexpr (NORM) {
+        pq.load(q, t0, nrow, H, h, 0, DK);
+        pk.load(k, t0, nrow, H, h, 0, DK);
+    }
+
     // ---- chunk-internal parts: dQh += dP Kc, dKh += dM Kc, dKc += dP^T Qh + dM^T Kh ----
 #pragma unroll
     for (int mm = 0; mm < KPW; ++mm) {
         const int ti = mm / J4, tj = ((wave - 2 * ti) & 3) + 4 * (mm % J4);
 #pragma unroll
-        for (int s0_ = 0; s0_ < kBC; s0_ += 4) {
-            const int s = s0_ + g;
+        for (int u0 = 0; u0 < kBC; u0 += 4) {
+            const int s = u0 + g;
             const float kcv = sm.kc[s * LK + 16 * tj + r];
             aQh[mm] = mma4(sm.dp[(16 * ti + r) * kLC + s], kcv, aQh[mm]);
             aKh[mm] = mma4(sm.dt[(16 * ti + r) * kLC + s], kcv, aKh[mm]);
@@ -778,56 +898,61 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
         }
     }
     // ---- state parts: dQh += dO S^T, dKh -= dX S^T;  dgamma += rowsum(dS' S) ----
+    {
+        StateBlock<DV> db;                              // the same rows of dS'
+        db.load(dSg, 0);
 #pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb) {
-        load_block(Sg, kb);
-        __syncthreads();
-        int ti, tj;
-        block_tile(kb, ti, tj);
-        f32x4 aq = zero4(), ak = zero4();
-#pragma unroll 8
-        for (int j0 = 0; j0 < DV; j0 += 4) {
-            const float sv = sm.sblk[(16 * (tj - 2 * kb) + r) * LV + j0 + g];
-            aq = mma4(sm.dout[(16 * ti + r) * LV + j0 + g], sv, aq);
-            ak = mma4(sm.vn[(16 * ti + r) * LV + j0 + g], sv, ak);
-        }
-        if (ti == 0) {
-            aQh[kb >> 1] += aq;
-            aKh[kb >> 1] -= ak;
-        } else {
-            aQh[J4 + (kb >> 1)] += aq;
-            aKh[J4 + (kb >> 1)] -= ak;
-        }
-        {
-            const int row = tid >> 3, part = tid & 7;         // 8 lanes per state row
-            float acc = 0.f;
-            for (int j = part * 4; j < DV; j += 32) {
-                const float4 a = *reinterpret_cast<const float4*>(dSg + (32 * kb + row) * DV + j);
-                const float4 b = *reinterpret_cast<const float4*>(&sm.sblk[row * LV + j]);
-                acc += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+        for (int kb = 0; kb < NKB; ++kb) {
+            sb.put(sm.sblk, LV);
+            // dgamma: this thread's pieces of rows of S and dS' (the same positions)
+#pragma unroll
+            for (int j = 0; j < StateBlock<DV>::NP; ++j) {
+                const f32x4 a = sb.v[j], b = db.v[j];
+                float part = a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+#pragma unroll
+                for (int sh = 1; sh < StateBlock<DV>::PR; sh <<= 1) part += __shfl_xor(part, sh);
+                const int pc = tid + j * kBT;
+                if (pc % StateBlock<DV>::PR == 0) atomicAdd(&sm.dgam[32 * kb + pc / StateBlock<DV>::PR], part);
             }
-#pragma unroll
-            for (int sh = 1; sh < 8; sh <<= 1) acc += __shfl_xor(acc, sh);
-            if (part == 0) atomicAdd(&sm.dgam[32 * kb + row], acc);
+            __syncthreads();
+            if (kb + 1 < NKB) {
+                sb.load(Sg, kb + 1);
+                db.load(dSg, kb + 1);
+            }
+            int ti, tj;
+            block_tile(kb, ti, tj);
+            f32x4 aq = zero4(), ak = zero4();
+#pragma unroll 8
+            for (int j0 = 0; j0 < DV; j0 += 4) {
+                const float sv = sm.sblk[(16 * (tj - 2 * kb) + r) * LV + j0 + g];
+                aq = mma4(sm.dout[(16 * ti + r) * LV + j0 + g], sv, aq);
+                ak = mma4(sm.vn[(16 * ti + r) * LV + j0 + g], sv, ak);
+            }
+            if (ti == 0) {
+                aQh[kb >> 1] += aq;
+                aKh[kb >> 1] -= ak;
+            } else {
+                aQh[J4 + (kb >> 1)] += aq;
+                aKh[J4 + (kb >> 1)] -= ak;
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
     // ---- dv = dX, db ----
-    for (int i = tid; i < kBC * DV; i += kBT) {
-        const int row = i / DV, cc = i % DV;
-        if (row < nrow) stf(dv + ((t0 + row) * H + h) * DV + cc, sm.vn[row * LV + cc]);
-    }
+    store_rows<E, DV>(dv, sm.vn, LV, t0, nrow, H, h);
     if (tid < nrow) stf(dbeta + (t0 + tid) * H + h, sm.dbeta[tid]);
     __syncthreads();
 
     // ---- through the decays: G again (flat area 0), then dQ, dK, dG ----
-    float* F0 = sm.x;                       // G, then dQ
+    float* F0 = sm.x;                       // log a, G, then dQ
     float* F1 = sm.x + kBC * LK;            // dK
     float* F2 = sm.x + 2 * kBC * LK;        // dG, then dlog a
+    pl.put(F0, LK, nrow);
+    __syncthreads();
     if (tid < DK) {
         float G = 0.f;
         for (int row = 0; row < kBC; ++row) {
-            if (row < nrow) G += ldf(la + ((t0 + row) * H + h) * DK + tid);
+            G += F0[row * LK + tid];
             F0[row * LK + tid] = G;
         }
     }
@@ -855,40 +980,41 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
         }
     }
     if constexpr (NORM) {
-        // dx = (dx^ - x^ (x^ . dx^)) / |x| for x^ = x / |x|, x = q, k of the row
-        const int row = tid >> 3, part = tid & 7;
-        float dotq = 0.f, dotk = 0.f;
-        if (row < nrow) {
-            for (int cc = part; cc < DK; cc += 8) {
-                const int64_t off = ((t0 + row) * H + h) * DK + cc;
-                dotq += ldf(q + off) * sm.qinv[row] * F0[row * LK + cc];
-                dotk += ldf(k + off) * sm.kinv[row] * F1[row * LK + cc];
-            }
-        }
+        // dx = (dx^ - x^ (x^ . dx^)) / |x| for x^ = x / |x|, x = q, k of the row; the row's
+        // pieces sit in consecutive threads
+        using RP = RowPieces<E, DK>;
 #pragma unroll
-        for (int sh = 1; sh < 8; sh <<= 1) {
-            dotq += __shfl_xor(dotq, sh);
-            dotk += __shfl_xor(dotk, sh);
-        }
-        if (row < nrow) {
-            for (int cc = part; cc < DK; cc += 8) {
-                const int64_t off = ((t0 + row) * H + h) * DK + cc;
-                const float qn = ldf(q + off) * sm.qinv[row], kn = ldf(k + off) * sm.kinv[row];
-                F0[row * LK + cc] = (F0[row * LK + cc] - qn * dotq) * sm.qinv[row];
-                F1[row * LK + cc] = (F1[row * LK + cc] - kn * dotk) * sm.kinv[row];
+        for (int j = 0; j < RP::NP; ++j) {
+            const int pc = tid + j * kBT, row = min(pc / RP::PPR, kBC - 1), c0 = (pc % RP::PPR) * RP::EPP;
+            float xq[RP::EPP], xk[RP::EPP];
+            put16<E>(xq, pq.v[j], true);
+            put16<E>(xk, pk.v[j], true);
+            float dotq = 0.f, dotk = 0.f;
+#pragma unroll
+            for (int e = 0; e < RP::EPP; ++e) {
+                xq[e] *= sm.qinv[row];
+                xk[e] *= sm.kinv[row];
+                dotq += xq[e] * F0[row * LK + c0 + e];
+                dotk += xk[e] * F1[row * LK + c0 + e];
+            }
+#pragma unroll
+            for (int sh = 1; sh < RP::PPR; sh <<= 1) {
+                dotq += __shfl_xor(dotq, sh);
+                dotk += __shfl_xor(dotk, sh);
+            }
+            if (pc < kBC * RP::PPR) {
+#pragma unroll
+                for (int e = 0; e < RP::EPP; ++e) {
+                    F0[row * LK + c0 + e] = (F0[row * LK + c0 + e] - xq[e] * dotq) * sm.qinv[row];
+                    F1[row * LK + c0 + e] = (F1[row * LK + c0 + e] - xk[e] * dotk) * sm.kinv[row];
+                }
             }
         }
     }
     __syncthreads();
-    for (int i = tid; i < kBC * DK; i += kBT) {
-        const int row = i / DK, cc = i % DK;
-        if (row < nrow) {
-            const int64_t off = ((t0 + row) * H + h) * DK + cc;
-            stf(dq + off, F0[row * LK + cc]);
-            stf(dk + off, F1[row * LK + cc]);
-            stf(dla + off, F2[row * LK + cc]);
-        }
-    }
+    store_rows<E, DK>(dq, F0, LK, t0, nrow, H, h);
+    store_rows<E, DK>(dk, F1, LK, t0, nrow, H, h);
+    store_rows<E, DK>(dla, F2, LK, t0, nrow, H, h);
 }
 
 // ---------------------------------------------------------------------------
