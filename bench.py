@@ -106,6 +106,47 @@ def kernel_bytes(spec, kernel: str) -> int:
     return algorithmic_bytes(spec)
 
 
+BWD_C = 32
+BWD_KERNELS = {"bwd_plan": "kda_bwd_plan_kernel", "bwd_prep": "kda_bwd_prep_kernel",
+               "bwd_state": "kda_bwd_state_kernel", "bwd_dstate": "kda_bwd_dstate_kernel",
+               "bwd_grad": "kda_bwd_grad_kernel"}
+
+
+def bwd_chunk_heads(spec) -> int:
+    return sum((n + BWD_C - 1) // BWD_C for n in spec.seq_lens) * spec.heads
+
+
+def bwd_kernel_macs(spec, kernel: str) -> int:
+    """Multiply-adds of the matrix products of one launch (32-token chunks, fp32 MFMA)."""
+    C, dk, dv = BWD_C, spec.dk, spec.dv
+    per = {
+        # M, P; X, dVn state term, dKbar, dQh and dKh state terms; Vn, dVn P term, dP, Z,
+        # dT and the four chunk-internal products; dA
+        "bwd_grad": 2 * C * C * dk + 5 * C * dk * dv + 5 * C * C * dv + 4 * C * C * dk + 2 * C ** 3,
+        "bwd_prep": 2 * C * C * dk,
+        "bwd_state": 2 * C * dk * dv + C * C * dv,
+        "bwd_dstate": 3 * C * dk * dv + 2 * C * C * dv,
+    }.get(kernel, 0)
+    return per * bwd_chunk_heads(spec)
+
+
+def bwd_kernel_bytes(spec, kernel: str) -> int:
+    """Algorithmic bytes of one launch of each backward kernel."""
+    es = 4 if spec.dtype == "f32" else 2
+    C, dk, dv, H, T = BWD_C, spec.dk, spec.dv, spec.heads, spec.total_tokens
+    ch = bwd_chunk_heads(spec)
+    state = ch * dk * dv * 4
+    if kernel == "bwd_grad":    # q, k, log a, v, dO, beta; S and dS per chunk; five gradients
+        return T * H * (3 * dk + 2 * dv + 1) * es + 2 * state + T * H * (2 * dk + dk + dv + 1) * es
+    if kernel == "bwd_prep":    # q, k, log a, beta; Kh, Kc, Qh, T, P, gamma, beta records
+        return T * H * (3 * dk + 1) * es + ch * (3 * C * dk + 2 * C * C + dk + C) * 4
+    if kernel == "bwd_state":   # Kh, Kc, T, gamma, beta records and V; S per chunk
+        return ch * (2 * C * dk + C * C + dk + C) * 4 + T * H * dv * es + state
+    if kernel == "bwd_dstate":  # Kh, Kc, Qh, T, P, gamma, beta records and dO; dS per chunk
+        return ch * (3 * C * dk + 2 * C * C + dk + C) * 4 + T * H * dv * es + state
+    return 4 * (len(spec.seq_lens) + 1)
+
+
 def chunk_flops(spec) -> int:
     """Dense chunk contractions per launch: 10*C*d + 6*d^2 per head-token (d = d_k = d_v)."""
     d = spec.dk
@@ -138,6 +179,51 @@ def cpu_baseline(spec, a):
                       f"{spec.head_tokens} head-tokens, fp64 token recurrence, {dt:.2f} s wall"}
 
 
+def backward_bench(args, spec, t, cu, dev):
+    """The gradient step (kda_backward) on the same workload: K timed steps after W warm-ups."""
+    import torch
+    from delta_rule_recurrent_kda_amd import kda
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    d_out = torch.randn(t["v"].shape, device=dev, generator=g).to(t["v"].dtype)
+
+    def step():
+        kda.backward(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], cu, d_out, with_initial_grad=False)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    for name in BWD_KERNELS:
+        kda.timing_read(name)
+    kda.timing_enable(True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    kda.timing_enable(False)
+    kernels = {}
+    for name in BWD_KERNELS:
+        n, ms = kda.timing_read(name)
+        if n:
+            macs, b = bwd_kernel_macs(spec, name), bwd_kernel_bytes(spec, name)
+            sec = ms / n * 1e-3
+            kernels[name] = {"launches": n, "ms_avg": ms / n, "flops": 2 * macs,
+                             "achieved_TFLOPs": 2 * macs / sec / 1e12, "algorithmic_bytes": b,
+                             "achieved_GBs": b / sec / 1e9}
+    dom = max(kernels, key=lambda k: kernels[k]["ms_avg"])
+    kd = kernels[dom]
+    ms_step = wall * 1e3 / args.steps
+    return {"metric": "KDA backward head-tokens/s (gradients of q, k, v, log a, beta)",
+            "value": spec.head_tokens / (ms_step * 1e-3), "unit": "tokens/s", "ms_per_step": ms_step,
+            "dtype": "f32 arithmetic on " + spec.dtype + " data",
+            "roofline": {"bound": "mfma", "achieved": kd["achieved_TFLOPs"], "peak": MFMA_F32_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": kd["achieved_TFLOPs"] / MFMA_F32_PEAK_TFLOPS,
+                         "traffic": None, "kernel": BWD_KERNELS[dom], "kernel_ms_avg": kd["ms_avg"]},
+            "kernels": kernels}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,6 +231,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="packed8", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after timing, run 3 plain device copies of this many MiB (for scaling "
                          "HBM byte counters)")
@@ -236,6 +323,8 @@ def main():
         "mfma": {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s", "frac": tflops / mfma_peak,
                  "flops_per_launch": flops},
     }
+    if not args.no_backward:
+        rec["backward"] = backward_bench(args, spec, t, cu, dev)
     if args.copy_calib_mib:
         n = args.copy_calib_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

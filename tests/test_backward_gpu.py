@@ -101,6 +101,35 @@ def test_backward_vs_oracle(case):
     _compare(spec, got, ref, f"backward {name}")
 
 
+def _sampled(spec, heads, seed):
+    """The full-size workload on the GPU (all heads), the oracle on the listed heads."""
+    a = inputs.generate(spec)
+    do, _, _ = _draw_grads(spec, seed)
+    got = _run(spec, a, do, None, None, False)
+    sl = {x: a[x][:, heads] for x in ("q", "k", "v", "log_alpha", "beta")}
+    sl["cu_seqlens"] = a["cu_seqlens"]
+    sub = inputs.KdaSpec(spec.name, spec.seq_lens, len(heads), spec.dk, spec.dv, spec.dtype,
+                         spec.log_alpha_range, spec.seed)
+    ref = _oracle(sub, sl, do[:, heads], None, None, False)
+    got = [x[:, heads] for x in got]
+    _compare(sub, got, ref, f"backward {spec.name} heads {heads}")
+
+
+def test_backward_config1_sampled_heads():
+    gu.log("case backward config 1 (packed 8 samples, 17,108 tokens), heads 0 and 11")
+    _sampled(inputs.config(1), [0, 11], 74)
+
+
+def test_backward_config2_sampled_head():
+    gu.log("case backward config 2 (4 x 4,352 tokens), head 5")
+    _sampled(inputs.config(2), [5], 75)
+
+
+def test_backward_config3_sampled_head():
+    gu.log("case backward config 3 (33,272 tokens, one sample), head 3")
+    _sampled(inputs.config(3), [3], 76)
+
+
 def test_backward_timing_records_each_kernel():
     import torch
     from delta_rule_recurrent_kda_amd import kda
