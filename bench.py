@@ -30,15 +30,19 @@ MFMA_F32_PEAK_TFLOPS = 157.3
 KERNEL_SOURCES = ["delta_rule_recurrent_kda_amd/csrc/kda_wy.hip",
                   "delta_rule_recurrent_kda_amd/csrc/kda_device.h",
                   "delta_rule_recurrent_kda_amd/csrc/kda_internal.h"]
+BWD_SOURCES = ["delta_rule_recurrent_kda_amd/csrc/kda_bwd.hip",
+               "delta_rule_recurrent_kda_amd/csrc/kda_device.h",
+               "delta_rule_recurrent_kda_amd/csrc/kda_internal.h"]
 WORKLOADS = {"tiny": 0, "packed8": 1, "image4": 2, "clip5s": 3, "clip30s": 4}
 CHUNK = 64
 KERNEL_SYMBOL = {"prep": "kda_wy_prep_kernel", "chain": "kda_wy_chain_kernel", "plan": "kda_wy_plan_kernel",
                  "segments": "kda_wy_chain_kernel", "scan": "kda_fwd"}
 
 
-def kernel_sha() -> str:
+def kernel_sha(sources=None) -> str:
+    """Hash of the sources a kernel is built from (the forward ones by default)."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in (KERNEL_SOURCES if sources is None else sources):
         h.update(open(os.path.join(ROOT, p), "rb").read())
     return h.hexdigest()[:16]
 
@@ -153,13 +157,13 @@ def chunk_flops(spec) -> int:
     return spec.head_tokens * (10 * CHUNK * d + 6 * d * d)
 
 
-def traffic_for(workload: str, kernel: str):
+def traffic_for(workload: str, kernel: str, sha: str = None):
     """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel is unchanged."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_sha") != kernel_sha():
+    if rec.get("kernel_sha") != (kernel_sha() if sha is None else sha):
         return None
     return rec.get("bytes_per_launch")
 
@@ -220,7 +224,10 @@ def backward_bench(args, spec, t, cu, dev):
             "dtype": "f32 arithmetic on " + spec.dtype + " data",
             "roofline": {"bound": "mfma", "achieved": kd["achieved_TFLOPs"], "peak": MFMA_F32_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": kd["achieved_TFLOPs"] / MFMA_F32_PEAK_TFLOPS,
-                         "traffic": None, "kernel": BWD_KERNELS[dom], "kernel_ms_avg": kd["ms_avg"]},
+                         "traffic": traffic_for(args.workload, BWD_KERNELS[dom], kernel_sha(BWD_SOURCES)),
+                         "kernel": BWD_KERNELS[dom], "kernel_ms_avg": kd["ms_avg"],
+                         "flops": kd["flops"], "algorithmic_bytes": kd["algorithmic_bytes"],
+                         "kernel_sha": kernel_sha(BWD_SOURCES)},
             "kernels": kernels}
 
 
