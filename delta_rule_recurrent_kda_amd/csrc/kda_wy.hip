@@ -612,10 +612,13 @@ __global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
         const int idx = min(ltid + j * LT, NP - 1);
         src[j] = idx + (idx >= SH16 ? vt * U16 : 0);
     }
-    // 64-piece blocks a pass never reads are skipped: the first pass of the sequence
-    // split writes no output (no Qh, no P), and its transition tiles take U as zero
+    // 64-piece blocks a pass never reads are skipped: P fragments (rt, kb) = (0, 1) and
+    // (1, 1) lie above the diagonal (never written, never read); the first pass of the
+    // sequence split writes no output (no Qh, no P), and its transition tiles take U as zero
+    static_assert(Lay::P % 512 == 0, "P fragments start on a 64-piece block");
     auto needed = [&](int b0) {
-        if constexpr (MODE != 1) return true;
+        const bool p_upper = b0 == Lay::P / 8 + 64 || b0 == Lay::P / 8 + 3 * 64;
+        if constexpr (MODE != 1) return !p_upper;
         const bool in_q = b0 >= Lay::Q / 8 && b0 + 64 <= Lay::K / 8;
         const bool in_p = b0 >= Lay::P / 8 && b0 + 64 <= Lay::G / 8;
         const bool in_u = b0 >= SH16;
