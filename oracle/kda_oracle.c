@@ -44,9 +44,9 @@
  * (token, head) are first divided by their Euclidean length (a zero vector stays
  * zero) and the recurrence then runs on the unit vectors. The paper's training
  * setup names chunked KDA kernels with fused normalization; its form is not
- * printed, and this is the per-token L2 normalisation of queries and keys that the
- * unit-key statements of the explainer page (erase-then-write of one direction)
- * take for granted.
+ * printed. The form taken is the per-token L2 normalisation of queries and keys:
+ * with a unit key, I - beta k k^T scales the state's component along k by 1 - beta,
+ * so that beta acts as the erase fraction the paper's KDA paragraph describes.
  *
  * kda_oracle_backward is the reverse-mode derivative of the same recurrence (the
  * paper trains with these kernels: training setup paragraph on the custom kernels).
