@@ -183,6 +183,24 @@ def cpu_baseline(spec, a):
                       f"{spec.head_tokens} head-tokens, fp64 token recurrence, {dt:.2f} s wall"}
 
 
+def flushed_steps(step, stream, dev, n: int) -> float:
+    """Median duration (ms) of single steps, each after a 512 MiB write that evicts the caches."""
+    import torch
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    times = []
+    for _ in range(n):
+        scratch.fill_(1)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del scratch
+    return float(np.median(times))
+
+
 def backward_bench(args, spec, t, cu, dev):
     """The gradient step (kda_backward) on the same workload: K timed steps after W warm-ups."""
     import torch
@@ -285,6 +303,7 @@ def main():
     wall = time.perf_counter() - w0
     kda.timing_enable(False)
     ms_per_step = wall * 1e3 / args.steps
+    flushed = flushed_steps(step, stream, dev, 10)
     kernels = {}
     for name in KERNEL_SYMBOL:
         n, ms = kda.timing_read(name)
@@ -327,6 +346,9 @@ def main():
                      "kernel_sha": kernel_sha()},
         "kernels": kernels,
         "path": {"algorithmic_bytes": bytes_, "achieved_GBs": path_gbs, "frac_hbm": path_gbs / HBM_PEAK_GBS},
+        "flushed": {"ms_per_step_median": flushed, "value": spec.head_tokens / (flushed * 1e-3),
+                    "note": "one step at a time after writing 512 MiB (evicts L2 and the 256 MB Infinity "
+                            "Cache); HIP events on the launch stream around the step only"},
         "mfma": {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s", "frac": tflops / mfma_peak,
                  "flops_per_launch": flops},
     }

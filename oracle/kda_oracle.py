@@ -15,7 +15,10 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kda_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle_kda.so")
+_CONV_SRC = os.path.join(_HERE, "short_conv_oracle.c")
+_CONV_LIB = os.path.join(_HERE, "liboracle_short_conv.so")
 _handle = None
+_conv_handle = None
 
 
 def library_path() -> str:
@@ -23,12 +26,13 @@ def library_path() -> str:
 
 
 def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (plain -O2, fp64, pthreads)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + f".tmp{os.getpid()}"
-        subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", tmp, _SRC,
-                        "-lm", "-lpthread"], check=True)
-        os.replace(tmp, _LIB)
+    """Compile the oracles with gcc (plain -O2, fp64, pthreads)."""
+    for src, lib in ((_SRC, _LIB), (_CONV_SRC, _CONV_LIB)):
+        if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(src):
+            tmp = lib + f".tmp{os.getpid()}"
+            subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", tmp, src,
+                            "-lm", "-lpthread"], check=True)
+            os.replace(tmp, lib)
     return _LIB
 
 
@@ -175,3 +179,56 @@ def backward_from(path: str):
     def bwd(*args, **kw):
         return backward(*args, _library=lib, **kw)
     return bwd
+
+
+def _load_conv(path: str):
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    lib.kda_oracle_short_conv.argtypes = [dp, dp, dp, ip, ip, ip] + [ctypes.c_int32] * 6 + [dp]
+    lib.kda_oracle_short_conv.restype = ctypes.c_int
+    return lib
+
+
+def short_conv(x, w_text, w_vis, cu_seqlens, text_len, grid, _library=None):
+    """Direct fp64 modality-aware short convolution.
+
+    x: [T, C]; w_text: [kx, C]; w_vis: [kt, kh, kw, C]; cu_seqlens: [N+1]; text_len: [N];
+    grid: [N, 3] (frames, height, width) with text_len + frames*height*width = each sample's
+    length. Returns y [T, C] in fp64.
+    """
+    global _conv_handle
+    x = np.ascontiguousarray(x, np.float64)
+    wt = np.ascontiguousarray(w_text, np.float64)
+    wv = np.ascontiguousarray(w_vis, np.float64)
+    cu = np.ascontiguousarray(cu_seqlens, np.int32)
+    tl = np.ascontiguousarray(text_len, np.int32)
+    gr = np.ascontiguousarray(grid, np.int32).reshape(-1, 3)
+    T, C = x.shape
+    N = len(cu) - 1
+    assert wt.shape[1] == C and wv.shape[3] == C and tl.shape == (N,) and gr.shape == (N, 3)
+    y = np.zeros((T, C))
+    if _library is None:
+        if _conv_handle is None:
+            build()
+            _conv_handle = _load_conv(_CONV_LIB)
+        lib = _conv_handle
+    else:
+        lib = _library
+    P = ctypes.c_double
+    I = ctypes.c_int32
+    rc = lib.kda_oracle_short_conv(_ptr(x, P), _ptr(wt, P), _ptr(wv, P), _ptr(cu, I), _ptr(tl, I),
+                                   _ptr(gr, I), N, C, wt.shape[0], wv.shape[0], wv.shape[1],
+                                   wv.shape[2], _ptr(y, P))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_short_conv failed (bad arguments)")
+    return y
+
+
+def short_conv_from(path: str):
+    """short_conv() bound to another build of the same C source (mutation tests)."""
+    lib = _load_conv(path)
+
+    def conv(*args, **kw):
+        return short_conv(*args, _library=lib, **kw)
+    return conv
