@@ -11,6 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
 SOURCES = [os.path.join(CSRC, "kda_fwd.hip"), os.path.join(CSRC, "kda_fwd_pipe.hip"),
            os.path.join(CSRC, "kda_wy.hip"), os.path.join(CSRC, "kda_bwd.hip"),
+           os.path.join(CSRC, "kda_conv.hip"),
            os.path.join(CSRC, "kda_api.cpp")]
 HEADERS = [os.path.join(CSRC, "kda_internal.h"), os.path.join(CSRC, "kda_device.h"),
            os.path.join(ROOT, "include", "kda.h")]

@@ -206,7 +206,7 @@ kda_status kda_backward(const void* q, const void* k, const void* v, const void*
                            "d_initial_state"};
     for (int i = 0; i < 8; ++i)
         if (ptrs[i] && !aligned16(ptrs[i])) return fail(KDA_E_ALIGN, "%s is not 16-byte aligned", names[i]);
-    const void* ins[] = {q, k, v, log_alpha, beta, d_out, initial_state, d_final_state};
+    const void* ins[] = {q, k, v, log_alpha, beta, cu_seqlens, d_out, initial_state, d_final_state};
     const void* outs[] = {dq, dk, dv, dlog_alpha, dbeta, d_initial_state};
     for (const void* o : outs)
         for (const void* i : ins)
@@ -243,6 +243,57 @@ size_t kda_backward_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int3
     if (total_tokens < 0 || num_seqs <= 0 || num_heads < 1) return 0;
     if ((d_k != 64 && d_k != 128) || (d_v != 64 && d_v != 128)) return 0;
     return kda::bwd_workspace_bytes(total_tokens, num_seqs, num_heads, d_k, d_v);
+}
+
+kda_status kda_short_conv(const void* x, const float* w_text, const float* w_vis, const int32_t* cu_seqlens,
+                          const int32_t* text_len, const int32_t* grid, void* y, int64_t total_tokens,
+                          int32_t num_seqs, int32_t channels, int32_t k_text, int32_t k_t, int32_t k_h, int32_t k_w,
+                          kda_dtype dtype, hipStream_t stream)
+{
+    g_last_error.clear();
+    if (dtype != KDA_F32 && dtype != KDA_BF16)
+        return fail(KDA_E_DTYPE, "dtype %d is neither KDA_F32 nor KDA_BF16", int(dtype));
+    if (total_tokens < 0 || num_seqs < 0 || channels < 1)
+        return fail(KDA_E_SHAPE, "bad sizes: total_tokens=%lld num_seqs=%d channels=%d", (long long)total_tokens,
+                    num_seqs, channels);
+    if (channels % 8 != 0)
+        return fail(KDA_E_UNSUPPORTED, "channels=%d: a multiple of 8 is required", channels);
+    if (k_text < 1 || k_text > 8 || k_t < 1 || k_t > 4 || k_h < 1 || k_h > 5 || k_w < 1 || k_w > 5 ||
+        k_h % 2 == 0 || k_w % 2 == 0)
+        return fail(KDA_E_UNSUPPORTED, "kernel sizes text %d, visual %dx%dx%d: supported text 1..8, time 1..4, "
+                    "height and width odd 1..5", k_text, k_t, k_h, k_w);
+    if (total_tokens * channels >= (int64_t(1) << 31))
+        return fail(KDA_E_UNSUPPORTED, "problem too large for 32-bit element offsets");
+    if (!cu_seqlens || !text_len || !grid) return fail(KDA_E_NULL, "cu_seqlens, text_len or grid is NULL");
+    if (total_tokens > 0 && (!x || !y || !w_text || !w_vis)) return fail(KDA_E_NULL, "a tensor pointer is NULL");
+    if ((x && !aligned16(x)) || (y && !aligned16(y))) return fail(KDA_E_ALIGN, "x or y is not 16-byte aligned");
+    if (x && x == y) return fail(KDA_E_SHAPE, "y aliases x");
+    if (num_seqs == 0 || total_tokens == 0) return KDA_OK;
+    if (validate_env()) {
+        std::vector<int32_t> hc(size_t(num_seqs) + 1), ht(num_seqs), hg(size_t(num_seqs) * 3);
+        hipError_t e = hipMemcpyAsync(hc.data(), cu_seqlens, hc.size() * 4, hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess) e = hipMemcpyAsync(ht.data(), text_len, ht.size() * 4, hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess) e = hipMemcpyAsync(hg.data(), grid, hg.size() * 4, hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return fail(KDA_E_HIP, "reading the sample tables: %s", hipGetErrorString(e));
+        if (hc[0] != 0 || hc[num_seqs] != total_tokens) return fail(KDA_E_SEQLENS, "cu_seqlens does not span the tokens");
+        for (int32_t n = 0; n < num_seqs; ++n) {
+            const int64_t len = int64_t(hc[n + 1]) - hc[n];
+            const int64_t vis = int64_t(hg[3 * n]) * hg[3 * n + 1] * hg[3 * n + 2];
+            if (len < 0 || ht[n] < 0 || hg[3 * n] < 0 || hg[3 * n + 1] < 0 || hg[3 * n + 2] < 0 || ht[n] + vis != len)
+                return fail(KDA_E_SEQLENS, "sample %d: text_len + T*H*W != its length", n);
+        }
+    }
+    std::unique_lock<std::mutex> lk(g_timing.mu);
+    kda::TimingHook* th = g_timing.on ? &g_timing : nullptr;
+    if (!th) lk.unlock();
+    const kda::ConvArgs a{x, w_text, w_vis, cu_seqlens, text_len, grid, y, total_tokens, num_seqs, channels,
+                          k_text, k_t, k_h, k_w, dtype == KDA_BF16 ? 1 : 0, stream};
+    if (th) th->begin("conv", stream);
+    hipError_t e = kda::launch_short_conv(a);
+    if (th) th->end(stream);
+    if (e != hipSuccess) return fail(KDA_E_HIP, "launch failed: %s", hipGetErrorString(e));
+    return KDA_OK;
 }
 
 kda_status kda_timing_enable(int32_t on)

@@ -67,6 +67,18 @@ struct BwdArgs {
 hipError_t launch_backward(const BwdArgs& a, void* workspace, TimingHook* th);
 size_t bwd_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads, int d_k, int d_v);
 
+// Modality-aware short convolution over packed samples (no workspace).
+struct ConvArgs {
+    const void* x;
+    const float *w_text, *w_vis;    // [k_text][C], [k_t][k_h][k_w][C]
+    const int32_t *cu_seqlens, *text_len, *grid;   // [N+1], [N], [N][3]
+    void* y;
+    int64_t total_tokens;
+    int32_t num_seqs, channels, k_text, k_t, k_h, k_w, dtype_bf16;
+    hipStream_t stream;
+};
+hipError_t launch_short_conv(const ConvArgs& a);
+
 // LDS bytes one workgroup uses.
 size_t smem_bytes(int dtype_bf16, int d_k);
 size_t smem_bytes_pipe(int d_k);

@@ -62,6 +62,8 @@ def library() -> ctypes.CDLL:
         lib.kda_backward_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                                      ctypes.c_int32, ctypes.c_int32]
         lib.kda_backward_workspace_bytes.restype = ctypes.c_size_t
+        lib.kda_short_conv.argtypes = [vp] * 7 + [ctypes.c_int64] + [ctypes.c_int32] * 6 + [ctypes.c_int, vp]
+        lib.kda_short_conv.restype = ctypes.c_int
         lib.kda_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int]
         lib.kda_workspace_bytes.restype = ctypes.c_size_t
@@ -250,3 +252,49 @@ def backward(q, k, v, log_alpha, beta, cu_seqlens, d_out, d_final_state=None, in
     if st != 0:
         raise KdaError(st, library().kda_last_error().decode())
     return (*g, dinit)
+
+
+def short_conv_raw(x, w_text, w_vis, cu_seqlens, text_len, grid, y, total_tokens: int, num_seqs: int,
+                   channels: int, k_text: int, k_t: int, k_h: int, k_w: int, dtype: int,
+                   stream: Optional[int]) -> int:
+    """Direct C call of kda_short_conv; returns the status code."""
+    return library().kda_short_conv(x, w_text, w_vis, cu_seqlens, text_len, grid, y, int(total_tokens),
+                                    int(num_seqs), int(channels), int(k_text), int(k_t), int(k_h),
+                                    int(k_w), int(dtype), stream)
+
+
+def short_conv(x, w_text, w_vis, cu_seqlens, text_len, grid, y=None,
+               stream: Optional[torch.cuda.Stream] = None):
+    """The modality-aware short convolution: x [T, C] (float32 or bfloat16); w_text [k, C] and
+    w_vis [kt, kh, kw, C] float32; cu_seqlens [N+1], text_len [N], grid [N, 3] int32. Returns y."""
+    if x.dim() != 2 or w_text.dim() != 2 or w_vis.dim() != 4:
+        raise ValueError("x must be [T, C], w_text [k, C], w_vis [kt, kh, kw, C]")
+    T, C = x.shape
+    if w_text.shape[1] != C or w_vis.shape[3] != C:
+        raise ValueError("weights must have the channels of x last")
+    for name, t, dt in (("w_text", w_text, torch.float32), ("w_vis", w_vis, torch.float32),
+                        ("cu_seqlens", cu_seqlens, torch.int32), ("text_len", text_len, torch.int32),
+                        ("grid", grid, torch.int32)):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} GPU tensor")
+    N = cu_seqlens.numel() - 1
+    if text_len.numel() != N or grid.numel() != 3 * N:
+        raise ValueError("text_len must be [N] and grid [N, 3]")
+    if x.dtype == torch.bfloat16:
+        dt = KDA_BF16
+    elif x.dtype == torch.float32:
+        dt = KDA_F32
+    else:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous GPU tensor")
+    if y is None:
+        y = torch.empty_like(x)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    st = short_conv_raw(_ptr(x), _ptr(w_text), _ptr(w_vis), _ptr(cu_seqlens), _ptr(text_len), _ptr(grid),
+                        _ptr(y), T, N, C, w_text.shape[0], w_vis.shape[0], w_vis.shape[1], w_vis.shape[2],
+                        dt, stream.cuda_stream)
+    if st != 0:
+        raise KdaError(st, library().kda_last_error().decode())
+    return y

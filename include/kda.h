@@ -190,6 +190,40 @@ size_t kda_backward_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int3
                                     int32_t d_k, int32_t d_v);
 
 /*
+ * kda_short_conv -- the modality-aware depthwise short convolution over packed samples.
+ *
+ * The layer's short convolution that supplies local structure next to the scan (paper
+ * Sec. 3.4 and the NoPE discussion of position selection; explainer page "What RoPE was
+ * actually doing"): a depthwise kernel per channel that mixes tokens at fixed index
+ * offsets, text tokens along the token index (causal), visual tokens over their (T, H, W)
+ * latent grid (causal in time), in one pass over the packed tokens. Sample n owns tokens
+ * [cu_seqlens[n], cu_seqlens[n+1]): its first text_len[n] tokens are text, the rest its
+ * grid (grid[3n], grid[3n+1], grid[3n+2]) = (T, H, W) in temporal-major raster order,
+ * position (i, j, k) at index i*H*W + j*W + k after the text. For channel c:
+ *   text    y[t][c] = sum_{i < k_text} w_text[i][c] x[t - i][c]                  (t - i >= 0)
+ *   visual  y[i,j,k][c] = sum_{a < k_t, b < k_h, d < k_w} w_vis[a][b][d][c]
+ *                         x[i - a, j + b - (k_h-1)/2, k + d - (k_w-1)/2][c]
+ * with zeros outside the sample's text or grid: text and visual tokens never read each
+ * other, and no sample reads another. The pages fix neither the kernel sizes nor a bias or
+ * activation; there is none, and the sizes are arguments.
+ *
+ *   x, y        : [total_tokens][channels] dtype, DEVICE, 16-byte aligned; y may not alias x
+ *   w_text      : [k_text][channels] fp32;  w_vis : [k_t][k_h][k_w][channels] fp32 (DEVICE)
+ *   cu_seqlens  : [num_seqs + 1] int32; text_len : [num_seqs] int32; grid : [num_seqs][3] int32
+ *                 (DEVICE); text_len[n] + T*H*W must equal the sample's length (checked on the
+ *                 host only with KDA_VALIDATE=1; otherwise the kernel reads only inside the
+ *                 sample and writes zeros for grid positions that do not fit)
+ *   channels    : a multiple of 8; k_text 1..8, k_t 1..4, k_h and k_w odd in 1..5
+ * Arithmetic is fp32; y is rounded to nearest-even for bf16. No workspace. Execution and
+ * errors as kda_forward; the timing hook names the kernel "conv".
+ */
+kda_status kda_short_conv(const void *x, const float *w_text, const float *w_vis,
+                          const int32_t *cu_seqlens, const int32_t *text_len, const int32_t *grid,
+                          void *y, int64_t total_tokens, int32_t num_seqs, int32_t channels,
+                          int32_t k_text, int32_t k_t, int32_t k_h, int32_t k_w, kda_dtype dtype,
+                          hipStream_t stream);
+
+/*
  * kda_workspace_bytes -- bytes of device workspace the default bf16 scan takes for
  * these sizes (0 when it takes none: fp32 data, no samples, unsupported sizes).
  * Layout: per (64-token chunk, head) record of the chunk's decayed operands and

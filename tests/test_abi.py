@@ -27,7 +27,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert {"kda_forward", "kda_forward_from_state", "kda_forward_ex", "kda_workspace_bytes", "kda_timing_enable",
+    assert {"kda_forward", "kda_forward_from_state", "kda_forward_ex", "kda_backward", "kda_backward_workspace_bytes",
+            "kda_short_conv", "kda_workspace_bytes", "kda_timing_enable",
             "kda_timing_read", "kda_status_str", "kda_last_error", "kda_version"} <= set(declared_functions())
 
 
@@ -153,6 +154,76 @@ def test_qk_norm_on_single_kernel_variant_is_unsupported(lib, monkeypatch):
     monkeypatch.setenv("KDA_SCAN_VARIANT", "pipe")
     st, msg = _call_ex({})
     assert st == 5 and "QK_L2NORM" in msg
+
+
+def _call_conv(kw):
+    from delta_rule_recurrent_kda_amd import kda
+    a = dict(x=0x1000, w_text=0x2000, w_vis=0x3000, cu_seqlens=0x4000, text_len=0x5000, grid=0x6000,
+             y=0x7000, total_tokens=100, num_seqs=1, channels=64, k_text=4, k_t=3, k_h=3, k_w=3,
+             dtype=kda.KDA_BF16, stream=None)
+    a.update(kw)
+    st = kda.short_conv_raw(**a)
+    return st, kda.library().kda_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), 2),
+    (dict(channels=60), 5),
+    (dict(k_text=9), 5),
+    (dict(k_t=5), 5),
+    (dict(k_h=2), 5),
+    (dict(k_w=7), 5),
+    (dict(total_tokens=-1), 3),
+    (dict(grid=None), 1),
+    (dict(x=None), 1),
+    (dict(y=0x7008), 4),
+    (dict(y=0x1000), 3),
+    (dict(total_tokens=1 << 25), 5),
+])
+def test_short_conv_bad_arguments_are_rejected_without_launch(lib, kw, code):
+    st, msg = _call_conv(kw)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def _call_bwd(kw):
+    from delta_rule_recurrent_kda_amd import kda
+    a = dict(q=0x1000, k=0x2000, v=0x3000, log_alpha=0x4000, beta=0x5000, cu_seqlens=0x6000,
+             initial_state=None, d_out=0x7000, d_final_state=None, dq=0x8000, dk=0x9000, dv=0xA000,
+             dlog_alpha=0xB000, dbeta=0xC000, d_initial_state=None, total_tokens=128, num_seqs=1,
+             num_heads=2, d_k=128, d_v=128, dtype=kda.KDA_BF16, options=0, stream=None)
+    a.update(kw)
+    st = kda.kda_backward_raw(**a)
+    return st, kda.library().kda_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(options=4), 5),
+    (dict(dtype=9), 2),
+    (dict(d_k=32), 5),
+    (dict(d_out=None), 1),
+    (dict(dbeta=None), 1),
+    (dict(dv=0xA008), 4),
+    (dict(dq=0x1000), 3),                            # a gradient aliases an input
+    (dict(dk=0x8000), 3),                            # two gradients alias
+    (dict(d_initial_state=0x6000), 3),
+])
+def test_backward_bad_arguments_are_rejected_without_launch(lib, kw, code):
+    st, msg = _call_bwd(kw)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def test_backward_workspace_bytes(lib):
+    from delta_rule_recurrent_kda_amd import kda
+    # 32-token chunks: chunk table, one fp32 record (Kh, Kc, Qh [32][d_k], T, P [32][32], gamma, b)
+    # and the state and its gradient (fp32 [d_k][d_v] each) per (chunk, head)
+    T, N, H = 1000, 3, 2
+    chunks = (T + 31) // 32 + N
+    rec = (3 * 32 * 128 + 2 * 32 * 32 + 128 + 32) * 4
+    table = ((N + 1) * 4 + 255) // 256 * 256
+    assert kda.backward_workspace_bytes(T, N, H, 128, 128) == table + chunks * H * (rec + 2 * 128 * 128 * 4)
+    assert kda.backward_workspace_bytes(T, 0, H, 128, 128) == 0
 
 
 def test_workspace_bytes(lib):
