@@ -287,11 +287,19 @@ kda_status kda_short_conv(const void* x, const float* w_text, const float* w_vis
     std::unique_lock<std::mutex> lk(g_timing.mu);
     kda::TimingHook* th = g_timing.on ? &g_timing : nullptr;
     if (!th) lk.unlock();
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || !prepare_pool(dev))
+        return fail(KDA_E_HIP, "setting up the workspace pool: %s", hipGetErrorString(e));
+    void* ws = nullptr;
+    const size_t bytes = kda::conv_workspace_bytes(num_seqs);
+    e = hipMallocAsync(&ws, bytes, stream);
+    if (e != hipSuccess) return fail(KDA_E_HIP, "workspace of %zu bytes: %s", bytes, hipGetErrorString(e));
     const kda::ConvArgs a{x, w_text, w_vis, cu_seqlens, text_len, grid, y, total_tokens, num_seqs, channels,
                           k_text, k_t, k_h, k_w, dtype == KDA_BF16 ? 1 : 0, stream};
-    if (th) th->begin("conv", stream);
-    hipError_t e = kda::launch_short_conv(a);
-    if (th) th->end(stream);
+    e = kda::launch_short_conv(a, ws, th);
+    const hipError_t ef = hipFreeAsync(ws, stream);
+    if (e == hipSuccess) e = ef;
     if (e != hipSuccess) return fail(KDA_E_HIP, "launch failed: %s", hipGetErrorString(e));
     return KDA_OK;
 }

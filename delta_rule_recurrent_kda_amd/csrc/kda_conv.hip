@@ -11,11 +11,23 @@
 //   visual: y[i,j,k][c] = sum_{a<kt, b<kh, d<kw} w_vis[a][b][d][c] x[i-a, j+b-(kh-1)/2, k+d-(kw-1)/2][c]
 // with zeros outside the sample's text or grid.
 //
-// The pass is bound by HBM (read x once, write y once). One thread computes 8 channels
-// of a token from 16-byte loads of its taps. A workgroup covers 128 tokens x 64 channels,
-// and the tiles are numbered so that each XCD walks a contiguous token range of one
-// channel block: the rows above and the frames before a tile (128 bytes per token per
-// channel block) were read shortly before by the same XCD and are still in its L2.
+// Every input feeds kt*kh*kw outputs, so the pass does 27 fp32 FMAs per output element for
+// the 3x3x3 kernel; with packed fp32 arithmetic off, that vector work and the bf16 widening
+// of the inputs, not HBM, bound it. The design therefore spends VALU on little else:
+//   - Work is cut into tiles over 64 channels: a text tile is 128 text tokens of one sample;
+//     a visual tile is 32 column strips, a strip being 4 adjacent columns of one row of one
+//     frame (strips run frame-, row-, column-major through the sample's grid). A thread owns
+//     one strip and 8 channels, so each loaded input column feeds the kw taps of up to 4
+//     outputs and is widened from bf16 once.
+//   - Inputs come straight from global memory: the kt*kh rows a strip reads are shared with
+//     the strips of neighbouring rows and frames, which run at the same time on the same XCD
+//     and find them in its L2.
+//   - For whole-frame samples under 1 GiB the loads are buffer loads over the sample's grid
+//     tokens: a position outside the grid gets an offset past the buffer's end and reads as
+//     zero, so no lane spends arithmetic on padding.
+//   - A plan kernel counts the tiles per sample; a fixed grid of workgroups walks the tile
+//     list channel-block-major, each XCD a contiguous part of it, with the weights of the
+//     current channel block in LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,12 +42,16 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kCT = 256;            // threads per workgroup
 constexpr int kCB = 64;             // channels per tile
-constexpr int kTPT = 4;             // tokens per thread
-constexpr int kTok = kCT / (kCB / 8) * kTPT;   // tokens per tile: 128
-constexpr int kMaxTaps = 8 + 4 * 5 * 5;
+constexpr int kTextTok = 128;       // tokens per text tile
+constexpr int kSW = 4;              // columns per thread strip
+constexpr int kStrips = kCT / 8;    // column strips per visual tile
+constexpr int kWgPerCu = 4;         // resident workgroups per CU of the persistent grid
+constexpr uint32_t kBufLimit = 1u << 30;    // bytes a buffer-load tile may span; also the "outside" offset
+constexpr int kBufFlags = 0x00020000;       // raw buffer resource: 32-bit data format, no swizzle
 
 template <typename E> struct Vec8;
 template <> struct Vec8<uint16_t> {
+    static constexpr int kBytes = 16;
     __device__ static void load(const uint16_t* p, float (&f)[8]) {
         const u32x4 u = *reinterpret_cast<const u32x4*>(p);
 #pragma unroll
@@ -47,8 +63,21 @@ template <> struct Vec8<uint16_t> {
     __device__ static void store(uint16_t* p, const float (&f)[8]) {
         *reinterpret_cast<u32x4*>(p) = u32x4{pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
     }
+    // 8 channels as loaded (two bf16 per dword), widened one element at a time
+    struct Raw { u32x4 u; };
+    __device__ static Raw load_raw(const uint16_t* p, bool ok) {
+        return Raw{ok ? *reinterpret_cast<const u32x4*>(p) : u32x4{0u, 0u, 0u, 0u}};
+    }
+    __device__ static float at(const Raw& r, int e) {
+        return __uint_as_float((e & 1) ? (r.u[e >> 1] & 0xFFFF0000u) : (r.u[e >> 1] << 16));
+    }
+    // bytes at `off` of the buffer; zeros when off is past its end
+    __device__ static Raw load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        return Raw{__builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0)};
+    }
 };
 template <> struct Vec8<float> {
+    static constexpr int kBytes = 32;
     __device__ static void load(const float* p, float (&f)[8]) {
         const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
 #pragma unroll
@@ -61,106 +90,305 @@ template <> struct Vec8<float> {
         *reinterpret_cast<f32x4*>(p) = f32x4{f[0], f[1], f[2], f[3]};
         *reinterpret_cast<f32x4*>(p + 4) = f32x4{f[4], f[5], f[6], f[7]};
     }
+    struct Raw { f32x4 a, b; };
+    __device__ static Raw load_raw(const float* p, bool ok) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        return Raw{ok ? *reinterpret_cast<const f32x4*>(p) : z, ok ? *reinterpret_cast<const f32x4*>(p + 4) : z};
+    }
+    __device__ static float at(const Raw& r, int e) { return e < 4 ? r.a[e] : r.b[e - 4]; }
+    __device__ static Raw load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
+        return Raw{f32x4{__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]), __uint_as_float(a[3])},
+                   f32x4{__uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]), __uint_as_float(b[3])}};
+    }
 };
 
-template <typename E>
-__global__ __launch_bounds__(kCT) void kda_short_conv_kernel(
+// Extent of sample n, with every value clamped so that the kernel reads and writes only
+// inside the sample whatever the tables hold. Element offsets fit in 32 bits (the caller
+// checks tokens x channels < 2^31). The grid is cut to the frames and rows that hold tokens:
+// positions past the sample's last token read as zero either way, so this changes no output.
+struct SampleGeom {
+    int32_t base, L, nv;            // first token, text tokens, grid tokens present
+    int32_t Tn, Hn, Wn;             // frames holding a token, rows, columns (0 frames: no grid)
+    int32_t past;                   // first grid token past T*H*W (== nv when the grid fits)
+};
+__device__ __forceinline__ SampleGeom sample_geom(const int32_t* cu, const int32_t* text_len, const int32_t* grid,
+                                                  int n, int64_t T) {
+    SampleGeom g;
+    const int64_t base = min<int64_t>(max<int64_t>(cu[n], 0), T);
+    const int64_t end = min<int64_t>(max<int64_t>(cu[n + 1], base), T);
+    const int64_t L = min<int64_t>(max(text_len[n], 0), end - base), nv = end - base - L;
+    int64_t Tn = max(grid[3 * n], 0), Hn = max(grid[3 * n + 1], 0), Wn = max(grid[3 * n + 2], 0);
+    int64_t past = 0;                           // no grid: every visual token past it
+    if (Tn == 0 || Hn == 0 || Wn == 0 || nv == 0) {
+        Tn = 0;
+    } else {
+        const int64_t hw = Hn * Wn;             // < 2^62
+        past = Tn >= (nv + hw - 1) / hw ? nv : Tn * hw;
+        // rows and frames past the last token hold none; the raster index of every
+        // position that holds a token is unchanged by these cuts
+        Wn = min(Wn, nv);
+        Hn = min(Hn, (nv + Wn - 1) / Wn);
+        Tn = min(Tn, (nv + Hn * Wn - 1) / (Hn * Wn));
+    }
+    g.base = int32_t(base); g.L = int32_t(L); g.nv = int32_t(nv);
+    g.Tn = int32_t(Tn); g.Hn = int32_t(Hn); g.Wn = int32_t(Wn); g.past = int32_t(past);
+    return g;
+}
+
+// Tiles of sample n per channel block: text tiles of 128 tokens, visual tiles of 32 column
+// strips (a strip is 4 adjacent columns of one row of one frame; strips run frame, row,
+// column-major), then tiles of 128 tokens past the grid, which get zeros.
+struct SampleTiles {
+    int32_t ntext, nvis, nzero, nsw;  // nsw: strips per row
+};
+__device__ __forceinline__ SampleTiles sample_tiles(const SampleGeom& g) {
+    SampleTiles t;
+    t.ntext = (g.L + kTextTok - 1) / kTextTok;
+    t.nsw = (g.Wn + kSW - 1) / kSW;
+    t.nvis = g.Tn > 0 ? int32_t((int64_t(g.Tn) * g.Hn * t.nsw + kStrips - 1) / kStrips) : 0;
+    t.nzero = (g.nv - g.past + kTextTok - 1) / kTextTok;
+    return t;
+}
+
+// tile_off[n] = tiles of samples 0..n-1 (per channel block); one workgroup
+__global__ __launch_bounds__(1024) void kda_conv_plan_kernel(const int32_t* __restrict__ cu,
+                                                             const int32_t* __restrict__ text_len,
+                                                             const int32_t* __restrict__ grid,
+                                                             int32_t* __restrict__ tile_off, int num_seqs, int64_t T)
+{
+    __shared__ int32_t part[1024];
+    const int tid = threadIdx.x;
+    int32_t carry = 0;
+    for (int b0 = 0; b0 < num_seqs; b0 += 1024) {
+        const int n = b0 + tid;
+        int32_t cnt = 0;
+        if (n < num_seqs) {
+            const SampleTiles t = sample_tiles(sample_geom(cu, text_len, grid, n, T));
+            cnt = t.ntext + t.nvis + t.nzero;
+        }
+        part[tid] = cnt;
+        __syncthreads();
+        for (int d = 1; d < 1024; d <<= 1) {
+            const int32_t add = tid >= d ? part[tid - d] : 0;
+            __syncthreads();
+            part[tid] += add;
+            __syncthreads();
+        }
+        if (n < num_seqs) tile_off[n + 1] = carry + part[tid];
+        carry += part[1023];
+        __syncthreads();
+    }
+    if (tid == 0) tile_off[0] = 0;
+}
+
+template <typename E, int KW>
+__global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kWgPerCu))) void kda_short_conv_kernel(
     const E* __restrict__ x, const float* __restrict__ w_text, const float* __restrict__ w_vis,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ text_len, const int32_t* __restrict__ grid,
-    E* __restrict__ y, int64_t T, int num_seqs, int C, int kx, int kt, int kh, int kw, int ntb, int ncb)
+    const int32_t* __restrict__ tile_off, E* __restrict__ y, int64_t T, int num_seqs, int C, int kx, int kt, int kh,
+    int ncb)
 {
-    __shared__ float wl[kMaxTaps * kCB];     // [tap][channel of the tile]: text taps, then visual
-    const int tid = threadIdx.x;
-    // tiles of one XCD are consecutive: logical tile = xcd * per + slot
-    const int nt = ntb * ncb, per = (nt + 7) / 8;
-    const int lt = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-    if (lt >= nt) return;
-    const int cb = lt / ntb, tb = lt % ntb;
+    constexpr int kw = KW;
+    extern __shared__ __align__(16) float wl[];                          // [tap][64]: text taps, then visual
     const int ntaps = kx + kt * kh * kw;
-    for (int i = tid; i < ntaps * kCB; i += kCT) {
-        const int tap = i / kCB, c = kCB * cb + i % kCB;
-        float w = 0.f;
-        if (c < C) w = tap < kx ? w_text[int64_t(tap) * C + c] : w_vis[int64_t(tap - kx) * C + c];
-        wl[i] = w;
-    }
-    __syncthreads();
-
-    const int vec = tid & 7, c0 = kCB * cb + 8 * vec;
-    if (c0 >= C) return;
-    const float* wv = wl + 8 * vec;
+    const int tid = threadIdx.x, vec = tid & 7;
     const int ph = (kh - 1) / 2, pw = (kw - 1) / 2;
-#pragma unroll 1
-    for (int u = 0; u < kTPT; ++u) {
-        const int64_t tok = int64_t(tb) * kTok + (tid >> 3) + 32 * u;
-        if (tok >= T) break;
-        // owning sample: cu[n] <= tok < cu[n + 1]
-        int lo = 0, hi = num_seqs;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (cu[mid] <= tok) lo = mid; else hi = mid;
+
+    const int per_cb = tile_off[num_seqs];
+    const int64_t total = int64_t(per_cb) * ncb;
+    // this XCD's contiguous range of the tile list (channel-block-major, so the tiles that
+    // share inputs sit together); its workgroups take it in turn
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, ng = gridDim.x >> 3;
+    const int64_t per = (total + 7) / 8;
+    const int64_t t_end = min<int64_t>(total, (xcd + 1) * per);
+    int cb_loaded = -1;
+    for (int64_t tile = xcd * per + slot; tile < t_end; tile += ng) {
+        const int cb = int(tile / per_cb), tp = int(tile % per_cb);
+        if (cb != cb_loaded) {                      // weights of this channel block
+            __syncthreads();
+            for (int i = tid; i < ntaps * kCB; i += kCT) {
+                const int tap = i / kCB, c = kCB * cb + i % kCB;
+                float w = 0.f;
+                if (c < C) w = tap < kx ? w_text[tap * C + c] : w_vis[(tap - kx) * C + c];
+                wl[i] = w;
+            }
+            __syncthreads();
+            cb_loaded = cb;
         }
-        // bounds clamped to the tokens, so malformed offsets never address outside x
-        const int64_t base = min<int64_t>(max<int64_t>(cu[lo], 0), T);
-        const int64_t end = min<int64_t>(max<int64_t>(cu[lo + 1], base), T);
-        const int64_t L = min<int64_t>(max(text_len[lo], 0), end - base), rel = tok - base;
-        float acc[8];
+        int n = 0, hi = num_seqs;                   // tile_off[n] <= tp < tile_off[n + 1]
+        while (hi - n > 1) {
+            const int mid = (n + hi) >> 1;
+            if (tile_off[mid] <= tp) n = mid; else hi = mid;
+        }
+        const SampleGeom g = sample_geom(cu, text_len, grid, n, T);
+        const SampleTiles st = sample_tiles(g);
+        const int local = tp - tile_off[n];
+        const int c0 = kCB * cb + 8 * vec;
+        if (c0 >= C) continue;
+        const float* wv = wl + 8 * vec;
+
+        if (local < st.ntext) {
+            // ---- text tile: 128 tokens, a thread per token and 8 channels ----
+            for (int r = tid >> 3; r < kTextTok; r += kCT / 8) {
+                const int rel = local * kTextTok + r;
+                if (rel >= g.L) break;
+                const int tok = g.base + rel;
+                float acc[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-        if (rel < L) {
-            for (int i = 0; i < kx && rel - i >= 0; ++i) {
-                float f[8];
-                Vec8<E>::load(x + (tok - i) * C + c0, f);
+                for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+                for (int i = 0; i < kx && rel - i >= 0; ++i) {
+                    float f[8];
+                    Vec8<E>::load(x + (tok - i) * C + c0, f);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] += wv[i * kCB + e] * f[e];
-            }
-        } else {
-            const int64_t Hn = grid[3 * lo + 1], Wn = grid[3 * lo + 2];
-            const int64_t nv = end - base - L, m = rel - L;          // grid tokens present, this one's index
-            if (Hn <= 0 || Wn <= 0 || m >= nv) {                     // grid inconsistent with the sample
+                    for (int e = 0; e < 8; ++e) acc[e] += wv[i * kCB + e] * f[e];
+                }
                 Vec8<E>::store(y + tok * C + c0, acc);
-                continue;
             }
-            const int64_t i = m / (Hn * Wn), j = (m / Wn) % Hn, k = m % Wn;
-            for (int a = 0; a < kt && i - a >= 0; ++a)
-                for (int b = 0; b < kh; ++b) {
-                    const int64_t jj = j + b - ph;
-                    if (jj < 0 || jj >= Hn) continue;
-                    for (int d = 0; d < kw; ++d) {
-                        const int64_t kk = k + d - pw;
-                        const int64_t mm = ((i - a) * Hn + jj) * Wn + kk;
-                        if (kk < 0 || kk >= Wn || mm >= nv) continue;
-                        float f[8];
-                        Vec8<E>::load(x + (base + L + mm) * C + c0, f);
-                        const float* w = wv + (kx + (a * kh + b) * kw + d) * kCB;
+            continue;
+        }
+        if (local >= st.ntext + st.nvis) {
+            // ---- tokens past the grid: zeros ----
+            const float zero[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int r = tid >> 3; r < kTextTok; r += kCT / 8) {
+                const int m = g.past + (local - st.ntext - st.nvis) * kTextTok + r;
+                if (m < g.nv) Vec8<E>::store(y + (g.base + g.L + m) * C + c0, zero);
+            }
+            continue;
+        }
+
+        // ---- visual tile: 32 strips; this thread's strip is 4 columns x 8 channels ----
+        const int sidx = (local - st.ntext) * kStrips + (tid >> 3);
+        const int per_frame = g.Hn * st.nsw;
+        const int f = sidx / per_frame;
+        if (f >= g.Tn) continue;
+        const int j = (sidx - f * per_frame) / st.nsw;
+        const int kq = (sidx - f * per_frame - j * st.nsw) * kSW;
+        const E* xs = x + (g.base + g.L) * C + c0;  // this sample's grid tokens, this thread's channels
+        float acc[kSW][8];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) acc[e] += w[e] * f[e];
+        for (int q = 0; q < kSW; ++q)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[q][e] = 0.f;
+        const bool fast = g.past == g.nv && int64_t(g.Tn) * g.Hn * g.Wn == g.nv &&
+                          int64_t(g.nv) * C * int64_t(sizeof(E)) <= kBufLimit;
+        if (fast) {
+            // Whole frames, sample under 1 GiB: buffer loads over the sample's grid tokens, so a
+            // position outside the grid is an offset of at least kBufLimit and reads as zero.
+            // Each position is widened once and feeds the KW taps of the strip that use it.
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<E*>(x + (g.base + g.L) * C), 0, int(int64_t(g.nv) * C * sizeof(E)), kBufFlags);
+            const uint32_t rowb = uint32_t(g.Wn) * uint32_t(C) * sizeof(E);
+            uint32_t colv[kSW + KW - 1];
+#pragma unroll
+            for (int p = 0; p < kSW + KW - 1; ++p) {
+                const int kk = kq + p - pw;
+                colv[p] = kk >= 0 && kk < g.Wn ? uint32_t(kk * C + c0) * sizeof(E) : kBufLimit;
+            }
+            for (int a = 0; a < kt && f - a >= 0; ++a)
+                for (int b = 0; b < kh; ++b) {
+                    const int jj = j + b - ph;
+                    const uint32_t roff = jj >= 0 && jj < g.Hn ? uint32_t((f - a) * g.Hn + jj) * rowb : kBufLimit;
+                    typename Vec8<E>::Raw in[kSW + KW - 1];
+#pragma unroll
+                    for (int p = 0; p < kSW + KW - 1; ++p) in[p] = Vec8<E>::load_buf(rs, roff + colv[p]);
+                    const float* wr = wv + (kx + (a * kh + b) * KW) * kCB;
+                    float w[KW][8];
+#pragma unroll
+                    for (int d = 0; d < KW; ++d)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) w[d][e] = wr[d * kCB + e];
+#pragma unroll
+                    for (int p = 0; p < kSW + KW - 1; ++p) {
+                        float xf[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) xf[e] = Vec8<E>::at(in[p], e);
+#pragma unroll
+                        for (int d = 0; d < KW; ++d) {
+                            const int q = p - d;
+                            if (q < 0 || q >= kSW) continue;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) acc[q][e] += w[d][e] * xf[e];
+                        }
                     }
                 }
+        } else
+        for (int a = 0; a < kt && f - a >= 0; ++a)
+            for (int b = 0; b < kh; ++b) {
+                const int jj = j + b - ph;
+                if (jj < 0 || jj >= g.Hn) continue;
+                const int row = ((f - a) * g.Hn + jj) * g.Wn;         // grid index of column 0
+                // columns kq - pw .. kq + kSW - 1 + pw, zero outside the grid or the sample
+                typename Vec8<E>::Raw in[kSW + KW - 1];
+#pragma unroll
+                for (int q = 0; q < kSW + KW - 1; ++q) {
+                    const int kk = kq + q - pw;
+                    const bool ok = kk >= 0 && kk < g.Wn && row + kk < g.nv;
+                    in[q] = Vec8<E>::load_raw(xs + (ok ? row + kk : 0) * C, ok);
+                }
+                const float* wr = wv + (kx + (a * kh + b) * kw) * kCB;
+#pragma unroll
+                for (int d = 0; d < KW; ++d) {
+                    float w[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) w[e] = wr[d * kCB + e];
+#pragma unroll
+                    for (int q = 0; q < kSW; ++q)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[q][e] += w[e] * Vec8<E>::at(in[q + d], e);
+                }
+            }
+#pragma unroll
+        for (int q = 0; q < kSW; ++q) {
+            const int kk = kq + q, m = (f * g.Hn + j) * g.Wn + kk;
+            if (kk < g.Wn && m < g.past) Vec8<E>::store(y + (g.base + g.L + m) * C + c0, acc[q]);
         }
-        Vec8<E>::store(y + tok * C + c0, acc);
+    }
+}
+
+template <typename E, int KW>
+void launch_conv_kw(const ConvArgs& a, int32_t* tile_off, size_t smem, int blocks, int ncb)
+{
+    hipLaunchKernelGGL((kda_short_conv_kernel<E, KW>), dim3(blocks), dim3(kCT), smem, a.stream,
+                       static_cast<const E*>(a.x), a.w_text, a.w_vis, a.cu_seqlens, a.text_len, a.grid, tile_off,
+                       static_cast<E*>(a.y), a.total_tokens, a.num_seqs, a.channels, a.k_text, a.k_t, a.k_h, ncb);
+}
+
+// the kernel width is a template argument: it sizes the strip's input registers
+template <typename E>
+void launch_conv(const ConvArgs& a, int32_t* tile_off, size_t smem, int blocks, int ncb)
+{
+    switch (a.k_w) {
+    case 1: launch_conv_kw<E, 1>(a, tile_off, smem, blocks, ncb); break;
+    case 3: launch_conv_kw<E, 3>(a, tile_off, smem, blocks, ncb); break;
+    default: launch_conv_kw<E, 5>(a, tile_off, smem, blocks, ncb); break;
     }
 }
 
 }  // namespace
 
-hipError_t launch_short_conv(const ConvArgs& a)
+size_t conv_workspace_bytes(int32_t num_seqs) { return ((size_t(num_seqs) + 1) * 4 + 255) & ~size_t(255); }
+
+hipError_t launch_short_conv(const ConvArgs& a, void* workspace, TimingHook* th)
 {
     if (a.total_tokens == 0 || a.num_seqs == 0) return hipSuccess;
-    const int64_t ntb = (a.total_tokens + kTok - 1) / kTok;
+    const size_t smem = size_t(a.k_text + a.k_t * a.k_h * a.k_w) * kCB * sizeof(float);
     const int ncb = (a.channels + kCB - 1) / kCB;
-    if (ntb * ncb > 0x7FFFFFFF - 8) return hipErrorInvalidValue;
-    const int nt = int(ntb * ncb);
-    const int blocks = ((nt + 7) / 8) * 8;
+    int32_t* tile_off = static_cast<int32_t*>(workspace);
+    if (th) th->begin("conv_plan", a.stream);
+    hipLaunchKernelGGL(kda_conv_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, a.text_len, a.grid,
+                       tile_off, a.num_seqs, a.total_tokens);
+    if (th) th->end(a.stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int blocks = 256 * kWgPerCu;              // every CU, kWgPerCu resident workgroups each
+    if (th) th->begin("conv", a.stream);
     if (a.dtype_bf16)
-        hipLaunchKernelGGL(kda_short_conv_kernel<uint16_t>, dim3(blocks), dim3(kCT), 0, a.stream,
-                           static_cast<const uint16_t*>(a.x), a.w_text, a.w_vis, a.cu_seqlens, a.text_len, a.grid,
-                           static_cast<uint16_t*>(a.y), a.total_tokens, a.num_seqs, a.channels, a.k_text, a.k_t,
-                           a.k_h, a.k_w, int(ntb), ncb);
+        launch_conv<uint16_t>(a, tile_off, smem, blocks, ncb);
     else
-        hipLaunchKernelGGL(kda_short_conv_kernel<float>, dim3(blocks), dim3(kCT), 0, a.stream,
-                           static_cast<const float*>(a.x), a.w_text, a.w_vis, a.cu_seqlens, a.text_len, a.grid,
-                           static_cast<float*>(a.y), a.total_tokens, a.num_seqs, a.channels, a.k_text, a.k_t, a.k_h,
-                           a.k_w, int(ntb), ncb);
+        launch_conv<float>(a, tile_off, smem, blocks, ncb);
+    if (th) th->end(a.stream);
     return hipGetLastError();
 }
 

@@ -77,7 +77,8 @@ struct ConvArgs {
     int32_t num_seqs, channels, k_text, k_t, k_h, k_w, dtype_bf16;
     hipStream_t stream;
 };
-hipError_t launch_short_conv(const ConvArgs& a);
+hipError_t launch_short_conv(const ConvArgs& a, void* workspace, TimingHook* th);
+size_t conv_workspace_bytes(int32_t num_seqs);
 
 // LDS bytes one workgroup uses.
 size_t smem_bytes(int dtype_bf16, int d_k);

@@ -211,11 +211,13 @@ size_t kda_backward_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int3
  *   w_text      : [k_text][channels] fp32;  w_vis : [k_t][k_h][k_w][channels] fp32 (DEVICE)
  *   cu_seqlens  : [num_seqs + 1] int32; text_len : [num_seqs] int32; grid : [num_seqs][3] int32
  *                 (DEVICE); text_len[n] + T*H*W must equal the sample's length (checked on the
- *                 host only with KDA_VALIDATE=1; otherwise the kernel reads only inside the
- *                 sample and writes zeros for grid positions that do not fit)
+ *                 host only with KDA_VALIDATE=1). Otherwise the kernel still reads and writes
+ *                 only inside the sample: grid positions past its last token read as zero,
+ *                 and tokens past T*H*W (or after the text when T, H or W is 0) get zeros
  *   channels    : a multiple of 8; k_text 1..8, k_t 1..4, k_h and k_w odd in 1..5
- * Arithmetic is fp32; y is rounded to nearest-even for bf16. No workspace. Execution and
- * errors as kda_forward; the timing hook names the kernel "conv".
+ * Arithmetic is fp32; y is rounded to nearest-even for bf16. A workspace of (num_seqs + 1)
+ * int32 (the tile table) comes from the stream-ordered pool as for kda_forward. Execution
+ * and errors as kda_forward; the timing hook names the kernels "conv_plan" and "conv".
  */
 kda_status kda_short_conv(const void *x, const float *w_text, const float *w_vis,
                           const int32_t *cu_seqlens, const int32_t *text_len, const int32_t *grid,

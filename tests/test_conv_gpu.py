@@ -86,6 +86,55 @@ def test_short_conv_image_batch_layout():
     _check(83, [(256, 1, 64, 64)] * 4, 64, (4, 3, 3, 3), "bf16", "image4 layout")
 
 
+def _bound_check(y, ref, mag, label):
+    bound = 2.0 ** -8 * np.abs(ref) + 64 * 2.0 ** -24 * mag
+    err = np.abs(y - ref)
+    worst = float((err / np.maximum(bound, 1e-300)).max()) if err.size else 0.0
+    gu.log(f"[{label}] worst error / bound {worst:.3f}")
+    assert np.all(err <= bound), (label, worst)
+
+
+def test_short_conv_grid_not_matching_length():
+    """Samples whose grid does not match their length (the caller's error, not checked unless
+    asked): the kernel still reads and writes only inside each sample. Grid positions past a
+    sample's last token read as zero, so the present tokens equal the oracle on the full grid
+    with the missing tokens zero; tokens past T*H*W equal zero. Packed with a well-formed
+    sample, whose output must be unaffected, over 40 channels (a partial channel block)."""
+    import oracle
+    C, ks = 40, (4, 3, 3, 3)
+    # (text_len, grid tokens present, stored grid T, H, W)
+    samples = [(4, 47, (3, 4, 5)),      # grid longer than the sample, last frame partial
+               (2, 20, (2, 6, 7)),      # first frame partial: rows past the last token
+               (3, 10, (1, 3, 50)),     # one row longer than every token present
+               (5, 25, (2, 3, 3)),      # grid shorter than the sample: 7 tokens past it
+               (6, 9, (0, 3, 3)),       # no frames: every visual token past the grid
+               (3, 30, (2, 3, 5))]      # well formed
+    rng = np.random.default_rng(85)
+    lens = [L + nv for L, nv, _ in samples]
+    x = inputs.bf16_bits_to_f64(inputs.f64_to_bf16_bits(rng.standard_normal((sum(lens), C))))
+    wt = rng.standard_normal((ks[0], C)).astype(np.float32) * 0.5
+    wv = rng.standard_normal((ks[1], ks[2], ks[3], C)).astype(np.float32) * 0.3
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    tl = np.array([s[0] for s in samples], np.int32)
+    gr = np.array([s[2] for s in samples], np.int32)
+    gu.log(f"case short conv grid not matching length: {len(samples)} samples, {len(x)} tokens, C={C}")
+    y = _run(x, wt, wv, cu, tl, gr, "bf16")
+    for n, (L, nv, (T, H, W)) in enumerate(samples):
+        xs = x[cu[n]:cu[n + 1]]
+        full = L + T * H * W
+        xf = np.zeros((full, C))
+        keep = min(L + nv, full)
+        xf[:keep] = xs[:keep]
+        one = lambda a, u, v: oracle.short_conv(a, u, v, np.array([0, full], np.int32), np.array([L], np.int32),
+                                                np.array([[T, H, W]], np.int32))
+        ref = np.zeros((L + nv, C))
+        mag = np.zeros((L + nv, C))
+        ref[:keep] = one(xf, wt, wv)[:keep]
+        mag[:keep] = one(np.abs(xf), np.abs(wt), np.abs(wv))[:keep]
+        _bound_check(y[cu[n]:cu[n + 1]], ref, mag, f"sample {n} grid {T}x{H}x{W}, {nv} grid tokens")
+        assert np.all(y[cu[n] + keep:cu[n + 1]] == 0)
+
+
 def test_short_conv_timing_hook():
     import torch
     from delta_rule_recurrent_kda_amd import kda
@@ -95,6 +144,7 @@ def test_short_conv_timing_hook():
         _run(x, wt, wv, cu, tl, gr, "bf16")
     finally:
         kda.timing_enable(False)
-    n, ms = kda.timing_read("conv")
-    assert n == 1 and ms > 0
+    for name in ("conv_plan", "conv"):
+        n, ms = kda.timing_read(name)
+        assert n == 1 and ms > 0, name
     torch.cuda.synchronize()
