@@ -27,12 +27,18 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
 MFMA_F32_PEAK_TFLOPS = 157.3
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # fp32 vector FMA, published (counts dual-issue/packed)
 KERNEL_SOURCES = ["delta_rule_recurrent_kda_amd/csrc/kda_wy.hip",
                   "delta_rule_recurrent_kda_amd/csrc/kda_device.h",
                   "delta_rule_recurrent_kda_amd/csrc/kda_internal.h"]
 BWD_SOURCES = ["delta_rule_recurrent_kda_amd/csrc/kda_bwd.hip",
                "delta_rule_recurrent_kda_amd/csrc/kda_device.h",
                "delta_rule_recurrent_kda_amd/csrc/kda_internal.h"]
+CONV_SOURCES = ["delta_rule_recurrent_kda_amd/csrc/kda_conv.hip",
+                "delta_rule_recurrent_kda_amd/csrc/kda_device.h",
+                "delta_rule_recurrent_kda_amd/csrc/kda_internal.h"]
+CONV_KERNELS = {"conv_plan": "kda_conv_plan_kernel", "conv": "kda_short_conv_kernel"}
+CONV_TAPS = (4, 3, 3, 3)        # text taps; visual frames x rows x columns
 WORKLOADS = {"tiny": 0, "packed8": 1, "image4": 2, "clip5s": 3, "clip30s": 4}
 CHUNK = 64
 KERNEL_SYMBOL = {"prep": "kda_wy_prep_kernel", "chain": "kda_wy_chain_kernel", "plan": "kda_wy_plan_kernel",
@@ -249,6 +255,75 @@ def backward_bench(args, spec, t, cu, dev):
             "kernels": kernels}
 
 
+def conv_bench(args, spec, dev):
+    """The modality-aware short convolution over heads x d_k channels of one packed batch.
+
+    The layout is the workload's (text prefix + latent grid per sample) when it has a grid,
+    else the 5-second clip (512 text tokens + a 21 x 30 x 52 grid). A step is one
+    kda_short_conv call; K timed steps after W warm-ups, HIP events around each kernel.
+    """
+    import torch
+    from delta_rule_recurrent_kda_amd import inputs, kda
+    cs = spec if spec.grid is not None else inputs.config(WORKLOADS["clip5s"])
+    C = cs.heads * cs.dk
+    n = len(cs.seq_lens)
+    T = cs.total_tokens
+    g = torch.Generator(device=dev)
+    g.manual_seed(4321)
+    x = torch.randn((T, C), device=dev, generator=g).to(torch.bfloat16)
+    wt = torch.randn((CONV_TAPS[0], C), device=dev, generator=g) * 0.5
+    wv = torch.randn((*CONV_TAPS[1:], C), device=dev, generator=g) * 0.3
+    cu = torch.from_numpy(cs.cu_seqlens()).to(dev)
+    tl = torch.tensor(list(cs.text_tokens), dtype=torch.int32, device=dev)
+    gr = torch.tensor([list(cs.grid)] * n, dtype=torch.int32, device=dev)
+    y = torch.empty_like(x)
+
+    def step():
+        kda.short_conv(x, wt, wv, cu, tl, gr, y)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    for name in CONV_KERNELS:
+        kda.timing_read(name)
+    kda.timing_enable(True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    kda.timing_enable(False)
+    kernels = {}
+    for name in CONV_KERNELS:
+        k, ms = kda.timing_read(name)
+        if k:
+            kernels[name] = {"launches": k, "ms_avg": ms / k}
+    ms_step = wall * 1e3 / args.steps
+    text = int(sum(cs.text_tokens))
+    vis = T - text
+    taps = CONV_TAPS[1] * CONV_TAPS[2] * CONV_TAPS[3]
+    flops = 2 * C * (vis * taps + text * CONV_TAPS[0])     # one FMA per tap and output element
+    nbytes = 2 * T * C * 2 + (CONV_TAPS[0] + taps) * C * 4  # read x, write y (bf16), weights
+    kms = kernels["conv"]["ms_avg"]
+    tflops = flops / (kms * 1e-3) / 1e12
+    gbs = nbytes / (kms * 1e-3) / 1e9
+    sha = kernel_sha(CONV_SOURCES)
+    return {"metric": "short convolution tokens/s (depthwise over heads x d_k channels)",
+            "value": T / (ms_step * 1e-3), "unit": "tokens/s", "ms_per_step": ms_step,
+            "dtype": "f32 arithmetic on bf16 data",
+            "config": {"workload": cs.name, "tokens": T, "channels": C, "text_taps": CONV_TAPS[0],
+                       "visual_kernel": list(CONV_TAPS[1:])},
+            "roofline": {"bound": "alu", "achieved": tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tflops / FP32_VECTOR_PEAK_TFLOPS,
+                         "traffic": traffic_for(cs.name.split("-")[0], CONV_KERNELS["conv"], sha),
+                         "kernel": CONV_KERNELS["conv"], "kernel_ms_avg": kms, "flops": flops,
+                         "kernel_sha": sha},
+            "hbm": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                    "algorithmic_bytes": nbytes},
+            "kernels": kernels}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -257,6 +332,7 @@ def main():
     ap.add_argument("--workload", default="packed8", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after timing, run 3 plain device copies of this many MiB (for scaling "
                          "HBM byte counters)")
@@ -354,6 +430,8 @@ def main():
     }
     if not args.no_backward:
         rec["backward"] = backward_bench(args, spec, t, cu, dev)
+    if not args.no_conv:
+        rec["short_conv"] = conv_bench(args, spec, dev)
     if args.copy_calib_mib:
         n = args.copy_calib_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
