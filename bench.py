@@ -118,8 +118,24 @@ def kernel_bytes(spec, kernel: str) -> int:
 
 BWD_C = 32
 BWD_KERNELS = {"bwd_plan": "kda_bwd_plan_kernel", "bwd_prep": "kda_bwd_prep_kernel",
-               "bwd_state": "kda_bwd_state_kernel", "bwd_dstate": "kda_bwd_dstate_kernel",
+               "bwd_state_seg": "kda_bwd_state_kernel", "bwd_state": "kda_bwd_state_kernel",
+               "bwd_dstate_seg": "kda_bwd_dstate_kernel", "bwd_dstate": "kda_bwd_dstate_kernel",
                "bwd_grad": "kda_bwd_grad_kernel"}
+
+
+def bwd_split_chunks(spec) -> int:
+    """Chunks (of 32 tokens) in samples that the backward chains split into several
+    segments (the library's rule: at most 64 chain workgroups, segments of at least 64
+    chunks); the first passes of the split walk exactly these."""
+    chunks = [(n + BWD_C - 1) // BWD_C for n in spec.seq_lens]
+    bound = (spec.total_tokens + BWD_C - 1) // BWD_C
+    if len(chunks) * spec.heads * (spec.dv // 64) > 64:
+        return 0
+    segs = max(1, 256 // (spec.heads * (spec.dv // 64)))
+    lseg = max(64, (bound + segs - 1) // segs)
+    if lseg >= bound:
+        return 0
+    return sum(c for c in chunks if c > lseg)
 
 
 def bwd_chunk_heads(spec) -> int:
@@ -137,6 +153,10 @@ def bwd_kernel_macs(spec, kernel: str) -> int:
         "bwd_state": 2 * C * dk * dv + C * C * dv,
         "bwd_dstate": 3 * C * dk * dv + 2 * C * C * dv,
     }.get(kernel, 0)
+    if kernel == "bwd_state_seg":           # value tiles and the transition's d_k columns
+        return (2 * C * dk + C * C) * (dv + dk) * bwd_split_chunks(spec) * spec.heads
+    if kernel == "bwd_dstate_seg":
+        return (3 * C * dk * dv + 2 * C * C * dv) * bwd_split_chunks(spec) * spec.heads
     return per * bwd_chunk_heads(spec)
 
 
@@ -154,6 +174,11 @@ def bwd_kernel_bytes(spec, kernel: str) -> int:
         return ch * (2 * C * dk + C * C + dk + C) * 4 + T * H * dv * es + state
     if kernel == "bwd_dstate":  # Kh, Kc, Qh, T, P, gamma, beta records and dO; dS per chunk
         return ch * (3 * C * dk + 2 * C * C + dk + C) * 4 + T * H * dv * es + state
+    sc = bwd_split_chunks(spec) * H
+    if kernel == "bwd_state_seg":   # Kh, Kc, T, gamma, beta records and V of split samples
+        return sc * (2 * C * dk + C * C + dk + C) * 4 + sc * C * dv * es
+    if kernel == "bwd_dstate_seg":  # all records and dO of split samples
+        return sc * (3 * C * dk + 2 * C * C + dk + C) * 4 + sc * C * dv * es
     return 4 * (len(spec.seq_lens) + 1)
 
 

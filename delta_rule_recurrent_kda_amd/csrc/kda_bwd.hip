@@ -28,7 +28,8 @@
 // gamma, b; a chain carrying S forwards that saves the state entering every chunk; a
 // chain carrying dS backwards that saves the gradient of the state leaving every chunk;
 // and a gradient kernel over all (chunk, head) pairs that rebuilds the chunk's
-// operands and applies the formulas above.
+// operands and applies the formulas above. For packs of few long samples each chain
+// runs as two passes over segments of the samples (the sequence split below).
 //
 // MFMA: v_mfma_f32_16x16x4f32; lane (r = lane%16, g = lane/16) supplies A(r, k) and
 // B(k, r) for the four k of a step, and holds D(4g + v, r), v = 0..3. Supplying
@@ -36,6 +37,8 @@
 // stands; every operand read from LDS takes any k order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -121,36 +124,49 @@ template <int DK> struct BRec {
 };
 
 // ---------------------------------------------------------------------------
-// chunk table: chunk_off[n] = number of 32-token chunks of samples 0..n-1
+// chunk table: chunk_off[n] = number of 32-token chunks of samples 0..n-1; with the
+// sequence split (lseg > 0 chunks per segment) also seg_off[n] = number of segments of
+// samples 0..n-1, every sample having at least one (an empty sample has one, empty)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void kda_bwd_plan_kernel(const int32_t* __restrict__ cu,
-                                                            int32_t* __restrict__ chunk_off, int num_seqs,
-                                                            int64_t total_tokens)
+                                                            int32_t* __restrict__ chunk_off, int32_t* __restrict__ seg_off,
+                                                            int num_seqs, int64_t total_tokens, int lseg)
 {
-    __shared__ int32_t part[1024];
+    __shared__ int32_t part[1024], spart[1024];
     const int tid = threadIdx.x;
-    int32_t carry = 0;
+    int32_t carry = 0, scarry = 0;
     for (int base = 0; base < num_seqs; base += 1024) {
         const int n = base + tid;
-        int32_t cnt = 0;
+        int32_t cnt = 0, scnt = 0;
         if (n < num_seqs) {
             const int64_t s0 = min<int64_t>(max<int64_t>(cu[n], 0), total_tokens);
             const int64_t s1 = min<int64_t>(max<int64_t>(cu[n + 1], s0), total_tokens);
             cnt = int32_t((s1 - s0 + kBC - 1) / kBC);
+            scnt = lseg > 0 ? max(1, (cnt + lseg - 1) / lseg) : 1;
         }
         part[tid] = cnt;
+        spart[tid] = scnt;
         __syncthreads();
         for (int d = 1; d < 1024; d <<= 1) {
             const int32_t add = tid >= d ? part[tid - d] : 0;
+            const int32_t sadd = tid >= d ? spart[tid - d] : 0;
             __syncthreads();
             part[tid] += add;
+            spart[tid] += sadd;
             __syncthreads();
         }
-        if (n < num_seqs) chunk_off[n + 1] = carry + part[tid];
+        if (n < num_seqs) {
+            chunk_off[n + 1] = carry + part[tid];
+            if (seg_off) seg_off[n + 1] = scarry + spart[tid];
+        }
         carry += part[1023];
+        scarry += spart[1023];
         __syncthreads();
     }
-    if (tid == 0) chunk_off[0] = 0;
+    if (tid == 0) {
+        chunk_off[0] = 0;
+        if (seg_off) seg_off[0] = 0;
+    }
 }
 
 __device__ __forceinline__ void bounds(const int32_t* cu, int n, int64_t T, int64_t& s0, int64_t& s1) {
@@ -168,6 +184,43 @@ __device__ __forceinline__ int owner(const int32_t* chunk_off, int num_seqs, int
         if (chunk_off[mid] <= c) lo = mid; else hi = mid;
     }
     return lo;
+}
+
+// The chunks a chain workgroup walks. Without the split (lseg == 0) a unit is a
+// (sample, head) and walks the whole sample; with it a unit is a (segment, head):
+// segment sid is segment `seg` of `nseg` of sample n (seg_off[n] <= sid < seg_off[n+1]),
+// chunks [c0, c1) starting at token t0. Returns false past the last segment.
+struct ChainSpan {
+    int n, seg, nseg, c0, c1;
+    int64_t t0, s1;                 // first token of the span, end of the sample
+};
+__device__ __forceinline__ bool chain_span(int sid, const int32_t* cu, const int32_t* chunk_off,
+                                           const int32_t* seg_off, int num_seqs, int lseg, int max_chunks,
+                                           int max_segs, int64_t T, ChainSpan& o) {
+    int n = sid, seg = 0, nseg = 1;
+    if (lseg > 0) {
+        if (sid >= min(seg_off[num_seqs], max_segs)) return false;
+        int lo = 0, hi = num_seqs;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (seg_off[mid] <= sid) lo = mid; else hi = mid;
+        }
+        n = lo;
+        seg = sid - seg_off[n];
+        nseg = seg_off[n + 1] - seg_off[n];
+    } else if (sid >= num_seqs) {
+        return false;
+    }
+    const int cs0 = min(chunk_off[n], max_chunks), cs1 = min(chunk_off[n + 1], max_chunks);
+    o.n = n;
+    o.seg = seg;
+    o.nseg = nseg;
+    o.c0 = lseg > 0 ? min(cs0 + seg * lseg, cs1) : cs0;
+    o.c1 = lseg > 0 ? min(o.c0 + lseg, cs1) : cs1;
+    int64_t s0;
+    bounds(cu, n, T, s0, o.s1);
+    o.t0 = s0 + int64_t(o.c0 - cs0) * kBC;
+    return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -386,48 +439,132 @@ template <typename E, int DK, bool GRAD> struct ChainFetch {
     }
 };
 
-template <typename E, int DK, int DV>
+// Sequence split of the chains (lseg > 0), for packs whose (sample, head) units are too
+// few to fill the GPU. Each chunk maps the state affinely: S_out = M S_in + b, and the
+// gradient back: dS_in = M^T dS_out + e. Over a segment of chunks the state pass gives
+// both parts: started from zero it gives the segment's b (S_loc), started from the
+// identity with V = 0 it gives the product of the M (Phi, d_k columns); the gradient
+// pass started from zero gives the segment's e. So:
+//   MODE 1 state:     per segment, S_loc (value tiles) and Phi (d_k / 64 more tiles);
+//   MODE 2 state:     S_in(seg) = Phi(k) S_in(k) + S_loc(k) over the sample's earlier
+//                     segments k (from the initial state), then the segment with the
+//                     state entering each chunk saved, as MODE 0 does for a sample;
+//   MODE 1 gradient:  per segment, e from dS = 0 at its end;
+//   MODE 2 gradient:  dS at the segment's end = Phi(k)^T dS + e(k) over the later
+//                     segments k, from d_final_state, then the segment as MODE 0.
+// Samples of one segment skip MODE 1. The arithmetic stays fp32 throughout.
+template <int DK, int DV>
+__device__ __forceinline__ void seg_prefix_state(f32x4 (&S)[DK / 16], const float* __restrict__ phi,
+                                                 const float* __restrict__ sloc, int sid0, int nk, int H, int h,
+                                                 int col, int r, int g) {
+    constexpr int NCT = DK / 16;
+    for (int k = 0; k < nk; ++k) {
+        const int64_t ks = int64_t(sid0 + k) * H + h;
+        const float* ph = phi + ks * DK * DK;
+        const float* sl = sloc + ks * DK * DV;
+        f32x4 nS[NCT];
+#pragma unroll
+        for (int t2 = 0; t2 < NCT; ++t2) {
+            f32x4 acc;
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) acc[v4] = sl[int64_t(16 * t2 + 4 * g + v4) * DV + col];
+#pragma unroll
+            for (int ti = 0; ti < NCT; ++ti) {
+                const f32x4 a4 = *reinterpret_cast<const f32x4*>(ph + int64_t(16 * t2 + r) * DK + 16 * ti + 4 * g);
+#pragma unroll
+                for (int st = 0; st < 4; ++st) acc = mma4(a4[st], S[ti][st], acc);
+            }
+            nS[t2] = acc;
+        }
+#pragma unroll
+        for (int t2 = 0; t2 < NCT; ++t2) S[t2] = nS[t2];
+    }
+}
+
+// phi_t holds each Phi transposed, so that Phi^T is read like Phi above
+template <int DK, int DV>
+__device__ __forceinline__ void seg_prefix_grad(f32x4 (&dS)[DK / 16], const float* __restrict__ phi_t,
+                                                const float* __restrict__ eseg, int sid_last, int sid_stop, int H,
+                                                int h, int col, int r, int g) {
+    constexpr int NCT = DK / 16;
+    for (int sid = sid_last; sid > sid_stop; --sid) {
+        const int64_t ks = int64_t(sid) * H + h;
+        const float* pt = phi_t + ks * DK * DK;
+        const float* es = eseg + ks * DK * DV;
+        f32x4 nS[NCT];
+#pragma unroll
+        for (int t2 = 0; t2 < NCT; ++t2) {
+            f32x4 acc;
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) acc[v4] = es[int64_t(16 * t2 + 4 * g + v4) * DV + col];
+#pragma unroll
+            for (int ti = 0; ti < NCT; ++ti) {
+                const f32x4 a4 = *reinterpret_cast<const f32x4*>(pt + int64_t(16 * t2 + r) * DK + 16 * ti + 4 * g);
+#pragma unroll
+                for (int st = 0; st < 4; ++st) acc = mma4(a4[st], dS[ti][st], acc);
+            }
+            nS[t2] = acc;
+        }
+#pragma unroll
+        for (int t2 = 0; t2 < NCT; ++t2) dS[t2] = nS[t2];
+    }
+}
+
+template <typename E, int DK, int DV, int MODE>
 __global__ __launch_bounds__(kBT) void kda_bwd_state_kernel(
     const E* __restrict__ v, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
-    const float* __restrict__ rec_ws, const float* __restrict__ init_state, float* __restrict__ s_in,
-    int num_seqs, int H, int64_t total_tokens, int max_chunks)
+    const int32_t* __restrict__ seg_off, const float* __restrict__ rec_ws, const float* __restrict__ init_state,
+    float* __restrict__ s_in, float* __restrict__ sloc, float* __restrict__ phi, float* __restrict__ phi_t,
+    int num_seqs, int H, int64_t total_tokens, int max_chunks, int lseg, int max_segs)
 {
     using R = BRec<DK>;
     constexpr int NCT = DK / 16, LK = DK + 4, LV = 64 + 4;
+    constexpr int NT = MODE == 1 ? DV / 64 + DK / 64 : DV / 64;     // column tiles per unit
     extern __shared__ __align__(16) unsigned char smem_raw[];
     ChainLds<DK>& sm = *reinterpret_cast<ChainLds<DK>*>(smem_raw);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
-    int unit, vt;
-    chain_unit(blockIdx.x, DV / 64, unit, vt);
-    if (unit >= num_seqs * H) return;
-    const int n = unit / H, h = unit % H;
-    const int col = 64 * vt + 16 * wave + r;             // this lane's value column
-    const int c0 = min(chunk_off[n], max_chunks), c1 = min(chunk_off[n + 1], max_chunks);
-    int64_t s0, s1;
-    bounds(cu, n, total_tokens, s0, s1);
+    int unit, tile;
+    chain_unit(blockIdx.x, NT, unit, tile);
+    const int sid = unit / H, h = unit % H;
+    ChainSpan sp;
+    if (!chain_span(sid, cu, chunk_off, seg_off, num_seqs, MODE == 0 ? 0 : lseg, max_chunks, max_segs, total_tokens,
+                    sp))
+        return;
+    if (MODE == 1 && sp.nseg == 1) return;
+    const int n = sp.n;
+    const bool trans = MODE == 1 && tile >= DV / 64;                 // a tile of Phi: identity start, V = 0
+    const int vt = trans ? 0 : tile;
+    const int col = 64 * (trans ? tile - DV / 64 : tile) + 16 * wave + r;   // this lane's column
+    const int c0 = sp.c0, c1 = sp.c1;
 
     f32x4 S[NCT];
 #pragma unroll
     for (int ti = 0; ti < NCT; ++ti) {
 #pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4)
-            S[ti][v4] = init_state ? init_state[((int64_t(n) * H + h) * DK + 16 * ti + 4 * g + v4) * DV + col] : 0.f;
+        for (int v4 = 0; v4 < 4; ++v4) {
+            const int row = 16 * ti + 4 * g + v4;
+            S[ti][v4] = trans ? (row == col ? 1.f : 0.f)
+                              : (init_state && MODE != 1 ? init_state[((int64_t(n) * H + h) * DK + row) * DV + col] : 0.f);
+        }
     }
+    if constexpr (MODE == 2) seg_prefix_state<DK, DV>(S, phi, sloc, sid - sp.seg, sp.seg, H, h, col, r, g);
     ChainFetch<E, DK, false> f;
     auto fetch = [&](int cc) __attribute__((always_inline)) {
-        const int64_t t0 = s0 + int64_t(cc - c0) * kBC;
-        f.load(rec_ws + (int64_t(h) * max_chunks + cc) * R::TOTAL, v, t0, int(min<int64_t>(kBC, s1 - t0)), H, h,
+        const int64_t t0 = sp.t0 + int64_t(cc - c0) * kBC;
+        f.load(rec_ws + (int64_t(h) * max_chunks + cc) * R::TOTAL, v, t0, int(min<int64_t>(kBC, sp.s1 - t0)), H, h,
                DV, 64 * vt);
     };
     if (c0 < c1) fetch(c0);
     for (int cc = c0; cc < c1; ++cc) {
         f.put(sm);
         __syncthreads();
-        float* so = s_in + (int64_t(h) * max_chunks + cc) * DK * DV;
+        if constexpr (MODE != 1) {
+            float* so = s_in + (int64_t(h) * max_chunks + cc) * DK * DV;
 #pragma unroll
-        for (int ti = 0; ti < NCT; ++ti)
+            for (int ti = 0; ti < NCT; ++ti)
 #pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) so[(16 * ti + 4 * g + v4) * DV + col] = S[ti][v4];
+                for (int v4 = 0; v4 < 4; ++v4) so[(16 * ti + 4 * g + v4) * DV + col] = S[ti][v4];
+        }
         fetch(min(cc + 1, c1 - 1));                       // in flight during this chunk's products
         // X = V - Kh S, then Y = diag(b) X (rows 16xi + 4g + v)
         f32x4 Y[2];
@@ -437,11 +574,12 @@ __global__ __launch_bounds__(kBT) void kda_bwd_state_kernel(
 #pragma unroll
             for (int ti = 0; ti < NCT; ++ti)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) acc = mma4(sm.kh[(16 * xi + r) * LK + 16 * ti + 4 * g + s], S[ti][s], acc);
+                for (int st = 0; st < 4; ++st) acc = mma4(sm.kh[(16 * xi + r) * LK + 16 * ti + 4 * g + st], S[ti][st], acc);
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) {
                 const int row = 16 * xi + 4 * g + v4;
-                Y[xi][v4] = sm.beta[row] * (sm.vt[row * LV + 16 * wave + r] - acc[v4]);
+                const float vv = trans ? 0.f : sm.vt[row * LV + 16 * wave + r];
+                Y[xi][v4] = sm.beta[row] * (vv - acc[v4]);
             }
         }
         // Vn = T Y
@@ -452,7 +590,7 @@ __global__ __launch_bounds__(kBT) void kda_bwd_state_kernel(
 #pragma unroll
             for (int xi = 0; xi < 2; ++xi)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) acc = mma4(sm.t[(16 * vi + r) * kLC + 16 * xi + 4 * g + s], Y[xi][s], acc);
+                for (int st = 0; st < 4; ++st) acc = mma4(sm.t[(16 * vi + r) * kLC + 16 * xi + 4 * g + st], Y[xi][st], acc);
             Vn[vi] = acc;
         }
         // S <- diag(gamma) (S + Kc^T Vn)
@@ -462,19 +600,35 @@ __global__ __launch_bounds__(kBT) void kda_bwd_state_kernel(
 #pragma unroll
             for (int vi = 0; vi < 2; ++vi)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) acc = mma4(sm.kc[(16 * vi + 4 * g + s) * LK + 16 * ti + r], Vn[vi][s], acc);
+                for (int st = 0; st < 4; ++st) acc = mma4(sm.kc[(16 * vi + 4 * g + st) * LK + 16 * ti + r], Vn[vi][st], acc);
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) S[ti][v4] = sm.gam[16 * ti + 4 * g + v4] * (S[ti][v4] + acc[v4]);
         }
         __syncthreads();
     }
+    if constexpr (MODE == 1) {
+        // the segment's S_loc (value tiles) or Phi (transition tiles)
+        const int64_t ks = int64_t(sid) * H + h;
+        float* dst = trans ? phi + ks * DK * DK : sloc + ks * DK * DV;
+        const int ld = trans ? DK : DV;
+#pragma unroll
+        for (int ti = 0; ti < NCT; ++ti)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) dst[int64_t(16 * ti + 4 * g + v4) * ld + col] = S[ti][v4];
+        if (trans) {                            // and Phi^T: column col of Phi is row col
+            float* dt = phi_t + ks * DK * DK + int64_t(col) * DK;
+#pragma unroll
+            for (int ti = 0; ti < NCT; ++ti) *reinterpret_cast<f32x4*>(dt + 16 * ti + 4 * g) = S[ti];
+        }
+    }
 }
 
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV, int MODE>
 __global__ __launch_bounds__(kBT) void kda_bwd_dstate_kernel(
     const E* __restrict__ d_out, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
-    const float* __restrict__ rec_ws, const float* __restrict__ d_final, float* __restrict__ ds_out,
-    float* __restrict__ d_init, int num_seqs, int H, int64_t total_tokens, int max_chunks)
+    const int32_t* __restrict__ seg_off, const float* __restrict__ rec_ws, const float* __restrict__ d_final,
+    float* __restrict__ ds_out, float* __restrict__ d_init, const float* __restrict__ phi_t, float* __restrict__ eseg,
+    int num_seqs, int H, int64_t total_tokens, int max_chunks, int lseg, int max_segs)
 {
     using R = BRec<DK>;
     constexpr int NCT = DK / 16, LK = DK + 4, LV = 64 + 4;
@@ -483,34 +637,41 @@ __global__ __launch_bounds__(kBT) void kda_bwd_dstate_kernel(
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
     int unit, vt;
     chain_unit(blockIdx.x, DV / 64, unit, vt);
-    if (unit >= num_seqs * H) return;
-    const int n = unit / H, h = unit % H;
+    const int sid = unit / H, h = unit % H;
+    ChainSpan sp;
+    if (!chain_span(sid, cu, chunk_off, seg_off, num_seqs, MODE == 0 ? 0 : lseg, max_chunks, max_segs, total_tokens,
+                    sp))
+        return;
+    if (MODE == 1 && sp.nseg == 1) return;
+    const int n = sp.n;
     const int col = 64 * vt + 16 * wave + r;
-    const int c0 = min(chunk_off[n], max_chunks), c1 = min(chunk_off[n + 1], max_chunks);
-    int64_t s0, s1;
-    bounds(cu, n, total_tokens, s0, s1);
+    const int c0 = sp.c0, c1 = sp.c1;
 
     f32x4 dS[NCT];
 #pragma unroll
     for (int ti = 0; ti < NCT; ++ti)
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4)
-            dS[ti][v4] = d_final ? d_final[((int64_t(n) * H + h) * DK + 16 * ti + 4 * g + v4) * DV + col] : 0.f;
+            dS[ti][v4] = d_final && MODE != 1 ? d_final[((int64_t(n) * H + h) * DK + 16 * ti + 4 * g + v4) * DV + col] : 0.f;
+    if constexpr (MODE == 2)
+        seg_prefix_grad<DK, DV>(dS, phi_t, eseg, sid - sp.seg + sp.nseg - 1, sid, H, h, col, r, g);
     ChainFetch<E, DK, true> f;
     auto fetch = [&](int cc) __attribute__((always_inline)) {
-        const int64_t t0 = s0 + int64_t(cc - c0) * kBC;
-        f.load(rec_ws + (int64_t(h) * max_chunks + cc) * R::TOTAL, d_out, t0, int(min<int64_t>(kBC, s1 - t0)),
+        const int64_t t0 = sp.t0 + int64_t(cc - c0) * kBC;
+        f.load(rec_ws + (int64_t(h) * max_chunks + cc) * R::TOTAL, d_out, t0, int(min<int64_t>(kBC, sp.s1 - t0)),
                H, h, DV, 64 * vt);
     };
     if (c0 < c1) fetch(c1 - 1);
     for (int cc = c1 - 1; cc >= c0; --cc) {
         f.put(sm);
         __syncthreads();
-        float* so = ds_out + (int64_t(h) * max_chunks + cc) * DK * DV;
+        if constexpr (MODE != 1) {
+            float* so = ds_out + (int64_t(h) * max_chunks + cc) * DK * DV;
 #pragma unroll
-        for (int ti = 0; ti < NCT; ++ti)
+            for (int ti = 0; ti < NCT; ++ti)
 #pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) so[(16 * ti + 4 * g + v4) * DV + col] = dS[ti][v4];
+                for (int v4 = 0; v4 < 4; ++v4) so[(16 * ti + 4 * g + v4) * DV + col] = dS[ti][v4];
+        }
         fetch(max(cc - 1, c0));                           // in flight during this chunk's products
         // dVn = P^T dO + Kc diag(gamma) dS
         f32x4 dVn[2];
@@ -523,9 +684,9 @@ __global__ __launch_bounds__(kBT) void kda_bwd_dstate_kernel(
 #pragma unroll
             for (int ti = 0; ti < NCT; ++ti)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int c = 16 * ti + 4 * g + s;
-                    acc = mma4(sm.kc[(16 * vi + r) * LK + c] * sm.gam[c], dS[ti][s], acc);
+                for (int st = 0; st < 4; ++st) {
+                    const int c = 16 * ti + 4 * g + st;
+                    acc = mma4(sm.kc[(16 * vi + r) * LK + c] * sm.gam[c], dS[ti][st], acc);
                 }
             dVn[vi] = acc;
         }
@@ -537,7 +698,7 @@ __global__ __launch_bounds__(kBT) void kda_bwd_dstate_kernel(
 #pragma unroll
             for (int vi = 0; vi < 2; ++vi)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) acc = mma4(sm.t[(16 * vi + 4 * g + s) * kLC + 16 * zi + r], dVn[vi][s], acc);
+                for (int st = 0; st < 4; ++st) acc = mma4(sm.t[(16 * vi + 4 * g + st) * kLC + 16 * zi + r], dVn[vi][st], acc);
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) dX[zi][v4] = sm.beta[16 * zi + 4 * g + v4] * acc[v4];
         }
@@ -551,13 +712,19 @@ __global__ __launch_bounds__(kBT) void kda_bwd_dstate_kernel(
 #pragma unroll
             for (int zi = 0; zi < 2; ++zi)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) acc = mma4(-sm.kh[(16 * zi + 4 * g + s) * LK + 16 * ti + r], dX[zi][s], acc);
+                for (int st = 0; st < 4; ++st) acc = mma4(-sm.kh[(16 * zi + 4 * g + st) * LK + 16 * ti + r], dX[zi][st], acc);
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) dS[ti][v4] = sm.gam[16 * ti + 4 * g + v4] * dS[ti][v4] + acc[v4];
         }
         __syncthreads();
     }
-    if (d_init) {
+    if constexpr (MODE == 1) {
+        float* es = eseg + (int64_t(sid) * H + h) * DK * DV;
+#pragma unroll
+        for (int ti = 0; ti < NCT; ++ti)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) es[int64_t(16 * ti + 4 * g + v4) * DV + col] = dS[ti][v4];
+    } else if (d_init && sp.seg == 0) {
 #pragma unroll
         for (int ti = 0; ti < NCT; ++ti)
 #pragma unroll
@@ -1022,17 +1189,35 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
 // ---------------------------------------------------------------------------
 struct BwdPlan {
     int max_chunks;
-    size_t table_bytes, rec_bytes, state_bytes;
+    int lseg;          // chunks per segment of the chains' sequence split; 0 = no split
+    int max_segs;
+    size_t table_bytes, rec_bytes, state_bytes, seg_bytes, phi_bytes;
 };
 
+// Sequence split: when the pack gives at most 64 chain workgroups (a quarter of the CUs
+// or less), each sample is cut into segments of lseg chunks (at least 64, i.e. 2,048
+// tokens) so that about 256 workgroups run the second passes.
 BwdPlan bwd_plan(int64_t total_tokens, int32_t num_seqs, int32_t num_heads, int d_k, int d_v)
 {
     BwdPlan p{};
-    p.max_chunks = int((total_tokens + kBC - 1) / kBC + num_seqs);
-    p.table_bytes = ((size_t(num_seqs) + 1) * sizeof(int32_t) + 255) & ~size_t(255);
+    const int64_t chunks_bound = (total_tokens + kBC - 1) / kBC;
+    p.max_chunks = int(chunks_bound + num_seqs);
+    p.lseg = 0;
+    const int64_t units = int64_t(num_seqs) * num_heads * (d_v / 64);
+    if (units <= 64) {
+        const int64_t segs = std::max<int64_t>(1, 256 / (int64_t(num_heads) * (d_v / 64)));
+        const int64_t lseg = std::max<int64_t>(64, (chunks_bound + segs - 1) / segs);
+        if (lseg < chunks_bound) p.lseg = int(lseg);
+    }
+    // every sample has at most ceil(chunks / lseg) <= chunks / lseg + 1 segments, and the
+    // chunks of all samples number at most chunks_bound + num_seqs
+    p.max_segs = p.lseg ? int((chunks_bound + num_seqs + p.lseg - 1) / p.lseg + num_seqs) : 0;
+    p.table_bytes = (2 * (size_t(num_seqs) + 1) * sizeof(int32_t) + 255) & ~size_t(255);
     const size_t rec = d_k == 128 ? BRec<128>::TOTAL : BRec<64>::TOTAL;
     p.rec_bytes = size_t(p.max_chunks) * num_heads * rec * sizeof(float);
     p.state_bytes = size_t(p.max_chunks) * num_heads * d_k * d_v * sizeof(float);
+    p.seg_bytes = size_t(p.max_segs) * num_heads * d_k * d_v * sizeof(float);
+    p.phi_bytes = size_t(p.max_segs) * num_heads * d_k * d_k * sizeof(float);
     return p;
 }
 
@@ -1047,9 +1232,21 @@ hipError_t launch_bwd_t(const BwdArgs& a, void* workspace, TimingHook* th)
     const BwdPlan p = bwd_plan(a.total_tokens, a.num_seqs, a.num_heads, DK, DV);
     char* base = static_cast<char*>(workspace);
     int32_t* chunk_off = reinterpret_cast<int32_t*>(base);
-    float* rec = reinterpret_cast<float*>(base + p.table_bytes);
-    float* s_in = reinterpret_cast<float*>(base + p.table_bytes + p.rec_bytes);
-    float* ds_out = reinterpret_cast<float*>(base + p.table_bytes + p.rec_bytes + p.state_bytes);
+    int32_t* seg_off = chunk_off + (a.num_seqs + 1);
+    char* next = base + p.table_bytes;
+    float* rec = reinterpret_cast<float*>(next);
+    next += p.rec_bytes;
+    float* s_in = reinterpret_cast<float*>(next);
+    next += p.state_bytes;
+    float* ds_out = reinterpret_cast<float*>(next);
+    next += p.state_bytes;
+    float* sloc = p.lseg ? reinterpret_cast<float*>(next) : nullptr;
+    next += p.seg_bytes;
+    float* eseg = p.lseg ? reinterpret_cast<float*>(next) : nullptr;
+    next += p.seg_bytes;
+    float* phi = p.lseg ? reinterpret_cast<float*>(next) : nullptr;
+    next += p.phi_bytes;
+    float* phi_t = p.lseg ? reinterpret_cast<float*>(next) : nullptr;
     const E* q = static_cast<const E*>(a.q);
     const E* k = static_cast<const E*>(a.k);
     const E* v = static_cast<const E*>(a.v);
@@ -1060,8 +1257,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, void* workspace, TimingHook* th)
     hipError_t e;
 
     if (th) th->begin("bwd_plan", a.stream);
-    hipLaunchKernelGGL(kda_bwd_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, chunk_off, a.num_seqs,
-                       a.total_tokens);
+    hipLaunchKernelGGL(kda_bwd_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, chunk_off,
+                       p.lseg ? seg_off : nullptr, a.num_seqs, a.total_tokens, p.lseg);
     if (th) th->end(a.stream);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
@@ -1074,23 +1271,40 @@ hipError_t launch_bwd_t(const BwdArgs& a, void* workspace, TimingHook* th)
     if (th) th->end(a.stream);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    const int units = a.num_seqs * H;
-    const int cblocks = ((units + 7) / 8) * 8 * (DV / 64);
+    // chain grids: units of (sample or segment, head), padded to 8, times the column tiles
+    const int units = p.lseg ? p.max_segs * H : a.num_seqs * H;
+    const int ublocks = ((units + 7) / 8) * 8;
     const size_t chain_smem = sizeof(ChainLds<DK>);
-    auto st = kda_bwd_state_kernel<E, DK, DV>;
-    auto dst = kda_bwd_dstate_kernel<E, DK, DV>;
-    if ((e = set_smem(st, chain_smem)) != hipSuccess) return e;
-    if ((e = set_smem(dst, chain_smem)) != hipSuccess) return e;
-    if (th) th->begin("bwd_state", a.stream);
-    hipLaunchKernelGGL(st, dim3(cblocks), dim3(kBT), chain_smem, a.stream, v, a.cu_seqlens, chunk_off, rec,
-                       a.init_state, s_in, a.num_seqs, H, a.total_tokens, p.max_chunks);
-    if (th) th->end(a.stream);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (th) th->begin("bwd_dstate", a.stream);
-    hipLaunchKernelGGL(dst, dim3(cblocks), dim3(kBT), chain_smem, a.stream, dout, a.cu_seqlens, chunk_off, rec,
-                       a.d_final_state, ds_out, a.d_init_state, a.num_seqs, H, a.total_tokens, p.max_chunks);
-    if (th) th->end(a.stream);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    auto launch_state = [&](auto kern, int ntiles, const char* name) -> hipError_t {
+        hipError_t err = set_smem(kern, chain_smem);
+        if (err != hipSuccess) return err;
+        if (th) th->begin(name, a.stream);
+        hipLaunchKernelGGL(kern, dim3(ublocks * ntiles), dim3(kBT), chain_smem, a.stream, v, a.cu_seqlens, chunk_off,
+                           seg_off, rec, a.init_state, s_in, sloc, phi, phi_t, a.num_seqs, H, a.total_tokens,
+                           p.max_chunks, p.lseg, p.max_segs);
+        if (th) th->end(a.stream);
+        return hipGetLastError();
+    };
+    auto launch_dstate = [&](auto kern, const char* name) -> hipError_t {
+        hipError_t err = set_smem(kern, chain_smem);
+        if (err != hipSuccess) return err;
+        if (th) th->begin(name, a.stream);
+        hipLaunchKernelGGL(kern, dim3(ublocks * (DV / 64)), dim3(kBT), chain_smem, a.stream, dout, a.cu_seqlens,
+                           chunk_off, seg_off, rec, a.d_final_state, ds_out, a.d_init_state, phi_t, eseg, a.num_seqs, H,
+                           a.total_tokens, p.max_chunks, p.lseg, p.max_segs);
+        if (th) th->end(a.stream);
+        return hipGetLastError();
+    };
+    if (p.lseg == 0) {
+        if ((e = launch_state(kda_bwd_state_kernel<E, DK, DV, 0>, DV / 64, "bwd_state")) != hipSuccess) return e;
+        if ((e = launch_dstate(kda_bwd_dstate_kernel<E, DK, DV, 0>, "bwd_dstate")) != hipSuccess) return e;
+    } else {
+        if ((e = launch_state(kda_bwd_state_kernel<E, DK, DV, 1>, DV / 64 + DK / 64, "bwd_state_seg")) != hipSuccess)
+            return e;
+        if ((e = launch_state(kda_bwd_state_kernel<E, DK, DV, 2>, DV / 64, "bwd_state")) != hipSuccess) return e;
+        if ((e = launch_dstate(kda_bwd_dstate_kernel<E, DK, DV, 1>, "bwd_dstate_seg")) != hipSuccess) return e;
+        if ((e = launch_dstate(kda_bwd_dstate_kernel<E, DK, DV, 2>, "bwd_dstate")) != hipSuccess) return e;
+    }
 
     const size_t grad_smem = sizeof(GradLds<DK, DV>);
     auto grad = kda_bwd_grad_kernel<E, DK, DV, NORM>;
@@ -1118,7 +1332,7 @@ hipError_t launch_bwd_n(const BwdArgs& a, void* ws, TimingHook* th)
 size_t bwd_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads, int d_k, int d_v)
 {
     const BwdPlan p = bwd_plan(total_tokens, num_seqs, num_heads, d_k, d_v);
-    return p.table_bytes + p.rec_bytes + 2 * p.state_bytes;
+    return p.table_bytes + p.rec_bytes + 2 * p.state_bytes + 2 * p.seg_bytes + 2 * p.phi_bytes;
 }
 
 hipError_t launch_backward(const BwdArgs& a, void* workspace, TimingHook* th)

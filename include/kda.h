@@ -241,7 +241,8 @@ size_t kda_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_h
  * "segments" is the first pass of the within-GPU sequence split, "plan" the chunk
  * table, launched only for packs of more than 64 samples or with the split) or
  * "scan" (single-kernel scans); kda_backward records "bwd_plan", "bwd_prep",
- * "bwd_state", "bwd_dstate" and "bwd_grad". kda_timing_read waits for the recorded events of `kernel`,
+ * "bwd_state", "bwd_dstate" and "bwd_grad", plus "bwd_state_seg" and "bwd_dstate_seg" (the
+ * first passes of the chains' sequence split, for packs of few long samples). kda_timing_read waits for the recorded events of `kernel`,
  * returns their count and summed duration in milliseconds, and drops them.
  * Process-wide state guarded by a mutex; returns KDA_E_NULL on NULL arguments and
  * KDA_E_HIP if an event cannot be read (all records are then dropped).

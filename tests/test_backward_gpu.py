@@ -82,6 +82,12 @@ CASES = [
     ("bf16_norm", (129, 0, 64, 200, 1, 63), 2, 128, 128, "bf16", True, True),
     ("f32_d64", (100, 37, 0, 250), 2, 64, 64, "f32", False, True),
     ("f32_d128_norm", (70, 130), 2, 128, 128, "f32", True, True),
+    # few long samples: the chains run as two passes over segments of 64 chunks
+    # (157, 0, 10 and 66 chunks: three segments, an empty sample, one, two)
+    ("bf16_split", (5000, 0, 300, 2100), 2, 128, 128, "bf16", False, True),
+    ("f32_split", (2500, 2200), 1, 64, 64, "f32", False, True),
+    ("bf16_split_norm_d64_128", (4200,), 1, 64, 128, "bf16", True, True),
+    ("bf16_split_zero_state", (4200, 33), 1, 128, 128, "bf16", False, False),
 ]
 
 
@@ -143,6 +149,24 @@ def test_backward_timing_records_each_kernel():
     finally:
         kda.timing_enable(False)
     for name in ("bwd_plan", "bwd_prep", "bwd_state", "bwd_dstate", "bwd_grad"):
+        n, ms = kda.timing_read(name)
+        assert n == 1 and ms > 0, (name, n, ms)
+    torch.cuda.synchronize()
+
+
+def test_backward_split_timing_records_each_kernel():
+    import torch
+    from delta_rule_recurrent_kda_amd import kda
+    spec = inputs.KdaSpec("bwd_split_timing", (4200,), 1, 128, 128, "bf16", (0.001, 0.1), 7373)
+    gu.log("case backward split timing")
+    a = inputs.generate(spec)
+    do, _, _ = _draw_grads(spec, 77)
+    kda.timing_enable(True)
+    try:
+        _run(spec, a, do, None, None, False)
+    finally:
+        kda.timing_enable(False)
+    for name in ("bwd_plan", "bwd_prep", "bwd_state_seg", "bwd_state", "bwd_dstate_seg", "bwd_dstate", "bwd_grad"):
         n, ms = kda.timing_read(name)
         assert n == 1 and ms > 0, (name, n, ms)
     torch.cuda.synchronize()
