@@ -209,9 +209,47 @@ def cpu_baseline(spec, a):
     t0 = time.perf_counter()
     oracle.forward(f["q"], f["k"], f["v"], f["log_alpha"], f["beta"], a["cu_seqlens"], threads=cores)
     dt = time.perf_counter() - t0
+    # one thread on one (sample, head) unit of the image workload, a rate that compares hosts
+    s2 = inputs.config(WORKLOADS["image4"])
+    a2 = inputs.generate(s2, heads=[0])
+    L = s2.seq_lens[0]
+    f2 = {x: inputs.to_f64(np.ascontiguousarray(a2[x][:L, :1]), s2.dtype) for x in ("q", "k", "v", "log_alpha", "beta")}
+    t1 = time.perf_counter()
+    oracle.forward(f2["q"], f2["k"], f2["v"], f2["log_alpha"], f2["beta"], np.array([0, L], np.int32), threads=1)
+    d1 = time.perf_counter() - t1
     return {"value": spec.head_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"whole workload: {len(spec.seq_lens)} samples x {spec.heads} heads, "
-                      f"{spec.head_tokens} head-tokens, fp64 token recurrence, {dt:.2f} s wall"}
+                      f"{spec.head_tokens} head-tokens, fp64 token recurrence, {dt:.2f} s wall",
+            "single_thread": {"value": L / d1, "unit": "tokens/s", "cores": 1,
+                              "sample": f"image workload, sample 0, head 0: {L} tokens, d = {s2.dk}, {d1:.3f} s"}}
+
+
+def measured_ceilings(dev):
+    """Rates this GPU reaches on plain work: a 1 GiB device copy (read + write bytes) and a
+    8192^3 bf16 matrix product (the vendor GEMM through torch, contiguous operands)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    a = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
+    b = torch.randn((8192, 8192), device=dev).to(torch.bfloat16).contiguous()
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    tc = timed(lambda: dst.copy_(src), 10)
+    tg = timed(lambda: torch.matmul(a, b), 10)
+    del src, dst, a, b
+    return {"bw_copy_GBs": 2 * n / tc / 1e9, "mfma_bf16_gemm_TFLOPs": 2 * 8192 ** 3 / tg / 1e12}
 
 
 def flushed_steps(step, stream, dev, n: int) -> float:
@@ -404,7 +442,7 @@ def main():
     wall = time.perf_counter() - w0
     kda.timing_enable(False)
     ms_per_step = wall * 1e3 / args.steps
-    flushed = flushed_steps(step, stream, dev, 10)
+    flushed = flushed_steps(step, stream, dev, 20)
     kernels = {}
     for name in KERNEL_SYMBOL:
         n, ms = kda.timing_read(name)
@@ -453,6 +491,11 @@ def main():
         "mfma": {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s", "frac": tflops / mfma_peak,
                  "flops_per_launch": flops},
     }
+    ceil = measured_ceilings(dev)
+    ceil.update({"roofline_frac_of_copy": achieved / ceil["bw_copy_GBs"],
+                 "path_frac_of_copy": path_gbs / ceil["bw_copy_GBs"],
+                 "mfma_frac_of_gemm": tflops / ceil["mfma_bf16_gemm_TFLOPs"]})
+    rec["measured_ceilings"] = ceil
     if not args.no_backward:
         rec["backward"] = backward_bench(args, spec, t, cu, dev)
     if not args.no_conv:
