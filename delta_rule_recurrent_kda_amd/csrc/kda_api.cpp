@@ -32,6 +32,30 @@ kda_status fail(kda_status s, const char* fmt, ...)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// A caller's array as a byte range; a NULL pointer or an empty range overlaps nothing.
+struct Span {
+    const void* p;
+    int64_t bytes;
+    const char* name;
+};
+bool overlap(const Span& a, const Span& b)
+{
+    if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a.p), y = reinterpret_cast<uintptr_t>(b.p);
+    return x < y + uintptr_t(b.bytes) && y < x + uintptr_t(a.bytes);
+}
+// every output against every input and against the other outputs
+kda_status check_overlaps(const Span* outs, int nout, const Span* ins, int nin)
+{
+    for (int o = 0; o < nout; ++o) {
+        for (int i = 0; i < nin; ++i)
+            if (overlap(outs[o], ins[i])) return fail(KDA_E_SHAPE, "%s overlaps %s", outs[o].name, ins[i].name);
+        for (int j = o + 1; j < nout; ++j)
+            if (overlap(outs[o], outs[j])) return fail(KDA_E_SHAPE, "%s overlaps %s", outs[o].name, outs[j].name);
+    }
+    return KDA_OK;
+}
+
 bool validate_env()
 {
     const char* e = std::getenv("KDA_VALIDATE");
@@ -206,14 +230,19 @@ kda_status kda_backward(const void* q, const void* k, const void* v, const void*
                            "d_initial_state"};
     for (int i = 0; i < 8; ++i)
         if (ptrs[i] && !aligned16(ptrs[i])) return fail(KDA_E_ALIGN, "%s is not 16-byte aligned", names[i]);
-    const void* ins[] = {q, k, v, log_alpha, beta, cu_seqlens, d_out, initial_state, d_final_state};
-    const void* outs[] = {dq, dk, dv, dlog_alpha, dbeta, d_initial_state};
-    for (const void* o : outs)
-        for (const void* i : ins)
-            if (o && o == i) return fail(KDA_E_SHAPE, "a gradient output aliases an input");
-    for (int i = 0; i < 6; ++i)
-        for (int j = i + 1; j < 6; ++j)
-            if (outs[i] && outs[i] == outs[j]) return fail(KDA_E_SHAPE, "two gradient outputs alias");
+    {
+        const int64_t es = dtype == KDA_BF16 ? 2 : 4, th = total_tokens * num_heads;
+        const int64_t st_bytes = int64_t(num_seqs) * num_heads * d_k * d_v * 4;
+        const Span ins[] = {{q, th * d_k * es, "q"}, {k, th * d_k * es, "k"}, {v, th * d_v * es, "v"},
+                            {log_alpha, th * d_k * es, "log_alpha"}, {beta, th * es, "beta"},
+                            {cu_seqlens, (int64_t(num_seqs) + 1) * 4, "cu_seqlens"},
+                            {d_out, th * d_v * es, "d_out"}, {initial_state, st_bytes, "initial_state"},
+                            {d_final_state, st_bytes, "d_final_state"}};
+        const Span outs[] = {{dq, th * d_k * es, "dq"}, {dk, th * d_k * es, "dk"}, {dv, th * d_v * es, "dv"},
+                             {dlog_alpha, th * d_k * es, "dlog_alpha"}, {dbeta, th * es, "dbeta"},
+                             {d_initial_state, st_bytes, "d_initial_state"}};
+        if ((st = check_overlaps(outs, 6, ins, 9)) != KDA_OK) return st;
+    }
     if (num_seqs == 0) return KDA_OK;
 
     std::unique_lock<std::mutex> lk(g_timing.mu);
@@ -267,7 +296,18 @@ kda_status kda_short_conv(const void* x, const float* w_text, const float* w_vis
     if (!cu_seqlens || !text_len || !grid) return fail(KDA_E_NULL, "cu_seqlens, text_len or grid is NULL");
     if (total_tokens > 0 && (!x || !y || !w_text || !w_vis)) return fail(KDA_E_NULL, "a tensor pointer is NULL");
     if ((x && !aligned16(x)) || (y && !aligned16(y))) return fail(KDA_E_ALIGN, "x or y is not 16-byte aligned");
-    if (x && x == y) return fail(KDA_E_SHAPE, "y aliases x");
+    {
+        const int64_t es = dtype == KDA_BF16 ? 2 : 4;
+        const Span ins[] = {{x, total_tokens * channels * es, "x"},
+                            {w_text, int64_t(k_text) * channels * 4, "w_text"},
+                            {w_vis, int64_t(k_t) * k_h * k_w * channels * 4, "w_vis"},
+                            {cu_seqlens, (int64_t(num_seqs) + 1) * 4, "cu_seqlens"},
+                            {text_len, int64_t(num_seqs) * 4, "text_len"},
+                            {grid, int64_t(num_seqs) * 12, "grid"}};
+        const Span outs[] = {{y, total_tokens * channels * es, "y"}};
+        const kda_status st = check_overlaps(outs, 1, ins, 6);
+        if (st != KDA_OK) return st;
+    }
     if (num_seqs == 0 || total_tokens == 0) return KDA_OK;
     if (validate_env()) {
         std::vector<int32_t> hc(size_t(num_seqs) + 1), ht(num_seqs), hg(size_t(num_seqs) * 3);
@@ -382,10 +422,17 @@ kda_status check_args(const void* q, const void* k, const void* v, const void* l
     for (int i = 0; i < 9; ++i)
         if (ptrs[i] && !aligned16(ptrs[i]))
             return fail(KDA_E_ALIGN, "%s is not 16-byte aligned", names[i]);
-    if (out && (out == q || out == k || out == v || out == log_alpha || out == beta))
-        return fail(KDA_E_SHAPE, "out aliases an input");
-    if (initial_state && final_state && static_cast<const void*>(initial_state) == final_state)
-        return fail(KDA_E_SHAPE, "final_state aliases initial_state");
+    {
+        const int64_t es = dtype == KDA_BF16 ? 2 : 4, th = total_tokens * num_heads;
+        const int64_t st_bytes = int64_t(num_seqs) * num_heads * d_k * d_v * 4;
+        const Span ins[] = {{q, th * d_k * es, "q"}, {k, th * d_k * es, "k"}, {v, th * d_v * es, "v"},
+                            {log_alpha, th * d_k * es, "log_alpha"}, {beta, th * es, "beta"},
+                            {cu_seqlens, (int64_t(num_seqs) + 1) * 4, "cu_seqlens"},
+                            {initial_state, st_bytes, "initial_state"}};
+        const Span outs[] = {{out, th * d_v * es, "out"}, {final_state, st_bytes, "final_state"}};
+        const kda_status st = check_overlaps(outs, 2, ins, 7);
+        if (st != KDA_OK) return st;
+    }
     if (num_seqs == 0) return KDA_OK;
     if (initial_state && (dtype != KDA_BF16 || variant_env() != Variant::Wy))
         return fail(KDA_E_UNSUPPORTED, "initial_state is supported for bf16 data on the default scan");

@@ -290,6 +290,12 @@ def short_conv(x, w_text, w_vis, cu_seqlens, text_len, grid, y=None,
         raise ValueError("x must be a contiguous GPU tensor")
     if y is None:
         y = torch.empty_like(x)
+    elif y.dtype != x.dtype or y.shape != x.shape or not y.is_cuda or not y.is_contiguous():
+        raise ValueError("y must be a contiguous GPU tensor of the shape and dtype of x")
+    for name, t in (("w_text", w_text), ("w_vis", w_vis), ("cu_seqlens", cu_seqlens), ("text_len", text_len),
+                    ("grid", grid), ("y", y)):
+        if t.device != x.device:
+            raise ValueError(f"{name} is on {t.device}, x on {x.device}")
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     st = short_conv_raw(_ptr(x), _ptr(w_text), _ptr(w_vis), _ptr(cu_seqlens), _ptr(text_len), _ptr(grid),

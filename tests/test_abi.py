@@ -57,8 +57,8 @@ def test_status_strings(lib):
 
 def _call(kw):
     from delta_rule_recurrent_kda_amd import kda
-    a = dict(q=0x1000, k=0x2000, v=0x3000, log_alpha=0x4000, beta=0x5000, cu_seqlens=0x6000,
-             out=0x7000, final_state=0x8000, total_tokens=128, num_seqs=1, num_heads=2, d_k=128,
+    a = dict(q=0x100000, k=0x200000, v=0x300000, log_alpha=0x400000, beta=0x500000, cu_seqlens=0x600000,
+             out=0x700000, final_state=0x800000, total_tokens=128, num_seqs=1, num_heads=2, d_k=128,
              d_v=128, dtype=kda.KDA_BF16, stream=None)
     a.update(kw)
     st = kda.kda_forward_raw(**a)
@@ -75,9 +75,11 @@ def _call(kw):
     (dict(cu_seqlens=None), 1),
     (dict(q=None), 1),
     (dict(out=None), 1),
-    (dict(v=0x3008), 4),
-    (dict(final_state=0x8004), 4),
-    (dict(out=0x1000), 3),
+    (dict(v=0x300008), 4),
+    (dict(final_state=0x800004), 4),
+    (dict(out=0x100000), 3),
+    (dict(out=0x108000), 3),                           # out starts inside q
+    (dict(final_state=0x708000), 3),                   # final_state overlaps out
     (dict(total_tokens=1 << 26, num_heads=64), 5),
 ])
 def test_bad_arguments_are_rejected_without_launch(lib, kw, code):
@@ -93,8 +95,8 @@ def test_empty_batch_is_a_no_op(lib):
 
 def _call_from_state(kw):
     from delta_rule_recurrent_kda_amd import kda
-    a = dict(q=0x1000, k=0x2000, v=0x3000, log_alpha=0x4000, beta=0x5000, cu_seqlens=0x6000,
-             initial_state=0x9000, out=0x7000, final_state=0x8000, total_tokens=128, num_seqs=1,
+    a = dict(q=0x100000, k=0x200000, v=0x300000, log_alpha=0x400000, beta=0x500000, cu_seqlens=0x600000,
+             initial_state=0x900000, out=0x700000, final_state=0x800000, total_tokens=128, num_seqs=1,
              num_heads=2, d_k=128, d_v=128, dtype=kda.KDA_BF16, stream=None)
     a.update(kw)
     st = kda.kda_forward_from_state_raw(**a)
@@ -102,8 +104,8 @@ def _call_from_state(kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(initial_state=0x9004), 4),                 # misaligned
-    (dict(final_state=0x9000), 3),                   # final_state aliases initial_state
+    (dict(initial_state=0x900004), 4),                 # misaligned
+    (dict(final_state=0x900000), 3),                   # final_state aliases initial_state
     (dict(dtype=0), 5),                              # fp32 scan takes no initial state
     (dict(d_k=96), 5),
     (dict(q=None), 1),
@@ -122,8 +124,8 @@ def test_from_state_on_single_kernel_variant_is_unsupported(lib, monkeypatch):
 
 def _call_ex(kw):
     from delta_rule_recurrent_kda_amd import kda
-    a = dict(q=0x1000, k=0x2000, v=0x3000, log_alpha=0x4000, beta=0x5000, cu_seqlens=0x6000,
-             initial_state=None, out=0x7000, final_state=0x8000, total_tokens=128, num_seqs=1,
+    a = dict(q=0x100000, k=0x200000, v=0x300000, log_alpha=0x400000, beta=0x500000, cu_seqlens=0x600000,
+             initial_state=None, out=0x700000, final_state=0x800000, total_tokens=128, num_seqs=1,
              num_heads=2, d_k=128, d_v=128, dtype=kda.KDA_BF16, options=kda.KDA_OPT_QK_L2NORM,
              stream=None)
     a.update(kw)
@@ -134,10 +136,10 @@ def _call_ex(kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(options=2), 5),                            # unknown option bit
     (dict(options=0x80000001), 5),
-    (dict(initial_state=0x9000, dtype=0), 5),        # fp32 scan takes no initial state
+    (dict(initial_state=0x900000, dtype=0), 5),        # fp32 scan takes no initial state
     (dict(d_v=96), 5),
     (dict(k=None), 1),
-    (dict(out=0x2000), 3),
+    (dict(out=0x200000), 3),
 ])
 def test_forward_ex_bad_arguments_are_rejected_without_launch(lib, kw, code):
     st, msg = _call_ex(kw)
@@ -158,8 +160,8 @@ def test_qk_norm_on_single_kernel_variant_is_unsupported(lib, monkeypatch):
 
 def _call_conv(kw):
     from delta_rule_recurrent_kda_amd import kda
-    a = dict(x=0x1000, w_text=0x2000, w_vis=0x3000, cu_seqlens=0x4000, text_len=0x5000, grid=0x6000,
-             y=0x7000, total_tokens=100, num_seqs=1, channels=64, k_text=4, k_t=3, k_h=3, k_w=3,
+    a = dict(x=0x100000, w_text=0x200000, w_vis=0x300000, cu_seqlens=0x400000, text_len=0x500000, grid=0x600000,
+             y=0x700000, total_tokens=100, num_seqs=1, channels=64, k_text=4, k_t=3, k_h=3, k_w=3,
              dtype=kda.KDA_BF16, stream=None)
     a.update(kw)
     st = kda.short_conv_raw(**a)
@@ -176,8 +178,10 @@ def _call_conv(kw):
     (dict(total_tokens=-1), 3),
     (dict(grid=None), 1),
     (dict(x=None), 1),
-    (dict(y=0x7008), 4),
-    (dict(y=0x1000), 3),
+    (dict(y=0x700008), 4),
+    (dict(y=0x100000), 3),
+    (dict(y=0x100800), 3),                             # y starts inside x
+    (dict(y=0x5fff00), 3),                             # y runs into grid
     (dict(total_tokens=1 << 25), 5),
 ])
 def test_short_conv_bad_arguments_are_rejected_without_launch(lib, kw, code):
@@ -188,9 +192,9 @@ def test_short_conv_bad_arguments_are_rejected_without_launch(lib, kw, code):
 
 def _call_bwd(kw):
     from delta_rule_recurrent_kda_amd import kda
-    a = dict(q=0x1000, k=0x2000, v=0x3000, log_alpha=0x4000, beta=0x5000, cu_seqlens=0x6000,
-             initial_state=None, d_out=0x7000, d_final_state=None, dq=0x8000, dk=0x9000, dv=0xA000,
-             dlog_alpha=0xB000, dbeta=0xC000, d_initial_state=None, total_tokens=128, num_seqs=1,
+    a = dict(q=0x100000, k=0x200000, v=0x300000, log_alpha=0x400000, beta=0x500000, cu_seqlens=0x600000,
+             initial_state=None, d_out=0x700000, d_final_state=None, dq=0x800000, dk=0x900000, dv=0xa00000,
+             dlog_alpha=0xb00000, dbeta=0xc00000, d_initial_state=None, total_tokens=128, num_seqs=1,
              num_heads=2, d_k=128, d_v=128, dtype=kda.KDA_BF16, options=0, stream=None)
     a.update(kw)
     st = kda.kda_backward_raw(**a)
@@ -203,10 +207,12 @@ def _call_bwd(kw):
     (dict(d_k=32), 5),
     (dict(d_out=None), 1),
     (dict(dbeta=None), 1),
-    (dict(dv=0xA008), 4),
-    (dict(dq=0x1000), 3),                            # a gradient aliases an input
-    (dict(dk=0x8000), 3),                            # two gradients alias
-    (dict(d_initial_state=0x6000), 3),
+    (dict(dv=0xa00008), 4),
+    (dict(dq=0x100000), 3),                            # a gradient aliases an input
+    (dict(dk=0x800000), 3),                            # two gradients alias
+    (dict(d_initial_state=0x600000), 3),
+    (dict(dk=0x808000), 3),                            # dk starts inside dq
+    (dict(dbeta=0x5ffff0), 3),                         # dbeta runs into cu_seqlens
 ])
 def test_backward_bad_arguments_are_rejected_without_launch(lib, kw, code):
     st, msg = _call_bwd(kw)
