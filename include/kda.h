@@ -61,7 +61,7 @@ typedef enum {
  *   cu_seqlens      : [num_seqs + 1] int32, 0 = c_0 <= c_1 <= ... <= c_N = total_tokens;
  *                     sample n owns tokens [c_n, c_{n+1}); zero-length samples allowed.
  *                     A dense [B][L] batch passes {0, L, 2L, ..., B*L}.
- *   out             : [total_tokens][num_heads][d_v]   dtype (written; may not alias inputs)
+ *   out             : [total_tokens][num_heads][d_v]   dtype (written; may not overlap an input)
  *   final_state     : [num_seqs][num_heads][d_k][d_v] fp32, rows = key channels, the state
  *                     after each sample's last token (zeros for an empty sample). May be NULL.
  *
@@ -110,7 +110,7 @@ kda_status kda_forward(const void *q, const void *k, const void *v, const void *
  * floating-point rounding.
  *
  *   initial_state : [num_seqs][num_heads][d_k][d_v] fp32 DEVICE pointer, rows = key
- *                   channels, 16-byte aligned; read only; may not alias final_state.
+ *                   channels, 16-byte aligned; read only; may not overlap final_state.
  *                   NULL means zero states (then identical to kda_forward).
  * All other arguments, errors and execution as kda_forward. Supported for bf16 data
  * on the default scan; KDA_E_UNSUPPORTED otherwise (non-NULL initial_state).
@@ -170,7 +170,7 @@ kda_status kda_forward_ex(const void *q, const void *k, const void *v, const voi
  *   d_initial_state : [num_seqs][num_heads][d_k][d_v] fp32 or NULL (not written); the
  *                     gradient with respect to the initial states (equal to d_final_state
  *                     for an empty sample)
- * Outputs may not alias inputs or each other. Arithmetic is fp32 throughout (fp32
+ * No output may overlap an input or another output (byte ranges; KDA_E_SHAPE). Arithmetic is fp32 throughout (fp32
  * MFMA), over 32-token chunks; results in the data dtype, rounded to nearest-even.
  * Same size limits as kda_forward. Execution: enqueued on `stream`; takes a workspace of
  * kda_backward_workspace_bytes(...) bytes (chunk operands and the per-chunk state and
@@ -207,7 +207,7 @@ size_t kda_backward_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int3
  * other, and no sample reads another. The pages fix neither the kernel sizes nor a bias or
  * activation; there is none, and the sizes are arguments.
  *
- *   x, y        : [total_tokens][channels] dtype, DEVICE, 16-byte aligned; y may not alias x
+ *   x, y        : [total_tokens][channels] dtype, DEVICE, 16-byte aligned; y may not overlap an input
  *   w_text      : [k_text][channels] fp32;  w_vis : [k_t][k_h][k_w][channels] fp32 (DEVICE)
  *   cu_seqlens  : [num_seqs + 1] int32; text_len : [num_seqs] int32; grid : [num_seqs][3] int32
  *                 (DEVICE); text_len[n] + T*H*W must equal the sample's length (checked on the
