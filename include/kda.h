@@ -170,12 +170,15 @@ kda_status kda_forward_ex(const void *q, const void *k, const void *v, const voi
  *   d_initial_state : [num_seqs][num_heads][d_k][d_v] fp32 or NULL (not written); the
  *                     gradient with respect to the initial states (equal to d_final_state
  *                     for an empty sample)
- * No output may overlap an input or another output (byte ranges; KDA_E_SHAPE). Arithmetic is fp32 throughout (fp32
- * MFMA), over 32-token chunks; results in the data dtype, rounded to nearest-even.
- * Same size limits as kda_forward. Execution: enqueued on `stream`; takes a workspace of
+ * No output may overlap an input or another output (byte ranges; KDA_E_SHAPE).
+ * Arithmetic is fp32 throughout (fp32 MFMA), over 32-token chunks; results in the data
+ * dtype, rounded to nearest-even. Same size limits as kda_forward. For packs of few long
+ * samples the chains run as two passes over segments of the samples (same results up to
+ * rounding). Execution: enqueued on `stream`; takes a workspace of
  * kda_backward_workspace_bytes(...) bytes (chunk operands and the per-chunk state and
- * state gradient, about 5 KB per token and head at d = 128) from the device's default
- * stream-ordered pool, returned on `stream` after the kernels. Errors as kda_forward.
+ * state gradient, about 5 KB per token and head at d = 128, plus per-segment summaries
+ * when the chains are split) from the device's default stream-ordered pool, returned on
+ * `stream` after the kernels. Errors as kda_forward.
  */
 kda_status kda_backward(const void *q, const void *k, const void *v, const void *log_alpha,
                         const void *beta, const int32_t *cu_seqlens, const float *initial_state,
