@@ -743,6 +743,10 @@ template <int DK, int DV> struct GradLds {
     float x[kBC * LV], dout[kBC * LV], vn[kBC * LV], dvn[kBC * LV], sblk[kBC * LV];
     float m[kBC * kLC], t[kBC * kLC], p[kBC * kLC], dp[kBC * kLC], dt[kBC * kLC];
     float gam[DK], dgam[DK], beta[kBC], dbeta[kBC], qinv[kBC], kinv[kBC];
+    // partial sums of dgamma and db, one writer per slot, added in a fixed order (no
+    // atomics, so the gradients are bitwise reproducible)
+    float dgam_p[3][DK];                // dVn pass, token tiles 0 and 1; the state pass
+    float dbeta_p[4][kBC];              // one per wave
     static_assert(5 * kBC * LV + 5 * kBC * kLC >= 3 * kBC * LK, "flat area holds three [C][DK] arrays");
 };
 
@@ -826,8 +830,6 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
     pd.load(d_out, t0, nrow, H, h, 0, DV);
     StateBlock<DV> sb;
     sb.load(Sg, 0);
-    if (tid < DK) sm.dgam[tid] = 0.f;
-    if (tid < kBC) sm.dbeta[tid] = 0.f;
     const ChunkLds L{sm.qh, sm.kh, sm.kc, sm.m, sm.t, sm.p, sm.gam, sm.beta, sm.qinv, sm.kinv};
     chunk_operands<E, DK, NORM>(L, q, k, la, beta, t0, nrow, H, h);   // ends with a barrier
     pv.put(sm.x, LV, nrow);
@@ -937,7 +939,9 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
             float part = 0.f;
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) part += acc[v4] * sm.kc[(16 * ti + 4 * g + v4) * LK + cc];
-            atomicAdd(&sm.dgam[cc], part);
+            part += __shfl_xor(part, 16);       // the tile's 16 rows, held by lanes r + 16 g'
+            part += __shfl_xor(part, 32);
+            if (g == 0) sm.dgam_p[ti][cc] = part;
             if (ti == 0) {
 #pragma unroll
                 for (int v4 = 0; v4 < 4; ++v4) aKc[kb >> 1][v4] += acc[v4] * gm;
@@ -971,6 +975,7 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
             sm.dp[i * kLC + j] = i >= j ? acc[v4] : 0.f;
         }
     }
+    float dbw[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};   // this wave's db, rows 16 ti + 4 g + v4
 #pragma unroll
     for (int mm = 0; mm < XPW; ++mm) {
         int ti, tj;
@@ -985,9 +990,15 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
             float part = acc[v4] * sm.x[row * LV + 16 * tj + r];
 #pragma unroll
             for (int sh = 1; sh < 16; sh <<= 1) part += __shfl_xor(part, sh);
-            if (r == 0) atomicAdd(&sm.dbeta[row], part);
+            dbw[4 * mm / NVT][v4] += part;     // = ti (the waves' tiles never straddle a row tile)
             adx[mm][v4] = sm.beta[row] * acc[v4];
         }
+    }
+    if (r == 0) {
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) sm.dbeta_p[wave][16 * ti + 4 * g + v4] = dbw[ti][v4];
     }
     __syncthreads();
     // ---- dX over Vn (dead); dT = dVn X^T diag(b) ----
@@ -1037,7 +1048,7 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
             float part = da * sm.m[i * kLC + s];
 #pragma unroll
             for (int sh = 1; sh < 16; sh <<= 1) part += __shfl_xor(part, sh);
-            if (r == 0) atomicAdd(&sm.dbeta[i], part);
+            if (r == 0) sm.dbeta_p[wave][i] += part;
         }
     }
     __syncthreads();
@@ -1079,7 +1090,7 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
 #pragma unroll
                 for (int sh = 1; sh < StateBlock<DV>::PR; sh <<= 1) part += __shfl_xor(part, sh);
                 const int pc = tid + j * kBT;
-                if (pc % StateBlock<DV>::PR == 0) atomicAdd(&sm.dgam[32 * kb + pc / StateBlock<DV>::PR], part);
+                if (pc % StateBlock<DV>::PR == 0) sm.dgam_p[2][32 * kb + pc / StateBlock<DV>::PR] = part;
             }
             __syncthreads();
             if (kb + 1 < NKB) {
@@ -1105,9 +1116,11 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
             __syncthreads();
         }
     }
-    // ---- dv = dX, db ----
+    // ---- dv = dX, db (the waves' parts in a fixed order); dgamma likewise ----
     store_rows<E, DV>(dv, sm.vn, LV, t0, nrow, H, h);
-    if (tid < nrow) stf(dbeta + (t0 + tid) * H + h, sm.dbeta[tid]);
+    if (tid < nrow)
+        stf(dbeta + (t0 + tid) * H + h, ((sm.dbeta_p[0][tid] + sm.dbeta_p[1][tid]) + sm.dbeta_p[2][tid]) + sm.dbeta_p[3][tid]);
+    if (tid < DK) sm.dgam[tid] = (sm.dgam_p[0][tid] + sm.dgam_p[1][tid]) + sm.dgam_p[2][tid];
     __syncthreads();
 
     // ---- through the decays: G again (flat area 0), then dQ, dK, dG ----

@@ -178,7 +178,8 @@ kda_status kda_forward_ex(const void *q, const void *k, const void *v, const voi
  * kda_backward_workspace_bytes(...) bytes (chunk operands and the per-chunk state and
  * state gradient, about 5 KB per token and head at d = 128, plus per-segment summaries
  * when the chains are split) from the device's default stream-ordered pool, returned on
- * `stream` after the kernels. Errors as kda_forward.
+ * `stream` after the kernels. Results are bitwise reproducible for identical inputs, sizes
+ * and device (partial sums are added in a fixed order, no atomics). Errors as kda_forward.
  */
 kda_status kda_backward(const void *q, const void *k, const void *v, const void *log_alpha,
                         const void *beta, const int32_t *cu_seqlens, const float *initial_state,

@@ -170,3 +170,16 @@ def test_backward_split_timing_records_each_kernel():
         n, ms = kda.timing_read(name)
         assert n == 1 and ms > 0, (name, n, ms)
     torch.cuda.synchronize()
+
+
+def test_backward_bitwise_deterministic():
+    """Two runs on the same inputs give the same gradients bit for bit (the partial sums of
+    dbeta and dgamma are added in a fixed order), also with the chains split."""
+    spec = inputs.KdaSpec("bwd_det", (300, 77, 1000, 4200), 1, 128, 128, "bf16", (0.001, 0.1), 7474)
+    gu.log("case backward determinism")
+    a = inputs.generate(spec)
+    do, dfs, s0 = _draw_grads(spec, 78)
+    g1 = _run(spec, a, do, dfs, s0, False)
+    g2 = _run(spec, a, do, dfs, s0, False)
+    for name, x, y in zip(NAMES, g1, g2):
+        assert np.array_equal(x, y), name
