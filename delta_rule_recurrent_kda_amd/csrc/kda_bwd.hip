@@ -233,6 +233,40 @@ struct ChunkLds {
     float *qinv, *kinv;     // [C]: 1/|q_t|, 1/|k_t| (1 without normalisation)
 };
 
+// Cumulative sums down the C = 32 rows of a [C][ld] fp32 LDS array on fp32 MFMA, as a
+// product with a triangular ones matrix: UPPER = false gives the inclusive prefix sum
+// G[i] = sum_{k <= i} X[k], UPPER = true the suffix sum over the rows k >= i, k < nrow.
+// Wave w takes the column tiles w * NCT / 4 ..; lane (r, g) receives the sums of rows
+// 16 ti + 4 g + v, column 16 tj + r in out[ti][tj'][v] (tj' the wave's tile index).
+template <int NCT, bool UPPER>
+__device__ __forceinline__ void tri_cumsum(const float* __restrict__ x, int ld, int nrow, int wave, int r, int g,
+                                           f32x4 (&out)[2][NCT / 4]) {
+#pragma unroll
+    for (int u = 0; u < NCT / 4; ++u) {
+        const int tj = wave * (NCT / 4) + u;
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int k0 = UPPER ? 16 * ti : 0; k0 < (UPPER ? kBC : 16 * ti + 16); k0 += 4) {
+                const int i = 16 * ti + r, kk = k0 + g;
+                const float a = UPPER ? ((kk >= i && kk < nrow) ? 1.f : 0.f) : (kk <= i ? 1.f : 0.f);
+                acc = mma4(a, x[kk * ld + 16 * tj + r], acc);
+            }
+            out[ti][u] = acc;
+        }
+    }
+}
+
+// X Y from accumulator tiles of X^T and Y (16 x 16, fp32): with k = 4g + s in step s,
+// element s of a tile is directly the operand
+__device__ __forceinline__ f32x4 mm16(const f32x4& xt, const f32x4& y) {
+    f32x4 c = zero4();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(xt[s], y[s], c, 0, 0, 0);
+    return c;
+}
+
 template <typename E, int DK, bool NORM>
 __device__ void chunk_operands(const ChunkLds& L, const E* __restrict__ q, const E* __restrict__ k,
                                const E* __restrict__ la, const E* __restrict__ beta, int64_t t0, int nrow,
@@ -278,20 +312,29 @@ __device__ void chunk_operands(const ChunkLds& L, const E* __restrict__ q, const
             L.kinv[tid] = 1.f;
         }
     }
-    // cumulative log decay down each key channel, the decayed operands and gamma
-    if (tid < DK) {
-        const int c = tid;
-        float G = 0.f, ex = 1.f;
-        for (int row = 0; row < kBC; ++row) {
-            G += L.kc[row * LK + c];
-            ex = expf(G);
-            const float qv = L.qh[row * LK + c] * (NORM ? L.qinv[row] : 1.f);
-            const float kv = L.kh[row * LK + c] * (NORM ? L.kinv[row] : 1.f);
-            L.qh[row * LK + c] = qv * ex;
-            L.kh[row * LK + c] = kv * ex;
-            L.kc[row * LK + c] = kv * expf(-G);
+    // cumulative log decay down each key channel (rows past the sample's end add 0), the
+    // decayed operands and gamma; each wave reads and writes only its own column tiles
+    {
+        constexpr int NCT = DK / 16;
+        f32x4 G[2][NCT / 4];
+        tri_cumsum<NCT, false>(L.kc, LK, kBC, wave, r, g, G);
+#pragma unroll
+        for (int u = 0; u < NCT / 4; ++u) {
+            const int c = 16 * (wave * (NCT / 4) + u) + r;
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int row = 16 * ti + 4 * g + v;
+                    const float ex = expf(G[ti][u][v]);
+                    const float qv = L.qh[row * LK + c] * (NORM ? L.qinv[row] : 1.f);
+                    const float kv = L.kh[row * LK + c] * (NORM ? L.kinv[row] : 1.f);
+                    L.qh[row * LK + c] = qv * ex;
+                    L.kh[row * LK + c] = kv * ex;
+                    L.kc[row * LK + c] = kv * expf(-G[ti][u][v]);
+                    if (row == kBC - 1) L.gam[c] = ex;
+                }
         }
-        L.gam[c] = ex;
     }
     __syncthreads();
     // M = Kh Kc^T and P = LowerIncl(Qh Kc^T): wave w computes tile (w >> 1, w & 1) of each
@@ -312,20 +355,45 @@ __device__ void chunk_operands(const ChunkLds& L, const E* __restrict__ q, const
         }
     }
     __syncthreads();
-    // T = (I + A)^-1, A = StrictLower(diag(b) M): thread j forward-substitutes column j
-    // (T is unit lower triangular, so entries above the diagonal stay 0)
-    if (tid < kBC) {
-        const int j = tid;
-        float col[kBC];
+    // T = (I + A)^-1, A = StrictLower(diag(b) M), by 16-row blocks:
+    //   T_bb = (I + A_bb)^-1 = (I - A)(I + A^2)(I + A^4)(I + A^8) exactly (A_bb^16 = 0),
+    //   T_10 = -T_11 A_10 T_00,  T_01 = 0.
+    if (wave < 2) {
+        const int b = wave;
+        f32x4 ac, at, id;                       // A_bb, A_bb^T, I as accumulator tiles
 #pragma unroll
-        for (int i = 0; i < kBC; ++i) {
-            float acc = 0.f;
-#pragma unroll
-            for (int s = 0; s < i; ++s) acc += L.m[i * kLC + s] * col[s];
-            col[i] = (i == j ? 1.f : 0.f) - L.beta[i] * acc;
+        for (int s = 0; s < 4; ++s) {
+            const int i = 16 * b + 4 * g + s, j = 16 * b + r;       // A_bb[4g + s][r]
+            ac[s] = 4 * g + s > r ? L.beta[i] * L.m[i * kLC + j] : 0.f;
+            const int i2 = 16 * b + r, j2 = 16 * b + 4 * g + s;     // A_bb[r][4g + s]
+            at[s] = r > 4 * g + s ? L.beta[i2] * L.m[i2 * kLC + j2] : 0.f;
+            id[s] = 4 * g + s == r ? 1.f : 0.f;
         }
+        const f32x4 b1 = mm16(at, ac), b1t = mm16(ac, at);         // A^2, (A^2)^T
+        const f32x4 b2 = mm16(b1t, b1), b2t = mm16(b1, b1t);       // A^4, (A^4)^T
+        const f32x4 b3 = mm16(b2t, b2);                            // A^8
+        const f32x4 x1t = id - at + b1t - mm16(b1, at);            // ((I - A)(I + A^2))^T
+        const f32x4 x2t = x1t + mm16(b2, x1t);                     // (.. (I + A^4))^T
+        const f32x4 tt = x2t + mm16(b3, x2t);                      // T_bb^T: T_bb[r][4g + s]
 #pragma unroll
-        for (int i = 0; i < kBC; ++i) L.t[i * kLC + j] = col[i];
+        for (int s = 0; s < 4; ++s) {
+            L.t[(16 * b + r) * kLC + 16 * b + 4 * g + s] = tt[s];
+            if (b == 0) L.t[r * kLC + 16 + 4 * g + s] = 0.f;
+        }
+    }
+    __syncthreads();
+    if (wave == 2) {
+        f32x4 a10t, t00, t11t;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            a10t[s] = L.beta[16 + r] * L.m[(16 + r) * kLC + 4 * g + s];   // A_10[r][4g + s]
+            t00[s] = L.t[(4 * g + s) * kLC + r];                         // T_00[4g + s][r]
+            t11t[s] = L.t[(16 + r) * kLC + 16 + 4 * g + s];              // T_11[r][4g + s]
+        }
+        const f32x4 z = mm16(a10t, t00);                                // A_10 T_00
+        const f32x4 t10 = mm16(t11t, z);                                // T_11 A_10 T_00
+#pragma unroll
+        for (int v = 0; v < 4; ++v) L.t[(16 + 4 * g + v) * kLC + r] = -t10[v];
     }
     __syncthreads();
 }
@@ -1129,12 +1197,16 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
     float* F2 = sm.x + 2 * kBC * LK;        // dG, then dlog a
     pl.put(F0, LK, nrow);
     __syncthreads();
-    if (tid < DK) {
-        float G = 0.f;
-        for (int row = 0; row < kBC; ++row) {
-            G += F0[row * LK + tid];
-            F0[row * LK + tid] = G;
-        }
+    {
+        f32x4 G[2][NCT / 4];
+        tri_cumsum<NCT, false>(F0, LK, kBC, wave, r, g, G);
+#pragma unroll
+        for (int u = 0; u < NCT / 4; ++u)
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    F0[(16 * ti + 4 * g + v) * LK + 16 * (wave * (NCT / 4) + u) + r] = G[ti][u][v];
     }
     __syncthreads();
 #pragma unroll
@@ -1152,11 +1224,20 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
     }
     __syncthreads();
     // dlog a: reverse cumsum of dG over the valid rows, dgamma gamma entering at the last one
-    if (tid < DK) {
-        float acc = sm.dgam[tid] * sm.gam[tid];
-        for (int row = kBC - 1; row >= 0; --row) {
-            if (row < nrow) acc += F2[row * LK + tid];
-            F2[row * LK + tid] = row < nrow ? acc : 0.f;
+    {
+        f32x4 R[2][NCT / 4];
+        tri_cumsum<NCT, true>(F2, LK, nrow, wave, r, g, R);
+#pragma unroll
+        for (int u = 0; u < NCT / 4; ++u) {
+            const int c = 16 * (wave * (NCT / 4) + u) + r;
+            const float dg = sm.dgam[c] * sm.gam[c];
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int row = 16 * ti + 4 * g + v;
+                    F2[row * LK + c] = row < nrow ? R[ti][u][v] + dg : 0.f;
+                }
         }
     }
     if constexpr (NORM) {
