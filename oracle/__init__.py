@@ -3,4 +3,4 @@
 Only tests, the smoke check and the benchmark's CPU-baseline leg may import
 this package. The product path (the HIP library and its binding) never does.
 """
-from .kda_oracle import backward, build, forward, library_path, short_conv  # noqa: F401
+from .kda_oracle import backward, build, forward, library_path, short_conv, short_conv_backward  # noqa: F401

@@ -187,6 +187,9 @@ def _load_conv(path: str):
     ip = ctypes.POINTER(ctypes.c_int32)
     lib.kda_oracle_short_conv.argtypes = [dp, dp, dp, ip, ip, ip] + [ctypes.c_int32] * 6 + [dp]
     lib.kda_oracle_short_conv.restype = ctypes.c_int
+    if hasattr(lib, "kda_oracle_short_conv_backward"):
+        lib.kda_oracle_short_conv_backward.argtypes = [dp, dp, dp, ip, ip, ip] + [ctypes.c_int32] * 6 + [dp] * 4
+        lib.kda_oracle_short_conv_backward.restype = ctypes.c_int
     return lib
 
 
@@ -223,6 +226,49 @@ def short_conv(x, w_text, w_vis, cu_seqlens, text_len, grid, _library=None):
     if rc != 0:
         raise RuntimeError("kda_oracle_short_conv failed (bad arguments)")
     return y
+
+
+def short_conv_backward(x, w_text, w_vis, cu_seqlens, text_len, grid, dy, _library=None):
+    """Reverse mode of short_conv: the gradients (dx [T, C], dw_text [kx, C], dw_vis
+    [kt, kh, kw, C]) of a loss with gradient dy [T, C] with respect to y, in fp64."""
+    global _conv_handle
+    x = np.ascontiguousarray(x, np.float64)
+    wt = np.ascontiguousarray(w_text, np.float64)
+    wv = np.ascontiguousarray(w_vis, np.float64)
+    g = np.ascontiguousarray(dy, np.float64)
+    cu = np.ascontiguousarray(cu_seqlens, np.int32)
+    tl = np.ascontiguousarray(text_len, np.int32)
+    gr = np.ascontiguousarray(grid, np.int32).reshape(-1, 3)
+    T, C = x.shape
+    N = len(cu) - 1
+    assert g.shape == x.shape and wt.shape[1] == C and wv.shape[3] == C and tl.shape == (N,) and gr.shape == (N, 3)
+    dx = np.zeros((T, C))
+    dwt = np.zeros(wt.shape)
+    dwv = np.zeros(wv.shape)
+    if _library is None:
+        if _conv_handle is None:
+            build()
+            _conv_handle = _load_conv(_CONV_LIB)
+        lib = _conv_handle
+    else:
+        lib = _library
+    P = ctypes.c_double
+    I = ctypes.c_int32
+    rc = lib.kda_oracle_short_conv_backward(_ptr(x, P), _ptr(wt, P), _ptr(wv, P), _ptr(cu, I), _ptr(tl, I),
+                                            _ptr(gr, I), N, C, wt.shape[0], wv.shape[0], wv.shape[1],
+                                            wv.shape[2], _ptr(g, P), _ptr(dx, P), _ptr(dwt, P), _ptr(dwv, P))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_short_conv_backward failed (bad arguments)")
+    return dx, dwt, dwv
+
+
+def short_conv_backward_from(path: str):
+    """short_conv_backward() bound to another build of the same C source (mutation tests)."""
+    lib = _load_conv(path)
+
+    def conv_bwd(*args, **kw):
+        return short_conv_backward(*args, _library=lib, **kw)
+    return conv_bwd
 
 
 def short_conv_from(path: str):

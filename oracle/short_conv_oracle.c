@@ -71,3 +71,58 @@ int kda_oracle_short_conv(const double *x, const double *w_text, const double *w
     }
     return 0;
 }
+
+/*
+ * The reverse mode of the same convolution. For a loss whose gradient with respect to y
+ * is dy, the gradients dx, dw_text and dw_vis. The convolution is linear in x and in the
+ * weights: every term w * x[src] that makes up an output y[t] sends dy[t] * w back to
+ * dx[src] and dy[t] * x[src] to the weight. This is that transpose, term by term, walked
+ * in the forward's own order; dx, dw_text and dw_vis are overwritten.
+ */
+int kda_oracle_short_conv_backward(const double *x, const double *w_text, const double *w_vis,
+                                   const int32_t *cu, const int32_t *text_len, const int32_t *grid,
+                                   int32_t n_seqs, int32_t C, int32_t kx, int32_t kt, int32_t kh, int32_t kw,
+                                   const double *dy, double *dx, double *dw_text, double *dw_vis)
+{
+    if (!cu || n_seqs < 0 || C <= 0 || kx < 1 || kt < 1 || kh < 1 || kw < 1 || kh % 2 == 0 || kw % 2 == 0)
+        return -1;
+    const int32_t ph = (kh - 1) / 2, pw = (kw - 1) / 2;
+    const int64_t T_all = cu[n_seqs];
+    for (int64_t e = 0; e < T_all * C; ++e) dx[e] = 0.0;
+    for (int64_t e = 0; e < (int64_t)kx * C; ++e) dw_text[e] = 0.0;
+    for (int64_t e = 0; e < (int64_t)kt * kh * kw * C; ++e) dw_vis[e] = 0.0;
+    for (int32_t n = 0; n < n_seqs; ++n) {
+        const int64_t base = cu[n], len = (int64_t)cu[n + 1] - cu[n];
+        const int64_t L = text_len[n];
+        const int64_t T = grid[3 * n], H = grid[3 * n + 1], W = grid[3 * n + 2];
+        if (L < 0 || T < 0 || H < 0 || W < 0 || L + T * H * W != len) return -1;
+        for (int64_t t = 0; t < L; ++t)
+            for (int32_t c = 0; c < C; ++c) {
+                const double g = dy[(base + t) * C + c];
+                for (int32_t ti = 0; ti < kx; ++ti)
+                    if (t - ti >= 0) {
+                        dx[(base + t - ti) * C + c] += w_text[(int64_t)ti * C + c] * g;
+                        dw_text[(int64_t)ti * C + c] += x[(base + t - ti) * C + c] * g;
+                    }
+            }
+        const int64_t v0 = base + L;
+        for (int64_t i = 0; i < T; ++i)
+            for (int64_t j = 0; j < H; ++j)
+                for (int64_t k = 0; k < W; ++k)
+                    for (int32_t c = 0; c < C; ++c) {
+                        const double g = dy[(v0 + (i * H + j) * W + k) * C + c];
+                        for (int32_t ta = 0; ta < kt; ++ta)
+                            for (int32_t tb = 0; tb < kh; ++tb)
+                                for (int32_t td = 0; td < kw; ++td) {
+                                    const int64_t si = i - ta, sj = j + tb - ph, sk = k + td - pw;
+                                    if (si < 0 || sj < 0 || sj >= H || sk < 0 || sk >= W) continue;
+                                    const int64_t src = (v0 + (si * H + sj) * W + sk) * C + c;
+                                    const int64_t wi = (((int64_t)ta * kh + tb) * kw + td) * C + c;
+                                    dx[src] += w_vis[wi] * g;
+                                    dw_vis[wi] += x[src] * g;
+                                }
+                    }
+    }
+    return 0;
+}
+
