@@ -38,6 +38,8 @@ CONV_SOURCES = ["delta_rule_recurrent_kda_amd/csrc/kda_conv.hip",
                 "delta_rule_recurrent_kda_amd/csrc/kda_device.h",
                 "delta_rule_recurrent_kda_amd/csrc/kda_internal.h"]
 CONV_KERNELS = {"conv_plan": "kda_conv_plan_kernel", "conv": "kda_short_conv_kernel"}
+CONV_BWD_KERNELS = {"conv_bwd_plan": "kda_conv_plan_kernel", "conv_dx": "kda_short_conv_kernel",
+                    "conv_dw": "kda_short_conv_dw_kernel", "conv_dw_reduce": "kda_short_conv_dw_reduce_kernel"}
 CONV_TAPS = (4, 3, 3, 3)        # text taps; visual frames x rows x columns
 WORKLOADS = {"tiny": 0, "packed8": 1, "image4": 2, "clip5s": 3, "clip30s": 4}
 CHUNK = 64
@@ -372,6 +374,7 @@ def conv_bench(args, spec, dev):
     tflops = flops / (kms * 1e-3) / 1e12
     gbs = nbytes / (kms * 1e-3) / 1e9
     sha = kernel_sha(CONV_SOURCES)
+    bwd = conv_backward_bench(args, x, wt, wv, cu, tl, gr, flops, nbytes, sha, cs.name.split("-")[0])
     return {"metric": "short convolution tokens/s (depthwise over heads x d_k channels)",
             "value": T / (ms_step * 1e-3), "unit": "tokens/s", "ms_per_step": ms_step,
             "dtype": "f32 arithmetic on bf16 data",
@@ -384,6 +387,63 @@ def conv_bench(args, spec, dev):
                          "kernel_sha": sha},
             "hbm": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                     "algorithmic_bytes": nbytes},
+            "kernels": kernels,
+            "backward": bwd}
+
+
+def conv_backward_bench(args, x, wt, wv, cu, tl, gr, fwd_flops, fwd_bytes, sha, workload):
+    """kda_short_conv_backward on the same inputs (dy random bf16): dx and both weight gradients.
+
+    dx is the forward's arithmetic on dy (same FLOPs and bytes); the weight gradients do the
+    same FMAs again (one per tap and output element) reading x and dy, plus a small partial-sum
+    buffer. The roofline entry is the dominant kernel against the fp32 vector peak."""
+    import torch
+    from delta_rule_recurrent_kda_amd import kda
+    g = torch.Generator(device=x.device)
+    g.manual_seed(8765)
+    dy = torch.randn(x.shape, device=x.device, generator=g).to(x.dtype)
+    dx = torch.empty_like(x)
+    dwt = torch.empty_like(wt)
+    dwv = torch.empty_like(wv)
+
+    def step():
+        kda.short_conv_backward(x, wt, wv, cu, tl, gr, dy, dx, dwt, dwv)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    for name in CONV_BWD_KERNELS:
+        kda.timing_read(name)
+    kda.timing_enable(True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    kda.timing_enable(False)
+    work = {"conv_dx": (fwd_flops, fwd_bytes), "conv_dw": (fwd_flops, fwd_bytes)}
+    kernels = {}
+    for name in CONV_BWD_KERNELS:
+        k, ms = kda.timing_read(name)
+        if k:
+            kernels[name] = {"launches": k, "ms_avg": ms / k}
+            if name in work:
+                f, b = work[name]
+                sec = ms / k * 1e-3
+                kernels[name].update({"flops": f, "achieved_TFLOPs": f / sec / 1e12, "algorithmic_bytes": b,
+                                      "achieved_GBs": b / sec / 1e9})
+    dom = max(work, key=lambda n: kernels[n]["ms_avg"])
+    kd = kernels[dom]
+    ms_step = wall * 1e3 / args.steps
+    return {"metric": "short convolution backward tokens/s (dx, dw_text, dw_vis)",
+            "value": x.shape[0] / (ms_step * 1e-3), "unit": "tokens/s", "ms_per_step": ms_step,
+            "dtype": "f32 arithmetic on bf16 data",
+            "roofline": {"bound": "alu", "achieved": kd["achieved_TFLOPs"], "peak": FP32_VECTOR_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": kd["achieved_TFLOPs"] / FP32_VECTOR_PEAK_TFLOPS,
+                         "traffic": traffic_for(workload, CONV_BWD_KERNELS[dom], sha),
+                         "kernel": CONV_BWD_KERNELS[dom], "kernel_ms_avg": kd["ms_avg"], "flops": kd["flops"],
+                         "kernel_sha": sha},
             "kernels": kernels}
 
 

@@ -274,12 +274,15 @@ size_t kda_backward_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int3
     return kda::bwd_workspace_bytes(total_tokens, num_seqs, num_heads, d_k, d_v);
 }
 
-kda_status kda_short_conv(const void* x, const float* w_text, const float* w_vis, const int32_t* cu_seqlens,
-                          const int32_t* text_len, const int32_t* grid, void* y, int64_t total_tokens,
-                          int32_t num_seqs, int32_t channels, int32_t k_text, int32_t k_t, int32_t k_h, int32_t k_w,
-                          kda_dtype dtype, hipStream_t stream)
+namespace {
+
+// Argument checks shared by the short convolution and its reverse mode; outs/ins are the
+// byte ranges that must not overlap. Reads the sample tables back under KDA_VALIDATE=1.
+kda_status conv_check(const void* x, const float* w_text, const float* w_vis, const int32_t* cu_seqlens,
+                      const int32_t* text_len, const int32_t* grid, int64_t total_tokens, int32_t num_seqs,
+                      int32_t channels, int32_t k_text, int32_t k_t, int32_t k_h, int32_t k_w, kda_dtype dtype,
+                      const Span* outs, int nout, const void* const* tok_outs, int ntok_out, hipStream_t stream)
 {
-    g_last_error.clear();
     if (dtype != KDA_F32 && dtype != KDA_BF16)
         return fail(KDA_E_DTYPE, "dtype %d is neither KDA_F32 nor KDA_BF16", int(dtype));
     if (total_tokens < 0 || num_seqs < 0 || channels < 1)
@@ -293,9 +296,14 @@ kda_status kda_short_conv(const void* x, const float* w_text, const float* w_vis
                     "height and width odd 1..5", k_text, k_t, k_h, k_w);
     if (total_tokens * channels >= (int64_t(1) << 31))
         return fail(KDA_E_UNSUPPORTED, "problem too large for 32-bit element offsets");
-    if (!cu_seqlens || !text_len || !grid) return fail(KDA_E_NULL, "cu_seqlens, text_len or grid is NULL");
-    if (total_tokens > 0 && (!x || !y || !w_text || !w_vis)) return fail(KDA_E_NULL, "a tensor pointer is NULL");
-    if ((x && !aligned16(x)) || (y && !aligned16(y))) return fail(KDA_E_ALIGN, "x or y is not 16-byte aligned");
+    if (!cu_seqlens || (num_seqs > 0 && (!text_len || !grid)))
+        return fail(KDA_E_NULL, "cu_seqlens, text_len or grid is NULL");
+    if (total_tokens > 0 && (!x || !w_text || !w_vis)) return fail(KDA_E_NULL, "a tensor pointer is NULL");
+    for (int i = 0; i < nout; ++i)
+        if (total_tokens > 0 && !outs[i].p) return fail(KDA_E_NULL, "%s is NULL", outs[i].name);
+    if (x && !aligned16(x)) return fail(KDA_E_ALIGN, "x is not 16-byte aligned");
+    for (int i = 0; i < ntok_out; ++i)
+        if (tok_outs[i] && !aligned16(tok_outs[i])) return fail(KDA_E_ALIGN, "a token tensor is not 16-byte aligned");
     {
         const int64_t es = dtype == KDA_BF16 ? 2 : 4;
         const Span ins[] = {{x, total_tokens * channels * es, "x"},
@@ -304,8 +312,7 @@ kda_status kda_short_conv(const void* x, const float* w_text, const float* w_vis
                             {cu_seqlens, (int64_t(num_seqs) + 1) * 4, "cu_seqlens"},
                             {text_len, int64_t(num_seqs) * 4, "text_len"},
                             {grid, int64_t(num_seqs) * 12, "grid"}};
-        const Span outs[] = {{y, total_tokens * channels * es, "y"}};
-        const kda_status st = check_overlaps(outs, 1, ins, 6);
+        const kda_status st = check_overlaps(outs, nout, ins, 6);
         if (st != KDA_OK) return st;
     }
     if (num_seqs == 0 || total_tokens == 0) return KDA_OK;
@@ -324,6 +331,23 @@ kda_status kda_short_conv(const void* x, const float* w_text, const float* w_vis
                 return fail(KDA_E_SEQLENS, "sample %d: text_len + T*H*W != its length", n);
         }
     }
+    return KDA_OK;
+}
+
+}  // namespace
+
+kda_status kda_short_conv(const void* x, const float* w_text, const float* w_vis, const int32_t* cu_seqlens,
+                          const int32_t* text_len, const int32_t* grid, void* y, int64_t total_tokens,
+                          int32_t num_seqs, int32_t channels, int32_t k_text, int32_t k_t, int32_t k_h, int32_t k_w,
+                          kda_dtype dtype, hipStream_t stream)
+{
+    g_last_error.clear();
+    const int64_t es = dtype == KDA_BF16 ? 2 : 4;
+    const Span outs[] = {{y, total_tokens * channels * es, "y"}};
+    const void* const tok_outs[] = {y};
+    kda_status st = conv_check(x, w_text, w_vis, cu_seqlens, text_len, grid, total_tokens, num_seqs, channels,
+                               k_text, k_t, k_h, k_w, dtype, outs, 1, tok_outs, 1, stream);
+    if (st != KDA_OK || num_seqs == 0 || total_tokens == 0) return st;
     std::unique_lock<std::mutex> lk(g_timing.mu);
     kda::TimingHook* th = g_timing.on ? &g_timing : nullptr;
     if (!th) lk.unlock();
@@ -338,6 +362,56 @@ kda_status kda_short_conv(const void* x, const float* w_text, const float* w_vis
     const kda::ConvArgs a{x, w_text, w_vis, cu_seqlens, text_len, grid, y, total_tokens, num_seqs, channels,
                           k_text, k_t, k_h, k_w, dtype == KDA_BF16 ? 1 : 0, stream};
     e = kda::launch_short_conv(a, ws, th);
+    const hipError_t ef = hipFreeAsync(ws, stream);
+    if (e == hipSuccess) e = ef;
+    if (e != hipSuccess) return fail(KDA_E_HIP, "launch failed: %s", hipGetErrorString(e));
+    return KDA_OK;
+}
+
+kda_status kda_short_conv_backward(const void* x, const float* w_text, const float* w_vis,
+                                   const int32_t* cu_seqlens, const int32_t* text_len, const int32_t* grid,
+                                   const void* dy, void* dx, float* dw_text, float* dw_vis, int64_t total_tokens,
+                                   int32_t num_seqs, int32_t channels, int32_t k_text, int32_t k_t, int32_t k_h,
+                                   int32_t k_w, kda_dtype dtype, hipStream_t stream)
+{
+    g_last_error.clear();
+    const int64_t es = dtype == KDA_BF16 ? 2 : 4;
+    if (total_tokens > 0 && !dy) return fail(KDA_E_NULL, "dy is NULL");
+    if (dy && !aligned16(dy)) return fail(KDA_E_ALIGN, "dy is not 16-byte aligned");
+    const Span outs[] = {{dx, total_tokens * channels * es, "dx"},
+                         {dw_text, int64_t(k_text) * channels * 4, "dw_text"},
+                         {dw_vis, int64_t(k_t) * k_h * k_w * channels * 4, "dw_vis"}};
+    const void* const tok_outs[] = {dx};
+    kda_status st = conv_check(x, w_text, w_vis, cu_seqlens, text_len, grid, total_tokens, num_seqs, channels,
+                               k_text, k_t, k_h, k_w, dtype, outs, 3, tok_outs, 1, stream);
+    if (st != KDA_OK) return st;
+    {
+        const Span dys[] = {{dy, total_tokens * channels * es, "dy"}};
+        st = check_overlaps(outs, 3, dys, 1);
+        if (st != KDA_OK) return st;
+    }
+    std::unique_lock<std::mutex> lk(g_timing.mu);
+    kda::TimingHook* th = g_timing.on ? &g_timing : nullptr;
+    if (!th) lk.unlock();
+    const kda::ConvBwdArgs a{{x, w_text, w_vis, cu_seqlens, text_len, grid, nullptr, total_tokens, num_seqs,
+                              channels, k_text, k_t, k_h, k_w, dtype == KDA_BF16 ? 1 : 0, stream},
+                             dy, dx, dw_text, dw_vis};
+    if (num_seqs == 0 || total_tokens == 0) {
+        // no tokens: the weight gradients are empty sums, written as zeros without a workspace
+        if (!dw_text || !dw_vis) return fail(KDA_E_NULL, "dw_text or dw_vis is NULL");
+        const hipError_t e = kda::launch_short_conv_backward(a, nullptr, th);
+        if (e != hipSuccess) return fail(KDA_E_HIP, "launch failed: %s", hipGetErrorString(e));
+        return KDA_OK;
+    }
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || !prepare_pool(dev))
+        return fail(KDA_E_HIP, "setting up the workspace pool: %s", hipGetErrorString(e));
+    void* ws = nullptr;
+    const size_t bytes = kda::conv_bwd_workspace_bytes(num_seqs, channels, k_text, k_t, k_h, k_w);
+    e = hipMallocAsync(&ws, bytes, stream);
+    if (e != hipSuccess) return fail(KDA_E_HIP, "workspace of %zu bytes: %s", bytes, hipGetErrorString(e));
+    e = kda::launch_short_conv_backward(a, ws, th);
     const hipError_t ef = hipFreeAsync(ws, stream);
     if (e == hipSuccess) e = ef;
     if (e != hipSuccess) return fail(KDA_E_HIP, "launch failed: %s", hipGetErrorString(e));

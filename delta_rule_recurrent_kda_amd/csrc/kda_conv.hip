@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -183,7 +185,14 @@ __global__ __launch_bounds__(1024) void kda_conv_plan_kernel(const int32_t* __re
     if (tid == 0) tile_off[0] = 0;
 }
 
-template <typename E, int KW>
+// REV = false: y = conv(x). REV = true: the input gradient, dx = conv^T(dy), with dy passed as
+// x and dx as y. The transpose of a causal-in-time, centred-in-space depthwise kernel is the
+// same kind of kernel anti-causal in time with the taps mirrored in space:
+//   dx[i,j,k] = sum_{a,b,d} w_vis[a][kh-1-b][kw-1-d] dy[i+a, j+b-(kh-1)/2, k+d-(kw-1)/2]
+//   dx[t]     = sum_i w_text[i] dy[t+i]                                     (t+i < text_len)
+// so REV mirrors the weights as it stages them and walks frames and text tokens forward.
+// dy positions past the sample's grid tokens read as zero, like x positions in the forward.
+template <typename E, int KW, bool REV>
 __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kWgPerCu))) void kda_short_conv_kernel(
     const E* __restrict__ x, const float* __restrict__ w_text, const float* __restrict__ w_vis,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ text_len, const int32_t* __restrict__ grid,
@@ -211,7 +220,14 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kWgPerCu)))
             for (int i = tid; i < ntaps * kCB; i += kCT) {
                 const int tap = i / kCB, c = kCB * cb + i % kCB;
                 float w = 0.f;
-                if (c < C) w = tap < kx ? w_text[tap * C + c] : w_vis[(tap - kx) * C + c];
+                if (c < C) {
+                    int src = tap - kx;
+                    if (REV && src >= 0) {          // mirror (b, d) within the time tap
+                        const int hw = kh * kw, a = src / hw, b = (src - a * hw) / kw, d = src - a * hw - b * kw;
+                        src = (a * kh + (kh - 1 - b)) * kw + (kw - 1 - d);
+                    }
+                    w = tap < kx ? w_text[tap * C + c] : w_vis[src * C + c];
+                }
                 wl[i] = w;
             }
             __syncthreads();
@@ -238,9 +254,9 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kWgPerCu)))
                 float acc[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-                for (int i = 0; i < kx && rel - i >= 0; ++i) {
+                for (int i = 0; i < kx && (REV ? rel + i < g.L : rel - i >= 0); ++i) {
                     float f[8];
-                    Vec8<E>::load(x + (tok - i) * C + c0, f);
+                    Vec8<E>::load(x + (REV ? tok + i : tok - i) * C + c0, f);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) acc[e] += wv[i * kCB + e] * f[e];
                 }
@@ -286,10 +302,10 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kWgPerCu)))
                 const int kk = kq + p - pw;
                 colv[p] = kk >= 0 && kk < g.Wn ? uint32_t(kk * C + c0) * sizeof(E) : kBufLimit;
             }
-            for (int a = 0; a < kt && f - a >= 0; ++a)
+            for (int a = 0; a < kt && (REV ? f + a < g.Tn : f - a >= 0); ++a)
                 for (int b = 0; b < kh; ++b) {
-                    const int jj = j + b - ph;
-                    const uint32_t roff = jj >= 0 && jj < g.Hn ? uint32_t((f - a) * g.Hn + jj) * rowb : kBufLimit;
+                    const int jj = j + b - ph, fa = REV ? f + a : f - a;
+                    const uint32_t roff = jj >= 0 && jj < g.Hn ? uint32_t(fa * g.Hn + jj) * rowb : kBufLimit;
                     typename Vec8<E>::Raw in[kSW + KW - 1];
 #pragma unroll
                     for (int p = 0; p < kSW + KW - 1; ++p) in[p] = Vec8<E>::load_buf(rs, roff + colv[p]);
@@ -314,17 +330,17 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kWgPerCu)))
                     }
                 }
         } else
-        for (int a = 0; a < kt && f - a >= 0; ++a)
+        for (int a = 0; a < kt && (REV ? f + a < g.Tn : f - a >= 0); ++a)
             for (int b = 0; b < kh; ++b) {
                 const int jj = j + b - ph;
                 if (jj < 0 || jj >= g.Hn) continue;
-                const int row = ((f - a) * g.Hn + jj) * g.Wn;         // grid index of column 0
+                const int row = ((REV ? f + a : f - a) * g.Hn + jj) * g.Wn;   // grid index of column 0
                 // columns kq - pw .. kq + kSW - 1 + pw, zero outside the grid or the sample
                 typename Vec8<E>::Raw in[kSW + KW - 1];
 #pragma unroll
                 for (int q = 0; q < kSW + KW - 1; ++q) {
                     const int kk = kq + q - pw;
-                    const bool ok = kk >= 0 && kk < g.Wn && row + kk < g.nv;
+                    const bool ok = kk >= 0 && kk < g.Wn && row + kk < (REV ? g.past : g.nv);
                     in[q] = Vec8<E>::load_raw(xs + (ok ? row + kk : 0) * C, ok);
                 }
                 const float* wr = wv + (kx + (a * kh + b) * kw) * kCB;
@@ -347,28 +363,293 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kWgPerCu)))
     }
 }
 
-template <typename E, int KW>
-void launch_conv_kw(const ConvArgs& a, int32_t* tile_off, size_t smem, int blocks, int ncb)
+// ---- weight gradients ----
+// dw_text[i][c]      = sum over text tokens t (t-i >= 0)   x[t-i][c] dy[t][c]
+// dw_vis[a][b][d][c] = sum over grid outputs (i, j, k)     x[i-a, j+b-(kh-1)/2, k+d-(kw-1)/2][c] dy[i,j,k][c]
+// with x zero outside the grid. A work unit is (channel block, part of the block's tile
+// list, row group): row group a < kt sums the kh*kw visual taps of time offset a, row group
+// kt the text taps. A thread holds 4 channels and every tap of its group for a strip lane;
+// per visual strip it widens the strip's 4 dy columns once and each x row's kw+3 columns
+// once, then does kw*4*4 FMAs per row. The unit's 16 strip lanes are added in LDS in a
+// fixed order and written as one partial per (tap, channel); the reduce kernel adds the
+// parts in order, so the result does not depend on scheduling.
+constexpr int kDwLanes = kCT / 16;  // strip lanes per unit (x 16 channel quads = 64 channels)
+constexpr int kDwUnitsTarget = 4096;
+
+int dw_parts(int C, int kt)
 {
-    hipLaunchKernelGGL((kda_short_conv_kernel<E, KW>), dim3(blocks), dim3(kCT), smem, a.stream,
-                       static_cast<const E*>(a.x), a.w_text, a.w_vis, a.cu_seqlens, a.text_len, a.grid, tile_off,
-                       static_cast<E*>(a.y), a.total_tokens, a.num_seqs, a.channels, a.k_text, a.k_t, a.k_h, ncb);
+    const int per_part = ((C + kCB - 1) / kCB) * (kt + 1);
+    return std::max(1, std::min(1024, (kDwUnitsTarget + per_part - 1) / per_part));
+}
+
+template <typename E> struct Vec4;
+template <> struct Vec4<uint16_t> {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    struct Raw { u32x2 u; };
+    __device__ static Raw load_raw(const uint16_t* p, bool ok) {
+        return Raw{ok ? *reinterpret_cast<const u32x2*>(p) : u32x2{0u, 0u}};
+    }
+    __device__ static Raw load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        return Raw{__builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0)};
+    }
+    __device__ static float at(const Raw& r, int e) {
+        return __uint_as_float((e & 1) ? (r.u[e >> 1] & 0xFFFF0000u) : (r.u[e >> 1] << 16));
+    }
+};
+template <> struct Vec4<float> {
+    struct Raw { u32x4 u; };
+    __device__ static Raw load_raw(const float* p, bool ok) {
+        return Raw{ok ? *reinterpret_cast<const u32x4*>(p) : u32x4{0u, 0u, 0u, 0u}};
+    }
+    __device__ static Raw load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        return Raw{__builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0)};
+    }
+    __device__ static float at(const Raw& r, int e) { return __uint_as_float(r.u[e]); }
+};
+
+template <typename E, int KH, int KW>
+__global__ __launch_bounds__(kCT) void kda_short_conv_dw_kernel(
+    const E* __restrict__ x, const E* __restrict__ dy, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ text_len, const int32_t* __restrict__ grid, const int32_t* __restrict__ tile_off,
+    float* __restrict__ partial, int64_t T, int num_seqs, int C, int kx, int kt, int parts, int units)
+{
+    constexpr int kh = KH;
+    constexpr int NACC = KH * KW > 8 ? KH * KW : 8;         // visual taps of one time offset, or text taps
+    constexpr int es = int(sizeof(E));
+    __shared__ float red[kCT * 4];
+    const int u = (blockIdx.x & 7) * int(gridDim.x >> 3) + int(blockIdx.x >> 3);
+    if (u >= units) return;                                 // uniform over the workgroup
+    const int tid = threadIdx.x, cq = tid & 15, sl = tid >> 4;
+    const int rg = u % (kt + 1), p = (u / (kt + 1)) % parts, cb = u / ((kt + 1) * parts);
+    const bool text = rg == kt;
+    const int a = rg, ph = (kh - 1) / 2, pw = (KW - 1) / 2;
+    const int per_cb = tile_off[num_seqs];
+    const int t0 = int(int64_t(per_cb) * p / parts), t1 = int(int64_t(per_cb) * (p + 1) / parts);
+    const int c0 = kCB * cb + 4 * cq;
+    const bool cok = c0 < C;                                // C is a multiple of 8: all 4 channels exist
+    float acc[NACC][4];
+#pragma unroll
+    for (int s = 0; s < NACC; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[s][e] = 0.f;
+
+    int n = 0;
+    if (t0 < t1) {                                          // tile_off[n] <= t0 < tile_off[n + 1]
+        int hi = num_seqs;
+        while (hi - n > 1) {
+            const int mid = (n + hi) >> 1;
+            if (tile_off[mid] <= t0) n = mid; else hi = mid;
+        }
+    }
+    for (int tp = t0; cok && tp < t1; ++tp) {
+        while (tile_off[n + 1] <= tp) ++n;                  // next sample with tiles
+        const SampleGeom g = sample_geom(cu, text_len, grid, n, T);
+        const SampleTiles st = sample_tiles(g);
+        const int local = tp - tile_off[n];
+        if (text) {
+            if (local >= st.ntext) { tp = tile_off[n + 1] - 1; continue; }
+            for (int r = sl; r < kTextTok; r += kDwLanes) {
+                const int rel = local * kTextTok + r;
+                if (rel >= g.L) break;
+                const int tok = g.base + rel;
+                const typename Vec4<E>::Raw gr = Vec4<E>::load_raw(dy + int64_t(tok) * C + c0, true);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    if (i >= kx || rel - i < 0) break;
+                    const typename Vec4<E>::Raw xr = Vec4<E>::load_raw(x + int64_t(tok - i) * C + c0, true);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][e] += Vec4<E>::at(xr, e) * Vec4<E>::at(gr, e);
+                }
+            }
+            continue;
+        }
+        if (local < st.ntext) { tp = tile_off[n] + st.ntext - 1; continue; }
+        if (local >= st.ntext + st.nvis) { tp = tile_off[n + 1] - 1; continue; }
+        const bool fast = g.past == g.nv && int64_t(g.Tn) * g.Hn * g.Wn == g.nv &&
+                          int64_t(g.nv) * C * es <= kBufLimit;
+        const int64_t v0 = int64_t(g.base + g.L) * C;
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<E*>(x + v0), 0, fast ? int(int64_t(g.nv) * C * es) : 0, kBufFlags);
+        const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<E*>(dy + v0), 0, fast ? int(int64_t(g.nv) * C * es) : 0, kBufFlags);
+        const int per_frame = g.Hn * st.nsw;
+        for (int h = 0; h < kStrips / kDwLanes; ++h) {
+            const int sidx = (local - st.ntext) * kStrips + sl + kDwLanes * h;
+            const int f = sidx / per_frame;
+            if (f >= g.Tn || f - a < 0) continue;
+            const int j = (sidx - f * per_frame) / st.nsw;
+            const int kq = (sidx - f * per_frame - j * st.nsw) * kSW;
+            float gv[kSW][4];
+            if (fast) {
+                const uint32_t rowb = uint32_t(g.Wn) * uint32_t(C) * es;
+                uint32_t colv[kSW + KW - 1];
+#pragma unroll
+                for (int q = 0; q < kSW + KW - 1; ++q) {
+                    const int kk = kq + q - pw;
+                    colv[q] = kk >= 0 && kk < g.Wn ? uint32_t(kk * C + c0) * es : kBufLimit;
+                }
+                const uint32_t doff = uint32_t(f * g.Hn + j) * rowb;
+#pragma unroll
+                for (int q = 0; q < kSW; ++q) {
+                    const int kk = kq + q;
+                    const typename Vec4<E>::Raw r =
+                        Vec4<E>::load_buf(rd, doff + (kk < g.Wn ? uint32_t(kk * C + c0) * es : kBufLimit));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) gv[q][e] = Vec4<E>::at(r, e);
+                }
+#pragma unroll
+                for (int b = 0; b < KH; ++b) {
+                    const int jj = j + b - ph;
+                    const uint32_t roff = jj >= 0 && jj < g.Hn ? uint32_t((f - a) * g.Hn + jj) * rowb : kBufLimit;
+                    typename Vec4<E>::Raw in[kSW + KW - 1];
+#pragma unroll
+                    for (int q = 0; q < kSW + KW - 1; ++q) in[q] = Vec4<E>::load_buf(rx, roff + colv[q]);
+#pragma unroll
+                    for (int q = 0; q < kSW + KW - 1; ++q) {
+                        float xf[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) xf[e] = Vec4<E>::at(in[q], e);
+#pragma unroll
+                        for (int d = 0; d < KW; ++d) {
+                            const int o = q - d;                // output column fed by this tap
+                            if (o < 0 || o >= kSW) continue;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) acc[b * KW + d][e] += xf[e] * gv[o][e];
+                        }
+                    }
+                }
+            } else {
+                const E* xs = x + v0 + c0;
+                const E* ds = dy + v0 + c0;
+                const int orow = (f * g.Hn + j) * g.Wn;
+#pragma unroll
+                for (int q = 0; q < kSW; ++q) {
+                    const int kk = kq + q;
+                    const bool ok = kk < g.Wn && orow + kk < g.past;
+                    const typename Vec4<E>::Raw r = Vec4<E>::load_raw(ds + int64_t(ok ? orow + kk : 0) * C, ok);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) gv[q][e] = Vec4<E>::at(r, e);
+                }
+#pragma unroll
+                for (int b = 0; b < KH; ++b) {
+                    const int jj = j + b - ph;
+                    if (jj < 0 || jj >= g.Hn) continue;
+                    const int row = ((f - a) * g.Hn + jj) * g.Wn;
+                    typename Vec4<E>::Raw in[kSW + KW - 1];
+#pragma unroll
+                    for (int q = 0; q < kSW + KW - 1; ++q) {
+                        const int kk = kq + q - pw;
+                        const bool ok = kk >= 0 && kk < g.Wn && row + kk < g.past;
+                        in[q] = Vec4<E>::load_raw(xs + int64_t(ok ? row + kk : 0) * C, ok);
+                    }
+#pragma unroll
+                    for (int q = 0; q < kSW + KW - 1; ++q)
+#pragma unroll
+                        for (int d = 0; d < KW; ++d) {
+                            const int o = q - d;
+                            if (o < 0 || o >= kSW) continue;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) acc[b * KW + d][e] += Vec4<E>::at(in[q], e) * gv[o][e];
+                        }
+                }
+            }
+        }
+    }
+
+    // the 16 strip lanes of each channel quad, added in lane order; one tap at a time
+    const int ntaps = kx + kt * kh * KW;
+#pragma unroll
+    for (int s = 0; s < NACC; ++s) {
+        const bool live = text ? s < kx : s / KW < kh;      // uniform over the workgroup
+        if (!live) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[tid * 4 + e] = acc[s][e];
+        __syncthreads();
+        if (tid < 64) {
+            const int q = tid >> 2, e = tid & 3, c = kCB * cb + 4 * q + e;
+            float sum = 0.f;
+            for (int l = 0; l < kDwLanes; ++l) sum += red[(l * 16 + q) * 4 + e];
+            const int tap = text ? s : kx + (a * kh + s / KW) * KW + s % KW;
+            if (c < C) partial[(int64_t(p) * ntaps + tap) * C + c] = sum;
+        }
+        __syncthreads();
+    }
+}
+
+// dw[tap][c] = sum over parts, in part order; taps < kx go to dw_text, the rest to dw_vis
+__global__ __launch_bounds__(256) void kda_short_conv_dw_reduce_kernel(const float* __restrict__ partial,
+                                                                       float* __restrict__ dw_text,
+                                                                       float* __restrict__ dw_vis, int C, int kx,
+                                                                       int ntaps, int parts)
+{
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t nel = int64_t(ntaps) * C;
+    if (i >= nel) return;
+    float sum = 0.f;
+    for (int q = 0; q < parts; ++q) sum += partial[q * nel + i];
+    if (i < int64_t(kx) * C) dw_text[i] = sum; else dw_vis[i - int64_t(kx) * C] = sum;
+}
+
+template <typename E, int KW, bool REV>
+void launch_conv_kw(const ConvArgs& a, const void* in, void* out, int32_t* tile_off, size_t smem, int blocks,
+                    int ncb)
+{
+    hipLaunchKernelGGL((kda_short_conv_kernel<E, KW, REV>), dim3(blocks), dim3(kCT), smem, a.stream,
+                       static_cast<const E*>(in), a.w_text, a.w_vis, a.cu_seqlens, a.text_len, a.grid, tile_off,
+                       static_cast<E*>(out), a.total_tokens, a.num_seqs, a.channels, a.k_text, a.k_t, a.k_h, ncb);
 }
 
 // the kernel width is a template argument: it sizes the strip's input registers
-template <typename E>
-void launch_conv(const ConvArgs& a, int32_t* tile_off, size_t smem, int blocks, int ncb)
+template <typename E, bool REV>
+void launch_conv(const ConvArgs& a, const void* in, void* out, int32_t* tile_off, size_t smem, int blocks, int ncb)
 {
     switch (a.k_w) {
-    case 1: launch_conv_kw<E, 1>(a, tile_off, smem, blocks, ncb); break;
-    case 3: launch_conv_kw<E, 3>(a, tile_off, smem, blocks, ncb); break;
-    default: launch_conv_kw<E, 5>(a, tile_off, smem, blocks, ncb); break;
+    case 1: launch_conv_kw<E, 1, REV>(a, in, out, tile_off, smem, blocks, ncb); break;
+    case 3: launch_conv_kw<E, 3, REV>(a, in, out, tile_off, smem, blocks, ncb); break;
+    default: launch_conv_kw<E, 5, REV>(a, in, out, tile_off, smem, blocks, ncb); break;
+    }
+}
+
+template <typename E, int KH, int KW>
+void launch_dw_k(const ConvBwdArgs& a, int32_t* tile_off, float* partial, int blocks, int parts, int units)
+{
+    hipLaunchKernelGGL((kda_short_conv_dw_kernel<E, KH, KW>), dim3(blocks), dim3(kCT), 0, a.f.stream,
+                       static_cast<const E*>(a.f.x), static_cast<const E*>(a.dy), a.f.cu_seqlens, a.f.text_len,
+                       a.f.grid, tile_off, partial, a.f.total_tokens, a.f.num_seqs, a.f.channels, a.f.k_text,
+                       a.f.k_t, parts, units);
+}
+
+// the kernel's height and width are template arguments: they size the per-thread tap sums
+template <typename E, int KH>
+void launch_dw_h(const ConvBwdArgs& a, int32_t* tile_off, float* partial, int blocks, int parts, int units)
+{
+    switch (a.f.k_w) {
+    case 1: launch_dw_k<E, KH, 1>(a, tile_off, partial, blocks, parts, units); break;
+    case 3: launch_dw_k<E, KH, 3>(a, tile_off, partial, blocks, parts, units); break;
+    default: launch_dw_k<E, KH, 5>(a, tile_off, partial, blocks, parts, units); break;
+    }
+}
+
+template <typename E>
+void launch_dw(const ConvBwdArgs& a, int32_t* tile_off, float* partial, int blocks, int parts, int units)
+{
+    switch (a.f.k_h) {
+    case 1: launch_dw_h<E, 1>(a, tile_off, partial, blocks, parts, units); break;
+    case 3: launch_dw_h<E, 3>(a, tile_off, partial, blocks, parts, units); break;
+    default: launch_dw_h<E, 5>(a, tile_off, partial, blocks, parts, units); break;
     }
 }
 
 }  // namespace
 
 size_t conv_workspace_bytes(int32_t num_seqs) { return ((size_t(num_seqs) + 1) * 4 + 255) & ~size_t(255); }
+
+size_t conv_bwd_workspace_bytes(int32_t num_seqs, int32_t channels, int32_t k_text, int32_t k_t, int32_t k_h,
+                                int32_t k_w)
+{
+    const size_t ntaps = size_t(k_text) + size_t(k_t) * k_h * k_w;
+    return conv_workspace_bytes(num_seqs) + size_t(dw_parts(channels, k_t)) * ntaps * size_t(channels) * 4;
+}
 
 hipError_t launch_short_conv(const ConvArgs& a, void* workspace, TimingHook* th)
 {
@@ -385,9 +666,54 @@ hipError_t launch_short_conv(const ConvArgs& a, void* workspace, TimingHook* th)
     const int blocks = 256 * kWgPerCu;              // every CU, kWgPerCu resident workgroups each
     if (th) th->begin("conv", a.stream);
     if (a.dtype_bf16)
-        launch_conv<uint16_t>(a, tile_off, smem, blocks, ncb);
+        launch_conv<uint16_t, false>(a, a.x, a.y, tile_off, smem, blocks, ncb);
     else
-        launch_conv<float>(a, tile_off, smem, blocks, ncb);
+        launch_conv<float, false>(a, a.x, a.y, tile_off, smem, blocks, ncb);
+    if (th) th->end(a.stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_short_conv_backward(const ConvBwdArgs& b, void* workspace, TimingHook* th)
+{
+    const ConvArgs& a = b.f;
+    const int ntaps = a.k_text + a.k_t * a.k_h * a.k_w;
+    const int64_t nel = int64_t(ntaps) * a.channels;
+    if (a.total_tokens == 0 || a.num_seqs == 0) {         // empty sums: zeros, no workspace
+        hipLaunchKernelGGL(kda_short_conv_dw_reduce_kernel, dim3(unsigned((nel + 255) / 256)), dim3(256), 0,
+                           a.stream, static_cast<const float*>(nullptr), b.dw_text, b.dw_vis, a.channels, a.k_text,
+                           ntaps, 0);
+        return hipGetLastError();
+    }
+    const size_t smem = size_t(ntaps) * kCB * sizeof(float);
+    const int ncb = (a.channels + kCB - 1) / kCB;
+    int32_t* tile_off = static_cast<int32_t*>(workspace);
+    float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + conv_workspace_bytes(a.num_seqs));
+    if (th) th->begin("conv_bwd_plan", a.stream);
+    hipLaunchKernelGGL(kda_conv_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, a.text_len, a.grid,
+                       tile_off, a.num_seqs, a.total_tokens);
+    if (th) th->end(a.stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (th) th->begin("conv_dx", a.stream);
+    if (a.dtype_bf16)
+        launch_conv<uint16_t, true>(a, b.dy, b.dx, tile_off, smem, 256 * kWgPerCu, ncb);
+    else
+        launch_conv<float, true>(a, b.dy, b.dx, tile_off, smem, 256 * kWgPerCu, ncb);
+    if (th) th->end(a.stream);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int parts = dw_parts(a.channels, a.k_t);
+    const int units = ncb * parts * (a.k_t + 1);
+    const int blocks = (units + 7) / 8 * 8;
+    if (th) th->begin("conv_dw", a.stream);
+    if (a.dtype_bf16)
+        launch_dw<uint16_t>(b, tile_off, partial, blocks, parts, units);
+    else
+        launch_dw<float>(b, tile_off, partial, blocks, parts, units);
+    if (th) th->end(a.stream);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (th) th->begin("conv_dw_reduce", a.stream);
+    hipLaunchKernelGGL(kda_short_conv_dw_reduce_kernel, dim3(unsigned((nel + 255) / 256)), dim3(256), 0, a.stream,
+                       partial, b.dw_text, b.dw_vis, a.channels, a.k_text, ntaps, parts);
     if (th) th->end(a.stream);
     return hipGetLastError();
 }

@@ -67,7 +67,7 @@ struct BwdArgs {
 hipError_t launch_backward(const BwdArgs& a, void* workspace, TimingHook* th);
 size_t bwd_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads, int d_k, int d_v);
 
-// Modality-aware short convolution over packed samples (no workspace).
+// Modality-aware short convolution over packed samples (workspace: the tile table).
 struct ConvArgs {
     const void* x;
     const float *w_text, *w_vis;    // [k_text][C], [k_t][k_h][k_w][C]
@@ -79,6 +79,17 @@ struct ConvArgs {
 };
 hipError_t launch_short_conv(const ConvArgs& a, void* workspace, TimingHook* th);
 size_t conv_workspace_bytes(int32_t num_seqs);
+
+// Its reverse mode: f holds the forward's arguments (f.y unused); dy in, dx, dw_text, dw_vis out.
+struct ConvBwdArgs {
+    ConvArgs f;
+    const void* dy;
+    void* dx;
+    float *dw_text, *dw_vis;
+};
+hipError_t launch_short_conv_backward(const ConvBwdArgs& a, void* workspace, TimingHook* th);
+size_t conv_bwd_workspace_bytes(int32_t num_seqs, int32_t channels, int32_t k_text, int32_t k_t, int32_t k_h,
+                                int32_t k_w);
 
 // LDS bytes one workgroup uses.
 size_t smem_bytes(int dtype_bf16, int d_k);

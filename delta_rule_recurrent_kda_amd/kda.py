@@ -64,6 +64,8 @@ def library() -> ctypes.CDLL:
         lib.kda_backward_workspace_bytes.restype = ctypes.c_size_t
         lib.kda_short_conv.argtypes = [vp] * 7 + [ctypes.c_int64] + [ctypes.c_int32] * 6 + [ctypes.c_int, vp]
         lib.kda_short_conv.restype = ctypes.c_int
+        lib.kda_short_conv_backward.argtypes = [vp] * 10 + [ctypes.c_int64] + [ctypes.c_int32] * 6 + [ctypes.c_int, vp]
+        lib.kda_short_conv_backward.restype = ctypes.c_int
         lib.kda_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int]
         lib.kda_workspace_bytes.restype = ctypes.c_size_t
@@ -263,10 +265,8 @@ def short_conv_raw(x, w_text, w_vis, cu_seqlens, text_len, grid, y, total_tokens
                                     int(k_w), int(dtype), stream)
 
 
-def short_conv(x, w_text, w_vis, cu_seqlens, text_len, grid, y=None,
-               stream: Optional[torch.cuda.Stream] = None):
-    """The modality-aware short convolution: x [T, C] (float32 or bfloat16); w_text [k, C] and
-    w_vis [kt, kh, kw, C] float32; cu_seqlens [N+1], text_len [N], grid [N, 3] int32. Returns y."""
+def _conv_check(x, w_text, w_vis, cu_seqlens, text_len, grid, outs):
+    """Shapes, dtypes and devices of a short-convolution call; returns (T, C, N, dtype code)."""
     if x.dim() != 2 or w_text.dim() != 2 or w_vis.dim() != 4:
         raise ValueError("x must be [T, C], w_text [k, C], w_vis [kt, kh, kw, C]")
     T, C = x.shape
@@ -288,14 +288,23 @@ def short_conv(x, w_text, w_vis, cu_seqlens, text_len, grid, y=None,
         raise ValueError(f"unsupported dtype {x.dtype}")
     if not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous GPU tensor")
-    if y is None:
-        y = torch.empty_like(x)
-    elif y.dtype != x.dtype or y.shape != x.shape or not y.is_cuda or not y.is_contiguous():
-        raise ValueError("y must be a contiguous GPU tensor of the shape and dtype of x")
+    for name, t, like, like_name in outs:
+        if t.dtype != like.dtype or t.shape != like.shape or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor of the shape and dtype of {like_name}")
     for name, t in (("w_text", w_text), ("w_vis", w_vis), ("cu_seqlens", cu_seqlens), ("text_len", text_len),
-                    ("grid", grid), ("y", y)):
+                    ("grid", grid), *((o[0], o[1]) for o in outs)):
         if t.device != x.device:
             raise ValueError(f"{name} is on {t.device}, x on {x.device}")
+    return T, C, N, dt
+
+
+def short_conv(x, w_text, w_vis, cu_seqlens, text_len, grid, y=None,
+               stream: Optional[torch.cuda.Stream] = None):
+    """The modality-aware short convolution: x [T, C] (float32 or bfloat16); w_text [k, C] and
+    w_vis [kt, kh, kw, C] float32; cu_seqlens [N+1], text_len [N], grid [N, 3] int32. Returns y."""
+    if y is None and x.dim() == 2 and x.is_cuda:
+        y = torch.empty_like(x)
+    T, C, N, dt = _conv_check(x, w_text, w_vis, cu_seqlens, text_len, grid, [("y", y, x, "x")] if y is not None else [])
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     st = short_conv_raw(_ptr(x), _ptr(w_text), _ptr(w_vis), _ptr(cu_seqlens), _ptr(text_len), _ptr(grid),
@@ -304,3 +313,35 @@ def short_conv(x, w_text, w_vis, cu_seqlens, text_len, grid, y=None,
     if st != 0:
         raise KdaError(st, library().kda_last_error().decode())
     return y
+
+
+def short_conv_backward_raw(x, w_text, w_vis, cu_seqlens, text_len, grid, dy, dx, dw_text, dw_vis,
+                            total_tokens: int, num_seqs: int, channels: int, k_text: int, k_t: int, k_h: int,
+                            k_w: int, dtype: int, stream: Optional[int]) -> int:
+    """Direct C call of kda_short_conv_backward; returns the status code."""
+    return library().kda_short_conv_backward(x, w_text, w_vis, cu_seqlens, text_len, grid, dy, dx, dw_text,
+                                             dw_vis, int(total_tokens), int(num_seqs), int(channels), int(k_text),
+                                             int(k_t), int(k_h), int(k_w), int(dtype), stream)
+
+
+def short_conv_backward(x, w_text, w_vis, cu_seqlens, text_len, grid, dy, dx=None, dw_text=None, dw_vis=None,
+                        stream: Optional[torch.cuda.Stream] = None):
+    """Reverse mode of short_conv: dy [T, C] of the dtype of x. Returns (dx, dw_text, dw_vis), dx of the
+    dtype of x and the weight gradients float32 of the weights' shapes."""
+    if x.dim() == 2 and x.is_cuda:
+        dx = torch.empty_like(x) if dx is None else dx
+        dw_text = torch.empty_like(w_text) if dw_text is None else dw_text
+        dw_vis = torch.empty_like(w_vis) if dw_vis is None else dw_vis
+    outs = [("dy", dy, x, "x"), ("dx", dx, x, "x"), ("dw_text", dw_text, w_text, "w_text"),
+            ("dw_vis", dw_vis, w_vis, "w_vis")]
+    if any(o[1] is None for o in outs):
+        raise ValueError("x must be a [T, C] GPU tensor")
+    T, C, N, dt = _conv_check(x, w_text, w_vis, cu_seqlens, text_len, grid, outs)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    st = short_conv_backward_raw(_ptr(x), _ptr(w_text), _ptr(w_vis), _ptr(cu_seqlens), _ptr(text_len), _ptr(grid),
+                                 _ptr(dy), _ptr(dx), _ptr(dw_text), _ptr(dw_vis), T, N, C, w_text.shape[0],
+                                 w_vis.shape[0], w_vis.shape[1], w_vis.shape[2], dt, stream.cuda_stream)
+    if st != 0:
+        raise KdaError(st, library().kda_last_error().decode())
+    return dx, dw_text, dw_vis

@@ -214,7 +214,8 @@ size_t kda_backward_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int3
  *   x, y        : [total_tokens][channels] dtype, DEVICE, 16-byte aligned; y may not overlap an input
  *   w_text      : [k_text][channels] fp32;  w_vis : [k_t][k_h][k_w][channels] fp32 (DEVICE)
  *   cu_seqlens  : [num_seqs + 1] int32; text_len : [num_seqs] int32; grid : [num_seqs][3] int32
- *                 (DEVICE); text_len[n] + T*H*W must equal the sample's length (checked on the
+ *                 (DEVICE; text_len and grid may be NULL when num_seqs is 0);
+ *                 text_len[n] + T*H*W must equal the sample's length (checked on the
  *                 host only with KDA_VALIDATE=1). Otherwise the kernel still reads and writes
  *                 only inside the sample: grid positions past its last token read as zero,
  *                 and tokens past T*H*W (or after the text when T, H or W is 0) get zeros
@@ -228,6 +229,42 @@ kda_status kda_short_conv(const void *x, const float *w_text, const float *w_vis
                           void *y, int64_t total_tokens, int32_t num_seqs, int32_t channels,
                           int32_t k_text, int32_t k_t, int32_t k_h, int32_t k_w, kda_dtype dtype,
                           hipStream_t stream);
+
+/*
+ * kda_short_conv_backward -- the reverse mode of kda_short_conv: for a loss whose gradient
+ * with respect to y is dy, the gradients dx, dw_text and dw_vis.
+ *
+ * The convolution above is linear in x and, separately, in the weights, so each gradient is
+ * the transpose of one of those linear maps applied to dy (same passages as kda_short_conv):
+ *   dx[t][c]           = sum_{i < k_text, t + i < text_len} w_text[i][c] dy[t + i][c]
+ *   dx[i,j,k][c]       = sum_{a,b,d} w_vis[a][b][d][c] dy[i + a, j - b + (k_h-1)/2, k - d + (k_w-1)/2][c]
+ *   dw_text[i][c]      = sum over text tokens t with t - i >= 0 of x[t - i][c] dy[t][c]
+ *   dw_vis[a][b][d][c] = sum over grid positions (i, j, k) of x[i - a, j + b - (k_h-1)/2, k + d - (k_w-1)/2][c] dy[i,j,k][c]
+ * with terms outside the sample's text or grid zero; the weight sums run over every sample.
+ *
+ *   x, dy, dx   : [total_tokens][channels] dtype, DEVICE, 16-byte aligned
+ *   dw_text     : [k_text][channels] fp32; dw_vis : [k_t][k_h][k_w][channels] fp32 (DEVICE),
+ *                 overwritten (not accumulated into)
+ *   the rest    : as kda_short_conv. No output may overlap an input or another output.
+ * When a sample's grid does not match its length the calls read and write only inside the
+ * sample, as kda_short_conv: grid positions past its last token hold zero in x and in dy, and
+ * dx is zero for tokens past T*H*W. With no samples or no tokens dw_text and dw_vis are zero
+ * and dx is not touched.
+ * Arithmetic is fp32; dx is rounded to nearest-even for bf16. dx comes from the forward's
+ * kernel with the taps mirrored and the time and text directions reversed; the weight sums
+ * are formed per (channel block, slice of the tile list) and the slices then added in a
+ * fixed order, so the result is the same bit for bit from run to run. A workspace of the
+ * tile table plus parts * (k_text + k_t*k_h*k_w) * channels fp32 partial sums (parts is
+ * about 4096 / (ceil(channels / 64) * (k_t + 1)), at least 1) comes from the stream-ordered
+ * pool as for kda_forward. Execution and errors as kda_forward; the timing hook names the
+ * kernels "conv_bwd_plan", "conv_dx", "conv_dw" and "conv_dw_reduce".
+ */
+kda_status kda_short_conv_backward(const void *x, const float *w_text, const float *w_vis,
+                                   const int32_t *cu_seqlens, const int32_t *text_len,
+                                   const int32_t *grid, const void *dy, void *dx, float *dw_text,
+                                   float *dw_vis, int64_t total_tokens, int32_t num_seqs,
+                                   int32_t channels, int32_t k_text, int32_t k_t, int32_t k_h,
+                                   int32_t k_w, kda_dtype dtype, hipStream_t stream);
 
 /*
  * kda_workspace_bytes -- bytes of device workspace the default bf16 scan takes for

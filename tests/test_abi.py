@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert {"kda_forward", "kda_forward_from_state", "kda_forward_ex", "kda_backward", "kda_backward_workspace_bytes",
-            "kda_short_conv", "kda_workspace_bytes", "kda_timing_enable",
+            "kda_short_conv", "kda_short_conv_backward", "kda_workspace_bytes", "kda_timing_enable",
             "kda_timing_read", "kda_status_str", "kda_last_error", "kda_version"} <= set(declared_functions())
 
 
@@ -186,6 +186,43 @@ def _call_conv(kw):
 ])
 def test_short_conv_bad_arguments_are_rejected_without_launch(lib, kw, code):
     st, msg = _call_conv(kw)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def test_short_conv_with_no_samples_takes_null_tables(lib):
+    st, msg = _call_conv(dict(num_seqs=0, total_tokens=0, text_len=None, grid=None))
+    assert st == 0, msg
+
+
+def _call_conv_bwd(kw):
+    from delta_rule_recurrent_kda_amd import kda
+    a = dict(x=0x100000, w_text=0x200000, w_vis=0x300000, cu_seqlens=0x400000, text_len=0x500000, grid=0x600000,
+             dy=0x700000, dx=0x800000, dw_text=0x900000, dw_vis=0xa00000, total_tokens=100, num_seqs=1,
+             channels=64, k_text=4, k_t=3, k_h=3, k_w=3, dtype=kda.KDA_BF16, stream=None)
+    a.update(kw)
+    st = kda.short_conv_backward_raw(**a)
+    return st, kda.library().kda_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), 2),
+    (dict(channels=12), 5),
+    (dict(k_w=4), 5),
+    (dict(k_t=0), 5),
+    (dict(dy=None), 1),
+    (dict(dx=None), 1),
+    (dict(dw_vis=None), 1),
+    (dict(dy=0x700004), 4),
+    (dict(dx=0x800008), 4),
+    (dict(dx=0x700000), 3),                            # dx aliases dy
+    (dict(dw_text=0x100040), 3),                       # dw_text starts inside x
+    (dict(dw_vis=0x8ffff0), 3),                        # dw_vis runs into dw_text
+    (dict(dw_text=0x300100), 3),                       # dw_text inside w_vis
+    (dict(total_tokens=1 << 25), 5),
+])
+def test_short_conv_backward_bad_arguments_are_rejected_without_launch(lib, kw, code):
+    st, msg = _call_conv_bwd(kw)
     assert st == code, (st, msg)
     assert msg
 

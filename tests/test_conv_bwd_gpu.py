@@ -1,0 +1,223 @@
+"""GPU parity of kda_short_conv_backward (through the C ABI) against the fp64 oracle.
+
+Bounds from the arithmetic (u32 = 2^-24, fp32 accumulation with fused multiply-adds):
+  dx: |dx - ref| <= u |ref| + 1.01 * (n_taps + 1) * u32 * sum_taps |w| |dy|, u = 2^-8 for bf16
+      (one rounding of the fp32 result), 0 for fp32; n_taps = k_text + k_t*k_h*k_w bounds the
+      terms of one element.
+  dw: |dw - ref| <= (n_terms + 1) * u32 * sum |x| |dy|, n_terms <= the number of tokens, which
+      bounds the terms of any order of summation.
+sum |w||dy| and sum |x||dy| are the oracle applied to absolute values (the maps are linear).
+At full sizes the inputs are small integers, so every product and partial sum is exact in
+fp32 (and dx in bf16): there the results must equal the oracle exactly.
+"""
+import numpy as np
+import pytest
+
+import gpu_util as gu
+from delta_rule_recurrent_kda_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _tables(shapes):
+    lens = [L + T * H * W for L, T, H, W in shapes]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    tl = np.array([s[0] for s in shapes], np.int32)
+    gr = np.array([s[1:] for s in shapes], np.int32).reshape(-1, 3)
+    return cu, tl, gr
+
+
+def _round(a, dtype):
+    return inputs.bf16_bits_to_f64(inputs.f64_to_bf16_bits(a)) if dtype == "bf16" else a.astype(np.float32).astype(np.float64)
+
+
+def _case(seed, shapes, C, ks, dtype, integer=False):
+    rng = np.random.default_rng(seed)
+    cu, tl, gr = _tables(shapes)
+    tot = int(cu[-1])
+    if integer:
+        x = rng.integers(-1, 2, (tot, C)).astype(np.float64)
+        dy = rng.integers(-1, 2, (tot, C)).astype(np.float64)
+        wt = rng.integers(-1, 2, (ks[0], C)).astype(np.float32)
+        wv = rng.integers(-1, 2, (ks[1], ks[2], ks[3], C)).astype(np.float32)
+    else:
+        x = _round(rng.standard_normal((tot, C)), dtype)
+        dy = _round(rng.standard_normal((tot, C)), dtype)
+        wt = rng.standard_normal((ks[0], C)).astype(np.float32) * 0.5
+        wv = rng.standard_normal((ks[1], ks[2], ks[3], C)).astype(np.float32) * 0.3
+    return x, dy, wt, wv, cu, tl, gr
+
+
+def _dev(a, dtype):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(inputs.f64_to_bf16_bits(a).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda:0")
+
+
+def _run(x, dy, wt, wv, cu, tl, gr, dtype):
+    import torch
+    from delta_rule_recurrent_kda_amd import kda
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+    dx, dwt, dwv = kda.short_conv_backward(_dev(x, dtype), t(wt), t(wv), t(cu), t(tl), t(gr), _dev(dy, dtype))
+    torch.cuda.synchronize()
+    return dx.float().cpu().double().numpy(), dwt.cpu().double().numpy(), dwv.cpu().double().numpy()
+
+
+def _check(seed, shapes, C, ks, dtype, label):
+    import oracle
+    x, dy, wt, wv, cu, tl, gr = _case(seed, shapes, C, ks, dtype)
+    gu.log(f"case short conv backward {label}: {len(shapes)} samples, {len(x)} tokens, C={C}, kernels {ks}, {dtype}")
+    dx, dwt, dwv = _run(x, dy, wt, wv, cu, tl, gr, dtype)
+    rdx, rdwt, rdwv = oracle.short_conv_backward(x, wt, wv, cu, tl, gr, dy)
+    mdx, mdwt, mdwv = oracle.short_conv_backward(np.abs(x), np.abs(wt), np.abs(wv), cu, tl, gr, np.abs(dy))
+    u = 2.0 ** -8 if dtype == "bf16" else 0.0
+    ntaps = ks[0] + ks[1] * ks[2] * ks[3]
+    bdx = u * np.abs(rdx) + 1.01 * (ntaps + 1) * 2.0 ** -24 * mdx
+    e = np.abs(dx - rdx)
+    gu.log(f"[{label}] dx worst error / bound {float((e / np.maximum(bdx, 1e-300)).max(initial=0)):.3f}")
+    assert np.all(e <= bdx), label
+    assert np.all(dx[mdx == 0] == 0)
+    n = len(x) + 1
+    for name, got, ref, mag in (("dw_text", dwt, rdwt, mdwt), ("dw_vis", dwv, rdwv, mdwv)):
+        b = n * 2.0 ** -24 * mag
+        e = np.abs(got - ref)
+        gu.log(f"[{label}] {name} worst error / bound {float((e / np.maximum(b, 1e-300)).max(initial=0)):.3f}")
+        assert np.all(e <= b), (label, name)
+
+
+CASES = [
+    ("mixed_bf16", [(5, 3, 4, 6), (0, 2, 3, 3), (9, 1, 5, 5), (7, 0, 2, 2), (0, 0, 1, 1), (3, 4, 1, 1)],
+     72, (4, 3, 3, 3), "bf16"),
+    ("mixed_f32", [(5, 3, 4, 6), (0, 2, 3, 3), (9, 1, 5, 5), (7, 0, 2, 2), (3, 4, 1, 1)], 64, (4, 3, 3, 3), "f32"),
+    ("largest_kernels", [(20, 6, 7, 9), (3, 1, 2, 2)], 16, (8, 4, 5, 5), "bf16"),
+    ("largest_kernels_f32", [(11, 5, 6, 6)], 24, (8, 4, 5, 5), "f32"),
+    ("pointwise", [(6, 2, 3, 3), (0, 1, 4, 4)], 24, (1, 1, 1, 1), "bf16"),
+    ("uneven_kernels", [(11, 5, 3, 8)], 8, (2, 2, 3, 1), "f32"),
+    ("tall_kernel", [(4, 3, 7, 5)], 16, (3, 2, 5, 1), "bf16"),
+    ("wide_kernel", [(4, 3, 4, 11)], 16, (3, 2, 1, 5), "bf16"),
+    ("many_channel_blocks", [(33, 3, 6, 7), (0, 2, 5, 5)], 520, (4, 3, 3, 3), "bf16"),
+    ("many_tiles", [(300, 6, 17, 23), (129, 2, 9, 31)], 64, (4, 3, 3, 3), "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_short_conv_backward_vs_oracle(case):
+    name, shapes, C, ks, dt = case
+    _check(91, shapes, C, ks, dt, name)
+
+
+@pytest.mark.parametrize("label,shapes,C", [
+    ("clip5s_full_width", [(512, 21, 30, 52)], 2048),      # 5-second clip, 16 heads x 128 channels
+    ("image4", [(256, 1, 64, 64)] * 4, 256),               # four images, 256 text tokens + 64 x 64 each
+])
+def test_short_conv_backward_exact_at_full_size(label, shapes, C):
+    """Small-integer inputs: every product and partial sum is exact, so the kernels must match
+    the oracle bit for bit, at the sizes and launch shape the benchmark uses."""
+    import oracle
+    ks = (4, 3, 3, 3)
+    x, dy, wt, wv, cu, tl, gr = _case(92, shapes, C, ks, "bf16", integer=True)
+    gu.log(f"case short conv backward exact {label}: {len(x)} tokens, C={C}")
+    dx, dwt, dwv = _run(x, dy, wt, wv, cu, tl, gr, "bf16")
+    rdx, rdwt, rdwv = oracle.short_conv_backward(x, wt, wv, cu, tl, gr, dy)
+    for name, got, ref in (("dx", dx, rdx), ("dw_text", dwt, rdwt), ("dw_vis", dwv, rdwv)):
+        bad = int(np.count_nonzero(got != ref))
+        gu.log(f"[{label}] {name}: {bad} of {ref.size} differ")
+        assert bad == 0, (label, name)
+
+
+def test_short_conv_backward_grid_not_matching_length():
+    """Samples whose grid does not match their length: the kernels read and write only inside
+    each sample. The expected values are the oracle on the full grid with the missing x and dy
+    tokens zero; dx is zero for tokens past T*H*W."""
+    import oracle
+    C, ks = 40, (4, 3, 3, 3)
+    samples = [(4, 47, (3, 4, 5)), (2, 20, (2, 6, 7)), (3, 10, (1, 3, 50)), (5, 25, (2, 3, 3)),
+               (6, 9, (0, 3, 3)), (3, 30, (2, 3, 5))]
+    rng = np.random.default_rng(93)
+    lens = [L + nv for L, nv, _ in samples]
+    x = _round(rng.standard_normal((sum(lens), C)), "bf16")
+    dy = _round(rng.standard_normal((sum(lens), C)), "bf16")
+    wt = rng.standard_normal((ks[0], C)).astype(np.float32) * 0.5
+    wv = rng.standard_normal((ks[1], ks[2], ks[3], C)).astype(np.float32) * 0.3
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    tl = np.array([s[0] for s in samples], np.int32)
+    gr = np.array([s[2] for s in samples], np.int32)
+    gu.log(f"case short conv backward grid not matching length: {len(samples)} samples, {len(x)} tokens")
+    dx, dwt, dwv = _run(x, dy, wt, wv, cu, tl, gr, "bf16")
+    rwt = np.zeros_like(dwt)
+    rwv = np.zeros_like(dwv)
+    mwt = np.zeros_like(dwt)
+    mwv = np.zeros_like(dwv)
+    for n, (L, nv, (T, H, W)) in enumerate(samples):
+        full = L + T * H * W
+        keep = min(L + nv, full)
+        xf = np.zeros((full, C))
+        gf = np.zeros((full, C))
+        xf[:keep] = x[cu[n]:cu[n] + keep]
+        gf[:keep] = dy[cu[n]:cu[n] + keep]
+        tabs = (np.array([0, full], np.int32), np.array([L], np.int32), np.array([[T, H, W]], np.int32))
+        rdx, a, b = oracle.short_conv_backward(xf, wt, wv, *tabs, gf)
+        mdx, ma, mb = oracle.short_conv_backward(np.abs(xf), np.abs(wt), np.abs(wv), *tabs, np.abs(gf))
+        rwt += a
+        rwv += b
+        mwt += ma
+        mwv += mb
+        got = dx[cu[n]:cu[n + 1]]
+        bound = 2.0 ** -8 * np.abs(rdx[:keep]) + 1.01 * 32 * 2.0 ** -24 * mdx[:keep]
+        assert np.all(np.abs(got[:keep] - rdx[:keep]) <= bound), n
+        assert np.all(got[keep:] == 0), n
+    nb = (len(x) + 1) * 2.0 ** -24
+    assert np.all(np.abs(dwt - rwt) <= nb * mwt)
+    assert np.all(np.abs(dwv - rwv) <= nb * mwv)
+
+
+def test_short_conv_backward_no_tokens_gives_zero_weight_gradients():
+    import torch
+    from delta_rule_recurrent_kda_amd import kda
+    dev = "cuda:0"
+    C = 16
+    for cu_list, tl_list, gr_list in (([0], [], []), ([0, 0, 0], [0, 0], [[0, 1, 1], [0, 3, 3]])):
+        N = len(cu_list) - 1
+        gu.log(f"case short conv backward no tokens: {N} samples")
+        x = torch.zeros((0, C), dtype=torch.bfloat16, device=dev)
+        wt = torch.randn((4, C), device=dev)
+        wv = torch.randn((3, 3, 3, C), device=dev)
+        dwt = torch.full_like(wt, float("nan"))
+        dwv = torch.full_like(wv, float("nan"))
+        cu = torch.tensor(cu_list, dtype=torch.int32, device=dev)
+        tl = torch.tensor(tl_list, dtype=torch.int32, device=dev)
+        gr = torch.tensor(gr_list, dtype=torch.int32, device=dev).reshape(-1, 3)
+        kda.short_conv_backward(x, wt, wv, cu, tl, gr, x.clone(), torch.empty_like(x), dwt, dwv)
+        torch.cuda.synchronize()
+        assert torch.all(dwt == 0) and torch.all(dwv == 0)
+
+
+def test_short_conv_backward_bitwise_deterministic():
+    import torch
+    from delta_rule_recurrent_kda_amd import kda
+    x, dy, wt, wv, cu, tl, gr = _case(94, [(64, 5, 12, 20), (17, 3, 7, 9)], 128, (4, 3, 3, 3), "bf16")
+    gu.log(f"case short conv backward determinism: {len(x)} tokens")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+    args = (_dev(x, "bf16"), t(wt), t(wv), t(cu), t(tl), t(gr), _dev(dy, "bf16"))
+    first = [v.clone() for v in kda.short_conv_backward(*args)]
+    for _ in range(3):
+        again = kda.short_conv_backward(*args)
+        for a, b in zip(first, again):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+
+def test_short_conv_backward_timing_hook():
+    import torch
+    from delta_rule_recurrent_kda_amd import kda
+    x, dy, wt, wv, cu, tl, gr = _case(95, [(10, 2, 4, 4)], 32, (4, 3, 3, 3), "bf16")
+    kda.timing_enable(True)
+    try:
+        _run(x, dy, wt, wv, cu, tl, gr, "bf16")
+    finally:
+        kda.timing_enable(False)
+    for name in ("conv_bwd_plan", "conv_dx", "conv_dw", "conv_dw_reduce"):
+        n, ms = kda.timing_read(name)
+        assert n == 1 and ms > 0, name
+    torch.cuda.synchronize()
