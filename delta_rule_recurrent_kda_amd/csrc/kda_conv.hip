@@ -368,44 +368,22 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kWgPerCu)))
 // dw_vis[a][b][d][c] = sum over grid outputs (i, j, k)     x[i-a, j+b-(kh-1)/2, k+d-(kw-1)/2][c] dy[i,j,k][c]
 // with x zero outside the grid. A work unit is (channel block, part of the block's tile
 // list, row group): row group a < kt sums the kh*kw visual taps of time offset a, row group
-// kt the text taps. A thread holds 4 channels and every tap of its group for a strip lane;
-// per visual strip it widens the strip's 4 dy columns once and each x row's kw+3 columns
-// once, then does kw*4*4 FMAs per row. The unit's 16 strip lanes are added in LDS in a
-// fixed order and written as one partial per (tap, channel); the reduce kernel adds the
-// parts in order, so the result does not depend on scheduling.
-constexpr int kDwLanes = kCT / 16;  // strip lanes per unit (x 16 channel quads = 64 channels)
-constexpr int kDwUnitsTarget = 4096;
+// kt the text taps. A thread holds 8 channels and every tap of its group for one strip lane
+// (a visual tile's 32 strips, one per lane); per strip it widens the strip's 4 dy columns
+// once and each x row's kw+3 columns once, then does kw*4*8 FMAs per row. The unit's 32
+// strip lanes are added in LDS in a fixed order and written as one partial per (tap,
+// channel); the reduce kernel adds the parts in order, so the result does not depend on
+// scheduling. The unit's tile loop has one straight-line body per case (text, whole-frame
+// buffer loads, checked loads), so the 8*kh*kw tap sums stay in their registers across
+// iterations; like the forward, the pass is bound by vector instructions (FMAs plus the bf16
+// widening), not by HBM.
+constexpr int kDwUnitsTarget = 2048;
 
 int dw_parts(int C, int kt)
 {
     const int per_part = ((C + kCB - 1) / kCB) * (kt + 1);
     return std::max(1, std::min(1024, (kDwUnitsTarget + per_part - 1) / per_part));
 }
-
-template <typename E> struct Vec4;
-template <> struct Vec4<uint16_t> {
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    struct Raw { u32x2 u; };
-    __device__ static Raw load_raw(const uint16_t* p, bool ok) {
-        return Raw{ok ? *reinterpret_cast<const u32x2*>(p) : u32x2{0u, 0u}};
-    }
-    __device__ static Raw load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-        return Raw{__builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0)};
-    }
-    __device__ static float at(const Raw& r, int e) {
-        return __uint_as_float((e & 1) ? (r.u[e >> 1] & 0xFFFF0000u) : (r.u[e >> 1] << 16));
-    }
-};
-template <> struct Vec4<float> {
-    struct Raw { u32x4 u; };
-    __device__ static Raw load_raw(const float* p, bool ok) {
-        return Raw{ok ? *reinterpret_cast<const u32x4*>(p) : u32x4{0u, 0u, 0u, 0u}};
-    }
-    __device__ static Raw load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-        return Raw{__builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0)};
-    }
-    __device__ static float at(const Raw& r, int e) { return __uint_as_float(r.u[e]); }
-};
 
 template <typename E, int KH, int KW>
 __global__ __launch_bounds__(kCT) void kda_short_conv_dw_kernel(
@@ -416,131 +394,172 @@ __global__ __launch_bounds__(kCT) void kda_short_conv_dw_kernel(
     constexpr int kh = KH;
     constexpr int NACC = KH * KW > 8 ? KH * KW : 8;         // visual taps of one time offset, or text taps
     constexpr int es = int(sizeof(E));
-    __shared__ float red[kCT * 4];
+    constexpr int kLanes = kCT / 8;                         // strip lanes (x 8 channel groups = 64 channels)
+    static_assert(kLanes == kStrips, "one strip per lane per visual tile");
+    __shared__ float red[kCT * 8];
     const int u = (blockIdx.x & 7) * int(gridDim.x >> 3) + int(blockIdx.x >> 3);
     if (u >= units) return;                                 // uniform over the workgroup
-    const int tid = threadIdx.x, cq = tid & 15, sl = tid >> 4;
+    const int tid = threadIdx.x, cv = tid & 7, sl = tid >> 3;
     const int rg = u % (kt + 1), p = (u / (kt + 1)) % parts, cb = u / ((kt + 1) * parts);
     const bool text = rg == kt;
     const int a = rg, ph = (kh - 1) / 2, pw = (KW - 1) / 2;
     const int per_cb = tile_off[num_seqs];
     const int t0 = int(int64_t(per_cb) * p / parts), t1 = int(int64_t(per_cb) * (p + 1) / parts);
-    const int c0 = kCB * cb + 4 * cq;
-    const bool cok = c0 < C;                                // C is a multiple of 8: all 4 channels exist
-    float acc[NACC][4];
+    // lanes past the last channel read channels 0..7 of the same tokens and write nothing, so
+    // every lane runs the same code
+    const bool cok = kCB * cb + 8 * cv < C;                 // C is a multiple of 8: all 8 channels exist
+    const int c0 = cok ? kCB * cb + 8 * cv : 0;
+    float acc[NACC][8];
 #pragma unroll
     for (int s = 0; s < NACC; ++s)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[s][e] = 0.f;
+        for (int e = 0; e < 8; ++e) acc[s][e] = 0.f;
 
-    int n = 0;
-    if (t0 < t1) {                                          // tile_off[n] <= t0 < tile_off[n + 1]
+    int n0 = 0;
+    if (t0 < t1) {                                          // tile_off[n0] <= t0 < tile_off[n0 + 1]
         int hi = num_seqs;
-        while (hi - n > 1) {
-            const int mid = (n + hi) >> 1;
-            if (tile_off[mid] <= t0) n = mid; else hi = mid;
+        while (hi - n0 > 1) {
+            const int mid = (n0 + hi) >> 1;
+            if (tile_off[mid] <= t0) n0 = mid; else hi = mid;
         }
     }
-    for (int tp = t0; cok && tp < t1; ++tp) {
-        while (tile_off[n + 1] <= tp) ++n;                  // next sample with tiles
-        const SampleGeom g = sample_geom(cu, text_len, grid, n, T);
-        const SampleTiles st = sample_tiles(g);
-        const int local = tp - tile_off[n];
-        if (text) {
+    // Three loops over the unit's tiles, each with its own straight-line body, so the tap sums
+    // stay in place: text taps; visual taps when every sample the unit touches is whole frames
+    // under the buffer limit (out-of-grid positions read as zero through the buffer bounds);
+    // visual taps with per-position checks otherwise.
+    bool all_fast = !text;
+    for (int m = n0; all_fast && m < num_seqs && tile_off[m] < t1; ++m) {
+        const SampleGeom g = sample_geom(cu, text_len, grid, m, T);
+        if (g.Tn > 0 && !(g.past == g.nv && int64_t(g.Tn) * g.Hn * g.Wn == g.nv &&
+                          int64_t(g.nv) * C * es <= kBufLimit))
+            all_fast = false;
+    }
+    if (text) {
+        int n = n0;
+        for (int tp = t0; tp < t1; ++tp) {
+            while (tile_off[n + 1] <= tp) ++n;              // next sample with tiles
+            const SampleGeom g = sample_geom(cu, text_len, grid, n, T);
+            const SampleTiles st = sample_tiles(g);
+            const int local = tp - tile_off[n];
             if (local >= st.ntext) { tp = tile_off[n + 1] - 1; continue; }
-            for (int r = sl; r < kTextTok; r += kDwLanes) {
+            for (int r = sl; r < kTextTok; r += kLanes) {
                 const int rel = local * kTextTok + r;
                 if (rel >= g.L) break;
                 const int tok = g.base + rel;
-                const typename Vec4<E>::Raw gr = Vec4<E>::load_raw(dy + int64_t(tok) * C + c0, true);
+                const typename Vec8<E>::Raw gr = Vec8<E>::load_raw(dy + int64_t(tok) * C + c0, true);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     if (i >= kx || rel - i < 0) break;
-                    const typename Vec4<E>::Raw xr = Vec4<E>::load_raw(x + int64_t(tok - i) * C + c0, true);
+                    const typename Vec8<E>::Raw xr = Vec8<E>::load_raw(x + int64_t(tok - i) * C + c0, true);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[i][e] += Vec4<E>::at(xr, e) * Vec4<E>::at(gr, e);
+                    for (int e = 0; e < 8; ++e) acc[i][e] += Vec8<E>::at(xr, e) * Vec8<E>::at(gr, e);
                 }
             }
-            continue;
         }
-        if (local < st.ntext) { tp = tile_off[n] + st.ntext - 1; continue; }
-        if (local >= st.ntext + st.nvis) { tp = tile_off[n + 1] - 1; continue; }
-        const bool fast = g.past == g.nv && int64_t(g.Tn) * g.Hn * g.Wn == g.nv &&
-                          int64_t(g.nv) * C * es <= kBufLimit;
-        const int64_t v0 = int64_t(g.base + g.L) * C;
-        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<E*>(x + v0), 0, fast ? int(int64_t(g.nv) * C * es) : 0, kBufFlags);
-        const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<E*>(dy + v0), 0, fast ? int(int64_t(g.nv) * C * es) : 0, kBufFlags);
-        const int per_frame = g.Hn * st.nsw;
-        for (int h = 0; h < kStrips / kDwLanes; ++h) {
-            const int sidx = (local - st.ntext) * kStrips + sl + kDwLanes * h;
+    } else if (all_fast) {
+        // samples in turn, then the sample's visual tiles inside [t0, t1): no branch in the
+        // tile loop, so the tap sums keep their registers
+        for (int n = n0; n < num_seqs && tile_off[n] < t1; ++n) {
+            const SampleGeom g = sample_geom(cu, text_len, grid, n, T);
+            const SampleTiles st = sample_tiles(g);
+            const int v_lo = max(t0, tile_off[n] + st.ntext), v_hi = min(t1, tile_off[n] + st.ntext + st.nvis);
+            for (int tp = v_lo; tp < v_hi; ++tp) {
+                const int local = tp - tile_off[n];
+                const int sidx = (local - st.ntext) * kStrips + sl;
+                const int per_frame = g.Hn * st.nsw;
+                const int f = sidx / per_frame;
+                const int j = (sidx - f * per_frame) / st.nsw;
+                const int kq = (sidx - f * per_frame - j * st.nsw) * kSW;
+                const bool vo = f < g.Tn;                       // the strip's outputs exist
+                const bool vx = vo && f - a >= 0;               // and so does its x frame
+                const int64_t v0 = int64_t(g.base + g.L) * C;
+                const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<E*>(x + v0), 0, int(int64_t(g.nv) * C * es), kBufFlags);
+                const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<E*>(dy + v0), 0, int(int64_t(g.nv) * C * es), kBufFlags);
+                const uint32_t rowb = uint32_t(g.Wn) * uint32_t(C) * es;
+                const uint32_t doff = vo ? uint32_t(f * g.Hn + j) * rowb : kBufLimit;
+                {
+                    float gv[kSW][8];
+#pragma unroll
+                    for (int q = 0; q < kSW; ++q) {
+                        const int kk = kq + q;
+                        const typename Vec8<E>::Raw r =
+                            Vec8<E>::load_buf(rd, doff + (kk < g.Wn ? uint32_t(kk * C + c0) * es : kBufLimit));
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) gv[q][e] = Vec8<E>::at(r, e);
+                    }
+                    uint32_t colv[kSW + KW - 1];
+#pragma unroll
+                    for (int q = 0; q < kSW + KW - 1; ++q) {
+                        const int kk = kq + q - pw;
+                        colv[q] = kk >= 0 && kk < g.Wn ? uint32_t(kk * C + c0) * es : kBufLimit;
+                    }
+#pragma unroll
+                    for (int b = 0; b < KH; ++b) {
+                        const int jj = j + b - ph;
+                        const uint32_t roff =
+                            vx && jj >= 0 && jj < g.Hn ? uint32_t((f - a) * g.Hn + jj) * rowb : kBufLimit;
+                        typename Vec8<E>::Raw in[kSW + KW - 1];
+#pragma unroll
+                        for (int q = 0; q < kSW + KW - 1; ++q) in[q] = Vec8<E>::load_buf(rx, roff + colv[q]);
+#pragma unroll
+                        for (int q = 0; q < kSW + KW - 1; ++q) {
+                            float xf[8];
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) xf[e] = Vec8<E>::at(in[q], e);
+#pragma unroll
+                            for (int d = 0; d < KW; ++d) {
+                                const int o = q - d;            // output column fed by this tap
+                                if (o < 0 || o >= kSW) continue;
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) acc[b * KW + d][e] += xf[e] * gv[o][e];
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    } else {
+        int n = n0;
+        for (int tp = t0; tp < t1; ++tp) {
+            while (tile_off[n + 1] <= tp) ++n;
+            const SampleGeom g = sample_geom(cu, text_len, grid, n, T);
+            const SampleTiles st = sample_tiles(g);
+            const int local = tp - tile_off[n];
+            if (local < st.ntext) { tp = tile_off[n] + st.ntext - 1; continue; }
+            if (local >= st.ntext + st.nvis) { tp = tile_off[n + 1] - 1; continue; }
+            const int sidx = (local - st.ntext) * kStrips + sl;
+            const int per_frame = g.Hn * st.nsw;
             const int f = sidx / per_frame;
             if (f >= g.Tn || f - a < 0) continue;
             const int j = (sidx - f * per_frame) / st.nsw;
             const int kq = (sidx - f * per_frame - j * st.nsw) * kSW;
-            float gv[kSW][4];
-            if (fast) {
-                const uint32_t rowb = uint32_t(g.Wn) * uint32_t(C) * es;
-                uint32_t colv[kSW + KW - 1];
-#pragma unroll
-                for (int q = 0; q < kSW + KW - 1; ++q) {
-                    const int kk = kq + q - pw;
-                    colv[q] = kk >= 0 && kk < g.Wn ? uint32_t(kk * C + c0) * es : kBufLimit;
-                }
-                const uint32_t doff = uint32_t(f * g.Hn + j) * rowb;
-#pragma unroll
-                for (int q = 0; q < kSW; ++q) {
-                    const int kk = kq + q;
-                    const typename Vec4<E>::Raw r =
-                        Vec4<E>::load_buf(rd, doff + (kk < g.Wn ? uint32_t(kk * C + c0) * es : kBufLimit));
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) gv[q][e] = Vec4<E>::at(r, e);
-                }
-#pragma unroll
-                for (int b = 0; b < KH; ++b) {
-                    const int jj = j + b - ph;
-                    const uint32_t roff = jj >= 0 && jj < g.Hn ? uint32_t((f - a) * g.Hn + jj) * rowb : kBufLimit;
-                    typename Vec4<E>::Raw in[kSW + KW - 1];
-#pragma unroll
-                    for (int q = 0; q < kSW + KW - 1; ++q) in[q] = Vec4<E>::load_buf(rx, roff + colv[q]);
-#pragma unroll
-                    for (int q = 0; q < kSW + KW - 1; ++q) {
-                        float xf[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) xf[e] = Vec4<E>::at(in[q], e);
-#pragma unroll
-                        for (int d = 0; d < KW; ++d) {
-                            const int o = q - d;                // output column fed by this tap
-                            if (o < 0 || o >= kSW) continue;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) acc[b * KW + d][e] += xf[e] * gv[o][e];
-                        }
-                    }
-                }
-            } else {
-                const E* xs = x + v0 + c0;
-                const E* ds = dy + v0 + c0;
-                const int orow = (f * g.Hn + j) * g.Wn;
+            const int64_t v0 = int64_t(g.base + g.L) * C;
+            const E* xs = x + v0 + c0;
+            const E* ds = dy + v0 + c0;
+            const int orow = (f * g.Hn + j) * g.Wn;
+            {
+                float gv[kSW][8];
 #pragma unroll
                 for (int q = 0; q < kSW; ++q) {
                     const int kk = kq + q;
                     const bool ok = kk < g.Wn && orow + kk < g.past;
-                    const typename Vec4<E>::Raw r = Vec4<E>::load_raw(ds + int64_t(ok ? orow + kk : 0) * C, ok);
+                    const typename Vec8<E>::Raw r = Vec8<E>::load_raw(ds + int64_t(ok ? orow + kk : 0) * C, ok);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) gv[q][e] = Vec4<E>::at(r, e);
+                    for (int e = 0; e < 8; ++e) gv[q][e] = Vec8<E>::at(r, e);
                 }
 #pragma unroll
                 for (int b = 0; b < KH; ++b) {
                     const int jj = j + b - ph;
                     if (jj < 0 || jj >= g.Hn) continue;
                     const int row = ((f - a) * g.Hn + jj) * g.Wn;
-                    typename Vec4<E>::Raw in[kSW + KW - 1];
+                    typename Vec8<E>::Raw in[kSW + KW - 1];
 #pragma unroll
                     for (int q = 0; q < kSW + KW - 1; ++q) {
                         const int kk = kq + q - pw;
                         const bool ok = kk >= 0 && kk < g.Wn && row + kk < g.past;
-                        in[q] = Vec4<E>::load_raw(xs + int64_t(ok ? row + kk : 0) * C, ok);
+                        in[q] = Vec8<E>::load_raw(xs + int64_t(ok ? row + kk : 0) * C, ok);
                     }
 #pragma unroll
                     for (int q = 0; q < kSW + KW - 1; ++q)
@@ -549,28 +568,28 @@ __global__ __launch_bounds__(kCT) void kda_short_conv_dw_kernel(
                             const int o = q - d;
                             if (o < 0 || o >= kSW) continue;
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) acc[b * KW + d][e] += Vec4<E>::at(in[q], e) * gv[o][e];
+                            for (int e = 0; e < 8; ++e) acc[b * KW + d][e] += Vec8<E>::at(in[q], e) * gv[o][e];
                         }
                 }
             }
         }
     }
 
-    // the 16 strip lanes of each channel quad, added in lane order; one tap at a time
+    // the 32 strip lanes of each channel group, added in lane order; one tap at a time
     const int ntaps = kx + kt * kh * KW;
 #pragma unroll
     for (int s = 0; s < NACC; ++s) {
         const bool live = text ? s < kx : s / KW < kh;      // uniform over the workgroup
         if (!live) continue;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red[tid * 4 + e] = acc[s][e];
+        for (int e = 0; e < 8; ++e) red[tid * 8 + e] = acc[s][e];
         __syncthreads();
         if (tid < 64) {
-            const int q = tid >> 2, e = tid & 3, c = kCB * cb + 4 * q + e;
+            const int q = tid >> 3, e = tid & 7, c = kCB * cb + 8 * q + e;
             float sum = 0.f;
-            for (int l = 0; l < kDwLanes; ++l) sum += red[(l * 16 + q) * 4 + e];
+            for (int l = 0; l < kLanes; ++l) sum += red[(l * 8 + q) * 8 + e];
             const int tap = text ? s : kx + (a * kh + s / KW) * KW + s % KW;
-            if (c < C) partial[(int64_t(p) * ntaps + tap) * C + c] = sum;
+            if (c < C) partial[(int64_t(p) * ntaps + tap) * C + c] = sum;   // lanes past C hold no channel
         }
         __syncthreads();
     }

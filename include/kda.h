@@ -255,7 +255,7 @@ kda_status kda_short_conv(const void *x, const float *w_text, const float *w_vis
  * are formed per (channel block, slice of the tile list) and the slices then added in a
  * fixed order, so the result is the same bit for bit from run to run. A workspace of the
  * tile table plus parts * (k_text + k_t*k_h*k_w) * channels fp32 partial sums (parts is
- * about 4096 / (ceil(channels / 64) * (k_t + 1)), at least 1) comes from the stream-ordered
+ * about 2048 / (ceil(channels / 64) * (k_t + 1)), at least 1) comes from the stream-ordered
  * pool as for kda_forward. Execution and errors as kda_forward; the timing hook names the
  * kernels "conv_bwd_plan", "conv_dx", "conv_dw" and "conv_dw_reduce".
  */
