@@ -25,10 +25,10 @@
 //     reverse cumsum of dG over the chunk's rows.
 //
 // Kernels: a chunk table; a prep over all (chunk, head) pairs writing Kh, Kc, Qh, T, P,
-// gamma, b; a chain carrying S forwards that saves the state entering every chunk; a
-// chain carrying dS backwards that saves the gradient of the state leaving every chunk;
-// and a gradient kernel over all (chunk, head) pairs that rebuilds the chunk's
-// operands and applies the formulas above. For packs of few long samples each chain
+// M, gamma, b (and the norms' reciprocals); a chain carrying S forwards that saves the
+// state entering every chunk; a chain carrying dS backwards that saves the gradient of
+// the state leaving every chunk; and a gradient kernel over all (chunk, head) pairs that
+// reads the chunk's operands back from the prep's record and applies the formulas above. For packs of few long samples each chain
 // runs as two passes over segments of the samples (the sequence split below).
 //
 // MFMA: v_mfma_f32_16x16x4f32; lane (r = lane%16, g = lane/16) supplies A(r, k) and
@@ -110,7 +110,8 @@ template <typename E, int W> struct RowPieces {
     }
 };
 
-// Record of one (chunk, head) written by the prep for the two chains (floats).
+// Record of one (chunk, head) written by the prep: every chunk operand, for the two
+// chains and the gradient kernel (floats).
 template <int DK> struct BRec {
     static constexpr int KH = 0;                    // Kh [C][DK]
     static constexpr int KC = KH + kBC * DK;        // Kc [C][DK]
@@ -119,8 +120,12 @@ template <int DK> struct BRec {
     static constexpr int P = T + kBC * kBC;         // P  [C][C]
     static constexpr int GAM = P + kBC * kBC;       // gamma [DK]
     static constexpr int BETA = GAM + DK;           // b [C] (0 past the sample's end)
-    static constexpr int TOTAL = BETA + kBC;
-    static_assert(TOTAL % 4 == 0, "16-byte records");
+    static constexpr int M = BETA + kBC;            // M = Kh Kc^T [C][C]
+    static constexpr int QINV = M + kBC * kBC;      // 1/|q_t| [C] (1 without normalisation)
+    static constexpr int KINV = QINV + kBC;         // 1/|k_t| [C]
+    static constexpr int TOTAL = KINV + kBC;
+    static_assert(KC % 4 == 0 && QH % 4 == 0 && T % 4 == 0 && P % 4 == 0 && GAM % 4 == 0 && BETA % 4 == 0 &&
+                  M % 4 == 0 && QINV % 4 == 0 && KINV % 4 == 0 && TOTAL % 4 == 0, "16-byte fields and records");
 };
 
 // ---------------------------------------------------------------------------
@@ -437,9 +442,61 @@ __global__ __launch_bounds__(kBT) void kda_bwd_prep_kernel(
     for (int i = tid; i < kBC * kBC; i += kBT) {
         rec[R::T + i] = sm.t[(i / kBC) * kLC + i % kBC];
         rec[R::P + i] = sm.p[(i / kBC) * kLC + i % kBC];
+        rec[R::M + i] = sm.m[(i / kBC) * kLC + i % kBC];
     }
     if (tid < DK) rec[R::GAM + tid] = sm.gam[tid];
-    if (tid < kBC) rec[R::BETA + tid] = sm.beta[tid];
+    if (tid < kBC) {
+        rec[R::BETA + tid] = sm.beta[tid];
+        rec[R::QINV + tid] = sm.qinv[tid];
+        rec[R::KINV + tid] = sm.kinv[tid];
+    }
+}
+
+// The chunk operands of the gradient kernel, read back from the prep's record into the
+// LDS layout chunk_operands() builds (the same values, so the same gradients): every
+// 16-byte load is issued before the first LDS write. Ends with a barrier.
+template <int DK>
+__device__ __forceinline__ void record_operands(const ChunkLds& L, const float* __restrict__ rec)
+{
+    using R = BRec<DK>;
+    constexpr int LK = DK + 4;
+    constexpr int NK = kBC * DK / 4 / kBT;          // f32x4 per thread per [C][DK] array
+    static_assert(kBC * kBC / 4 == kBT, "one f32x4 of each [C][C] array per thread");
+    const int tid = threadIdx.x;
+    const f32x4* r4 = reinterpret_cast<const f32x4*>(rec);
+    f32x4 kh[NK], kc[NK], qh[NK];
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+        const int i = tid + j * kBT;
+        kh[j] = r4[R::KH / 4 + i];
+        kc[j] = r4[R::KC / 4 + i];
+        qh[j] = r4[R::QH / 4 + i];
+    }
+    const f32x4 t = r4[R::T / 4 + tid], p = r4[R::P / 4 + tid], m = r4[R::M / 4 + tid];
+    f32x4 small = zero4();                          // gamma, b, 1/|q|, 1/|k|
+    constexpr int NG = DK / 4, NB = kBC / 4;
+    if (tid < NG) small = r4[R::GAM / 4 + tid];
+    else if (tid < NG + NB) small = r4[R::BETA / 4 + tid - NG];
+    else if (tid < NG + 2 * NB) small = r4[R::QINV / 4 + tid - NG - NB];
+    else if (tid < NG + 3 * NB) small = r4[R::KINV / 4 + tid - NG - 2 * NB];
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+        const int e = 4 * (tid + j * kBT), row = e / DK, col = e % DK;
+        *reinterpret_cast<f32x4*>(L.kh + row * LK + col) = kh[j];
+        *reinterpret_cast<f32x4*>(L.kc + row * LK + col) = kc[j];
+        *reinterpret_cast<f32x4*>(L.qh + row * LK + col) = qh[j];
+    }
+    {
+        const int e = 4 * tid, row = e / kBC, col = e % kBC;
+        *reinterpret_cast<f32x4*>(L.t + row * kLC + col) = t;
+        *reinterpret_cast<f32x4*>(L.p + row * kLC + col) = p;
+        *reinterpret_cast<f32x4*>(L.m + row * kLC + col) = m;
+    }
+    if (tid < NG) *reinterpret_cast<f32x4*>(L.gam + 4 * tid) = small;
+    else if (tid < NG + NB) *reinterpret_cast<f32x4*>(L.beta + 4 * (tid - NG)) = small;
+    else if (tid < NG + 2 * NB) *reinterpret_cast<f32x4*>(L.qinv + 4 * (tid - NG - NB)) = small;
+    else if (tid < NG + 3 * NB) *reinterpret_cast<f32x4*>(L.kinv + 4 * (tid - NG - 2 * NB)) = small;
+    __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -867,9 +924,9 @@ template <typename E, int DK, int DV, bool NORM>
 __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ la,
     const E* __restrict__ beta, const E* __restrict__ d_out, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ chunk_off, const float* __restrict__ s_in, const float* __restrict__ ds_out,
-    E* __restrict__ dq, E* __restrict__ dk, E* __restrict__ dv, E* __restrict__ dla, E* __restrict__ dbeta,
-    int num_seqs, int H, int64_t total_tokens, int max_chunks)
+    const int32_t* __restrict__ chunk_off, const float* __restrict__ rec_ws, const float* __restrict__ s_in,
+    const float* __restrict__ ds_out, E* __restrict__ dq, E* __restrict__ dk, E* __restrict__ dv,
+    E* __restrict__ dla, E* __restrict__ dbeta, int num_seqs, int H, int64_t total_tokens, int max_chunks)
 {
     using S_ = GradLds<DK, DV>;
     constexpr int LK = S_::LK, LV = S_::LV;
@@ -899,7 +956,7 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
     StateBlock<DV> sb;
     sb.load(Sg, 0);
     const ChunkLds L{sm.qh, sm.kh, sm.kc, sm.m, sm.t, sm.p, sm.gam, sm.beta, sm.qinv, sm.kinv};
-    chunk_operands<E, DK, NORM>(L, q, k, la, beta, t0, nrow, H, h);   // ends with a barrier
+    record_operands<DK>(L, rec_ws + (int64_t(h) * max_chunks + c) * BRec<DK>::TOTAL);   // ends with a barrier
     pv.put(sm.x, LV, nrow);
     pd.put(sm.dout, LV, nrow);
 
@@ -1405,7 +1462,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, void* workspace, TimingHook* th)
     if ((e = set_smem(grad, grad_smem)) != hipSuccess) return e;
     if (th) th->begin("bwd_grad", a.stream);
     hipLaunchKernelGGL(grad, dim3(p.max_chunks, H), dim3(kBT), grad_smem, a.stream, q, k, v, la, beta, dout,
-                       a.cu_seqlens, chunk_off, s_in, ds_out, static_cast<E*>(a.dq), static_cast<E*>(a.dk),
+                       a.cu_seqlens, chunk_off, rec, s_in, ds_out, static_cast<E*>(a.dq), static_cast<E*>(a.dk),
                        static_cast<E*>(a.dv), static_cast<E*>(a.dlog_alpha), static_cast<E*>(a.dbeta), a.num_seqs,
                        H, a.total_tokens, p.max_chunks);
     if (th) th->end(a.stream);
