@@ -259,11 +259,11 @@ def test_backward_bad_arguments_are_rejected_without_launch(lib, kw, code):
 
 def test_backward_workspace_bytes(lib):
     from delta_rule_recurrent_kda_amd import kda
-    # 32-token chunks: chunk table, one fp32 record (Kh, Kc, Qh [32][d_k], T, P [32][32], gamma, b)
-    # and the state and its gradient (fp32 [d_k][d_v] each) per (chunk, head)
+    # 32-token chunks: chunk table, one fp32 record (Kh, Kc, Qh [32][d_k], T, P, M [32][32], gamma,
+    # b, 1/|q|, 1/|k|) and the state and its gradient (fp32 [d_k][d_v] each) per (chunk, head)
     T, N, H = 1000, 3, 2
     chunks = (T + 31) // 32 + N
-    rec = (3 * 32 * 128 + 2 * 32 * 32 + 128 + 32) * 4
+    rec = (3 * 32 * 128 + 3 * 32 * 32 + 128 + 3 * 32) * 4
     table = ((N + 1) * 4 + 255) // 256 * 256
     assert kda.backward_workspace_bytes(T, N, H, 128, 128) == table + chunks * H * (rec + 2 * 128 * 128 * 4)
     assert kda.backward_workspace_bytes(T, 0, H, 128, 128) == 0
