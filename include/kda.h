@@ -176,7 +176,7 @@ kda_status kda_forward_ex(const void *q, const void *k, const void *v, const voi
  * samples the chains run as two passes over segments of the samples (same results up to
  * rounding). Execution: enqueued on `stream`; takes a workspace of
  * kda_backward_workspace_bytes(...) bytes (chunk operands and the per-chunk state and
- * state gradient, about 5 KB per token and head at d = 128, plus per-segment summaries
+ * state gradient, about 6 KB per token and head at d = 128, plus per-segment summaries
  * when the chains are split) from the device's default stream-ordered pool, returned on
  * `stream` after the kernels. Results are bitwise reproducible for identical inputs, sizes
  * and device (partial sums are added in a fixed order, no atomics). Errors as kda_forward.
