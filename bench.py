@@ -447,6 +447,62 @@ def conv_backward_bench(args, x, wt, wv, cu, tl, gr, fwd_flops, fwd_bytes, sha, 
             "kernels": kernels}
 
 
+def shard_bench(args, dev):
+    """One GPU's share of the 30-second clip (config 4: 189,272 tokens, 16 heads, d = 128) under the
+    two splits the scan allows across GPUs, timed at its real shape:
+    - head split over 8 GPUs: the whole sequence with 2 of the 16 heads (no exchange);
+    - sequence split over 8 GPUs: one eighth of the tokens (23,659) with all 16 heads, scanned from
+      an initial state (kda_forward_from_state), as each GPU would after the all-gather of the
+      segment summaries.
+    Inputs are drawn on the device with the workload's distributions (q, k unit length, v ~ N(0,1),
+    log a ~ -U(0.0005, 0.05), beta = sigmoid(N(0,1))); K timed steps after W warm-ups."""
+    import torch
+    from delta_rule_recurrent_kda_amd import kda
+    g = torch.Generator(device=dev)
+    g.manual_seed(2468)
+
+    def draw(T, H, d=128):
+        q = torch.nn.functional.normalize(torch.randn((T, H, d), device=dev, generator=g), dim=-1)
+        k = torch.nn.functional.normalize(torch.randn((T, H, d), device=dev, generator=g), dim=-1)
+        v = torch.randn((T, H, d), device=dev, generator=g)
+        la = -(0.0005 + 0.0495 * torch.rand((T, H, d), device=dev, generator=g))
+        b = torch.sigmoid(torch.randn((T, H), device=dev, generator=g))
+        return [t.to(torch.bfloat16).contiguous() for t in (q, k, v, la, b)]
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - w0) * 1e3 / args.steps
+
+    out = {}
+    T = 512 + 121 * 30 * 52
+    q, k, v, la, b = draw(T, 2)
+    cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    o = torch.empty_like(v)
+    fs = torch.empty((1, 2, 128, 128), dtype=torch.float32, device=dev)
+    ms = timed(lambda: kda.kda_forward(q, k, v, la, b, cu, o, fs))
+    out["head_split_8"] = {"tokens": T, "heads": 2, "ms_per_step": ms, "value": T * 2 / (ms * 1e-3),
+                           "unit": "tokens/s"}
+    del q, k, v, la, b, o
+    Ts = (T + 7) // 8
+    q, k, v, la, b = draw(Ts, 16)
+    cu = torch.tensor([0, Ts], dtype=torch.int32, device=dev)
+    s0 = 0.05 * torch.randn((1, 16, 128, 128), device=dev, generator=g)
+    o = torch.empty_like(v)
+    fs = torch.empty((1, 16, 128, 128), dtype=torch.float32, device=dev)
+    ms = timed(lambda: kda.kda_forward(q, k, v, la, b, cu, o, fs, initial_state=s0))
+    out["sequence_split_8"] = {"tokens": Ts, "heads": 16, "ms_per_step": ms, "value": Ts * 16 / (ms * 1e-3),
+                               "unit": "tokens/s", "initial_state": True}
+    out["note"] = ("one GPU's share of config 4 (189,272 tokens x 16 heads) under an 8-way head or sequence split; "
+                   "the sequence split also needs the all-gather of the segment summaries and their prefix, not timed")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -456,6 +512,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
+    ap.add_argument("--no-shard", action="store_true")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after timing, run 3 plain device copies of this many MiB (for scaling "
                          "HBM byte counters)")
@@ -560,6 +617,8 @@ def main():
         rec["backward"] = backward_bench(args, spec, t, cu, dev)
     if not args.no_conv:
         rec["short_conv"] = conv_bench(args, spec, dev)
+    if not args.no_shard:
+        rec["shard"] = shard_bench(args, dev)
     if args.copy_calib_mib:
         n = args.copy_calib_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
