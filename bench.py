@@ -227,9 +227,13 @@ def cpu_baseline(spec, a):
 
 
 def measured_ceilings(dev):
-    """Rates this GPU reaches on plain work: a 1 GiB device copy (read + write bytes) and a
-    8192^3 bf16 matrix product (the vendor GEMM through torch, contiguous operands)."""
+    """Rates this GPU reaches on plain work: 1 GiB device copies (read + write bytes), torch's and
+    the probe library's grid-stride 16-byte copy at 4 and 8 workgroups per CU, the probe's
+    read-only pass, and a 8192^3 bf16 matrix product (the vendor GEMM through torch, contiguous
+    operands). bw_copy_GBs is the best copy."""
+    import ctypes
     import torch
+    from delta_rule_recurrent_kda_amd import build as kbuild
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
@@ -250,8 +254,23 @@ def measured_ceilings(dev):
 
     tc = timed(lambda: dst.copy_(src), 10)
     tg = timed(lambda: torch.matmul(a, b), 10)
+    out = {"bw_torch_copy_GBs": 2 * n / tc / 1e9, "mfma_bf16_gemm_TFLOPs": 2 * 8192 ** 3 / tg / 1e12}
+    probe = ctypes.CDLL(kbuild.PROBE_LIB)
+    probe.kda_bw_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                   ctypes.c_void_p]
+    probe.kda_bw_probe.restype = ctypes.c_int
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    for mode, key, factor in ((0, "bw_probe_copy_GBs", 2), (1, "bw_probe_read_GBs", 1)):
+        best = 0.0
+        for blocks in (1024, 2048):             # 4 and 8 workgroups per CU
+            def run():
+                if probe.kda_bw_probe(mode, src.data_ptr(), dst.data_ptr(), n, blocks, stream) != 0:
+                    raise RuntimeError("bandwidth probe launch failed")
+            best = max(best, factor * n / timed(run, 10) / 1e9)
+        out[key] = best
+    out["bw_copy_GBs"] = max(out["bw_torch_copy_GBs"], out["bw_probe_copy_GBs"])
     del src, dst, a, b
-    return {"bw_copy_GBs": 2 * n / tc / 1e9, "mfma_bf16_gemm_TFLOPs": 2 * 8192 ** 3 / tg / 1e12}
+    return out
 
 
 def flushed_steps(step, stream, dev, n: int) -> float:

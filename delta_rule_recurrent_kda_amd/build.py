@@ -9,6 +9,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
+# bandwidth probes for the benchmark's measured ceilings (not part of the scan library)
+PROBE_SRC = os.path.join(CSRC, "bw_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libkda_probe.so")
 SOURCES = [os.path.join(CSRC, "kda_fwd.hip"), os.path.join(CSRC, "kda_fwd_pipe.hip"),
            os.path.join(CSRC, "kda_wy.hip"), os.path.join(CSRC, "kda_bwd.hip"),
            os.path.join(CSRC, "kda_conv.hip"),
@@ -30,21 +33,29 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, *SOURCES]
+def _hipcc_shared(out: str, sources, verbose: bool) -> None:
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libkda.so")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"hipcc failed building {os.path.basename(out)}")
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Build libkda.so and the benchmark's bandwidth probes (libkda_probe.so)."""
+    _hipcc_shared(LIB, SOURCES, verbose)
+    _hipcc_shared(PROBE_LIB, [PROBE_SRC], verbose)
     return LIB
 
 
 def is_stale() -> bool:
-    if not os.path.exists(LIB):
+    if not os.path.exists(LIB) or not os.path.exists(PROBE_LIB):
+        return True
+    if os.path.getmtime(PROBE_SRC) > os.path.getmtime(PROBE_LIB):
         return True
     t = os.path.getmtime(LIB)
     return any(os.path.getmtime(s) > t for s in SOURCES + HEADERS)

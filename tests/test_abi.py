@@ -296,3 +296,18 @@ def test_workspace_bytes(lib):
     assert kda.workspace_bytes(1000, 2, 2, 128, 128, kda.KDA_F32) == 0
     assert kda.workspace_bytes(1000, 0, 2, 128, 128, kda.KDA_BF16) == 0
     assert kda.workspace_bytes(1000, 2, 2, 96, 128, kda.KDA_BF16) == 0
+
+
+def test_bandwidth_probe_library_builds_and_exports(lib):
+    from delta_rule_recurrent_kda_amd import build as kbuild
+    assert os.path.exists(kbuild.PROBE_LIB)
+    nm = subprocess.run(["nm", "-D", "--defined-only", kbuild.PROBE_LIB], capture_output=True, text=True,
+                        check=True).stdout
+    assert re.search(r"\bT kda_bw_probe$", nm, flags=re.M)
+    probe = ctypes.CDLL(kbuild.PROBE_LIB)
+    probe.kda_bw_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                   ctypes.c_void_p]
+    # bad arguments are refused before any launch
+    assert probe.kda_bw_probe(0, None, None, 16, 1, None) != 0
+    assert probe.kda_bw_probe(2, 0x100000, 0x200000, 16, 1, None) != 0
+    assert probe.kda_bw_probe(0, 0x100000, 0x200000, 15, 1, None) != 0
