@@ -107,18 +107,19 @@ def test_short_conv_backward_vs_oracle(case):
     _check(91, shapes, C, ks, dt, name)
 
 
-@pytest.mark.parametrize("label,shapes,C", [
-    ("clip5s_full_width", [(512, 21, 30, 52)], 2048),      # 5-second clip, 16 heads x 128 channels
-    ("image4", [(256, 1, 64, 64)] * 4, 256),               # four images, 256 text tokens + 64 x 64 each
+@pytest.mark.parametrize("label,shapes,C,dt", [
+    ("clip5s_full_width", [(512, 21, 30, 52)], 2048, "bf16"),   # 5-second clip, 16 heads x 128 channels
+    ("image4", [(256, 1, 64, 64)] * 4, 256, "bf16"),            # four images, 256 text tokens + 64 x 64 each
+    ("clip5s_f32", [(512, 21, 30, 52)], 256, "f32"),            # the fp32 data path at the clip's layout
 ])
-def test_short_conv_backward_exact_at_full_size(label, shapes, C):
+def test_short_conv_backward_exact_at_full_size(label, shapes, C, dt):
     """Small-integer inputs: every product and partial sum is exact, so the kernels must match
     the oracle bit for bit, at the sizes and launch shape the benchmark uses."""
     import oracle
     ks = (4, 3, 3, 3)
-    x, dy, wt, wv, cu, tl, gr = _case(92, shapes, C, ks, "bf16", integer=True)
-    gu.log(f"case short conv backward exact {label}: {len(x)} tokens, C={C}")
-    dx, dwt, dwv = _run(x, dy, wt, wv, cu, tl, gr, "bf16")
+    x, dy, wt, wv, cu, tl, gr = _case(92, shapes, C, ks, dt, integer=True)
+    gu.log(f"case short conv backward exact {label}: {len(x)} tokens, C={C}, {dt}")
+    dx, dwt, dwv = _run(x, dy, wt, wv, cu, tl, gr, dt)
     rdx, rdwt, rdwv = oracle.short_conv_backward(x, wt, wv, cu, tl, gr, dy)
     for name, got, ref in (("dx", dx, rdx), ("dw_text", dwt, rdwt), ("dw_vis", dwv, rdwv)):
         bad = int(np.count_nonzero(got != ref))

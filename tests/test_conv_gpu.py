@@ -82,6 +82,31 @@ def test_short_conv_clip5s_layout():
     _check(82, [(512, 21, 30, 52)], 128, (4, 3, 3, 3), "bf16", "clip5s layout")
 
 
+@pytest.mark.parametrize("label,shapes,C,dt", [
+    ("clip5s_full_width", [(512, 21, 30, 52)], 2048, "bf16"),   # the benchmark's layout and width
+    ("image4", [(256, 1, 64, 64)] * 4, 256, "bf16"),
+    ("clip5s_f32", [(512, 21, 30, 52)], 256, "f32"),
+])
+def test_short_conv_exact_at_full_size(label, shapes, C, dt):
+    """Inputs and weights in {-1, 0, 1}: every product and partial sum is exact in fp32 and every
+    output (|y| <= 31) exact in bf16, so the kernel must equal the oracle bit for bit."""
+    import oracle
+    rng = np.random.default_rng(86)
+    lens = [L + T * H * W for L, T, H, W in shapes]
+    x = rng.integers(-1, 2, (sum(lens), C)).astype(np.float64)
+    wt = rng.integers(-1, 2, (4, C)).astype(np.float32)
+    wv = rng.integers(-1, 2, (3, 3, 3, C)).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    tl = np.array([s[0] for s in shapes], np.int32)
+    gr = np.array([s[1:] for s in shapes], np.int32).reshape(-1, 3)
+    gu.log(f"case short conv exact {label}: {len(x)} tokens, C={C}, {dt}")
+    y = _run(x, wt, wv, cu, tl, gr, dt)
+    ref = oracle.short_conv(x, wt, wv, cu, tl, gr)
+    bad = int(np.count_nonzero(y != ref))
+    gu.log(f"[{label}] {bad} of {ref.size} differ")
+    assert bad == 0
+
+
 def test_short_conv_image_batch_layout():
     # four images: 256 text tokens + a 64 x 64 grid each
     _check(83, [(256, 1, 64, 64)] * 4, 64, (4, 3, 3, 3), "bf16", "image4 layout")
