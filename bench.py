@@ -148,9 +148,9 @@ def bwd_kernel_macs(spec, kernel: str) -> int:
     """Multiply-adds of the matrix products of one launch (32-token chunks, fp32 MFMA)."""
     C, dk, dv = BWD_C, spec.dk, spec.dv
     per = {
-        # M, P; X, dVn state term, dKbar, dQh and dKh state terms; Vn, dVn P term, dP, Z,
-        # dT and the four chunk-internal products; dA
-        "bwd_grad": 2 * C * C * dk + 5 * C * dk * dv + 5 * C * C * dv + 4 * C * C * dk + 2 * C ** 3,
+        # X, dVn state term, dKbar, dQh and dKh state terms; Vn, dVn P term, dP, Z, dT and
+        # the four chunk-internal products; dA (M and P come with the prep's record)
+        "bwd_grad": 5 * C * dk * dv + 5 * C * C * dv + 4 * C * C * dk + 2 * C ** 3,
         "bwd_prep": 2 * C * C * dk,
         "bwd_state": 2 * C * dk * dv + C * C * dv,
         "bwd_dstate": 3 * C * dk * dv + 2 * C * C * dv,
@@ -168,10 +168,11 @@ def bwd_kernel_bytes(spec, kernel: str) -> int:
     C, dk, dv, H, T = BWD_C, spec.dk, spec.dv, spec.heads, spec.total_tokens
     ch = bwd_chunk_heads(spec)
     state = ch * dk * dv * 4
-    if kernel == "bwd_grad":    # q, k, log a, v, dO, beta; S and dS per chunk; five gradients
-        return T * H * (3 * dk + 2 * dv + 1) * es + 2 * state + T * H * (2 * dk + dk + dv + 1) * es
-    if kernel == "bwd_prep":    # q, k, log a, beta; Kh, Kc, Qh, T, P, gamma, beta records
-        return T * H * (3 * dk + 1) * es + ch * (3 * C * dk + 2 * C * C + dk + C) * 4
+    rec = ch * (3 * C * dk + 3 * C * C + dk + 3 * C) * 4     # Kh, Kc, Qh, T, P, M, gamma, b, 1/|q|, 1/|k|
+    if kernel == "bwd_grad":    # the records, log a, v, dO; S and dS per chunk; five gradients
+        return rec + T * H * (dk + 2 * dv) * es + 2 * state + T * H * (2 * dk + dk + dv + 1) * es
+    if kernel == "bwd_prep":    # q, k, log a, beta; the records
+        return T * H * (3 * dk + 1) * es + rec
     if kernel == "bwd_state":   # Kh, Kc, T, gamma, beta records and V; S per chunk
         return ch * (2 * C * dk + C * C + dk + C) * 4 + T * H * dv * es + state
     if kernel == "bwd_dstate":  # Kh, Kc, Qh, T, P, gamma, beta records and dO; dS per chunk
