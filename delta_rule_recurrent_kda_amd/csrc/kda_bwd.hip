@@ -1372,6 +1372,33 @@ BwdPlan bwd_plan(int64_t total_tokens, int32_t num_seqs, int32_t num_heads, int 
     return p;
 }
 
+// A second stream per host thread and device, with a fork and a join event: the two
+// chains of the backward are independent (the state-gradient chain reads the records and
+// dO, never S), so the state-gradient chain runs beside the state chain and takes the CUs
+// that the state chain's shorter samples leave idle. Default priority; created on first use.
+struct SideStream {
+    int dev = -1;
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+hipError_t side_stream(SideStream*& out)
+{
+    static thread_local SideStream cache[16];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 16) return hipErrorInvalidDevice;
+    SideStream& s = cache[dev];
+    if (!s.stream) {
+        if ((e = hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&s.fork, hipEventDisableTiming)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&s.join, hipEventDisableTiming)) != hipSuccess) return e;
+        s.dev = dev;
+    }
+    out = &s;
+    return hipSuccess;
+}
+
 template <typename K> hipError_t set_smem(K kern, size_t bytes) {
     return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                int(bytes));
@@ -1426,36 +1453,50 @@ hipError_t launch_bwd_t(const BwdArgs& a, void* workspace, TimingHook* th)
     const int units = p.lseg ? p.max_segs * H : a.num_seqs * H;
     const int ublocks = ((units + 7) / 8) * 8;
     const size_t chain_smem = sizeof(ChainLds<DK>);
-    auto launch_state = [&](auto kern, int ntiles, const char* name) -> hipError_t {
+    auto launch_state = [&](auto kern, int ntiles, const char* name, hipStream_t st) -> hipError_t {
         hipError_t err = set_smem(kern, chain_smem);
         if (err != hipSuccess) return err;
-        if (th) th->begin(name, a.stream);
-        hipLaunchKernelGGL(kern, dim3(ublocks * ntiles), dim3(kBT), chain_smem, a.stream, v, a.cu_seqlens, chunk_off,
+        if (th) th->begin(name, st);
+        hipLaunchKernelGGL(kern, dim3(ublocks * ntiles), dim3(kBT), chain_smem, st, v, a.cu_seqlens, chunk_off,
                            seg_off, rec, a.init_state, s_in, sloc, phi, phi_t, a.num_seqs, H, a.total_tokens,
                            p.max_chunks, p.lseg, p.max_segs);
-        if (th) th->end(a.stream);
+        if (th) th->end(st);
         return hipGetLastError();
     };
-    auto launch_dstate = [&](auto kern, const char* name) -> hipError_t {
+    auto launch_dstate = [&](auto kern, const char* name, hipStream_t st) -> hipError_t {
         hipError_t err = set_smem(kern, chain_smem);
         if (err != hipSuccess) return err;
-        if (th) th->begin(name, a.stream);
-        hipLaunchKernelGGL(kern, dim3(ublocks * (DV / 64)), dim3(kBT), chain_smem, a.stream, dout, a.cu_seqlens,
+        if (th) th->begin(name, st);
+        hipLaunchKernelGGL(kern, dim3(ublocks * (DV / 64)), dim3(kBT), chain_smem, st, dout, a.cu_seqlens,
                            chunk_off, seg_off, rec, a.d_final_state, ds_out, a.d_init_state, phi_t, eseg, a.num_seqs, H,
                            a.total_tokens, p.max_chunks, p.lseg, p.max_segs);
-        if (th) th->end(a.stream);
+        if (th) th->end(st);
         return hipGetLastError();
     };
+    // fork: the state chain on the side stream once the prep is done; the state-gradient
+    // chain, the longer of the two, goes first on the caller's stream so that it takes
+    // the CUs first
+    SideStream* ss = nullptr;
+    if ((e = side_stream(ss)) != hipSuccess) return e;
+    if ((e = hipEventRecord(ss->fork, a.stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(ss->stream, ss->fork, 0)) != hipSuccess) return e;
     if (p.lseg == 0) {
-        if ((e = launch_state(kda_bwd_state_kernel<E, DK, DV, 0>, DV / 64, "bwd_state")) != hipSuccess) return e;
-        if ((e = launch_dstate(kda_bwd_dstate_kernel<E, DK, DV, 0>, "bwd_dstate")) != hipSuccess) return e;
-    } else {
-        if ((e = launch_state(kda_bwd_state_kernel<E, DK, DV, 1>, DV / 64 + DK / 64, "bwd_state_seg")) != hipSuccess)
+        if ((e = launch_dstate(kda_bwd_dstate_kernel<E, DK, DV, 0>, "bwd_dstate", a.stream)) != hipSuccess) return e;
+        if ((e = launch_state(kda_bwd_state_kernel<E, DK, DV, 0>, DV / 64, "bwd_state", ss->stream)) != hipSuccess)
             return e;
-        if ((e = launch_state(kda_bwd_state_kernel<E, DK, DV, 2>, DV / 64, "bwd_state")) != hipSuccess) return e;
-        if ((e = launch_dstate(kda_bwd_dstate_kernel<E, DK, DV, 1>, "bwd_dstate_seg")) != hipSuccess) return e;
-        if ((e = launch_dstate(kda_bwd_dstate_kernel<E, DK, DV, 2>, "bwd_dstate")) != hipSuccess) return e;
+    } else {
+        if ((e = launch_dstate(kda_bwd_dstate_kernel<E, DK, DV, 1>, "bwd_dstate_seg", a.stream)) != hipSuccess)
+            return e;
+        if ((e = launch_dstate(kda_bwd_dstate_kernel<E, DK, DV, 2>, "bwd_dstate", a.stream)) != hipSuccess) return e;
+        if ((e = launch_state(kda_bwd_state_kernel<E, DK, DV, 1>, DV / 64 + DK / 64, "bwd_state_seg", ss->stream)) !=
+            hipSuccess)
+            return e;
+        if ((e = launch_state(kda_bwd_state_kernel<E, DK, DV, 2>, DV / 64, "bwd_state", ss->stream)) != hipSuccess)
+            return e;
     }
+    // join: the gradient kernel needs both chains
+    if ((e = hipEventRecord(ss->join, ss->stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(a.stream, ss->join, 0)) != hipSuccess) return e;
 
     const size_t grad_smem = sizeof(GradLds<DK, DV>);
     auto grad = kda_bwd_grad_kernel<E, DK, DV, NORM>;

@@ -174,7 +174,10 @@ kda_status kda_forward_ex(const void *q, const void *k, const void *v, const voi
  * Arithmetic is fp32 throughout (fp32 MFMA), over 32-token chunks; results in the data
  * dtype, rounded to nearest-even. Same size limits as kda_forward. For packs of few long
  * samples the chains run as two passes over segments of the samples (same results up to
- * rounding). Execution: enqueued on `stream`; takes a workspace of
+ * rounding). Execution: enqueued on `stream`. The state chain runs on a second stream
+ * that the library keeps per host thread and device (default priority): it waits for
+ * `stream` after the prep, and `stream` waits for it before the gradient kernel, so the
+ * call is ordered on `stream` as a whole. Takes a workspace of
  * kda_backward_workspace_bytes(...) bytes (chunk operands and the per-chunk state and
  * state gradient, about 6 KB per token and head at d = 128, plus per-segment summaries
  * when the chains are split) from the device's default stream-ordered pool, returned on

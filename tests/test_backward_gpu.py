@@ -183,3 +183,36 @@ def test_backward_bitwise_deterministic():
     g2 = _run(spec, a, do, dfs, s0, False)
     for name, x, y in zip(NAMES, g1, g2):
         assert np.array_equal(x, y), name
+
+
+def test_backward_on_two_caller_streams():
+    """The chains run on the caller's stream and a second internal stream, forked after the
+    prep and joined before the gradient kernel: two calls enqueued back to back on two other
+    streams, with no host synchronisation between them, give the default-stream gradients bit
+    for bit."""
+    import torch
+    from delta_rule_recurrent_kda_amd import kda
+    spec = inputs.KdaSpec("bwd_streams", (700, 2100, 96), 2, 128, 128, "bf16", (0.001, 0.1), 7475)
+    gu.log("case backward on two caller streams")
+    a = inputs.generate(spec)
+    d = gu.device_inputs(spec, a)
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(79)
+    do = torch.randn((spec.total_tokens, spec.heads, spec.dv), device="cuda:0", generator=g).to(torch.bfloat16)
+    args = (d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"], do)
+    ref = [t.clone() for t in kda.backward(*args) if t is not None]
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s1):
+        r1 = kda.backward(*args, stream=s1)
+    with torch.cuda.stream(s2):
+        r2 = kda.backward(*args, stream=s2)
+    torch.cuda.synchronize()
+    for res in (r1, r2):
+        got = [t for t in res if t is not None]
+        for x, y in zip(got, ref):
+            bx = x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32)
+            by = y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32)
+            assert torch.equal(bx, by)
