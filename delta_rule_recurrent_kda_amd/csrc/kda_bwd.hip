@@ -131,13 +131,17 @@ template <int DK> struct BRec {
 // ---------------------------------------------------------------------------
 // chunk table: chunk_off[n] = number of 32-token chunks of samples 0..n-1; with the
 // sequence split (lseg > 0 chunks per segment) also seg_off[n] = number of segments of
-// samples 0..n-1, every sample having at least one (an empty sample has one, empty)
+// samples 0..n-1, every sample having at least one (an empty sample has one, empty).
+// order[r] = the sample with the r-th most chunks (ties by index) for packs of at most
+// 1024 samples, else r: chain units walk samples longest first, so the chains that set
+// the length of a pass start first when CUs free up.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void kda_bwd_plan_kernel(const int32_t* __restrict__ cu,
                                                             int32_t* __restrict__ chunk_off, int32_t* __restrict__ seg_off,
-                                                            int num_seqs, int64_t total_tokens, int lseg)
+                                                            int32_t* __restrict__ order, int num_seqs,
+                                                            int64_t total_tokens, int lseg)
 {
-    __shared__ int32_t part[1024], spart[1024];
+    __shared__ int32_t part[1024], spart[1024], len[1024];
     const int tid = threadIdx.x;
     int32_t carry = 0, scarry = 0;
     for (int base = 0; base < num_seqs; base += 1024) {
@@ -151,7 +155,15 @@ __global__ __launch_bounds__(1024) void kda_bwd_plan_kernel(const int32_t* __res
         }
         part[tid] = cnt;
         spart[tid] = scnt;
+        len[tid] = cnt;
         __syncthreads();
+        if (num_seqs <= 1024 && n < num_seqs) {     // one block of samples: rank by length
+            int rank = 0;
+            for (int j = 0; j < num_seqs; ++j) rank += len[j] > cnt || (len[j] == cnt && j < n);
+            order[rank] = n;
+        } else if (n < num_seqs) {
+            order[n] = n;
+        }
         for (int d = 1; d < 1024; d <<= 1) {
             const int32_t add = tid >= d ? part[tid - d] : 0;
             const int32_t sadd = tid >= d ? spart[tid - d] : 0;
@@ -200,8 +212,8 @@ struct ChainSpan {
     int64_t t0, s1;                 // first token of the span, end of the sample
 };
 __device__ __forceinline__ bool chain_span(int sid, const int32_t* cu, const int32_t* chunk_off,
-                                           const int32_t* seg_off, int num_seqs, int lseg, int max_chunks,
-                                           int max_segs, int64_t T, ChainSpan& o) {
+                                           const int32_t* seg_off, const int32_t* order, int num_seqs, int lseg,
+                                           int max_chunks, int max_segs, int64_t T, ChainSpan& o) {
     int n = sid, seg = 0, nseg = 1;
     if (lseg > 0) {
         if (sid >= min(seg_off[num_seqs], max_segs)) return false;
@@ -215,6 +227,8 @@ __device__ __forceinline__ bool chain_span(int sid, const int32_t* cu, const int
         nseg = seg_off[n + 1] - seg_off[n];
     } else if (sid >= num_seqs) {
         return false;
+    } else {
+        n = order[sid];                 // samples longest first
     }
     const int cs0 = min(chunk_off[n], max_chunks), cs1 = min(chunk_off[n + 1], max_chunks);
     o.n = n;
@@ -638,7 +652,8 @@ __device__ __forceinline__ void seg_prefix_grad(f32x4 (&dS)[DK / 16], const floa
 template <typename E, int DK, int DV, int MODE>
 __global__ __launch_bounds__(kBT) void kda_bwd_state_kernel(
     const E* __restrict__ v, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
-    const int32_t* __restrict__ seg_off, const float* __restrict__ rec_ws, const float* __restrict__ init_state,
+    const int32_t* __restrict__ seg_off, const int32_t* __restrict__ order, const float* __restrict__ rec_ws,
+    const float* __restrict__ init_state,
     float* __restrict__ s_in, float* __restrict__ sloc, float* __restrict__ phi, float* __restrict__ phi_t,
     int num_seqs, int H, int64_t total_tokens, int max_chunks, int lseg, int max_segs)
 {
@@ -652,7 +667,7 @@ __global__ __launch_bounds__(kBT) void kda_bwd_state_kernel(
     chain_unit(blockIdx.x, NT, unit, tile);
     const int sid = unit / H, h = unit % H;
     ChainSpan sp;
-    if (!chain_span(sid, cu, chunk_off, seg_off, num_seqs, MODE == 0 ? 0 : lseg, max_chunks, max_segs, total_tokens,
+    if (!chain_span(sid, cu, chunk_off, seg_off, order, num_seqs, MODE == 0 ? 0 : lseg, max_chunks, max_segs, total_tokens,
                     sp))
         return;
     if (MODE == 1 && sp.nseg == 1) return;
@@ -751,7 +766,8 @@ __global__ __launch_bounds__(kBT) void kda_bwd_state_kernel(
 template <typename E, int DK, int DV, int MODE>
 __global__ __launch_bounds__(kBT) void kda_bwd_dstate_kernel(
     const E* __restrict__ d_out, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
-    const int32_t* __restrict__ seg_off, const float* __restrict__ rec_ws, const float* __restrict__ d_final,
+    const int32_t* __restrict__ seg_off, const int32_t* __restrict__ order, const float* __restrict__ rec_ws,
+    const float* __restrict__ d_final,
     float* __restrict__ ds_out, float* __restrict__ d_init, const float* __restrict__ phi_t, float* __restrict__ eseg,
     int num_seqs, int H, int64_t total_tokens, int max_chunks, int lseg, int max_segs)
 {
@@ -764,7 +780,7 @@ __global__ __launch_bounds__(kBT) void kda_bwd_dstate_kernel(
     chain_unit(blockIdx.x, DV / 64, unit, vt);
     const int sid = unit / H, h = unit % H;
     ChainSpan sp;
-    if (!chain_span(sid, cu, chunk_off, seg_off, num_seqs, MODE == 0 ? 0 : lseg, max_chunks, max_segs, total_tokens,
+    if (!chain_span(sid, cu, chunk_off, seg_off, order, num_seqs, MODE == 0 ? 0 : lseg, max_chunks, max_segs, total_tokens,
                     sp))
         return;
     if (MODE == 1 && sp.nseg == 1) return;
@@ -1363,7 +1379,7 @@ BwdPlan bwd_plan(int64_t total_tokens, int32_t num_seqs, int32_t num_heads, int 
     // every sample has at most ceil(chunks / lseg) <= chunks / lseg + 1 segments, and the
     // chunks of all samples number at most chunks_bound + num_seqs
     p.max_segs = p.lseg ? int((chunks_bound + num_seqs + p.lseg - 1) / p.lseg + num_seqs) : 0;
-    p.table_bytes = (2 * (size_t(num_seqs) + 1) * sizeof(int32_t) + 255) & ~size_t(255);
+    p.table_bytes = ((3 * size_t(num_seqs) + 2) * sizeof(int32_t) + 255) & ~size_t(255);
     const size_t rec = d_k == 128 ? BRec<128>::TOTAL : BRec<64>::TOTAL;
     p.rec_bytes = size_t(p.max_chunks) * num_heads * rec * sizeof(float);
     p.state_bytes = size_t(p.max_chunks) * num_heads * d_k * d_v * sizeof(float);
@@ -1411,6 +1427,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, void* workspace, TimingHook* th)
     char* base = static_cast<char*>(workspace);
     int32_t* chunk_off = reinterpret_cast<int32_t*>(base);
     int32_t* seg_off = chunk_off + (a.num_seqs + 1);
+    int32_t* order = seg_off + (a.num_seqs + 1);
     char* next = base + p.table_bytes;
     float* rec = reinterpret_cast<float*>(next);
     next += p.rec_bytes;
@@ -1436,7 +1453,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, void* workspace, TimingHook* th)
 
     if (th) th->begin("bwd_plan", a.stream);
     hipLaunchKernelGGL(kda_bwd_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, chunk_off,
-                       p.lseg ? seg_off : nullptr, a.num_seqs, a.total_tokens, p.lseg);
+                       p.lseg ? seg_off : nullptr, order, a.num_seqs, a.total_tokens, p.lseg);
     if (th) th->end(a.stream);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
@@ -1458,7 +1475,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, void* workspace, TimingHook* th)
         if (err != hipSuccess) return err;
         if (th) th->begin(name, st);
         hipLaunchKernelGGL(kern, dim3(ublocks * ntiles), dim3(kBT), chain_smem, st, v, a.cu_seqlens, chunk_off,
-                           seg_off, rec, a.init_state, s_in, sloc, phi, phi_t, a.num_seqs, H, a.total_tokens,
+                           seg_off, order, rec, a.init_state, s_in, sloc, phi, phi_t, a.num_seqs, H, a.total_tokens,
                            p.max_chunks, p.lseg, p.max_segs);
         if (th) th->end(st);
         return hipGetLastError();
@@ -1468,7 +1485,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, void* workspace, TimingHook* th)
         if (err != hipSuccess) return err;
         if (th) th->begin(name, st);
         hipLaunchKernelGGL(kern, dim3(ublocks * (DV / 64)), dim3(kBT), chain_smem, st, dout, a.cu_seqlens,
-                           chunk_off, seg_off, rec, a.d_final_state, ds_out, a.d_init_state, phi_t, eseg, a.num_seqs, H,
+                           chunk_off, seg_off, order, rec, a.d_final_state, ds_out, a.d_init_state, phi_t, eseg, a.num_seqs, H,
                            a.total_tokens, p.max_chunks, p.lseg, p.max_segs);
         if (th) th->end(st);
         return hipGetLastError();

@@ -264,7 +264,7 @@ def test_backward_workspace_bytes(lib):
     T, N, H = 1000, 3, 2
     chunks = (T + 31) // 32 + N
     rec = (3 * 32 * 128 + 3 * 32 * 32 + 128 + 3 * 32) * 4
-    table = ((N + 1) * 4 + 255) // 256 * 256
+    table = ((3 * N + 2) * 4 + 255) // 256 * 256      # chunk and segment tables, longest-first order
     assert kda.backward_workspace_bytes(T, N, H, 128, 128) == table + chunks * H * (rec + 2 * 128 * 128 * 4)
     assert kda.backward_workspace_bytes(T, 0, H, 128, 128) == 0
 
