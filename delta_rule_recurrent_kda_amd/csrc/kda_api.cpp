@@ -56,6 +56,45 @@ kda_status check_overlaps(const Span* outs, int nout, const Span* ins, int nin)
     return KDA_OK;
 }
 
+}  // namespace
+
+namespace kda {
+
+hipError_t aux_stream(int idx, AuxStream*& out)
+{
+    static thread_local AuxStream cache[16][4];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 16 || idx < 0 || idx >= 4) return hipErrorInvalidValue;
+    AuxStream& s = cache[dev][idx];
+    if (!s.stream) {
+        AuxStream n;
+        if ((e = hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming)) != hipSuccess) return e;
+        s = n;
+    }
+    out = &s;
+    return hipSuccess;
+}
+
+hipError_t aux_fork(hipStream_t main, AuxStream* aux)
+{
+    hipError_t e = hipEventRecord(aux->fork, main);
+    return e != hipSuccess ? e : hipStreamWaitEvent(aux->stream, aux->fork, 0);
+}
+
+hipError_t aux_join(hipStream_t main, AuxStream* aux)
+{
+    hipError_t e = hipEventRecord(aux->join, aux->stream);
+    return e != hipSuccess ? e : hipStreamWaitEvent(main, aux->join, 0);
+}
+
+}  // namespace kda
+
+namespace {
+
 bool validate_env()
 {
     const char* e = std::getenv("KDA_VALIDATE");

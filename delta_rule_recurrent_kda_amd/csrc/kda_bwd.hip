@@ -1388,33 +1388,6 @@ BwdPlan bwd_plan(int64_t total_tokens, int32_t num_seqs, int32_t num_heads, int 
     return p;
 }
 
-// A second stream per host thread and device, with a fork and a join event: the two
-// chains of the backward are independent (the state-gradient chain reads the records and
-// dO, never S), so the state-gradient chain runs beside the state chain and takes the CUs
-// that the state chain's shorter samples leave idle. Default priority; created on first use.
-struct SideStream {
-    int dev = -1;
-    hipStream_t stream = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-};
-hipError_t side_stream(SideStream*& out)
-{
-    static thread_local SideStream cache[16];
-    int dev = -1;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 16) return hipErrorInvalidDevice;
-    SideStream& s = cache[dev];
-    if (!s.stream) {
-        if ((e = hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking)) != hipSuccess) return e;
-        if ((e = hipEventCreateWithFlags(&s.fork, hipEventDisableTiming)) != hipSuccess) return e;
-        if ((e = hipEventCreateWithFlags(&s.join, hipEventDisableTiming)) != hipSuccess) return e;
-        s.dev = dev;
-    }
-    out = &s;
-    return hipSuccess;
-}
-
 template <typename K> hipError_t set_smem(K kern, size_t bytes) {
     return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                int(bytes));
@@ -1490,13 +1463,14 @@ hipError_t launch_bwd_t(const BwdArgs& a, void* workspace, TimingHook* th)
         if (th) th->end(st);
         return hipGetLastError();
     };
-    // fork: the state chain on the side stream once the prep is done; the state-gradient
-    // chain, the longer of the two, goes first on the caller's stream so that it takes
-    // the CUs first
-    SideStream* ss = nullptr;
-    if ((e = side_stream(ss)) != hipSuccess) return e;
-    if ((e = hipEventRecord(ss->fork, a.stream)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(ss->stream, ss->fork, 0)) != hipSuccess) return e;
+    // The two chains are independent (the state-gradient chain reads the records and dO,
+    // never S). Fork: the state chain on an auxiliary stream once the prep is done; the
+    // state-gradient chain, the longer of the two, goes first on the caller's stream so
+    // that it takes the CUs first, and the state chain gets the CUs its shorter samples
+    // free.
+    AuxStream* ss = nullptr;
+    if ((e = aux_stream(0, ss)) != hipSuccess) return e;
+    if ((e = aux_fork(a.stream, ss)) != hipSuccess) return e;
     if (p.lseg == 0) {
         if ((e = launch_dstate(kda_bwd_dstate_kernel<E, DK, DV, 0>, "bwd_dstate", a.stream)) != hipSuccess) return e;
         if ((e = launch_state(kda_bwd_state_kernel<E, DK, DV, 0>, DV / 64, "bwd_state", ss->stream)) != hipSuccess)
@@ -1512,8 +1486,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, void* workspace, TimingHook* th)
             return e;
     }
     // join: the gradient kernel needs both chains
-    if ((e = hipEventRecord(ss->join, ss->stream)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(a.stream, ss->join, 0)) != hipSuccess) return e;
+    if ((e = aux_join(a.stream, ss)) != hipSuccess) return e;
 
     const size_t grad_smem = sizeof(GradLds<DK, DV>);
     auto grad = kda_bwd_grad_kernel<E, DK, DV, NORM>;

@@ -91,6 +91,20 @@ hipError_t launch_short_conv_backward(const ConvBwdArgs& a, void* workspace, Tim
 size_t conv_bwd_workspace_bytes(int32_t num_seqs, int32_t channels, int32_t k_text, int32_t k_t, int32_t k_h,
                                 int32_t k_w);
 
+// Auxiliary streams for work that runs beside the caller's stream inside one call: idx
+// 0..3, one set per host thread and device, default priority, created on first use, each
+// with a fork event (recorded on the caller's stream, waited on by the aux stream) and a
+// join event (recorded on the aux stream, waited on by the caller's stream).
+struct AuxStream {
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+hipError_t aux_stream(int idx, AuxStream*& out);
+// fork: `aux` starts after the work enqueued so far on `main`
+hipError_t aux_fork(hipStream_t main, AuxStream* aux);
+// join: work enqueued next on `main` waits for the work enqueued so far on `aux`
+hipError_t aux_join(hipStream_t main, AuxStream* aux);
+
 // LDS bytes one workgroup uses.
 size_t smem_bytes(int dtype_bf16, int d_k);
 size_t smem_bytes_pipe(int d_k);
