@@ -1,14 +1,17 @@
 """Benchmark of the KDA forward scan on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload packed8|image4|clip5s|clip30s|tiny]
+                [--no-backward] [--no-conv] [--no-shard] [--no-cpu-baseline] [--copy-calib-mib M]
 
 A step is one kda_forward call over the whole packed batch (every stage of the
 scan runs inside it: chunk table, chunk prep, state chain). Inputs are generated
 once, copied to HBM, and the timed region holds exactly K back-to-back steps
 between two device synchronisations. Inside the timed region the library records
 HIP events on the launch stream around each of its kernels; the roofline entry is
-for the kernel with the largest average duration, priced with that kernel's own
-algorithmic bytes. Prints one JSON line.
+for the kernel with the largest time per step, priced with that kernel's own
+algorithmic bytes per launch. The same line carries the backward, the short
+convolution and its backward, one GPU's share under a head or sequence split, the
+measured ceilings and the oracle's CPU rate. Prints one JSON line.
 """
 from __future__ import annotations
 

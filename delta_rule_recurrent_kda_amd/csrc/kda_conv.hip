@@ -28,6 +28,10 @@
 //   - A plan kernel counts the tiles per sample; a fixed grid of workgroups walks the tile
 //     list channel-block-major, each XCD a contiguous part of it, with the weights of the
 //     current channel block in LDS.
+// The reverse mode (the gradients for a given dy) reuses the tiles: dx is the same kernel
+// run on dy with the taps mirrored and time and text walked forward (REV); the weight
+// gradients are sums over all tokens, formed per (channel block, slice of the tile list,
+// time offset) in fp32 and added in a fixed order by a reduce kernel.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
