@@ -222,3 +222,39 @@ def test_short_conv_backward_timing_hook():
         n, ms = kda.timing_read(name)
         assert n == 1 and ms > 0, name
     torch.cuda.synchronize()
+
+
+def test_short_conv_at_the_offset_limit():
+    """Tokens x channels just under 2^31, the library's limit for 32-bit element offsets: 21,845
+    identical samples (16 text tokens and a 2 x 4 x 4 grid) at 2,048 channels, 4.3 GB per bf16
+    tensor. With inputs and weights in {-1, 0, 1} every result is exact, so every sample's y
+    and dx must equal the oracle on one sample, and dw_text and dw_vis must equal 21,845 times
+    the one-sample weight gradients (|sum| < 2^24)."""
+    import torch
+    import oracle
+    from delta_rule_recurrent_kda_amd import kda
+    C, L, grid1 = 2048, 16, (2, 4, 4)
+    n1 = L + grid1[0] * grid1[1] * grid1[2]
+    N = (2 ** 31 - 1) // (n1 * C)
+    assert N * n1 * C < 2 ** 31 and (N + 1) * n1 * C >= 2 ** 31
+    ks = (4, 3, 3, 3)
+    x1, dy1, wt, wv, cu1, tl1, gr1 = _case(96, [(L, *grid1)], C, ks, "bf16", integer=True)
+    y_ref = oracle.short_conv(x1, wt, wv, cu1, tl1, gr1)
+    dx_ref, dwt_ref, dwv_ref = oracle.short_conv_backward(x1, wt, wv, cu1, tl1, gr1, dy1)
+    gu.log(f"case short conv at the offset limit: {N} samples x {n1} tokens x {C} channels = {N * n1 * C} elements")
+    dev = "cuda:0"
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    x = _dev(x1, "bf16").repeat(N, 1)
+    dy = _dev(dy1, "bf16").repeat(N, 1)
+    cu = torch.arange(N + 1, dtype=torch.int32, device=dev) * n1
+    tl = torch.full((N,), L, dtype=torch.int32, device=dev)
+    gr = torch.tensor([list(grid1)], dtype=torch.int32, device=dev).repeat(N, 1)
+    y = kda.short_conv(x, t(wt), t(wv), cu, tl, gr)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(N, n1, C).float(), t(y_ref).float().unsqueeze(0).expand(N, n1, C))
+    del y
+    dx, dwt, dwv = kda.short_conv_backward(x, t(wt), t(wv), cu, tl, gr, dy)
+    torch.cuda.synchronize()
+    assert torch.equal(dx.view(N, n1, C).float(), t(dx_ref).float().unsqueeze(0).expand(N, n1, C))
+    assert np.array_equal(dwt.cpu().double().numpy(), N * dwt_ref)
+    assert np.array_equal(dwv.cpu().double().numpy(), N * dwv_ref)
