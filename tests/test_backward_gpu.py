@@ -216,3 +216,15 @@ def test_backward_on_two_caller_streams():
             bx = x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32)
             by = y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32)
             assert torch.equal(bx, by)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_backward_without_decay(dt):
+    """log a = 0 (a = 1, no forgetting): every decay factor of the chunked form is exactly 1."""
+    spec = inputs.KdaSpec(f"bwd_nodecay_{dt}", (129, 0, 300, 64), 2, 128, 128, dt, (0.0, 0.0), 7272)
+    gu.log(f"case backward without decay, {dt}")
+    a = inputs.generate(spec)
+    do, dfs, s0 = _draw_grads(spec, 73)
+    got = _run(spec, a, do, dfs, s0, False)
+    ref = _oracle(spec, a, do, dfs, s0, False)
+    _compare(spec, got, ref, f"backward without decay {dt}")

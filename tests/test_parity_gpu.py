@@ -271,3 +271,40 @@ def test_kernel_timing_records_each_kernel():
         assert kda.timing_read("scan") == (0, 0.0)
     finally:
         kda.timing_enable(False)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_without_decay(dt):
+    """log a = 0 (a = 1, no forgetting): every decay factor of the chunked form is exactly 1."""
+    spec = inputs.KdaSpec(f"nodecay_{dt}", (129, 0, 300, 64), 2, 128, 128, dt, (0.0, 0.0), 7373)
+    _check(spec, label=f"no decay {dt}")
+
+
+def test_exact_recall():
+    """a = 1, b = 1 and unit keys: reading with the key just written returns the value just
+    written (the write replaces the stored value along the key). Tokens 0..127 write the
+    columns of a random orthogonal matrix, tokens 128..255 the same directions again in another
+    order with new values, so a failed erase would leak the old value into the readout. With
+    q_t = k_t every output row must be v_t; checked against the oracle and against v, at the
+    bf16 tolerance."""
+    rng = np.random.default_rng(74)
+    T, H, D = 256, 2, 128
+    Q, _ = np.linalg.qr(rng.standard_normal((D, D)))
+    k = np.zeros((T, H, D))
+    for h in range(H):
+        k[:D, h] = Q.T
+        k[D:, h] = Q.T[rng.permutation(D)]
+    v = rng.standard_normal((T, H, D))
+    spec = inputs.KdaSpec("recall", (T,), H, D, D, "bf16", (0.0, 0.0), 1)
+    kb = inputs.f64_to_bf16_bits(k)
+    a = {"q": kb, "k": kb, "v": inputs.f64_to_bf16_bits(v), "log_alpha": np.zeros((T, H, D), np.uint16),
+         "beta": inputs.f64_to_bf16_bits(np.ones((T, H))), "cu_seqlens": spec.cu_seqlens()}
+    gu.log("case exact recall")
+    d = gu.device_inputs(spec, a)
+    out, fs = gu.run_hip(spec, d)
+    o_ref, f_ref = gu.oracle_ref(spec, a)
+    gu.compare(spec, out, fs, o_ref, f_ref, label="exact recall")
+    vb = inputs.bf16_bits_to_f64(a["v"])
+    err = np.linalg.norm(out - vb, axis=2) / np.linalg.norm(vb, axis=2)
+    gu.log(f"[exact recall] worst row |o - v| / |v| = {err.max():.3e}")
+    assert err.max() <= 3e-2
