@@ -258,3 +258,59 @@ def test_short_conv_at_the_offset_limit():
     assert torch.equal(dx.view(N, n1, C).float(), t(dx_ref).float().unsqueeze(0).expand(N, n1, C))
     assert np.array_equal(dwt.cpu().double().numpy(), N * dwt_ref)
     assert np.array_equal(dwv.cpu().double().numpy(), N * dwv_ref)
+
+
+def test_short_conv_sample_over_one_gib():
+    """One sample of 512 text tokens and a 169 x 30 x 52 grid at 2,048 channels: 1.0006 GiB of
+    bf16 grid tokens, past what the kernels address with buffer loads, so they take the checked
+    path. Every frame holds the same values (small integers, exact arithmetic), which fixes the
+    results from the oracle on the same sample cut to 4 and 5 frames:
+      y:  frames 0 and 1 as in the 5-frame sample, every later frame as its frame 2;
+      dx: frames up to T-3 as the 5-frame sample's frame 0, the last two as its last two;
+      dw: dw(5) + (T - 5) (dw(5) - dw(4)), a frame with every time tap inside the grid adding
+          dw(5) - dw(4)."""
+    import torch
+    import oracle
+    from delta_rule_recurrent_kda_amd import kda
+    C, L, Tf, Hh, Ww = 2048, 512, 169, 30, 52
+    assert Tf * Hh * Ww * C * 2 > 1 << 30
+    ks = (4, 3, 3, 3)
+    rng = np.random.default_rng(97)
+    xt = rng.integers(-1, 2, (L, C)).astype(np.float64)
+    gt = rng.integers(-1, 2, (L, C)).astype(np.float64)
+    xf = rng.integers(-1, 2, (Hh * Ww, C)).astype(np.float64)      # one frame, repeated
+    gf = rng.integers(-1, 2, (Hh * Ww, C)).astype(np.float64)
+    wt = rng.integers(-1, 2, (ks[0], C)).astype(np.float32)
+    wv = rng.integers(-1, 2, (ks[1], ks[2], ks[3], C)).astype(np.float32)
+
+    def ref(nf):
+        x = np.concatenate([xt] + [xf] * nf)
+        g = np.concatenate([gt] + [gf] * nf)
+        tabs = (np.array([0, len(x)], np.int32), np.array([L], np.int32), np.array([[nf, Hh, Ww]], np.int32))
+        return oracle.short_conv(x, wt, wv, *tabs), oracle.short_conv_backward(x, wt, wv, *tabs, g)
+
+    y5, (dx5, dwt5, dwv5) = ref(5)
+    _, (_, dwt4, dwv4) = ref(4)
+    gu.log(f"case short conv sample over 1 GiB: {L + Tf * Hh * Ww} tokens, C={C}")
+    dev = "cuda:0"
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    fr = Hh * Ww
+    x = torch.cat([_dev(xt, "bf16"), _dev(xf, "bf16").repeat(Tf, 1)])
+    dy = torch.cat([_dev(gt, "bf16"), _dev(gf, "bf16").repeat(Tf, 1)])
+    tabs = (t(np.array([0, len(x)], np.int32)), t(np.array([L], np.int32)), t(np.array([[Tf, Hh, Ww]], np.int32)))
+    y = kda.short_conv(x, t(wt), t(wv), *tabs).float()
+    torch.cuda.synchronize()
+    y5t = t(y5).float()
+    assert torch.equal(y[:L + 2 * fr], y5t[:L + 2 * fr])
+    assert torch.equal(y[L + 2 * fr:].view(Tf - 2, fr, C), y5t[L + 2 * fr:L + 3 * fr].unsqueeze(0).expand(Tf - 2, fr, C))
+    del y
+    dx, dwt, dwv = kda.short_conv_backward(x, t(wt), t(wv), *tabs, dy)
+    torch.cuda.synchronize()
+    dx = dx.float()
+    dx5t = t(dx5).float()
+    assert torch.equal(dx[:L], dx5t[:L])
+    assert torch.equal(dx[L:L + (Tf - 2) * fr].view(Tf - 2, fr, C),
+                       dx5t[L:L + fr].unsqueeze(0).expand(Tf - 2, fr, C))
+    assert torch.equal(dx[L + (Tf - 2) * fr:], dx5t[L + 3 * fr:])
+    assert np.array_equal(dwt.cpu().double().numpy(), dwt5 + (Tf - 5) * (dwt5 - dwt4))
+    assert np.array_equal(dwv.cpu().double().numpy(), dwv5 + (Tf - 5) * (dwv5 - dwv4))
