@@ -11,7 +11,8 @@ HIP events on the launch stream around each of its kernels; the roofline entry i
 for the kernel with the largest time per step, priced with that kernel's own
 algorithmic bytes per launch. The same line carries the backward, the short
 convolution and its backward, one GPU's share under a head or sequence split, the
-measured ceilings and the oracle's CPU rate. Prints one JSON line.
+step replayed from a HIP graph, the measured ceilings and the oracle's CPU rate.
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -275,6 +276,28 @@ def measured_ceilings(dev):
     out["bw_copy_GBs"] = max(out["bw_torch_copy_GBs"], out["bw_probe_copy_GBs"])
     del src, dst, a, b
     return out
+
+
+def graph_steps(step, n: int) -> float:
+    """ms per step when the step is captured once in a HIP graph and replayed n times back to
+    back (the same kernels without the host's launch work)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    g.replay()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for _ in range(n):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - w0) * 1e3 / n
 
 
 def flushed_steps(step, stream, dev, n: int) -> float:
@@ -562,8 +585,9 @@ def main():
     fs = torch.empty((len(spec.seq_lens), spec.heads, spec.dk, spec.dv), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        kda.kda_forward(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], cu, out, fs, stream=stream)
+    def step():     # on torch's current stream: the default stream, or the capture stream of a graph
+        kda.kda_forward(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], cu, out, fs,
+                        stream=torch.cuda.current_stream(dev))
 
     for _ in range(args.warmup):
         step()
@@ -583,6 +607,7 @@ def main():
     kda.timing_enable(False)
     ms_per_step = wall * 1e3 / args.steps
     flushed = flushed_steps(step, stream, dev, 20)
+    graph_ms = graph_steps(step, args.steps)
     # a kernel may run several times per step (the pipelined forward launches the prep and the
     # chain once per sample group): bytes per launch = the step's bytes / launches per step,
     # so that bytes per launch / mean launch duration = the step's bytes / the kernel's time
@@ -629,6 +654,8 @@ def main():
                      "kernel_sha": kernel_sha()},
         "kernels": kernels,
         "path": {"algorithmic_bytes": bytes_, "achieved_GBs": path_gbs, "frac_hbm": path_gbs / HBM_PEAK_GBS},
+        "graph": {"ms_per_step": graph_ms, "value": spec.head_tokens / (graph_ms * 1e-3),
+                  "note": "the same step captured once in a HIP graph and replayed K times back to back"},
         "flushed": {"ms_per_step_median": flushed, "value": spec.head_tokens / (flushed * 1e-3),
                     "note": "one step at a time after writing 512 MiB (evicts L2 and the 256 MB Infinity "
                             "Cache); HIP events on the launch stream around the step only"},

@@ -77,7 +77,10 @@ typedef enum {
  *
  * Execution: enqueued on `stream` (NULL = the null stream) and returns without
  * synchronising; buffers must stay valid until the stream reaches the work. The
- * library keeps no pointer after returning. For bf16 data the default scan takes a
+ * library keeps no pointer after returning. Every entry point may be captured into a
+ * HIP graph by stream capture on a non-null stream: workspaces are stream-ordered
+ * allocations, other streams are forked and joined by events, and no call records a
+ * memset. For bf16 data the default scan takes a
  * workspace of kda_workspace_bytes(...) bytes (about 1.2 KB per token and head)
  * from the device's default stream-ordered memory pool (hipMallocAsync on `stream`,
  * released with hipFreeAsync on `stream` after the kernels; the pool keeps the
