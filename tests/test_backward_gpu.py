@@ -136,6 +136,31 @@ def test_backward_config3_sampled_head():
     _sampled(inputs.config(3), [3], 76)
 
 
+def test_backward_config4_sampled_head():
+    """The 30-second-clip workload (one sample of 189,272 tokens, 16 heads, the chains split
+    into segments) on the GPU; the oracle on head 9. Only that head's slices come back to
+    the host."""
+    import torch
+    from delta_rule_recurrent_kda_amd import kda
+    spec = inputs.config(4)
+    heads = [9]
+    gu.log("case backward config 4 (one sample, 189,272 tokens), head 9")
+    a = inputs.generate(spec)
+    do, _, _ = _draw_grads(spec, 77)
+    d = gu.device_inputs(spec, a)
+    tdo = torch.from_numpy(do.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    g = kda.backward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"], tdo)
+    torch.cuda.synchronize()
+    got = [x[:, heads].float().cpu().double().numpy() for x in g]
+    del g, d, tdo
+    sl = {x: a[x][:, heads] for x in ("q", "k", "v", "log_alpha", "beta")}
+    sl["cu_seqlens"] = a["cu_seqlens"]
+    sub = inputs.KdaSpec(spec.name, spec.seq_lens, len(heads), spec.dk, spec.dv, spec.dtype,
+                         spec.log_alpha_range, spec.seed)
+    ref = _oracle(sub, sl, do[:, heads], None, None, False)
+    _compare(sub, got, ref, f"backward {spec.name} heads {heads}")
+
+
 def test_backward_timing_records_each_kernel():
     import torch
     from delta_rule_recurrent_kda_amd import kda
