@@ -94,7 +94,7 @@ template <typename E, int DK, int C, bool NORM>
 __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ la, const E* __restrict__ beta, const int32_t* __restrict__ cu,
-    E* __restrict__ out, float* __restrict__ final_state,
+    E* __restrict__ out, float* __restrict__ final_state, const float* __restrict__ init_state,
     int num_seqs, int H, int DV)
 {
     using EL = Elt<E>;
@@ -141,10 +141,20 @@ __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
     // the blocks of P and -A above the diagonal are never written: clear once
     for (int i = tid; i < C * LDC; i += kThreads) { sm.p[i] = E(0); sm.ab[i] = E(0); }
 
-    // state: wave owns value columns [16*wave, 16*wave+16) of the tile; NCT tiles of 16 key rows
+    // state: wave owns value columns [16*wave, 16*wave+16) of the tile; NCT tiles of 16 key rows,
+    // lane (r, g) element i of tile ct = S[16ct + 4g + i][col0 + 16 wave + r]; zero at the start
+    // of the sample, or the given state
     f32x4 S[NCT];
+    if (init_state) {
+        const float* is = init_state + ((int64_t(n) * H + h) * DK) * DV + col0 + 16 * wave + r;
 #pragma unroll
-    for (int i = 0; i < NCT; ++i) S[i] = zero4();
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[ct][i] = is[int64_t(16 * ct + 4 * g + i) * DV];
+    } else {
+#pragma unroll
+        for (int i = 0; i < NCT; ++i) S[i] = zero4();
+    }
 
     // ---- raw loads of one chunk into registers --------------------------------
     Vec rq[RPT], rk[RPT], rla[RPT];
@@ -540,7 +550,7 @@ hipError_t launch_t(const LaunchArgs& a)
     hipLaunchKernelGGL(kern, grid, block, shmem, a.stream,
                        static_cast<const E*>(a.q), static_cast<const E*>(a.k), static_cast<const E*>(a.v),
                        static_cast<const E*>(a.log_alpha), static_cast<const E*>(a.beta), a.cu_seqlens,
-                       static_cast<E*>(a.out), a.final_state, a.num_seqs, a.num_heads, a.d_v);
+                       static_cast<E*>(a.out), a.final_state, a.init_state, a.num_seqs, a.num_heads, a.d_v);
     return hipGetLastError();
 }
 

@@ -106,7 +106,6 @@ def _call_from_state(kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(initial_state=0x900004), 4),                 # misaligned
     (dict(final_state=0x900000), 3),                   # final_state aliases initial_state
-    (dict(dtype=0), 5),                              # fp32 scan takes no initial state
     (dict(d_k=96), 5),
     (dict(q=None), 1),
 ])
@@ -136,7 +135,6 @@ def _call_ex(kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(options=2), 5),                            # unknown option bit
     (dict(options=0x80000001), 5),
-    (dict(initial_state=0x900000, dtype=0), 5),        # fp32 scan takes no initial state
     (dict(d_v=96), 5),
     (dict(k=None), 1),
     (dict(out=0x200000), 3),

@@ -137,11 +137,19 @@ def test_single_kernel_variants(monkeypatch, variant, case):
         _check(spec, label=f"ragged d64 {variant}")
 
 
-@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64)])
-def test_initial_state_vs_oracle(dk, dv):
+# (d_k, d_v, dtype, scan variant): the default two-kernel scan for bf16 data, the sequential
+# kernel for fp32 data and for bf16 data when selected
+INIT = [(128, 128, "bf16", None), (64, 64, "bf16", None), (128, 64, "bf16", None),
+        (128, 128, "f32", None), (64, 128, "f32", None), (128, 64, "bf16", "sequential")]
+
+
+@pytest.mark.parametrize("dk,dv,dt,variant", INIT, ids=[f"{a}x{b}_{c}_{d or 'default'}" for a, b, c, d in INIT])
+def test_initial_state_vs_oracle(monkeypatch, dk, dv, dt, variant):
     import torch
-    spec = inputs.KdaSpec(f"init_{dk}_{dv}", (129, 0, 64, 200, 1, 63), 3, dk, dv, "bf16", (0.001, 0.1), 5151)
-    gu.log(f"case initial_state dk={dk} dv={dv}")
+    if variant:
+        monkeypatch.setenv("KDA_SCAN_VARIANT", variant)
+    spec = inputs.KdaSpec(f"init_{dk}_{dv}_{dt}", (129, 0, 64, 200, 1, 63), 3, dk, dv, dt, (0.001, 0.1), 5151)
+    gu.log(f"case initial_state dk={dk} dv={dv} {dt} {variant or 'default'}")
     a = inputs.generate(spec)
     d = gu.device_inputs(spec, a)
     s0 = np.random.default_rng(17).standard_normal((len(spec.seq_lens), spec.heads, dk, dv)) * 0.5
@@ -308,3 +316,33 @@ def test_exact_recall():
     err = np.linalg.norm(out - vb, axis=2) / np.linalg.norm(vb, axis=2)
     gu.log(f"[exact recall] worst row |o - v| / |v| = {err.max():.3e}")
     assert err.max() <= 3e-2
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_all_samples_empty(dt):
+    """No tokens in any sample (T = 0, N = 2): the final state is the initial state (zero without
+    one), and the backward passes d_final_state straight to d_initial_state."""
+    import torch
+    from delta_rule_recurrent_kda_amd import kda
+    gu.log(f"case all samples empty, {dt}")
+    dev = "cuda:0"
+    H, dk, dv = 2, 128, 128
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    q, k, la = (torch.empty((0, H, dk), dtype=tdt, device=dev) for _ in range(3))
+    v = torch.empty((0, H, dv), dtype=tdt, device=dev)
+    beta = torch.empty((0, H), dtype=tdt, device=dev)
+    cu = torch.zeros(3, dtype=torch.int32, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(81)
+    s0 = torch.randn((2, H, dk, dv), device=dev, generator=g)
+    dfs = torch.randn((2, H, dk, dv), device=dev, generator=g)
+    out, fs = kda.forward(q, k, v, la, beta, cu)
+    torch.cuda.synchronize()
+    assert out.shape == (0, H, dv) and torch.count_nonzero(fs).item() == 0
+    out, fs = kda.forward(q, k, v, la, beta, cu, initial_state=s0)
+    torch.cuda.synchronize()
+    assert torch.equal(fs, s0)
+    grads = kda.backward(q, k, v, la, beta, cu, torch.empty_like(v), d_final_state=dfs, initial_state=s0)
+    torch.cuda.synchronize()
+    assert all(x.numel() == 0 for x in grads[:5])
+    assert torch.equal(grads[5], dfs)
