@@ -547,8 +547,6 @@ kda_status check_args(const void* q, const void* k, const void* v, const void* l
         if (st != KDA_OK) return st;
     }
     if (num_seqs == 0) return KDA_OK;
-    if (initial_state && dtype == KDA_BF16 && variant_env() == Variant::Pipe)
-        return fail(KDA_E_UNSUPPORTED, "initial_state is not supported by the pipelined scan");
     if ((options & KDA_OPT_QK_L2NORM) && dtype == KDA_BF16 && variant_env() == Variant::Pipe)
         return fail(KDA_E_UNSUPPORTED, "KDA_OPT_QK_L2NORM is not supported by the pipelined scan");
 

@@ -101,7 +101,8 @@ template <int DK>
 __global__ __launch_bounds__(kPThreads) void kda_fwd_pipe_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ la, const uint16_t* __restrict__ beta, const int32_t* __restrict__ cu,
-    uint16_t* __restrict__ out, float* __restrict__ final_state, int num_seqs, int H, int DV)
+    uint16_t* __restrict__ out, float* __restrict__ final_state, const float* __restrict__ init_state,
+    int num_seqs, int H, int DV)
 {
     using EL = Elt<uint16_t>;
     using Frag = EL::Frag;
@@ -147,9 +148,19 @@ __global__ __launch_bounds__(kPThreads) void kda_fwd_pipe_kernel(
         sm.slot[0].ab[i] = 0; sm.slot[1].ab[i] = 0;
     }
 
+    // the state, in waves 0-3 (16 value columns each): zero at the start of the sample, or
+    // the given state, in the layout of the final_state write below
     f32x4 S[NCT];
+    if (init_state && wave < 4) {
+        const float* is = init_state + ((int64_t(n) * H + h) * DK) * DV + col0 + 16 * wave + r;
 #pragma unroll
-    for (int i = 0; i < NCT; ++i) S[i] = zero4();
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[ct][i] = is[int64_t(16 * ct + 4 * g + i) * DV];
+    } else {
+#pragma unroll
+        for (int i = 0; i < NCT; ++i) S[i] = zero4();
+    }
 
     // ---- raw loads, one chunk ahead ---------------------------------------------
     // One register set: the rows of chunk c+1 are loaded at the end of the
@@ -464,7 +475,7 @@ hipError_t launch_pipe(const LaunchArgs& a)
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.log_alpha),
                        static_cast<const uint16_t*>(a.beta), a.cu_seqlens, static_cast<uint16_t*>(a.out),
-                       a.final_state, a.num_seqs, a.num_heads, a.d_v);
+                       a.final_state, a.init_state, a.num_seqs, a.num_heads, a.d_v);
     return hipGetLastError();
 }
 

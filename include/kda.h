@@ -115,9 +115,8 @@ kda_status kda_forward(const void *q, const void *k, const void *v, const void *
  *   initial_state : [num_seqs][num_heads][d_k][d_v] fp32 DEVICE pointer, rows = key
  *                   channels, 16-byte aligned; read only; may not overlap final_state.
  *                   NULL means zero states (then identical to kda_forward).
- * All other arguments, errors and execution as kda_forward. Supported for fp32 and
- * bf16 data on the default scans; KDA_E_UNSUPPORTED with KDA_SCAN_VARIANT=pipe
- * (non-NULL initial_state).
+ * All other arguments, errors and execution as kda_forward; supported for fp32 and
+ * bf16 data on every scan variant.
  */
 kda_status kda_forward_from_state(const void *q, const void *k, const void *v,
                                   const void *log_alpha, const void *beta,

@@ -115,12 +115,6 @@ def test_from_state_bad_arguments_are_rejected_without_launch(lib, kw, code):
     assert msg
 
 
-def test_from_state_on_single_kernel_variant_is_unsupported(lib, monkeypatch):
-    monkeypatch.setenv("KDA_SCAN_VARIANT", "pipe")
-    st, msg = _call_from_state({})
-    assert st == 5 and "initial_state" in msg
-
-
 def _call_ex(kw):
     from delta_rule_recurrent_kda_amd import kda
     a = dict(q=0x100000, k=0x200000, v=0x300000, log_alpha=0x400000, beta=0x500000, cu_seqlens=0x600000,

@@ -138,9 +138,10 @@ def test_single_kernel_variants(monkeypatch, variant, case):
 
 
 # (d_k, d_v, dtype, scan variant): the default two-kernel scan for bf16 data, the sequential
-# kernel for fp32 data and for bf16 data when selected
+# kernel for fp32 data and for bf16 data when selected, and the pipelined kernel
 INIT = [(128, 128, "bf16", None), (64, 64, "bf16", None), (128, 64, "bf16", None),
-        (128, 128, "f32", None), (64, 128, "f32", None), (128, 64, "bf16", "sequential")]
+        (128, 128, "f32", None), (64, 128, "f32", None), (128, 64, "bf16", "sequential"),
+        (128, 128, "bf16", "pipe"), (64, 64, "bf16", "pipe")]
 
 
 @pytest.mark.parametrize("dk,dv,dt,variant", INIT, ids=[f"{a}x{b}_{c}_{d or 'default'}" for a, b, c, d in INIT])
