@@ -160,19 +160,20 @@ Timing g_timing;
 
 // The device's default stream-ordered pool keeps freed workspace for reuse instead of
 // returning it to the driver at every synchronisation.
+std::mutex g_pool_mu;
+std::vector<bool> g_pool_done;           // devices whose default pool the library has prepared
+
 bool prepare_pool(int dev)
 {
-    static std::mutex mu;
-    static std::vector<bool> done;
-    std::lock_guard<std::mutex> lk(mu);
+    std::lock_guard<std::mutex> lk(g_pool_mu);
     if (dev < 0) return false;
-    if (size_t(dev) >= done.size()) done.resize(size_t(dev) + 1, false);
-    if (done[size_t(dev)]) return true;
+    if (size_t(dev) >= g_pool_done.size()) g_pool_done.resize(size_t(dev) + 1, false);
+    if (g_pool_done[size_t(dev)]) return true;
     hipMemPool_t pool = nullptr;
     if (hipDeviceGetDefaultMemPool(&pool, dev) != hipSuccess) return false;
     uint64_t thr = UINT64_MAX;
     if (hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr) != hipSuccess) return false;
-    done[size_t(dev)] = true;
+    g_pool_done[size_t(dev)] = true;
     return true;
 }
 
@@ -186,6 +187,19 @@ kda_status run(const kda::LaunchArgs& a);
 }  // namespace
 
 extern "C" {
+
+kda_status kda_release(void)
+{
+    std::lock_guard<std::mutex> lk(g_pool_mu);
+    for (size_t d = 0; d < g_pool_done.size(); ++d) {
+        if (!g_pool_done[d]) continue;
+        hipMemPool_t pool = nullptr;
+        hipError_t e = hipDeviceGetDefaultMemPool(&pool, int(d));
+        if (e == hipSuccess) e = hipMemPoolTrimTo(pool, 0);
+        if (e != hipSuccess) return fail(KDA_E_HIP, "kda_release, device %zu: %s", d, hipGetErrorString(e));
+    }
+    return KDA_OK;
+}
 
 const char* kda_status_str(kda_status s)
 {

@@ -119,6 +119,13 @@ def timing_enable(on: bool) -> None:
     library().kda_timing_enable(1 if on else 0)
 
 
+def release() -> None:
+    """kda_release: give the workspace memory that earlier calls freed back to the driver."""
+    st = library().kda_release()
+    if st != 0:
+        raise KdaError(st, library().kda_last_error().decode())
+
+
 def timing_read(kernel: str):
     """(launches, total milliseconds) of the named kernel since the last read."""
     n = ctypes.c_int32(0)

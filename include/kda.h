@@ -297,6 +297,19 @@ size_t kda_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_h
 kda_status kda_timing_enable(int32_t on);
 kda_status kda_timing_read(const char *kernel, int32_t *launches, double *total_ms);
 
+/*
+ * kda_release -- give the workspace memory that earlier calls freed back to the driver.
+ *
+ * Every entry point takes its workspace from the default stream-ordered pool of the
+ * device (hipMallocAsync on the caller's stream) and returns it there in stream order
+ * (hipFreeAsync); the library raises that pool's release threshold so the memory is
+ * kept for the next call. This call trims the default pool of every device the library
+ * has used down to the memory still held (hipMemPoolTrimTo, nothing kept): memory that
+ * pending work still uses stays allocated. It enqueues nothing and may be called from
+ * any host thread. Returns KDA_OK, or KDA_E_HIP with the HIP message in kda_last_error().
+ */
+kda_status kda_release(void);
+
 /* Static string naming a status code. */
 const char *kda_status_str(kda_status status);
 

@@ -29,7 +29,11 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert {"kda_forward", "kda_forward_from_state", "kda_forward_ex", "kda_backward", "kda_backward_workspace_bytes",
             "kda_short_conv", "kda_short_conv_backward", "kda_workspace_bytes", "kda_timing_enable",
-            "kda_timing_read", "kda_status_str", "kda_last_error", "kda_version"} <= set(declared_functions())
+            "kda_timing_read", "kda_release", "kda_status_str", "kda_last_error", "kda_version"} <= set(declared_functions())
+
+
+def test_release_before_any_call_is_ok(lib):
+    assert lib.kda_release() == 0
 
 
 def test_every_declared_symbol_is_exported(lib):

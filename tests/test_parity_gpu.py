@@ -347,3 +347,29 @@ def test_all_samples_empty(dt):
     torch.cuda.synchronize()
     assert all(x.numel() == 0 for x in grads[:5])
     assert torch.equal(grads[5], dfs)
+
+
+def test_release_between_calls():
+    """kda_release after a forward and a backward gives the pooled workspace back; the next
+    calls allocate again and give the same results bit for bit."""
+    import torch
+    from delta_rule_recurrent_kda_amd import kda
+    spec = inputs.KdaSpec("release", (700, 2100, 96), 2, 128, 128, "bf16", (0.001, 0.1), 7476)
+    gu.log("case release between calls")
+    a = inputs.generate(spec)
+    d = gu.device_inputs(spec, a)
+    args = (d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"])
+    do = torch.ones((spec.total_tokens, spec.heads, spec.dv), dtype=torch.bfloat16, device="cuda:0")
+    o1, f1 = kda.forward(*args)
+    g1 = kda.backward(*args, do)
+    torch.cuda.synchronize()
+    kda.release()
+    o2, f2 = kda.forward(*args)
+    g2 = kda.backward(*args, do)
+    torch.cuda.synchronize()
+    kda.release()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(f1, f2)
+    for x, y in zip(g1, g2):
+        bx = x.view(torch.int16) if x.dtype == torch.bfloat16 else x
+        by = y.view(torch.int16) if y.dtype == torch.bfloat16 else y
+        assert torch.equal(bx, by)
