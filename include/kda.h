@@ -77,14 +77,14 @@ typedef enum {
  *
  * Execution: enqueued on `stream` (NULL = the null stream) and returns without
  * synchronising; buffers must stay valid until the stream reaches the work. The
- * library keeps no pointer after returning. Every entry point may be captured into a
+ * library keeps no pointer after returning. Every entry point that enqueues work may be captured into a
  * HIP graph by stream capture on a non-null stream: workspaces are stream-ordered
  * allocations, other streams are forked and joined by events, and no call records a
  * memset. For bf16 data the default scan takes a
  * workspace of kda_workspace_bytes(...) bytes (about 1.2 KB per token and head)
  * from the device's default stream-ordered memory pool (hipMallocAsync on `stream`,
  * released with hipFreeAsync on `stream` after the kernels; the pool keeps the
- * memory for the next call). The environment variable KDA_SCAN_VARIANT=pipe or
+ * memory for the next call, and kda_release gives it back to the driver). The environment variable KDA_SCAN_VARIANT=pipe or
  * =sequential selects a single-kernel bf16 scan that needs no workspace; fp32 data
  * always uses the sequential one. Results are bitwise deterministic for identical
  * inputs on the same device and variant.
