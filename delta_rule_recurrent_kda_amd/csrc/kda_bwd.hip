@@ -1471,22 +1471,30 @@ hipError_t launch_bwd_t(const BwdArgs& a, void* workspace, TimingHook* th)
     AuxStream* ss = nullptr;
     if ((e = aux_stream(0, ss)) != hipSuccess) return e;
     if ((e = aux_fork(a.stream, ss)) != hipSuccess) return e;
-    if (p.lseg == 0) {
-        if ((e = launch_dstate(kda_bwd_dstate_kernel<E, DK, DV, 0>, "bwd_dstate", a.stream)) != hipSuccess) return e;
-        if ((e = launch_state(kda_bwd_state_kernel<E, DK, DV, 0>, DV / 64, "bwd_state", ss->stream)) != hipSuccess)
-            return e;
-    } else {
-        if ((e = launch_dstate(kda_bwd_dstate_kernel<E, DK, DV, 1>, "bwd_dstate_seg", a.stream)) != hipSuccess)
-            return e;
-        if ((e = launch_dstate(kda_bwd_dstate_kernel<E, DK, DV, 2>, "bwd_dstate", a.stream)) != hipSuccess) return e;
-        if ((e = launch_state(kda_bwd_state_kernel<E, DK, DV, 1>, DV / 64 + DK / 64, "bwd_state_seg", ss->stream)) !=
-            hipSuccess)
-            return e;
-        if ((e = launch_state(kda_bwd_state_kernel<E, DK, DV, 2>, DV / 64, "bwd_state", ss->stream)) != hipSuccess)
-            return e;
-    }
+    // from here on every path joins the auxiliary stream back, so that nothing enqueued on
+    // it outlives the call's stream order (the workspace is freed on the caller's stream);
+    // the first error is kept
+    auto chains = [&]() -> hipError_t {
+        hipError_t err;
+        if (p.lseg == 0) {
+            if ((err = launch_dstate(kda_bwd_dstate_kernel<E, DK, DV, 0>, "bwd_dstate", a.stream)) != hipSuccess)
+                return err;
+            return launch_state(kda_bwd_state_kernel<E, DK, DV, 0>, DV / 64, "bwd_state", ss->stream);
+        }
+        if ((err = launch_dstate(kda_bwd_dstate_kernel<E, DK, DV, 1>, "bwd_dstate_seg", a.stream)) != hipSuccess)
+            return err;
+        if ((err = launch_dstate(kda_bwd_dstate_kernel<E, DK, DV, 2>, "bwd_dstate", a.stream)) != hipSuccess)
+            return err;
+        if ((err = launch_state(kda_bwd_state_kernel<E, DK, DV, 1>, DV / 64 + DK / 64, "bwd_state_seg",
+                                ss->stream)) != hipSuccess)
+            return err;
+        return launch_state(kda_bwd_state_kernel<E, DK, DV, 2>, DV / 64, "bwd_state", ss->stream);
+    };
+    e = chains();
     // join: the gradient kernel needs both chains
-    if ((e = aux_join(a.stream, ss)) != hipSuccess) return e;
+    const hipError_t ej = aux_join(a.stream, ss);
+    if (e == hipSuccess) e = ej;
+    if (e != hipSuccess) return e;
 
     const size_t grad_smem = sizeof(GradLds<DK, DV>);
     auto grad = kda_bwd_grad_kernel<E, DK, DV, NORM>;

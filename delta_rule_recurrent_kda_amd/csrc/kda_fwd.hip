@@ -41,12 +41,6 @@
 #include "kda_device.h"
 #include "kda_internal.h"
 
-// Optional per-phase cycle accounting hooks (empty in normal builds).
-#ifndef KDA_PHASE_DECL
-#define KDA_PHASE_DECL
-#define KDA_PHASE_MARK(i) ((void)0)
-#define KDA_PHASE_FLUSH
-#endif
 
 namespace kda {
 namespace {
@@ -99,6 +93,7 @@ __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
 {
     using EL = Elt<E>;
     using Frag = typename EL::Frag;
+    using Frag16 = typename EL::Frag16;
     using Vec = typename EL::Vec;
     using S_ = Smem<E, DK, C>;
     constexpr int VE = EL::kVec;            // elements per 16-byte vector
@@ -184,7 +179,6 @@ __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
         rb = beta[(t0 + min(tid % C, last)) * H + h];
     };
     if (nchunks > 0) load_chunk(0);
-    KDA_PHASE_DECL
 
     for (int c = 0; c < nchunks; ++c) {
         const int64_t t0 = seq0 + int64_t(c) * C;
@@ -264,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
             if ((lane & (NV / RPT - 1)) == 0) sm.diag[drow] = tot;
         }
         if (tid < C) sm.beta[tid] = EL::to_f(rb);
-        KDA_PHASE_MARK(0); lds_barrier(); KDA_PHASE_MARK(1);  // B1
+        lds_barrier();  // B1
 
         // ---- phase B: decay factors and decayed operands -------------------------
         // (the V tile goes in only now: the previous chunk's O store read this buffer)
@@ -346,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
                     EL::template store_run<2>(&sm.kbt[(vcol * VE + e) * LDC + rg * RPT + i], kb[e]);
             }
         }
-        KDA_PHASE_MARK(2); lds_barrier(); KDA_PHASE_MARK(3);  // B2
+        lds_barrier();  // B2
 
         // ---- phase C: P and A tiles, inverse of this wave's diagonal block of I + A,
         //      and the S-dependent products that need neither -------------------------
@@ -420,6 +414,8 @@ __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
 #pragma unroll
             for (int kb = 0; kb < NKD; ++kb) sf[kb] = EL::from_acc(S[2 * kb], S[2 * kb + 1]);
 #pragma unroll
+            for (int kb = 0; kb < NKD; kb += 2) EL::ready(sf[kb], sf[kb + 1]);
+#pragma unroll
             for (int rt = 0; rt < NRT; ++rt) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) X[rt][i] = EL::to_f(sm.vo[(16 * rt + 4 * g + i) * LDV + vc]);
@@ -460,7 +456,7 @@ __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
                 }
             }
         }
-        KDA_PHASE_MARK(4); lds_barrier(); KDA_PHASE_MARK(5);  // B3
+        lds_barrier();  // B3
 
         // ---- phase E: innovations, output, state update ----------------------------
         // prefetch the next chunk while this one finishes
@@ -476,17 +472,25 @@ __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
             for (int bb = 0; bb < NRT; ++bb) {
                 f32x4 acc = X[bb];
 #pragma unroll
-                for (int kb = 0; kb < bb / 2; ++kb)
-                    acc = EL::mma(EL::load(&sm.ab[(16 * bb + r) * LDC + 32 * kb], g),
-                                  EL::from_acc(Vn[2 * kb], Vn[2 * kb + 1]), acc);
-                if (bb & 1)
-                    acc = EL::mma16(EL::load16(&sm.ab[(16 * bb + r) * LDC + 16 * (bb - 1)], g),
-                                    EL::from_acc16(Vn[bb - 1]), acc);
-                Vn[bb] = EL::mma16(EL::load16(&sm.tbb[(16 * bb + r) * LDT], g), EL::from_acc16(acc), zero4());
+                for (int kb = 0; kb < bb / 2; ++kb) {
+                    Frag vb = EL::from_acc(Vn[2 * kb], Vn[2 * kb + 1]);
+                    EL::ready(vb);
+                    acc = EL::mma(EL::load(&sm.ab[(16 * bb + r) * LDC + 32 * kb], g), vb, acc);
+                }
+                if (bb & 1) {
+                    Frag16 vb = EL::from_acc16(Vn[bb - 1]);
+                    EL::ready(vb);
+                    acc = EL::mma16(EL::load16(&sm.ab[(16 * bb + r) * LDC + 16 * (bb - 1)], g), vb, acc);
+                }
+                Frag16 pa = EL::from_acc16(acc);
+                EL::ready(pa);
+                Vn[bb] = EL::mma16(EL::load16(&sm.tbb[(16 * bb + r) * LDT], g), pa, zero4());
             }
             Frag vf[NKC];
 #pragma unroll
             for (int kb = 0; kb < NKC; ++kb) vf[kb] = EL::from_acc(Vn[2 * kb], Vn[2 * kb + 1]);
+#pragma unroll
+            for (int kb = 0; kb < NKC; ++kb) EL::ready(vf[kb]);
 
             // O += P Vn, to the staging tile
 #pragma unroll
@@ -510,7 +514,7 @@ __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
                 for (int ct = 0; ct < NCT; ++ct)
                     S[ct] = EL::mma(EL::load(&sm.kbt[(16 * ct + r) * LDC + 32 * kb], g), vf[kb], S[ct]);
         }
-        KDA_PHASE_MARK(6); lds_barrier(); KDA_PHASE_MARK(7);  // B4
+        lds_barrier();  // B4
 
         // ---- phase F: coalesced store of the output tile ---------------------------
 #pragma unroll
@@ -522,8 +526,6 @@ __global__ __launch_bounds__(kThreads) void kda_fwd_kernel(
                     *reinterpret_cast<const uint4*>(&sm.vo[row * LDV + part * (16 / sizeof(E))]);
         }
     }
-    KDA_PHASE_MARK(15);
-    KDA_PHASE_FLUSH
 
     // ---- final state: rows = key channels, this wave's 16 columns -----------------
     if (final_state) {

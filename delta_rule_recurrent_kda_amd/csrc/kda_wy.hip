@@ -27,11 +27,6 @@
 #include "kda_device.h"
 #include "kda_internal.h"
 
-#ifndef KDA_PHASE_DECL
-#define KDA_PHASE_DECL
-#define KDA_PHASE_MARK(i) ((void)0)
-#define KDA_PHASE_FLUSH
-#endif
 
 namespace kda {
 namespace {
@@ -277,7 +272,8 @@ __global__ __launch_bounds__(kWThreads, 2) void kda_wy_prep_kernel(
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 // transposed tile: Lam[16rp + 4g + s][16ct + r], the A operand of Lam^T
-                const Frag16 lamT = EL::from_acc16(EL::mma16(Frag16{lds4(sm.lr, 16 * rp + r, 16 * ct + 4 * g)}, ident, zero4()));
+                Frag16 lamT = EL::from_acc16(EL::mma16(Frag16{lds4(sm.lr, 16 * rp + r, 16 * ct + 4 * g)}, ident, zero4()));
+                EL::ready(lamT);
                 gt[ct] = EL::mma16(lamT, lb, gt[ct]);
             }
         }
@@ -479,15 +475,26 @@ __global__ __launch_bounds__(kWThreads, 2) void kda_wy_prep_kernel(
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) tf[ii].u = *reinterpret_cast<const uint2*>(&sm.at[ii * 16 * 20 + lane * 2]);
     auto solve = [&](f32x4 (&y)[4]) {
-        y[0] = EL::mma16(tf[0], EL::from_acc16(y[0]), zero4());
+        Frag16 py[4];
+        py[0] = EL::from_acc16(y[0]);
+        EL::ready(py[0]);
+        y[0] = EL::mma16(tf[0], py[0], zero4());
+        py[0] = EL::from_acc16(y[0]);
+        EL::ready(py[0]);
 #pragma unroll
         for (int ii = 1; ii < 4; ++ii) {
             f32x4 acc = y[ii];
 #pragma unroll
             for (int jj = 0; jj < ii; ++jj)
                 acc = EL::mma16(Frag16{*reinterpret_cast<const uint2*>(&sm.aoff[((ii * (ii - 1)) / 2 + jj) * 256 + lane * 4])},
-                                EL::from_acc16(y[jj]), acc);
-            y[ii] = EL::mma16(tf[ii], EL::from_acc16(acc), zero4());
+                                py[jj], acc);
+            Frag16 pa = EL::from_acc16(acc);
+            EL::ready(pa);
+            y[ii] = EL::mma16(tf[ii], pa, zero4());
+            if (ii < 3) {
+                py[ii] = EL::from_acc16(y[ii]);
+                EL::ready(py[ii]);
+            }
         }
     };
 #pragma unroll
@@ -506,7 +513,9 @@ __global__ __launch_bounds__(kWThreads, 2) void kda_wy_prep_kernel(
         for (int rt = 0; rt < 4; ++rt) {
             // -W tile (rt, ct) in token rows: transpose with the identity product
             const f32x4 nw = -yw[u][rt];
-            const f32x4 wt = EL::mma16(EL::from_acc16(nw), ident, zero4());   // W[16rt + r][16ct + 4g + s]
+            Frag16 pw = EL::from_acc16(nw);
+            EL::ready(pw);
+            const f32x4 wt = EL::mma16(pw, ident, zero4());   // W[16rt + r][16ct + 4g + s]
             *reinterpret_cast<uint2*>(rec + Lay::W + ((rt * NKB + ct / 2) * 64 + lane) * 8 + (ct & 1) * 4) = pack4(wt);
         }
     }
@@ -648,6 +657,10 @@ __global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
         for (int j = 0; j < CPW; ++j)
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) sf[j][kb] = EL::from_acc(S[j][2 * kb], S[j][2 * kb + 1]);
+#pragma unroll
+        for (int j = 0; j < CPW; ++j)
+#pragma unroll
+            for (int kb = 0; kb < NKB; kb += 2) EL::ready(sf[j][kb], sf[j][kb + 1]);
         // Vn = U - W S: tile (j, rt) holds Vn[16rt + 4g + s][16 vc_j + r]
         f32x4 X[CPW][4];
 #pragma unroll
@@ -685,6 +698,7 @@ __global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
         for (int j = 0; j < CPW; ++j) {
             vf[j][0] = EL::from_acc(X[j][0], X[j][1]);
             vf[j][1] = EL::from_acc(X[j][2], X[j][3]);
+            EL::ready(vf[j][0], vf[j][1]);
         }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
@@ -728,18 +742,16 @@ __global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
     // The two roles run separate loops with the same barrier sequence (one barrier
     // after the prologue and one per chunk). In iteration i the state waves read
     // buffer i & 1 while the loading waves fill buffer (i + 1) & 1, freed by chunk i - 1.
-    KDA_PHASE_DECL
     if (loader) {
         if (nch > 0) dma(0, 0);
         dma_barrier();
-        KDA_PHASE_MARK(5);
+       
         for (int i = 0; i < nch; ++i) {
             if (i + 1 < nch) dma(i + 1, (i + 1) & 1);
-            KDA_PHASE_MARK(3);
+           
             dma_barrier();
-            KDA_PHASE_MARK(4);
+           
         }
-        KDA_PHASE_FLUSH
         return;
     }
 
@@ -788,6 +800,7 @@ __global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
                     }
                     shi[kb] = EL::from_acc(S[j][2 * kb], S[j][2 * kb + 1]);
                     slo[kb] = EL::from_acc(l0, l1);
+                    EL::ready(shi[kb], slo[kb]);
                 }
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) {
@@ -807,7 +820,8 @@ __global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
                             b0[s] = a0[s] - bf2f(f2bf(a0[s]));
                             b1[s] = a1[s] - bf2f(f2bf(a1[s]));
                         }
-                        const Frag ahi = EL::from_acc(a0, a1), alo = EL::from_acc(b0, b1);
+                        Frag ahi = EL::from_acc(a0, a1), alo = EL::from_acc(b0, b1);
+                        EL::ready(ahi, alo);
                         acc = EL::mma(ahi, shi[kb], acc);
                         acc = EL::mma(ahi, slo[kb], acc);
                         acc = EL::mma(alo, shi[kb], acc);
@@ -818,14 +832,13 @@ __global__ __launch_bounds__(kCThreads) void kda_wy_chain_kernel(
         }
     }
     lds_barrier();
-    KDA_PHASE_MARK(5);
+   
     for (int i = 0; i < nch; ++i) {
         products(S, i, i & 1);
-        KDA_PHASE_MARK(0);
+       
         lds_barrier();
-        KDA_PHASE_MARK(1);
+       
     }
-    KDA_PHASE_FLUSH
     if constexpr (MODE == 1) {
         // segment result: S_loc (value tiles) or Phi (transition tiles)
         const int64_t ks = int64_t(sid) * H + h;
