@@ -102,15 +102,15 @@ bool validate_env()
 }
 
 // KDA_SCAN_VARIANT selects the bf16 scan: "wy" (default; a prep kernel over all
-// chunks and a chain kernel, with a workspace), "pipe" (one software-pipelined
-// kernel) or "sequential" (one chunk at a time). fp32 data always uses the
-// sequential kernel.
-enum class Variant { Wy, Pipe, Sequential };
+// chunks and a chain kernel, with a workspace), "fused" (d_k = d_v = 128: one kernel
+// that computes every chunk's operands on the CU; other sizes take "wy") or
+// "sequential" (one chunk at a time). fp32 data always uses the sequential kernel.
+enum class Variant { Wy, Fused, Sequential };
 Variant variant_env()
 {
     const char* e = std::getenv("KDA_SCAN_VARIANT");
     if (e && std::strcmp(e, "sequential") == 0) return Variant::Sequential;
-    if (e && std::strcmp(e, "pipe") == 0) return Variant::Pipe;
+    if (e && std::strcmp(e, "fused") == 0) return Variant::Fused;
     return Variant::Wy;
 }
 
@@ -514,6 +514,10 @@ size_t kda_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_h
 {
     if (dtype != KDA_BF16 || total_tokens < 0 || num_seqs <= 0 || num_heads < 1) return 0;
     if ((d_k != 64 && d_k != 128) || (d_v != 64 && d_v != 128)) return 0;
+    const Variant var = variant_env();
+    if (var == Variant::Sequential) return 0;
+    if (d_k == 128 && d_v == 128 && var == Variant::Fused)
+        return kda::fused_workspace_bytes(total_tokens, num_seqs, num_heads);
     return kda::wy_workspace_bytes(total_tokens, num_seqs, num_heads, d_k, d_v);
 }
 
@@ -561,8 +565,6 @@ kda_status check_args(const void* q, const void* k, const void* v, const void* l
         if (st != KDA_OK) return st;
     }
     if (num_seqs == 0) return KDA_OK;
-    if ((options & KDA_OPT_QK_L2NORM) && dtype == KDA_BF16 && variant_env() == Variant::Pipe)
-        return fail(KDA_E_UNSUPPORTED, "KDA_OPT_QK_L2NORM is not supported by the pipelined scan");
 
     if (validate_env()) {
         std::vector<int32_t> h(size_t(num_seqs) + 1);
@@ -587,22 +589,28 @@ kda_status run(const kda::LaunchArgs& a)
     if (!th) lk.unlock();
     const Variant var = a.dtype_bf16 ? variant_env() : Variant::Sequential;
     hipError_t e = hipSuccess;
-    if (var == Variant::Wy) {
-        int dev = -1;
-        e = hipGetDevice(&dev);
-        if (e != hipSuccess || !prepare_pool(dev))
-            return fail(KDA_E_HIP, "setting up the workspace pool: %s", hipGetErrorString(e));
-        const size_t bytes = kda::wy_workspace_bytes(a.total_tokens, a.num_seqs, a.num_heads, a.d_k, a.d_v);
+    if (var != Variant::Sequential) {
+        const bool fused = var == Variant::Fused && kda::fused_supported(a);
+        const size_t bytes = fused ? kda::fused_workspace_bytes(a.total_tokens, a.num_seqs, a.num_heads)
+                                   : kda::wy_workspace_bytes(a.total_tokens, a.num_seqs, a.num_heads, a.d_k, a.d_v);
         void* ws = nullptr;
-        e = hipMallocAsync(&ws, bytes, a.stream);
-        if (e != hipSuccess)
-            return fail(KDA_E_HIP, "workspace of %zu bytes: %s", bytes, hipGetErrorString(e));
-        e = kda::launch_forward_wy(a, ws, th);
-        const hipError_t ef = hipFreeAsync(ws, a.stream);
-        if (e == hipSuccess) e = ef;
+        if (bytes) {
+            int dev = -1;
+            e = hipGetDevice(&dev);
+            if (e != hipSuccess || !prepare_pool(dev))
+                return fail(KDA_E_HIP, "setting up the workspace pool: %s", hipGetErrorString(e));
+            e = hipMallocAsync(&ws, bytes, a.stream);
+            if (e != hipSuccess)
+                return fail(KDA_E_HIP, "workspace of %zu bytes: %s", bytes, hipGetErrorString(e));
+        }
+        e = fused ? kda::launch_forward_fused(a, ws, th) : kda::launch_forward_wy(a, ws, th);
+        if (ws) {
+            const hipError_t ef = hipFreeAsync(ws, a.stream);
+            if (e == hipSuccess) e = ef;
+        }
     } else {
         if (th) th->begin("scan", a.stream);
-        e = var == Variant::Pipe ? kda::launch_forward_pipe(a) : kda::launch_forward_seq(a);
+        e = kda::launch_forward_seq(a);
         if (th) th->end(a.stream);
     }
     if (e != hipSuccess) return fail(KDA_E_HIP, "launch failed: %s", hipGetErrorString(e));

@@ -30,9 +30,6 @@ struct LaunchArgs {
 // Sequential: 4 waves per (sample, head, 64-column tile), 64-token chunks for bf16
 // and 32-token chunks for fp32, one chunk at a time.
 hipError_t launch_forward_seq(const LaunchArgs& a);
-// Pipelined (bf16 only): 8 waves, 32-token chunks, the decayed operands of the
-// next chunk computed while the current chunk's products run.
-hipError_t launch_forward_pipe(const LaunchArgs& a);
 
 // Records a pair of HIP events on the launch stream around each kernel launch
 // (diagnostic per-kernel timing; NULL when off).
@@ -41,6 +38,15 @@ struct TimingHook {
     virtual void end(hipStream_t stream) = 0;
     virtual ~TimingHook() = default;
 };
+
+// Fused path (bf16, d_k = d_v = 128): one workgroup per (sample segment, head) computes
+// every chunk's operands on the CU and carries the state; samples are cut into segments
+// (a summary pass, a combine and the output pass) when they give too few workgroups.
+// `workspace` must hold fused_workspace_bytes(...) bytes (0 when no sample is cut),
+// 256-byte aligned.
+bool fused_supported(const LaunchArgs& a);
+hipError_t launch_forward_fused(const LaunchArgs& a, void* workspace, TimingHook* th);
+size_t fused_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads);
 
 // Two-kernel path (bf16 only): a prep kernel over all (64-token chunk, head) pairs
 // writes the chunk operands to `workspace`, a chain kernel carries the state.
@@ -107,6 +113,5 @@ hipError_t aux_join(hipStream_t main, AuxStream* aux);
 
 // LDS bytes one workgroup uses.
 size_t smem_bytes(int dtype_bf16, int d_k);
-size_t smem_bytes_pipe(int d_k);
 
 }  // namespace kda

@@ -84,9 +84,12 @@ typedef enum {
  * workspace of kda_workspace_bytes(...) bytes (about 1.2 KB per token and head)
  * from the device's default stream-ordered memory pool (hipMallocAsync on `stream`,
  * released with hipFreeAsync on `stream` after the kernels; the pool keeps the
- * memory for the next call, and kda_release gives it back to the driver). The environment variable KDA_SCAN_VARIANT=pipe or
- * =sequential selects a single-kernel bf16 scan that needs no workspace; fp32 data
- * always uses the sequential one. Results are bitwise deterministic for identical
+ * memory for the next call, and kda_release gives it back to the driver). The environment
+ * variable KDA_SCAN_VARIANT selects another bf16 scan: "sequential", a single kernel that
+ * needs no workspace, or "fused" (d_k = d_v = 128; other sizes keep the default), one kernel
+ * that forms every chunk's operands on the CU and whose workspace, taken only when a few
+ * long samples are cut into segments, holds two 64 KB summaries per (segment, head).
+ * fp32 data always uses the sequential scan. Results are bitwise deterministic for identical
  * inputs on the same device and variant.
  * cu_seqlens is read on the device; its content is checked on the host only when the
  * environment variable KDA_VALIDATE=1 (one synchronous device-to-host copy).
@@ -143,8 +146,8 @@ kda_status kda_forward_from_state(const void *q, const void *k, const void *v,
  *   initial_state : as kda_forward_from_state (NULL = zero states).
  *   options       : bitwise OR of KDA_OPT_* values; unknown bits give KDA_E_UNSUPPORTED.
  * All other arguments, errors and execution as kda_forward. KDA_OPT_QK_L2NORM is
- * supported for fp32 and bf16 data on the default scans (KDA_E_UNSUPPORTED with
- * KDA_SCAN_VARIANT=pipe); initial_state as for kda_forward_from_state.
+ * supported for fp32 and bf16 data on every scan; initial_state as for
+ * kda_forward_from_state.
  */
 kda_status kda_forward_ex(const void *q, const void *k, const void *v, const void *log_alpha,
                           const void *beta, const int32_t *cu_seqlens, const float *initial_state,
@@ -273,10 +276,12 @@ kda_status kda_short_conv_backward(const void *x, const float *w_text, const flo
                                    int32_t k_w, kda_dtype dtype, hipStream_t stream);
 
 /*
- * kda_workspace_bytes -- bytes of device workspace the default bf16 scan takes for
- * these sizes (0 when it takes none: fp32 data, no samples, unsupported sizes).
- * Layout: per (64-token chunk, head) record of the chunk's decayed operands and
- * WY factors, plus a chunk table. Pure function of the sizes; no device access.
+ * kda_workspace_bytes -- bytes of device workspace the bf16 scan selected by
+ * KDA_SCAN_VARIANT takes for these sizes (0 when it takes none: fp32 data, no samples,
+ * unsupported sizes, the sequential scan). Default scan: per (64-token chunk, head) record of
+ * the chunk's decayed operands and WY factors, plus a chunk table. Fused scan: per
+ * (segment, head) state and transition when samples are cut into segments, else nothing.
+ * Pure function of the sizes and the environment; no device access.
  */
 size_t kda_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads,
                            int32_t d_k, int32_t d_v, kda_dtype dtype);

@@ -1,9 +1,9 @@
 """Summaries of rocprofv3 result databases (kernel trace and PMC counter runs).
 
-python -m delta_rule_recurrent_kda_amd.profile_summary trace DB [--kernel NAME]
-python -m delta_rule_recurrent_kda_amd.profile_summary traffic FETCH_DB WRITE_DB --calib-bytes N
+python profile_summary.py trace DB [--kernel NAME]
+python profile_summary.py traffic FETCH_DB WRITE_DB --calib-bytes N
     [--kernel NAME] [--out JSON] [--workload W] [--kernel-sha SHA]
-python -m delta_rule_recurrent_kda_amd.profile_summary mfma DB --trace TRACE_DB [--kernel NAME]
+python profile_summary.py mfma DB --trace TRACE_DB [--kernel NAME]
 
 `trace` prints per-kernel call counts and durations. `traffic` scales the
 FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) of one kernel by the

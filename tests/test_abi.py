@@ -148,12 +148,6 @@ def test_forward_ex_empty_batch_is_a_no_op(lib):
     assert st == 0
 
 
-def test_qk_norm_on_single_kernel_variant_is_unsupported(lib, monkeypatch):
-    monkeypatch.setenv("KDA_SCAN_VARIANT", "pipe")
-    st, msg = _call_ex({})
-    assert st == 5 and "QK_L2NORM" in msg
-
-
 def _call_conv(kw):
     from delta_rule_recurrent_kda_amd import kda
     a = dict(x=0x100000, w_text=0x200000, w_vis=0x300000, cu_seqlens=0x400000, text_len=0x500000, grid=0x600000,
@@ -265,7 +259,7 @@ def test_backward_workspace_bytes(lib):
     assert kda.backward_workspace_bytes(T, 0, H, 128, 128) == 0
 
 
-def test_workspace_bytes(lib):
+def test_workspace_bytes(lib, monkeypatch):
     from delta_rule_recurrent_kda_amd import kda
     rec = {(128, 128): 74240, (128, 64): 74240 - 8192}
     # record: -W, Qh (4*d_k/32 fragments of 1 KB each), Kb^T (d_k/16 * 2 KB), P (8 KB),
@@ -276,8 +270,26 @@ def test_workspace_bytes(lib):
     # chunk and segment offset tables (rounded up to 256 bytes), one record per
     # (64-token chunk, head) for the upper bound ceil(T / 64) + N of chunks, and, when the
     # chain would get at most 64 workgroups, per-segment local states and transitions (fp32)
-    for T, N, H, dk, dv in [(17108, 8, 16, 128, 128), (1, 1, 1, 64, 64), (189272, 1, 16, 128, 64),
-                            (640, 300, 3, 64, 128), (189272, 1, 16, 128, 128), (5000, 1, 2, 128, 128)]:
+    cases = [(17108, 8, 16, 128, 128), (1, 1, 1, 64, 64), (189272, 1, 16, 128, 64), (640, 300, 3, 64, 128),
+             (189272, 1, 16, 128, 128), (5000, 1, 2, 128, 128), (100000, 100, 2, 128, 128), (4000, 600, 1, 128, 128)]
+    for fused, T, N, H, dk, dv in [(False,) + c for c in cases] + [(True,) + c for c in cases]:
+        if fused:
+            monkeypatch.setenv("KDA_SCAN_VARIANT", "fused")
+        else:
+            monkeypatch.delenv("KDA_SCAN_VARIANT", raising=False)
+        if dk == 128 and dv == 128 and fused:
+            # fused scan (32-token chunks): nothing unless the (sample, head) units are fewer than
+            # 512; then segments of lseg chunks, each (segment, head) with an fp32 local state and
+            # its transition as hi/lo bf16 (64 KB each), and a segment table for more than 64 samples
+            chunks = (T + 31) // 32 + N
+            expect = 0
+            if N * H < 512:
+                lseg = max(16, (chunks * H + 511) // 512)
+                if lseg < chunks:
+                    max_segs = (chunks + lseg - 1) // lseg + N
+                    expect = max_segs * H * 2 * 65536 + ((N + 1) * 4 + 255) // 256 * 256 * (N > 64)
+            assert kda.workspace_bytes(T, N, H, dk, dv, kda.KDA_BF16) == expect, (T, N, H, dk, dv)
+            continue
         bound = (T + 63) // 64
         chunks = bound + N
         table = (2 * (N + 1) * 4 + 255) // 256 * 256
@@ -292,6 +304,8 @@ def test_workspace_bytes(lib):
     assert kda.workspace_bytes(1000, 2, 2, 128, 128, kda.KDA_F32) == 0
     assert kda.workspace_bytes(1000, 0, 2, 128, 128, kda.KDA_BF16) == 0
     assert kda.workspace_bytes(1000, 2, 2, 96, 128, kda.KDA_BF16) == 0
+    monkeypatch.setenv("KDA_SCAN_VARIANT", "sequential")
+    assert kda.workspace_bytes(17108, 8, 16, 128, 128, kda.KDA_BF16) == 0
 
 
 def test_bandwidth_probe_library_builds_and_exports(lib):

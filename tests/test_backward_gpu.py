@@ -1,9 +1,21 @@
 """GPU parity of kda_backward (through the C ABI) against the fp64 reverse-mode oracle.
 
-Tolerance, per gradient tensor and per (sample, head) block, relative Frobenius norm of
-the difference: fp32 data 1e-4 (the arithmetic is fp32 throughout); bf16 data 1e-2
-(inputs, d_out and the gradients are bf16; one rounding of a gradient to bf16 is up to
-2^-9 relative per element). The worst row error relative to its row norm is reported.
+Two checks per gradient tensor:
+- per (sample, head) block, the relative Frobenius norm of the difference: fp32 data 1e-4
+  (the arithmetic is fp32 throughout); bf16 data 1e-2 (inputs, d_out and the gradients are
+  bf16; one rounding of a gradient to bf16 alone gives about 1.7e-3 on such blocks);
+- per row: for dq, dk, dv and dlog_alpha each (token, head) row over its channels, for
+  d_initial_state each key-channel row of each (sample, head) state, the largest absolute
+  error is at most ROW_TOL times that row's scale; dbeta has one value per (token, head),
+  its row is the value itself. A row's scale is its oracle norm, floored at ROW_FLOOR times
+  the root mean square of the row norms of its (sample, head) block: some rows are exactly
+  zero (dlog_alpha at the first token of a sample that starts from a zero state: the decay
+  acts on a zero state) or near-cancelling sums (single dbeta values), and have no relative
+  error of their own to speak of; the floor still fails a row that is wrong by more than a
+  small fraction of its neighbours' size. A block that is exactly zero as a whole (dlog_alpha
+  of a one-token sample from a zero state) takes the root mean square over all rows of its
+  head instead: the kernel forms it from sums of terms of that size. The first token of every sample is reported
+  separately: a wrong reset or boundary shows there first.
 """
 import numpy as np
 import pytest
@@ -14,6 +26,11 @@ from delta_rule_recurrent_kda_amd import inputs
 pytestmark = pytest.mark.gpu
 
 NAMES = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "d_initial_state")
+# per-row bounds: bf16 storage rounds each element to 2^-8 relative (RNE), so a row's largest
+# element error from the storage alone is at most 2^-8 of its largest element; 2e-2 of the row
+# norm (the forward's bound) leaves room for the fp32 arithmetic. fp32 data: 1e-3.
+ROW_TOL = {"bf16": 2e-2, "f32": 1e-3}
+ROW_FLOOR = 0.05
 
 
 def _draw_grads(spec, seed):
@@ -51,10 +68,35 @@ def _oracle(spec, a, do, dfs, s0, norm):
                            threads=16)
 
 
+def _row_errors(name, x, y, cu):
+    """Per-row relative errors of one gradient tensor (see the module docstring), and the mask
+    of rows that are the first token of a sample."""
+    if name == "d_initial_state":
+        e = np.abs(x - y).max(axis=3)
+        n = np.linalg.norm(y, axis=3)
+        return np.where(n > 0, e / np.where(n > 0, n, 1.0), np.where(e > 0, np.inf, 0.0)), None
+    first = np.zeros(x.shape[0], bool)
+    first[[c for c, c1 in zip(cu[:-1], cu[1:]) if c1 > c]] = True
+    if name == "dbeta":
+        e, norm = np.abs(x - y), np.abs(y)
+    else:
+        e, norm = np.abs(x - y).max(axis=2), np.linalg.norm(y, axis=2)
+    scale = norm.copy()
+    head_rms = np.sqrt(np.mean(norm ** 2, axis=0)) if norm.size else 0.0
+    for n0, n1 in zip(cu[:-1], cu[1:]):
+        if n1 > n0:
+            rms = np.sqrt(np.mean(norm[n0:n1] ** 2, axis=0))
+            rms = np.where(rms > 0, rms, head_rms)     # a block that is exactly zero
+            scale[n0:n1] = np.maximum(norm[n0:n1], ROW_FLOOR * rms)
+    rel = np.where(scale > 0, e / np.where(scale > 0, scale, 1.0), np.where(e > 0, np.inf, 0.0))
+    return rel, first
+
+
 def _compare(spec, got, ref, label):
     tol = 1e-4 if spec.dtype == "f32" else 1e-2
+    row_tol = ROW_TOL[spec.dtype]
     cu = spec.cu_seqlens()
-    worst = {}
+    worst, rows = {}, {}
     for name, x, y in zip(NAMES, got, ref):
         w = 0.0
         for n in range(len(cu) - 1):
@@ -69,9 +111,16 @@ def _compare(spec, got, ref, label):
                 e = np.linalg.norm(a - b) / nb if nb > 0 else np.abs(a).max()
                 w = max(w, e)
         worst[name] = w
+        rel, first = _row_errors(name, x, y, cu)
+        rows[name] = (float(rel.max()) if rel.size else 0.0,
+                      float(rel[first].max()) if first is not None and first.any() else 0.0)
     gu.log(f"[{label}] worst per-block rel frob: " + ", ".join(f"{k} {v:.2e}" for k, v in worst.items()))
+    gu.log(f"[{label}] worst row (first tokens of samples): " +
+           ", ".join(f"{k} {v[0]:.2e} ({v[1]:.2e})" for k, v in rows.items()))
     for name, w in worst.items():
         assert w <= tol, (label, name, w, tol)
+    for name, (w, _) in rows.items():
+        assert w <= row_tol, (label, name, "row", w, row_tol)
 
 
 CASES = [

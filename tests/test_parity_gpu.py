@@ -120,28 +120,39 @@ def test_named_config_full(cfg):
     _check(inputs.config(cfg))
 
 
-def test_config4_sampled_heads():
-    # full 189,272-token launch; the oracle recomputes three heads in full
-    _check(inputs.config(4), heads=[0, 7, 15])
+def test_config4_all_heads():
+    # the full 189,272-token launch; the oracle recomputes every one of the 16 heads
+    _check(inputs.config(4))
 
 
-@pytest.mark.parametrize("variant", ["sequential", "pipe"])
-@pytest.mark.parametrize("case", ["packed8", "ragged_d64"])
-def test_single_kernel_variants(monkeypatch, variant, case):
-    # the single-kernel bf16 scans stay selectable; they must meet the same bar
+@pytest.mark.parametrize("variant", ["sequential", "fused"])
+@pytest.mark.parametrize("case", ["packed8", "ragged_d64", "ragged_d128"])
+def test_selectable_variants(monkeypatch, variant, case):
+    # the single-kernel and fused bf16 scans stay selectable; they must meet the same bar
+    # (the fused scan covers d_k = d_v = 128; other sizes take the default scan)
     monkeypatch.setenv("KDA_SCAN_VARIANT", variant)
     if case == "packed8":
         _check(inputs.config(1), label=f"packed8 {variant}")
-    else:
+    elif case == "ragged_d64":
         spec = inputs.KdaSpec("ragged_d64_seq", (129, 3, 64, 200, 1), 3, 64, 64, "bf16", (0.001, 0.1), 4343)
         _check(spec, label=f"ragged d64 {variant}")
+    else:
+        spec = inputs.KdaSpec("ragged_d128", (1, 31, 32, 33, 0, 95, 700, 64), 3, 128, 128, "bf16",
+                              (0.001, 0.1), 4344)
+        _check(spec, label=f"ragged d128 {variant}")
 
 
-# (d_k, d_v, dtype, scan variant): the default two-kernel scan for bf16 data, the sequential
-# kernel for fp32 data and for bf16 data when selected, and the pipelined kernel
+def test_fused_config0_and_config4_sampled_heads(monkeypatch):
+    monkeypatch.setenv("KDA_SCAN_VARIANT", "fused")
+    _check(inputs.config(0), label="config0 fused")
+    _check(inputs.config(4), heads=[0, 7, 15], label="config4 fused")
+
+
+# (d_k, d_v, dtype, scan variant): the default scan for bf16 data, the sequential kernel for
+# fp32 data and for bf16 data when selected
 INIT = [(128, 128, "bf16", None), (64, 64, "bf16", None), (128, 64, "bf16", None),
         (128, 128, "f32", None), (64, 128, "f32", None), (128, 64, "bf16", "sequential"),
-        (128, 128, "bf16", "pipe"), (64, 64, "bf16", "pipe")]
+        (128, 128, "bf16", "fused")]
 
 
 @pytest.mark.parametrize("dk,dv,dt,variant", INIT, ids=[f"{a}x{b}_{c}_{d or 'default'}" for a, b, c, d in INIT])
@@ -170,6 +181,8 @@ NORM = [
     ("f32_d64", (100, 37, 0, 250), 2, 64, 64, "f32", None),
     ("f32_d128", (70, 130), 2, 128, 128, "f32", None),
     ("bf16_split", (5000,), 2, 128, 128, "bf16", None),
+    ("bf16_fused", (129, 0, 64, 200, 1, 63), 3, 128, 128, "bf16", "fused"),
+    ("bf16_fused_split", (5000,), 2, 128, 128, "bf16", "fused"),
 ]
 
 
@@ -247,6 +260,33 @@ def test_sequence_split(name, lens, H, dk, dv):
         for k in ("segments", "chain"):
             timing[k] = kda.timing_read(k)[0]
     assert timing["segments"] == 1 and timing["chain"] == 1, timing   # the split path ran
+
+
+# The fused scan splits samples into segments of 32-token chunks when the (sample, head)
+# units are fewer than 512: a summary pass, a combine over the segments, an output pass.
+FSPLIT = [
+    ("one_long", [5000], 2, ["fused_sum", "fused_combine", "fused"]),
+    ("ragged_pack", [3000, 0, 2100, 70, 1], 3, ["fused_sum", "fused_combine", "fused"]),
+    ("many_samples", [700] * 70 + [33] * 30, 1, ["fused_sum", "fused_combine", "fused", "plan"]),
+]
+
+
+@pytest.mark.parametrize("name,lens,H,kernels", FSPLIT, ids=[c[0] for c in FSPLIT])
+def test_fused_sequence_split(monkeypatch, name, lens, H, kernels):
+    from delta_rule_recurrent_kda_amd import kda
+    monkeypatch.setenv("KDA_SCAN_VARIANT", "fused")
+    names = ("fused_sum", "fused_combine", "fused", "plan")
+    for k in names:
+        kda.timing_read(k)
+    kda.timing_enable(True)
+    try:
+        spec = inputs.KdaSpec(f"fsplit_{name}", tuple(lens), H, 128, 128, "bf16", (0.0005, 0.05), 6262)
+        _check(spec, label=f"fused split {name}")
+    finally:
+        kda.timing_enable(False)
+        timing = {k: kda.timing_read(k)[0] for k in names}
+    for k in names:
+        assert timing[k] == (1 if k in kernels else 0), timing
 
 
 def test_sequence_split_from_state():
