@@ -1,18 +1,28 @@
 """Benchmark of the KDA forward scan on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload packed8|image4|clip5s|clip30s|tiny]
-                [--no-backward] [--no-conv] [--no-shard] [--no-cpu-baseline] [--copy-calib-mib M]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload clip30s|clip5s|image4|packed8|tiny]
+                [--no-backward] [--no-conv] [--no-shard] [--no-cpu-baseline] [--no-other-configs]
+                [--copy-calib-mib M]
 
-A step is one kda_forward call over the whole packed batch (every stage of the
-scan runs inside it: chunk table, chunk prep, state chain). Inputs are generated
-once, copied to HBM, and the timed region holds exactly K back-to-back steps
-between two device synchronisations. Inside the timed region the library records
-HIP events on the launch stream around each of its kernels; the roofline entry is
-for the kernel with the largest time per step, priced with that kernel's own
-algorithmic bytes per launch. The same line carries the backward, the short
-convolution and its backward, one GPU's share under a head or sequence split, the
-step replayed from a HIP graph, the measured ceilings and the oracle's CPU rate.
-Prints one JSON line.
+A step is one kda_forward call over the whole workload (every stage of the scan
+runs inside it). The default workload is the 30-second clip: one sample of 189,272
+tokens (512 text + a 121 x 30 x 52 latent grid), 16 heads, d_k = d_v = 128, bf16
+data with fp32 states, the largest of the five configurations. Inputs are
+generated once, copied to HBM, and the timed region holds exactly K back-to-back
+steps between two device synchronisations. Inside the timed region the library
+records HIP events on the launch stream around each of its kernels.
+
+roofline: the scan must move 1,282 bytes per head-token (read q, k, v, log a and
+beta once, write out once; bf16, d = 128) plus the fp32 final states. `achieved`
+prices those bytes against the mean duration of the kernel with the largest time
+per step; `path` prices them against the whole step. `traffic` is the kernel's
+HBM bytes per launch from committed counter runs (profiles/), `traffic_ratio` that
+over the algorithmic bytes.
+
+The same line carries the other configurations' forward steps, the backward, the
+short convolution and its backward, one GPU's share under a head or sequence
+split, the step replayed from a HIP graph, single steps after a cache flush, the
+measured ceilings and the oracle's CPU rate. Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -31,8 +41,12 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
 MFMA_F32_PEAK_TFLOPS = 157.3
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # fp32 vector FMA, published (counts dual-issue/packed)
-KERNEL_SOURCES = ["delta_rule_recurrent_kda_amd/csrc/kda_wy.hip",
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # fp32 vector FMA, published (counts packed fp32 FMAs)
+# fp32 vector FMA without packed ops (this build turns them off): 256 CUs x 4 SIMDs x 16 lanes
+# x 2 flops x 2.4 GHz
+FP32_VECTOR_UNPACKED_TFLOPS = 78.6
+KERNEL_SOURCES = ["delta_rule_recurrent_kda_amd/csrc/kda_fused.hip",
+                  "delta_rule_recurrent_kda_amd/csrc/kda_wy.hip",
                   "delta_rule_recurrent_kda_amd/csrc/kda_device.h",
                   "delta_rule_recurrent_kda_amd/csrc/kda_internal.h"]
 BWD_SOURCES = ["delta_rule_recurrent_kda_amd/csrc/kda_bwd.hip",
@@ -47,8 +61,11 @@ CONV_BWD_KERNELS = {"conv_bwd_plan": "kda_conv_plan_kernel", "conv_dx": "kda_sho
 CONV_TAPS = (4, 3, 3, 3)        # text taps; visual frames x rows x columns
 WORKLOADS = {"tiny": 0, "packed8": 1, "image4": 2, "clip5s": 3, "clip30s": 4}
 CHUNK = 64
-KERNEL_SYMBOL = {"prep": "kda_wy_prep_kernel", "chain": "kda_wy_chain_kernel", "plan": "kda_wy_plan_kernel",
+KERNEL_SYMBOL = {"fused": "kda_fused_kernel", "fused_sum": "kda_fused_kernel",
+                 "fused_combine": "kda_fused_combine_kernel", "plan": "kda_fused_plan_kernel",
+                 "prep": "kda_wy_prep_kernel", "chain": "kda_wy_chain_kernel",
                  "segments": "kda_wy_chain_kernel", "scan": "kda_fwd"}
+FUSED_C = 32                    # chunk of the fused scan (d_k = d_v = 128)
 
 
 def kernel_sha(sources=None) -> str:
@@ -102,11 +119,39 @@ def split_plan(spec):
     return lseg, inner_segs, inner_chunks
 
 
+def fused_split(spec):
+    """The fused scan's segment plan (the library's rule): chunks of 32 tokens per segment
+    (0 = one segment per sample) and, over all samples, the chunks and the (segment, head)
+    pairs of segments that are not their sample's last."""
+    H = spec.heads
+    chunks = (spec.total_tokens + FUSED_C - 1) // FUSED_C + len(spec.seq_lens)
+    lseg = 0
+    if len(spec.seq_lens) * H < 512:
+        cand = max(16, (chunks * H + 511) // 512)
+        lseg = cand if cand < chunks else 0
+    if not lseg:
+        return 0, 0, 0
+    nch = [(n + FUSED_C - 1) // FUSED_C for n in spec.seq_lens]
+    nsegs = [max(1, (c + lseg - 1) // lseg) for c in nch]
+    inner_chunks = sum(min(c, (s - 1) * lseg) for c, s in zip(nch, nsegs))
+    inner_segs = sum(s - 1 for s in nsegs)
+    return lseg, inner_chunks, inner_segs
+
+
 def kernel_bytes(spec, kernel: str) -> int:
     """Algorithmic bytes of one launch of each kernel of the default bf16 scan."""
     es = 2
     T, H, N = spec.total_tokens, spec.heads, len(spec.seq_lens)
     dk, dv = spec.dk, spec.dv
+    if kernel in ("fused", "fused_sum", "fused_combine"):
+        _, inner_chunks, inner_segs = fused_split(spec)
+        state = dk * dv * 4
+        if kernel == "fused":       # every input once, out once, final states; entry states of segments
+            return algorithmic_bytes(spec) + inner_segs * H * state
+        inner_tok = min(T, inner_chunks * FUSED_C)
+        if kernel == "fused_sum":   # k, v, log a, beta of inner segments; their local states and transitions
+            return inner_tok * H * (2 * dk + dv + 1) * es + inner_segs * H * 2 * state
+        return inner_segs * H * 3 * state       # combine: read S_loc and the transition, write S_in
     rec = chunk_heads(spec) * record_bytes(spec)
     _, inner_segs, inner_chunks = split_plan(spec)
     carry = inner_segs * H * (dk * dv + dk * dk) * 4       # S_loc and Phi of each inner segment
@@ -206,16 +251,33 @@ def traffic_for(workload: str, kernel: str, sha: str = None):
     return rec.get("bytes_per_launch")
 
 
+def host_cpu():
+    """CPU model name and the number of processors the host reports."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, os.cpu_count() or 1
+
+
 def cpu_baseline(spec, a):
-    """The fp64 oracle on the host cores over the whole workload (all samples, all heads)."""
+    """The fp64 oracle on the host cores over the whole workload (all samples, all heads): one
+    thread per (sample, head) unit, at most 16 (the host share of one GPU)."""
     import oracle
     from delta_rule_recurrent_kda_amd import inputs
-    cores = min(16, os.cpu_count() or 1)
+    model, nproc = host_cpu()
+    units = len(spec.seq_lens) * spec.heads
+    cores = max(1, min(16, units, nproc))
     f = {x: inputs.to_f64(a[x], spec.dtype) for x in ("q", "k", "v", "log_alpha", "beta")}
     oracle.build()
     t0 = time.perf_counter()
     oracle.forward(f["q"], f["k"], f["v"], f["log_alpha"], f["beta"], a["cu_seqlens"], threads=cores)
     dt = time.perf_counter() - t0
+    del f
     # one thread on one (sample, head) unit of the image workload, a rate that compares hosts
     s2 = inputs.config(WORKLOADS["image4"])
     a2 = inputs.generate(s2, heads=[0])
@@ -225,8 +287,9 @@ def cpu_baseline(spec, a):
     oracle.forward(f2["q"], f2["k"], f2["v"], f2["log_alpha"], f2["beta"], np.array([0, L], np.int32), threads=1)
     d1 = time.perf_counter() - t1
     return {"value": spec.head_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "nproc": nproc, "cpu_model": model, "units": units,
             "sample": f"whole workload: {len(spec.seq_lens)} samples x {spec.heads} heads, "
-                      f"{spec.head_tokens} head-tokens, fp64 token recurrence, {dt:.2f} s wall",
+                      f"{spec.head_tokens} head-tokens, fp64 token recurrence, {dt:.2f} s wall on {cores} threads",
             "single_thread": {"value": L / d1, "unit": "tokens/s", "cores": 1,
                               "sample": f"image workload, sample 0, head 0: {L} tokens, d = {s2.dk}, {d1:.3f} s"}}
 
@@ -426,8 +489,11 @@ def conv_bench(args, spec, dev):
             "dtype": "f32 arithmetic on bf16 data",
             "config": {"workload": cs.name, "tokens": T, "channels": C, "text_taps": CONV_TAPS[0],
                        "visual_kernel": list(CONV_TAPS[1:])},
-            "roofline": {"bound": "alu", "achieved": tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": tflops / FP32_VECTOR_PEAK_TFLOPS,
+            "roofline": {"bound": "alu", "achieved": tflops, "peak": FP32_VECTOR_UNPACKED_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tflops / FP32_VECTOR_UNPACKED_TFLOPS,
+                         "peak_published": FP32_VECTOR_PEAK_TFLOPS, "frac_published": tflops / FP32_VECTOR_PEAK_TFLOPS,
+                         "peak_note": "78.6 = 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz, fp32 FMA without "
+                                      "packed ops (off in this build); 157.3 is the published figure with them",
                          "traffic": traffic_for(cs.name.split("-")[0], CONV_KERNELS["conv"], sha),
                          "kernel": CONV_KERNELS["conv"], "kernel_ms_avg": kms, "flops": flops,
                          "kernel_sha": sha},
@@ -485,8 +551,10 @@ def conv_backward_bench(args, x, wt, wv, cu, tl, gr, fwd_flops, fwd_bytes, sha, 
     return {"metric": "short convolution backward tokens/s (dx, dw_text, dw_vis)",
             "value": x.shape[0] / (ms_step * 1e-3), "unit": "tokens/s", "ms_per_step": ms_step,
             "dtype": "f32 arithmetic on bf16 data",
-            "roofline": {"bound": "alu", "achieved": kd["achieved_TFLOPs"], "peak": FP32_VECTOR_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": kd["achieved_TFLOPs"] / FP32_VECTOR_PEAK_TFLOPS,
+            "roofline": {"bound": "alu", "achieved": kd["achieved_TFLOPs"], "peak": FP32_VECTOR_UNPACKED_TFLOPS,
+                         "unit": "TFLOP/s", "frac": kd["achieved_TFLOPs"] / FP32_VECTOR_UNPACKED_TFLOPS,
+                         "peak_published": FP32_VECTOR_PEAK_TFLOPS,
+                         "frac_published": kd["achieved_TFLOPs"] / FP32_VECTOR_PEAK_TFLOPS,
                          "traffic": traffic_for(workload, CONV_BWD_KERNELS[dom], sha),
                          "kernel": CONV_BWD_KERNELS[dom], "kernel_ms_avg": kd["ms_avg"], "flops": kd["flops"],
                          "kernel_sha": sha},
@@ -549,16 +617,88 @@ def shard_bench(args, dev):
     return out
 
 
+def device_tensors(spec, a, dev):
+    import torch
+    t = {}
+    for name in ("q", "k", "v", "log_alpha", "beta"):
+        arr = a[name]
+        t[name] = (torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16) if spec.dtype == "bf16"
+                   else torch.from_numpy(arr)).to(dev)
+    return t
+
+
+def forward_timing(spec, t, cu, dev, steps, warmup):
+    """W warm-ups, then K back-to-back forward steps between two synchronisations with the
+    library's per-kernel HIP events on; returns (ms per step, per-kernel records, step fn)."""
+    import torch
+    from delta_rule_recurrent_kda_amd import kda
+    out = torch.empty((spec.total_tokens, spec.heads, spec.dv), dtype=t["q"].dtype, device=dev)
+    fs = torch.empty((len(spec.seq_lens), spec.heads, spec.dk, spec.dv), dtype=torch.float32, device=dev)
+
+    def step():     # on torch's current stream: the default stream, or the capture stream of a graph
+        kda.kda_forward(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], cu, out, fs,
+                        stream=torch.cuda.current_stream(dev))
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    for name in KERNEL_SYMBOL:
+        kda.timing_read(name)
+    kda.timing_enable(True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    kda.timing_enable(False)
+    # a kernel may run several times per step: its launches share the step's bytes
+    kernels = {}
+    for name in KERNEL_SYMBOL:
+        n, ms = kda.timing_read(name)
+        if n:
+            per_step = n / steps
+            b = kernel_bytes(spec, name) / per_step
+            kernels[name] = {"launches": n, "launches_per_step": per_step, "ms_avg": ms / n,
+                             "ms_per_step": ms / steps, "algorithmic_bytes": b,
+                             "achieved_GBs": b / (ms / n * 1e-3) / 1e9}
+    return wall * 1e3 / steps, kernels, step
+
+
+def other_configs(args, dev):
+    """Forward steps of the other bf16 configurations (parity cases of the same scan), each
+    timed like the headline: K steps after W warm-ups."""
+    import torch
+    from delta_rule_recurrent_kda_amd import inputs
+    res = {}
+    for wl, cfg in WORKLOADS.items():
+        if wl == args.workload or cfg == 0:
+            continue
+        spec = inputs.config(cfg)
+        a = inputs.generate(spec)
+        t = device_tensors(spec, a, dev)
+        cu = torch.from_numpy(a["cu_seqlens"]).to(dev)
+        ms, kernels, _ = forward_timing(spec, t, cu, dev, args.steps, args.warmup)
+        b = algorithmic_bytes(spec)
+        res[wl] = {"workload": spec.name, "head_tokens": spec.head_tokens, "ms_per_step": ms,
+                   "value": spec.head_tokens / (ms * 1e-3), "unit": "tokens/s", "algorithmic_bytes": b,
+                   "path_frac_hbm": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                   "kernels": {k: v["ms_avg"] for k, v in kernels.items()}}
+        del t
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="packed8", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="clip30s", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-shard", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after timing, run 3 plain device copies of this many MiB (for scaling "
                          "HBM byte counters)")
@@ -569,63 +709,27 @@ def main():
         sys.exit(2)
 
     import torch
-    from delta_rule_recurrent_kda_amd import inputs, kda
+    from delta_rule_recurrent_kda_amd import inputs
 
     spec = inputs.config(WORKLOADS[args.workload])
     a = inputs.generate(spec)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    t = {}
-    for name in ("q", "k", "v", "log_alpha", "beta"):
-        arr = a[name]
-        t[name] = (torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16) if spec.dtype == "bf16"
-                   else torch.from_numpy(arr)).to(dev)
+    t = device_tensors(spec, a, dev)
     cu = torch.from_numpy(a["cu_seqlens"]).to(dev)
-    out = torch.empty((spec.total_tokens, spec.heads, spec.dv), dtype=t["q"].dtype, device=dev)
-    fs = torch.empty((len(spec.seq_lens), spec.heads, spec.dk, spec.dv), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():     # on torch's current stream: the default stream, or the capture stream of a graph
-        kda.kda_forward(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], cu, out, fs,
-                        stream=torch.cuda.current_stream(dev))
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    for name in KERNEL_SYMBOL:
-        kda.timing_read(name)
-
-    # timed region: K back-to-back steps; the library records HIP events on `stream`
-    # around each of its kernels
-    kda.timing_enable(True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    kda.timing_enable(False)
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step, kernels, step = forward_timing(spec, t, cu, dev, args.steps, args.warmup)
     flushed = flushed_steps(step, stream, dev, 20)
     graph_ms = graph_steps(step, args.steps)
-    # a kernel may run several times per step (the pipelined forward launches the prep and the
-    # chain once per sample group): bytes per launch = the step's bytes / launches per step,
-    # so that bytes per launch / mean launch duration = the step's bytes / the kernel's time
-    kernels = {}
-    for name in KERNEL_SYMBOL:
-        n, ms = kda.timing_read(name)
-        if n:
-            per_step = n / args.steps
-            b = kernel_bytes(spec, name) / per_step
-            kernels[name] = {"launches": n, "launches_per_step": per_step, "ms_avg": ms / n,
-                             "ms_per_step": ms / args.steps, "algorithmic_bytes": b,
-                             "achieved_GBs": b / (ms / n * 1e-3) / 1e9}
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     dom_ms = kernels[dom]["ms_avg"]
-    dom_bytes = kernels[dom]["algorithmic_bytes"]
 
     bytes_ = algorithmic_bytes(spec)
     flops = chunk_flops(spec)
+    # the path's algorithmic bytes over the dominant kernel's mean launch time (its launches
+    # per step share them when it runs several times per step)
+    dom_bytes = bytes_ / kernels[dom]["launches_per_step"]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     path_gbs = bytes_ / (ms_per_step * 1e-3) / 1e9
     tflops = flops / (ms_per_step * 1e-3) / 1e12
@@ -646,11 +750,13 @@ def main():
         "dtype": spec.dtype,
         "data": "synthetic",
         "config": {"workload": spec.name, "samples": len(spec.seq_lens), "tokens": spec.total_tokens,
-                   "heads": spec.heads, "d_k": spec.dk, "d_v": spec.dv, "chunk": CHUNK,
-                   "head_tokens": spec.head_tokens},
+                   "heads": spec.heads, "d_k": spec.dk, "d_v": spec.dv, "head_tokens": spec.head_tokens},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "traffic_ratio": None if traffic is None else traffic / dom_bytes,
                      "kernel": KERNEL_SYMBOL[dom], "kernel_ms_avg": dom_ms, "algorithmic_bytes": dom_bytes,
+                     "algorithmic_bytes_note": "1,282 B per head-token (q, k, v, log a, beta read once, out "
+                                               "written once; bf16, d = 128) plus the fp32 final states",
                      "kernel_sha": kernel_sha()},
         "kernels": kernels,
         "path": {"algorithmic_bytes": bytes_, "achieved_GBs": path_gbs, "frac_hbm": path_gbs / HBM_PEAK_GBS},
@@ -669,6 +775,8 @@ def main():
     rec["measured_ceilings"] = ceil
     if not args.no_backward:
         rec["backward"] = backward_bench(args, spec, t, cu, dev)
+    if not args.no_other_configs:
+        rec["other_configs"] = other_configs(args, dev)
     if not args.no_conv:
         rec["short_conv"] = conv_bench(args, spec, dev)
     if not args.no_shard:
@@ -683,6 +791,8 @@ def main():
         torch.cuda.synchronize()
         rec["copy_calib_bytes"] = n
     if not args.no_cpu_baseline:
+        del t
+        torch.cuda.empty_cache()
         rec["cpu_baseline"] = cpu_baseline(spec, a)
     print(json.dumps(rec), flush=True)
 
