@@ -12,7 +12,8 @@ LIB = os.path.join(PKG, "libkda.so")
 # bandwidth probes for the benchmark's measured ceilings (not part of the scan library)
 PROBE_SRC = os.path.join(CSRC, "bw_probe.hip")
 PROBE_LIB = os.path.join(PKG, "libkda_probe.so")
-SOURCES = [os.path.join(CSRC, "kda_fwd.hip"), os.path.join(CSRC, "kda_wy.hip"), os.path.join(CSRC, "kda_fused.hip"), os.path.join(CSRC, "kda_bwd.hip"),
+SOURCES = [os.path.join(CSRC, "kda_fwd.hip"), os.path.join(CSRC, "kda_wy.hip"), os.path.join(CSRC, "kda_fused.hip"), os.path.join(CSRC, "kda_noalloc.hip"),
+           os.path.join(CSRC, "kda_bwd.hip"),
            os.path.join(CSRC, "kda_conv.hip"),
            os.path.join(CSRC, "kda_api.cpp")]
 HEADERS = [os.path.join(CSRC, "kda_internal.h"), os.path.join(CSRC, "kda_device.h"),

@@ -181,7 +181,7 @@ kda_status check_args(const void* q, const void* k, const void* v, const void* l
                       const void* beta, const int32_t* cu_seqlens, void* out, float* final_state,
                       const float* initial_state, int64_t total_tokens, int32_t num_seqs,
                       int32_t num_heads, int32_t d_k, int32_t d_v, kda_dtype dtype, uint32_t options,
-                      hipStream_t stream);
+                      hipStream_t stream, bool host_checks = true);
 kda_status run(const kda::LaunchArgs& a);
 
 }  // namespace
@@ -259,6 +259,38 @@ kda_status kda_forward_ex(const void* q, const void* k, const void* v, const voi
     return run(kda::LaunchArgs{q, k, v, log_alpha, beta, cu_seqlens, out, final_state, initial_state,
                                total_tokens, num_seqs, num_heads, d_k, d_v, dtype == KDA_BF16 ? 1 : 0,
                                stream, (options & KDA_OPT_QK_L2NORM) ? 1 : 0});
+}
+
+kda_status kda_forward_noalloc(const void* q, const void* k, const void* v, const void* log_alpha,
+                               const void* beta, const int32_t* cu_seqlens, const float* initial_state,
+                               void* out, float* final_state, int64_t total_tokens, int32_t num_seqs,
+                               int32_t num_heads, int32_t d_k, int32_t d_v, kda_dtype dtype,
+                               uint32_t options, hipStream_t stream)
+{
+    g_last_error.clear();
+    const kda_status st = check_args(q, k, v, log_alpha, beta, cu_seqlens, out, final_state,
+                                     initial_state, total_tokens, num_seqs, num_heads, d_k, d_v, dtype,
+                                     options, stream, false);
+    if (st != KDA_OK || num_seqs == 0) return st;
+    const kda::LaunchArgs a{q, k, v, log_alpha, beta, cu_seqlens, out, final_state, initial_state,
+                            total_tokens, num_seqs, num_heads, d_k, d_v, dtype == KDA_BF16 ? 1 : 0,
+                            stream, (options & KDA_OPT_QK_L2NORM) ? 1 : 0};
+    hipError_t e;
+    if (kda::fused_supported(a)) {
+        const size_t cap = kda::noalloc_scratch_bytes();
+        const size_t bytes = kda::fused_workspace_bytes(total_tokens, num_seqs, num_heads, cap);
+        if (bytes > cap)
+            return fail(KDA_E_UNSUPPORTED, "the scan needs %zu bytes of scratch, more than the fixed %zu",
+                        bytes, cap);
+        void* ws = nullptr;
+        if (bytes && (e = kda::noalloc_scratch(&ws)) != hipSuccess)
+            return fail(KDA_E_HIP, "looking up the scratch buffer: %s", hipGetErrorString(e));
+        e = kda::launch_forward_fused(a, ws, nullptr, cap);
+    } else {
+        e = kda::launch_forward_seq(a);
+    }
+    if (e != hipSuccess) return fail(KDA_E_HIP, "launch failed: %s", hipGetErrorString(e));
+    return KDA_OK;
 }
 
 kda_status kda_backward(const void* q, const void* k, const void* v, const void* log_alpha,
@@ -529,7 +561,7 @@ kda_status check_args(const void* q, const void* k, const void* v, const void* l
                       const void* beta, const int32_t* cu_seqlens, void* out, float* final_state,
                       const float* initial_state, int64_t total_tokens, int32_t num_seqs,
                       int32_t num_heads, int32_t d_k, int32_t d_v, kda_dtype dtype, uint32_t options,
-                      hipStream_t stream)
+                      hipStream_t stream, bool host_checks)
 {
     if (options & ~uint32_t(KDA_OPT_QK_L2NORM))
         return fail(KDA_E_UNSUPPORTED, "unknown option bits 0x%x", unsigned(options & ~uint32_t(KDA_OPT_QK_L2NORM)));
@@ -566,7 +598,7 @@ kda_status check_args(const void* q, const void* k, const void* v, const void* l
     }
     if (num_seqs == 0) return KDA_OK;
 
-    if (validate_env()) {
+    if (host_checks && validate_env()) {
         std::vector<int32_t> h(size_t(num_seqs) + 1);
         hipError_t e = hipMemcpyAsync(h.data(), cu_seqlens, h.size() * sizeof(int32_t),
                                       hipMemcpyDeviceToHost, stream);

@@ -704,23 +704,33 @@ struct FusedPlan {
     size_t table_bytes, sloc_bytes, phi_bytes;
 };
 
-// Cut samples into segments when the (sample, head) units alone would fill fewer than two
-// workgroups per CU: about 512 segment-workgroups then run, of at least 16 chunks each.
-FusedPlan fused_plan(int64_t T, int32_t N, int32_t H)
+FusedPlan plan_with(int64_t chunks, int32_t N, int32_t H, int64_t lseg)
 {
     FusedPlan p{};
-    const int64_t units = int64_t(N) * H;
-    const int64_t chunks = (T + kFC - 1) / kFC + N;         // upper bound over all samples
-    p.lseg = 0;
-    if (units < 512) {
-        const int64_t lseg = std::max<int64_t>(16, (chunks * H + 511) / 512);
-        if (lseg < chunks) p.lseg = int(lseg);
-    }
+    p.lseg = lseg > 0 && lseg < chunks ? int(lseg) : 0;
     p.max_segs = p.lseg ? int((chunks + p.lseg - 1) / p.lseg + N) : N;
     p.table_bytes = (p.lseg && N > 64) ? ((size_t(N) + 1) * 4 + 255) & ~size_t(255) : 0;
     p.sloc_bytes = p.lseg ? size_t(p.max_segs) * H * kFD * kFD * 4 : 0;
     p.phi_bytes = p.lseg ? size_t(p.max_segs) * H * kFD * kFD * 4 : 0;   // hi + lo bf16
     return p;
+}
+
+// Cut samples into segments when the (sample, head) units alone would fill fewer than two
+// workgroups per CU: about 512 segment-workgroups then run, of at least 16 chunks each.
+// With a byte limit on the workspace, segments grow until their summaries fit (fewer,
+// longer segments); when not even one cut per sample fits, samples stay whole.
+FusedPlan fused_plan(int64_t T, int32_t N, int32_t H, size_t cap)
+{
+    const int64_t units = int64_t(N) * H;
+    const int64_t chunks = (T + kFC - 1) / kFC + N;         // upper bound over all samples
+    int64_t lseg = units < 512 ? std::max<int64_t>(16, (chunks * H + 511) / 512) : 0;
+    FusedPlan p = plan_with(chunks, N, H, lseg);
+    if (p.table_bytes + p.sloc_bytes + p.phi_bytes <= cap) return p;
+    const size_t slot = size_t(2) * kFD * kFD * 4 * size_t(H);          // one segment's summaries, all heads
+    const size_t avail = cap > p.table_bytes ? cap - p.table_bytes : 0;
+    const int64_t max_segs = int64_t(avail / slot);
+    lseg = max_segs > N ? std::max<int64_t>(lseg, (chunks + (max_segs - N) - 1) / (max_segs - N)) : 0;
+    return plan_with(chunks, N, H, lseg);
 }
 
 template <int PASS, bool NORM>
@@ -772,15 +782,15 @@ bool fused_supported(const LaunchArgs& a)
     return a.dtype_bf16 && a.d_k == kFD && a.d_v == kFD;
 }
 
-size_t fused_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads)
+size_t fused_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads, size_t cap)
 {
-    const FusedPlan p = fused_plan(total_tokens, num_seqs, num_heads);
+    const FusedPlan p = fused_plan(total_tokens, num_seqs, num_heads, cap);
     return p.table_bytes + p.sloc_bytes + p.phi_bytes;
 }
 
-hipError_t launch_forward_fused(const LaunchArgs& a, void* workspace, TimingHook* th)
+hipError_t launch_forward_fused(const LaunchArgs& a, void* workspace, TimingHook* th, size_t cap)
 {
-    const FusedPlan p = fused_plan(a.total_tokens, a.num_seqs, a.num_heads);
+    const FusedPlan p = fused_plan(a.total_tokens, a.num_seqs, a.num_heads, cap);
     if (int64_t(p.max_segs) * a.num_heads > 0x7FFFFFFF / 8) return hipErrorInvalidValue;
     char* base = static_cast<char*>(workspace);
     int32_t* seg_off = p.table_bytes ? reinterpret_cast<int32_t*>(base) : nullptr;

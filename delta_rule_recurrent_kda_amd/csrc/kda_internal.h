@@ -43,10 +43,16 @@ struct TimingHook {
 // every chunk's operands on the CU and carries the state; samples are cut into segments
 // (a summary pass, a combine and the output pass) when they give too few workgroups.
 // `workspace` must hold fused_workspace_bytes(...) bytes (0 when no sample is cut),
-// 256-byte aligned.
+// 256-byte aligned. `cap` bounds the workspace: the segment plan takes fewer, longer
+// segments (or none) so that it fits; the same cap must be passed to both calls.
 bool fused_supported(const LaunchArgs& a);
-hipError_t launch_forward_fused(const LaunchArgs& a, void* workspace, TimingHook* th);
-size_t fused_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads);
+hipError_t launch_forward_fused(const LaunchArgs& a, void* workspace, TimingHook* th, size_t cap = SIZE_MAX);
+size_t fused_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads, size_t cap = SIZE_MAX);
+
+// The library's fixed device buffer of noalloc_scratch_bytes() bytes on the current device
+// (its address there, looked up once per device); shared by every call on that device.
+hipError_t noalloc_scratch(void** ptr);
+size_t noalloc_scratch_bytes();
 
 // Two-kernel path (bf16 only): a prep kernel over all (64-token chunk, head) pairs
 // writes the chunk operands to `workspace`, a chain kernel carries the state.

@@ -55,6 +55,8 @@ def library() -> ctypes.CDLL:
                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_int, ctypes.c_uint32, vp]
         lib.kda_forward_ex.restype = ctypes.c_int
+        lib.kda_forward_noalloc.argtypes = lib.kda_forward_ex.argtypes
+        lib.kda_forward_noalloc.restype = ctypes.c_int
         lib.kda_backward.argtypes = [vp] * 15 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
                                                  ctypes.c_uint32, vp]
@@ -107,6 +109,31 @@ def kda_forward_ex_raw(q, k, v, log_alpha, beta, cu_seqlens, initial_state, out,
     return library().kda_forward_ex(q, k, v, log_alpha, beta, cu_seqlens, initial_state, out,
                                     final_state, int(total_tokens), int(num_seqs), int(num_heads),
                                     int(d_k), int(d_v), int(dtype), int(options), stream)
+
+
+def kda_forward_noalloc_raw(q, k, v, log_alpha, beta, cu_seqlens, initial_state, out, final_state,
+                            total_tokens: int, num_seqs: int, num_heads: int, d_k: int, d_v: int,
+                            dtype: int, options: int, stream: Optional[int]) -> int:
+    """Direct C call of kda_forward_noalloc; returns the status code."""
+    return library().kda_forward_noalloc(q, k, v, log_alpha, beta, cu_seqlens, initial_state, out,
+                                         final_state, int(total_tokens), int(num_seqs), int(num_heads),
+                                         int(d_k), int(d_v), int(dtype), int(options), stream)
+
+
+def forward_noalloc(q, k, v, log_alpha, beta, cu_seqlens, out, final_state=None, initial_state=None,
+                    qk_l2norm: bool = False, stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Enqueue the scan through kda_forward_noalloc into caller-owned ``out`` (and
+    ``final_state``); the library allocates nothing (same tensors as kda_forward)."""
+    T, N, H, dk, dv, dt = _check(q, k, v, log_alpha, beta, cu_seqlens, out, final_state,
+                                 initial_state)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = kda_forward_noalloc_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                 _ptr(cu_seqlens), _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                 T, N, H, dk, dv, dt, KDA_OPT_QK_L2NORM if qk_l2norm else 0,
+                                 stream.cuda_stream)
+    if st != 0:
+        raise KdaError(st, library().kda_last_error().decode())
 
 
 def workspace_bytes(total_tokens: int, num_seqs: int, num_heads: int, d_k: int, d_v: int,

@@ -156,6 +156,29 @@ kda_status kda_forward_ex(const void *q, const void *k, const void *v, const voi
                           uint32_t options, hipStream_t stream);
 
 /*
+ * kda_forward_noalloc -- kda_forward_ex that allocates no memory, for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, hosts that forbid it.
+ *
+ * Arguments, layouts, ownership and results are those of kda_forward_ex. bf16 data with
+ * d_k = d_v = 128 runs the fused scan ("fused" of KDA_SCAN_VARIANT) with its segment
+ * summaries in a fixed 32 MiB device buffer that the library holds on every device it runs
+ * on until the process ends; the segment plan is fitted to that buffer (fewer, longer
+ * segments, or whole samples), so every size the arguments admit fits. Other sizes and
+ * fp32 data run the sequential scan, which needs no buffer. No hipMalloc, hipFree or other
+ * allocating call is made; KDA_SCAN_VARIANT, KDA_VALIDATE and the timing diagnostics are
+ * not consulted. All calls on one device share the buffer: calls that overlap in time on
+ * one device (different streams or threads without ordering between them) race and give
+ * wrong results; order them on one stream. Nothing in the buffer needs to start at zero.
+ * Returns KDA_E_UNSUPPORTED if a plan should ever need more than the buffer.
+ */
+kda_status kda_forward_noalloc(const void *q, const void *k, const void *v, const void *log_alpha,
+                               const void *beta, const int32_t *cu_seqlens,
+                               const float *initial_state, void *out, float *final_state,
+                               int64_t total_tokens, int32_t num_seqs, int32_t num_heads,
+                               int32_t d_k, int32_t d_v, kda_dtype dtype, uint32_t options,
+                               hipStream_t stream);
+
+/*
  * kda_backward -- gradients of the KDA scan.
  *
  * The paper trains its model through these kernels (paper, training setup paragraph

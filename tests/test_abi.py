@@ -148,6 +148,35 @@ def test_forward_ex_empty_batch_is_a_no_op(lib):
     assert st == 0
 
 
+def _call_noalloc(kw):
+    from delta_rule_recurrent_kda_amd import kda
+    a = dict(q=0x100000, k=0x200000, v=0x300000, log_alpha=0x400000, beta=0x500000, cu_seqlens=0x600000,
+             initial_state=None, out=0x700000, final_state=0x800000, total_tokens=128, num_seqs=1,
+             num_heads=2, d_k=128, d_v=128, dtype=kda.KDA_BF16, options=0, stream=None)
+    a.update(kw)
+    st = kda.kda_forward_noalloc_raw(**a)
+    return st, kda.library().kda_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(options=2), 5),
+    (dict(d_k=96), 5),
+    (dict(beta=None), 1),
+    (dict(v=0x300008), 4),
+    (dict(final_state=0x100000), 3),                 # final_state aliases q
+    (dict(dtype=7), 2),
+])
+def test_forward_noalloc_bad_arguments_are_rejected_without_launch(lib, kw, code):
+    st, msg = _call_noalloc(kw)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def test_forward_noalloc_empty_batch_is_a_no_op(lib):
+    st, _ = _call_noalloc(dict(num_seqs=0, total_tokens=0))
+    assert st == 0
+
+
 def _call_conv(kw):
     from delta_rule_recurrent_kda_amd import kda
     a = dict(x=0x100000, w_text=0x200000, w_vis=0x300000, cu_seqlens=0x400000, text_len=0x500000, grid=0x600000,
