@@ -101,17 +101,17 @@ bool validate_env()
     return e && e[0] == '1';
 }
 
-// KDA_SCAN_VARIANT selects the bf16 scan: "wy" (default; a prep kernel over all
-// chunks and a chain kernel, with a workspace), "fused" (d_k = d_v = 128: one kernel
-// that computes every chunk's operands on the CU; other sizes take "wy") or
+// KDA_SCAN_VARIANT selects the bf16 scan: "fused" (the default for d_k = d_v = 128: one
+// kernel that computes every chunk's operands on the CU), "wy" (the default for other
+// sizes: a prep kernel over all chunks and a chain kernel, with a workspace) or
 // "sequential" (one chunk at a time). fp32 data always uses the sequential kernel.
 enum class Variant { Wy, Fused, Sequential };
 Variant variant_env()
 {
     const char* e = std::getenv("KDA_SCAN_VARIANT");
     if (e && std::strcmp(e, "sequential") == 0) return Variant::Sequential;
-    if (e && std::strcmp(e, "fused") == 0) return Variant::Fused;
-    return Variant::Wy;
+    if (e && std::strcmp(e, "wy") == 0) return Variant::Wy;
+    return Variant::Fused;
 }
 
 // ---- per-kernel event timing (diagnostics) ----

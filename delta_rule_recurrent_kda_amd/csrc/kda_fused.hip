@@ -7,44 +7,54 @@
 // Chunkwise form over chunks of C = 32 tokens (G = inclusive cumsum of log a over the
 // chunk's rows, per key channel; gamma = exp(G of the last row)):
 //     Qh = Q e^G, Kh = K e^G, Kc = K e^-G, Kb = gamma Kc
-//     A = StrictLower(diag(b) Kh Kc^T),  T = (I + A)^-1,  W = T diag(b) Kh,  U = T diag(b) V
-//     Vn = U - W S,  O = Qh S + LowerIncl(Qh Kc^T) Vn,  S <- diag(gamma) S + Kb^T Vn
+//     A = StrictLower(diag(b) Kh Kc^T),  T = (I + A)^-1
+//     X = T diag(b) (V - Kh S),  O = Qh S + LowerIncl(Qh Kc^T) X,  S <- diag(gamma) S + Kb^T X
+// (X = U - W S of the WY form with W = T diag(b) Kh, U = T diag(b) V, taken the other way
+// round: the residual V - Kh S is formed first and solved once, so W and U are never built).
 //
-// One workgroup of 8 wave64s owns one (sample segment, head) and all 128 value columns,
-// so every S-independent operand of a chunk is computed once, on the CU, from the raw
-// inputs, and never leaves it: the kernel reads q, k, v, log a, beta once and writes the
-// output once. Per chunk the eight waves run, between workgroup barriers:
-//   E  wave w owns token tile w & 1 and channel slab w >> 1 (32 channels): the chunk-local
-//      cumulative decay G as one product with a triangular ones matrix, e^{+-G}, Qh and Kc
-//      as hi/lo bf16 pairs, Kh, partial q.k sums, gamma; all to LDS.
-//   2  waves 0-2: the three 16x16 blocks of A, the two diagonal ones inverted exactly on
-//      fp32 MFMA (nilpotent product); waves 3-5: the three blocks of P = LowerIncl(Qh Kc^T)
-//      from the hi/lo pairs with the exact q.k diagonal; every wave w: the right-hand sides
-//      diag(b) Kh of key tile w and diag(b) V of value tile w, and the Kb^T tile of key
-//      channels 16w..16w+15.
-//   3  every wave solves (I + A) X = Y by 16-row blocks for its key tile (-W, to LDS) and
-//      its value tile (U, kept in registers for the chain).
-//   C  wave w carries the 16 value columns 16w..16w+15 of S (fp32 in registers) through
-//      the chunk: Vn = U - W S, O^T = S^T Qh^T + Vn^T P^T, S <- diag(gamma) S + Kb^T Vn.
-// The next chunk's raw rows are loaded into registers while the current chunk runs. Two
-// workgroups share a CU (57.5 KB of LDS each), so one's barriers and dependent products
-// overlap the other's.
+// One workgroup of 8 wave64s owns one (sample segment, head); q, k, v, log a and beta are
+// read once and the output written once. The waves split into two roles that work on
+// consecutive chunks at the same time, handing operands over through double-buffered LDS,
+// with two workgroup barriers per chunk:
+//   producers (waves 4-7; wave 4 + p owns key channels and value columns 32p..32p+31)
+//     before the first barrier: chunk c + 1's rows from 16-byte row loads (chunk c + 2's
+//     loads go out as registers fall free): G by a product with a triangular ones matrix,
+//     the decayed rows, -diag(b) Kh and Qh as fragments, Kb and diag(b) V transposed, the
+//     slab's share of A and P (products over the slab's 32 channels) and of diag(P) = q.k;
+//     after it: the sums of the shares, the inverses of the two diagonal blocks of I + A
+//     (waves 4, 5), -A10 (wave 6), P (wave 7);
+//   consumers (waves 0-3; wave j owns value columns 32j..32j+31) carry their columns of
+//     S (fp32, registers) through chunk c: Z = diag(b) (V - Kh S) and Qh S before the first
+//     barrier, then X = T Z by 16-row blocks (X0 = T00 Z0, X1 = T11 (Z1 - A10 X0)), O += P X,
+//     the output, and the state update.
+// Operand layouts are chosen so that every hand-over is a lane-ordered LDS store and load
+// and every transpose is an exact product with the identity (bf16 values).
+//
+// The inverse of a diagonal block (16x16, strictly lower N): (I + N)^-1 = (I - N)(I + N^2)
+// (I + N^4)(I + N^8) exactly (N^16 = 0), with every product on bf16 MFMA from hi/lo bf16
+// pairs of its fp32 operands (hi*hi + lo*hi + hi*lo, about 16 significant bits), in the
+// transposed form M = N^T so that the result is T^T, the operand layout of T.
 //
 // Long samples (few (sample, head) units for the CUs): the sample is cut into segments.
 //   pass 1  per segment that is not its sample's last: the state reached from zero
 //           (S_loc) and the segment's transition Phi (the same chunk pass on a d_k-column
-//           state started at the identity with U taken as zero), no output;
+//           state started at the identity with V taken as zero), no output;
 //   combine per (sample, head, 16 value columns): S_in(k+1) = Phi(k) S_in(k) + S_loc(k)
 //           from the sample's initial state, with hi/lo bf16 operands;
 //   pass 2  every segment from its S_in with outputs; the last one writes final_state.
 //
-// Fragment conventions are those of kda_device.h: an accumulator tile (rows 4g+i,
-// column r) is the B operand of the same matrix and the A operand of its transpose, and a
-// product with the identity as B operand transposes a bf16 tile exactly.
+// Fragment conventions: see kda_device.h. Here an operand over 32 channels of one slab
+// holds, in lane (r, g), the 8 contiguous channels 8g..8g+7 of row r (a 16-byte load),
+// and both operands of a product use that order. Transposed (channel-row) tiles come out
+// of products with the identity on half-slabs: virtual column c of half t is channel
+// 8(c/4) + 4t + c%4 of the slab. The consumers' state uses the same orders: key tile
+// kt = 2p + t, row m is key 32p + 8(m/4) + 4t + m%4; value half th of consumer j, column
+// c is value column 32j + 8(c/4) + 4th + c%4.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <algorithm>
+#include <utility>
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -52,41 +62,108 @@
 namespace kda {
 namespace {
 using namespace dev;
+using EL = Elt<uint16_t>;
+using Frag = EL::Frag;
+using Frag16 = EL::Frag16;
 
 constexpr int kFC = 32;            // tokens per chunk
 constexpr int kFD = 128;           // d_k = d_v
-constexpr int kFThreads = 512;     // 8 wave64
-constexpr int kLDK = kFD + 8;      // token-row stride of the LDS tiles (272 bytes)
+constexpr int kFThreads = 512;     // 4 consumer + 4 producer wave64
 constexpr uint16_t kOneBf = 0x3F80;
 constexpr int kCombThreads = 256;  // combine: 4 wave64 per (sample, head, 16 value columns)
 
+// one chunk's operands for the state pass, every array in lane order
+struct Buf {
+    uint4 qf[2][4][64];    // Qh B fragments [token tile][key slab][lane]
+    uint4 yk[2][4][64];    // -Kh A fragments [token tile][key slab][lane]
+    uint4 kf[8][64];       // Kc^T A fragments [key tile][lane]
+    uint4 yv[4][2][64];    // V, tokens down the rows [value slab][half][lane]
+    uint4 pf[2][64];       // P^T B fragments [token tile][lane]
+    uint2 tf[3][64];       // (I + A_00)^-1, (I + A_11)^-1, -A_10 as 16x16x16 A fragments
+    float gam[kFD];        // gamma per key channel
+    float beta[kFC];       // beta per token (0 past the sample's end)
+};
 struct FusedSmem {
-    alignas(16) uint16_t kh[kFC * kLDK];    // Kh (token rows); after the solve, -W
-    alignas(16) uint16_t kch[kFC * kLDK];   // Kc, hi part
-    alignas(16) uint16_t kcl[kFC * kLDK];   // Kc, lo part
-    alignas(16) uint16_t qh[kFC * kLDK];    // Qh, hi part
-    alignas(16) uint16_t ql[kFC * kLDK];    // Qh, lo part
-    alignas(16) uint4 kbt[8 * 64];          // Kb^T A fragments [key tile][lane]
-    alignas(16) uint4 pf[2 * 64];           // P^T B fragments [token tile][lane]
-    alignas(16) uint2 tinv[2 * 64];         // (I + A_ii)^-1 as 16x16x16 A fragments
-    alignas(16) uint2 na10[64];             // -A_10 as a 16x16x16 A fragment
-    alignas(16) float gam[kFD];
-    alignas(16) float beta[kFC];
-    alignas(16) float dpp[4 * kFC];         // partial q.k per 32-channel slab
-    alignas(16) float ssq[2 * 4 * kFC];     // partial sums of squares of q and k per slab
+    Buf buf[2];
+    f32x4 part[4][6][64];  // per producer slab: partial A and P^T blocks
+    float ablk[2][16][16]; // the diagonal blocks of A (rows, fp32) for the inverses
+    float ssq[2][4][kFC];  // sums of squares of q and k per (slab, token)
+    float dpp[4][kFC];     // q.k per (slab, token): the diagonal of P, from the raw rows
 };
 
+__device__ __forceinline__ uint32_t bfbits_lo(uint32_t u) { return u << 16; }
+__device__ __forceinline__ uint32_t bfbits_hi(uint32_t u) { return u & 0xFFFF0000u; }
+__device__ __forceinline__ void unpack8(const uint4& u, float (&f)[8]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[2 * j] = __uint_as_float(bfbits_lo(w[j]));
+        f[2 * j + 1] = __uint_as_float(bfbits_hi(w[j]));
+    }
+}
+__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
+    return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
+}
 __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
     return make_uint2(pack2(a, b), pack2(c, d));
 }
-__device__ __forceinline__ uint2 pack4(const f32x4& x) { return pack4(x[0], x[1], x[2], x[3]); }
-__device__ __forceinline__ void unpack4(const uint2& u, float (&f)[4]) {
-    f[0] = __uint_as_float(u.x << 16);
-    f[1] = __uint_as_float(u.x & 0xFFFF0000u);
-    f[2] = __uint_as_float(u.y << 16);
-    f[3] = __uint_as_float(u.y & 0xFFFF0000u);
+__device__ __forceinline__ uint2 half_of(const uint4& u, int t) {
+    return t ? make_uint2(u.z, u.w) : make_uint2(u.x, u.y);
 }
-__device__ __forceinline__ uint2 ld8(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+// the 8 values as hi and lo bf16 parts (x = hi + lo up to the rounding of lo)
+__device__ __forceinline__ void split8(const float (&f)[8], uint4& hi, uint4& lo) {
+    hi = pack8(f);
+    const uint32_t w[4] = {hi.x, hi.y, hi.z, hi.w};
+    float r[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        r[2 * j] = f[2 * j] - __uint_as_float(bfbits_lo(w[j]));
+        r[2 * j + 1] = f[2 * j + 1] - __uint_as_float(bfbits_hi(w[j]));
+    }
+    lo = pack8(r);
+}
+
+// One elimination step of the block inverse: row KK of T (lanes KK of each 16-lane row,
+// broadcast by DPP row_newbcast) leaves every row r > KK with -A[r][KK] T[KK][.].
+template <int KK>
+__device__ __forceinline__ void elim_step(float (&t)[4], const float (&ar)[16], int r) {
+    const float a = r > KK ? -ar[KK] : 0.f;
+    float tk[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        tk[m] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(t[m]), 0x150 + KK, 0xF, 0xF, false));
+#pragma unroll
+    for (int m = 0; m < 4; ++m) t[m] = fmaf(a, tk[m], t[m]);
+}
+template <int... KK>
+__device__ __forceinline__ void elim_rows(float (&t)[4], const float (&ar)[16], int r, std::integer_sequence<int, KK...>) {
+    (elim_step<KK>(t, ar, r), ...);
+}
+
+// Orders one wave's LDS writes before its later reads of other lanes' data: the LDS
+// executes a wave's instructions in order; the clobber keeps the compiler from moving them.
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// a 16x16 fp32 accumulator tile as hi/lo bf16 fragments
+struct HL {
+    Frag16 h, l;
+};
+__device__ __forceinline__ HL hl(const f32x4& x) {
+    HL o;
+    o.h.u = pack4(x[0], x[1], x[2], x[3]);
+    const f32x4 r = f32x4{x[0] - __uint_as_float(bfbits_lo(o.h.u.x)), x[1] - __uint_as_float(bfbits_hi(o.h.u.x)),
+                          x[2] - __uint_as_float(bfbits_lo(o.h.u.y)), x[3] - __uint_as_float(bfbits_hi(o.h.u.y))};
+    o.l.u = pack4(r[0], r[1], r[2], r[3]);
+    return o;
+}
+__device__ __forceinline__ void ready(HL& a) { mfma_ready(a.h.u, a.l.u); }
+__device__ __forceinline__ void ready(HL& a, HL& b) { mfma_ready(a.h.u, a.l.u, b.h.u, b.l.u); }
+// c + A B with A and B given by hi/lo fragments (the lo*lo term is left out)
+__device__ __forceinline__ f32x4 mmhl(const HL& a, const HL& b, f32x4 c) {
+    c = EL::mma16(a.l, b.h, c);
+    c = EL::mma16(a.h, b.l, c);
+    return EL::mma16(a.h, b.h, c);
+}
 
 // clamped sample bounds, so that malformed offsets never address outside the tokens
 __device__ __forceinline__ void bounds(const int32_t* cu, int n, int64_t T, int64_t& s0, int64_t& s1) {
@@ -166,33 +243,46 @@ __device__ __forceinline__ bool find_segment(int sid, const int32_t* cu, const i
     return true;
 }
 
-// raw rows of one chunk that wave (token tile tt, channel slab cs) and value tile w need
+// key of row m of the consumers' key tile kt; value column c of half th of consumer j
+__device__ __forceinline__ int key_of(int kt, int m) { return 32 * (kt >> 1) + 8 * (m >> 2) + 4 * (kt & 1) + (m & 3); }
+__device__ __forceinline__ int col_of(int j, int th, int c) { return 32 * j + 8 * (c >> 2) + 4 * th + (c & 3); }
+
+// raw rows of one chunk for producer slab p: token tiles 0 and 1, lane (r, g) = row r,
+// channels 32p + 8g .. +7; b = beta of tokens r and 16 + r
 struct Raw {
-    uint2 q[2], k[2], l[2], l0[2], v[2];
-    uint32_t b;
+    uint4 q[2], k[2], l[2], v[2];
+    uint16_t b[2];
 };
+
+// An empty asm that takes the rows as read-write operands: code that uses them cannot be
+// scheduled before it (and it is ordered after the barriers before it).
+__device__ __forceinline__ void pin_raw(Raw& x) {
+    auto q0 = as_v(x.q[0]), q1 = as_v(x.q[1]), k0 = as_v(x.k[0]), k1 = as_v(x.k[1]);
+    auto l0 = as_v(x.l[0]), l1 = as_v(x.l[1]), v0 = as_v(x.v[0]), v1 = as_v(x.v[1]);
+    asm volatile("" : "+v"(q0), "+v"(q1), "+v"(k0), "+v"(k1), "+v"(l0), "+v"(l1), "+v"(v0), "+v"(v1),
+                 "+v"(x.b[0]), "+v"(x.b[1]));
+    from_v(x.q[0], q0); from_v(x.q[1], q1); from_v(x.k[0], k0); from_v(x.k[1], k1);
+    from_v(x.l[0], l0); from_v(x.l[1], l1); from_v(x.v[0], v0); from_v(x.v[1], v1);
+}
 
 // ---------------------------------------------------------------------------
 // PASS 0: one segment per sample, outputs. PASS 1: segment summaries (S_loc, Phi), no
 // output. PASS 2: segments from their entry state, outputs.
 // ---------------------------------------------------------------------------
 template <int PASS, bool NORM>
-__global__ __launch_bounds__(kFThreads, 2) void kda_fused_kernel(
+__global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ la, const uint16_t* __restrict__ beta, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ seg_off, const float* __restrict__ init_state, const float* __restrict__ carry,
     uint16_t* __restrict__ out, float* __restrict__ final_state, float* __restrict__ sloc,
-    uint16_t* __restrict__ phi, int num_seqs, int H, int64_t T, int lseg, int max_segs)
+    float* __restrict__ phi, int num_seqs, int H, int64_t T, int lseg, int max_segs)
 {
-    using EL = Elt<uint16_t>;
-    using Frag = EL::Frag;
-    using Frag16 = EL::Frag16;
     constexpr bool kOut = PASS != 1;
 
     __shared__ FusedSmem sm;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: role and slab in SGPRs
     const int r = lane & 15, g = lane >> 4;
-    const int tt = w & 1, cs = w >> 1;          // elementwise role: token tile, 32-channel slab
 
     // block -> (segment, head): consecutive ids on one XCD, so the heads of a segment
     // share their XCD's L2 for beta's rows
@@ -208,25 +298,6 @@ __global__ __launch_bounds__(kFThreads, 2) void kda_fused_kernel(
     const int c0 = lseg > 0 ? min(sg.seg * lseg, nch) : 0;
     const int c1 = lseg > 0 ? min(c0 + lseg, nch) : nch;
 
-    // state: value columns 16w..16w+15; tile ct holds S[16ct + 4g + i][16w + r]. PASS 1 also
-    // carries columns 16w..16w+15 of Phi (identity start).
-    f32x4 S[8], Ph[PASS == 1 ? 8 : 1];
-    {
-        const float* src = nullptr;
-        if (PASS == 2 && sg.seg > 0) src = carry + (int64_t(sid - 1) * H + h) * kFD * kFD;
-        else if (PASS != 1 && init_state) src = init_state + (int64_t(sg.n) * H + h) * kFD * kFD;
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) S[ct][i] = src ? src[(16 * ct + 4 * g + i) * kFD + 16 * w + r] : 0.f;
-        if constexpr (PASS == 1) {
-#pragma unroll
-            for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Ph[ct][i] = (16 * ct + 4 * g + i == 16 * w + r) ? 1.f : 0.f;
-        }
-    }
-
     // constant fragments: identity, inclusive lower triangle (k <= column), all ones
     Frag16 ident, tri, ones;
     {
@@ -241,384 +312,472 @@ __global__ __launch_bounds__(kFThreads, 2) void kda_fused_kernel(
         ones.u = make_uint2(kOneBf | (uint32_t(kOneBf) << 16), kOneBf | (uint32_t(kOneBf) << 16));
     }
 
+    if (w < 4) {
+        // ================= consumer: value columns of consumer j = w =================
+        const int j = w;
+        // S[kt][th]: rows key_of(kt, 4g + i), column col_of(j, th, r). PASS 1 also carries
+        // Phi's columns (keys col_of(j, th, r)), from the identity.
+        f32x4 S[8][2], Ph[PASS == 1 ? 8 : 1][PASS == 1 ? 2 : 1];
+        {
+            const float* src = nullptr;
+            if (PASS == 2 && sg.seg > 0) src = carry + (int64_t(sid - 1) * H + h) * kFD * kFD;
+            else if (PASS != 1 && init_state) src = init_state + (int64_t(sg.n) * H + h) * kFD * kFD;
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+                for (int th = 0; th < 2; ++th)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int key = key_of(kt, 4 * g + i), col = col_of(j, th, r);
+                        S[kt][th][i] = src ? src[key * kFD + col] : 0.f;
+                        if constexpr (PASS == 1) Ph[kt][th][i] = key == col ? 1.f : 0.f;
+                    }
+        }
+        // iteration it: chunk it of the segment (the producers form chunk it + 1)
+        for (int it = c0 - 1; it < c1; ++it) {
+            const bool run = it >= c0;
+            const Buf& bf = sm.buf[it & 1];
+            const int64_t t0 = s0 + int64_t(it) * kFC;
+            f32x4 Z[2][2], ZP[PASS == 1 ? 2 : 1][PASS == 1 ? 2 : 1], O[2][2];
+            if constexpr (NORM) lds_barrier();
+            if (run) {
+                // ---- Z = diag(b) (V - Kh S); O = Qh S ----
+#pragma unroll
+                for (int th = 0; th < 2; ++th) {
+                    const uint4 yv = bf.yv[j][th][lane];         // slot (ja, i): token 16ja + 4g + i
+                    Z[0][th] = f32x4{__uint_as_float(bfbits_lo(yv.x)), __uint_as_float(bfbits_hi(yv.x)),
+                                     __uint_as_float(bfbits_lo(yv.y)), __uint_as_float(bfbits_hi(yv.y))};
+                    Z[1][th] = f32x4{__uint_as_float(bfbits_lo(yv.z)), __uint_as_float(bfbits_hi(yv.z)),
+                                     __uint_as_float(bfbits_lo(yv.w)), __uint_as_float(bfbits_hi(yv.w))};
+                    if constexpr (PASS == 1) ZP[0][th] = ZP[1][th] = zero4();
+                }
+                Frag sf[4][2];
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    Frag pf2[PASS == 1 ? 2 : 1];
+#pragma unroll
+                    for (int th = 0; th < 2; ++th) {
+                        sf[kb][th] = EL::from_acc(S[2 * kb][th], S[2 * kb + 1][th]);
+                        if constexpr (PASS == 1) pf2[th] = EL::from_acc(Ph[2 * kb][th], Ph[2 * kb + 1][th]);
+                    }
+                    if constexpr (PASS == 1) mfma_ready(sf[kb][0].u, sf[kb][1].u, pf2[0].u, pf2[1].u);
+                    else mfma_ready(sf[kb][0].u, sf[kb][1].u);
+#pragma unroll
+                    for (int ja = 0; ja < 2; ++ja) {
+                        const Frag ya{bf.yk[ja][kb][lane]};
+#pragma unroll
+                        for (int th = 0; th < 2; ++th) {
+                            Z[ja][th] = EL::mma(ya, sf[kb][th], Z[ja][th]);
+                            if constexpr (PASS == 1) ZP[ja][th] = EL::mma(ya, pf2[th], ZP[ja][th]);
+                        }
+                    }
+                }
+                if constexpr (kOut) {
+#pragma unroll
+                    for (int ja = 0; ja < 2; ++ja)
+#pragma unroll
+                        for (int th = 0; th < 2; ++th) O[ja][th] = zero4();
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                        for (int ja = 0; ja < 2; ++ja) {
+                            const Frag qb{bf.qf[ja][kb][lane]};
+#pragma unroll
+                            for (int th = 0; th < 2; ++th) O[ja][th] = EL::mma(sf[kb][th], qb, O[ja][th]);
+                        }
+                }
+                // rows scaled by beta of their tokens (16ja + 4g + i)
+#pragma unroll
+                for (int ja = 0; ja < 2; ++ja) {
+                    const float4 b4 = *reinterpret_cast<const float4*>(&bf.beta[16 * ja + 4 * g]);
+#pragma unroll
+                    for (int th = 0; th < 2; ++th) {
+                        Z[ja][th] = f32x4{Z[ja][th][0] * b4.x, Z[ja][th][1] * b4.y, Z[ja][th][2] * b4.z,
+                                          Z[ja][th][3] * b4.w};
+                        if constexpr (PASS == 1)
+                            ZP[ja][th] = f32x4{ZP[ja][th][0] * b4.x, ZP[ja][th][1] * b4.y, ZP[ja][th][2] * b4.z,
+                                               ZP[ja][th][3] * b4.w};
+                    }
+                }
+            }
+            lds_barrier();                                      // B1
+            if (run) {
+                // ---- X = T Z by 16-row blocks: X0 = T00 Z0, X1 = T11 (Z1 - A10 X0) ----
+                const Frag16 t00{bf.tf[0][lane]}, t11{bf.tf[1][lane]}, na10{bf.tf[2][lane]};
+                auto solve = [&](const f32x4 (&z)[2][2], int th, f32x4& x0, f32x4& x1) __attribute__((always_inline)) {
+                    Frag16 zf = EL::from_acc16(z[0][th]);
+                    mfma_ready(zf.u);
+                    x0 = EL::mma16(t00, zf, zero4());
+                    Frag16 xf0 = EL::from_acc16(x0);
+                    mfma_ready(xf0.u);
+                    const f32x4 z1 = EL::mma16(na10, xf0, z[1][th]);
+                    Frag16 zf1 = EL::from_acc16(z1);
+                    mfma_ready(zf1.u);
+                    x1 = EL::mma16(t11, zf1, zero4());
+                };
+                Frag xf[2], xpf[PASS == 1 ? 2 : 1];
+#pragma unroll
+                for (int th = 0; th < 2; ++th) {
+                    f32x4 x0, x1;
+                    solve(Z, th, x0, x1);
+                    xf[th] = EL::from_acc(x0, x1);
+                    if constexpr (PASS == 1) {
+                        solve(ZP, th, x0, x1);
+                        xpf[th] = EL::from_acc(x0, x1);
+                    }
+                }
+                if constexpr (PASS == 1) mfma_ready(xf[0].u, xf[1].u, xpf[0].u, xpf[1].u);
+                else mfma_ready(xf[0].u, xf[1].u);
+                // ---- O += P X, store ----
+                if constexpr (kOut) {
+                    const int nrow = int(min<int64_t>(kFC, s1 - t0));
+#pragma unroll
+                    for (int ja = 0; ja < 2; ++ja) {
+                        const Frag pb{bf.pf[ja][lane]};
+#pragma unroll
+                        for (int th = 0; th < 2; ++th) O[ja][th] = EL::mma(xf[th], pb, O[ja][th]);
+                        // lane (token r, g): columns 32j + 8g + 4th + i of token 16ja + r
+                        if (16 * ja + r < nrow)
+                            *reinterpret_cast<uint4*>(out + ((t0 + 16 * ja + r) * H + h) * kFD + 32 * j + 8 * g) =
+                                make_uint4(pack2(O[ja][0][0], O[ja][0][1]), pack2(O[ja][0][2], O[ja][0][3]),
+                                           pack2(O[ja][1][0], O[ja][1][1]), pack2(O[ja][1][2], O[ja][1][3]));
+                    }
+                }
+                // ---- S <- diag(gamma) S + Kb^T X = diag(gamma) (S + Kc^T X) ----
+#pragma unroll
+                for (int kt = 0; kt < 8; ++kt) {
+                    const Frag ka{bf.kf[kt][lane]};
+#pragma unroll
+                    for (int th = 0; th < 2; ++th) {
+                        S[kt][th] = EL::mma(ka, xf[th], S[kt][th]);
+                        if constexpr (PASS == 1) Ph[kt][th] = EL::mma(ka, xpf[th], Ph[kt][th]);
+                    }
+                }
+#pragma unroll
+                for (int kt = 0; kt < 8; ++kt) {
+                    const float4 g4 = *reinterpret_cast<const float4*>(&bf.gam[key_of(kt, 4 * g)]);
+#pragma unroll
+                    for (int th = 0; th < 2; ++th) {
+                        S[kt][th] = f32x4{S[kt][th][0] * g4.x, S[kt][th][1] * g4.y, S[kt][th][2] * g4.z,
+                                          S[kt][th][3] * g4.w};
+                        if constexpr (PASS == 1)
+                            Ph[kt][th] = f32x4{Ph[kt][th][0] * g4.x, Ph[kt][th][1] * g4.y, Ph[kt][th][2] * g4.z,
+                                               Ph[kt][th][3] * g4.w};
+                    }
+                }
+            }
+            lds_barrier();                                      // B2
+        }
+        // ---- the segment's results ----
+        float* dst = nullptr;
+        if constexpr (PASS == 1) {
+            const int64_t unit = int64_t(sid) * H + h;
+            dst = sloc + unit * kFD * kFD;
+            float* pd = phi + unit * kFD * kFD;
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+                for (int th = 0; th < 2; ++th)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) pd[key_of(kt, 4 * g + i) * kFD + col_of(j, th, r)] = Ph[kt][th][i];
+        } else if (final_state && sg.seg == sg.nseg - 1) {
+            dst = final_state + (int64_t(sg.n) * H + h) * kFD * kFD;
+        }
+        if (dst) {
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+                for (int th = 0; th < 2; ++th)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dst[key_of(kt, 4 * g + i) * kFD + col_of(j, th, r)] = S[kt][th][i];
+        }
+        return;
+    }
+
+    // ================= producer: slab p = w - 4 =================
+    const int p = w - 4;
     // Raw rows of chunk c (clamped to the segment's last chunk: a load past the end is issued
-    // all the same and never used). Every wave issues the same loads without conditions, so
-    // that the waits for one chunk's rows never include the loads issued after them.
-    auto load_raw = [&](Raw& x, int c) __attribute__((always_inline)) {
+    // all the same and never used; the segment has at least one chunk). Every step issues
+    // them without conditions, so that the waits for one chunk's rows never include the
+    // loads issued after them.
+    auto row_off = [&](int c, int tt) __attribute__((always_inline)) -> int64_t {
         const int64_t t0 = s0 + int64_t(min(c, c1 - 1)) * kFC;
         const int nrow = int(min<int64_t>(kFC, s1 - t0));
-        const int64_t ob = ((t0 + min(16 * tt + r, nrow - 1)) * H + h) * kFD + 32 * cs + 4 * g;
-        const int64_t o0 = ((t0 + min(r, nrow - 1)) * H + h) * kFD + 32 * cs + 4 * g;
+        return t0 + min(16 * tt + r, nrow - 1);
+    };
+    auto load_l = [&](Raw& x, int c) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            if constexpr (kOut) x.q[j] = ld8(q + ob + 16 * j);
-            x.k[j] = ld8(k + ob + 16 * j);
-            x.l[j] = ld8(la + ob + 16 * j);
-            x.l0[j] = ld8(la + o0 + 16 * j);
-        }
+        for (int tt = 0; tt < 2; ++tt)
+            x.l[tt] = *reinterpret_cast<const uint4*>(la + (row_off(c, tt) * H + h) * kFD + 32 * p + 8 * g);
+    };
+    auto load_tile = [&](Raw& x, int c, int tt) __attribute__((always_inline)) {
+        const int64_t row = row_off(c, tt);
+        const int64_t o = (row * H + h) * kFD + 32 * p + 8 * g;
+        if constexpr (kOut) x.q[tt] = *reinterpret_cast<const uint4*>(q + o);
+        x.k[tt] = *reinterpret_cast<const uint4*>(k + o);
+        x.v[tt] = *reinterpret_cast<const uint4*>(v + o);
+    };
+    // beta first in a step: the conversion of its 16 bits may be placed anywhere before the
+    // next step, and then waits for these two loads only (the counter is in order)
+    auto load_beta = [&](Raw& x, int c) __attribute__((always_inline)) {
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-            x.v[rt] = ld8(v + ((t0 + min(16 * rt + r, nrow - 1)) * H + h) * kFD + 16 * w + 4 * g);
-        x.b = beta[(t0 + min(lane & 31, nrow - 1)) * H + h];
+        for (int tt = 0; tt < 2; ++tt) x.b[tt] = beta[row_off(c, tt) * H + h];
     };
 
-    // One chunk: `cur` holds its raw rows, the next chunk's rows are loaded into `nxt`. The
-    // loop below alternates two register sets, so a chunk waits only for its own rows, which
-    // were loaded during the previous chunk (a copy of nxt into cur would tie every chunk's
-    // waits to the loads it has just issued).
-    auto step = [&](const Raw& cur, Raw& nxt, int c) __attribute__((always_inline)) {
+    // Operands of chunk c from its raw rows `cur`; the rows of chunk c + 1 are loaded into
+    // `nxt` piece by piece as `cur`'s registers fall free. Barriers as the consumers'.
+    auto step = [&](const Raw& cur_in, Raw& nxt, int c) __attribute__((always_inline)) {
+        Buf& bf = sm.buf[c & 1];
+        // the rows become visible here, after the previous step's last barrier: no use of them
+        // moves up into the previous step, where it would wait for the loads just issued
+        Raw cur = cur_in;
+        pin_raw(cur);
+        load_beta(nxt, c + 1);
         const int64_t t0 = s0 + int64_t(c) * kFC;
         const int nrow = int(min<int64_t>(kFC, s1 - t0));
-        load_raw(nxt, c + 1);
-
-        // ===== E: decayed operands of token tile tt, channels 32cs..32cs+31 =====
-        {
-            const bool rowok = 16 * tt + r < nrow;
-            const uint2 z2 = make_uint2(0u, 0u);
-            // G^T(ct, tt) = sum_{rp <= tt} Lam^T(ct, rp) L^T(rp, tt): lane (r, g) then holds
-            // G[16tt + r][16ct + 4g + i], the layout of the raw rows
-            Frag16 lf[2], l0f[2];
+        // ---- E: decayed rows, partial products over the slab, transposes ----
+        bool rowok[2];
+        float bt[2], qs[2] = {1.f, 1.f}, ks[2] = {1.f, 1.f};
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                lf[j] = EL::from_acc16(EL::mma16(Frag16{rowok ? cur.l[j] : z2}, ident, zero4()));
-                l0f[j] = tt ? EL::from_acc16(EL::mma16(Frag16{r < nrow ? cur.l0[j] : z2}, ident, zero4())) : Frag16{z2};
-            }
-            mfma_ready(lf[0].u, lf[1].u, l0f[0].u, l0f[1].u);
-            f32x4 G[2];
+        for (int tt = 0; tt < 2; ++tt) {
+            rowok[tt] = 16 * tt + r < nrow;
+            bt[tt] = rowok[tt] ? bf2f(cur.b[tt]) : 0.f;
+        }
+        if constexpr (NORM) {
+            // each row's sums of squares over the 128 channels: four lanes here and the
+            // three other slabs' waves, summed in a fixed order
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                G[j] = EL::mma16(lf[j], tri, zero4());
-                if (tt) G[j] = EL::mma16(l0f[j], ones, G[j]);
-            }
-            float qf[2][4], kf[2][4];
+            for (int tt = 0; tt < 2; ++tt) {
+                float kf[8], qf[8], qq = 0.f, kk = 0.f;
+                unpack8(cur.k[tt], kf);
+                if constexpr (kOut) unpack8(cur.q[tt], qf);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                if constexpr (kOut) unpack4(rowok ? cur.q[j] : z2, qf[j]);
-                unpack4(rowok ? cur.k[j] : z2, kf[j]);
-            }
-            if constexpr (NORM) {
-                // each row's sums of squares over the 128 channels: four lanes of this wave
-                // and the three waves of the row's other channel slabs
-                float qq = 0.f, kk = 0.f;
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        if constexpr (kOut) qq += qf[j][s] * qf[j][s];
-                        kk += kf[j][s] * kf[j][s];
-                    }
+                for (int e = 0; e < 8; ++e) {
+                    if constexpr (kOut) qq += qf[e] * qf[e];
+                    kk += kf[e] * kf[e];
+                }
                 qq += __shfl_xor(qq, 16);
                 qq += __shfl_xor(qq, 32);
                 kk += __shfl_xor(kk, 16);
                 kk += __shfl_xor(kk, 32);
                 if (g == 0) {
-                    sm.ssq[cs * kFC + 16 * tt + r] = qq;
-                    sm.ssq[(4 + cs) * kFC + 16 * tt + r] = kk;
+                    sm.ssq[0][p][16 * tt + r] = qq;
+                    sm.ssq[1][p][16 * tt + r] = kk;
                 }
-                lds_barrier();
+            }
+            lds_barrier();
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
                 float tq = 0.f, tk = 0.f;
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {      // fixed order: the same sum in every wave
-                    tq += sm.ssq[x * kFC + 16 * tt + r];
-                    tk += sm.ssq[(4 + x) * kFC + 16 * tt + r];
+                for (int x = 0; x < 4; ++x) {
+                    tq += sm.ssq[0][x][16 * tt + r];
+                    tk += sm.ssq[1][x][16 * tt + r];
                 }
-                const float qs = tq > 0.f ? 1.f / sqrtf(tq) : 0.f;
-                const float ks = tk > 0.f ? 1.f / sqrtf(tk) : 0.f;
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        if constexpr (kOut) qf[j][s] *= qs;
-                        kf[j][s] *= ks;
-                    }
+                qs[tt] = tq > 0.f ? 1.f / sqrtf(tq) : 0.f;
+                ks[tt] = tk > 0.f ? 1.f / sqrtf(tk) : 0.f;
             }
-            float dp = 0.f;
+        }
+        {
+            // G over the chunk: the half-slab tiles of log a transposed (product with the
+            // identity), then a product with the inclusive triangle, tile 1 plus tile 0's sum;
+            // lane (r, g) gets G[16tt + r][8g + 4t + i], the layout of its raw rows
+            Frag16 lt[2][2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int ct = 2 * cs + j;
-                float ex[4], fkh[4], fkc[4], lkc[4], fq[4], lq[4];
+            for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const float G2 = G[j][s] * kLog2e;
-                    ex[s] = fast_exp2(G2);
-                    const float ei = fast_exp2(-G2);
-                    fkh[s] = kf[j][s] * ex[s];
-                    fkc[s] = kf[j][s] * ei;
-                    lkc[s] = fkc[s] - bf2f(f2bf(fkc[s]));
-                    if constexpr (kOut) {
-                        dp += qf[j][s] * kf[j][s];
-                        fq[s] = qf[j][s] * ex[s];
-                        lq[s] = fq[s] - bf2f(f2bf(fq[s]));
-                    }
+                for (int t = 0; t < 2; ++t) {
+                    const uint2 lv = rowok[tt] ? half_of(cur.l[tt], t) : make_uint2(0u, 0u);
+                    lt[tt][t] = EL::from_acc16(EL::mma16(Frag16{lv}, ident, zero4()));
                 }
-                const int o = (16 * tt + r) * kLDK + 16 * ct + 4 * g;
-                *reinterpret_cast<uint2*>(&sm.kh[o]) = pack4(fkh[0], fkh[1], fkh[2], fkh[3]);
-                *reinterpret_cast<uint2*>(&sm.kch[o]) = pack4(fkc[0], fkc[1], fkc[2], fkc[3]);
-                *reinterpret_cast<uint2*>(&sm.kcl[o]) = pack4(lkc[0], lkc[1], lkc[2], lkc[3]);
+            mfma_ready(lt[0][0].u, lt[0][1].u, lt[1][0].u, lt[1][1].u);
+            f32x4 G[2][2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                G[0][t] = EL::mma16(lt[0][t], tri, zero4());
+                G[1][t] = EL::mma16(lt[0][t], ones, EL::mma16(lt[1][t], tri, zero4()));
+            }
+            load_l(nxt, c + 1);
+            if (p == 0 && g == 0) {
+                bf.beta[r] = bt[0];
+                bf.beta[16 + r] = bt[1];
+            }
+            // decayed rows (rows past the sample's end: beta is 0 there, so they reach no
+            // valid row through A, P, X or the state; log a is 0, so G and gamma stop there)
+            uint4 khF[2], kcH[2], qH[2];
+#pragma unroll
+            for (int pass_t = 0; pass_t < 2; ++pass_t) {
+                const int tt = 1 - pass_t;
+                float kf[8], qf[8];
+                unpack8(cur.k[tt], kf);
+                if constexpr (kOut) unpack8(cur.q[tt], qf);
+                float ex[8], ei[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float G2 = G[tt][e >> 2][e & 3] * kLog2e;
+                    ex[e] = fast_exp2(G2);
+                    ei[e] = fast_exp2(-G2);
+                }
+                // gamma = e^G of token 31, held by the lanes of row 15 of tile 1
+                if (tt == 1 && r == 15) {
+                    *reinterpret_cast<float4*>(&bf.gam[32 * p + 8 * g]) = make_float4(ex[0], ex[1], ex[2], ex[3]);
+                    *reinterpret_cast<float4*>(&bf.gam[32 * p + 8 * g + 4]) = make_float4(ex[4], ex[5], ex[6], ex[7]);
+                }
+                float fkh[8], fkc[8], fq[8];
+                float dp = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float kx = NORM ? kf[e] * ks[tt] : kf[e];
+                    const float qx = kOut ? (NORM ? qf[e] * qs[tt] : qf[e]) : 0.f;
+                    fkh[e] = kx * ex[e];
+                    fkc[e] = kx * ei[e];
+                    fq[e] = qx * ex[e];
+                    dp += kx * qx;
+                }
+                khF[tt] = pack8(fkh);
+                kcH[tt] = pack8(fkc);
+                bf.yk[tt][p][lane] = make_uint4(khF[tt].x ^ 0x80008000u, khF[tt].y ^ 0x80008000u,
+                                                khF[tt].z ^ 0x80008000u, khF[tt].w ^ 0x80008000u);
                 if constexpr (kOut) {
-                    *reinterpret_cast<uint2*>(&sm.qh[o]) = pack4(fq[0], fq[1], fq[2], fq[3]);
-                    *reinterpret_cast<uint2*>(&sm.ql[o]) = pack4(lq[0], lq[1], lq[2], lq[3]);
+                    // q.k of the row over the slab (e^G e^-G = 1 on the diagonal of P)
+                    dp += __shfl_xor(dp, 16);
+                    dp += __shfl_xor(dp, 32);
+                    if (g == 0) sm.dpp[p][16 * tt + r] = dp;
+                    qH[tt] = pack8(fq);
+                    bf.qf[tt][p][lane] = qH[tt];
+                } else {
+                    qH[tt] = make_uint4(0u, 0u, 0u, 0u);
                 }
-                // gamma = exp(G of row 31); rows past the sample's end add nothing to G
-                if (tt == 1 && r == 15)
-                    *reinterpret_cast<float4*>(&sm.gam[16 * ct + 4 * g]) = make_float4(ex[0], ex[1], ex[2], ex[3]);
+                load_tile(nxt, c + 1, tt);
             }
+            mfma_ready(khF[0], khF[1], kcH[0], kcH[1]);
+            mfma_ready(qH[0], qH[1]);
+            // partial products over the slab: Acc(X) holds X[4g + i][r]
+            f32x4* pp = &sm.part[p][0][0];
+            pp[0 * 64 + lane] = EL::mma(Frag{khF[0]}, Frag{kcH[0]}, zero4());   // Kh0 Kc0^T
+            pp[1 * 64 + lane] = EL::mma(Frag{khF[1]}, Frag{kcH[1]}, zero4());   // Kh1 Kc1^T
+            pp[2 * 64 + lane] = EL::mma(Frag{kcH[0]}, Frag{khF[1]}, zero4());   // (Kh1 Kc0^T)^T
             if constexpr (kOut) {
-                dp += __shfl_xor(dp, 16);
-                dp += __shfl_xor(dp, 32);
-                if (g == 0) sm.dpp[cs * kFC + 16 * tt + r] = dp;
+                // P^T blocks (Kc Qh^T): (0, 0), (1, 1), (1, 0)
+                pp[3 * 64 + lane] = EL::mma(Frag{kcH[0]}, Frag{qH[0]}, zero4());
+                pp[4 * 64 + lane] = EL::mma(Frag{kcH[1]}, Frag{qH[1]}, zero4());
+                pp[5 * 64 + lane] = EL::mma(Frag{kcH[0]}, Frag{qH[1]}, zero4());
             }
-            if (w == 0 && lane < kFC) sm.beta[lane] = lane < nrow ? bf2f(uint16_t(cur.b)) : 0.f;
-        }
-        lds_barrier();
-
-        // ===== 2: blocks of A (and its diagonal inverses) and of P; right-hand sides and
-        //       Kb^T of key tile w / value tile w =====
-        auto lds4 = [&](const uint16_t* arr, int row, int col) -> uint2 {
-            return *reinterpret_cast<const uint2*>(&arr[row * kLDK + col]);
-        };
-        if (w < 3) {
-            // A block (ti, tj): w0 (0, 0), w1 (1, 1), w2 (1, 0). With Kc rows as the A operand
-            // and Kh rows as the B operand, lane (r, g) holds (Kh Kc^T)[16ti + r][16tj + 4g + s],
-            // a row of the block: the A operand layout of a 16x16x16 product.
-            const int ti = w == 0 ? 0 : 1, tj = w == 1 ? 1 : 0;
-            f32x4 aa = zero4();
+            // transposes (channel rows over the chunk's tokens, exact): Kc^T and V to LDS
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-                aa = EL::mma(EL::load(&sm.kch[(16 * tj + r) * kLDK + 32 * kb], g),
-                             EL::load(&sm.kh[(16 * ti + r) * kLDK + 32 * kb], g), aa);
-            const float bt = sm.beta[16 * ti + r];
-            if (w == 2) {
-                sm.na10[lane] = pack4(-bt * aa[0], -bt * aa[1], -bt * aa[2], -bt * aa[3]);
-            } else {
-                // A_ii strictly lower: (I + A)^-1 = (I - A)(I + A^2)(I + A^4)(I + A^8) exactly
-                // (A^16 = 0), on fp32 MFMA. mm(xt, y) = X Y from the accumulator tiles of X^T and Y.
-                f32x4 at, id;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    at[s] = (4 * g + s < r) ? bt * aa[s] : 0.f;     // tile of A^T: A[r][4g + s]
-                    id[s] = (4 * g + s == r) ? 1.f : 0.f;
-                }
-                auto mm = [](const f32x4& xt, const f32x4& y) {
-                    f32x4 c = zero4();
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(xt[s], y[s], c, 0, 0, 0);
-                    return c;
-                };
-                const f32x4 ac = mm(at, id);                        // tile of A (exact transpose)
-                const f32x4 b1 = mm(at, ac), b1t = mm(ac, at);      // A^2, (A^2)^T
-                const f32x4 b2 = mm(b1t, b1), b2t = mm(b1, b1t);    // A^4, (A^4)^T
-                const f32x4 b3 = mm(b2t, b2);                       // A^8
-                const f32x4 x1t = id - at + b1t - mm(b1, at);       // ((I - A)(I + A^2))^T
-                const f32x4 x2t = x1t + mm(b2, x1t);                // (X1 (I + A^4))^T
-                const f32x4 tinv = x2t + mm(b3, x2t);               // T^T: lane holds T[r][4g + s]
-                sm.tinv[w * 64 + lane] = pack4(tinv);
-            }
-        } else if (kOut && w < 6) {
-            // P block (ti, tj): w3 (0, 0), w4 (1, 1), w5 (1, 0); hi*hi + lo*hi + hi*lo, and the
-            // exact q.k on the diagonal
-            const int ti = w == 3 ? 0 : 1, tj = w == 4 ? 1 : 0;
-            f32x4 pp = zero4();
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const Frag kch = EL::load(&sm.kch[(16 * tj + r) * kLDK + 32 * kb], g);
-                const Frag kcl = EL::load(&sm.kcl[(16 * tj + r) * kLDK + 32 * kb], g);
-                const Frag qhh = EL::load(&sm.qh[(16 * ti + r) * kLDK + 32 * kb], g);
-                const Frag qhl = EL::load(&sm.ql[(16 * ti + r) * kLDK + 32 * kb], g);
-                pp = EL::mma(kch, qhh, pp);
-                pp = EL::mma(kcl, qhh, pp);
-                pp = EL::mma(kch, qhl, pp);
-            }
-            float pv[4];
-            if (ti == tj) {
-                const int row = 16 * ti + r;
-                const float dg = sm.dpp[row] + sm.dpp[kFC + row] + sm.dpp[2 * kFC + row] + sm.dpp[3 * kFC + row];
-#pragma unroll
-                for (int s = 0; s < 4; ++s) pv[s] = 4 * g + s < r ? pp[s] : (4 * g + s == r ? dg : 0.f);
-            } else {
-#pragma unroll
-                for (int s = 0; s < 4; ++s) pv[s] = pp[s];
-            }
-            // the B fragment of P^T for output tile ti holds P[16ti + r][16t' + 4g + s], t' = tj
-            uint2* dst = reinterpret_cast<uint2*>(&sm.pf[ti * 64 + lane]);
-            dst[tj] = pack4(pv[0], pv[1], pv[2], pv[3]);
-            if (w == 3) dst[1] = make_uint2(0u, 0u);               // P(0, 1) is above the diagonal
-        }
-        // right-hand sides of key tile w and value tile w, channel-row layout: tile rt holds
-        // Y[16rt + 4g + s][16w + r] (the B operand over the chunk's tokens)
-        f32x4 yk[2], yv[2];
-        {
-            float4 b4[2];
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) b4[rt] = *reinterpret_cast<const float4*>(&sm.beta[16 * rt + 4 * g]);
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const f32x4 kt = EL::mma16(Frag16{lds4(sm.kh, 16 * rt + r, 16 * w + 4 * g)}, ident, zero4());
-                const f32x4 vt = EL::mma16(Frag16{16 * rt + r < nrow ? cur.v[rt] : make_uint2(0u, 0u)}, ident, zero4());
-                yk[rt] = f32x4{b4[rt].x * kt[0], b4[rt].y * kt[1], b4[rt].z * kt[2], b4[rt].w * kt[3]};
-                yv[rt] = f32x4{b4[rt].x * vt[0], b4[rt].y * vt[1], b4[rt].z * vt[2], b4[rt].w * vt[3]};
-            }
-            // Kb^T tile of key channels 16w..16w+15 as the A operand over the chunk's tokens:
-            // lane (r, g) holds gamma[16w + r] Kc[16t' + 4g + s][16w + r]
-            const float gm = sm.gam[16 * w + r];
-            uint2 kb2[2];
-#pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2) {
-                f32x4 kc = EL::mma16(Frag16{lds4(sm.kch, 16 * t2 + r, 16 * w + 4 * g)}, ident, zero4());
-                kc = EL::mma16(Frag16{lds4(sm.kcl, 16 * t2 + r, 16 * w + 4 * g)}, ident, kc);
-                kb2[t2] = pack4(gm * kc[0], gm * kc[1], gm * kc[2], gm * kc[3]);
-            }
-            sm.kbt[w * 64 + lane] = make_uint4(kb2[0].x, kb2[0].y, kb2[1].x, kb2[1].y);
-        }
-        lds_barrier();
-
-        // ===== 3: (I + A) X = Y by 16-row blocks: X0 = T00 Y0, X1 = T11 (Y1 - A10 X0) =====
-        {
-            const Frag16 t00{sm.tinv[lane]}, t11{sm.tinv[64 + lane]}, a10{sm.na10[lane]};
-            // U of value tile w (stays in registers) and W of key tile w, side by side
-            Frag16 pv = EL::from_acc16(yv[0]), pk = EL::from_acc16(yk[0]);
-            mfma_ready(pv.u, pk.u);
-            yv[0] = EL::mma16(t00, pv, zero4());
-            yk[0] = EL::mma16(t00, pk, zero4());
-            pv = EL::from_acc16(yv[0]);
-            pk = EL::from_acc16(yk[0]);
-            mfma_ready(pv.u, pk.u);
-            const f32x4 av = EL::mma16(a10, pv, yv[1]);
-            const f32x4 ak = EL::mma16(a10, pk, yk[1]);
-            pv = EL::from_acc16(av);
-            pk = EL::from_acc16(ak);
-            mfma_ready(pv.u, pk.u);
-            yv[1] = EL::mma16(t11, pv, zero4());
-            yk[1] = EL::mma16(t11, pk, zero4());
-            // -W in token rows (the A operand of W S): transpose with the identity product
-            Frag16 nw[2] = {EL::from_acc16(-yk[0]), EL::from_acc16(-yk[1])};
-            mfma_ready(nw[0].u, nw[1].u);
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const f32x4 wt = EL::mma16(nw[rt], ident, zero4());
-                *reinterpret_cast<uint2*>(&sm.kh[(16 * rt + r) * kLDK + 16 * w + 4 * g]) = pack4(wt);
+            for (int t = 0; t < 2; ++t) {
+                const f32x4 a0 = EL::mma16(Frag16{half_of(kcH[0], t)}, ident, zero4());
+                const f32x4 a1 = EL::mma16(Frag16{half_of(kcH[1], t)}, ident, zero4());
+                bf.kf[2 * p + t][lane] = EL::from_acc(a0, a1).u;
+                const f32x4 v0 = EL::mma16(Frag16{half_of(cur.v[0], t)}, ident, zero4());
+                const f32x4 v1 = EL::mma16(Frag16{half_of(cur.v[1], t)}, ident, zero4());
+                bf.yv[p][t][lane] = EL::from_acc(v0, v1).u;
             }
         }
-        lds_barrier();
-
-        // ===== C: the state pass over value columns 16w..16w+15 =====
-        {
-            Frag sf[4];
+        lds_barrier();                                          // B1
+        // ---- sums of the partial products: the diagonal blocks' inverses (waves 4, 5), -A10
+        //      (wave 6), P (wave 7) ----
+        if (p < 2) {
+            // A_ii = StrictLower(diag(b) Kh Kc^T) of diagonal block ii = p, rows to LDS
+            const int ii = p;
+            {
+                f32x4 n = zero4();
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) sf[kb] = EL::from_acc(S[2 * kb], S[2 * kb + 1]);
-            mfma_ready(sf[0].u, sf[1].u, sf[2].u, sf[3].u);
-            f32x4 X[2] = {yv[0], yv[1]};                 // Vn = U - W S: rows 16rt + 4g + i, column r
-            f32x4 XP[2] = {zero4(), zero4()};            // the transition's columns (U = 0)
-            Frag pfr[4];
-            if constexpr (PASS == 1) {
+                for (int x = 0; x < 4; ++x) n += sm.part[x][ii][lane];
+                const float4 b4 = *reinterpret_cast<const float4*>(&bf.beta[16 * ii + 4 * g]);
+                const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) pfr[kb] = EL::from_acc(Ph[2 * kb], Ph[2 * kb + 1]);
-                mfma_ready(pfr[0].u, pfr[1].u, pfr[2].u, pfr[3].u);
+                for (int i = 0; i < 4; ++i) sm.ablk[ii][4 * g + i][r] = 4 * g + i > r ? bb[i] * n[i] : 0.f;
+            }
+            lds_wait();
+            // T = (I + A_ii)^-1 in fp32 by elimination: lane (r, g) holds row r of A and
+            // T[r][4g..4g+3]; for k = 0..14 row k is final and every row below it takes
+            // -A[r][k] T[k][.], with T[k][.] broadcast along the lanes of the row (DPP)
+            float ar[16];
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4) {
+                const float4 a4 = *reinterpret_cast<const float4*>(&sm.ablk[ii][r][4 * k4]);
+                ar[4 * k4] = a4.x;
+                ar[4 * k4 + 1] = a4.y;
+                ar[4 * k4 + 2] = a4.z;
+                ar[4 * k4 + 3] = a4.w;
+            }
+            float t[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) t[m] = r == 4 * g + m ? 1.f : 0.f;
+            elim_rows(t, ar, r, std::make_integer_sequence<int, 15>{});
+            bf.tf[ii][lane] = pack4(t[0], t[1], t[2], t[3]);     // A operand: T_ii[r][4g + i]
+        } else if (p == 2) {
+            // A10 as the A operand: Acc((Kh1 Kc0^T)^T) holds (Kh1 Kc0^T)[r][4g + i], row r of block
+            // (1, 0), scaled by beta of token 16 + r; negated for the solve
+            f32x4 n = zero4();
+#pragma unroll
+            for (int x = 0; x < 4; ++x) n += sm.part[x][2][lane];
+            const float nbt = -bf.beta[16 + r];
+            bf.tf[2][lane] = pack4(nbt * n[0], nbt * n[1], nbt * n[2], nbt * n[3]);
+        } else if (kOut) {
+            f32x4 p00 = zero4(), p11 = zero4(), p10 = zero4();
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                p00 += sm.part[x][3][lane];
+                p11 += sm.part[x][4][lane];
+                p10 += sm.part[x][5][lane];
+            }
+            float dg[2] = {0.f, 0.f};                           // the exact diagonal, tokens r and 16 + r
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                dg[0] += sm.dpp[x][r];
+                dg[1] += sm.dpp[x][16 + r];
             }
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-                    const Frag wf = EL::load(&sm.kh[(16 * rt + r) * kLDK + 32 * kb], g);
-                    X[rt] = EL::mma(wf, sf[kb], X[rt]);
-                    if constexpr (PASS == 1) XP[rt] = EL::mma(wf, pfr[kb], XP[rt]);
-                }
-            f32x4 O[2] = {zero4(), zero4()};             // O^T: O[16rt + r][16w + 4g + i]
-            if constexpr (kOut) {
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                    for (int rt = 0; rt < 2; ++rt)
-                        O[rt] = EL::mma(sf[kb], EL::load(&sm.qh[(16 * rt + r) * kLDK + 32 * kb], g), O[rt]);
-            }
-            Frag vf = EL::from_acc(X[0], X[1]);          // Vn over the chunk's tokens
-            Frag vfp;
-            if constexpr (PASS == 1) {
-                vfp = EL::from_acc(XP[0], XP[1]);
-                mfma_ready(vf.u, vfp.u);
-            } else {
-                mfma_ready(vf.u);
-            }
-            if constexpr (kOut) {
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) O[rt] = EL::mma(vf, Frag{sm.pf[rt * 64 + lane]}, O[rt]);
-            }
-#pragma unroll
-            for (int ct = 0; ct < 8; ++ct) {
-                const float4 g4 = *reinterpret_cast<const float4*>(&sm.gam[16 * ct + 4 * g]);
-                const Frag kf = Frag{sm.kbt[ct * 64 + lane]};
-                S[ct] = f32x4{S[ct][0] * g4.x, S[ct][1] * g4.y, S[ct][2] * g4.z, S[ct][3] * g4.w};
-                S[ct] = EL::mma(kf, vf, S[ct]);
-                if constexpr (PASS == 1) {
-                    Ph[ct] = f32x4{Ph[ct][0] * g4.x, Ph[ct][1] * g4.y, Ph[ct][2] * g4.z, Ph[ct][3] * g4.w};
-                    Ph[ct] = EL::mma(kf, vfp, Ph[ct]);
+            for (int i = 0; i < 4; ++i) {                       // P[r][4g + i], inclusive lower
+                if (4 * g + i > r) {
+                    p00[i] = 0.f;
+                    p11[i] = 0.f;
+                } else if (4 * g + i == r) {
+                    p00[i] = dg[0];
+                    p11[i] = dg[1];
                 }
             }
-            if constexpr (kOut) {
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-                    const int row = 16 * rt + r;
-                    if (row < nrow)
-                        *reinterpret_cast<uint2*>(out + ((t0 + row) * H + h) * kFD + 16 * w + 4 * g) = pack4(O[rt]);
-                }
-            }
+            bf.pf[0][lane] = EL::from_acc(p00, zero4()).u;
+            bf.pf[1][lane] = EL::from_acc(p10, p11).u;
         }
-        lds_barrier();
+        lds_barrier();                                          // B2
     };
-    Raw ra, rb;
-    if (c0 < c1) load_raw(ra, c0);
-    for (int c = c0; c < c1; c += 2) {
-        step(ra, rb, c);
-        if (c + 1 < c1) step(rb, ra, c + 1);
-    }
 
-    if constexpr (PASS == 1) {
-        // S_loc (fp32, [d_k][d_v]) and Phi as hi/lo bf16 A fragments of the combine's products
-        // (rows = output key channel, k = input key channel): fragment (ct, kb) half w & 1 of
-        // kb = w >> 1 holds Phi[16ct + r][16w + 4g + s], the exact transpose of tile ct
-        const int64_t unit = int64_t(sid) * H + h;
-        float* sl = sloc + unit * kFD * kFD;
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sl[(16 * ct + 4 * g + i) * kFD + 16 * w + r] = S[ct][i];
-        uint16_t* pb = phi + unit * (2 * 8 * 4 * 64 * 8);
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-            f32x4 lo;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) lo[i] = Ph[ct][i] - bf2f(f2bf(Ph[ct][i]));
-            Frag16 fh = EL::from_acc16(Ph[ct]), fl = EL::from_acc16(lo);
-            mfma_ready(fh.u, fl.u);
-            const f32x4 th = EL::mma16(fh, ident, zero4());
-            const f32x4 tl = EL::mma16(fl, ident, zero4());
-            const int o = ((ct * 4 + (w >> 1)) * 64 + lane) * 8 + (w & 1) * 4;
-            *reinterpret_cast<uint2*>(pb + o) = pack4(th);
-            *reinterpret_cast<uint2*>(pb + 8 * 4 * 64 * 8 + o) = pack4(tl);
+    if (c0 < c1) {
+        // step c forms chunk c (the consumers' chunk c - 1); the loop alternates two
+        // register sets for the raw rows
+        Raw ra, rb;
+        load_beta(ra, c0);
+        load_l(ra, c0);
+        load_tile(ra, c0, 1);
+        load_tile(ra, c0, 0);
+        int c = c0;
+        for (; c + 1 < c1; c += 2) {
+            step(ra, rb, c);
+            step(rb, ra, c + 1);
         }
-    } else if (final_state && sg.seg == sg.nseg - 1) {
-        float* fs = final_state + (int64_t(sg.n) * H + h) * kFD * kFD;
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) fs[(16 * ct + 4 * g + i) * kFD + 16 * w + r] = S[ct][i];
+        if (c < c1) step(ra, rb, c);
     }
+    // the consumers' last chunk: barriers only
+    if constexpr (NORM) lds_barrier();
+    lds_barrier();
+    lds_barrier();
 }
 
 // ---------------------------------------------------------------------------
 // combine: per (sample, head, 16 value columns), the entry state of every segment,
 // S_in(k + 1) = Phi(k) S_in(k) + S_loc(k), S_in(0) = the initial state; S_in(k + 1) is
 // written over S_loc(k) (the slot of segment k), which no later step reads. Wave w
-// computes output rows 32w..32w+31 (key tiles 2w, 2w + 1); the full S_in enters every
-// wave's products as hi/lo bf16 B fragments through LDS.
+// computes output rows 32w..32w+31 (key tiles 2w, 2w + 1); Phi's rows (fp32) enter as
+// hi/lo bf16 A fragments, the full S_in as hi/lo B fragments through LDS.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kCombThreads) void kda_fused_combine_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ seg_off, const float* __restrict__ init_state,
-    float* __restrict__ sloc, const uint16_t* __restrict__ phi, int num_seqs, int H, int64_t T, int lseg,
+    float* __restrict__ sloc, const float* __restrict__ phi, int num_seqs, int H, int64_t T, int lseg,
     int max_segs)
 {
-    using EL = Elt<uint16_t>;
-    using Frag = EL::Frag;
     __shared__ uint4 sb[2][4][64];              // S_in as B fragments: [hi/lo][k-block][lane]
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int r = lane & 15, g = lane >> 4;
@@ -653,38 +812,37 @@ __global__ __launch_bounds__(kCombThreads) void kda_fused_combine_kernel(
         for (int i = 0; i < 4; ++i)
             S[j][i] = init_state ? init_state[((int64_t(n) * H + h) * kFD + 32 * w + 16 * j + 4 * g + i) * kFD + col]
                                  : 0.f;
-    constexpr int kPhiHalf = 8 * 4 * 64 * 8;    // bf16 elements of the hi (or lo) fragments
-    auto phi_frag = [&](int64_t u, int hl, int ct, int kb) -> Frag {
-        return Frag{*reinterpret_cast<const uint4*>(phi + u * 2 * kPhiHalf + hl * kPhiHalf + ((ct * 4 + kb) * 64 + lane) * 8)};
-    };
     for (int kseg = 0; kseg + 1 < nseg; ++kseg) {
         const int64_t u = int64_t(first + kseg) * H + h;
         // publish S_in(kseg): this wave's rows are k-block w of the products
         {
-            f32x4 l0, l1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                l0[i] = S[0][i] - bf2f(f2bf(S[0][i]));
-                l1[i] = S[1][i] - bf2f(f2bf(S[1][i]));
-            }
-            sb[0][w][lane] = EL::from_acc(S[0], S[1]).u;
-            sb[1][w][lane] = EL::from_acc(l0, l1).u;
+            const float s8[8] = {S[0][0], S[0][1], S[0][2], S[0][3], S[1][0], S[1][1], S[1][2], S[1][3]};
+            uint4 hi, lo;
+            split8(s8, hi, lo);
+            sb[0][w][lane] = hi;
+            sb[1][w][lane] = lo;
         }
         lds_barrier();
         float* sl = sloc + u * kFD * kFD;
+        const float* ph = phi + u * kFD * kFD;
         f32x4 acc[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int ct = 2 * w + j;
+            const int row = 32 * w + 16 * j;            // output key rows row + 4g + i (acc), row + r (A)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[j][i] = sl[(16 * ct + 4 * g + i) * kFD + col];
+            for (int i = 0; i < 4; ++i) acc[j][i] = sl[(row + 4 * g + i) * kFD + col];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                const Frag ah = phi_frag(u, 0, ct, kb), al = phi_frag(u, 1, ct, kb);
+                const float4 a0 = *reinterpret_cast<const float4*>(ph + (row + r) * kFD + 32 * kb + 4 * g);
+                const float4 a1 = *reinterpret_cast<const float4*>(ph + (row + r) * kFD + 32 * kb + 16 + 4 * g);
+                const float f8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+                Frag ah, al;
+                split8(f8, ah.u, al.u);
+                mfma_ready(ah.u, al.u);
                 const Frag bh{sb[0][kb][lane]}, bl{sb[1][kb][lane]};
-                acc[j] = EL::mma(ah, bh, acc[j]);
-                acc[j] = EL::mma(ah, bl, acc[j]);
                 acc[j] = EL::mma(al, bh, acc[j]);
+                acc[j] = EL::mma(ah, bl, acc[j]);
+                acc[j] = EL::mma(ah, bh, acc[j]);
             }
         }
         lds_barrier();
@@ -693,7 +851,7 @@ __global__ __launch_bounds__(kCombThreads) void kda_fused_combine_kernel(
         for (int j = 0; j < 2; ++j) {
             S[j] = acc[j];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sl[(16 * (2 * w + j) + 4 * g + i) * kFD + col] = acc[j][i];
+            for (int i = 0; i < 4; ++i) sl[(32 * w + 16 * j + 4 * g + i) * kFD + col] = acc[j][i];
         }
     }
 }
@@ -711,7 +869,7 @@ FusedPlan plan_with(int64_t chunks, int32_t N, int32_t H, int64_t lseg)
     p.max_segs = p.lseg ? int((chunks + p.lseg - 1) / p.lseg + N) : N;
     p.table_bytes = (p.lseg && N > 64) ? ((size_t(N) + 1) * 4 + 255) & ~size_t(255) : 0;
     p.sloc_bytes = p.lseg ? size_t(p.max_segs) * H * kFD * kFD * 4 : 0;
-    p.phi_bytes = p.lseg ? size_t(p.max_segs) * H * kFD * kFD * 4 : 0;   // hi + lo bf16
+    p.phi_bytes = p.lseg ? size_t(p.max_segs) * H * kFD * kFD * 4 : 0;
     return p;
 }
 
@@ -735,7 +893,7 @@ FusedPlan fused_plan(int64_t T, int32_t N, int32_t H, size_t cap)
 
 template <int PASS, bool NORM>
 hipError_t launch_pass(const LaunchArgs& a, const int32_t* seg_off, const FusedPlan& p, const float* carry,
-                       float* sloc, uint16_t* phi)
+                       float* sloc, float* phi)
 {
     const int units = (p.lseg ? p.max_segs : a.num_seqs) * a.num_heads;
     const int blocks = ((units + 7) / 8) * 8;
@@ -750,7 +908,7 @@ hipError_t launch_pass(const LaunchArgs& a, const int32_t* seg_off, const FusedP
 
 template <bool NORM>
 hipError_t launch_fused_norm(const LaunchArgs& a, const int32_t* seg_off, const FusedPlan& p, float* sloc,
-                             uint16_t* phi, TimingHook* th)
+                             float* phi, TimingHook* th)
 {
     hipError_t e;
     if (p.lseg == 0) {
@@ -795,7 +953,7 @@ hipError_t launch_forward_fused(const LaunchArgs& a, void* workspace, TimingHook
     char* base = static_cast<char*>(workspace);
     int32_t* seg_off = p.table_bytes ? reinterpret_cast<int32_t*>(base) : nullptr;
     float* sloc = p.lseg ? reinterpret_cast<float*>(base + p.table_bytes) : nullptr;
-    uint16_t* phi = p.lseg ? reinterpret_cast<uint16_t*>(base + p.table_bytes + p.sloc_bytes) : nullptr;
+    float* phi = p.lseg ? reinterpret_cast<float*>(base + p.table_bytes + p.sloc_bytes) : nullptr;
     if (seg_off) {
         if (th) th->begin("plan", a.stream);
         hipLaunchKernelGGL(kda_fused_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, seg_off,

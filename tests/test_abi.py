@@ -303,9 +303,9 @@ def test_workspace_bytes(lib, monkeypatch):
              (189272, 1, 16, 128, 128), (5000, 1, 2, 128, 128), (100000, 100, 2, 128, 128), (4000, 600, 1, 128, 128)]
     for fused, T, N, H, dk, dv in [(False,) + c for c in cases] + [(True,) + c for c in cases]:
         if fused:
-            monkeypatch.setenv("KDA_SCAN_VARIANT", "fused")
+            monkeypatch.delenv("KDA_SCAN_VARIANT", raising=False)     # the default
         else:
-            monkeypatch.delenv("KDA_SCAN_VARIANT", raising=False)
+            monkeypatch.setenv("KDA_SCAN_VARIANT", "wy")
         if dk == 128 and dv == 128 and fused:
             # fused scan (32-token chunks): nothing unless the (sample, head) units are fewer than
             # 512; then segments of lseg chunks, each (segment, head) with an fp32 local state and

@@ -125,11 +125,11 @@ def test_config4_all_heads():
     _check(inputs.config(4))
 
 
-@pytest.mark.parametrize("variant", ["sequential", "fused"])
+@pytest.mark.parametrize("variant", ["sequential", "wy"])
 @pytest.mark.parametrize("case", ["packed8", "ragged_d64", "ragged_d128"])
 def test_selectable_variants(monkeypatch, variant, case):
-    # the single-kernel and fused bf16 scans stay selectable; they must meet the same bar
-    # (the fused scan covers d_k = d_v = 128; other sizes take the default scan)
+    # the single-kernel and two-kernel (WY) bf16 scans stay selectable; they must meet the
+    # same bar (the default for d_k = d_v = 128 is the fused scan, for other sizes the WY one)
     monkeypatch.setenv("KDA_SCAN_VARIANT", variant)
     if case == "packed8":
         _check(inputs.config(1), label=f"packed8 {variant}")
@@ -152,7 +152,7 @@ def test_fused_config0_and_config4_sampled_heads(monkeypatch):
 # fp32 data and for bf16 data when selected
 INIT = [(128, 128, "bf16", None), (64, 64, "bf16", None), (128, 64, "bf16", None),
         (128, 128, "f32", None), (64, 128, "f32", None), (128, 64, "bf16", "sequential"),
-        (128, 128, "bf16", "fused")]
+        (128, 128, "bf16", "wy")]
 
 
 @pytest.mark.parametrize("dk,dv,dt,variant", INIT, ids=[f"{a}x{b}_{c}_{d or 'default'}" for a, b, c, d in INIT])
@@ -183,6 +183,8 @@ NORM = [
     ("bf16_split", (5000,), 2, 128, 128, "bf16", None),
     ("bf16_fused", (129, 0, 64, 200, 1, 63), 3, 128, 128, "bf16", "fused"),
     ("bf16_fused_split", (5000,), 2, 128, 128, "bf16", "fused"),
+    ("bf16_wy", (129, 0, 64, 200, 1, 63), 3, 128, 128, "bf16", "wy"),
+    ("bf16_wy_split", (5000,), 2, 128, 128, "bf16", "wy"),
 ]
 
 
@@ -234,8 +236,8 @@ def test_split_scan_matches_one_pass():
         gu.compare(spec, out, f2.cpu().double().numpy(), o_ref, f_ref, label=f"split at {cut}")
 
 
-# The sequence split cuts a sample into segments when the chain would otherwise use at
-# most 64 workgroups: one pass gives each segment's transition and local state, a
+# The WY scan's sequence split cuts a sample into segments when the chain would otherwise
+# use at most 64 workgroups: one pass gives each segment's transition and local state, a
 # second pass scans every segment from its true initial state.
 SPLIT = [
     ("one_long", [5000], 2, 128, 128),            # 3 segments of 32 chunks
@@ -246,8 +248,9 @@ SPLIT = [
 
 
 @pytest.mark.parametrize("name,lens,H,dk,dv", SPLIT, ids=[c[0] for c in SPLIT])
-def test_sequence_split(name, lens, H, dk, dv):
+def test_sequence_split(monkeypatch, name, lens, H, dk, dv):
     from delta_rule_recurrent_kda_amd import kda
+    monkeypatch.setenv("KDA_SCAN_VARIANT", "wy")
     timing = {}
     for k in ("segments", "chain"):
         kda.timing_read(k)
@@ -300,9 +303,10 @@ def test_sequence_split_from_state():
     gu.compare(spec, out, fs, o_ref, f_ref, label="split from state")
 
 
-def test_kernel_timing_records_each_kernel():
+def test_kernel_timing_records_each_kernel(monkeypatch):
     import torch
     from delta_rule_recurrent_kda_amd import kda
+    monkeypatch.setenv("KDA_SCAN_VARIANT", "wy")
     spec = inputs.custom([300, 40], heads=2, d=128, seed=9)
     d = gu.device_inputs(spec, inputs.generate(spec))
     for name in ("plan", "prep", "chain", "scan"):
