@@ -85,10 +85,10 @@ struct Buf {
 };
 struct FusedSmem {
     Buf buf[2];
-    f32x4 part[4][6][64];  // per producer slab: partial A and P^T blocks
-    float ablk[2][16][16]; // the diagonal blocks of A (rows, fp32) for the inverses
+    f32x4 part[2][4][6][64];  // per chunk (two in flight) and producer slab: partial A and P^T blocks
+    float ablk[2][16][20]; // the diagonal blocks of A (rows, fp32, padded) for the inverses
     float ssq[2][4][kFC];  // sums of squares of q and k per (slab, token)
-    float dpp[4][kFC];     // q.k per (slab, token): the diagonal of P, from the raw rows
+    float dpp[2][4][kFC];  // per chunk (two in flight): q.k per (slab, token), the diagonal of P
 };
 
 __device__ __forceinline__ uint32_t bfbits_lo(uint32_t u) { return u << 16; }
@@ -243,6 +243,16 @@ __device__ __forceinline__ bool find_segment(int sid, const int32_t* cu, const i
     return true;
 }
 
+// a value that is the same in every lane, moved to scalar registers
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(x));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x) >> 32));
+    return int64_t((uint64_t(hi) << 32) | lo);
+}
+// buffer resource word 3 for raw (untyped) loads on gfx9-family parts; loads past the
+// resource's byte range return zeros
+constexpr int kBufFlags = 0x00020000;
+
 // key of row m of the consumers' key tile kt; value column c of half th of consumer j
 __device__ __forceinline__ int key_of(int kt, int m) { return 32 * (kt >> 1) + 8 * (m >> 2) + 4 * (kt & 1) + (m & 3); }
 __device__ __forceinline__ int col_of(int j, int th, int c) { return 32 * j + 8 * (c >> 2) + 4 * th + (c & 3); }
@@ -278,6 +288,11 @@ __global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(
     float* __restrict__ phi, int num_seqs, int H, int64_t T, int lseg, int max_segs)
 {
     constexpr bool kOut = PASS != 1;
+    // Who sums the partial products and inverts the diagonal blocks of I + A: with outputs,
+    // the consumers, at the start of the chunk's own iteration (their first interval has room
+    // next to the producers' decay work); without, the producers in their second interval
+    // (the consumers' second interval then carries the state and the transition).
+    constexpr bool kConsInv = PASS != 1;
 
     __shared__ FusedSmem sm;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -340,6 +355,76 @@ __global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(
             const int64_t t0 = s0 + int64_t(it) * kFC;
             f32x4 Z[2][2], ZP[PASS == 1 ? 2 : 1][PASS == 1 ? 2 : 1], O[2][2];
             if constexpr (NORM) lds_barrier();
+            if (kConsInv && run) {
+                // ---- chunk it's sums of the producers' partial products: the inverses of the two
+                //      diagonal blocks of I + A (waves 0, 1), -A10 (wave 2), P (wave 3) ----
+                Buf& bw = sm.buf[it & 1];
+                const f32x4(*part)[6][64] = sm.part[it & 1];
+                if (j < 2) {
+                    // A_jj = StrictLower(diag(b) Kh Kc^T) of diagonal block j, rows to LDS
+                    {
+                        f32x4 n = zero4();
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) n += part[x][j][lane];
+                        const float4 b4 = *reinterpret_cast<const float4*>(&bw.beta[16 * j + 4 * g]);
+                        const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sm.ablk[j][4 * g + i][r] = 4 * g + i > r ? bb[i] * n[i] : 0.f;
+                    }
+                    lds_wait();
+                    // T = (I + A_jj)^-1 in fp32 by elimination: lane (r, g) holds row r of A and
+                    // T[r][4g..4g+3]; for k = 0..14 row k is final and every row below it takes
+                    // -A[r][k] T[k][.], with T[k][.] broadcast along the lanes of the row (DPP)
+                    float ar[16];
+#pragma unroll
+                    for (int k4 = 0; k4 < 4; ++k4) {
+                        const float4 a4 = *reinterpret_cast<const float4*>(&sm.ablk[j][r][4 * k4]);
+                        ar[4 * k4] = a4.x;
+                        ar[4 * k4 + 1] = a4.y;
+                        ar[4 * k4 + 2] = a4.z;
+                        ar[4 * k4 + 3] = a4.w;
+                    }
+                    float t[4];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) t[m] = r == 4 * g + m ? 1.f : 0.f;
+                    elim_rows(t, ar, r, std::make_integer_sequence<int, 15>{});
+                    bw.tf[j][lane] = pack4(t[0], t[1], t[2], t[3]);     // A operand: T_jj[r][4g + i]
+                } else if (j == 2) {
+                    // A10 as the A operand: Acc((Kh1 Kc0^T)^T) holds (Kh1 Kc0^T)[r][4g + i], row r
+                    // of block (1, 0), scaled by beta of token 16 + r; negated for the solve
+                    f32x4 n = zero4();
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) n += part[x][2][lane];
+                    const float nbt = -bw.beta[16 + r];
+                    bw.tf[2][lane] = pack4(nbt * n[0], nbt * n[1], nbt * n[2], nbt * n[3]);
+                } else if (kOut) {
+                    f32x4 p00 = zero4(), p11 = zero4(), p10 = zero4();
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        p00 += part[x][3][lane];
+                        p11 += part[x][4][lane];
+                        p10 += part[x][5][lane];
+                    }
+                    float dg[2] = {0.f, 0.f};                           // the exact diagonal, tokens r, 16 + r
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        dg[0] += sm.dpp[it & 1][x][r];
+                        dg[1] += sm.dpp[it & 1][x][16 + r];
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {                       // P[r][4g + i], inclusive lower
+                        if (4 * g + i > r) {
+                            p00[i] = 0.f;
+                            p11[i] = 0.f;
+                        } else if (4 * g + i == r) {
+                            p00[i] = dg[0];
+                            p11[i] = dg[1];
+                        }
+                    }
+                    bw.pf[0][lane] = EL::from_acc(p00, zero4()).u;
+                    bw.pf[1][lane] = EL::from_acc(p10, p11).u;
+                }
+            }
             if (run) {
                 // ---- Z = diag(b) (V - Kh S); O = Qh S ----
 #pragma unroll
@@ -496,32 +581,47 @@ __global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(
 
     // ================= producer: slab p = w - 4 =================
     const int p = w - 4;
-    // Raw rows of chunk c (clamped to the segment's last chunk: a load past the end is issued
-    // all the same and never used; the segment has at least one chunk). Every step issues
-    // them without conditions, so that the waits for one chunk's rows never include the
-    // loads issued after them.
-    auto row_off = [&](int c, int tt) __attribute__((always_inline)) -> int64_t {
-        const int64_t t0 = s0 + int64_t(min(c, c1 - 1)) * kFC;
-        const int nrow = int(min<int64_t>(kFC, s1 - t0));
-        return t0 + min(16 * tt + r, nrow - 1);
+    // The sample's rows through buffer resources whose range ends with the sample: a row past
+    // its end (in the last chunk, or the prefetch after it) reads as zeros, so log a, k, q, v
+    // and beta are 0 there and no row needs a mask. Offsets in bytes from the sample's first
+    // token; the lane's part is fixed, the chunk's part (32 rows) is a scalar.
+    const int64_t us0 = uniform64(s0), us1 = uniform64(s1);
+    const uint32_t rowb = uint32_t(H) * kFD * 2;              // one token's row over all heads
+    const int nbytes = int(uint32_t(us1 - us0) * rowb);
+    const int64_t base = us0 * int64_t(H) * kFD;
+    const auto rsq = __builtin_amdgcn_make_buffer_rsrc((void*)(q + base), 0, nbytes, kBufFlags);
+    const auto rsk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + base), 0, nbytes, kBufFlags);
+    const auto rsv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + base), 0, nbytes, kBufFlags);
+    const auto rsl = __builtin_amdgcn_make_buffer_rsrc((void*)(la + base), 0, nbytes, kBufFlags);
+    const auto rsb = __builtin_amdgcn_make_buffer_rsrc((void*)(beta + us0 * H), 0,
+                                                       int(uint32_t(us1 - us0) * uint32_t(H) * 2), kBufFlags);
+    uint32_t voff[2], boff[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        voff[tt] = uint32_t(16 * tt + r) * rowb + uint32_t(h) * kFD * 2 + 2 * (32 * p + 8 * g);
+        boff[tt] = (uint32_t(16 * tt + r) * uint32_t(H) + uint32_t(h)) * 2;
+    }
+    auto ld16 = [&](__amdgpu_buffer_rsrc_t rs, uint32_t vo, int c) __attribute__((always_inline)) -> uint4 {
+        const u32x4v x = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, int(uint32_t(c) * kFC * rowb), 0);
+        return make_uint4(x[0], x[1], x[2], x[3]);
     };
+    // Every step issues its loads without conditions, so that the waits for one chunk's rows
+    // never include the loads issued after them.
     auto load_l = [&](Raw& x, int c) __attribute__((always_inline)) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-            x.l[tt] = *reinterpret_cast<const uint4*>(la + (row_off(c, tt) * H + h) * kFD + 32 * p + 8 * g);
+        for (int tt = 0; tt < 2; ++tt) x.l[tt] = ld16(rsl, voff[tt], c);
     };
     auto load_tile = [&](Raw& x, int c, int tt) __attribute__((always_inline)) {
-        const int64_t row = row_off(c, tt);
-        const int64_t o = (row * H + h) * kFD + 32 * p + 8 * g;
-        if constexpr (kOut) x.q[tt] = *reinterpret_cast<const uint4*>(q + o);
-        x.k[tt] = *reinterpret_cast<const uint4*>(k + o);
-        x.v[tt] = *reinterpret_cast<const uint4*>(v + o);
+        if constexpr (kOut) x.q[tt] = ld16(rsq, voff[tt], c);
+        x.k[tt] = ld16(rsk, voff[tt], c);
+        x.v[tt] = ld16(rsv, voff[tt], c);
     };
     // beta first in a step: the conversion of its 16 bits may be placed anywhere before the
     // next step, and then waits for these two loads only (the counter is in order)
     auto load_beta = [&](Raw& x, int c) __attribute__((always_inline)) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) x.b[tt] = beta[row_off(c, tt) * H + h];
+        for (int tt = 0; tt < 2; ++tt)
+            x.b[tt] = __builtin_amdgcn_raw_buffer_load_b16(rsb, boff[tt], int(uint32_t(c) * kFC * uint32_t(H) * 2), 0);
     };
 
     // Operands of chunk c from its raw rows `cur`; the rows of chunk c + 1 are loaded into
@@ -533,16 +633,12 @@ __global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(
         Raw cur = cur_in;
         pin_raw(cur);
         load_beta(nxt, c + 1);
-        const int64_t t0 = s0 + int64_t(c) * kFC;
-        const int nrow = int(min<int64_t>(kFC, s1 - t0));
-        // ---- E: decayed rows, partial products over the slab, transposes ----
-        bool rowok[2];
+        // ---- E: decayed rows; after the first barrier the partial products over the slab
+        //      and the transposes ----
         float bt[2], qs[2] = {1.f, 1.f}, ks[2] = {1.f, 1.f};
+        uint4 khF[2], kcH[2], qH[2];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            rowok[tt] = 16 * tt + r < nrow;
-            bt[tt] = rowok[tt] ? bf2f(cur.b[tt]) : 0.f;
-        }
+        for (int tt = 0; tt < 2; ++tt) bt[tt] = bf2f(cur.b[tt]);
         if constexpr (NORM) {
             // each row's sums of squares over the 128 channels: four lanes here and the
             // three other slabs' waves, summed in a fixed order
@@ -587,8 +683,7 @@ __global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    const uint2 lv = rowok[tt] ? half_of(cur.l[tt], t) : make_uint2(0u, 0u);
-                    lt[tt][t] = EL::from_acc16(EL::mma16(Frag16{lv}, ident, zero4()));
+                    lt[tt][t] = EL::from_acc16(EL::mma16(Frag16{half_of(cur.l[tt], t)}, ident, zero4()));
                 }
             mfma_ready(lt[0][0].u, lt[0][1].u, lt[1][0].u, lt[1][1].u);
             f32x4 G[2][2];
@@ -602,9 +697,8 @@ __global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(
                 bf.beta[r] = bt[0];
                 bf.beta[16 + r] = bt[1];
             }
-            // decayed rows (rows past the sample's end: beta is 0 there, so they reach no
-            // valid row through A, P, X or the state; log a is 0, so G and gamma stop there)
-            uint4 khF[2], kcH[2], qH[2];
+            // decayed rows (rows past the sample's end are zeros: they reach no valid row
+            // through A, P, X or the state, and G and gamma stop at the last valid row)
 #pragma unroll
             for (int pass_t = 0; pass_t < 2; ++pass_t) {
                 const int tt = 1 - pass_t;
@@ -642,7 +736,7 @@ __global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(
                     // q.k of the row over the slab (e^G e^-G = 1 on the diagonal of P)
                     dp += __shfl_xor(dp, 16);
                     dp += __shfl_xor(dp, 32);
-                    if (g == 0) sm.dpp[p][16 * tt + r] = dp;
+                    if (g == 0) sm.dpp[c & 1][p][16 * tt + r] = dp;
                     qH[tt] = pack8(fq);
                     bf.qf[tt][p][lane] = qH[tt];
                 } else {
@@ -652,8 +746,10 @@ __global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(
             }
             mfma_ready(khF[0], khF[1], kcH[0], kcH[1]);
             mfma_ready(qH[0], qH[1]);
+        }
+        auto partials = [&]() __attribute__((always_inline)) {
             // partial products over the slab: Acc(X) holds X[4g + i][r]
-            f32x4* pp = &sm.part[p][0][0];
+            f32x4* pp = &sm.part[c & 1][p][0][0];
             pp[0 * 64 + lane] = EL::mma(Frag{khF[0]}, Frag{kcH[0]}, zero4());   // Kh0 Kc0^T
             pp[1 * 64 + lane] = EL::mma(Frag{khF[1]}, Frag{kcH[1]}, zero4());   // Kh1 Kc1^T
             pp[2 * 64 + lane] = EL::mma(Frag{kcH[0]}, Frag{khF[1]}, zero4());   // (Kh1 Kc0^T)^T
@@ -673,74 +769,79 @@ __global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(
                 const f32x4 v1 = EL::mma16(Frag16{half_of(cur.v[1], t)}, ident, zero4());
                 bf.yv[p][t][lane] = EL::from_acc(v0, v1).u;
             }
-        }
+        };
+        if constexpr (!kConsInv) partials();
         lds_barrier();                                          // B1
-        // ---- sums of the partial products: the diagonal blocks' inverses (waves 4, 5), -A10
-        //      (wave 6), P (wave 7) ----
-        if (p < 2) {
-            // A_ii = StrictLower(diag(b) Kh Kc^T) of diagonal block ii = p, rows to LDS
-            const int ii = p;
-            {
+        if constexpr (kConsInv) {
+            partials();
+        } else {
+            // ---- sums of the partial products: the diagonal blocks' inverses (waves 4, 5),
+            //      -A10 (wave 6), P (wave 7) ----
+            if (p < 2) {
+                // A_ii = StrictLower(diag(b) Kh Kc^T) of diagonal block ii = p, rows to LDS
+                const int ii = p;
+                {
+                    f32x4 n = zero4();
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) n += sm.part[c & 1][x][ii][lane];
+                    const float4 b4 = *reinterpret_cast<const float4*>(&bf.beta[16 * ii + 4 * g]);
+                    const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sm.ablk[ii][4 * g + i][r] = 4 * g + i > r ? bb[i] * n[i] : 0.f;
+                }
+                lds_wait();
+                // T = (I + A_ii)^-1 in fp32 by elimination: lane (r, g) holds row r of A and
+                // T[r][4g..4g+3]; for k = 0..14 row k is final and every row below it takes
+                // -A[r][k] T[k][.], with T[k][.] broadcast along the lanes of the row (DPP)
+                float ar[16];
+#pragma unroll
+                for (int k4 = 0; k4 < 4; ++k4) {
+                    const float4 a4 = *reinterpret_cast<const float4*>(&sm.ablk[ii][r][4 * k4]);
+                    ar[4 * k4] = a4.x;
+                    ar[4 * k4 + 1] = a4.y;
+                    ar[4 * k4 + 2] = a4.z;
+                    ar[4 * k4 + 3] = a4.w;
+                }
+                float t[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) t[m] = r == 4 * g + m ? 1.f : 0.f;
+                elim_rows(t, ar, r, std::make_integer_sequence<int, 15>{});
+                bf.tf[ii][lane] = pack4(t[0], t[1], t[2], t[3]);     // A operand: T_ii[r][4g + i]
+            } else if (p == 2) {
+                // A10 as the A operand: Acc((Kh1 Kc0^T)^T) holds (Kh1 Kc0^T)[r][4g + i], row r of block
+                // (1, 0), scaled by beta of token 16 + r; negated for the solve
                 f32x4 n = zero4();
 #pragma unroll
-                for (int x = 0; x < 4; ++x) n += sm.part[x][ii][lane];
-                const float4 b4 = *reinterpret_cast<const float4*>(&bf.beta[16 * ii + 4 * g]);
-                const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+                for (int x = 0; x < 4; ++x) n += sm.part[c & 1][x][2][lane];
+                const float nbt = -bf.beta[16 + r];
+                bf.tf[2][lane] = pack4(nbt * n[0], nbt * n[1], nbt * n[2], nbt * n[3]);
+            } else if (kOut) {
+                f32x4 p00 = zero4(), p11 = zero4(), p10 = zero4();
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sm.ablk[ii][4 * g + i][r] = 4 * g + i > r ? bb[i] * n[i] : 0.f;
-            }
-            lds_wait();
-            // T = (I + A_ii)^-1 in fp32 by elimination: lane (r, g) holds row r of A and
-            // T[r][4g..4g+3]; for k = 0..14 row k is final and every row below it takes
-            // -A[r][k] T[k][.], with T[k][.] broadcast along the lanes of the row (DPP)
-            float ar[16];
-#pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4) {
-                const float4 a4 = *reinterpret_cast<const float4*>(&sm.ablk[ii][r][4 * k4]);
-                ar[4 * k4] = a4.x;
-                ar[4 * k4 + 1] = a4.y;
-                ar[4 * k4 + 2] = a4.z;
-                ar[4 * k4 + 3] = a4.w;
-            }
-            float t[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) t[m] = r == 4 * g + m ? 1.f : 0.f;
-            elim_rows(t, ar, r, std::make_integer_sequence<int, 15>{});
-            bf.tf[ii][lane] = pack4(t[0], t[1], t[2], t[3]);     // A operand: T_ii[r][4g + i]
-        } else if (p == 2) {
-            // A10 as the A operand: Acc((Kh1 Kc0^T)^T) holds (Kh1 Kc0^T)[r][4g + i], row r of block
-            // (1, 0), scaled by beta of token 16 + r; negated for the solve
-            f32x4 n = zero4();
-#pragma unroll
-            for (int x = 0; x < 4; ++x) n += sm.part[x][2][lane];
-            const float nbt = -bf.beta[16 + r];
-            bf.tf[2][lane] = pack4(nbt * n[0], nbt * n[1], nbt * n[2], nbt * n[3]);
-        } else if (kOut) {
-            f32x4 p00 = zero4(), p11 = zero4(), p10 = zero4();
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                p00 += sm.part[x][3][lane];
-                p11 += sm.part[x][4][lane];
-                p10 += sm.part[x][5][lane];
-            }
-            float dg[2] = {0.f, 0.f};                           // the exact diagonal, tokens r and 16 + r
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                dg[0] += sm.dpp[x][r];
-                dg[1] += sm.dpp[x][16 + r];
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {                       // P[r][4g + i], inclusive lower
-                if (4 * g + i > r) {
-                    p00[i] = 0.f;
-                    p11[i] = 0.f;
-                } else if (4 * g + i == r) {
-                    p00[i] = dg[0];
-                    p11[i] = dg[1];
+                for (int x = 0; x < 4; ++x) {
+                    p00 += sm.part[c & 1][x][3][lane];
+                    p11 += sm.part[c & 1][x][4][lane];
+                    p10 += sm.part[c & 1][x][5][lane];
                 }
+                float dg[2] = {0.f, 0.f};                           // the exact diagonal, tokens r and 16 + r
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    dg[0] += sm.dpp[c & 1][x][r];
+                    dg[1] += sm.dpp[c & 1][x][16 + r];
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {                       // P[r][4g + i], inclusive lower
+                    if (4 * g + i > r) {
+                        p00[i] = 0.f;
+                        p11[i] = 0.f;
+                    } else if (4 * g + i == r) {
+                        p00[i] = dg[0];
+                        p11[i] = dg[1];
+                    }
+                }
+                bf.pf[0][lane] = EL::from_acc(p00, zero4()).u;
+                bf.pf[1][lane] = EL::from_acc(p10, p11).u;
             }
-            bf.pf[0][lane] = EL::from_acc(p00, zero4()).u;
-            bf.pf[1][lane] = EL::from_acc(p10, p11).u;
         }
         lds_barrier();                                          // B2
     };
