@@ -61,7 +61,7 @@ CONV_BWD_KERNELS = {"conv_bwd_plan": "kda_conv_plan_kernel", "conv_dx": "kda_sho
 CONV_TAPS = (4, 3, 3, 3)        # text taps; visual frames x rows x columns
 WORKLOADS = {"tiny": 0, "packed8": 1, "image4": 2, "clip5s": 3, "clip30s": 4}
 CHUNK = 64
-KERNEL_SYMBOL = {"fused": "kda_fused_kernel", "fused_sum": "kda_fused_kernel",
+KERNEL_SYMBOL = {"fused": "kda_fused_kernel (output pass)", "fused_sum": "kda_fused_kernel (summary pass)",
                  "fused_combine": "kda_fused_combine_kernel", "plan": "kda_fused_plan_kernel",
                  "prep": "kda_wy_prep_kernel", "chain": "kda_wy_chain_kernel",
                  "segments": "kda_wy_chain_kernel", "scan": "kda_fwd"}
@@ -241,7 +241,8 @@ def chunk_flops(spec) -> int:
 
 
 def traffic_for(workload: str, kernel: str, sha: str = None):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel is unchanged."""
+    """HBM bytes per launch of one kernel (by its timing name) from committed rocprofv3
+    counter runs, if the kernel sources are unchanged since."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -727,14 +728,14 @@ def main():
 
     bytes_ = algorithmic_bytes(spec)
     flops = chunk_flops(spec)
-    # the path's algorithmic bytes over the dominant kernel's mean launch time (its launches
-    # per step share them when it runs several times per step)
-    dom_bytes = bytes_ / kernels[dom]["launches_per_step"]
+    # the dominant kernel's own algorithmic bytes per launch (what its launch must read and
+    # write at the least, from the same per-head-token figures) over its mean launch time
+    dom_bytes = kernels[dom].get("algorithmic_bytes", bytes_ / kernels[dom]["launches_per_step"])
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     path_gbs = bytes_ / (ms_per_step * 1e-3) / 1e9
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if spec.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
-    traffic = traffic_for(args.workload, KERNEL_SYMBOL[dom])
+    traffic = traffic_for(args.workload, dom)
 
     rec = {
         "metric": "KDA fwd tokens/s (B·L·H) at dk=dv=128; % MFMA peak and % HBM BW, 1 MI355X",
@@ -755,8 +756,10 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "traffic_ratio": None if traffic is None else traffic / dom_bytes,
                      "kernel": KERNEL_SYMBOL[dom], "kernel_ms_avg": dom_ms, "algorithmic_bytes": dom_bytes,
-                     "algorithmic_bytes_note": "1,282 B per head-token (q, k, v, log a, beta read once, out "
-                                               "written once; bf16, d = 128) plus the fp32 final states",
+                     "algorithmic_bytes_note": "the dominant kernel's own bytes: per head-token it covers, "
+                                               "256 B each of q, k, v, log a read, 2 B of beta, 256 B of out "
+                                               "written (those of its pass), plus its state traffic; the path "
+                                               "as a whole is 1,282 B per head-token (see path)",
                      "kernel_sha": kernel_sha()},
         "kernels": kernels,
         "path": {"algorithmic_bytes": bytes_, "achieved_GBs": path_gbs, "frac_hbm": path_gbs / HBM_PEAK_GBS},
