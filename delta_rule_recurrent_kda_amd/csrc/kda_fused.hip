@@ -54,6 +54,8 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
+#include <type_traits>
 #include <utility>
 
 #include "kda_device.h"
@@ -70,6 +72,7 @@ constexpr int kFC = 32;            // tokens per chunk
 constexpr int kFD = 128;           // d_k = d_v
 constexpr int kFThreads = 512;     // 4 consumer + 4 producer wave64
 constexpr uint16_t kOneBf = 0x3F80;
+constexpr int kFCounters = 4;      // unit counters of the persistent passes (one per pass)
 constexpr int kCombThreads = 256;  // combine: 4 wave64 per (sample, head, 16 value columns)
 
 // one chunk's operands for the state pass, every array in lane order
@@ -184,10 +187,12 @@ __device__ __forceinline__ int seg_count(const int32_t* cu, int n, int64_t T, in
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void kda_fused_plan_kernel(const int32_t* __restrict__ cu,
                                                               int32_t* __restrict__ seg_off, int num_seqs,
-                                                              int64_t T, int lseg)
+                                                              int64_t T, int lseg, int* __restrict__ counters)
 {
     __shared__ int32_t part[1024];
     const int tid = threadIdx.x;
+    if (tid < kFCounters) counters[tid] = 0;        // the passes' unit counters
+    if (seg_off == nullptr) return;
     int32_t carry = 0;
     for (int base = 0; base < num_seqs; base += 1024) {
         const int n = base + tid;
@@ -279,13 +284,13 @@ __device__ __forceinline__ void pin_raw(Raw& x) {
 // PASS 0: one segment per sample, outputs. PASS 1: segment summaries (S_loc, Phi), no
 // output. PASS 2: segments from their entry state, outputs.
 // ---------------------------------------------------------------------------
-template <int PASS, bool NORM>
-__global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ la, const uint16_t* __restrict__ beta, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ seg_off, const float* __restrict__ init_state, const float* __restrict__ carry,
-    uint16_t* __restrict__ out, float* __restrict__ final_state, float* __restrict__ sloc,
-    float* __restrict__ phi, int num_seqs, int H, int64_t T, int lseg, int max_segs)
+template <int PASS, bool NORM, bool CONSUMER>
+__device__ __forceinline__ void fused_unit(
+    FusedSmem& sm, const int lin, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ la, const uint16_t* __restrict__ beta,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ seg_off, const float* __restrict__ init_state,
+    const float* __restrict__ carry, uint16_t* __restrict__ out, float* __restrict__ final_state,
+    float* __restrict__ sloc, float* __restrict__ phi, int num_seqs, int H, int64_t T, int lseg, int max_segs)
 {
     constexpr bool kOut = PASS != 1;
     // Who sums the partial products and inverts the diagonal blocks of I + A: with outputs,
@@ -294,24 +299,22 @@ __global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(
     // (the consumers' second interval then carries the state and the transition).
     constexpr bool kConsInv = PASS != 1;
 
-    __shared__ FusedSmem sm;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: role and slab in SGPRs
     const int r = lane & 15, g = lane >> 4;
 
-    // block -> (segment, head): consecutive ids on one XCD, so the heads of a segment
-    // share their XCD's L2 for beta's rows
-    const int nb = gridDim.x;                   // a multiple of 8
-    const int lin = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
+    // unit -> (segment, head): the heads of a segment are consecutive units
     const int sid = lin / H, h = lin % H;
     Seg sg;
     if (!find_segment(sid, cu, seg_off, num_seqs, T, lseg, max_segs, lane, sg)) return;
     if (PASS == 1 && sg.seg == sg.nseg - 1) return;          // the last segment needs no summary
     int64_t s0, s1;
     bounds(cu, sg.n, T, s0, s1);
+    // the chunk range is the same on every lane: in scalar registers, the chunk's part of a
+    // load's offset is a scalar operand (a per-lane one makes the compiler loop over lanes)
     const int nch = int((s1 - s0 + kFC - 1) / kFC);
-    const int c0 = lseg > 0 ? min(sg.seg * lseg, nch) : 0;
-    const int c1 = lseg > 0 ? min(c0 + lseg, nch) : nch;
+    const int c0 = __builtin_amdgcn_readfirstlane(lseg > 0 ? min(sg.seg * lseg, nch) : 0);
+    const int c1 = __builtin_amdgcn_readfirstlane(lseg > 0 ? min(c0 + lseg, nch) : nch);
 
     // constant fragments: identity, inclusive lower triangle (k <= column), all ones
     Frag16 ident, tri, ones;
@@ -327,7 +330,7 @@ __global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(
         ones.u = make_uint2(kOneBf | (uint32_t(kOneBf) << 16), kOneBf | (uint32_t(kOneBf) << 16));
     }
 
-    if (w < 4) {
+    if constexpr (CONSUMER) {
         // ================= consumer: value columns of consumer j = w =================
         const int j = w;
         // S[kt][th]: rows key_of(kt, 4g + i), column col_of(j, th, r). PASS 1 also carries
@@ -485,8 +488,13 @@ __global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(
                     }
                 }
             }
-            lds_barrier();                                      // B1
-            if (run) {
+            // The summary pass's block inverses are ready when its chunk starts (the producers
+            // formed them after the previous chunk's first barrier), so it solves before the first
+            // barrier and updates S and Phi after it; the output pass forms its inverses here and
+            // solves after the barrier.
+            constexpr bool kEarly = PASS == 1;
+            Frag xf[2], xpf[PASS == 1 ? 2 : 1];
+            auto solve_out = [&]() __attribute__((always_inline)) {
                 // ---- X = T Z by 16-row blocks: X0 = T00 Z0, X1 = T11 (Z1 - A10 X0) ----
                 const Frag16 t00{bf.tf[0][lane]}, t11{bf.tf[1][lane]}, na10{bf.tf[2][lane]};
                 auto solve = [&](const f32x4 (&z)[2][2], int th, f32x4& x0, f32x4& x1) __attribute__((always_inline)) {
@@ -500,7 +508,6 @@ __global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(
                     mfma_ready(zf1.u);
                     x1 = EL::mma16(t11, zf1, zero4());
                 };
-                Frag xf[2], xpf[PASS == 1 ? 2 : 1];
 #pragma unroll
                 for (int th = 0; th < 2; ++th) {
                     f32x4 x0, x1;
@@ -528,28 +535,45 @@ __global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(
                                            pack2(O[ja][1][0], O[ja][1][1]), pack2(O[ja][1][2], O[ja][1][3]));
                     }
                 }
+            };
+            auto update_state = [&]() __attribute__((always_inline)) {
                 // ---- S <- diag(gamma) S + Kb^T X = diag(gamma) (S + Kc^T X) ----
 #pragma unroll
                 for (int kt = 0; kt < 8; ++kt) {
                     const Frag ka{bf.kf[kt][lane]};
-#pragma unroll
-                    for (int th = 0; th < 2; ++th) {
-                        S[kt][th] = EL::mma(ka, xf[th], S[kt][th]);
-                        if constexpr (PASS == 1) Ph[kt][th] = EL::mma(ka, xpf[th], Ph[kt][th]);
-                    }
-                }
-#pragma unroll
-                for (int kt = 0; kt < 8; ++kt) {
                     const float4 g4 = *reinterpret_cast<const float4*>(&bf.gam[key_of(kt, 4 * g)]);
 #pragma unroll
                     for (int th = 0; th < 2; ++th) {
+                        S[kt][th] = EL::mma(ka, xf[th], S[kt][th]);
                         S[kt][th] = f32x4{S[kt][th][0] * g4.x, S[kt][th][1] * g4.y, S[kt][th][2] * g4.z,
                                           S[kt][th][3] * g4.w};
-                        if constexpr (PASS == 1)
-                            Ph[kt][th] = f32x4{Ph[kt][th][0] * g4.x, Ph[kt][th][1] * g4.y, Ph[kt][th][2] * g4.z,
-                                               Ph[kt][th][3] * g4.w};
                     }
                 }
+            };
+            // ---- Phi <- diag(gamma) (Phi + Kc^T Xp), Xp the solve with Phi in place of V - Kh S ----
+            auto update_phi = [&]() __attribute__((always_inline)) {
+                if constexpr (PASS == 1) {
+#pragma unroll
+                    for (int kt = 0; kt < 8; ++kt) {
+                        const Frag ka{bf.kf[kt][lane]};
+                        const float4 g4 = *reinterpret_cast<const float4*>(&bf.gam[key_of(kt, 4 * g)]);
+#pragma unroll
+                        for (int th = 0; th < 2; ++th) {
+                            Ph[kt][th] = EL::mma(ka, xpf[th], Ph[kt][th]);
+                            Ph[kt][th] = f32x4{Ph[kt][th][0] * g4.x, Ph[kt][th][1] * g4.y, Ph[kt][th][2] * g4.z,
+                                               Ph[kt][th][3] * g4.w};
+                        }
+                    }
+                }
+            };
+            if constexpr (kEarly) {
+                if (run) solve_out();
+            }
+            lds_barrier();                                      // B1
+            if (run) {
+                if constexpr (!kEarly) solve_out();
+                update_state();
+                update_phi();
             }
             lds_barrier();                                      // B2
         }
@@ -577,7 +601,7 @@ __global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(
                     for (int i = 0; i < 4; ++i) dst[key_of(kt, 4 * g + i) * kFD + col_of(j, th, r)] = S[kt][th][i];
         }
         return;
-    }
+    } else {
 
     // ================= producer: slab p = w - 4 =================
     const int p = w - 4;
@@ -633,6 +657,9 @@ __global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(
         Raw cur = cur_in;
         pin_raw(cur);
         load_beta(nxt, c + 1);
+        load_l(nxt, c + 1);
+        load_tile(nxt, c + 1, 1);
+        load_tile(nxt, c + 1, 0);
         // ---- E: decayed rows; after the first barrier the partial products over the slab
         //      and the transposes ----
         float bt[2], qs[2] = {1.f, 1.f}, ks[2] = {1.f, 1.f};
@@ -674,80 +701,76 @@ __global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(
                 ks[tt] = tk > 0.f ? 1.f / sqrtf(tk) : 0.f;
             }
         }
+        // G over the chunk: the half-slab tiles of log a transposed (product with the identity),
+        // then a product with the inclusive triangle, tile 1 plus tile 0's sum; lane (r, g) gets
+        // G[16tt + r][8g + 4t + i], the layout of its raw rows
+        f32x4 G[2][2];
         {
-            // G over the chunk: the half-slab tiles of log a transposed (product with the
-            // identity), then a product with the inclusive triangle, tile 1 plus tile 0's sum;
-            // lane (r, g) gets G[16tt + r][8g + 4t + i], the layout of its raw rows
             Frag16 lt[2][2];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
+                for (int t = 0; t < 2; ++t)
                     lt[tt][t] = EL::from_acc16(EL::mma16(Frag16{half_of(cur.l[tt], t)}, ident, zero4()));
-                }
             mfma_ready(lt[0][0].u, lt[0][1].u, lt[1][0].u, lt[1][1].u);
-            f32x4 G[2][2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 G[0][t] = EL::mma16(lt[0][t], tri, zero4());
                 G[1][t] = EL::mma16(lt[0][t], ones, EL::mma16(lt[1][t], tri, zero4()));
             }
-            load_l(nxt, c + 1);
-            if (p == 0 && g == 0) {
-                bf.beta[r] = bt[0];
-                bf.beta[16 + r] = bt[1];
+        }
+        if (p == 0 && g == 0) {
+            bf.beta[r] = bt[0];
+            bf.beta[16 + r] = bt[1];
+        }
+        // decayed rows of token tile tt (rows past the sample's end are zeros: they reach no
+        // valid row through A, P, X or the state, and G and gamma stop at the last valid row);
+        // the tile's next rows are loaded as its registers fall free
+        auto tile_pass = [&](const int tt) __attribute__((always_inline)) {
+            float kf[8], qf[8];
+            unpack8(cur.k[tt], kf);
+            if constexpr (kOut) unpack8(cur.q[tt], qf);
+            float ex[8], ei[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float G2 = G[tt][e >> 2][e & 3] * kLog2e;
+                ex[e] = fast_exp2(G2);
+                ei[e] = fast_exp2(-G2);
             }
-            // decayed rows (rows past the sample's end are zeros: they reach no valid row
-            // through A, P, X or the state, and G and gamma stop at the last valid row)
-#pragma unroll
-            for (int pass_t = 0; pass_t < 2; ++pass_t) {
-                const int tt = 1 - pass_t;
-                float kf[8], qf[8];
-                unpack8(cur.k[tt], kf);
-                if constexpr (kOut) unpack8(cur.q[tt], qf);
-                float ex[8], ei[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float G2 = G[tt][e >> 2][e & 3] * kLog2e;
-                    ex[e] = fast_exp2(G2);
-                    ei[e] = fast_exp2(-G2);
-                }
-                // gamma = e^G of token 31, held by the lanes of row 15 of tile 1
-                if (tt == 1 && r == 15) {
-                    *reinterpret_cast<float4*>(&bf.gam[32 * p + 8 * g]) = make_float4(ex[0], ex[1], ex[2], ex[3]);
-                    *reinterpret_cast<float4*>(&bf.gam[32 * p + 8 * g + 4]) = make_float4(ex[4], ex[5], ex[6], ex[7]);
-                }
-                float fkh[8], fkc[8], fq[8];
-                float dp = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float kx = NORM ? kf[e] * ks[tt] : kf[e];
-                    const float qx = kOut ? (NORM ? qf[e] * qs[tt] : qf[e]) : 0.f;
-                    fkh[e] = kx * ex[e];
-                    fkc[e] = kx * ei[e];
-                    fq[e] = qx * ex[e];
-                    dp += kx * qx;
-                }
-                khF[tt] = pack8(fkh);
-                kcH[tt] = pack8(fkc);
-                bf.yk[tt][p][lane] = make_uint4(khF[tt].x ^ 0x80008000u, khF[tt].y ^ 0x80008000u,
-                                                khF[tt].z ^ 0x80008000u, khF[tt].w ^ 0x80008000u);
-                if constexpr (kOut) {
-                    // q.k of the row over the slab (e^G e^-G = 1 on the diagonal of P)
-                    dp += __shfl_xor(dp, 16);
-                    dp += __shfl_xor(dp, 32);
-                    if (g == 0) sm.dpp[c & 1][p][16 * tt + r] = dp;
-                    qH[tt] = pack8(fq);
-                    bf.qf[tt][p][lane] = qH[tt];
-                } else {
-                    qH[tt] = make_uint4(0u, 0u, 0u, 0u);
-                }
-                load_tile(nxt, c + 1, tt);
+            // gamma = e^G of token 31, held by the lanes of row 15 of tile 1
+            if (tt == 1 && r == 15) {
+                *reinterpret_cast<float4*>(&bf.gam[32 * p + 8 * g]) = make_float4(ex[0], ex[1], ex[2], ex[3]);
+                *reinterpret_cast<float4*>(&bf.gam[32 * p + 8 * g + 4]) = make_float4(ex[4], ex[5], ex[6], ex[7]);
             }
+            float fkh[8], fkc[8], fq[8];
+            float dp = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float kx = NORM ? kf[e] * ks[tt] : kf[e];
+                const float qx = kOut ? (NORM ? qf[e] * qs[tt] : qf[e]) : 0.f;
+                fkh[e] = kx * ex[e];
+                fkc[e] = kx * ei[e];
+                fq[e] = qx * ex[e];
+                dp += kx * qx;
+            }
+            khF[tt] = pack8(fkh);
+            kcH[tt] = pack8(fkc);
+            bf.yk[tt][p][lane] = make_uint4(khF[tt].x ^ 0x80008000u, khF[tt].y ^ 0x80008000u,
+                                            khF[tt].z ^ 0x80008000u, khF[tt].w ^ 0x80008000u);
+            if constexpr (kOut) {
+                // q.k of the row over the slab (e^G e^-G = 1 on the diagonal of P)
+                dp += __shfl_xor(dp, 16);
+                dp += __shfl_xor(dp, 32);
+                if (g == 0) sm.dpp[c & 1][p][16 * tt + r] = dp;
+                qH[tt] = pack8(fq);
+                bf.qf[tt][p][lane] = qH[tt];
+            } else {
+                qH[tt] = make_uint4(0u, 0u, 0u, 0u);
+            }
+        };
+        auto partials = [&]() __attribute__((always_inline)) {
             mfma_ready(khF[0], khF[1], kcH[0], kcH[1]);
             mfma_ready(qH[0], qH[1]);
-        }
-        auto partials = [&]() __attribute__((always_inline)) {
             // partial products over the slab: Acc(X) holds X[4g + i][r]
             f32x4* pp = &sm.part[c & 1][p][0][0];
             pp[0 * 64 + lane] = EL::mma(Frag{khF[0]}, Frag{kcH[0]}, zero4());   // Kh0 Kc0^T
@@ -770,9 +793,17 @@ __global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(
                 bf.yv[p][t][lane] = EL::from_acc(v0, v1).u;
             }
         };
-        if constexpr (!kConsInv) partials();
+        // The output pass splits its decay work at the first barrier (the consumers' second
+        // interval is the longer one there); the summary pass does all of it first and its
+        // inverses after the barrier.
+        tile_pass(1);
+        if constexpr (!kConsInv) {
+            tile_pass(0);
+            partials();
+        }
         lds_barrier();                                          // B1
         if constexpr (kConsInv) {
+            tile_pass(0);
             partials();
         } else {
             // ---- sums of the partial products: the diagonal blocks' inverses (waves 4, 5),
@@ -865,6 +896,53 @@ __global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(
     if constexpr (NORM) lds_barrier();
     lds_barrier();
     lds_barrier();
+    }
+}
+
+struct FusedArgs {
+    const uint16_t *q, *k, *v, *la, *beta;
+    const int32_t *cu, *seg_off;
+    const float *init_state, *carry;
+    uint16_t* out;
+    float *final_state, *sloc, *phi;
+    int* counter;          // next unit; starts at zero
+    int64_t T;
+    int num_seqs, H, lseg, max_segs, units;
+};
+using KernArgs = const __attribute__((address_space(4))) FusedArgs*;
+
+// A persistent grid, one workgroup per CU: each workgroup takes the next unit from a counter
+// in memory until none is left, so units run wherever a CU is free (a grid of two or more
+// workgroups per CU leaves some CUs idle while others run a third unit, since the dispatcher
+// does not place workgroups on whichever CU finished first).
+template <int PASS, bool NORM>
+__global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(const FusedArgs args)
+{
+    __shared__ FusedSmem sm;
+    __shared__ int next_unit;
+    // each role in a loop of its own (the same barriers per unit), so that neither keeps the
+    // other's values live
+    auto run = [&](auto role) __attribute__((always_inline)) {
+        for (;;) {
+            // the arguments are loaded again for every unit, through a pointer the compiler cannot
+            // follow across iterations: kept in scalar registers over the loop they would crowd
+            // out the unit's own
+            uint64_t kp = reinterpret_cast<uint64_t>(__builtin_amdgcn_kernarg_segment_ptr());
+            asm volatile("" : "+s"(kp));
+            const KernArgs ap = reinterpret_cast<KernArgs>(kp);
+            if (threadIdx.x == 0) next_unit = atomicAdd(ap->counter, 1);
+            lds_barrier();
+            const int lin = __builtin_amdgcn_readfirstlane(next_unit);
+            lds_barrier();                              // every wave has read it before the next
+            if (lin >= ap->units) break;
+            fused_unit<PASS, NORM, decltype(role)::value>(sm, lin, ap->q, ap->k, ap->v, ap->la, ap->beta, ap->cu,
+                                                          ap->seg_off, ap->init_state, ap->carry, ap->out,
+                                                          ap->final_state, ap->sloc, ap->phi, ap->num_seqs, ap->H,
+                                                          ap->T, ap->lseg, ap->max_segs);
+        }
+    };
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4) run(std::true_type{});   // waves 0-3
+    else run(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------
@@ -961,6 +1039,8 @@ struct FusedPlan {
     int lseg;          // chunks (32 tokens) per segment; 0 = one segment per sample
     int max_segs;
     size_t table_bytes, sloc_bytes, phi_bytes;
+    size_t total() const { return kCounterBytes + table_bytes + sloc_bytes + phi_bytes; }
+    static constexpr size_t kCounterBytes = 256;
 };
 
 FusedPlan plan_with(int64_t chunks, int32_t N, int32_t H, int64_t lseg)
@@ -984,42 +1064,76 @@ FusedPlan fused_plan(int64_t T, int32_t N, int32_t H, size_t cap)
     const int64_t chunks = (T + kFC - 1) / kFC + N;         // upper bound over all samples
     int64_t lseg = units < 512 ? std::max<int64_t>(16, (chunks * H + 511) / 512) : 0;
     FusedPlan p = plan_with(chunks, N, H, lseg);
-    if (p.table_bytes + p.sloc_bytes + p.phi_bytes <= cap) return p;
+    if (p.total() <= cap) return p;
     const size_t slot = size_t(2) * kFD * kFD * 4 * size_t(H);          // one segment's summaries, all heads
-    const size_t avail = cap > p.table_bytes ? cap - p.table_bytes : 0;
+    const size_t fixed = FusedPlan::kCounterBytes + p.table_bytes;
+    const size_t avail = cap > fixed ? cap - fixed : 0;
     const int64_t max_segs = int64_t(avail / slot);
     lseg = max_segs > N ? std::max<int64_t>(lseg, (chunks + (max_segs - N) - 1) / (max_segs - N)) : 0;
     return plan_with(chunks, N, H, lseg);
 }
 
+// CUs of the current device (cached per device)
+hipError_t device_cus(int& n)
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64 && (n = cache[dev].load(std::memory_order_relaxed)) > 0) return hipSuccess;
+    if ((e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if (n <= 0) return hipErrorInvalidDevice;
+    if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return hipSuccess;
+}
+
 template <int PASS, bool NORM>
 hipError_t launch_pass(const LaunchArgs& a, const int32_t* seg_off, const FusedPlan& p, const float* carry,
-                       float* sloc, float* phi)
+                       float* sloc, float* phi, int* counter)
 {
     const int units = (p.lseg ? p.max_segs : a.num_seqs) * a.num_heads;
-    const int blocks = ((units + 7) / 8) * 8;
-    hipLaunchKernelGGL((kda_fused_kernel<PASS, NORM>), dim3(blocks), dim3(kFThreads), 0, a.stream,
-                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.log_alpha),
-                       static_cast<const uint16_t*>(a.beta), a.cu_seqlens, seg_off, a.init_state, carry,
-                       static_cast<uint16_t*>(a.out), a.final_state, sloc, phi, a.num_seqs, a.num_heads,
-                       a.total_tokens, p.lseg, p.max_segs);
+    int cus = 0;
+    const hipError_t e = device_cus(cus);
+    if (e != hipSuccess) return e;
+    const int blocks = std::min(units, cus);
+    FusedArgs fa{};
+    fa.q = static_cast<const uint16_t*>(a.q);
+    fa.k = static_cast<const uint16_t*>(a.k);
+    fa.v = static_cast<const uint16_t*>(a.v);
+    fa.la = static_cast<const uint16_t*>(a.log_alpha);
+    fa.beta = static_cast<const uint16_t*>(a.beta);
+    fa.cu = a.cu_seqlens;
+    fa.seg_off = seg_off;
+    fa.init_state = a.init_state;
+    fa.carry = carry;
+    fa.out = static_cast<uint16_t*>(a.out);
+    fa.final_state = a.final_state;
+    fa.sloc = sloc;
+    fa.phi = phi;
+    fa.counter = counter;
+    fa.T = a.total_tokens;
+    fa.num_seqs = a.num_seqs;
+    fa.H = a.num_heads;
+    fa.lseg = p.lseg;
+    fa.max_segs = p.max_segs;
+    fa.units = units;
+    hipLaunchKernelGGL((kda_fused_kernel<PASS, NORM>), dim3(blocks), dim3(kFThreads), 0, a.stream, fa);
     return hipGetLastError();
 }
 
 template <bool NORM>
 hipError_t launch_fused_norm(const LaunchArgs& a, const int32_t* seg_off, const FusedPlan& p, float* sloc,
-                             float* phi, TimingHook* th)
+                             float* phi, int* counters, TimingHook* th)
 {
     hipError_t e;
     if (p.lseg == 0) {
         if (th) th->begin("fused", a.stream);
-        e = launch_pass<0, NORM>(a, seg_off, p, nullptr, nullptr, nullptr);
+        e = launch_pass<0, NORM>(a, seg_off, p, nullptr, nullptr, nullptr, counters);
         if (th) th->end(a.stream);
         return e;
     }
     if (th) th->begin("fused_sum", a.stream);
-    e = launch_pass<1, NORM>(a, seg_off, p, nullptr, sloc, phi);
+    e = launch_pass<1, NORM>(a, seg_off, p, nullptr, sloc, phi, counters + 1);
     if (th) th->end(a.stream);
     if (e != hipSuccess) return e;
     if (th) th->begin("fused_combine", a.stream);
@@ -1029,7 +1143,7 @@ hipError_t launch_fused_norm(const LaunchArgs& a, const int32_t* seg_off, const 
     if (th) th->end(a.stream);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (th) th->begin("fused", a.stream);
-    e = launch_pass<2, NORM>(a, seg_off, p, sloc, nullptr, nullptr);
+    e = launch_pass<2, NORM>(a, seg_off, p, sloc, nullptr, nullptr, counters + 2);
     if (th) th->end(a.stream);
     return e;
 }
@@ -1043,28 +1157,29 @@ bool fused_supported(const LaunchArgs& a)
 
 size_t fused_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads, size_t cap)
 {
-    const FusedPlan p = fused_plan(total_tokens, num_seqs, num_heads, cap);
-    return p.table_bytes + p.sloc_bytes + p.phi_bytes;
+    return fused_plan(total_tokens, num_seqs, num_heads, cap).total();
 }
 
 hipError_t launch_forward_fused(const LaunchArgs& a, void* workspace, TimingHook* th, size_t cap)
 {
     const FusedPlan p = fused_plan(a.total_tokens, a.num_seqs, a.num_heads, cap);
     if (int64_t(p.max_segs) * a.num_heads > 0x7FFFFFFF / 8) return hipErrorInvalidValue;
+    if (workspace == nullptr) return hipErrorInvalidValue;
     char* base = static_cast<char*>(workspace);
+    int* counters = reinterpret_cast<int*>(base);
+    base += FusedPlan::kCounterBytes;
     int32_t* seg_off = p.table_bytes ? reinterpret_cast<int32_t*>(base) : nullptr;
     float* sloc = p.lseg ? reinterpret_cast<float*>(base + p.table_bytes) : nullptr;
     float* phi = p.lseg ? reinterpret_cast<float*>(base + p.table_bytes + p.sloc_bytes) : nullptr;
-    if (seg_off) {
-        if (th) th->begin("plan", a.stream);
-        hipLaunchKernelGGL(kda_fused_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, seg_off,
-                           a.num_seqs, a.total_tokens, p.lseg);
-        if (th) th->end(a.stream);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    return a.qk_l2norm ? launch_fused_norm<true>(a, seg_off, p, sloc, phi, th)
-                       : launch_fused_norm<false>(a, seg_off, p, sloc, phi, th);
+    // the unit counters start at zero (and the segment table is built) in one small kernel
+    if (th) th->begin("plan", a.stream);
+    hipLaunchKernelGGL(kda_fused_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, seg_off,
+                       a.num_seqs, a.total_tokens, p.lseg, counters);
+    if (th) th->end(a.stream);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return a.qk_l2norm ? launch_fused_norm<true>(a, seg_off, p, sloc, phi, counters, th)
+                       : launch_fused_norm<false>(a, seg_off, p, sloc, phi, counters, th);
 }
 
 }  // namespace kda

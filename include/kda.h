@@ -86,8 +86,9 @@ typedef enum {
  * released with hipFreeAsync on `stream` after the kernels; the pool keeps the
  * memory for the next call, and kda_release gives it back to the driver). The environment
  * variable KDA_SCAN_VARIANT selects the bf16 scan: "fused" (the default for d_k = d_v = 128),
- * one kernel that forms every chunk's operands on the CU and whose workspace, taken only when
- * a few long samples are cut into segments, holds two 64 KB summaries per (segment, head);
+ * one kernel that forms every chunk's operands on the CU and whose workspace holds the
+ * counters its persistent workgroups take (segment, head) units from (256 bytes) and, when a
+ * few long samples are cut into segments, two 64 KB summaries per (segment, head);
  * "wy" (the default for other sizes), a prep kernel whose per-chunk records the workspace
  * holds and a chain kernel; "sequential", a single kernel that needs no workspace. fp32 data
  * always uses the sequential scan. Results are bitwise deterministic for identical inputs on
@@ -302,8 +303,8 @@ kda_status kda_short_conv_backward(const void *x, const float *w_text, const flo
 /*
  * kda_workspace_bytes -- bytes of device workspace the bf16 scan selected by
  * KDA_SCAN_VARIANT takes for these sizes (0 when it takes none: fp32 data, no samples,
- * unsupported sizes, the sequential scan). Fused scan: per (segment, head) state and
- * transition when samples are cut into segments, else nothing. WY scan: per (64-token
+ * unsupported sizes, the sequential scan). Fused scan: 256 bytes of unit counters, plus per
+ * (segment, head) state and transition when samples are cut into segments. WY scan: per (64-token
  * chunk, head) record of the chunk's decayed operands and WY factors (about 1.2 KB per token
  * and head), plus a chunk table.
  * Pure function of the sizes and the environment; no device access.
@@ -317,8 +318,8 @@ size_t kda_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_h
  * launches, named "fused", "fused_sum" and "fused_combine" (fused bf16 scan: the output
  * pass, and for samples cut into segments the summary pass and the combine over segments),
  * "prep", "segments" and "chain" (WY bf16 scan; "segments" is the first pass of its
- * sequence split), "plan" (a table over the samples, launched only for packs of more than
- * 64 samples) or "scan" (single-kernel scans); kda_backward records "bwd_plan", "bwd_prep",
+ * sequence split), "plan" (a table over the samples for packs of more than 64 samples; for
+ * the fused scan it also clears the unit counters, on every call) or "scan" (single-kernel scans); kda_backward records "bwd_plan", "bwd_prep",
  * "bwd_state", "bwd_dstate" and "bwd_grad", plus "bwd_state_seg" and "bwd_dstate_seg" (the
  * first passes of the chains' sequence split, for packs of few long samples). kda_timing_read waits for the recorded events of `kernel`,
  * returns their count and summed duration in milliseconds, and drops them.

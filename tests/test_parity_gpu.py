@@ -267,9 +267,11 @@ def test_sequence_split(monkeypatch, name, lens, H, dk, dv):
 
 # The fused scan splits samples into segments of 32-token chunks when the (sample, head)
 # units are fewer than 512: a summary pass, a combine over the segments, an output pass.
+# "plan" runs on every call (it clears the persistent passes' unit counters, and for more
+# than 64 samples, as in many_samples, also builds the segment table).
 FSPLIT = [
-    ("one_long", [5000], 2, ["fused_sum", "fused_combine", "fused"]),
-    ("ragged_pack", [3000, 0, 2100, 70, 1], 3, ["fused_sum", "fused_combine", "fused"]),
+    ("one_long", [5000], 2, ["fused_sum", "fused_combine", "fused", "plan"]),
+    ("ragged_pack", [3000, 0, 2100, 70, 1], 3, ["fused_sum", "fused_combine", "fused", "plan"]),
     ("many_samples", [700] * 70 + [33] * 30, 1, ["fused_sum", "fused_combine", "fused", "plan"]),
 ]
 
