@@ -991,8 +991,38 @@ __global__ __launch_bounds__(kCombThreads) void kda_fused_combine_kernel(
         for (int i = 0; i < 4; ++i)
             S[j][i] = init_state ? init_state[((int64_t(n) * H + h) * kFD + 32 * w + 16 * j + 4 * g + i) * kFD + col]
                                  : 0.f;
-    for (int kseg = 0; kseg + 1 < nseg; ++kseg) {
+    // Phi(k) and S_loc(k) do not depend on the chain: the next segment's are loaded while the
+    // current product runs, so a step waits only for its own products
+    struct Next {
+        float a[2][4][8];       // Phi rows row + r, columns 32 kb + [4g, 4g + 4) and + 16
+        f32x4 c[2];             // S_loc rows row + 4g + i, column col
+    };
+    auto load_next = [&](Next& x, int kseg) __attribute__((always_inline)) {
         const int64_t u = int64_t(first + kseg) * H + h;
+        const float* sl = sloc + u * kFD * kFD;
+        const float* ph = phi + u * kFD * kFD;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row = 32 * w + 16 * j;            // output key rows row + 4g + i (acc), row + r (A)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x.c[j][i] = sl[(row + 4 * g + i) * kFD + col];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const float4 a0 = *reinterpret_cast<const float4*>(ph + (row + r) * kFD + 32 * kb + 4 * g);
+                const float4 a1 = *reinterpret_cast<const float4*>(ph + (row + r) * kFD + 32 * kb + 16 + 4 * g);
+                x.a[j][kb][0] = a0.x; x.a[j][kb][1] = a0.y; x.a[j][kb][2] = a0.z; x.a[j][kb][3] = a0.w;
+                x.a[j][kb][4] = a1.x; x.a[j][kb][5] = a1.y; x.a[j][kb][6] = a1.z; x.a[j][kb][7] = a1.w;
+            }
+        }
+    };
+    auto step = [&](const Next& cur, Next& nxt, int kseg) __attribute__((always_inline)) {
+        // Phi(kseg) as hi/lo fragments before the chain's own wait
+        Frag ah[2][4], al[2][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) split8(cur.a[j][kb], ah[j][kb].u, al[j][kb].u);
+        if (kseg + 2 < nseg) load_next(nxt, kseg + 1);
         // publish S_in(kseg): this wave's rows are k-block w of the products
         {
             const float s8[8] = {S[0][0], S[0][1], S[0][2], S[0][3], S[1][0], S[1][1], S[1][2], S[1][3]};
@@ -1002,37 +1032,37 @@ __global__ __launch_bounds__(kCombThreads) void kda_fused_combine_kernel(
             sb[1][w][lane] = lo;
         }
         lds_barrier();
-        float* sl = sloc + u * kFD * kFD;
-        const float* ph = phi + u * kFD * kFD;
         f32x4 acc[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int row = 32 * w + 16 * j;            // output key rows row + 4g + i (acc), row + r (A)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[j][i] = sl[(row + 4 * g + i) * kFD + col];
+            acc[j] = cur.c[j];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                const float4 a0 = *reinterpret_cast<const float4*>(ph + (row + r) * kFD + 32 * kb + 4 * g);
-                const float4 a1 = *reinterpret_cast<const float4*>(ph + (row + r) * kFD + 32 * kb + 16 + 4 * g);
-                const float f8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-                Frag ah, al;
-                split8(f8, ah.u, al.u);
-                mfma_ready(ah.u, al.u);
+                mfma_ready(ah[j][kb].u, al[j][kb].u);
                 const Frag bh{sb[0][kb][lane]}, bl{sb[1][kb][lane]};
-                acc[j] = EL::mma(al, bh, acc[j]);
-                acc[j] = EL::mma(ah, bl, acc[j]);
-                acc[j] = EL::mma(ah, bh, acc[j]);
+                acc[j] = EL::mma(al[j][kb], bh, acc[j]);
+                acc[j] = EL::mma(ah[j][kb], bl, acc[j]);
+                acc[j] = EL::mma(ah[j][kb], bh, acc[j]);
             }
         }
         lds_barrier();
         // S_in(kseg + 1) over S_loc(kseg): the same lanes read and write these elements
+        float* sl = sloc + (int64_t(first + kseg) * H + h) * kFD * kFD;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             S[j] = acc[j];
 #pragma unroll
             for (int i = 0; i < 4; ++i) sl[(32 * w + 16 * j + 4 * g + i) * kFD + col] = acc[j][i];
         }
+    };
+    Next na, nb;
+    load_next(na, 0);
+    int kseg = 0;
+    for (; kseg + 2 < nseg; kseg += 2) {
+        step(na, nb, kseg);
+        step(nb, na, kseg + 1);
     }
+    if (kseg + 1 < nseg) step(na, nb, kseg);
 }
 
 struct FusedPlan {
