@@ -138,6 +138,15 @@ def fused_split(spec):
     return lseg, inner_chunks, inner_segs
 
 
+def fused_chunk_heads(spec, kernel: str) -> int:
+    """(32-token chunk, head) steps one launch of a fused pass runs (0 for other kernels)."""
+    if kernel == "fused":
+        return sum((n + FUSED_C - 1) // FUSED_C for n in spec.seq_lens) * spec.heads
+    if kernel == "fused_sum":
+        return fused_split(spec)[1] * spec.heads
+    return 0
+
+
 def kernel_bytes(spec, kernel: str) -> int:
     """Algorithmic bytes of one launch of each kernel of the default bf16 scan."""
     es = 2
@@ -655,6 +664,7 @@ def forward_timing(spec, t, cu, dev, steps, warmup):
     kda.timing_enable(False)
     # a kernel may run several times per step: its launches share the step's bytes
     kernels = {}
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
     for name in KERNEL_SYMBOL:
         n, ms = kda.timing_read(name)
         if n:
@@ -663,6 +673,12 @@ def forward_timing(spec, t, cu, dev, steps, warmup):
             kernels[name] = {"launches": n, "launches_per_step": per_step, "ms_avg": ms / n,
                              "ms_per_step": ms / steps, "algorithmic_bytes": b,
                              "achieved_GBs": b / (ms / n * 1e-3) / 1e9}
+            ch = fused_chunk_heads(spec, name)
+            if ch:
+                # the serial state step as the pass runs it: one CU's time per 32-token chunk
+                # (the launch's time spread over its chunk-heads, one workgroup per CU)
+                kernels[name]["chunk_heads"] = ch
+                kernels[name]["us_per_chunk_step"] = ms / n * 1e3 * cus / ch
     return wall * 1e3 / steps, kernels, step
 
 
