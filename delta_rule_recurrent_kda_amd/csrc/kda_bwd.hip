@@ -1,5 +1,6 @@
 // kda_bwd.hip -- gradients of the KDA scan (q, k, v, log alpha, beta and the initial
-// state) for fp32 and bf16 data, fp32 arithmetic on fp32 MFMA (gfx950).
+// state) for fp32 and bf16 data, fp32 arithmetic (gfx950): fp32 MFMA, except the two chains
+// on bf16 data, whose products take hi/lo bf16 operands (three bf16 MFMA terms).
 //
 // The paper trains its model through these kernels (training setup paragraph on the
 // custom kernels over the packed tokens). The recurrence, per (sample, head)
@@ -53,6 +54,70 @@ constexpr int kLC = kBC + 4;       // row stride of [C][C] tiles in LDS
 
 __device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// bf16 products for bf16 data in the chains (v_mfma_f32_16x16x32_bf16, fp32 accumulate). A
+// k-block of 32 is split over the lanes as elsewhere in these kernels: lane group g supplies
+// k = 4g + s and 16 + 4g + s (s = 0..3), so two accumulator tiles (rows 4g + v of tiles t and
+// t + 1) make one B fragment as they stand. Every fp32 operand enters as a hi + lo bf16 pair
+// (16 bits of mantissa) and a product as the three terms hi*hi, hi*lo, lo*hi: the chains
+// carry the state over the whole sequence, and db sums products of residuals (V - Kh S) that
+// cancel, so single bf16 operands are not enough there. dO (bf16 data) is exact as one bf16.
+struct BF {
+    uint4 u;
+};
+struct BF2 {
+    BF h, l;
+};
+__device__ __forceinline__ BF bf_pack(const float (&f)[8]) {
+    return BF{make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]))};
+}
+__device__ __forceinline__ BF2 bf_split(const float (&f)[8]) {
+    BF2 o;
+    o.h = bf_pack(f);
+    const uint32_t w[4] = {o.h.u.x, o.h.u.y, o.h.u.z, o.h.u.w};
+    float r[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        r[2 * j] = f[2 * j] - __uint_as_float(w[j] << 16);
+        r[2 * j + 1] = f[2 * j + 1] - __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+    o.l = bf_pack(r);
+    return o;
+}
+__device__ __forceinline__ BF2 bf_split(const f32x4& a, const f32x4& b) {
+    const float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return bf_split(f);
+}
+__device__ __forceinline__ f32x4 mmab(const BF& a, const BF& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.u), __builtin_bit_cast(bf16x8, b.u),
+                                                   c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mm3(const BF2& a, const BF2& b, f32x4 c) {
+    return mmab(a.h, b.h, mmab(a.h, b.l, mmab(a.l, b.h, c)));
+}
+__device__ __forceinline__ f32x4 mm2(const BF2& a, const BF& b, f32x4 c) { return mmab(a.h, b, mmab(a.l, b, c)); }
+__device__ __forceinline__ void ready(BF2& a) { mfma_ready(a.h.u, a.l.u); }
+__device__ __forceinline__ void ready(BF2& a, BF2& b) { mfma_ready(a.h.u, a.l.u, b.h.u, b.l.u); }
+// the 8 values a lane supplies from column `col` of a [32][ld] fp32 LDS array (k = row)
+__device__ __forceinline__ void col8(const float* a, int ld, int col, int g, float (&f)[8]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        f[s] = a[(4 * g + s) * ld + col];
+        f[4 + s] = a[(16 + 4 * g + s) * ld + col];
+    }
+}
+__device__ __forceinline__ BF2 bf_col(const float* a, int ld, int col, int g) {
+    float f[8];
+    col8(a, ld, col, g, f);
+    return bf_split(f);
+}
+// ... and from row `row` (k = column k0 + ...), 16-byte aligned pieces
+__device__ __forceinline__ BF2 bf_row(const float* a, int ld, int row, int k0, int g) {
+    const float4 x = *reinterpret_cast<const float4*>(a + row * ld + k0 + 4 * g);
+    const float4 y = *reinterpret_cast<const float4*>(a + row * ld + k0 + 16 + 4 * g);
+    const float f[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+    return bf_split(f);
 }
 
 template <typename E> __device__ __forceinline__ float ldf(const E* p);
@@ -660,6 +725,7 @@ __global__ __launch_bounds__(kBT) void kda_bwd_state_kernel(
     using R = BRec<DK>;
     constexpr int NCT = DK / 16, LK = DK + 4, LV = 64 + 4;
     constexpr int NT = MODE == 1 ? DV / 64 + DK / 64 : DV / 64;     // column tiles per unit
+    constexpr bool kBf = sizeof(E) == 2;                            // bf16 data: bf16 products
     extern __shared__ __align__(16) unsigned char smem_raw[];
     ChainLds<DK>& sm = *reinterpret_cast<ChainLds<DK>*>(smem_raw);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
@@ -707,42 +773,88 @@ __global__ __launch_bounds__(kBT) void kda_bwd_state_kernel(
         }
         fetch(min(cc + 1, c1 - 1));                       // in flight during this chunk's products
         // X = V - Kh S, then Y = diag(b) X (rows 16xi + 4g + v)
-        f32x4 Y[2];
+        f32x4 Y[2], Vn[2];
+        if constexpr (kBf) {
+            BF2 sf[NCT / 2];
 #pragma unroll
-        for (int xi = 0; xi < 2; ++xi) {
-            f32x4 acc = zero4();
+            for (int b = 0; b < NCT / 2; ++b) sf[b] = bf_split(S[2 * b], S[2 * b + 1]);
 #pragma unroll
-            for (int ti = 0; ti < NCT; ++ti)
+            for (int b = 0; b < NCT / 2; b += 2) ready(sf[b], sf[b + 1]);
 #pragma unroll
-                for (int st = 0; st < 4; ++st) acc = mma4(sm.kh[(16 * xi + r) * LK + 16 * ti + 4 * g + st], S[ti][st], acc);
+            for (int xi = 0; xi < 2; ++xi) {
+                BF2 a[NCT / 2];
 #pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) {
-                const int row = 16 * xi + 4 * g + v4;
-                const float vv = trans ? 0.f : sm.vt[row * LV + 16 * wave + r];
-                Y[xi][v4] = sm.beta[row] * (vv - acc[v4]);
+                for (int b = 0; b < NCT / 2; ++b) a[b] = bf_row(sm.kh, LK, 16 * xi + r, 32 * b, g);
+#pragma unroll
+                for (int b = 0; b < NCT / 2; b += 2) ready(a[b], a[b + 1]);
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int b = 0; b < NCT / 2; ++b) acc = mm3(a[b], sf[b], acc);
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4) {
+                    const int row = 16 * xi + 4 * g + v4;
+                    const float vv = trans ? 0.f : sm.vt[row * LV + 16 * wave + r];
+                    Y[xi][v4] = sm.beta[row] * (vv - acc[v4]);
+                }
             }
-        }
-        // Vn = T Y
-        f32x4 Vn[2];
+            // Vn = T Y
+            BF2 yf = bf_split(Y[0], Y[1]), ta[2];
 #pragma unroll
-        for (int vi = 0; vi < 2; ++vi) {
-            f32x4 acc = zero4();
+            for (int vi = 0; vi < 2; ++vi) ta[vi] = bf_row(sm.t, kLC, 16 * vi + r, 0, g);
+            ready(yf);
+            ready(ta[0], ta[1]);
 #pragma unroll
-            for (int xi = 0; xi < 2; ++xi)
+            for (int vi = 0; vi < 2; ++vi) Vn[vi] = mm3(ta[vi], yf, zero4());
+            // S <- diag(gamma) (S + Kc^T Vn)
+            BF2 vf = bf_split(Vn[0], Vn[1]);
+            ready(vf);
 #pragma unroll
-                for (int st = 0; st < 4; ++st) acc = mma4(sm.t[(16 * vi + r) * kLC + 16 * xi + 4 * g + st], Y[xi][st], acc);
-            Vn[vi] = acc;
-        }
-        // S <- diag(gamma) (S + Kc^T Vn)
+            for (int ti = 0; ti < NCT; ti += 2) {
+                BF2 ka = bf_col(sm.kc, LK, 16 * ti + r, g), kb = bf_col(sm.kc, LK, 16 * (ti + 1) + r, g);
+                ready(ka, kb);
+                const f32x4 a0 = mm3(ka, vf, zero4()), a1 = mm3(kb, vf, zero4());
 #pragma unroll
-        for (int ti = 0; ti < NCT; ++ti) {
-            f32x4 acc = zero4();
+                for (int v4 = 0; v4 < 4; ++v4) {
+                    S[ti][v4] = sm.gam[16 * ti + 4 * g + v4] * (S[ti][v4] + a0[v4]);
+                    S[ti + 1][v4] = sm.gam[16 * (ti + 1) + 4 * g + v4] * (S[ti + 1][v4] + a1[v4]);
+                }
+            }
+        } else {
 #pragma unroll
-            for (int vi = 0; vi < 2; ++vi)
+            for (int xi = 0; xi < 2; ++xi) {
+                f32x4 acc = zero4();
 #pragma unroll
-                for (int st = 0; st < 4; ++st) acc = mma4(sm.kc[(16 * vi + 4 * g + st) * LK + 16 * ti + r], Vn[vi][st], acc);
+                for (int ti = 0; ti < NCT; ++ti)
 #pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) S[ti][v4] = sm.gam[16 * ti + 4 * g + v4] * (S[ti][v4] + acc[v4]);
+                    for (int st = 0; st < 4; ++st) acc = mma4(sm.kh[(16 * xi + r) * LK + 16 * ti + 4 * g + st], S[ti][st], acc);
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4) {
+                    const int row = 16 * xi + 4 * g + v4;
+                    const float vv = trans ? 0.f : sm.vt[row * LV + 16 * wave + r];
+                    Y[xi][v4] = sm.beta[row] * (vv - acc[v4]);
+                }
+            }
+            // Vn = T Y
+#pragma unroll
+            for (int vi = 0; vi < 2; ++vi) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int xi = 0; xi < 2; ++xi)
+#pragma unroll
+                    for (int st = 0; st < 4; ++st) acc = mma4(sm.t[(16 * vi + r) * kLC + 16 * xi + 4 * g + st], Y[xi][st], acc);
+                Vn[vi] = acc;
+            }
+            // S <- diag(gamma) (S + Kc^T Vn)
+#pragma unroll
+            for (int ti = 0; ti < NCT; ++ti) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int vi = 0; vi < 2; ++vi)
+#pragma unroll
+                    for (int st = 0; st < 4; ++st) acc = mma4(sm.kc[(16 * vi + 4 * g + st) * LK + 16 * ti + r], Vn[vi][st], acc);
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4) S[ti][v4] = sm.gam[16 * ti + 4 * g + v4] * (S[ti][v4] + acc[v4]);
+            }
         }
         __syncthreads();
     }
@@ -773,6 +885,7 @@ __global__ __launch_bounds__(kBT) void kda_bwd_dstate_kernel(
 {
     using R = BRec<DK>;
     constexpr int NCT = DK / 16, LK = DK + 4, LV = 64 + 4;
+    constexpr bool kBf = sizeof(E) == 2;                            // bf16 data: bf16 products
     extern __shared__ __align__(16) unsigned char smem_raw[];
     ChainLds<DK>& sm = *reinterpret_cast<ChainLds<DK>*>(smem_raw);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
@@ -814,48 +927,107 @@ __global__ __launch_bounds__(kBT) void kda_bwd_dstate_kernel(
                 for (int v4 = 0; v4 < 4; ++v4) so[(16 * ti + 4 * g + v4) * DV + col] = dS[ti][v4];
         }
         fetch(max(cc - 1, c0));                           // in flight during this chunk's products
-        // dVn = P^T dO + Kc diag(gamma) dS
-        f32x4 dVn[2];
+        f32x4 dVn[2], dX[2];
+        if constexpr (kBf) {
+            // dVn = P^T dO + Kc diag(gamma) dS
+            BF2 df[NCT / 2];
 #pragma unroll
-        for (int vi = 0; vi < 2; ++vi) {
-            f32x4 acc = zero4();
+            for (int b = 0; b < NCT / 2; ++b) df[b] = bf_split(dS[2 * b], dS[2 * b + 1]);
 #pragma unroll
-            for (int k0 = 0; k0 < kBC; k0 += 4)
-                acc = mma4(sm.p[(k0 + g) * kLC + 16 * vi + r], sm.vt[(k0 + g) * LV + 16 * wave + r], acc);
+            for (int b = 0; b < NCT / 2; b += 2) ready(df[b], df[b + 1]);
+            BF dof;                                                         // dO as B (exact in bf16)
+            {
+                float f[8];
+                col8(sm.vt, LV, 16 * wave + r, g, f);
+                dof = bf_pack(f);
+            }
 #pragma unroll
-            for (int ti = 0; ti < NCT; ++ti)
+            for (int vi = 0; vi < 2; ++vi) {
+                BF2 pa = bf_col(sm.p, kLC, 16 * vi + r, g);
+                BF2 a[NCT / 2];
 #pragma unroll
-                for (int st = 0; st < 4; ++st) {
-                    const int c = 16 * ti + 4 * g + st;
-                    acc = mma4(sm.kc[(16 * vi + r) * LK + c] * sm.gam[c], dS[ti][st], acc);
+                for (int b = 0; b < NCT / 2; ++b) {
+                    const float* kr = sm.kc + (16 * vi + r) * LK + 32 * b + 4 * g;
+                    const float* gr = sm.gam + 32 * b + 4 * g;
+                    const float4 k0 = *reinterpret_cast<const float4*>(kr), k1 = *reinterpret_cast<const float4*>(kr + 16);
+                    const float4 g0 = *reinterpret_cast<const float4*>(gr), g1 = *reinterpret_cast<const float4*>(gr + 16);
+                    const float f[8] = {k0.x * g0.x, k0.y * g0.y, k0.z * g0.z, k0.w * g0.w,
+                                        k1.x * g1.x, k1.y * g1.y, k1.z * g1.z, k1.w * g1.w};
+                    a[b] = bf_split(f);
                 }
-            dVn[vi] = acc;
-        }
-        // dX = diag(b) T^T dVn
-        f32x4 dX[2];
+                mfma_ready(pa.h.u, pa.l.u, dof.u, dof.u);
 #pragma unroll
-        for (int zi = 0; zi < 2; ++zi) {
-            f32x4 acc = zero4();
+                for (int b = 0; b < NCT / 2; b += 2) ready(a[b], a[b + 1]);
+                f32x4 acc = mm2(pa, dof, zero4());
 #pragma unroll
-            for (int vi = 0; vi < 2; ++vi)
+                for (int b = 0; b < NCT / 2; ++b) acc = mm3(a[b], df[b], acc);
+                dVn[vi] = acc;
+            }
+            // dX = diag(b) T^T dVn
+            BF2 vf = bf_split(dVn[0], dVn[1]), ta[2];
 #pragma unroll
-                for (int st = 0; st < 4; ++st) acc = mma4(sm.t[(16 * vi + 4 * g + st) * kLC + 16 * zi + r], dVn[vi][st], acc);
+            for (int zi = 0; zi < 2; ++zi) ta[zi] = bf_col(sm.t, kLC, 16 * zi + r, g);
+            ready(vf);
+            ready(ta[0], ta[1]);
 #pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) dX[zi][v4] = sm.beta[16 * zi + 4 * g + v4] * acc[v4];
-        }
-        // dS <- diag(gamma) dS + Qh^T dO - Kh^T dX
+            for (int zi = 0; zi < 2; ++zi) {
+                const f32x4 acc = mm3(ta[zi], vf, zero4());
 #pragma unroll
-        for (int ti = 0; ti < NCT; ++ti) {
-            f32x4 acc = zero4();
+                for (int v4 = 0; v4 < 4; ++v4) dX[zi][v4] = sm.beta[16 * zi + 4 * g + v4] * acc[v4];
+            }
+            // dS <- diag(gamma) dS + Qh^T dO - Kh^T dX
+            BF2 xf = bf_split(-dX[0], -dX[1]);
+            ready(xf);
 #pragma unroll
-            for (int k0 = 0; k0 < kBC; k0 += 4)
-                acc = mma4(sm.qh[(k0 + g) * LK + 16 * ti + r], sm.vt[(k0 + g) * LV + 16 * wave + r], acc);
+            for (int ti = 0; ti < NCT; ++ti) {
+                BF2 qa = bf_col(sm.qh, LK, 16 * ti + r, g), ka = bf_col(sm.kh, LK, 16 * ti + r, g);
+                ready(qa, ka);
+                const f32x4 acc = mm3(ka, xf, mm2(qa, dof, zero4()));
 #pragma unroll
-            for (int zi = 0; zi < 2; ++zi)
+                for (int v4 = 0; v4 < 4; ++v4) dS[ti][v4] = sm.gam[16 * ti + 4 * g + v4] * dS[ti][v4] + acc[v4];
+            }
+        } else {
+            // dVn = P^T dO + Kc diag(gamma) dS
 #pragma unroll
-                for (int st = 0; st < 4; ++st) acc = mma4(-sm.kh[(16 * zi + 4 * g + st) * LK + 16 * ti + r], dX[zi][st], acc);
+            for (int vi = 0; vi < 2; ++vi) {
+                f32x4 acc = zero4();
 #pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) dS[ti][v4] = sm.gam[16 * ti + 4 * g + v4] * dS[ti][v4] + acc[v4];
+                for (int k0 = 0; k0 < kBC; k0 += 4)
+                    acc = mma4(sm.p[(k0 + g) * kLC + 16 * vi + r], sm.vt[(k0 + g) * LV + 16 * wave + r], acc);
+#pragma unroll
+                for (int ti = 0; ti < NCT; ++ti)
+#pragma unroll
+                    for (int st = 0; st < 4; ++st) {
+                        const int c = 16 * ti + 4 * g + st;
+                        acc = mma4(sm.kc[(16 * vi + r) * LK + c] * sm.gam[c], dS[ti][st], acc);
+                    }
+                dVn[vi] = acc;
+            }
+            // dX = diag(b) T^T dVn
+#pragma unroll
+            for (int zi = 0; zi < 2; ++zi) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int vi = 0; vi < 2; ++vi)
+#pragma unroll
+                    for (int st = 0; st < 4; ++st) acc = mma4(sm.t[(16 * vi + 4 * g + st) * kLC + 16 * zi + r], dVn[vi][st], acc);
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4) dX[zi][v4] = sm.beta[16 * zi + 4 * g + v4] * acc[v4];
+            }
+            // dS <- diag(gamma) dS + Qh^T dO - Kh^T dX
+#pragma unroll
+            for (int ti = 0; ti < NCT; ++ti) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int k0 = 0; k0 < kBC; k0 += 4)
+                    acc = mma4(sm.qh[(k0 + g) * LK + 16 * ti + r], sm.vt[(k0 + g) * LV + 16 * wave + r], acc);
+#pragma unroll
+                for (int zi = 0; zi < 2; ++zi)
+#pragma unroll
+                    for (int st = 0; st < 4; ++st) acc = mma4(-sm.kh[(16 * zi + 4 * g + st) * LK + 16 * ti + r], dX[zi][st], acc);
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4) dS[ti][v4] = sm.gam[16 * ti + 4 * g + v4] * dS[ti][v4] + acc[v4];
+            }
         }
         __syncthreads();
     }
