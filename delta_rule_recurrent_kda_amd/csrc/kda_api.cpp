@@ -184,6 +184,28 @@ kda_status check_args(const void* q, const void* k, const void* v, const void* l
                       hipStream_t stream, bool host_checks = true);
 kda_status run(const kda::LaunchArgs& a);
 
+bool debug_sync_env()
+{
+    const char* e = std::getenv("KDA_DEBUG_SYNC");
+    return e && e[0] == '1';
+}
+
+// The end of every call that enqueued work: a launch error, or else, under KDA_DEBUG_SYNC=1
+// and outside stream capture, the stream's completion, so that a failed kernel is reported by
+// the call that enqueued it rather than by a later one.
+kda_status finish(hipError_t e, hipStream_t stream)
+{
+    if (e != hipSuccess) return fail(KDA_E_HIP, "launch failed: %s", hipGetErrorString(e));
+    if (!debug_sync_env()) return KDA_OK;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if ((e = hipStreamIsCapturing(stream, &cs)) != hipSuccess)
+        return fail(KDA_E_HIP, "KDA_DEBUG_SYNC: stream capture status: %s", hipGetErrorString(e));
+    if (cs != hipStreamCaptureStatusNone) return KDA_OK;
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess)
+        return fail(KDA_E_HIP, "KDA_DEBUG_SYNC: the call's kernels failed: %s", hipGetErrorString(e));
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -289,8 +311,7 @@ kda_status kda_forward_noalloc(const void* q, const void* k, const void* v, cons
     } else {
         e = kda::launch_forward_seq(a);
     }
-    if (e != hipSuccess) return fail(KDA_E_HIP, "launch failed: %s", hipGetErrorString(e));
-    return KDA_OK;
+    return finish(e, stream);
 }
 
 kda_status kda_backward(const void* q, const void* k, const void* v, const void* log_alpha,
@@ -347,8 +368,7 @@ kda_status kda_backward(const void* q, const void* k, const void* v, const void*
     e = kda::launch_backward(a, ws, th);
     const hipError_t ef = hipFreeAsync(ws, stream);
     if (e == hipSuccess) e = ef;
-    if (e != hipSuccess) return fail(KDA_E_HIP, "launch failed: %s", hipGetErrorString(e));
-    return KDA_OK;
+    return finish(e, stream);
 }
 
 size_t kda_backward_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads, int32_t d_k,
@@ -449,8 +469,7 @@ kda_status kda_short_conv(const void* x, const float* w_text, const float* w_vis
     e = kda::launch_short_conv(a, ws, th);
     const hipError_t ef = hipFreeAsync(ws, stream);
     if (e == hipSuccess) e = ef;
-    if (e != hipSuccess) return fail(KDA_E_HIP, "launch failed: %s", hipGetErrorString(e));
-    return KDA_OK;
+    return finish(e, stream);
 }
 
 kda_status kda_short_conv_backward(const void* x, const float* w_text, const float* w_vis,
@@ -484,9 +503,7 @@ kda_status kda_short_conv_backward(const void* x, const float* w_text, const flo
     if (num_seqs == 0 || total_tokens == 0) {
         // no tokens: the weight gradients are empty sums, written as zeros without a workspace
         if (!dw_text || !dw_vis) return fail(KDA_E_NULL, "dw_text or dw_vis is NULL");
-        const hipError_t e = kda::launch_short_conv_backward(a, nullptr, th);
-        if (e != hipSuccess) return fail(KDA_E_HIP, "launch failed: %s", hipGetErrorString(e));
-        return KDA_OK;
+        return finish(kda::launch_short_conv_backward(a, nullptr, th), stream);
     }
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
@@ -499,8 +516,7 @@ kda_status kda_short_conv_backward(const void* x, const float* w_text, const flo
     e = kda::launch_short_conv_backward(a, ws, th);
     const hipError_t ef = hipFreeAsync(ws, stream);
     if (e == hipSuccess) e = ef;
-    if (e != hipSuccess) return fail(KDA_E_HIP, "launch failed: %s", hipGetErrorString(e));
-    return KDA_OK;
+    return finish(e, stream);
 }
 
 kda_status kda_timing_enable(int32_t on)
@@ -645,8 +661,7 @@ kda_status run(const kda::LaunchArgs& a)
         e = kda::launch_forward_seq(a);
         if (th) th->end(a.stream);
     }
-    if (e != hipSuccess) return fail(KDA_E_HIP, "launch failed: %s", hipGetErrorString(e));
-    return KDA_OK;
+    return finish(e, a.stream);
 }
 
 }  // namespace

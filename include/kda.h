@@ -98,6 +98,9 @@ typedef enum {
  *
  * Errors: returns KDA_OK or an error code; argument checks run before any launch and
  * nothing is enqueued on error. kda_last_error() gives a message for the calling thread.
+ * With the environment variable KDA_DEBUG_SYNC=1, every call that enqueues work (the
+ * forward, backward and short-convolution entry points) waits for its stream before it
+ * returns, outside stream capture, and reports a failure of its kernels as KDA_E_HIP.
  */
 kda_status kda_forward(const void *q, const void *k, const void *v, const void *log_alpha,
                        const void *beta, const int32_t *cu_seqlens, void *out,

@@ -8,6 +8,8 @@
   so permuting or zeroing columns of V permutes or zeroes the same columns of O and S;
 - the same results with every kernel launch serialised (AMD_SERIALIZE_KERNEL=3);
 - KDA_VALIDATE=1 turns malformed sample tables into KDA_E_SEQLENS before any launch;
+- KDA_DEBUG_SYNC=1 (each call waits for its stream) changes no result, and a call captured
+  into a graph under it does not wait;
 - kda_release gives the pooled workspace memory back to the driver.
 """
 import json
@@ -228,3 +230,59 @@ def test_release_returns_pool_memory():
     free1, _ = torch.cuda.mem_get_info()
     gu.log(f"[release] workspace {ws / 2**20:.0f} MiB, free memory +{(free1 - free0) / 2**20:.0f} MiB")
     assert free1 - free0 >= ws // 2, (free0, free1, ws)
+
+
+def test_debug_sync_same_results(monkeypatch):
+    """Forward, backward and short convolution with KDA_DEBUG_SYNC=1 return KDA_OK and the same
+    results bit for bit; under stream capture the call does not synchronise (which capture
+    forbids), and the replayed graph gives the eager result."""
+    import torch
+    from delta_rule_recurrent_kda_amd import kda
+    gu.log("case KDA_DEBUG_SYNC")
+    spec = inputs.custom([700, 0, 1300, 65], heads=2, d=128, seed=33)
+    d = gu.device_inputs(spec, inputs.generate(spec))
+    dev = "cuda:0"
+    T, H, N = spec.total_tokens, spec.heads, len(spec.seq_lens)
+    g = torch.Generator(device=dev)
+    g.manual_seed(35)
+    do = torch.randn((T, H, spec.dv), device=dev, generator=g).to(torch.bfloat16)
+    x = torch.randn((90, 32), device=dev, generator=g).to(torch.bfloat16)
+    wt = torch.randn((4, 32), device=dev, generator=g)
+    wv = torch.randn((3, 3, 3, 32), device=dev, generator=g)
+    ccu = torch.tensor([0, 40, 90], dtype=torch.int32, device=dev)
+    tl = torch.tensor([4, 2], dtype=torch.int32, device=dev)
+    grid = torch.tensor([[2, 3, 6], [2, 4, 6]], dtype=torch.int32, device=dev)
+
+    def run_all():
+        o = kda.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"])
+        gr = kda.backward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"], do)
+        y = kda.short_conv(x, wt, wv, ccu, tl, grid)
+        torch.cuda.synchronize()
+        return [t.clone() for t in (list(o) + list(gr) + [y])]
+
+    plain = run_all()
+    monkeypatch.setenv("KDA_DEBUG_SYNC", "1")
+    synced = run_all()
+    assert len(plain) == len(synced)
+    for i, (a, b) in enumerate(zip(plain, synced)):
+        assert torch.equal(_bits(a), _bits(b)), i
+    # captured: the forward records its kernels and no wait
+    out = torch.empty((T, H, spec.dv), dtype=torch.bfloat16, device=dev)
+    fs = torch.empty((N, H, spec.dk, spec.dv), dtype=torch.float32, device=dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        kda.kda_forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"], out, fs,
+                        stream=torch.cuda.current_stream())
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        kda.kda_forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"], out, fs,
+                        stream=torch.cuda.current_stream())
+    out.zero_()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(out), _bits(plain[0]))
+    assert torch.equal(fs, plain[1])
