@@ -429,7 +429,8 @@ def backward_bench(args, spec, t, cu, dev):
     ms_step = wall * 1e3 / args.steps
     return {"metric": "KDA backward head-tokens/s (gradients of q, k, v, log a, beta)",
             "value": spec.head_tokens / (ms_step * 1e-3), "unit": "tokens/s", "ms_per_step": ms_step,
-            "dtype": "f32 arithmetic on " + spec.dtype + " data",
+            "dtype": "f32 arithmetic on " + spec.dtype + " data (fp32 MFMA; on bf16 data the two chains take "
+                     "hi/lo bf16 MFMA terms)",
             "roofline": {"bound": "mfma", "achieved": kd["achieved_TFLOPs"], "peak": MFMA_F32_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": kd["achieved_TFLOPs"] / MFMA_F32_PEAK_TFLOPS,
                          "traffic": traffic_for(args.workload, BWD_KERNELS[dom], kernel_sha(BWD_SOURCES)),
