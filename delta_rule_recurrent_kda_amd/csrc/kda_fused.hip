@@ -39,7 +39,7 @@
 //   pass 1  per segment that is not its sample's last: the state reached from zero
 //           (S_loc) and the segment's transition Phi (the same chunk pass on a d_k-column
 //           state started at the identity with V taken as zero), no output;
-//   combine per (sample, head, 16 value columns): S_in(k+1) = Phi(k) S_in(k) + S_loc(k)
+//   combine per (sample, head, 32 value columns): S_in(k+1) = Phi(k) S_in(k) + S_loc(k)
 //           from the sample's initial state, with hi/lo bf16 operands;
 //   pass 2  every segment from its S_in with outputs; the last one writes final_state.
 //
@@ -73,7 +73,8 @@ constexpr int kFD = 128;           // d_k = d_v
 constexpr int kFThreads = 512;     // 4 consumer + 4 producer wave64
 constexpr uint16_t kOneBf = 0x3F80;
 constexpr int kFCounters = 4;      // unit counters of the persistent passes (one per pass)
-constexpr int kCombThreads = 256;  // combine: 4 wave64 per (sample, head, 16 value columns)
+constexpr int kCombThreads = 256;  // combine: 4 wave64 per (sample, head, kCombCT 16-column value tiles)
+constexpr int kCombCT = 2;         // value tiles per combine workgroup (each Phi fragment serves all of them)
 
 // one chunk's operands for the state pass, every array in lane order
 struct Buf {
@@ -946,7 +947,7 @@ __global__ __launch_bounds__(kFThreads, 1) void kda_fused_kernel(const FusedArgs
 }
 
 // ---------------------------------------------------------------------------
-// combine: per (sample, head, 16 value columns), the entry state of every segment,
+// combine: per (sample, head, kCombCT value tiles of 16 columns), the entry state of every segment,
 // S_in(k + 1) = Phi(k) S_in(k) + S_loc(k), S_in(0) = the initial state; S_in(k + 1) is
 // written over S_loc(k) (the slot of segment k), which no later step reads. Wave w
 // computes output rows 32w..32w+31 (key tiles 2w, 2w + 1); Phi's rows (fp32) enter as
@@ -957,11 +958,13 @@ __global__ __launch_bounds__(kCombThreads) void kda_fused_combine_kernel(
     float* __restrict__ sloc, const float* __restrict__ phi, int num_seqs, int H, int64_t T, int lseg,
     int max_segs)
 {
-    __shared__ uint4 sb[2][4][64];              // S_in as B fragments: [hi/lo][k-block][lane]
+    constexpr int CT = kCombCT;
+    __shared__ uint4 sb[2][4][CT][64];          // S_in as B fragments: [hi/lo][k-block][value tile][lane]
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int r = lane & 15, g = lane >> 4;
-    const int ct0 = blockIdx.x & 7;             // value tile: columns 16 ct0 + r
-    const int unit = blockIdx.x >> 3;
+    constexpr int kGroups = 8 / CT;             // workgroups per (sample, head)
+    const int ct0 = (blockIdx.x % kGroups) * CT;    // value tiles ct0 .. ct0 + CT - 1: columns 16 ct + r
+    const int unit = blockIdx.x / kGroups;
     if (unit >= num_seqs * H) return;
     const int n = unit / H, h = unit % H;
     // first segment id of sample n and its segment count
@@ -983,19 +986,22 @@ __global__ __launch_bounds__(kCombThreads) void kda_fused_combine_kernel(
     if (first + nseg > max_segs) nseg = max(0, max_segs - first);
     if (nseg <= 1) return;
 
-    const int col = 16 * ct0 + r;
-    f32x4 S[2];
+    f32x4 S[CT][2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int c = 0; c < CT; ++c)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[j][i] = init_state ? init_state[((int64_t(n) * H + h) * kFD + 32 * w + 16 * j + 4 * g + i) * kFD + col]
-                                 : 0.f;
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S[c][j][i] = init_state ? init_state[((int64_t(n) * H + h) * kFD + 32 * w + 16 * j + 4 * g + i) * kFD +
+                                                     16 * (ct0 + c) + r]
+                                        : 0.f;
     // Phi(k) and S_loc(k) do not depend on the chain: the next segment's are loaded while the
-    // current product runs, so a step waits only for its own products
+    // current product runs, so a step waits only for its own products. Each fragment of Phi
+    // serves the workgroup's CT value tiles.
     struct Next {
         float a[2][4][8];       // Phi rows row + r, columns 32 kb + [4g, 4g + 4) and + 16
-        f32x4 c[2];             // S_loc rows row + 4g + i, column col
+        f32x4 c[CT][2];         // S_loc rows row + 4g + i, columns 16 ct + r
     };
     auto load_next = [&](Next& x, int kseg) __attribute__((always_inline)) {
         const int64_t u = int64_t(first + kseg) * H + h;
@@ -1005,7 +1011,9 @@ __global__ __launch_bounds__(kCombThreads) void kda_fused_combine_kernel(
         for (int j = 0; j < 2; ++j) {
             const int row = 32 * w + 16 * j;            // output key rows row + 4g + i (acc), row + r (A)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x.c[j][i] = sl[(row + 4 * g + i) * kFD + col];
+            for (int c = 0; c < CT; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x.c[c][j][i] = sl[(row + 4 * g + i) * kFD + 16 * (ct0 + c) + r];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 const float4 a0 = *reinterpret_cast<const float4*>(ph + (row + r) * kFD + 32 * kb + 4 * g);
@@ -1024,36 +1032,47 @@ __global__ __launch_bounds__(kCombThreads) void kda_fused_combine_kernel(
             for (int kb = 0; kb < 4; ++kb) split8(cur.a[j][kb], ah[j][kb].u, al[j][kb].u);
         if (kseg + 2 < nseg) load_next(nxt, kseg + 1);
         // publish S_in(kseg): this wave's rows are k-block w of the products
-        {
-            const float s8[8] = {S[0][0], S[0][1], S[0][2], S[0][3], S[1][0], S[1][1], S[1][2], S[1][3]};
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+            const float s8[8] = {S[c][0][0], S[c][0][1], S[c][0][2], S[c][0][3],
+                                 S[c][1][0], S[c][1][1], S[c][1][2], S[c][1][3]};
             uint4 hi, lo;
             split8(s8, hi, lo);
-            sb[0][w][lane] = hi;
-            sb[1][w][lane] = lo;
+            sb[0][w][c][lane] = hi;
+            sb[1][w][c][lane] = lo;
         }
         lds_barrier();
-        f32x4 acc[2];
+        f32x4 acc[CT][2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            acc[j] = cur.c[j];
+        for (int c = 0; c < CT; ++c)
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                mfma_ready(ah[j][kb].u, al[j][kb].u);
-                const Frag bh{sb[0][kb][lane]}, bl{sb[1][kb][lane]};
-                acc[j] = EL::mma(al[j][kb], bh, acc[j]);
-                acc[j] = EL::mma(ah[j][kb], bl, acc[j]);
-                acc[j] = EL::mma(ah[j][kb], bh, acc[j]);
+            for (int j = 0; j < 2; ++j) acc[c][j] = cur.c[c][j];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) mfma_ready(ah[j][kb].u, al[j][kb].u);
+#pragma unroll
+            for (int c = 0; c < CT; ++c) {
+                const Frag bh{sb[0][kb][c][lane]}, bl{sb[1][kb][c][lane]};
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    acc[c][j] = EL::mma(al[j][kb], bh, acc[c][j]);
+                    acc[c][j] = EL::mma(ah[j][kb], bl, acc[c][j]);
+                    acc[c][j] = EL::mma(ah[j][kb], bh, acc[c][j]);
+                }
             }
         }
         lds_barrier();
         // S_in(kseg + 1) over S_loc(kseg): the same lanes read and write these elements
         float* sl = sloc + (int64_t(first + kseg) * H + h) * kFD * kFD;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            S[j] = acc[j];
+        for (int c = 0; c < CT; ++c)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sl[(32 * w + 16 * j + 4 * g + i) * kFD + col] = acc[j][i];
-        }
+            for (int j = 0; j < 2; ++j) {
+                S[c][j] = acc[c][j];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sl[(32 * w + 16 * j + 4 * g + i) * kFD + 16 * (ct0 + c) + r] = acc[c][j][i];
+            }
     };
     Next na, nb;
     load_next(na, 0);
@@ -1167,7 +1186,7 @@ hipError_t launch_fused_norm(const LaunchArgs& a, const int32_t* seg_off, const 
     if (th) th->end(a.stream);
     if (e != hipSuccess) return e;
     if (th) th->begin("fused_combine", a.stream);
-    hipLaunchKernelGGL(kda_fused_combine_kernel, dim3(a.num_seqs * a.num_heads * 8), dim3(kCombThreads), 0,
+    hipLaunchKernelGGL(kda_fused_combine_kernel, dim3(a.num_seqs * a.num_heads * (8 / kCombCT)), dim3(kCombThreads), 0,
                        a.stream, a.cu_seqlens, seg_off, a.init_state, sloc, phi, a.num_seqs, a.num_heads,
                        a.total_tokens, p.lseg, p.max_segs);
     if (th) th->end(a.stream);
