@@ -126,8 +126,8 @@ def fused_split(spec):
     H = spec.heads
     chunks = (spec.total_tokens + FUSED_C - 1) // FUSED_C + len(spec.seq_lens)
     lseg = 0
-    if len(spec.seq_lens) * H < 512:
-        cand = max(16, (chunks * H + 511) // 512)
+    if len(spec.seq_lens) * H < 256:
+        cand = max(16, (chunks * H + 255) // 256)
         lseg = cand if cand < chunks else 0
     if not lseg:
         return 0, 0, 0

@@ -1103,15 +1103,16 @@ FusedPlan plan_with(int64_t chunks, int32_t N, int32_t H, int64_t lseg)
     return p;
 }
 
-// Cut samples into segments when the (sample, head) units alone would fill fewer than two
-// workgroups per CU: about 512 segment-workgroups then run, of at least 16 chunks each.
+// Cut samples into segments when the (sample, head) units alone would not give every CU one:
+// about 256 segment units then run, one per CU, of at least 16 chunks each (two rounds of
+// half-length segments take as long for the passes and double the combine's chain).
 // With a byte limit on the workspace, segments grow until their summaries fit (fewer,
 // longer segments); when not even one cut per sample fits, samples stay whole.
 FusedPlan fused_plan(int64_t T, int32_t N, int32_t H, size_t cap)
 {
     const int64_t units = int64_t(N) * H;
     const int64_t chunks = (T + kFC - 1) / kFC + N;         // upper bound over all samples
-    int64_t lseg = units < 512 ? std::max<int64_t>(16, (chunks * H + 511) / 512) : 0;
+    int64_t lseg = units < 256 ? std::max<int64_t>(16, (chunks * H + 255) / 256) : 0;
     FusedPlan p = plan_with(chunks, N, H, lseg);
     if (p.total() <= cap) return p;
     const size_t slot = size_t(2) * kFD * kFD * 4 * size_t(H);          // one segment's summaries, all heads

@@ -308,12 +308,12 @@ def test_workspace_bytes(lib, monkeypatch):
             monkeypatch.setenv("KDA_SCAN_VARIANT", "wy")
         if dk == 128 and dv == 128 and fused:
             # fused scan (32-token chunks): 256 bytes of unit counters; when the (sample, head)
-            # units are fewer than 512, segments of lseg chunks, each (segment, head) with an fp32
+            # units are fewer than 256, segments of lseg chunks, each (segment, head) with an fp32
             # local state and its transition (64 KB each), and a segment table for more than 64 samples
             chunks = (T + 31) // 32 + N
             expect = 256
-            if N * H < 512:
-                lseg = max(16, (chunks * H + 511) // 512)
+            if N * H < 256:
+                lseg = max(16, (chunks * H + 255) // 256)
                 if lseg < chunks:
                     max_segs = (chunks + lseg - 1) // lseg + N
                     expect += max_segs * H * 2 * 65536 + ((N + 1) * 4 + 255) // 256 * 256 * (N > 64)

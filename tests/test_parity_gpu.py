@@ -266,7 +266,7 @@ def test_sequence_split(monkeypatch, name, lens, H, dk, dv):
 
 
 # The fused scan splits samples into segments of 32-token chunks when the (sample, head)
-# units are fewer than 512: a summary pass, a combine over the segments, an output pass.
+# units are fewer than 256: a summary pass, a combine over the segments, an output pass.
 # "plan" runs on every call (it clears the persistent passes' unit counters, and for more
 # than 64 samples, as in many_samples, also builds the segment table).
 FSPLIT = [
