@@ -21,16 +21,23 @@
 //     outputs and is widened from bf16 once.
 //   - Inputs come straight from global memory: the kt*kh rows a strip reads are shared with
 //     the strips of neighbouring rows and frames, which run at the same time on the same XCD
-//     and find them in its L2.
+//     and find them in its L2. Each XCD owns a contiguous part of the tile list and its
+//     workgroups take those tiles one at a time from the XCD's counter, so the tiles in
+//     flight are always the latest ones started, a window that slides through the frames
+//     (with tiles dealt out in turn the workgroups drift apart over a long sample and the
+//     window spreads). A tile reads its time taps in the order of that walk: the frames the
+//     tiles before it read last first, its newest frame last. Outputs are streaming stores.
+//     Reads come to about 1.2-1.3x the input on the clip layouts (counters); reading the own
+//     frame first, with tiles dealt out in turn, made them 1.9x.
 //   - For whole-frame samples under 1 GiB the loads are buffer loads over the sample's grid
 //     tokens: a position outside the grid gets an offset past the buffer's end and reads as
 //     zero, so no lane spends arithmetic on padding.
-//   - A plan kernel counts the tiles per sample; a fixed grid of workgroups walks the tile
-//     list channel-block-major, each XCD a contiguous part of it, with the weights of the
-//     current channel block in LDS.
+//   - A plan kernel counts the tiles per sample and clears the counters; a fixed grid of
+//     workgroups walks the tile list channel-block-major, with the weights of the current
+//     channel block in LDS.
 // The reverse mode (the gradients for a given dy) reuses the tiles: dx is the same kernel
 // run on dy with the taps mirrored and time and text walked forward (REV); the weight
-// gradients are sums over all tokens, formed per (channel block, slice of the tile list,
+// gradients are sums over all tokens, formed per (channel block, part of the tile list,
 // time offset) in fp32 and added in a fixed order by a reduce kernel.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -52,6 +59,7 @@ constexpr int kTextTok = 128;       // tokens per text tile
 constexpr int kSW = 4;              // columns per thread strip
 constexpr int kStrips = kCT / 8;    // column strips per visual tile
 constexpr int kWgPerCu = 4;         // resident workgroups per CU of the persistent grid
+constexpr int kQueueBytes = 8 * 128;        // a tile counter per XCD, each on its own 128-byte line
 constexpr uint32_t kBufLimit = 1u << 30;    // bytes a buffer-load tile may span; also the "outside" offset
 constexpr int kBufFlags = 0x00020000;       // raw buffer resource: 32-bit data format, no swizzle
 
@@ -66,8 +74,11 @@ template <> struct Vec8<uint16_t> {
             f[2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
         }
     }
+    // outputs are written once and not read again here: streaming stores, so that they do not
+    // push the inputs the neighbouring tiles still read out of the L2
     __device__ static void store(uint16_t* p, const float (&f)[8]) {
-        *reinterpret_cast<u32x4*>(p) = u32x4{pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
+        __builtin_nontemporal_store(u32x4{pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])},
+                                    reinterpret_cast<u32x4*>(p));
     }
     // 8 channels as loaded (two bf16 per dword), widened one element at a time
     struct Raw { u32x4 u; };
@@ -93,8 +104,8 @@ template <> struct Vec8<float> {
         }
     }
     __device__ static void store(float* p, const float (&f)[8]) {
-        *reinterpret_cast<f32x4*>(p) = f32x4{f[0], f[1], f[2], f[3]};
-        *reinterpret_cast<f32x4*>(p + 4) = f32x4{f[4], f[5], f[6], f[7]};
+        __builtin_nontemporal_store(f32x4{f[0], f[1], f[2], f[3]}, reinterpret_cast<f32x4*>(p));
+        __builtin_nontemporal_store(f32x4{f[4], f[5], f[6], f[7]}, reinterpret_cast<f32x4*>(p + 4));
     }
     struct Raw { f32x4 a, b; };
     __device__ static Raw load_raw(const float* p, bool ok) {
@@ -158,14 +169,17 @@ __device__ __forceinline__ SampleTiles sample_tiles(const SampleGeom& g) {
     return t;
 }
 
-// tile_off[n] = tiles of samples 0..n-1 (per channel block); one workgroup
+// tile_off[n] = tiles of samples 0..n-1 (per channel block), and the per-XCD tile counters
+// cleared (queue may be null); one workgroup
 __global__ __launch_bounds__(1024) void kda_conv_plan_kernel(const int32_t* __restrict__ cu,
                                                              const int32_t* __restrict__ text_len,
                                                              const int32_t* __restrict__ grid,
-                                                             int32_t* __restrict__ tile_off, int num_seqs, int64_t T)
+                                                             int32_t* __restrict__ tile_off, int* __restrict__ queue,
+                                                             int num_seqs, int64_t T)
 {
     __shared__ int32_t part[1024];
     const int tid = threadIdx.x;
+    if (queue && tid < 8) queue[32 * tid] = 0;
     int32_t carry = 0;
     for (int b0 = 0; b0 < num_seqs; b0 += 1024) {
         const int n = b0 + tid;
@@ -200,8 +214,8 @@ template <typename E, int KW, bool REV>
 __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kWgPerCu))) void kda_short_conv_kernel(
     const E* __restrict__ x, const float* __restrict__ w_text, const float* __restrict__ w_vis,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ text_len, const int32_t* __restrict__ grid,
-    const int32_t* __restrict__ tile_off, E* __restrict__ y, int64_t T, int num_seqs, int C, int kx, int kt, int kh,
-    int ncb)
+    const int32_t* __restrict__ tile_off, int* __restrict__ queue, E* __restrict__ y, int64_t T, int num_seqs, int C,
+    int kx, int kt, int kh, int ncb)
 {
     constexpr int kw = KW;
     extern __shared__ __align__(16) float wl[];                          // [tap][64]: text taps, then visual
@@ -212,12 +226,16 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kWgPerCu)))
     const int per_cb = tile_off[num_seqs];
     const int64_t total = int64_t(per_cb) * ncb;
     // this XCD's contiguous range of the tile list (channel-block-major, so the tiles that
-    // share inputs sit together); its workgroups take it in turn
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, ng = gridDim.x >> 3;
+    // share inputs sit together), taken one tile at a time from the XCD's counter: the tiles
+    // in flight are always the latest ones started, a window that slides through the frames
+    // and finds the rows it shares with the tiles before it still in the XCD's L2
+    const int xcd = blockIdx.x & 7;
     const int64_t per = (total + 7) / 8;
-    const int64_t t_end = min<int64_t>(total, (xcd + 1) * per);
+    const int64_t t_begin = xcd * per, t_end = min<int64_t>(total, (xcd + 1) * per);
+    int* const ctr = queue + 32 * xcd;
+    __shared__ int next_tile;
     int cb_loaded = -1;
-    for (int64_t tile = xcd * per + slot; tile < t_end; tile += ng) {
+    auto run_tile = [&](const int64_t tile) __attribute__((always_inline)) {
         const int cb = int(tile / per_cb), tp = int(tile % per_cb);
         if (cb != cb_loaded) {                      // weights of this channel block
             __syncthreads();
@@ -246,7 +264,7 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kWgPerCu)))
         const SampleTiles st = sample_tiles(g);
         const int local = tp - tile_off[n];
         const int c0 = kCB * cb + 8 * vec;
-        if (c0 >= C) continue;
+        if (c0 >= C) return;
         const float* wv = wl + 8 * vec;
 
         if (local < st.ntext) {
@@ -266,7 +284,7 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kWgPerCu)))
                 }
                 Vec8<E>::store(y + tok * C + c0, acc);
             }
-            continue;
+            return;
         }
         if (local >= st.ntext + st.nvis) {
             // ---- tokens past the grid: zeros ----
@@ -275,14 +293,14 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kWgPerCu)))
                 const int m = g.past + (local - st.ntext - st.nvis) * kTextTok + r;
                 if (m < g.nv) Vec8<E>::store(y + (g.base + g.L + m) * C + c0, zero);
             }
-            continue;
+            return;
         }
 
         // ---- visual tile: 32 strips; this thread's strip is 4 columns x 8 channels ----
         const int sidx = (local - st.ntext) * kStrips + (tid >> 3);
         const int per_frame = g.Hn * st.nsw;
         const int f = sidx / per_frame;
-        if (f >= g.Tn) continue;
+        if (f >= g.Tn) return;
         const int j = (sidx - f * per_frame) / st.nsw;
         const int kq = (sidx - f * per_frame - j * st.nsw) * kSW;
         const E* xs = x + (g.base + g.L) * C + c0;  // this sample's grid tokens, this thread's channels
@@ -291,6 +309,9 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kWgPerCu)))
         for (int q = 0; q < kSW; ++q)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[q][e] = 0.f;
+        // the time taps whose frame exists, read in the order of the walk through the frames:
+        // first the frames the tiles started before this one read last, the newest frame last
+        const int na = REV ? min(kt, g.Tn - f) : min(kt, f + 1);
         const bool fast = g.past == g.nv && int64_t(g.Tn) * g.Hn * g.Wn == g.nv &&
                           int64_t(g.nv) * C * int64_t(sizeof(E)) <= kBufLimit;
         if (fast) {
@@ -306,8 +327,8 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kWgPerCu)))
                 const int kk = kq + p - pw;
                 colv[p] = kk >= 0 && kk < g.Wn ? uint32_t(kk * C + c0) * sizeof(E) : kBufLimit;
             }
-            for (int a = 0; a < kt && (REV ? f + a < g.Tn : f - a >= 0); ++a)
-                for (int b = 0; b < kh; ++b) {
+            for (int ai = 0; ai < na; ++ai)
+                for (int b = 0, a = REV ? ai : na - 1 - ai; b < kh; ++b) {
                     const int jj = j + b - ph, fa = REV ? f + a : f - a;
                     const uint32_t roff = jj >= 0 && jj < g.Hn ? uint32_t(fa * g.Hn + jj) * rowb : kBufLimit;
                     typename Vec8<E>::Raw in[kSW + KW - 1];
@@ -334,8 +355,8 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kWgPerCu)))
                     }
                 }
         } else
-        for (int a = 0; a < kt && (REV ? f + a < g.Tn : f - a >= 0); ++a)
-            for (int b = 0; b < kh; ++b) {
+        for (int ai = 0; ai < na; ++ai)
+            for (int b = 0, a = REV ? ai : na - 1 - ai; b < kh; ++b) {
                 const int jj = j + b - ph;
                 if (jj < 0 || jj >= g.Hn) continue;
                 const int row = ((REV ? f + a : f - a) * g.Hn + jj) * g.Wn;   // grid index of column 0
@@ -364,6 +385,17 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kWgPerCu)))
             const int kk = kq + q, m = (f * g.Hn + j) * g.Wn + kk;
             if (kk < g.Wn && m < g.past) Vec8<E>::store(y + (g.base + g.L + m) * C + c0, acc[q]);
         }
+    };
+    if (tid == 0) next_tile = atomicAdd(ctr, 1);
+    __syncthreads();
+    for (int64_t tile = t_begin + next_tile; tile < t_end;) {
+        int claim = 0;
+        if (tid == 0) claim = atomicAdd(ctr, 1);            // the next tile, claimed while this one runs
+        run_tile(tile);
+        __syncthreads();                                    // every thread has read next_tile
+        if (tid == 0) next_tile = claim;
+        __syncthreads();
+        tile = t_begin + next_tile;
     }
 }
 
@@ -372,7 +404,11 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(kWgPerCu)))
 // dw_vis[a][b][d][c] = sum over grid outputs (i, j, k)     x[i-a, j+b-(kh-1)/2, k+d-(kw-1)/2][c] dy[i,j,k][c]
 // with x zero outside the grid. A work unit is (channel block, part of the block's tile
 // list, row group): row group a < kt sums the kh*kw visual taps of time offset a, row group
-// kt the text taps. A thread holds 8 channels and every tap of its group for one strip lane
+// kt the text taps. Part p holds every parts-th tile from tile p, so the units running
+// together cover adjacent tiles: the row groups of a part read the same dy rows at the same
+// time, and the x frame one row group reads is read by the next one a few tiles later, while
+// it is still in the XCD's L2 (with contiguous parts each frame was fetched once per row
+// group, 1.8x the input bytes; now about 1.1x). A thread holds 8 channels and every tap of its group for one strip lane
 // (a visual tile's 32 strips, one per lane); per strip it widens the strip's 4 dy columns
 // once and each x row's kw+3 columns once, then does kw*4*8 FMAs per row. The unit's 32
 // strip lanes are added in LDS in a fixed order and written as one partial per (tap,
@@ -408,7 +444,9 @@ __global__ __launch_bounds__(kCT) void kda_short_conv_dw_kernel(
     const bool text = rg == kt;
     const int a = rg, ph = (kh - 1) / 2, pw = (KW - 1) / 2;
     const int per_cb = tile_off[num_seqs];
-    const int t0 = int(int64_t(per_cb) * p / parts), t1 = int(int64_t(per_cb) * (p + 1) / parts);
+    // part p takes tiles p, p + parts, ... so that the parts running together cover adjacent tiles
+    const int t0 = p, t1 = per_cb, S = parts;
+    auto next_from = [&](int lo) { return lo + ((p - lo) % S + S) % S; };
     // lanes past the last channel read channels 0..7 of the same tokens and write nothing, so
     // every lane runs the same code
     const bool cok = kCB * cb + 8 * cv < C;                 // C is a multiple of 8: all 8 channels exist
@@ -440,12 +478,12 @@ __global__ __launch_bounds__(kCT) void kda_short_conv_dw_kernel(
     }
     if (text) {
         int n = n0;
-        for (int tp = t0; tp < t1; ++tp) {
+        for (int tp = t0; tp < t1; tp += S) {
             while (tile_off[n + 1] <= tp) ++n;              // next sample with tiles
             const SampleGeom g = sample_geom(cu, text_len, grid, n, T);
             const SampleTiles st = sample_tiles(g);
             const int local = tp - tile_off[n];
-            if (local >= st.ntext) { tp = tile_off[n + 1] - 1; continue; }
+            if (local >= st.ntext) { tp = next_from(tile_off[n + 1]) - S; continue; }
             for (int r = sl; r < kTextTok; r += kLanes) {
                 const int rel = local * kTextTok + r;
                 if (rel >= g.L) break;
@@ -467,7 +505,7 @@ __global__ __launch_bounds__(kCT) void kda_short_conv_dw_kernel(
             const SampleGeom g = sample_geom(cu, text_len, grid, n, T);
             const SampleTiles st = sample_tiles(g);
             const int v_lo = max(t0, tile_off[n] + st.ntext), v_hi = min(t1, tile_off[n] + st.ntext + st.nvis);
-            for (int tp = v_lo; tp < v_hi; ++tp) {
+            for (int tp = next_from(v_lo); tp < v_hi; tp += S) {
                 const int local = tp - tile_off[n];
                 const int sidx = (local - st.ntext) * kStrips + sl;
                 const int per_frame = g.Hn * st.nsw;
@@ -526,13 +564,13 @@ __global__ __launch_bounds__(kCT) void kda_short_conv_dw_kernel(
         }
     } else {
         int n = n0;
-        for (int tp = t0; tp < t1; ++tp) {
+        for (int tp = t0; tp < t1; tp += S) {
             while (tile_off[n + 1] <= tp) ++n;
             const SampleGeom g = sample_geom(cu, text_len, grid, n, T);
             const SampleTiles st = sample_tiles(g);
             const int local = tp - tile_off[n];
-            if (local < st.ntext) { tp = tile_off[n] + st.ntext - 1; continue; }
-            if (local >= st.ntext + st.nvis) { tp = tile_off[n + 1] - 1; continue; }
+            if (local < st.ntext) { tp = next_from(tile_off[n] + st.ntext) - S; continue; }
+            if (local >= st.ntext + st.nvis) { tp = next_from(tile_off[n + 1]) - S; continue; }
             const int sidx = (local - st.ntext) * kStrips + sl;
             const int per_frame = g.Hn * st.nsw;
             const int f = sidx / per_frame;
@@ -614,22 +652,23 @@ __global__ __launch_bounds__(256) void kda_short_conv_dw_reduce_kernel(const flo
 }
 
 template <typename E, int KW, bool REV>
-void launch_conv_kw(const ConvArgs& a, const void* in, void* out, int32_t* tile_off, size_t smem, int blocks,
-                    int ncb)
+void launch_conv_kw(const ConvArgs& a, const void* in, void* out, int32_t* tile_off, int* queue, size_t smem,
+                    int blocks, int ncb)
 {
     hipLaunchKernelGGL((kda_short_conv_kernel<E, KW, REV>), dim3(blocks), dim3(kCT), smem, a.stream,
                        static_cast<const E*>(in), a.w_text, a.w_vis, a.cu_seqlens, a.text_len, a.grid, tile_off,
-                       static_cast<E*>(out), a.total_tokens, a.num_seqs, a.channels, a.k_text, a.k_t, a.k_h, ncb);
+                       queue, static_cast<E*>(out), a.total_tokens, a.num_seqs, a.channels, a.k_text, a.k_t, a.k_h, ncb);
 }
 
 // the kernel width is a template argument: it sizes the strip's input registers
 template <typename E, bool REV>
-void launch_conv(const ConvArgs& a, const void* in, void* out, int32_t* tile_off, size_t smem, int blocks, int ncb)
+void launch_conv(const ConvArgs& a, const void* in, void* out, int32_t* tile_off, int* queue, size_t smem, int blocks,
+                 int ncb)
 {
     switch (a.k_w) {
-    case 1: launch_conv_kw<E, 1, REV>(a, in, out, tile_off, smem, blocks, ncb); break;
-    case 3: launch_conv_kw<E, 3, REV>(a, in, out, tile_off, smem, blocks, ncb); break;
-    default: launch_conv_kw<E, 5, REV>(a, in, out, tile_off, smem, blocks, ncb); break;
+    case 1: launch_conv_kw<E, 1, REV>(a, in, out, tile_off, queue, smem, blocks, ncb); break;
+    case 3: launch_conv_kw<E, 3, REV>(a, in, out, tile_off, queue, smem, blocks, ncb); break;
+    default: launch_conv_kw<E, 5, REV>(a, in, out, tile_off, queue, smem, blocks, ncb); break;
     }
 }
 
@@ -665,7 +704,8 @@ void launch_dw(const ConvBwdArgs& a, int32_t* tile_off, float* partial, int bloc
 
 }  // namespace
 
-size_t conv_workspace_bytes(int32_t num_seqs) { return ((size_t(num_seqs) + 1) * 4 + 255) & ~size_t(255); }
+static size_t conv_table_bytes(int32_t num_seqs) { return ((size_t(num_seqs) + 1) * 4 + 255) & ~size_t(255); }
+size_t conv_workspace_bytes(int32_t num_seqs) { return conv_table_bytes(num_seqs) + kQueueBytes; }
 
 size_t conv_bwd_workspace_bytes(int32_t num_seqs, int32_t channels, int32_t k_text, int32_t k_t, int32_t k_h,
                                 int32_t k_w)
@@ -681,17 +721,18 @@ hipError_t launch_short_conv(const ConvArgs& a, void* workspace, TimingHook* th)
     const int ncb = (a.channels + kCB - 1) / kCB;
     int32_t* tile_off = static_cast<int32_t*>(workspace);
     if (th) th->begin("conv_plan", a.stream);
+    int* queue = reinterpret_cast<int*>(static_cast<char*>(workspace) + conv_table_bytes(a.num_seqs));
     hipLaunchKernelGGL(kda_conv_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, a.text_len, a.grid,
-                       tile_off, a.num_seqs, a.total_tokens);
+                       tile_off, queue, a.num_seqs, a.total_tokens);
     if (th) th->end(a.stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int blocks = 256 * kWgPerCu;              // every CU, kWgPerCu resident workgroups each
     if (th) th->begin("conv", a.stream);
     if (a.dtype_bf16)
-        launch_conv<uint16_t, false>(a, a.x, a.y, tile_off, smem, blocks, ncb);
+        launch_conv<uint16_t, false>(a, a.x, a.y, tile_off, queue, smem, blocks, ncb);
     else
-        launch_conv<float, false>(a, a.x, a.y, tile_off, smem, blocks, ncb);
+        launch_conv<float, false>(a, a.x, a.y, tile_off, queue, smem, blocks, ncb);
     if (th) th->end(a.stream);
     return hipGetLastError();
 }
@@ -712,16 +753,17 @@ hipError_t launch_short_conv_backward(const ConvBwdArgs& b, void* workspace, Tim
     int32_t* tile_off = static_cast<int32_t*>(workspace);
     float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + conv_workspace_bytes(a.num_seqs));
     if (th) th->begin("conv_bwd_plan", a.stream);
+    int* queue = reinterpret_cast<int*>(static_cast<char*>(workspace) + conv_table_bytes(a.num_seqs));
     hipLaunchKernelGGL(kda_conv_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, a.text_len, a.grid,
-                       tile_off, a.num_seqs, a.total_tokens);
+                       tile_off, queue, a.num_seqs, a.total_tokens);
     if (th) th->end(a.stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (th) th->begin("conv_dx", a.stream);
     if (a.dtype_bf16)
-        launch_conv<uint16_t, true>(a, b.dy, b.dx, tile_off, smem, 256 * kWgPerCu, ncb);
+        launch_conv<uint16_t, true>(a, b.dy, b.dx, tile_off, queue, smem, 256 * kWgPerCu, ncb);
     else
-        launch_conv<float, true>(a, b.dy, b.dx, tile_off, smem, 256 * kWgPerCu, ncb);
+        launch_conv<float, true>(a, b.dy, b.dx, tile_off, queue, smem, 256 * kWgPerCu, ncb);
     if (th) th->end(a.stream);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int parts = dw_parts(a.channels, a.k_t);

@@ -257,9 +257,10 @@ size_t kda_backward_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int3
  *                 only inside the sample: grid positions past its last token read as zero,
  *                 and tokens past T*H*W (or after the text when T, H or W is 0) get zeros
  *   channels    : a multiple of 8; k_text 1..8, k_t 1..4, k_h and k_w odd in 1..5
- * Arithmetic is fp32; y is rounded to nearest-even for bf16. A workspace of (num_seqs + 1)
- * int32 (the tile table) comes from the stream-ordered pool as for kda_forward. Execution
- * and errors as kda_forward; the timing hook names the kernels "conv_plan" and "conv".
+ * Arithmetic is fp32; y is rounded to nearest-even for bf16. A workspace of the tile table
+ * ((num_seqs + 1) int32, rounded up to 256 bytes) and eight tile counters (1 KiB) comes from
+ * the stream-ordered pool as for kda_forward. Execution and errors as kda_forward; the
+ * timing hook names the kernels "conv_plan" and "conv".
  */
 kda_status kda_short_conv(const void *x, const float *w_text, const float *w_vis,
                           const int32_t *cu_seqlens, const int32_t *text_len, const int32_t *grid,
@@ -289,12 +290,12 @@ kda_status kda_short_conv(const void *x, const float *w_text, const float *w_vis
  * and dx is not touched.
  * Arithmetic is fp32; dx is rounded to nearest-even for bf16. dx comes from the forward's
  * kernel with the taps mirrored and the time and text directions reversed; the weight sums
- * are formed per (channel block, slice of the tile list) and the slices then added in a
- * fixed order, so the result is the same bit for bit from run to run. A workspace of the
- * tile table plus parts * (k_text + k_t*k_h*k_w) * channels fp32 partial sums (parts is
- * about 2048 / (ceil(channels / 64) * (k_t + 1)), at least 1) comes from the stream-ordered
- * pool as for kda_forward. Execution and errors as kda_forward; the timing hook names the
- * kernels "conv_bwd_plan", "conv_dx", "conv_dw" and "conv_dw_reduce".
+ * are formed per (channel block, part of the tile list: every parts-th tile) and the parts
+ * then added in a fixed order, so the result is the same bit for bit from run to run. A
+ * workspace of the forward's (table and counters) plus parts * (k_text + k_t*k_h*k_w) *
+ * channels fp32 partial sums (parts is about 2048 / (ceil(channels / 64) * (k_t + 1)), at
+ * least 1) comes from the stream-ordered pool as for kda_forward. Execution and errors as kda_forward; the timing
+ * hook names the kernels "conv_bwd_plan", "conv_dx", "conv_dw" and "conv_dw_reduce".
  */
 kda_status kda_short_conv_backward(const void *x, const float *w_text, const float *w_vis,
                                    const int32_t *cu_seqlens, const int32_t *text_len,

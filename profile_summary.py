@@ -48,7 +48,9 @@ def counters(db: str, counter: str):
 
 
 def _is_copy(name: str) -> bool:
-    return "copyBuffer" in name or "copy_kernel" in name
+    # the runtime's device copy and the probe library's copy kernel; not torch's dtype
+    # conversions, whose names also hold "copy_kernel" and which read other byte counts
+    return "copyBuffer" in name or "bw_copy_kernel" in name
 
 
 def traffic(fetch_db: str, write_db: str, calib_bytes: int, kernel: str = "kda_fwd_kernel"):
@@ -96,6 +98,20 @@ def mfma(db: str, trace_db: str, kernel: str):
     return rec
 
 
+def counter_means(db: str, kernel: str):
+    """Mean per dispatch of every counter collected in `db`, over the dispatches of `kernel`."""
+    con = _con(db)
+    names = [r[0] for r in con.execute("select distinct counter_name from counters_collection")]
+    out = {}
+    for name in names:
+        vals = [v for _, n, _, v, _ in counters(db, name) if kernel in n]
+        if vals:
+            out[name] = statistics.mean(vals)
+    out["dispatches"] = max((len([1 for _, n, _, _, _ in counters(db, nm) if kernel in n]) for nm in names),
+                            default=0)
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -113,7 +129,13 @@ def main(argv=None):
     m.add_argument("db")
     m.add_argument("--trace", required=True)
     m.add_argument("--kernel", default="kda_wy_chain_kernel")
+    k = sub.add_parser("counters")
+    k.add_argument("db")
+    k.add_argument("--kernel", required=True)
     a = ap.parse_args(argv)
+    if a.cmd == "counters":
+        print(json.dumps({"kernel": a.kernel, **counter_means(a.db, a.kernel)}, indent=1))
+        return 0
     if a.cmd == "mfma":
         print(json.dumps(mfma(a.db, a.trace, a.kernel), indent=1))
         return 0
