@@ -532,51 +532,56 @@ __global__ __launch_bounds__(kBT) void kda_bwd_prep_kernel(
 }
 
 // The chunk operands of the gradient kernel, read back from the prep's record into the
-// LDS layout chunk_operands() builds (the same values, so the same gradients): every
-// 16-byte load is issued before the first LDS write. Ends with a barrier.
-template <int DK>
-__device__ __forceinline__ void record_operands(const ChunkLds& L, const float* __restrict__ rec)
-{
+// LDS layout chunk_operands() builds (the same values, so the same gradients). load()
+// issues every 16-byte load into registers; put() writes them to LDS (the caller then
+// takes a barrier), so that loads issued between the two stay in flight.
+template <int DK> struct RecordRegs {
     using R = BRec<DK>;
-    constexpr int LK = DK + 4;
-    constexpr int NK = kBC * DK / 4 / kBT;          // f32x4 per thread per [C][DK] array
+    static constexpr int LK = DK + 4;
+    static constexpr int NK = kBC * DK / 4 / kBT;   // f32x4 per thread per [C][DK] array
+    static constexpr int NG = DK / 4, NB = kBC / 4;
     static_assert(kBC * kBC / 4 == kBT, "one f32x4 of each [C][C] array per thread");
-    const int tid = threadIdx.x;
-    const f32x4* r4 = reinterpret_cast<const f32x4*>(rec);
-    f32x4 kh[NK], kc[NK], qh[NK];
+    f32x4 kh[NK], kc[NK], qh[NK], t, p, m, small;   // small: gamma, b, 1/|q|, 1/|k|
+    __device__ __forceinline__ void load(const float* __restrict__ rec) {
+        const int tid = threadIdx.x;
+        const f32x4* r4 = reinterpret_cast<const f32x4*>(rec);
 #pragma unroll
-    for (int j = 0; j < NK; ++j) {
-        const int i = tid + j * kBT;
-        kh[j] = r4[R::KH / 4 + i];
-        kc[j] = r4[R::KC / 4 + i];
-        qh[j] = r4[R::QH / 4 + i];
+        for (int j = 0; j < NK; ++j) {
+            const int i = tid + j * kBT;
+            kh[j] = r4[R::KH / 4 + i];
+            kc[j] = r4[R::KC / 4 + i];
+            qh[j] = r4[R::QH / 4 + i];
+        }
+        t = r4[R::T / 4 + tid];
+        p = r4[R::P / 4 + tid];
+        m = r4[R::M / 4 + tid];
+        small = zero4();
+        if (tid < NG) small = r4[R::GAM / 4 + tid];
+        else if (tid < NG + NB) small = r4[R::BETA / 4 + tid - NG];
+        else if (tid < NG + 2 * NB) small = r4[R::QINV / 4 + tid - NG - NB];
+        else if (tid < NG + 3 * NB) small = r4[R::KINV / 4 + tid - NG - 2 * NB];
     }
-    const f32x4 t = r4[R::T / 4 + tid], p = r4[R::P / 4 + tid], m = r4[R::M / 4 + tid];
-    f32x4 small = zero4();                          // gamma, b, 1/|q|, 1/|k|
-    constexpr int NG = DK / 4, NB = kBC / 4;
-    if (tid < NG) small = r4[R::GAM / 4 + tid];
-    else if (tid < NG + NB) small = r4[R::BETA / 4 + tid - NG];
-    else if (tid < NG + 2 * NB) small = r4[R::QINV / 4 + tid - NG - NB];
-    else if (tid < NG + 3 * NB) small = r4[R::KINV / 4 + tid - NG - 2 * NB];
+    __device__ __forceinline__ void put(const ChunkLds& L) const {
+        const int tid = threadIdx.x;
 #pragma unroll
-    for (int j = 0; j < NK; ++j) {
-        const int e = 4 * (tid + j * kBT), row = e / DK, col = e % DK;
-        *reinterpret_cast<f32x4*>(L.kh + row * LK + col) = kh[j];
-        *reinterpret_cast<f32x4*>(L.kc + row * LK + col) = kc[j];
-        *reinterpret_cast<f32x4*>(L.qh + row * LK + col) = qh[j];
+        for (int j = 0; j < NK; ++j) {
+            const int e = 4 * (tid + j * kBT), row = e / DK, col = e % DK;
+            *reinterpret_cast<f32x4*>(L.kh + row * LK + col) = kh[j];
+            *reinterpret_cast<f32x4*>(L.kc + row * LK + col) = kc[j];
+            *reinterpret_cast<f32x4*>(L.qh + row * LK + col) = qh[j];
+        }
+        {
+            const int e = 4 * tid, row = e / kBC, col = e % kBC;
+            *reinterpret_cast<f32x4*>(L.t + row * kLC + col) = t;
+            *reinterpret_cast<f32x4*>(L.p + row * kLC + col) = p;
+            *reinterpret_cast<f32x4*>(L.m + row * kLC + col) = m;
+        }
+        if (tid < NG) *reinterpret_cast<f32x4*>(L.gam + 4 * tid) = small;
+        else if (tid < NG + NB) *reinterpret_cast<f32x4*>(L.beta + 4 * (tid - NG)) = small;
+        else if (tid < NG + 2 * NB) *reinterpret_cast<f32x4*>(L.qinv + 4 * (tid - NG - NB)) = small;
+        else if (tid < NG + 3 * NB) *reinterpret_cast<f32x4*>(L.kinv + 4 * (tid - NG - 2 * NB)) = small;
     }
-    {
-        const int e = 4 * tid, row = e / kBC, col = e % kBC;
-        *reinterpret_cast<f32x4*>(L.t + row * kLC + col) = t;
-        *reinterpret_cast<f32x4*>(L.p + row * kLC + col) = p;
-        *reinterpret_cast<f32x4*>(L.m + row * kLC + col) = m;
-    }
-    if (tid < NG) *reinterpret_cast<f32x4*>(L.gam + 4 * tid) = small;
-    else if (tid < NG + NB) *reinterpret_cast<f32x4*>(L.beta + 4 * (tid - NG)) = small;
-    else if (tid < NG + 2 * NB) *reinterpret_cast<f32x4*>(L.qinv + 4 * (tid - NG - NB)) = small;
-    else if (tid < NG + 3 * NB) *reinterpret_cast<f32x4*>(L.kinv + 4 * (tid - NG - 2 * NB)) = small;
-    __syncthreads();
-}
+};
 
 // ---------------------------------------------------------------------------
 // chains: one workgroup per (sample, head, 64-column value tile); wave w holds columns
@@ -1137,16 +1142,23 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
     const float* Sg = s_in + (int64_t(h) * max_chunks + c) * DK * DV;
     const float* dSg = ds_out + (int64_t(h) * max_chunks + c) * DK * DV;
 
-    // ---- operands, V and dO (every load issued before the first wait) ----
+    // ---- operands, V and dO, S and dS' (every load issued before the first wait) ----
     RowPieces<E, DV> pv, pd;
     pv.load(v, t0, nrow, H, h, 0, DV);
     pd.load(d_out, t0, nrow, H, h, 0, DV);
-    StateBlock<DV> sb;
-    sb.load(Sg, 0);
+    RecordRegs<DK> rr;
+    rr.load(rec_ws + (int64_t(h) * max_chunks + c) * BRec<DK>::TOTAL);
+    // the state entering the chunk and the gradient of the one leaving it stay in registers
+    // from here to the last product that reads them, so each is read from memory once
+    StateBlock<DV> sS[NKB], sD[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sS[kb].load(Sg, kb);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sD[kb].load(dSg, kb);
     const ChunkLds L{sm.qh, sm.kh, sm.kc, sm.m, sm.t, sm.p, sm.gam, sm.beta, sm.qinv, sm.kinv};
-    record_operands<DK>(L, rec_ws + (int64_t(h) * max_chunks + c) * BRec<DK>::TOTAL);   // ends with a barrier
+    rr.put(L);
     pv.put(sm.x, LV, nrow);
-    pd.put(sm.dout, LV, nrow);
+    pd.put(sm.dout, LV, nrow);      // the first barrier of the X pass orders these writes
 
     // a [C][DV]-shaped result: tile index wave + 4 mm
     auto xtile = [&](int mm, int& ti, int& tj) {
@@ -1167,10 +1179,8 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
         for (int mm = 0; mm < XPW; ++mm) ax[mm] = zero4();
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            sb.put(sm.sblk, LV);
+            sS[kb].put(sm.sblk, LV);
             __syncthreads();
-            if (kb + 1 < NKB) sb.load(Sg, kb + 1);
-            else sb.load(dSg, 0);                        // first block of the next pass
 #pragma unroll
             for (int mm = 0; mm < XPW; ++mm) {
                 int ti, tj;
@@ -1227,10 +1237,8 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
         }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            sb.put(sm.sblk, LV);
+            sD[kb].put(sm.sblk, LV);
             __syncthreads();
-            if (kb + 1 < NKB) sb.load(dSg, kb + 1);
-            else sb.load(Sg, 0);                         // first block of the last pass
 #pragma unroll
             for (int mm = 0; mm < XPW; ++mm) {
                 int ti, tj;
@@ -1390,15 +1398,13 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
     }
     // ---- state parts: dQh += dO S^T, dKh -= dX S^T;  dgamma += rowsum(dS' S) ----
     {
-        StateBlock<DV> db;                              // the same rows of dS'
-        db.load(dSg, 0);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            sb.put(sm.sblk, LV);
+            sS[kb].put(sm.sblk, LV);
             // dgamma: this thread's pieces of rows of S and dS' (the same positions)
 #pragma unroll
             for (int j = 0; j < StateBlock<DV>::NP; ++j) {
-                const f32x4 a = sb.v[j], b = db.v[j];
+                const f32x4 a = sS[kb].v[j], b = sD[kb].v[j];
                 float part = a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
 #pragma unroll
                 for (int sh = 1; sh < StateBlock<DV>::PR; sh <<= 1) part += __shfl_xor(part, sh);
@@ -1406,10 +1412,6 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
                 if (pc % StateBlock<DV>::PR == 0) sm.dgam_p[2][32 * kb + pc / StateBlock<DV>::PR] = part;
             }
             __syncthreads();
-            if (kb + 1 < NKB) {
-                sb.load(Sg, kb + 1);
-                db.load(dSg, kb + 1);
-            }
             int ti, tj;
             block_tile(kb, ti, tj);
             f32x4 aq = zero4(), ak = zero4();
