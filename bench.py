@@ -2,7 +2,7 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload clip30s|clip5s|image4|packed8|tiny]
                 [--no-backward] [--no-conv] [--no-shard] [--no-cpu-baseline] [--no-other-configs]
-                [--copy-calib-mib M]
+                [--no-state-step] [--copy-calib-mib M]
 
 A step is one kda_forward call over the whole workload (every stage of the scan
 runs inside it). The default workload is the 30-second clip: one sample of 189,272
@@ -22,7 +22,8 @@ over the algorithmic bytes.
 The same line carries the other configurations' forward steps, the backward, the
 short convolution and its backward, one GPU's share under a head or sequence
 split, the step replayed from a HIP graph, single steps after a cache flush, the
-measured ceilings and the oracle's CPU rate. Prints one JSON line.
+serial state step of each scan kernel (state_step), the measured ceilings and the
+oracle's CPU rate. Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -628,6 +629,66 @@ def shard_bench(args, dev):
     return out
 
 
+def state_step(args, dev):
+    """The serial state step of each scan kernel: packs of 256 samples x 1 head (one (sample,
+    head) unit per CU, so no sequence split) at two sample lengths; a kernel's step is its
+    mean launch time over the chunks one unit walks. Every CU runs a unit, so the step
+    includes its share of HBM."""
+    import torch
+    from delta_rule_recurrent_kda_amd import inputs, kda
+    lens = (2048, 8192)
+    # (timing name, scan variant or "bwd", tokens per step)
+    kinds = (("fused", None, 32), ("chain", "wy", 64), ("bwd_state", "bwd", 32), ("bwd_dstate", "bwd", 32))
+    ms = {name: [] for name, _, _ in kinds}
+    for L in lens:
+        spec = inputs.custom([L] * 256, heads=1, d=128, seed=31)
+        a = inputs.generate(spec)
+        t = device_tensors(spec, a, dev)
+        cu = torch.from_numpy(a["cu_seqlens"]).to(dev)
+        for variant in (None, "wy"):
+            if variant:
+                os.environ["KDA_SCAN_VARIANT"] = variant
+            try:
+                _, kern, _ = forward_timing(spec, t, cu, dev, 5, 2)
+            finally:
+                os.environ.pop("KDA_SCAN_VARIANT", None)
+            for name, var, _ in kinds:
+                if var == variant and name in kern:
+                    ms[name].append(kern[name]["ms_avg"])
+        g = torch.Generator(device=dev)
+        g.manual_seed(77)
+        d_out = torch.randn(t["v"].shape, device=dev, generator=g).to(t["v"].dtype)
+        for _ in range(2):
+            kda.backward(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], cu, d_out, with_initial_grad=False)
+        torch.cuda.synchronize()
+        for name in BWD_KERNELS:
+            kda.timing_read(name)
+        kda.timing_enable(True)
+        for _ in range(3):
+            kda.backward(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], cu, d_out, with_initial_grad=False)
+        torch.cuda.synchronize()
+        kda.timing_enable(False)
+        for name in ("bwd_state", "bwd_dstate"):
+            n, tot = kda.timing_read(name)
+            if n:
+                ms[name].append(tot / n)
+        del t, d_out
+        torch.cuda.empty_cache()
+    out = {}
+    for name, _, tok in kinds:
+        if len(ms[name]) != len(lens):
+            continue
+        out[name] = {"tokens_per_step": tok,
+                     "us_per_step": {str(L): m * 1e3 / (L // tok) for L, m in zip(lens, ms[name])},
+                     "launch_ms": {str(L): m for L, m in zip(lens, ms[name])}}
+    out["note"] = ("256 samples x 1 head, d = 128, bf16, samples of 2,048 and 8,192 tokens (one unit per CU, no "
+                   "sequence split); us_per_step = a kernel's mean launch time over the steps one unit walks, fill "
+                   "and drain included. fused: the fused scan (32-token chunks, 8 waves per CU); chain: the WY "
+                   "scan's chain (64-token chunks); bwd_state, bwd_dstate: the backward's two chains per 64-column "
+                   "tile (32-token chunks), which run side by side on two streams and share the CUs")
+    return out
+
+
 def device_tensors(spec, a, dev):
     import torch
     t = {}
@@ -717,6 +778,7 @@ def main():
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-shard", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true")
+    ap.add_argument("--no-state-step", action="store_true")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after timing, run 3 plain device copies of this many MiB (for scaling "
                          "HBM byte counters)")
@@ -801,6 +863,8 @@ def main():
         rec["short_conv"] = conv_bench(args, spec, dev)
     if not args.no_shard:
         rec["shard"] = shard_bench(args, dev)
+    if not args.no_state_step:
+        rec["state_step"] = state_step(args, dev)
     if args.copy_calib_mib:
         n = args.copy_calib_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

@@ -30,10 +30,10 @@
 // Operand layouts are chosen so that every hand-over is a lane-ordered LDS store and load
 // and every transpose is an exact product with the identity (bf16 values).
 //
-// The inverse of a diagonal block (16x16, strictly lower N): (I + N)^-1 = (I - N)(I + N^2)
-// (I + N^4)(I + N^8) exactly (N^16 = 0), with every product on bf16 MFMA from hi/lo bf16
-// pairs of its fp32 operands (hi*hi + lo*hi + hi*lo, about 16 significant bits), in the
-// transposed form M = N^T so that the result is T^T, the operand layout of T.
+// The inverse of a diagonal block (16x16, I + A with A strictly lower) is formed in fp32 by
+// elimination: lane (r, g) holds row r of A and T[r][4g..4g+3]; for k = 0..14 row k of T
+// is final, is broadcast along the 16 lanes of each row by DPP, and every row r > k takes
+// -A[r][k] T[k][.] (15 steps of 4 broadcasts and 4 FMAs).
 //
 // Long samples (few (sample, head) units for the CUs): the sample is cut into segments.
 //   pass 1  per segment that is not its sample's last: the state reached from zero
@@ -147,27 +147,6 @@ __device__ __forceinline__ void elim_rows(float (&t)[4], const float (&ar)[16], 
 // Orders one wave's LDS writes before its later reads of other lanes' data: the LDS
 // executes a wave's instructions in order; the clobber keeps the compiler from moving them.
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-// a 16x16 fp32 accumulator tile as hi/lo bf16 fragments
-struct HL {
-    Frag16 h, l;
-};
-__device__ __forceinline__ HL hl(const f32x4& x) {
-    HL o;
-    o.h.u = pack4(x[0], x[1], x[2], x[3]);
-    const f32x4 r = f32x4{x[0] - __uint_as_float(bfbits_lo(o.h.u.x)), x[1] - __uint_as_float(bfbits_hi(o.h.u.x)),
-                          x[2] - __uint_as_float(bfbits_lo(o.h.u.y)), x[3] - __uint_as_float(bfbits_hi(o.h.u.y))};
-    o.l.u = pack4(r[0], r[1], r[2], r[3]);
-    return o;
-}
-__device__ __forceinline__ void ready(HL& a) { mfma_ready(a.h.u, a.l.u); }
-__device__ __forceinline__ void ready(HL& a, HL& b) { mfma_ready(a.h.u, a.l.u, b.h.u, b.l.u); }
-// c + A B with A and B given by hi/lo fragments (the lo*lo term is left out)
-__device__ __forceinline__ f32x4 mmhl(const HL& a, const HL& b, f32x4 c) {
-    c = EL::mma16(a.l, b.h, c);
-    c = EL::mma16(a.h, b.l, c);
-    return EL::mma16(a.h, b.h, c);
-}
 
 // clamped sample bounds, so that malformed offsets never address outside the tokens
 __device__ __forceinline__ void bounds(const int32_t* cu, int n, int64_t T, int64_t& s0, int64_t& s1) {
