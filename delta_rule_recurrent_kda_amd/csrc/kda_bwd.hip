@@ -1637,11 +1637,13 @@ hipError_t launch_bwd_t(const BwdArgs& a, void* workspace, TimingHook* th)
         if (th) th->end(st);
         return hipGetLastError();
     };
-    // The two chains are independent (the state-gradient chain reads the records and dO,
-    // never S). Fork: the state chain on an auxiliary stream once the prep is done; the
-    // state-gradient chain, the longer of the two, goes first on the caller's stream so
-    // that it takes the CUs first, and the state chain gets the CUs its shorter samples
-    // free.
+    // Without the sequence split the two chains are independent (the state-gradient chain
+    // reads the records and dO, never S). Fork: the state chain on an auxiliary stream once
+    // the prep is done; the state-gradient chain, the longer of the two, goes first on the
+    // caller's stream so that it takes the CUs first, and the state chain gets the CUs its
+    // shorter samples free. With the split, the state-gradient chain's second pass reads the
+    // transposed segment transitions that the state chain's first pass writes: that pass is
+    // launched first, and the caller's stream waits for it before the second pass.
     AuxStream* ss = nullptr;
     if ((e = aux_stream(0, ss)) != hipSuccess) return e;
     if ((e = aux_fork(a.stream, ss)) != hipSuccess) return e;
@@ -1655,12 +1657,14 @@ hipError_t launch_bwd_t(const BwdArgs& a, void* workspace, TimingHook* th)
                 return err;
             return launch_state(kda_bwd_state_kernel<E, DK, DV, 0>, DV / 64, "bwd_state", ss->stream);
         }
-        if ((err = launch_dstate(kda_bwd_dstate_kernel<E, DK, DV, 1>, "bwd_dstate_seg", a.stream)) != hipSuccess)
-            return err;
-        if ((err = launch_dstate(kda_bwd_dstate_kernel<E, DK, DV, 2>, "bwd_dstate", a.stream)) != hipSuccess)
-            return err;
         if ((err = launch_state(kda_bwd_state_kernel<E, DK, DV, 1>, DV / 64 + DK / 64, "bwd_state_seg",
                                 ss->stream)) != hipSuccess)
+            return err;
+        if ((err = launch_dstate(kda_bwd_dstate_kernel<E, DK, DV, 1>, "bwd_dstate_seg", a.stream)) != hipSuccess)
+            return err;
+        // Phi^T (phi_t) is complete once the state chain's first pass is
+        if ((err = aux_join(a.stream, ss)) != hipSuccess) return err;
+        if ((err = launch_dstate(kda_bwd_dstate_kernel<E, DK, DV, 2>, "bwd_dstate", a.stream)) != hipSuccess)
             return err;
         return launch_state(kda_bwd_state_kernel<E, DK, DV, 2>, DV / 64, "bwd_state", ss->stream);
     };

@@ -156,6 +156,25 @@ def test_backward_vs_oracle(case):
     _compare(spec, got, ref, f"backward {name}")
 
 
+def test_backward_split_reads_this_calls_transitions():
+    """With the chains split into segments, the state-gradient chain's second pass reads the
+    transposed segment transitions that the state chain's first pass writes on the other
+    stream. Without decay and with a small beta a segment's transition is far from zero (about
+    0.85 of the identity over 2,048 tokens), so a transition left in the workspace by an
+    earlier call would show in every gradient of the earlier segments: a call on the same
+    shapes with the drawn beta (whose transitions have a norm under 0.02) runs first."""
+    spec = inputs.KdaSpec("bwd_split_phi", (6000,), 1, 128, 128, "bf16", (0.0, 0.0), 7474)
+    gu.log("case backward split: segment transitions of this call (three segments, no decay, small beta)")
+    a = inputs.generate(spec)
+    do, dfs, s0 = _draw_grads(spec, 75)
+    _run(spec, a, do, dfs, s0, False)
+    b = dict(a)
+    b["beta"] = inputs.f64_to_bf16_bits(0.02 * inputs.to_f64(a["beta"], spec.dtype))
+    got = _run(spec, b, do, dfs, s0, False)
+    ref = _oracle(spec, b, do, dfs, s0, False)
+    _compare(spec, got, ref, "backward split, transitions of this call")
+
+
 def _sampled(spec, heads, seed):
     """The full-size workload on the GPU (all heads), the oracle on the listed heads."""
     a = inputs.generate(spec)
