@@ -120,6 +120,35 @@ __device__ __forceinline__ BF2 bf_row(const float* a, int ld, int row, int k0, i
     return bf_split(f);
 }
 
+// ... one bf16 per value, for values that are bf16 already (dO of bf16 data: exact)
+__device__ __forceinline__ BF bf_row1(const float* a, int ld, int row, int k0, int g) {
+    const float4 x = *reinterpret_cast<const float4*>(a + row * ld + k0 + 4 * g);
+    const float4 y = *reinterpret_cast<const float4*>(a + row * ld + k0 + 16 + 4 * g);
+    const float f[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+    return bf_pack(f);
+}
+// acc + sum over the W columns j of a[ra][j] * b[rb][j] ([*][ld] fp32 LDS arrays, rows ra
+// and rb as the lane's A row and B column): hi/lo bf16 products, three terms, or two when
+// a holds bf16 values (EXACT_A)
+template <int W, bool EXACT_A>
+__device__ __forceinline__ f32x4 rowdot(const float* a, int ra, const float* b, int rb, int ld, int g, f32x4 acc) {
+#pragma unroll
+    for (int j0 = 0; j0 < W; j0 += 32) {
+        BF2 y = bf_row(b, ld, rb, j0, g);
+        if constexpr (EXACT_A) {
+            BF x = bf_row1(a, ld, ra, j0, g);
+            mfma_ready(x.u);
+            ready(y);
+            acc = mmab(x, y.h, mmab(x, y.l, acc));
+        } else {
+            BF2 x = bf_row(a, ld, ra, j0, g);
+            ready(x, y);
+            acc = mm3(x, y, acc);
+        }
+    }
+    return acc;
+}
+
 template <typename E> __device__ __forceinline__ float ldf(const E* p);
 template <> __device__ __forceinline__ float ldf<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float ldf<uint16_t>(const uint16_t* p) { return bf2f(*p); }
@@ -1128,6 +1157,7 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
     constexpr int KPW = NCT / 2;            // [C][DK] tiles per wave
     constexpr int J4 = DK / 64;             // j' range of the owned tiles
     constexpr int NKB = DK / 32;            // 32-row blocks of a state matrix
+    constexpr bool kBf = sizeof(E) == 2;    // bf16 data: the row-by-row products on hi/lo bf16 MFMA
     extern __shared__ __align__(16) unsigned char smem_raw[];
     S_& sm = *reinterpret_cast<S_*>(smem_raw);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
@@ -1252,9 +1282,13 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
             int ti, tj;
             block_tile(kb, ti, tj);
             f32x4 acc = zero4();
+            if constexpr (kBf) {
+                acc = rowdot<DV, false>(sm.vn, 16 * ti + r, sm.sblk, 16 * (tj - 2 * kb) + r, LV, g, acc);
+            } else {
 #pragma unroll 8
-            for (int j0 = 0; j0 < DV; j0 += 4)
-                acc = mma4(sm.vn[(16 * ti + r) * LV + j0 + g], sm.sblk[(16 * (tj - 2 * kb) + r) * LV + j0 + g], acc);
+                for (int j0 = 0; j0 < DV; j0 += 4)
+                    acc = mma4(sm.vn[(16 * ti + r) * LV + j0 + g], sm.sblk[(16 * (tj - 2 * kb) + r) * LV + j0 + g], acc);
+            }
             const int cc = 16 * tj + r;
             const float gm = sm.gam[cc];
             float part = 0.f;
@@ -1287,9 +1321,13 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
     {
         const int ti = wave >> 1, tj = wave & 1;
         f32x4 acc = zero4();
+        if constexpr (kBf) {
+            acc = rowdot<DV, true>(sm.dout, 16 * ti + r, sm.vn, 16 * tj + r, LV, g, acc);
+        } else {
 #pragma unroll 8
-        for (int j0 = 0; j0 < DV; j0 += 4)
-            acc = mma4(sm.dout[(16 * ti + r) * LV + j0 + g], sm.vn[(16 * tj + r) * LV + j0 + g], acc);
+            for (int j0 = 0; j0 < DV; j0 += 4)
+                acc = mma4(sm.dout[(16 * ti + r) * LV + j0 + g], sm.vn[(16 * tj + r) * LV + j0 + g], acc);
+        }
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4) {
             const int i = 16 * ti + 4 * g + v4, j = 16 * tj + r;
@@ -1333,9 +1371,13 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
     {
         const int ti = wave >> 1, tj = wave & 1;
         f32x4 acc = zero4();
+        if constexpr (kBf) {
+            acc = rowdot<DV, false>(sm.dvn, 16 * ti + r, sm.x, 16 * tj + r, LV, g, acc);
+        } else {
 #pragma unroll 8
-        for (int j0 = 0; j0 < DV; j0 += 4)
-            acc = mma4(sm.dvn[(16 * ti + r) * LV + j0 + g], sm.x[(16 * tj + r) * LV + j0 + g], acc);
+            for (int j0 = 0; j0 < DV; j0 += 4)
+                acc = mma4(sm.dvn[(16 * ti + r) * LV + j0 + g], sm.x[(16 * tj + r) * LV + j0 + g], acc);
+        }
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4) {
             const int i = 16 * ti + 4 * g + v4, s = 16 * tj + r;
@@ -1415,11 +1457,24 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
             int ti, tj;
             block_tile(kb, ti, tj);
             f32x4 aq = zero4(), ak = zero4();
+            if constexpr (kBf) {
+#pragma unroll
+                for (int j0 = 0; j0 < DV; j0 += 32) {
+                    BF2 sv = bf_row(sm.sblk, LV, 16 * (tj - 2 * kb) + r, j0, g);
+                    BF xo = bf_row1(sm.dout, LV, 16 * ti + r, j0, g);
+                    BF2 xx = bf_row(sm.vn, LV, 16 * ti + r, j0, g);
+                    ready(sv, xx);
+                    mfma_ready(xo.u);
+                    aq = mmab(xo, sv.h, mmab(xo, sv.l, aq));
+                    ak = mm3(xx, sv, ak);
+                }
+            } else {
 #pragma unroll 8
-            for (int j0 = 0; j0 < DV; j0 += 4) {
-                const float sv = sm.sblk[(16 * (tj - 2 * kb) + r) * LV + j0 + g];
-                aq = mma4(sm.dout[(16 * ti + r) * LV + j0 + g], sv, aq);
-                ak = mma4(sm.vn[(16 * ti + r) * LV + j0 + g], sv, ak);
+                for (int j0 = 0; j0 < DV; j0 += 4) {
+                    const float sv = sm.sblk[(16 * (tj - 2 * kb) + r) * LV + j0 + g];
+                    aq = mma4(sm.dout[(16 * ti + r) * LV + j0 + g], sv, aq);
+                    ak = mma4(sm.vn[(16 * ti + r) * LV + j0 + g], sv, ak);
+                }
             }
             if (ti == 0) {
                 aQh[kb >> 1] += aq;
