@@ -221,6 +221,20 @@ def bwd_kernel_macs(spec, kernel: str) -> int:
     return per * bwd_chunk_heads(spec)
 
 
+def bwd_grad_mfma_floor_s(spec) -> float:
+    """The least time the matrix cores need for one launch of the gradient kernel: on bf16
+    data the products that contract over value columns (dO S^T and dO Vn^T with dO exact as
+    one bf16: two bf16 terms; dX S^T, Vn dS'^T and dVn X^T: three) run on bf16 MFMA, the
+    rest on fp32 MFMA; fp32 data runs every product on fp32 MFMA."""
+    C, dk, dv = BWD_C, spec.dk, spec.dv
+    ch = bwd_chunk_heads(spec)
+    if spec.dtype != "bf16":
+        return 2 * bwd_kernel_macs(spec, "bwd_grad") / (MFMA_F32_PEAK_TFLOPS * 1e12)
+    f32_macs = (2 * C * dk * dv + 3 * C * C * dv + 4 * C * C * dk + 2 * C ** 3) * ch
+    bf16_term_macs = ((2 + 3 + 3) * C * dk * dv + (2 + 3) * C * C * dv) * ch
+    return 2 * f32_macs / (MFMA_F32_PEAK_TFLOPS * 1e12) + 2 * bf16_term_macs / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+
+
 def bwd_kernel_bytes(spec, kernel: str) -> int:
     """Algorithmic bytes of one launch of each backward kernel."""
     es = 4 if spec.dtype == "f32" else 2
@@ -428,12 +442,22 @@ def backward_bench(args, spec, t, cu, dev):
     dom = max(kernels, key=lambda k: kernels[k]["ms_avg"])
     kd = kernels[dom]
     ms_step = wall * 1e3 / args.steps
+    # the matrix cores' peak for the dominant kernel's mix of fp32 and bf16 products: its
+    # algorithmic flops over the least time the mix needs
+    peak = MFMA_F32_PEAK_TFLOPS
+    peak_note = "fp32 MFMA peak"
+    if dom == "bwd_grad":
+        peak = kd["flops"] / bwd_grad_mfma_floor_s(spec) / 1e12
+        if spec.dtype == "bf16":
+            peak_note = ("the kernel's mix: algorithmic flops over (fp32-product flops / 157.3 TFLOP/s + bf16 "
+                         "hi/lo term flops / 2,500 TFLOP/s), so frac = that floor time / the kernel's time")
     return {"metric": "KDA backward head-tokens/s (gradients of q, k, v, log a, beta)",
             "value": spec.head_tokens / (ms_step * 1e-3), "unit": "tokens/s", "ms_per_step": ms_step,
-            "dtype": "f32 arithmetic on " + spec.dtype + " data (fp32 MFMA; on bf16 data the two chains take "
-                     "hi/lo bf16 MFMA terms)",
-            "roofline": {"bound": "mfma", "achieved": kd["achieved_TFLOPs"], "peak": MFMA_F32_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": kd["achieved_TFLOPs"] / MFMA_F32_PEAK_TFLOPS,
+            "dtype": "f32 arithmetic on " + spec.dtype + " data (fp32 MFMA; on bf16 data the two chains and the "
+                     "gradient kernel's products over value columns take hi/lo bf16 MFMA terms)",
+            "roofline": {"bound": "mfma", "achieved": kd["achieved_TFLOPs"], "peak": peak,
+                         "peak_note": peak_note,
+                         "unit": "TFLOP/s", "frac": kd["achieved_TFLOPs"] / peak,
                          "traffic": traffic_for(args.workload, BWD_KERNELS[dom], kernel_sha(BWD_SOURCES)),
                          "kernel": BWD_KERNELS[dom], "kernel_ms_avg": kd["ms_avg"],
                          "flops": kd["flops"], "algorithmic_bytes": kd["algorithmic_bytes"],

@@ -1,6 +1,7 @@
 // kda_bwd.hip -- gradients of the KDA scan (q, k, v, log alpha, beta and the initial
-// state) for fp32 and bf16 data, fp32 arithmetic (gfx950): fp32 MFMA, except the two chains
-// on bf16 data, whose products take hi/lo bf16 operands (three bf16 MFMA terms).
+// state) for fp32 and bf16 data, fp32 arithmetic (gfx950): fp32 MFMA, except on bf16 data
+// the two chains' products and the gradient kernel's products over value columns, which
+// take hi/lo bf16 operands (three bf16 MFMA terms, two where one operand is bf16 data).
 //
 // The paper trains its model through these kernels (training setup paragraph on the
 // custom kernels over the packed tokens). The recurrence, per (sample, head)
