@@ -644,6 +644,7 @@ __device__ __forceinline__ void fused_unit(
         //      and the transposes ----
         float bt[2], qs[2] = {1.f, 1.f}, ks[2] = {1.f, 1.f};
         uint4 khF[2], kcH[2], qH[2];
+        uint4 kcL[2], qL[2];      // the bf16 remainders of Kc and Qh for P (output passes)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) bt[tt] = bf2f(cur.b[tt]);
         if constexpr (NORM) {
@@ -734,7 +735,8 @@ __device__ __forceinline__ void fused_unit(
                 dp += kx * qx;
             }
             khF[tt] = pack8(fkh);
-            kcH[tt] = pack8(fkc);
+            if constexpr (kOut) split8(fkc, kcH[tt], kcL[tt]);
+            else kcH[tt] = pack8(fkc);
             bf.yk[tt][p][lane] = make_uint4(khF[tt].x ^ 0x80008000u, khF[tt].y ^ 0x80008000u,
                                             khF[tt].z ^ 0x80008000u, khF[tt].w ^ 0x80008000u);
             if constexpr (kOut) {
@@ -742,7 +744,7 @@ __device__ __forceinline__ void fused_unit(
                 dp += __shfl_xor(dp, 16);
                 dp += __shfl_xor(dp, 32);
                 if (g == 0) sm.dpp[c & 1][p][16 * tt + r] = dp;
-                qH[tt] = pack8(fq);
+                split8(fq, qH[tt], qL[tt]);
                 bf.qf[tt][p][lane] = qH[tt];
             } else {
                 qH[tt] = make_uint4(0u, 0u, 0u, 0u);
@@ -751,16 +753,24 @@ __device__ __forceinline__ void fused_unit(
         auto partials = [&]() __attribute__((always_inline)) {
             mfma_ready(khF[0], khF[1], kcH[0], kcH[1]);
             mfma_ready(qH[0], qH[1]);
+            if constexpr (kOut) mfma_ready(kcL[0], kcL[1], qL[0], qL[1]);
             // partial products over the slab: Acc(X) holds X[4g + i][r]
             f32x4* pp = &sm.part[c & 1][p][0][0];
             pp[0 * 64 + lane] = EL::mma(Frag{khF[0]}, Frag{kcH[0]}, zero4());   // Kh0 Kc0^T
             pp[1 * 64 + lane] = EL::mma(Frag{khF[1]}, Frag{kcH[1]}, zero4());   // Kh1 Kc1^T
             pp[2 * 64 + lane] = EL::mma(Frag{kcH[0]}, Frag{khF[1]}, zero4());   // (Kh1 Kc0^T)^T
             if constexpr (kOut) {
-                // P^T blocks (Kc Qh^T): (0, 0), (1, 1), (1, 0)
-                pp[3 * 64 + lane] = EL::mma(Frag{kcH[0]}, Frag{qH[0]}, zero4());
-                pp[4 * 64 + lane] = EL::mma(Frag{kcH[1]}, Frag{qH[1]}, zero4());
-                pp[5 * 64 + lane] = EL::mma(Frag{kcH[0]}, Frag{qH[1]}, zero4());
+                // P^T blocks (Kc Qh^T): (0, 0), (1, 1), (1, 0), each from hi/lo bf16 parts of both
+                // operands (lo*hi + hi*lo + hi*hi): a row whose output is mostly P X (a sample's
+                // first chunk, where the state is zero) can be much shorter than |q| |k| |X|, and
+                // single bf16 operands put an error of about 2^-9 |q| |k| on each of its terms
+                auto p3 = [&](int a, int b) __attribute__((always_inline)) {
+                    return EL::mma(Frag{kcH[a]}, Frag{qH[b]},
+                                   EL::mma(Frag{kcH[a]}, Frag{qL[b]}, EL::mma(Frag{kcL[a]}, Frag{qH[b]}, zero4())));
+                };
+                pp[3 * 64 + lane] = p3(0, 0);
+                pp[4 * 64 + lane] = p3(1, 1);
+                pp[5 * 64 + lane] = p3(0, 1);
             }
             // transposes (channel rows over the chunk's tokens, exact): Kc^T and V to LDS
 #pragma unroll
