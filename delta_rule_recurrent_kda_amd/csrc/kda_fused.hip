@@ -90,7 +90,7 @@ struct Buf {
 struct FusedSmem {
     Buf buf[2];
     f32x4 part[2][4][6][64];  // per chunk (two in flight) and producer slab: partial A and P^T blocks
-    float ablk[2][16][20]; // the diagonal blocks of A (rows, fp32, padded) for the inverses
+    float ablk[4][16][20]; // the diagonal blocks of A (rows, fp32, padded) for the inverses, one per inverting wave
     float ssq[2][4][kFC];  // sums of squares of q and k per (slab, token)
     float dpp[2][4][kFC];  // per chunk (two in flight): q.k per (slab, token), the diagonal of P
 };
@@ -142,6 +142,21 @@ __device__ __forceinline__ void elim_step(float (&t)[4], const float (&ar)[16], 
 template <int... KK>
 __device__ __forceinline__ void elim_rows(float (&t)[4], const float (&ar)[16], int r, std::integer_sequence<int, KK...>) {
     (elim_step<KK>(t, ar, r), ...);
+}
+// The same on two columns per lane (half of the block's columns per wave)
+template <int KK>
+__device__ __forceinline__ void elim_step2(float (&t)[2], const float (&ar)[16], int r) {
+    const float a = r > KK ? -ar[KK] : 0.f;
+    float tk[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+        tk[m] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(t[m]), 0x150 + KK, 0xF, 0xF, false));
+#pragma unroll
+    for (int m = 0; m < 2; ++m) t[m] = fmaf(a, tk[m], t[m]);
+}
+template <int... KK>
+__device__ __forceinline__ void elim_rows2(float (&t)[2], const float (&ar)[16], int r, std::integer_sequence<int, KK...>) {
+    (elim_step2<KK>(t, ar, r), ...);
 }
 
 // Orders one wave's LDS writes before its later reads of other lanes' data: the LDS
@@ -796,39 +811,45 @@ __device__ __forceinline__ void fused_unit(
             tile_pass(0);
             partials();
         } else {
-            // ---- sums of the partial products: the diagonal blocks' inverses (waves 4, 5),
-            //      -A10 (wave 6), P (wave 7) ----
-            if (p < 2) {
-                // A_ii = StrictLower(diag(b) Kh Kc^T) of diagonal block ii = p, rows to LDS
-                const int ii = p;
+            // ---- sums of the partial products and the inverses of the two diagonal blocks of
+            //      I + A: wave 4 + p inverts block p & 1 on its columns 8 (p >> 1) .. + 7 (the
+            //      columns of an inverse are independent, so two waves halve the chain of
+            //      dependent steps); wave 6 also forms -A10 ----
+            {
+                const int ii = p & 1, hc = p >> 1;
                 {
+                    // A_ii = StrictLower(diag(b) Kh Kc^T) of diagonal block ii, rows to this wave's copy
                     f32x4 n = zero4();
 #pragma unroll
                     for (int x = 0; x < 4; ++x) n += sm.part[c & 1][x][ii][lane];
                     const float4 b4 = *reinterpret_cast<const float4*>(&bf.beta[16 * ii + 4 * g]);
                     const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) sm.ablk[ii][4 * g + i][r] = 4 * g + i > r ? bb[i] * n[i] : 0.f;
+                    for (int i = 0; i < 4; ++i) sm.ablk[p][4 * g + i][r] = 4 * g + i > r ? bb[i] * n[i] : 0.f;
                 }
                 lds_wait();
-                // T = (I + A_ii)^-1 in fp32 by elimination: lane (r, g) holds row r of A and
-                // T[r][4g..4g+3]; for k = 0..14 row k is final and every row below it takes
-                // -A[r][k] T[k][.], with T[k][.] broadcast along the lanes of the row (DPP)
+                // T = (I + A_ii)^-1 in fp32 by elimination: lane (r, g) holds row r of A and T[r][j0],
+                // T[r][j0 + 1] with j0 = 8 hc + 2 g; for k = 0..14 row k is final and every row below
+                // it takes -A[r][k] T[k][.], T[k][.] broadcast along the lanes of the row (DPP)
                 float ar[16];
 #pragma unroll
                 for (int k4 = 0; k4 < 4; ++k4) {
-                    const float4 a4 = *reinterpret_cast<const float4*>(&sm.ablk[ii][r][4 * k4]);
+                    const float4 a4 = *reinterpret_cast<const float4*>(&sm.ablk[p][r][4 * k4]);
                     ar[4 * k4] = a4.x;
                     ar[4 * k4 + 1] = a4.y;
                     ar[4 * k4 + 2] = a4.z;
                     ar[4 * k4 + 3] = a4.w;
                 }
-                float t[4];
+                const int j0 = 8 * hc + 2 * g;
+                float t[2];
 #pragma unroll
-                for (int m = 0; m < 4; ++m) t[m] = r == 4 * g + m ? 1.f : 0.f;
-                elim_rows(t, ar, r, std::make_integer_sequence<int, 15>{});
-                bf.tf[ii][lane] = pack4(t[0], t[1], t[2], t[3]);     // A operand: T_ii[r][4g + i]
-            } else if (p == 2) {
+                for (int m = 0; m < 2; ++m) t[m] = r == j0 + m ? 1.f : 0.f;
+                elim_rows2(t, ar, r, std::make_integer_sequence<int, 15>{});
+                // A operand of T_ii: lane (r, g') holds T[r][4g' .. 4g' + 3]; columns j0, j0 + 1 are
+                // its elements 2 (g & 1), + 1 in lane (r, j0 / 4)
+                reinterpret_cast<uint32_t*>(&bf.tf[ii][16 * (j0 >> 2) + r])[g & 1] = pack2(t[0], t[1]);
+            }
+            if (p == 2) {
                 // A10 as the A operand: Acc((Kh1 Kc0^T)^T) holds (Kh1 Kc0^T)[r][4g + i], row r of block
                 // (1, 0), scaled by beta of token 16 + r; negated for the solve
                 f32x4 n = zero4();
@@ -836,32 +857,6 @@ __device__ __forceinline__ void fused_unit(
                 for (int x = 0; x < 4; ++x) n += sm.part[c & 1][x][2][lane];
                 const float nbt = -bf.beta[16 + r];
                 bf.tf[2][lane] = pack4(nbt * n[0], nbt * n[1], nbt * n[2], nbt * n[3]);
-            } else if (kOut) {
-                f32x4 p00 = zero4(), p11 = zero4(), p10 = zero4();
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    p00 += sm.part[c & 1][x][3][lane];
-                    p11 += sm.part[c & 1][x][4][lane];
-                    p10 += sm.part[c & 1][x][5][lane];
-                }
-                float dg[2] = {0.f, 0.f};                           // the exact diagonal, tokens r and 16 + r
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    dg[0] += sm.dpp[c & 1][x][r];
-                    dg[1] += sm.dpp[c & 1][x][16 + r];
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {                       // P[r][4g + i], inclusive lower
-                    if (4 * g + i > r) {
-                        p00[i] = 0.f;
-                        p11[i] = 0.f;
-                    } else if (4 * g + i == r) {
-                        p00[i] = dg[0];
-                        p11[i] = dg[1];
-                    }
-                }
-                bf.pf[0][lane] = EL::from_acc(p00, zero4()).u;
-                bf.pf[1][lane] = EL::from_acc(p10, p11).u;
             }
         }
         lds_barrier();                                          // B2
