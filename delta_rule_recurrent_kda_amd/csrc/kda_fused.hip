@@ -20,13 +20,16 @@
 //     before the first barrier: chunk c + 1's rows from 16-byte row loads (chunk c + 2's
 //     loads go out as registers fall free): G by a product with a triangular ones matrix,
 //     the decayed rows, -diag(b) Kh and Qh as fragments, Kb and diag(b) V transposed, the
-//     slab's share of A and P (products over the slab's 32 channels) and of diag(P) = q.k;
-//     after it: the sums of the shares, the inverses of the two diagonal blocks of I + A
-//     (waves 4, 5), -A10 (wave 6), P (wave 7);
+//     slab's share of A and P (products over the slab's 32 channels) and of diag(P) = q.k
+//     (the output pass forms only token tile 1 before it, and tile 0, the shares and the
+//     transposes after it);
+//     in the summary pass, after it: the sums of the shares and the inverses of the two
+//     diagonal blocks of I + A (each block's columns split over two waves), -A10 (wave 6);
 //   consumers (waves 0-3; wave j owns value columns 32j..32j+31) carry their columns of
-//     S (fp32, registers) through chunk c: Z = diag(b) (V - Kh S) and Qh S before the first
-//     barrier, then X = T Z by 16-row blocks (X0 = T00 Z0, X1 = T11 (Z1 - A10 X0)), O += P X,
-//     the output, and the state update.
+//     S (fp32, registers) through chunk c: in the output pass they first sum the shares into
+//     the inverses of the diagonal blocks (waves 0, 1), -A10 (wave 2) and P (wave 3); then
+//     Z = diag(b) (V - Kh S) and Qh S before the first barrier, X = T Z by 16-row blocks
+//     (X0 = T00 Z0, X1 = T11 (Z1 - A10 X0)), O += P X, the output, and the state update.
 // Operand layouts are chosen so that every hand-over is a lane-ordered LDS store and load
 // and every transpose is an exact product with the identity (bf16 values).
 //
