@@ -1203,7 +1203,11 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
         tj = 4 * (kb >> 1) + ((wave - 2 * ti) & 3);
     };
 
-    // ---- X = V - Kh S (S streamed in 32-row blocks, the next one loaded ahead) ----
+    // On bf16 data the products over key channels with a state block take hi/lo bf16 MFMA
+    // terms too: this wave's [C][DV] tiles mm are (mm / NTJ, wave + 4 (mm % NTJ)), so it needs
+    // two row fragments (token tiles 0, 1) and NTJ column fragments of the block.
+    constexpr int NTJ = NVT / 4;
+    // ---- X = V - Kh S (S put into LDS one 32-row block at a time) ----
     {
         f32x4 ax[XPW];
 #pragma unroll
@@ -1212,13 +1216,27 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
         for (int kb = 0; kb < NKB; ++kb) {
             sS[kb].put(sm.sblk, LV);
             __syncthreads();
+            if constexpr (kBf) {
+                BF2 ka[2], sc[NTJ];
 #pragma unroll
-            for (int mm = 0; mm < XPW; ++mm) {
-                int ti, tj;
-                xtile(mm, ti, tj);
+                for (int i = 0; i < 2; ++i) ka[i] = bf_row(sm.kh, LK, 16 * i + r, 32 * kb, g);
 #pragma unroll
-                for (int k0 = 0; k0 < 32; k0 += 4)
-                    ax[mm] = mma4(sm.kh[(16 * ti + r) * LK + 32 * kb + k0 + g], sm.sblk[(k0 + g) * LV + 16 * tj + r], ax[mm]);
+                for (int i = 0; i < NTJ; ++i) sc[i] = bf_col(sm.sblk, LV, 16 * (wave + 4 * i) + r, g);
+                ready(ka[0], ka[1]);
+#pragma unroll
+                for (int i = 0; i < NTJ; ++i) ready(sc[i]);
+#pragma unroll
+                for (int mm = 0; mm < XPW; ++mm) ax[mm] = mm3(ka[mm / NTJ], sc[mm % NTJ], ax[mm]);
+            } else {
+#pragma unroll
+                for (int mm = 0; mm < XPW; ++mm) {
+                    int ti, tj;
+                    xtile(mm, ti, tj);
+#pragma unroll
+                    for (int k0 = 0; k0 < 32; k0 += 4)
+                        ax[mm] = mma4(sm.kh[(16 * ti + r) * LK + 32 * kb + k0 + g], sm.sblk[(k0 + g) * LV + 16 * tj + r],
+                                      ax[mm]);
+                }
             }
             __syncthreads();
         }
@@ -1270,14 +1288,37 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
         for (int kb = 0; kb < NKB; ++kb) {
             sD[kb].put(sm.sblk, LV);
             __syncthreads();
+            if constexpr (kBf) {
+                BF2 ka[2], sc[NTJ];
 #pragma unroll
-            for (int mm = 0; mm < XPW; ++mm) {
-                int ti, tj;
-                xtile(mm, ti, tj);
+                for (int i = 0; i < 2; ++i) {
+                    // Kc diag(gamma): row 16 i + r over channels 32 kb + ..
+                    const float* kr = sm.kc + (16 * i + r) * LK + 32 * kb + 4 * g;
+                    const float* gr = sm.gam + 32 * kb + 4 * g;
+                    const float4 k0 = *reinterpret_cast<const float4*>(kr), k1 = *reinterpret_cast<const float4*>(kr + 16);
+                    const float4 g0 = *reinterpret_cast<const float4*>(gr), g1 = *reinterpret_cast<const float4*>(gr + 16);
+                    const float f[8] = {k0.x * g0.x, k0.y * g0.y, k0.z * g0.z, k0.w * g0.w,
+                                        k1.x * g1.x, k1.y * g1.y, k1.z * g1.z, k1.w * g1.w};
+                    ka[i] = bf_split(f);
+                }
 #pragma unroll
-                for (int k0 = 0; k0 < 32; k0 += 4) {
-                    const int cc = 32 * kb + k0 + g;
-                    adv[mm] = mma4(sm.kc[(16 * ti + r) * LK + cc] * sm.gam[cc], sm.sblk[(k0 + g) * LV + 16 * tj + r], adv[mm]);
+                for (int i = 0; i < NTJ; ++i) sc[i] = bf_col(sm.sblk, LV, 16 * (wave + 4 * i) + r, g);
+                ready(ka[0], ka[1]);
+#pragma unroll
+                for (int i = 0; i < NTJ; ++i) ready(sc[i]);
+#pragma unroll
+                for (int mm = 0; mm < XPW; ++mm) adv[mm] = mm3(ka[mm / NTJ], sc[mm % NTJ], adv[mm]);
+            } else {
+#pragma unroll
+                for (int mm = 0; mm < XPW; ++mm) {
+                    int ti, tj;
+                    xtile(mm, ti, tj);
+#pragma unroll
+                    for (int k0 = 0; k0 < 32; k0 += 4) {
+                        const int cc = 32 * kb + k0 + g;
+                        adv[mm] = mma4(sm.kc[(16 * ti + r) * LK + cc] * sm.gam[cc], sm.sblk[(k0 + g) * LV + 16 * tj + r],
+                                       adv[mm]);
+                    }
                 }
             }
             int ti, tj;
