@@ -223,15 +223,16 @@ def bwd_kernel_macs(spec, kernel: str) -> int:
 
 def bwd_grad_mfma_floor_s(spec) -> float:
     """The least time the matrix cores need for one launch of the gradient kernel: on bf16
-    data the products that contract over value columns (dO S^T and dO Vn^T with dO exact as
-    one bf16: two bf16 terms; dX S^T, Vn dS'^T and dVn X^T: three) run on bf16 MFMA, the
-    rest on fp32 MFMA; fp32 data runs every product on fp32 MFMA."""
+    data the five products with a state matrix (Kh S, Kc diag(gamma) dS', Vn dS'^T, dO S^T
+    and dX S^T) and dO Vn^T, dVn X^T run on bf16 MFMA (three hi/lo terms, two where dO, exact
+    as one bf16, is an operand), the products over tokens on fp32 MFMA; fp32 data runs every
+    product on fp32 MFMA."""
     C, dk, dv = BWD_C, spec.dk, spec.dv
     ch = bwd_chunk_heads(spec)
     if spec.dtype != "bf16":
         return 2 * bwd_kernel_macs(spec, "bwd_grad") / (MFMA_F32_PEAK_TFLOPS * 1e12)
-    f32_macs = (2 * C * dk * dv + 3 * C * C * dv + 4 * C * C * dk + 2 * C ** 3) * ch
-    bf16_term_macs = ((2 + 3 + 3) * C * dk * dv + (2 + 3) * C * C * dv) * ch
+    f32_macs = (3 * C * C * dv + 4 * C * C * dk + 2 * C ** 3) * ch
+    bf16_term_macs = ((3 + 3 + 3 + 2 + 3) * C * dk * dv + (2 + 3) * C * C * dv) * ch
     return 2 * f32_macs / (MFMA_F32_PEAK_TFLOPS * 1e12) + 2 * bf16_term_macs / (MFMA_BF16_PEAK_TFLOPS * 1e12)
 
 
@@ -454,7 +455,8 @@ def backward_bench(args, spec, t, cu, dev):
     return {"metric": "KDA backward head-tokens/s (gradients of q, k, v, log a, beta)",
             "value": spec.head_tokens / (ms_step * 1e-3), "unit": "tokens/s", "ms_per_step": ms_step,
             "dtype": "f32 arithmetic on " + spec.dtype + " data (fp32 MFMA; on bf16 data the two chains and the "
-                     "gradient kernel's products over value columns take hi/lo bf16 MFMA terms)",
+                     "gradient kernel's products with the state and over value columns take hi/lo bf16 MFMA "
+                     "terms)",
             "roofline": {"bound": "mfma", "achieved": kd["achieved_TFLOPs"], "peak": peak,
                          "peak_note": peak_note,
                          "unit": "TFLOP/s", "frac": kd["achieved_TFLOPs"] / peak,
