@@ -1559,7 +1559,7 @@ __global__ __launch_bounds__(kBT) void kda_bwd_grad_kernel(
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4) {
             const int row = 16 * ti + 4 * g + v4, cc = 16 * tj + r, o = row * LK + cc;
-            const float G = F0[o], ex = expf(G), ei = expf(-G);
+            const float G = F0[o], G2 = G * kLog2e, ex = fast_exp2(G2), ei = fast_exp2(-G2);
             const float a = aQh[mm][v4], b = aKh[mm][v4], e = aKc[mm][v4];
             F0[o] = a * ex;
             F1[o] = b * ex + e * ei;
