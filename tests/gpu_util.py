@@ -96,13 +96,16 @@ def compare(spec, out, fs, o_ref, f_ref, heads=None, label=""):
     zero = rown == 0
     assert np.all(rowe[zero] == 0), "rows with a zero reference must be exactly zero"
     rel = np.where(zero, 0.0, rowe / np.where(zero, 1.0, rown))
+    if rel.size == 0:                   # a pack with no tokens: only the final states to compare
+        rel = np.zeros((1, 1))
+        rown = np.zeros((1, 1))
     i = np.unravel_index(np.argmax(rel), rel.shape)
     srn = np.linalg.norm(srf, axis=3)
     sre = np.abs(s - srf).max(axis=3)
     szero = srn == 0
     assert np.all(sre[szero] == 0)
     srel = np.where(szero, 0.0, sre / np.where(szero, 1.0, srn))
-    frob = np.linalg.norm(o - orf) / max(np.linalg.norm(orf), 1e-300)
+    frob = np.linalg.norm(o - orf) / max(np.linalg.norm(orf), 1e-300) if orf.size else 0.0
     stats.update(worst_row=float(rel.max()), worst_row_at=(int(i[0]), hs[int(i[1])]),
                  worst_row_norm=float(rown[i]), median_row=float(np.median(rel)),
                  worst_state_row=float(srel.max()), frob_out=float(frob))

@@ -42,7 +42,7 @@ def _describe(spec, norm, init):
             f"norm={norm} initial_state={init}")
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_pack_forward(seed):
     import torch
     spec, norm, init = _case(seed)
@@ -62,7 +62,7 @@ def test_random_pack_forward(seed):
     gu.compare(spec, out, fs, o_ref, f_ref, label=f"random forward {seed}")
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(16))
 def test_random_pack_backward(seed):
     spec, norm, init = _case(100 + seed)
     gu.log(f"case random backward {seed}: {_describe(spec, norm, init)}")
