@@ -395,6 +395,20 @@ def test_all_samples_empty(dt):
     assert torch.equal(grads[5], dfs)
 
 
+def _pool_reserved_bytes(device: int = 0) -> int:
+    """Bytes the device's default stream-ordered memory pool holds from the driver, read with
+    hipMemPoolGetAttribute(hipMemPoolAttrReservedMemCurrent) from the HIP runtime that the
+    library is linked against (the loader returns the copy already in the process)."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    pool = ctypes.c_void_p()
+    assert hip.hipDeviceGetDefaultMemPool(ctypes.byref(pool), ctypes.c_int(device)) == 0
+    val = ctypes.c_uint64(0)
+    reserved_mem_current = 0x5
+    assert hip.hipMemPoolGetAttribute(pool, ctypes.c_int(reserved_mem_current), ctypes.byref(val)) == 0
+    return int(val.value)
+
+
 def test_release_between_calls():
     """kda_release after a forward and a backward gives the pooled workspace back; the next
     calls allocate again and give the same results bit for bit."""
@@ -409,7 +423,14 @@ def test_release_between_calls():
     o1, f1 = kda.forward(*args)
     g1 = kda.backward(*args, do)
     torch.cuda.synchronize()
+    held = _pool_reserved_bytes()
     kda.release()
+    after = _pool_reserved_bytes()
+    gu.log(f"default pool reserved: {held} B after the calls, {after} B after kda_release")
+    # the workspaces come from the device's default stream-ordered pool, which the library
+    # keeps (release threshold at its maximum); kda_release trims it, and with nothing in
+    # flight nothing stays reserved
+    assert held > 0 and after == 0
     o2, f2 = kda.forward(*args)
     g2 = kda.backward(*args, do)
     torch.cuda.synchronize()
